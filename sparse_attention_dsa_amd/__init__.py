@@ -1,0 +1,8 @@
+"""DeepSeek Sparse Attention (DSA) step for AMD MI355X (gfx950).
+
+Lightning-indexer scores, top-K selection and sparse MQA-mode MLA over a
+paged latent / indexer-key cache, as hand-written HIP kernels behind the C ABI
+in ``include/dsa.h``.  ``binding`` is the thin Python front end.
+"""
+from .binding import (Batch, DsaError, decode_step, indexer_scores, lib, sparse_mla_decode,  # noqa: F401
+                      sparse_mla_prefill, topk, workspace_size)

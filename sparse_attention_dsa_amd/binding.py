@@ -1,0 +1,214 @@
+"""ctypes binding of libdsa.so (include/dsa.h), one function per C entry point.
+
+Argument marshalling only: torch tensors are used for device memory and the
+current stream; every step of the computation runs in the library's HIP
+kernels.  The library must be built (``python -m sparse_attention_dsa_amd.build``);
+loading fails loudly otherwise and there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
+
+DSA_OK = 0
+F32, BF16, E4M3 = 0, 1, 2
+OP_TOPK, OP_MLA_DECODE, OP_MLA_PREFILL, OP_DECODE_STEP = 1, 2, 3, 4
+
+EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
+           "dsa_decode_step", "dsa_workspace_size", "dsa_status_string", "dsa_check_device")
+
+
+class DsaBatch(C.Structure):
+    _fields_ = [("num_requests", C.c_int32), ("total_q", C.c_int32), ("max_q_len", C.c_int32),
+                ("max_context_len", C.c_int32), ("context_lens", C.c_void_p),
+                ("query_start_loc", C.c_void_p), ("page_table", C.c_void_p),
+                ("max_blocks", C.c_int32), ("block_size", C.c_int32)]
+
+
+class DsaIndexCache(C.Structure):
+    _fields_ = [("keys", C.c_void_p), ("scales", C.c_void_p), ("dtype", C.c_int32), ("dim", C.c_int32)]
+
+
+class DsaLatentCache(C.Structure):
+    _fields_ = [("kv", C.c_void_p), ("scales", C.c_void_p), ("dtype", C.c_int32),
+                ("d_latent", C.c_int32), ("d_rope", C.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libdsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libdsa.so is not built; run `python -m sparse_attention_dsa_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        P = C.POINTER
+        vp, i32, i64, sz, f32 = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t, C.c_float
+        L.dsa_indexer_scores.argtypes = [P(DsaBatch), P(DsaIndexCache), vp, vp, i32, vp, i64, vp]
+        L.dsa_topk.argtypes = [P(DsaBatch), vp, i64, i32, vp, vp, sz, vp]
+        mla = [P(DsaBatch), P(DsaLatentCache), vp, i32, vp, i32, f32, vp, vp, vp, sz, vp]
+        L.dsa_sparse_mla_decode.argtypes = mla
+        L.dsa_sparse_mla_prefill.argtypes = mla
+        L.dsa_decode_step.argtypes = [P(DsaBatch), P(DsaIndexCache), vp, vp, i32, P(DsaLatentCache), vp, i32,
+                                      i32, f32, vp, vp, vp, vp, sz, vp]
+        L.dsa_workspace_size.argtypes = [i32, P(DsaBatch), i32, i32, i32]
+        L.dsa_workspace_size.restype = sz
+        L.dsa_status_string.argtypes = [i32]
+        L.dsa_status_string.restype = C.c_char_p
+        L.dsa_check_device.argtypes = []
+        for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
+                     "dsa_decode_step", "dsa_check_device"):
+            getattr(L, name).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+class DsaError(RuntimeError):
+    def __init__(self, fn, status):
+        msg = lib().dsa_status_string(status).decode()
+        super().__init__("%s failed: %s (%d)" % (fn, msg, status))
+        self.status = status
+
+
+def _check(fn, status):
+    if status != DSA_OK:
+        raise DsaError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libdsa must be contiguous")
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return E4M3
+    raise ValueError("unsupported cache dtype %s" % t.dtype)
+
+
+class Batch:
+    """Batch geometry: device int32 tensors plus the host-known maxima."""
+
+    def __init__(self, context_lens: torch.Tensor, query_start_loc: torch.Tensor, page_table: torch.Tensor,
+                 block_size: int, max_q_len: int, max_context_len: int):
+        for t in (context_lens, query_start_loc, page_table):
+            if t.dtype != torch.int32 or not t.is_cuda:
+                raise ValueError("batch arrays must be int32 device tensors")
+        self.context_lens, self.query_start_loc, self.page_table = context_lens, query_start_loc, page_table
+        self.num_requests = context_lens.shape[0]
+        self.total_q = int(query_start_loc[-1].item()) if query_start_loc.numel() else 0
+        self.block_size, self.max_q_len, self.max_context_len = block_size, max_q_len, max_context_len
+
+    def struct(self) -> DsaBatch:
+        return DsaBatch(self.num_requests, self.total_q, self.max_q_len, self.max_context_len,
+                        self.context_lens.data_ptr(), self.query_start_loc.data_ptr(),
+                        self.page_table.data_ptr(), self.page_table.shape[1], self.block_size)
+
+
+def index_cache(keys: torch.Tensor, scales: Optional[torch.Tensor]) -> DsaIndexCache:
+    return DsaIndexCache(keys.data_ptr(), scales.data_ptr() if scales is not None else None,
+                         dtype_code(keys), keys.shape[-1])
+
+
+def latent_cache(kv: torch.Tensor, scales: Optional[torch.Tensor], d_latent: int) -> DsaLatentCache:
+    return DsaLatentCache(kv.data_ptr(), scales.data_ptr() if scales is not None else None,
+                          dtype_code(kv), d_latent, kv.shape[-1] - d_latent)
+
+
+def workspace_size(op: int, batch: Batch, k: int, n_heads: int = 0, n_heads_idx: int = 0) -> int:
+    b = batch.struct()
+    return int(lib().dsa_workspace_size(op, C.byref(b), k, n_heads, n_heads_idx))
+
+
+def _workspace(op, batch, k, n_heads, device, workspace):
+    need = workspace_size(op, batch, k, n_heads)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def indexer_scores(batch: Batch, keys, key_scales, q_idx, w, scores=None, ld=None, stream=None):
+    """Scores [T][ld] fp32 (entries past each row's visible count are untouched)."""
+    ld = ld or ((batch.max_context_len + 63) // 64 * 64)
+    if scores is None:
+        scores = torch.empty((batch.total_q, ld), dtype=torch.float32, device=q_idx.device)
+    b, c = batch.struct(), index_cache(keys, key_scales)
+    _check("dsa_indexer_scores", lib().dsa_indexer_scores(
+        C.byref(b), C.byref(c), _ptr(q_idx), _ptr(w), q_idx.shape[1], _ptr(scores), ld, _stream(stream)))
+    return scores
+
+
+def topk(batch: Batch, scores, k: int, indices=None, workspace=None, stream=None):
+    """Top-k logical indices [T][k] int32, ascending, -1 padded."""
+    if indices is None:
+        indices = torch.empty((batch.total_q, k), dtype=torch.int32, device=scores.device)
+    ws = _workspace(OP_TOPK, batch, k, 0, scores.device, workspace)
+    b = batch.struct()
+    _check("dsa_topk", lib().dsa_topk(C.byref(b), _ptr(scores), scores.shape[1], k, _ptr(indices),
+                                      _ptr(ws), ws.numel(), _stream(stream)))
+    return indices
+
+
+def _out_like(kv, q, d_latent):
+    dt = torch.float32 if kv.dtype == torch.float32 else torch.bfloat16
+    return torch.empty((q.shape[0], q.shape[1], d_latent), dtype=dt, device=q.device)
+
+
+def _mla(fn, op, batch, kv, kv_scales, d_latent, q, indices, scale, out, lse, workspace, stream):
+    k = indices.shape[1]
+    if out is None:
+        out = _out_like(kv, q, d_latent)
+    ws = _workspace(op, batch, k, q.shape[1], q.device, workspace)
+    b, c = batch.struct(), latent_cache(kv, kv_scales, d_latent)
+    _check(fn, getattr(lib(), fn)(C.byref(b), C.byref(c), _ptr(q), q.shape[1], _ptr(indices), k,
+                                  float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def sparse_mla_decode(batch: Batch, kv, kv_scales, d_latent, q, indices, scale, out=None, lse=None,
+                      workspace=None, stream=None):
+    return _mla("dsa_sparse_mla_decode", OP_MLA_DECODE, batch, kv, kv_scales, d_latent, q, indices,
+                scale, out, lse, workspace, stream)
+
+
+def sparse_mla_prefill(batch: Batch, kv, kv_scales, d_latent, q, indices, scale, out=None, lse=None,
+                       workspace=None, stream=None):
+    return _mla("dsa_sparse_mla_prefill", OP_MLA_PREFILL, batch, kv, kv_scales, d_latent, q, indices,
+                scale, out, lse, workspace, stream)
+
+
+def decode_step(batch: Batch, keys, key_scales, q_idx, w, kv, kv_scales, d_latent, q_mla, k, scale,
+                out=None, lse=None, indices_out=None, workspace=None, stream=None):
+    """Indexer + top-k + sparse MLA in one call; returns out (and fills indices_out)."""
+    if out is None:
+        out = _out_like(kv, q_mla, d_latent)
+    ws = _workspace(OP_DECODE_STEP, batch, k, q_mla.shape[1], q_mla.device, workspace)
+    b, ic, lc = batch.struct(), index_cache(keys, key_scales), latent_cache(kv, kv_scales, d_latent)
+    _check("dsa_decode_step", lib().dsa_decode_step(
+        C.byref(b), C.byref(ic), _ptr(q_idx), _ptr(w), q_idx.shape[1], C.byref(lc), _ptr(q_mla),
+        q_mla.shape[1], k, float(scale), _ptr(out), _ptr(lse), _ptr(indices_out), _ptr(ws), ws.numel(),
+        _stream(stream)))
+    return out
+
+
+def check_device() -> int:
+    return int(lib().dsa_check_device())

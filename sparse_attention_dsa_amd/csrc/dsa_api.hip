@@ -1,0 +1,300 @@
+// C ABI of the DSA step (declared in include/dsa.h): argument validation,
+// workspace layout and kernel launches.  No allocation, no synchronisation,
+// no state kept between calls.
+#include <string.h>
+
+#include "dsa.h"
+#include "dsa_kernels.h"
+
+using namespace dsa;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+int64_t round_up64(int64_t x) { return (x + 63) / 64 * 64; }
+
+bool batch_ok(const dsa_batch* b) {
+    return b && b->num_requests >= 1 && b->total_q >= 1 && b->max_q_len >= 1 &&
+           b->max_context_len >= 1 && b->max_context_len >= b->max_q_len && b->context_lens &&
+           b->query_start_loc && b->page_table && b->block_size >= 1 && b->max_blocks >= 1 &&
+           (int64_t)b->max_blocks * b->block_size >= b->max_context_len;
+}
+
+Geometry geometry(const dsa_batch* b) {
+    Geometry g;
+    g.B = b->num_requests;
+    g.T = b->total_q;
+    g.max_q_len = b->max_q_len;
+    g.max_ctx = b->max_context_len;
+    g.ctx = b->context_lens;
+    g.qsl = b->query_start_loc;
+    g.page_table = b->page_table;
+    g.max_blocks = b->max_blocks;
+    g.block_size = b->block_size;
+    return g;
+}
+
+// Workspace pieces (byte offsets from the base, each 256-aligned).
+struct TopkLayout { size_t hist, counters, cand, end; };
+TopkLayout topk_layout(size_t base, int T) {
+    TopkLayout l;
+    l.hist = base;
+    l.counters = align_up(l.hist + sizeof(uint32_t) * (size_t)T * HIST_BINS);
+    l.cand = align_up(l.counters + sizeof(TopkCounters) * (size_t)T);
+    l.end = align_up(l.cand + sizeof(int32_t) * (size_t)T * TOPK_CAND_CAP);
+    return l;
+}
+
+struct MlaLayout { size_t part_o, part_lse, end; int splits; };
+MlaLayout mla_layout(size_t base, const dsa_batch* b, int k, int n_heads, bool prefill, bool fast) {
+    MlaLayout l;
+    l.splits = (fast && !prefill) ? mla_decode_splits(b->total_q, n_heads, k) : 1;
+    l.part_o = l.part_lse = l.end = base;
+    if (l.splits > 1) {
+        const size_t th = (size_t)b->total_q * n_heads * l.splits;
+        l.part_lse = align_up(base + sizeof(float) * th * 512);
+        l.end = align_up(l.part_lse + sizeof(float) * th);
+    }
+    return l;
+}
+
+struct StepLayout { size_t scores, indices; TopkLayout tk; MlaLayout ml; size_t end; int64_t ld; };
+StepLayout step_layout(const dsa_batch* b, int k, int n_heads, bool fast_mla) {
+    StepLayout l;
+    l.ld = round_up64(b->max_context_len);
+    l.scores = 0;
+    l.indices = align_up(sizeof(float) * (size_t)b->total_q * l.ld);
+    l.tk = topk_layout(align_up(l.indices + sizeof(int32_t) * (size_t)b->total_q * k), b->total_q);
+    l.ml = mla_layout(l.tk.end, b, k, n_heads, false, fast_mla);
+    l.end = l.ml.end;
+    return l;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH; }
+
+int device_arch_ok() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return DSA_ERR_DEVICE;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DSA_ERR_DEVICE;
+    return strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? DSA_OK : DSA_ERR_DEVICE;
+}
+
+int check_device_cached() {
+    // Per-device result; the arch of a device never changes.
+    static int cache[64];
+    static bool known[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return DSA_ERR_DEVICE;
+    if (dev < 0 || dev >= 64) return device_arch_ok();
+    if (!known[dev]) { cache[dev] = device_arch_ok(); known[dev] = true; }
+    return cache[dev];
+}
+
+bool index_cache_ok(const dsa_index_cache* c) {
+    return c && c->keys && c->dim >= 1 && (c->dtype == DSA_F32 || c->dtype == DSA_E4M3);
+}
+
+bool latent_cache_ok(const dsa_latent_cache* c) {
+    if (!c || !c->kv || c->d_latent < 1 || c->d_rope < 0) return false;
+    if (c->dtype == DSA_E4M3) return c->scales != nullptr;
+    return (c->dtype == DSA_F32 || c->dtype == DSA_BF16) && c->scales == nullptr;
+}
+
+int validate_indexer(const dsa_batch* b, const dsa_index_cache* c, const void* q, const float* w,
+                     int n_heads) {
+    if (!batch_ok(b) || !c || !c->keys || !q || !w || n_heads < 1) return DSA_ERR_INVALID_ARG;
+    if (!index_cache_ok(c)) return DSA_ERR_UNSUPPORTED;
+    if ((int64_t)n_heads * c->dim > 12288) return DSA_ERR_UNSUPPORTED;   // generic path's LDS
+    return DSA_OK;
+}
+
+int validate_mla(const dsa_batch* b, const dsa_latent_cache* c, const void* q, int n_heads, int k,
+                 const void* out) {
+    if (!batch_ok(b) || !q || !out || n_heads < 1 || k < 1) return DSA_ERR_INVALID_ARG;
+    if (!c || !c->kv) return DSA_ERR_INVALID_ARG;
+    if (!latent_cache_ok(c)) return DSA_ERR_UNSUPPORTED;
+    if (!mla_fast_path(c->dtype, c->d_latent, c->d_rope, n_heads, b->block_size)) {
+        // generic path keeps q row and logits in LDS
+        if ((size_t)(c->d_latent + c->d_rope + k) * sizeof(float) > 60 * 1024) return DSA_ERR_UNSUPPORTED;
+    }
+    return DSA_OK;
+}
+
+MlaArgs mla_args(const dsa_batch* b, const dsa_latent_cache* c, const void* q, int n_heads,
+                 const int32_t* indices, int k, float scale, void* out, float* lse) {
+    MlaArgs a;
+    a.g = geometry(b);
+    a.kv = c->kv; a.kv_scales = c->scales; a.kv_dtype = c->dtype;
+    a.d_latent = c->d_latent; a.d_rope = c->d_rope;
+    a.q = q; a.n_heads = n_heads;
+    a.indices = indices; a.k = k; a.scale = scale;
+    a.out = out; a.lse = lse;
+    a.part_o = nullptr; a.part_lse = nullptr; a.splits = 1;
+    return a;
+}
+
+// Workspace check for an MLA launch placed at `ws_base` (host only).
+int mla_workspace_ok(const dsa_batch* b, const dsa_latent_cache* c, int n_heads, int k, const void* ws,
+                     size_t ws_bytes, size_t ws_base, bool prefill) {
+    const bool fast = mla_fast_path(c->dtype, c->d_latent, c->d_rope, n_heads, b->block_size);
+    const MlaLayout l = mla_layout(ws_base, b, k, n_heads, prefill, fast);
+    if (l.splits > 1 && (!ws || l.end > ws_bytes)) return DSA_ERR_WORKSPACE;
+    return DSA_OK;
+}
+
+int run_mla(const dsa_batch* b, const dsa_latent_cache* c, const void* q, int n_heads,
+            const int32_t* indices, int k, float scale, void* out, float* lse, char* ws, size_t ws_bytes,
+            size_t ws_base, bool prefill, hipStream_t s) {
+    const bool fast = mla_fast_path(c->dtype, c->d_latent, c->d_rope, n_heads, b->block_size);
+    MlaLayout l = mla_layout(ws_base, b, k, n_heads, prefill, fast);
+    if (l.splits > 1 && (!ws || l.end > ws_bytes)) return DSA_ERR_WORKSPACE;
+    MlaArgs a = mla_args(b, c, q, n_heads, indices, k, scale, out, lse);
+    a.splits = l.splits;
+    if (l.splits > 1) {
+        if (!ws) return DSA_ERR_WORKSPACE;
+        a.part_o = (float*)(ws + l.part_o);
+        a.part_lse = (float*)(ws + l.part_lse);
+    }
+    return launch_status(launch_mla(a, prefill, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_string(int32_t status) {
+    switch (status) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_INVALID_ARG: return "invalid argument";
+    case DSA_ERR_UNSUPPORTED: return "unsupported dtype or shape";
+    case DSA_ERR_WORKSPACE: return "workspace too small";
+    case DSA_ERR_DEVICE: return "current device is not gfx950";
+    case DSA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int dsa_check_device(void) { return check_device_cached(); }
+
+size_t dsa_workspace_size(int32_t op, const dsa_batch* b, int32_t k, int32_t n_heads, int32_t n_heads_idx) {
+    (void)n_heads_idx;
+    if (!batch_ok(b)) return 0;
+    switch (op) {
+    case DSA_OP_TOPK:
+        if (k < 1 || k > TOPK_MAX_K) return 0;
+        return topk_layout(0, b->total_q).end;
+    case DSA_OP_MLA_DECODE:
+    case DSA_OP_MLA_PREFILL:
+        if (k < 1 || n_heads < 1) return 0;
+        // sized for the fast path; the generic path needs none
+        return mla_layout(0, b, k, n_heads, op == DSA_OP_MLA_PREFILL,
+                          n_heads % MLA_HEADS_PER_WG == 0).end;
+    case DSA_OP_DECODE_STEP:
+        if (k < 1 || k > TOPK_MAX_K || n_heads < 1) return 0;
+        return step_layout(b, k, n_heads, n_heads % MLA_HEADS_PER_WG == 0).end;
+    default:
+        return 0;
+    }
+}
+
+int dsa_indexer_scores(const dsa_batch* b, const dsa_index_cache* c, const void* q_idx, const float* w,
+                       int32_t n_heads_idx, float* scores, int64_t ld, dsa_stream_t stream) {
+    int st = validate_indexer(b, c, q_idx, w, n_heads_idx);
+    if (st != DSA_OK) return st;
+    if (!scores || ld < b->max_context_len) return DSA_ERR_INVALID_ARG;
+    if ((st = check_device_cached()) != DSA_OK) return st;
+    IndexerArgs a;
+    a.g = geometry(b);
+    a.keys = c->keys; a.key_scales = c->scales; a.key_dtype = c->dtype; a.dim = c->dim;
+    a.q = q_idx; a.w = w; a.n_heads = n_heads_idx;
+    a.scores = scores; a.ld = ld; a.hist = nullptr;
+    return launch_status(launch_indexer(a, (hipStream_t)stream));
+}
+
+int dsa_topk(const dsa_batch* b, const float* scores, int64_t ld, int32_t k, int32_t* indices,
+             void* ws, size_t ws_bytes, dsa_stream_t stream) {
+    if (!batch_ok(b) || !scores || !indices || k < 1 || ld < b->max_context_len) return DSA_ERR_INVALID_ARG;
+    if (k > TOPK_MAX_K) return DSA_ERR_UNSUPPORTED;
+    const TopkLayout l = topk_layout(0, b->total_q);
+    if (!ws || ws_bytes < l.end) return DSA_ERR_WORKSPACE;
+    int st = check_device_cached();
+    if (st != DSA_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    char* base = (char*)ws;
+    TopkArgs a;
+    a.g = geometry(b);
+    a.scores = scores; a.ld = ld; a.k = k; a.indices = indices;
+    a.hist = (uint32_t*)(base + l.hist);
+    a.counters = (TopkCounters*)(base + l.counters);
+    a.cand = (int32_t*)(base + l.cand);
+    hipError_t e = launch_zero_u32(a.hist, (l.cand - l.hist) / sizeof(uint32_t), s);
+    if (e == hipSuccess) e = launch_topk_hist(a, s);
+    if (e == hipSuccess) e = launch_topk_select(a, s);
+    return launch_status(e);
+}
+
+static int mla_entry(const dsa_batch* b, const dsa_latent_cache* c, const void* q, int32_t n_heads,
+                     const int32_t* indices, int32_t k, float scale, void* out, float* lse, void* ws,
+                     size_t ws_bytes, dsa_stream_t stream, bool prefill) {
+    int st = validate_mla(b, c, q, n_heads, k, out);
+    if (st != DSA_OK) return st;
+    if (!indices) return DSA_ERR_INVALID_ARG;
+    if ((st = mla_workspace_ok(b, c, n_heads, k, ws, ws ? ws_bytes : 0, 0, prefill)) != DSA_OK) return st;
+    if ((st = check_device_cached()) != DSA_OK) return st;
+    return run_mla(b, c, q, n_heads, indices, k, scale, out, lse, (char*)ws, ws ? ws_bytes : 0, 0, prefill,
+                   (hipStream_t)stream);
+}
+
+int dsa_sparse_mla_decode(const dsa_batch* b, const dsa_latent_cache* c, const void* q, int32_t n_heads,
+                          const int32_t* indices, int32_t k, float scale, void* out, float* lse, void* ws,
+                          size_t ws_bytes, dsa_stream_t stream) {
+    return mla_entry(b, c, q, n_heads, indices, k, scale, out, lse, ws, ws_bytes, stream, false);
+}
+
+int dsa_sparse_mla_prefill(const dsa_batch* b, const dsa_latent_cache* c, const void* q, int32_t n_heads,
+                           const int32_t* indices, int32_t k, float scale, void* out, float* lse, void* ws,
+                           size_t ws_bytes, dsa_stream_t stream) {
+    return mla_entry(b, c, q, n_heads, indices, k, scale, out, lse, ws, ws_bytes, stream, true);
+}
+
+int dsa_decode_step(const dsa_batch* b, const dsa_index_cache* ic, const void* q_idx, const float* w,
+                    int32_t n_heads_idx, const dsa_latent_cache* lc, const void* q_mla, int32_t n_heads,
+                    int32_t k, float scale, void* out, float* lse, int32_t* indices_out, void* ws,
+                    size_t ws_bytes, dsa_stream_t stream) {
+    int st = validate_indexer(b, ic, q_idx, w, n_heads_idx);
+    if (st != DSA_OK) return st;
+    if ((st = validate_mla(b, lc, q_mla, n_heads, k, out)) != DSA_OK) return st;
+    if (k > TOPK_MAX_K) return DSA_ERR_UNSUPPORTED;
+    const bool fast = mla_fast_path(lc->dtype, lc->d_latent, lc->d_rope, n_heads, b->block_size);
+    const StepLayout l = step_layout(b, k, n_heads, fast);
+    if (!ws || ws_bytes < l.end) return DSA_ERR_WORKSPACE;
+    if ((st = check_device_cached()) != DSA_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    char* base = (char*)ws;
+    float* scores = (float*)(base + l.scores);
+    int32_t* indices = indices_out ? indices_out : (int32_t*)(base + l.indices);
+
+    TopkArgs tk;
+    tk.g = geometry(b);
+    tk.scores = scores; tk.ld = l.ld; tk.k = k; tk.indices = indices;
+    tk.hist = (uint32_t*)(base + l.tk.hist);
+    tk.counters = (TopkCounters*)(base + l.tk.counters);
+    tk.cand = (int32_t*)(base + l.tk.cand);
+    hipError_t e = launch_zero_u32(tk.hist, (l.tk.cand - l.tk.hist) / sizeof(uint32_t), s);
+
+    IndexerArgs ia;
+    ia.g = tk.g;
+    ia.keys = ic->keys; ia.key_scales = ic->scales; ia.key_dtype = ic->dtype; ia.dim = ic->dim;
+    ia.q = q_idx; ia.w = w; ia.n_heads = n_heads_idx;
+    ia.scores = scores; ia.ld = l.ld; ia.hist = tk.hist;
+    if (e == hipSuccess) e = launch_indexer(ia, s);
+    if (e == hipSuccess) e = launch_topk_select(tk, s);
+    if (e != hipSuccess) return DSA_ERR_LAUNCH;
+    return run_mla(b, lc, q_mla, n_heads, indices, k, scale, out, lse, base, ws_bytes, l.tk.end, false, s);
+}
+
+}  // extern "C"

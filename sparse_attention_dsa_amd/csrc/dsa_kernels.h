@@ -1,0 +1,154 @@
+// Internal definitions shared by the DSA HIP kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+// ----------------------------------------------------------------- vectors
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Histogram of the top bits of the order-preserving score key, used to find
+// the bucket that holds the K-th largest score.
+constexpr int HIST_BITS = 12;
+constexpr int HIST_BINS = 1 << HIST_BITS;
+constexpr int HIST_SHIFT = 32 - HIST_BITS;
+
+// Candidates kept per query row for the exact refinement of the threshold
+// bucket; beyond this the refinement rescans the row's scores.
+constexpr int TOPK_CAND_CAP = 16384;
+constexpr int TOPK_MAX_K = 4096;
+
+// Per-row top-K bookkeeping in the workspace.
+struct TopkCounters {
+    uint32_t above;      // tokens in buckets above the threshold bucket
+    uint32_t cand;       // tokens in the threshold bucket
+    uint32_t bucket;     // threshold bucket
+    uint32_t pad;
+};
+
+// ----------------------------------------------------------- conversions
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// OCP e4m3fn code -> fp32, exactly: normal (1+m/8)*2^(e-7), subnormal m*2^-9.
+// (The NaN codes 0x7F/0xFF are not produced by the caches and decode to 480.)
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+    const uint32_t e = (code >> 3) & 0xFu, m = code & 7u;
+    float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+    return (code & 0x80u) ? -v : v;
+}
+
+// Order-preserving map of a float to uint32 (larger float -> larger key);
+// -0 is folded onto +0 so that equal scores get equal keys.
+__device__ __forceinline__ uint32_t score_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u << 1) == 0u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ------------------------------------------------------------------ MFMA
+// D = A(16x128 fp8) * B(128x16 fp8) + C, OCP e4m3 operands, fp32 accumulate.
+// Lane l holds row/column (l & 15) of A/B and 32 of the 128 k-values; A and
+// B use the same k assignment, so any consistent permutation of k is valid.
+__device__ __forceinline__ f32x4 mfma_fp8_16x16x128(i32x8 a, i32x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// D = A(16x32 bf16) * B(32x16 bf16) + C.  Lane l: A row / B column (l & 15),
+// k-values 8*(l>>4) .. 8*(l>>4)+7.  C/D: column (l & 15), rows 4*(l>>4)+i.
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ i32x8 join_i32x8(u32x4 lo, u32x4 hi) {
+    i32x8 r;
+    r[0] = (int)lo[0]; r[1] = (int)lo[1]; r[2] = (int)lo[2]; r[3] = (int)lo[3];
+    r[4] = (int)hi[0]; r[5] = (int)hi[1]; r[6] = (int)hi[2]; r[7] = (int)hi[3];
+    return r;
+}
+
+// ----------------------------------------------------------- batch maps
+// Request owning query row t: the largest r with qsl[r] <= t.
+__device__ __forceinline__ int find_request(const int32_t* qsl, int B, int t) {
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (qsl[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Visible-token count of query row t (query j of request r sees [0, L-ql+j]).
+__device__ __forceinline__ int visible_count(const int32_t* ctx, const int32_t* qsl, int r, int t) {
+    const int ql = qsl[r + 1] - qsl[r];
+    return ctx[r] - ql + (t - qsl[r]) + 1;
+}
+
+// ------------------------------------------------------- launch helpers
+struct Geometry {
+    int B, T, max_q_len, max_ctx;
+    const int32_t* ctx;
+    const int32_t* qsl;
+    const int32_t* page_table;
+    int max_blocks, block_size;
+};
+
+struct IndexerArgs {
+    Geometry g;
+    const void* keys; const float* key_scales; int key_dtype; int dim;
+    const void* q; const float* w; int n_heads;
+    float* scores; int64_t ld;
+    uint32_t* hist;     // [T][HIST_BINS] (zeroed) or nullptr
+};
+
+struct TopkArgs {
+    Geometry g;
+    const float* scores; int64_t ld;
+    int k;
+    int32_t* indices;        // [T][k]
+    uint32_t* hist;          // [T][HIST_BINS]
+    TopkCounters* counters;  // [T]
+    int32_t* cand;           // [T][TOPK_CAND_CAP]
+};
+
+struct MlaArgs {
+    Geometry g;
+    const void* kv; const float* kv_scales; int kv_dtype; int d_latent, d_rope;
+    const void* q; int n_heads;
+    const int32_t* indices; int k;
+    float scale;
+    void* out; float* lse;
+    float* part_o; float* part_lse;   // split partials or nullptr
+    int splits;
+};
+
+// Launchers (return hipError_t of the last launch).
+hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s);
+hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
+hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t s);
+hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s);
+hipError_t launch_mla(const MlaArgs& a, bool prefill, hipStream_t s);
+
+// Which MLA path serves these shapes, and how many splits it uses.
+bool mla_fast_path(int kv_dtype, int d_latent, int d_rope, int n_heads, int block_size);
+int mla_decode_splits(int T, int n_heads, int k);
+constexpr int MLA_HEADS_PER_WG = 64;
+
+}  // namespace dsa

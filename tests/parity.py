@@ -1,0 +1,99 @@
+"""Glue for the GPU parity tests: run the HIP library and the CPU oracle on the
+same seeded workload and compare by the rules of the method.
+
+Comparison rules:
+  * selections: each row holds min(K, n) distinct visible indices, ascending,
+    then -1 padding; the symmetric difference with the oracle's set may only
+    contain tokens whose oracle score lies within 1e-4 (relative) of the
+    oracle's K-th score (tokens on the selection boundary, where fp32 and
+    fp64 rounding may order them differently);
+  * outputs: max-abs <= 2e-2 for bf16 paths and <= 1e-4 for the fp32 path,
+    plus a relative Frobenius bound (1e-2 bf16, 1e-5 fp32) against the oracle
+    evaluated on the GPU's own selection.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import sparse_attention_dsa_amd as dsa
+import workloads
+
+BAND = 1e-4
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def upload(wl, dev="cuda"):
+    d = workloads.to_device(wl, dev)
+    batch = dsa.Batch(d["context_lens"], d["query_start_loc"], d["page_table"], wl.block_size,
+                      wl.max_q_len, wl.max_context_len)
+    return batch, d
+
+
+def gpu_step(wl, batch, d, lse=True):
+    """dsa_decode_step on the device; returns (out f32 numpy, lse, indices)."""
+    T, H = wl.total_q, wl.mla_heads
+    idx = torch.empty((T, wl.topk), dtype=torch.int32, device="cuda")
+    lse_t = torch.empty((T, H), dtype=torch.float32, device="cuda") if lse else None
+    out = dsa.decode_step(batch, d["idx_keys"], d["idx_scales"], d["q_idx"], d["w"], d["kv"], d["kv_scales"],
+                          wl.d_latent, d["q_mla"], wl.topk, wl.softmax_scale, lse=lse_t, indices_out=idx)
+    torch.cuda.synchronize()
+    return (out.float().cpu().numpy(), None if lse_t is None else lse_t.cpu().numpy(), idx.cpu().numpy())
+
+
+def check_selection(sel_row, scores_orc, K, band=BAND):
+    """Checks one GPU selection row against the oracle's scores; returns |diff|."""
+    n = scores_orc.shape[0]
+    m = min(K, n)
+    sel = np.asarray(sel_row)
+    assert sel.shape == (K,)
+    assert (sel[:m] >= 0).all(), "missing selections"
+    assert (sel[m:] == -1).all(), "padding must be -1"
+    s = sel[:m]
+    assert (np.diff(s) > 0).all(), "indices must be unique and ascending"
+    assert s[-1] < n, "non-causal index"
+    ref = oracle.topk(scores_orc, K)
+    diff = set(s.tolist()) ^ set(ref.tolist())
+    if diff:
+        assert n > K, "dense rows must select every visible token"
+        kth = float(scores_orc[ref[-1]])
+        bad = [x for x in diff if abs(float(scores_orc[x]) - kth) > band * abs(kth)]
+        assert not bad, "selection differs outside the tie band: %s" % bad[:8]
+    return len(diff)
+
+
+def check_out(gpu, ref, fp32):
+    atol = 1e-4 if fp32 else 2e-2
+    rel_bound = 1e-5 if fp32 else 1e-2
+    err = np.abs(gpu - ref).max()
+    rel = np.linalg.norm(gpu - ref) / max(np.linalg.norm(ref), 1e-30)
+    assert err <= atol, "max abs err %g > %g" % (err, atol)
+    assert rel <= rel_bound, "relative Frobenius err %g > %g" % (rel, rel_bound)
+    return err, rel
+
+
+def check_step_rows(wl, rows, out, lse, idx, threads=16, layer=1):
+    """Oracle-check the chosen query rows of a GPU step result."""
+    fp32 = wl.kv_dtype == "f32"
+    res = oracle.run_step(wl, rows=rows, threads=threads)
+    worst = 0.0
+    for t in rows:
+        r = res[t]
+        check_selection(idx[t], r["scores"], wl.topk)
+        # end to end against the oracle's own selection
+        check_out(out[t], r["out"], fp32)
+        # and against the oracle evaluated on the GPU's selection
+        sel = idx[t][idx[t] >= 0]
+        o2, l2 = oracle.query_mla(wl, t, sel, layer)
+        err, _ = check_out(out[t], o2, fp32)
+        worst = max(worst, err)
+        if lse is not None:
+            np.testing.assert_allclose(lse[t], l2, rtol=0, atol=1e-3 if not fp32 else 1e-5)
+    return worst

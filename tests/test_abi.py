@@ -1,0 +1,86 @@
+"""The C-ABI library: it loads, exports every entry point of include/dsa.h, and
+its host-side validation answers with the documented status codes without
+touching a device (no GPU is needed for any test here)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import sparse_attention_dsa_amd as dsa
+from sparse_attention_dsa_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return dsa.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert set(names) == set(B.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code, text in [(0, b"ok"), (-1, b"invalid argument"), (-3, b"workspace too small"),
+                       (-4, b"current device is not gfx950"), (7, b"unknown status")]:
+        assert L.dsa_status_string(code) == text
+
+
+def _batch(B_=2, T=2, maxq=1, maxctx=1000, bs=64, maxblocks=16):
+    # device pointers are never dereferenced by the host checks: any non-null value works
+    return B.DsaBatch(B_, T, maxq, maxctx, 0x1000, 0x2000, 0x3000, maxblocks, bs)
+
+
+def test_workspace_size_host_only(L):
+    b = _batch()
+    ws_topk = L.dsa_workspace_size(B.OP_TOPK, C.byref(b), 2048, 0, 0)
+    assert ws_topk > 2 * 4096 * 4
+    assert L.dsa_workspace_size(B.OP_TOPK, C.byref(b), 0, 0, 0) == 0
+    assert L.dsa_workspace_size(B.OP_TOPK, C.byref(b), 5000, 0, 0) == 0
+    assert L.dsa_workspace_size(99, C.byref(b), 16, 0, 0) == 0
+    step = L.dsa_workspace_size(B.OP_DECODE_STEP, C.byref(b), 2048, 128, 64)
+    assert step >= 2 * 1024 * 4 + ws_topk     # scores + selection bookkeeping
+    bad = _batch(maxctx=5000)                   # 16 blocks * 64 < 5000
+    assert L.dsa_workspace_size(B.OP_TOPK, C.byref(bad), 16, 0, 0) == 0
+
+
+def test_invalid_arguments_rejected_before_device(L):
+    b = _batch()
+    ic = B.DsaIndexCache(0x10, None, B.E4M3, 128)
+    assert L.dsa_indexer_scores(None, C.byref(ic), 0x1, 0x1, 64, 0x1, 1024, None) == -1
+    assert L.dsa_indexer_scores(C.byref(b), C.byref(ic), None, 0x1, 64, 0x1, 1024, None) == -1
+    assert L.dsa_indexer_scores(C.byref(b), C.byref(ic), 0x1, 0x1, 64, 0x1, 10, None) == -1  # ld < ctx
+    bad_dt = B.DsaIndexCache(0x10, None, B.BF16, 128)
+    assert L.dsa_indexer_scores(C.byref(b), C.byref(bad_dt), 0x1, 0x1, 64, 0x1, 1024, None) == -2
+    assert L.dsa_topk(C.byref(b), 0x1, 1024, 0, 0x1, 0x1, 1 << 30, None) == -1
+    assert L.dsa_topk(C.byref(b), 0x1, 1024, 5000, 0x1, 0x1, 1 << 30, None) == -2
+    assert L.dsa_topk(C.byref(b), 0x1, 1024, 16, 0x1, 0x1, 8, None) == -3
+    lc = B.DsaLatentCache(0x10, None, B.E4M3, 512, 64)      # fp8 latent needs scales
+    assert L.dsa_sparse_mla_decode(C.byref(b), C.byref(lc), 0x1, 128, 0x1, 2048, 0.1, 0x1, None,
+                                   0x1, 1 << 30, None) == -2
+    lc_ok = B.DsaLatentCache(0x10, None, B.BF16, 512, 64)
+    assert L.dsa_sparse_mla_decode(C.byref(b), C.byref(lc_ok), 0x1, 128, None, 2048, 0.1, 0x1, None,
+                                   0x1, 1 << 30, None) == -1
+    assert L.dsa_sparse_mla_decode(C.byref(b), C.byref(lc_ok), 0x1, 128, 0x1, 2048, 0.1, 0x1, None,
+                                   0x1, 16, None) == -3
+
+
+def test_valid_call_without_gpu_reports_device(L):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    b = _batch()
+    ic = B.DsaIndexCache(0x10, None, B.E4M3, 128)
+    assert L.dsa_indexer_scores(C.byref(b), C.byref(ic), 0x1, 0x1, 64, 0x1, 1024, None) == -4
+    assert L.dsa_check_device() == -4

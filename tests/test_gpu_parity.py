@@ -1,0 +1,198 @@
+"""GPU parity: every C entry point against the CPU oracle on seeded inputs
+small enough for the oracle (several tiles and ragged tails), plus the edge
+cases of the method (empty/short contexts, n around K, ties, MTP rows,
+fp8 latent, cross-layer index reuse)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_dsa_amd as dsa
+import workloads
+from parity import BAND, check_out, check_selection, check_step_rows, gpu_step, log, upload
+
+pytestmark = pytest.mark.gpu
+
+PROD = dict(idx_heads=64, idx_dim=128, mla_heads=128, d_latent=512, d_rope=64)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    assert dsa.binding.check_device() == 0, "not a gfx950 device"
+
+
+def _ragged(**kw):
+    # lengths straddle page (64) and K (2048) boundaries
+    return workloads.make_workload("single_b1_l32768", batch=8, seed=11,
+                                   context_lens=[1, 63, 64, 65, 2047, 2048, 2049, 5000], **kw)
+
+
+def test_indexer_scores_fp8_ragged():
+    wl = _ragged()
+    log("indexer fp8 ragged", wl.context_lens.tolist())
+    batch, d = upload(wl)
+    sc = dsa.indexer_scores(batch, d["idx_keys"], d["idx_scales"], d["q_idx"], d["w"])
+    torch.cuda.synchronize()
+    sc = sc.cpu().numpy()
+    for t, (r, p, n) in enumerate(wl.query_positions()):
+        ref = oracle.query_scores(wl, t)
+        np.testing.assert_allclose(sc[t, :n], ref, rtol=1e-5, atol=1e-5 * np.abs(ref).max())
+
+
+def test_indexer_scores_f32_tiny():
+    wl = workloads.make_workload("tiny_fp32_l4096")
+    batch, d = upload(wl)
+    sc = dsa.indexer_scores(batch, d["idx_keys"], None, d["q_idx"], d["w"]).cpu().numpy()
+    ref = oracle.query_scores(wl, 0)
+    np.testing.assert_allclose(sc[0, :4096], ref, rtol=1e-5, atol=1e-5 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("dup", [False, True])
+def test_topk_exact_on_identical_scores(dup):
+    """Both sides select from the same fp32 scores: the sets must be identical,
+    ties (duplicated values) included."""
+    rng = np.random.default_rng(5)
+    lens = [1, 100, 2048, 2049, 9000, 40000]
+    wl = workloads.make_workload("single_b1_l32768", batch=len(lens), context_lens=lens, seed=3)
+    batch, d = upload(wl)
+    ld = (max(lens) + 63) // 64 * 64
+    scores = np.full((len(lens), ld), np.nan, dtype=np.float32)
+    for t, n in enumerate(lens):
+        v = rng.standard_normal(n).astype(np.float32)
+        if dup:   # few distinct values -> massive ties around the threshold
+            v = np.round(v * 4).astype(np.float32) / 4
+        scores[t, :n] = v
+    idx = dsa.topk(batch, torch.from_numpy(scores).cuda(), 2048).cpu().numpy()
+    for t, n in enumerate(lens):
+        ref = oracle.topk(scores[t, :n].astype(np.float64), 2048)
+        m = min(n, 2048)
+        assert idx[t, :m].tolist() == sorted(ref.tolist())
+        assert (idx[t, m:] == -1).all()
+
+
+def test_topk_all_equal_takes_lowest_indices():
+    lens = [5000, 3000]
+    wl = workloads.make_workload("single_b1_l32768", batch=2, context_lens=lens, seed=3)
+    batch, _ = upload(wl)
+    scores = torch.zeros((2, 5056), dtype=torch.float32, device="cuda")
+    idx = dsa.topk(batch, scores, 2048).cpu().numpy()
+    assert idx[0].tolist() == list(range(2048))
+    assert idx[1].tolist() == list(range(2048))
+
+
+def test_mla_decode_on_oracle_selection():
+    wl = _ragged()
+    batch, d = upload(wl)
+    T = wl.total_q
+    sel = np.full((T, wl.topk), -1, dtype=np.int32)
+    for t in range(T):
+        s = oracle.topk(oracle.query_scores(wl, t), wl.topk)
+        sel[t, :len(s)] = np.sort(s)
+    lse = torch.empty((T, wl.mla_heads), dtype=torch.float32, device="cuda")
+    out = dsa.sparse_mla_decode(batch, d["kv"], None, wl.d_latent, d["q_mla"], torch.from_numpy(sel).cuda(),
+                                wl.softmax_scale, lse=lse)
+    out = out.float().cpu().numpy()
+    lse = lse.cpu().numpy()
+    for t in range(T):
+        s = sel[t][sel[t] >= 0]
+        ref, rlse = oracle.query_mla(wl, t, s)
+        check_out(out[t], ref, fp32=False)
+        np.testing.assert_allclose(lse[t], rlse, rtol=0, atol=1e-3)
+
+
+def test_mla_decode_unsorted_and_holey_indices():
+    """Indices in any order with -1 holes anywhere give the same result."""
+    wl = workloads.make_workload("single_b1_l32768", batch=1, context_lens=[3000], seed=4)
+    batch, d = upload(wl)
+    rng = np.random.default_rng(0)
+    s = rng.choice(3000, size=1500, replace=False).astype(np.int32)
+    sel = np.full((1, 2048), -1, dtype=np.int32)
+    pos = np.sort(rng.choice(2048, size=1500, replace=False))
+    sel[0, pos] = s
+    out = dsa.sparse_mla_decode(batch, d["kv"], None, 512, d["q_mla"], torch.from_numpy(sel).cuda(),
+                                wl.softmax_scale).float().cpu().numpy()
+    ref, _ = oracle.query_mla(wl, 0, s)
+    check_out(out[0], ref, fp32=False)
+
+
+@pytest.mark.parametrize("case", ["tiny_f32", "ragged_bf16", "mtp_fp8", "mtp_bf16", "peaked"])
+def test_decode_step(case):
+    if case == "tiny_f32":
+        wl = workloads.make_workload("tiny_fp32_l4096")
+    elif case == "ragged_bf16":
+        wl = _ragged()
+    elif case == "mtp_fp8":
+        wl = workloads.make_workload("mtp_b8_l202752", batch=3, context_lens=[2, 2049, 7001], seed=12)
+    elif case == "mtp_bf16":
+        wl = workloads.make_workload("mtp_b8_l202752", batch=3, context_lens=[2050, 130, 4099], seed=13,
+                                     kv_dtype="bf16")
+    else:
+        wl = workloads.make_workload("single_b1_l32768", batch=2, context_lens=[3000, 6000], seed=14)
+        # copy (scaled) a selected token's latent row into every head's query
+        rows = [int(np.sort(oracle.topk(oracle.query_scores(wl, t), wl.topk))[100 + 7 * t])
+                for t in range(wl.total_q)]
+        wl.q_mla = workloads.peaked_queries(wl, 1.0, rows)
+    log("decode_step", case, wl.context_lens.tolist(), "q_len", wl.q_lens.tolist())
+    batch, d = upload(wl)
+    out, lse, idx = gpu_step(wl, batch, d)
+    worst = check_step_rows(wl, list(range(wl.total_q)), out, lse, idx)
+    if case == "peaked":
+        assert np.abs(out).max() > 0.5      # outputs really are O(1)
+    log("  worst abs err", worst)
+
+
+def test_decode_step_zero_query_ties():
+    """All indexer scores tie at 0 -> the lowest K indices, bit-exact."""
+    wl = workloads.make_workload("single_b1_l32768", batch=2, context_lens=[4000, 2100], seed=15)
+    wl.q_idx[:] = 0
+    batch, d = upload(wl)
+    out, lse, idx = gpu_step(wl, batch, d)
+    assert idx[0].tolist() == list(range(2048))
+    assert idx[1].tolist() == list(range(2048))
+    check_step_rows(wl, [0, 1], out, lse, idx)
+
+
+def test_prefill_with_index_reuse():
+    """Chunked prefill: 96 new tokens after 3000 cached; top-K per query; the
+    second layer reuses the first layer's selection on its own cache."""
+    wl = workloads.make_workload("prefill_q4096_l131072", context_lens=[3096], q_len=96, seed=16)
+    batch, d = upload(wl)
+    T = wl.total_q
+    sc = dsa.indexer_scores(batch, d["idx_keys"], d["idx_scales"], d["q_idx"], d["w"])
+    idx = dsa.topk(batch, sc, wl.topk)
+    lse1 = torch.empty((T, wl.mla_heads), dtype=torch.float32, device="cuda")
+    out1 = dsa.sparse_mla_prefill(batch, d["kv"], None, 512, d["q_mla"], idx, wl.softmax_scale, lse=lse1)
+    out2 = dsa.sparse_mla_prefill(batch, d["kv2"], None, 512, d["q_mla2"], idx, wl.softmax_scale)
+    torch.cuda.synchronize()
+    sc, idx = sc.cpu().numpy(), idx.cpu().numpy()
+    out1, out2, lse1 = out1.float().cpu().numpy(), out2.float().cpu().numpy(), lse1.cpu().numpy()
+    rows = [0, 1, 47, 94, 95]
+    res = oracle.run_step(wl, rows=rows, layers=2)
+    for t in rows:
+        r = res[t]
+        np.testing.assert_allclose(sc[t, :len(r["scores"])], r["scores"], rtol=1e-5,
+                                   atol=1e-5 * np.abs(r["scores"]).max())
+        check_selection(idx[t], r["scores"], wl.topk)
+        sel = idx[t][idx[t] >= 0]
+        for layer, out in ((1, out1), (2, out2)):
+            ref, rl = oracle.query_mla(wl, t, sel, layer)
+            check_out(out[t], ref, fp32=False)
+        check_out(out1[t], r["out"], fp32=False)
+        check_out(out2[t], r["out2"], fp32=False)
+    # the decode entry point agrees with the prefill one on the same selection
+    out_dec = dsa.sparse_mla_decode(batch, d["kv"], None, 512, d["q_mla"], torch.from_numpy(idx).cuda(),
+                                    wl.softmax_scale).float().cpu().numpy()
+    np.testing.assert_allclose(out_dec, out1, rtol=0, atol=2e-2)
+
+
+def test_band_is_rarely_used():
+    """Selections differ from the oracle's only at genuine near-ties."""
+    wl = workloads.make_workload("single_b1_l32768", batch=4, context_lens=[9000, 12000, 3000, 20000], seed=17)
+    batch, d = upload(wl)
+    out, lse, idx = gpu_step(wl, batch, d, lse=False)
+    total = 0
+    for t in range(wl.total_q):
+        total += check_selection(idx[t], oracle.query_scores(wl, t), wl.topk, band=BAND)
+    assert total <= 4

@@ -303,3 +303,32 @@ def peaked_queries(wl: Workload, alpha: float, rows) -> np.ndarray:
             q[t, :, :] = alpha * rowf[None, :]
             t += 1
     return q if wl.kv_dtype == "f32" else bf16_bits(q)
+
+
+# ------------------------------------------------------------ device copy
+def _torch_of(a: np.ndarray, device):
+    """numpy storage codes -> torch tensor with the matching storage dtype."""
+    if a.dtype == np.uint16:    # bf16 bit patterns
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def to_device(wl: Workload, device="cuda") -> dict:
+    """Copy every array of a workload to `device` (storage dtypes kept)."""
+    d = dict(
+        context_lens=_torch_of(wl.context_lens, device),
+        query_start_loc=_torch_of(wl.query_start_loc, device),
+        page_table=_torch_of(wl.page_table, device),
+        idx_keys=_torch_of(wl.idx_keys, device),
+        idx_scales=None if wl.idx_scales is None else _torch_of(wl.idx_scales, device),
+        q_idx=_torch_of(wl.q_idx, device),
+        w=_torch_of(wl.w, device),
+        kv=_torch_of(wl.kv, device),
+        kv_scales=None if wl.kv_scales is None else _torch_of(wl.kv_scales, device),
+        q_mla=_torch_of(wl.q_mla, device),
+    )
+    if wl.layers >= 2:
+        d["kv2"] = _torch_of(wl.kv2, device)
+        d["kv2_scales"] = None if wl.kv2_scales is None else _torch_of(wl.kv2_scales, device)
+        d["q_mla2"] = _torch_of(wl.q_mla2, device)
+    return d
