@@ -38,13 +38,14 @@ Geometry geometry(const dsa_batch* b) {
 }
 
 // Workspace pieces (byte offsets from the base, each 256-aligned).
-struct TopkLayout { size_t hist, counters, cand, end; };
-TopkLayout topk_layout(size_t base, int T) {
+struct TopkLayout { size_t hist, counters, cand, above_list, end; };
+TopkLayout topk_layout(size_t base, int T, int k) {
     TopkLayout l;
     l.hist = base;
     l.counters = align_up(l.hist + sizeof(uint32_t) * (size_t)T * HIST_BINS);
     l.cand = align_up(l.counters + sizeof(TopkCounters) * (size_t)T);
-    l.end = align_up(l.cand + sizeof(int32_t) * (size_t)T * TOPK_CAND_CAP);
+    l.above_list = align_up(l.cand + sizeof(int32_t) * (size_t)T * TOPK_CAND_CAP);
+    l.end = align_up(l.above_list + sizeof(int32_t) * (size_t)T * k);
     return l;
 }
 
@@ -67,7 +68,7 @@ StepLayout step_layout(const dsa_batch* b, int k, int n_heads, bool fast_mla) {
     l.ld = round_up64(b->max_context_len);
     l.scores = 0;
     l.indices = align_up(sizeof(float) * (size_t)b->total_q * l.ld);
-    l.tk = topk_layout(align_up(l.indices + sizeof(int32_t) * (size_t)b->total_q * k), b->total_q);
+    l.tk = topk_layout(align_up(l.indices + sizeof(int32_t) * (size_t)b->total_q * k), b->total_q, k);
     l.ml = mla_layout(l.tk.end, b, k, n_heads, false, fast_mla);
     l.end = l.ml.end;
     return l;
@@ -186,7 +187,7 @@ size_t dsa_workspace_size(int32_t op, const dsa_batch* b, int32_t k, int32_t n_h
     switch (op) {
     case DSA_OP_TOPK:
         if (k < 1 || k > TOPK_MAX_K) return 0;
-        return topk_layout(0, b->total_q).end;
+        return topk_layout(0, b->total_q, k).end;
     case DSA_OP_MLA_DECODE:
     case DSA_OP_MLA_PREFILL:
         if (k < 1 || n_heads < 1) return 0;
@@ -219,7 +220,7 @@ int dsa_topk(const dsa_batch* b, const float* scores, int64_t ld, int32_t k, int
              void* ws, size_t ws_bytes, dsa_stream_t stream) {
     if (!batch_ok(b) || !scores || !indices || k < 1 || ld < b->max_context_len) return DSA_ERR_INVALID_ARG;
     if (k > TOPK_MAX_K) return DSA_ERR_UNSUPPORTED;
-    const TopkLayout l = topk_layout(0, b->total_q);
+    const TopkLayout l = topk_layout(0, b->total_q, k);
     if (!ws || ws_bytes < l.end) return DSA_ERR_WORKSPACE;
     int st = check_device_cached();
     if (st != DSA_OK) return st;
@@ -231,6 +232,7 @@ int dsa_topk(const dsa_batch* b, const float* scores, int64_t ld, int32_t k, int
     a.hist = (uint32_t*)(base + l.hist);
     a.counters = (TopkCounters*)(base + l.counters);
     a.cand = (int32_t*)(base + l.cand);
+    a.above_list = (int32_t*)(base + l.above_list);
     hipError_t e = launch_zero_u32(a.hist, (l.cand - l.hist) / sizeof(uint32_t), s);
     if (e == hipSuccess) e = launch_topk_hist(a, s);
     if (e == hipSuccess) e = launch_topk_select(a, s);
@@ -284,6 +286,7 @@ int dsa_decode_step(const dsa_batch* b, const dsa_index_cache* ic, const void* q
     tk.hist = (uint32_t*)(base + l.tk.hist);
     tk.counters = (TopkCounters*)(base + l.tk.counters);
     tk.cand = (int32_t*)(base + l.tk.cand);
+    tk.above_list = (int32_t*)(base + l.tk.above_list);
     hipError_t e = launch_zero_u32(tk.hist, (l.tk.cand - l.tk.hist) / sizeof(uint32_t), s);
 
     IndexerArgs ia;

@@ -27,10 +27,10 @@ constexpr int TOPK_MAX_K = 4096;
 
 // Per-row top-K bookkeeping in the workspace.
 struct TopkCounters {
-    uint32_t above;      // tokens in buckets above the threshold bucket
-    uint32_t cand;       // tokens in the threshold bucket
-    uint32_t bucket;     // threshold bucket
-    uint32_t pad;
+    uint32_t above;           // tokens appended above the threshold bucket
+    uint32_t cand;            // tokens appended from the threshold bucket
+    uint32_t bucket;          // threshold bucket
+    uint32_t above_expected;  // histogram count above the threshold bucket
 };
 
 // ----------------------------------------------------------- conversions
@@ -122,7 +122,8 @@ struct TopkArgs {
     Geometry g;
     const float* scores; int64_t ld;
     int k;
-    int32_t* indices;        // [T][k]
+    int32_t* indices;        // [T][k] result
+    int32_t* above_list;     // [T][k] tokens above the threshold bucket
     uint32_t* hist;          // [T][HIST_BINS]
     TopkCounters* counters;  // [T]
     int32_t* cand;           // [T][TOPK_CAND_CAP]

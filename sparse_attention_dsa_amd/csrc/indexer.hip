@@ -63,6 +63,36 @@ __device__ __forceinline__ float head_sum_transpose(const float part[4], int lan
     return keep + __shfl_xor(send, 16);
 }
 
+// Scores of one 64-token page for the NQ query rows: 16 MFMAs per row (heads x
+// tokens x full key), ReLU, head weights, head sum across the lane groups, key
+// scale.  Lane l returns the score of token l of the page.
+template <int NQ, int HT>
+__device__ __forceinline__ void page_scores(const i32x8 (&qf)[NQ][HT], const float (&wv)[NQ][HT][4],
+                                            const i32x8 (&kf)[4], float ksc, int lane, int nq,
+                                            float (&out)[NQ]) {
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+        if (j < nq) {
+            float part[4];
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                float acc = 0.f;
+#pragma unroll
+                for (int ht = 0; ht < HT; ++ht) {
+                    const f32x4 c = mfma_fp8_16x16x128(qf[j][ht], kf[nt], zero);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc += wv[j][ht][i] * fmaxf(c[i], 0.f);
+                }
+                part[nt] = acc;
+            }
+            out[j] = head_sum_transpose(part, lane) * ksc;
+        } else {
+            out[j] = 0.f;
+        }
+    }
+}
+
 template <int NQ, int HT, bool HIST>
 __global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_mfma(IndexerArgs a, int qgroups,
                                                                 int chunk_tokens) {
@@ -108,29 +138,18 @@ __global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_mfma(IndexerArgs a, i
     int pg = tok0 / IDX_PAGE + wave;
     KeyPage cur;
     if (pg < page1) load_key_page(keys, a.key_scales, pt[pg], lane, cur);
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
     for (; pg < page1; pg += 4) {
         KeyPage nxt;
         const bool more = pg + 4 < page1;
         if (more) load_key_page(keys, a.key_scales, pt[pg + 4], lane, nxt);
         const int pos = pg * IDX_PAGE + lane;
+        float ps[NQ];
+        page_scores<NQ, HT>(qf, wv, cur.frag, cur.scale, lane, nq, ps);
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
             if (j < nq) {
-                float part[4];
-#pragma unroll
-                for (int nt = 0; nt < 4; ++nt) {
-                    float acc = 0.f;
-#pragma unroll
-                    for (int ht = 0; ht < HT; ++ht) {
-                        const f32x4 c = mfma_fp8_16x16x128(qf[j][ht], cur.frag[nt], zero);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) acc += wv[j][ht][i] * fmaxf(c[i], 0.f);
-                    }
-                    part[nt] = acc;
-                }
-                const float s = head_sum_transpose(part, lane) * cur.scale;
+                const float s = ps[j];
                 const int t = qs + j0 + j;
                 const int n_j = L - ql + j0 + j + 1;
                 if (pos < n_j) {
@@ -150,6 +169,173 @@ __global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_mfma(IndexerArgs a, i
                 const uint32_t v = hist[j][b];
                 if (v) atomicAdd(gh + b, v);
             }
+        }
+    }
+}
+
+
+// ---------------------------------------------------------------------------
+// LDS-ring variant: each wave streams its pages through a private ring of
+// DMA_DEPTH page slots in LDS with global_load_lds_dwordx4 (one fully
+// coalesced 1 KB transfer per instruction, no registers held while in flight).
+// Within a page slot the 16-byte units of token t are XOR-permuted by
+// page_swz(t) so that the MFMA fragment reads of 16 tokens hit distinct banks.
+// Scores stay in registers until the wave's pages are done: global stores in
+// the loop would share the vector-memory counter the ring waits on.
+#ifndef IDX_DMA_DEPTH
+#define IDX_DMA_DEPTH 2
+#endif
+#ifndef IDX_DMA_PPW
+#define IDX_DMA_PPW 4
+#endif
+constexpr int DMA_DEPTH = IDX_DMA_DEPTH;     // pages in flight per wave
+constexpr int DMA_PPW = IDX_DMA_PPW;         // pages per wave per workgroup
+constexpr int DMA_OPS_PER_PAGE = 9;          // 8 x 1 KB of keys + 256 B of scales
+
+__device__ __forceinline__ int page_swz(int t) { return (t ^ (t >> 3)) & 7; }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    else if constexpr (N == 18) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    else if constexpr (N == 27) asm volatile("s_waitcnt vmcnt(27)" ::: "memory");
+    else static_assert(N == 0, "unsupported vmcnt");
+}
+
+template <int NQ, int HT, bool HIST>
+__global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_dma(IndexerArgs a, int qgroups) {
+    const Geometry& G = a.g;
+    const int r = blockIdx.y / qgroups, qg = blockIdx.y % qgroups;
+    const int L = G.ctx[r];
+    const int qs = G.qsl[r], ql = G.qsl[r + 1] - qs;
+    const int j0 = qg * NQ;
+    if (j0 >= ql) return;
+    const int nq = min(NQ, ql - j0);
+    const int n_last = L - ql + j0 + nq;
+    constexpr int CHUNK = 4 * DMA_PPW * IDX_PAGE;
+    const int tok0 = blockIdx.x * CHUNK;
+    if (tok0 >= n_last) return;
+    const int tok1 = min(n_last, tok0 + CHUNK);
+
+    __shared__ __attribute__((aligned(16))) uint8_t kbuf[4][DMA_DEPTH][IDX_PAGE * IDX_D];
+    __shared__ __attribute__((aligned(16))) float sbuf[4][DMA_DEPTH][IDX_PAGE];
+    __shared__ uint32_t hist[HIST ? NQ : 1][HIST ? HIST_BINS / 2 : 1];   // two 16-bit counts per word
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave index in a scalar register: page ids then come from scalar loads,
+    // which do not touch the vector-memory counter the ring waits on
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, col = lane & 15;
+    if constexpr (HIST)
+        for (int i = tid; i < NQ * HIST_BINS / 2; i += IDX_THREADS) (&hist[0][0])[i] = 0u;
+
+    const int32_t* pt = G.page_table + (size_t)r * G.max_blocks;
+    const uint8_t* keys = (const uint8_t*)a.keys;
+    const bool has_scale = a.key_scales != nullptr;
+    const int pfirst = tok0 / IDX_PAGE + wave;               // wave's page i is pfirst + 4 i
+    const int page1 = (tok1 + IDX_PAGE - 1) / IDX_PAGE;
+    const int npw = pfirst < page1 ? min(DMA_PPW, (page1 - pfirst + 3) / 4) : 0;
+
+    // physical blocks of the wave's pages, read before the ring starts
+    int blks[DMA_PPW];
+#pragma unroll
+    for (int i = 0; i < DMA_PPW; ++i) blks[i] = i < npw ? __builtin_amdgcn_readfirstlane(pt[pfirst + 4 * i]) : 0;
+    auto issue = [&](int i) {   // DMA page i of this wave into ring slot i % DMA_DEPTH
+        const int blk = blks[i];
+        const uint8_t* src = keys + (size_t)blk * (IDX_PAGE * IDX_D);
+        uint8_t* dst = &kbuf[wave][i % DMA_DEPTH][0];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int U = 64 * c + lane, t = U >> 3, u = (U & 7) ^ page_swz(t);
+            __builtin_amdgcn_global_load_lds((const void*)(src + t * IDX_D + 16 * u), (lds_ptr_t)(dst + 1024 * c),
+                                             16, 0, 0);
+        }
+        const void* ssrc = has_scale ? (const void*)(a.key_scales + (size_t)blk * IDX_PAGE + lane)
+                                     : (const void*)(src + 4 * lane);
+        __builtin_amdgcn_global_load_lds(ssrc, (lds_ptr_t)&sbuf[wave][i % DMA_DEPTH][0], 4, 0, 0);
+    };
+#pragma unroll
+    for (int d = 0; d < DMA_DEPTH; ++d)
+        if (d < npw) issue(d);
+
+    i32x8 qf[NQ][HT];
+    float wv[NQ][HT][4];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+        const int t = qs + j0 + min(j, nq - 1);
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            const uint8_t* qp = (const uint8_t*)a.q + ((size_t)t * a.n_heads + 16 * ht + col) * IDX_D + 16 * g;
+            qf[j][ht] = join_i32x8(*(const u32x4*)qp, *(const u32x4*)(qp + 64));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wv[j][ht][i] = a.w[(size_t)t * a.n_heads + 16 * ht + 4 * g + i];
+        }
+    }
+    if constexpr (HIST) __syncthreads();
+
+    float sc[NQ][DMA_PPW];
+#pragma unroll
+    for (int i = 0; i < DMA_PPW; ++i) {
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) sc[j][i] = 0.f;
+        if (i < npw) {
+            // page i has landed once at most the younger pages' transfers are pending
+            if (i + DMA_DEPTH - 1 < npw) wait_vmcnt<DMA_OPS_PER_PAGE * (DMA_DEPTH - 1)>();
+            else wait_vmcnt<0>();
+            const uint8_t* pb = &kbuf[wave][i % DMA_DEPTH][0];
+            i32x8 kf[4];
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const int t = 16 * nt + col;
+                const u32x4 lo = *(const u32x4*)(pb + t * IDX_D + 16 * (g ^ page_swz(t)));
+                const u32x4 hi = *(const u32x4*)(pb + t * IDX_D + 16 * ((4 + g) ^ page_swz(t)));
+                kf[nt] = join_i32x8(lo, hi);
+            }
+            const float ksc = has_scale ? sbuf[wave][i % DMA_DEPTH][lane] : 1.f;
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // slot read before it is refilled
+            if (i + DMA_DEPTH < npw) issue(i + DMA_DEPTH);
+            float ps[NQ];
+            page_scores<NQ, HT>(qf, wv, kf, ksc, lane, nq, ps);
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) sc[j][i] = ps[j];
+        }
+    }
+    // Stores and histogram counts after the ring has drained (LDS atomics
+    // issued while transfers are pending would make the compiler wait on them).
+    // (histogram first: its barrier then has no stores to wait for)
+    if constexpr (HIST) {
+#pragma unroll
+        for (int i = 0; i < DMA_PPW; ++i) {
+            const int pos = (pfirst + 4 * i) * IDX_PAGE + lane;
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) {
+                const int n_j = L - ql + j0 + j + 1;
+                if (i < npw && j < nq && pos < n_j) {
+                    const uint32_t b = score_key(sc[j][i]) >> HIST_SHIFT;
+                    atomicAdd(&hist[j][b >> 1], 1u << (16 * (b & 1)));
+                }
+            }
+        }
+        __syncthreads();
+        for (int j = 0; j < nq; ++j) {
+            uint32_t* gh = a.hist + (size_t)(qs + j0 + j) * HIST_BINS;
+            for (int w = tid; w < HIST_BINS / 2; w += IDX_THREADS) {
+                const uint32_t v = hist[j][w];
+                if (v & 0xFFFFu) atomicAdd(gh + 2 * w, v & 0xFFFFu);
+                if (v >> 16) atomicAdd(gh + 2 * w + 1, v >> 16);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < DMA_PPW; ++i) {
+        const int pos = (pfirst + 4 * i) * IDX_PAGE + lane;
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            const int n_j = L - ql + j0 + j + 1;
+            if (i < npw && j < nq && pos < n_j) a.scores[(size_t)(qs + j0 + j) * a.ld + pos] = sc[j][i];
         }
     }
 }
@@ -192,9 +378,22 @@ __global__ __launch_bounds__(256) void indexer_generic(IndexerArgs a) {
     if (a.hist) atomicAdd(a.hist + (size_t)t * HIST_BINS + (score_key(score) >> HIST_SHIFT), 1u);
 }
 
+#ifndef IDX_USE_DMA
+#define IDX_USE_DMA 1
+#endif
+
 template <int NQ, int HT>
 static hipError_t launch_fp8(const IndexerArgs& a, hipStream_t s) {
     const int qgroups = (a.g.max_q_len + NQ - 1) / NQ;
+    if (IDX_USE_DMA) {
+        const int chunk = 4 * DMA_PPW * IDX_PAGE;
+        dim3 grid((a.g.max_ctx + chunk - 1) / chunk, a.g.B * qgroups);
+        if (a.hist)
+            hipLaunchKernelGGL((indexer_fp8_dma<NQ, HT, true>), grid, dim3(IDX_THREADS), 0, s, a, qgroups);
+        else
+            hipLaunchKernelGGL((indexer_fp8_dma<NQ, HT, false>), grid, dim3(IDX_THREADS), 0, s, a, qgroups);
+        return hipGetLastError();
+    }
     const int chunk_tokens = IDX_CHUNK_PAGES * IDX_PAGE;
     dim3 grid((a.g.max_ctx + chunk_tokens - 1) / chunk_tokens, a.g.B * qgroups);
     if (a.hist)

@@ -5,66 +5,71 @@
 // selected tokens s_j, out[t,h,:] = softmax(z) . kv[s_j, 0:d]; K and V are the
 // same cached latent row, V being its first d columns.
 //
-// Fast path (d = 512, r = 64, 64-token blocks, bf16 or e4m3 latent, heads a
-// multiple of 64): a workgroup owns one query row, 64 heads (16 per wave) and
-// a contiguous slice of the row's selection.  Tiles of 32 selected tokens are
-// gathered through the page table into LDS twice:
-//   Ks  [32][576+8]  row-major, the A operand of S^T = K Q^T (k = latent dim);
-//   Vt  [512][32]    transposed with an XOR swizzle, the A operand of
-//                    O^T = V^T P^T (k = token).  The 8x8 bf16 transposes are
-//                    done in registers between the global loads and the
-//                    LDS stores.
-// Queries stay in registers as the B operand of the logit MFMAs.  Computing
-// S^T rather than S leaves each lane with one head and eight tokens, which is
-// exactly the B-operand layout P^T needs for the PV MFMAs (the token order
-// inside a 32-token step is permuted consistently on both sides), so the
-// probabilities never leave registers.  Online softmax in the exp2 domain;
-// each lane's O^T accumulators all belong to its own head, so the running
-// rescale is a per-lane scalar.  Decode rows split their selection across
-// workgroups and a second kernel merges the partial results by their
-// log-sum-exp; prefill rows have enough parallelism without splitting.
+// Fast path (d = 512, r = 64, bf16 or e4m3 latent, heads a multiple of 64): a
+// workgroup owns one query row, 64 heads (16 per wave) and a contiguous slice
+// of the row's selection, processed in tiles of 32 selected tokens.  A tile's
+// latent rows are gathered through the page table into one row-major LDS
+// buffer (1152 B per row; the 16-byte units of row r are XOR-permuted by
+// ks_swz(r) so that fragment reads of 16 rows hit distinct banks):
+//   * bf16 latent: async global_load_lds_dwordx4 transfers (one fully
+//     coalesced 1 KB segment per instruction) into a double buffer -- tile
+//     i+1 is in flight while tile i is computed, without holding registers;
+//   * e4m3 latent: register loads widened exactly to bf16 (e4m3 values are
+//     bf16-representable), the per-token scale applied to logits and
+//     probabilities.
+// Logits S^T = K Q^T use the LDS rows as the A operand (k = latent dim) and
+// register-resident queries as the B operand.  S^T's accumulator layout is
+// exactly the B-operand layout P^T needs for O^T = V^T P^T (token order inside
+// a 32-token step permuted consistently on both sides), so probabilities never
+// leave registers.  The V^T operand is read from the same row-major buffer
+// with ds_read_b64_tr_b16, which transposes 16-bit elements across each
+// 16-lane group.  Each lane's O^T accumulators belong to one head, so the
+// online-softmax rescale is a per-lane scalar.  Decode rows split their
+// selection across workgroups and a second kernel merges the partial results
+// by their log-sum-exp; prefill rows have enough parallelism without it.
 #include "dsa_kernels.h"
 
 namespace dsa {
 
 constexpr int M_DL = 512, M_DR = 64, M_DQK = M_DL + M_DR;
 constexpr int M_TILE = 32;                 // selected tokens per tile
-constexpr int M_KS_STRIDE = M_DQK + 8;     // bf16 elements per Ks row (16 B pad)
+constexpr int M_ROW_BYTES = 2 * M_DQK;     // 1152: one bf16 row in LDS
+constexpr int M_ROW_UNITS = M_ROW_BYTES / 16;
+constexpr int M_TILE_BYTES = M_TILE * M_ROW_BYTES;
 constexpr int M_THREADS = 256;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
-// Slot order inside a 32-token tile: B-operand slot 8g + j of P^T holds the
-// logit of token pi(g, j), where lane group g got tokens 4g..4g+3 from the
-// first 16-token logit tile and 16+4g..16+4g+3 from the second.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_vptr;
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+
+// Slot order inside a 32-token tile: k-slot 8g + j of lane group g holds token
+// slot_token(g, j); lane group g's logit accumulators hold tokens 4g..4g+3 of
+// the first 16-token half and 16+4g..16+4g+3 of the second.
 __device__ __forceinline__ int slot_token(int g, int j) {
     return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);
 }
 
-// 16-byte unit of row c of Vt that holds slot group g (XOR swizzle keeps the
-// reads of 8 or 16 consecutive rows on distinct bank groups).
-__device__ __forceinline__ int vt_unit(int c, int g) {
-    return g ^ (((c >> 1) ^ (c >> 2)) & 3);
-}
+// XOR permutation of the 16-byte units inside row r (within aligned groups of
+// 8 units; 72 units per row).
+__device__ __forceinline__ int ks_swz(int r) { return (r ^ (r >> 3)) & 7; }
 
-// Loads 8 latent columns [8*c8, 8*c8+8) of a cache row as 8 bf16 (16 bytes).
-template <bool FP8>
-__device__ __forceinline__ u32x4 load_cols8(const void* kv, const float* scales, int row, int c8) {
-    if (!FP8) {
-        return *(const u32x4*)((const uint16_t*)kv + (size_t)row * M_DQK + 8 * c8);
-    } else {
-        const u32x2 v = *(const u32x2*)((const uint8_t*)kv + (size_t)row * M_DQK + 8 * c8);
-        const float sc = scales[row];
-        u32x4 o;
+// Byte offset in a tile buffer of logical 16-byte unit u of row r.
+__device__ __forceinline__ int ks_off(int r, int u) { return r * M_ROW_BYTES + 16 * (u ^ ks_swz(r)); }
+
+// 8 latent columns [8u, 8u+8) of an e4m3 cache row widened exactly to bf16.
+__device__ __forceinline__ u32x4 load_e4m3_unit(const uint8_t* kv, int row, int u) {
+    const u32x2 v = *(const u32x2*)(kv + (size_t)row * M_DQK + 8 * u);
+    u32x4 o;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t w = v[i >> 1] >> (16 * (i & 1));
-            const float x0 = e4m3_to_f32(w & 0xFFu) * sc;
-            const float x1 = e4m3_to_f32((w >> 8) & 0xFFu) * sc;
-            o[i] = f32_to_bf16(x0) | (f32_to_bf16(x1) << 16);
-        }
-        return o;
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t w = v[i >> 1] >> (16 * (i & 1));
+        const uint32_t b0 = __float_as_uint(e4m3_to_f32(w & 0xFFu)) >> 16;
+        const uint32_t b1 = __float_as_uint(e4m3_to_f32((w >> 8) & 0xFFu)) >> 16;
+        o[i] = b0 | (b1 << 16);
     }
+    return o;
 }
 
 template <bool FP8, bool SPLIT>
@@ -78,23 +83,59 @@ void mla_bf16_mfma(MlaArgs a, int slice) {
     const int j_begin = sp * slice;
     const int j_end = min(a.k, j_begin + slice);
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[M_TILE * M_KS_STRIDE];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[M_DL * M_TILE];
-    __shared__ int32_t rows[2][M_TILE];   // physical rows of the current / next tile (-1: none)
+    // double buffer; each unrolled half names its buffer with a constant index,
+    // so the compiler can tell the buffer being read from the one an
+    // asynchronous transfer is filling (and folds the choice into offsets)
+    __shared__ __attribute__((aligned(16))) uint8_t Ks[FP8 ? 1 : 2][M_TILE_BYTES];
+    __shared__ int32_t rows[3][M_TILE];          // physical rows of tiles i, i+1, i+2 (-1: none)
+    __shared__ float tscale[FP8 ? 3 : 1][M_TILE];  // e4m3 per-token scales of those rows
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, col = lane & 15;
     const int head = hg * MLA_HEADS_PER_WG + wave * 16 + col;
 
     const int32_t* sel = a.indices + (size_t)t * a.k;
     const int32_t* pt = G.page_table + (size_t)r * G.max_blocks;
     const int nslots = max(0, j_end - j_begin);
-    auto row_of = [&](int j) -> int32_t {     // slot j of the slice
-        if (j >= nslots) return -1;
-        const int s = sel[j_begin + j];
-        return s < 0 ? -1 : pt[s / G.block_size] * G.block_size + s % G.block_size;
+    const int ntiles = (nslots + M_TILE - 1) / M_TILE;
+    auto stage_rows = [&](int b, int tile) {     // threads < M_TILE: row ids (+ scales) of a tile
+        const int j = tile * M_TILE + tid;
+        int row = -1;
+        if (j < nslots) {
+            const int s = sel[j_begin + j];
+            if (s >= 0) row = pt[s / G.block_size] * G.block_size + s % G.block_size;
+        }
+        rows[b][tid] = row;
+        if constexpr (FP8) tscale[b][tid] = row >= 0 ? a.kv_scales[row] : 0.f;
     };
-    if (tid < M_TILE) rows[0][tid] = row_of(tid);
+    // bf16: one tile's rows into a buffer, 9 coalesced 1 KB transfers per wave
+    auto issue = [&](uint8_t* dst, const int32_t* trow) {
+        // recomputed per tile on purpose: hoisting these offsets out of the tile
+        // loop costs more registers than the few instructions that make them
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+#pragma unroll
+        for (int i = 0; i < M_TILE_BYTES / 16 / M_THREADS; ++i) {
+            const int U = (wave * (M_TILE_BYTES / 16 / M_THREADS) + i) * 64 + ln;   // LDS unit
+            const int rr = U / M_ROW_UNITS, pu = U % M_ROW_UNITS;
+            const int u = pu ^ ks_swz(rr);                                       // logical unit
+            const int row = trow[rr];
+            const uint8_t* src = (const uint8_t*)a.kv + (size_t)(row < 0 ? 0 : row) * M_ROW_BYTES + 16 * u;
+            __builtin_amdgcn_global_load_lds((const void*)src,
+                                             (lds_vptr)(dst + 1024 * (wave * (M_TILE_BYTES / 16 / M_THREADS) + i)),
+                                             16, 0, 0);
+        }
+    };
+    // e4m3: one tile's rows widened to bf16 into the single buffer (synchronous)
+    auto gather_fp8 = [&](const int32_t* trow) {
+        for (int U = tid; U < M_TILE * M_ROW_UNITS; U += M_THREADS) {
+            const int rr = U / M_ROW_UNITS, u = U % M_ROW_UNITS;
+            const int row = trow[rr];
+            const u32x4 v = row >= 0 ? load_e4m3_unit((const uint8_t*)a.kv, row, u) : (u32x4){0u, 0u, 0u, 0u};
+            *(u32x4*)(&Ks[0][0] + ks_off(rr, u)) = v;
+        }
+    };
 
     // Queries: B operand of S^T = K Q^T, one 16-byte fragment per 32-wide k step.
     u32x4 qf[M_DQK / 32];
@@ -108,74 +149,60 @@ void mla_bf16_mfma(MlaArgs a, int slice) {
     for (int ct = 0; ct < M_DL / 16; ++ct) oacc[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
     const float zscale = a.scale * LOG2E;
-    __syncthreads();
 
-    // Gather roles: V part -> token group gv (slots 8gv..8gv+7), column chunk cv.
-    const int gv = tid & 3, cv = tid >> 2;             // cv in [0, 64)
-    const int rope_tok = tid >> 3, rope_c8 = 64 + (tid & 7);
-
-    for (int j0 = 0, buf = 0; j0 < nslots; j0 += M_TILE, buf ^= 1) {
-        const int32_t* trow = rows[buf];
-        // ---- gather tile into LDS, four tokens of the slot group at a time
+    // Per-lane LDS offsets.  XOR-ing a unit index with ks_swz(r) < 8 only
+    // touches its low 3 bits, so every fragment read is one of a few per-lane
+    // bases plus a compile-time immediate (128 B per 8 units).
+    int qk_base[2][2];                   // [token half][k-step parity]
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            u32x4 v[4];
+    for (int tt = 0; tt < 2; ++tt) {
+        const int rr = 16 * tt + col;
+        qk_base[tt][0] = rr * M_ROW_BYTES + 16 * (g ^ ks_swz(rr));
+        qk_base[tt][1] = rr * M_ROW_BYTES + 16 * ((4 + g) ^ ks_swz(rr));
+    }
+    // V^T fragments by transposing reads: source lane s of a 16-lane group
+    // points at token slot_token(g, s/4 + 4h), columns c0+4(s%4)..+3; this lane
+    // then receives 4 tokens of column c0 + col.
+    int pv_base[2][4];                   // [h][column-tile mod 4]
+    {
+        const int cq = 4 * (col & 3);
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int row = trow[slot_token(gv, 4 * half + jj)];
-                v[jj] = row >= 0 ? load_cols8<FP8>(a.kv, a.kv_scales, row, cv) : (u32x4){0u, 0u, 0u, 0u};
-            }
+        for (int h = 0; h < 2; ++h) {
+            const int tok = slot_token(g, (col >> 2) + 4 * h);
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                *(u32x4*)(Ks + slot_token(gv, 4 * half + jj) * M_KS_STRIDE + 8 * cv) = v[jj];
-            // 4x8 transpose: column cc of the chunk, these four slots in order.
-#pragma unroll
-            for (int cc = 0; cc < 8; ++cc) {
-                const int sh = 16 * (cc & 1), w = cc >> 1;
-                u32x2 o;
-#pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    const uint32_t lo = (v[2 * m][w] >> sh) & 0xFFFFu;
-                    const uint32_t hi = (v[2 * m + 1][w] >> sh) & 0xFFFFu;
-                    o[m] = lo | (hi << 16);
-                }
-                const int c = 8 * cv + cc;
-                *(u32x2*)(Vt + c * M_TILE + 8 * vt_unit(c, gv) + 4 * half) = o;
-            }
+            for (int m = 0; m < 4; ++m)
+                pv_base[h][m] = tok * M_ROW_BYTES + 16 * ((2 * m + (cq >> 3)) ^ ks_swz(tok)) + 2 * (cq & 7);
         }
-        {
-            const int rrow = trow[rope_tok];
-            const u32x4 vr = rrow >= 0 ? load_cols8<FP8>(a.kv, a.kv_scales, rrow, rope_c8)
-                                       : (u32x4){0u, 0u, 0u, 0u};
-            *(u32x4*)(Ks + rope_tok * M_KS_STRIDE + 8 * rope_c8) = vr;
-        }
-        __syncthreads();
+    }
 
-        // ---- logits S^T for two 16-token halves: lane holds tokens 16tt+4g+i of head `col`
+    // One tile from an LDS buffer: logits and online softmax (returns the
+    // bf16 probabilities in the P^T operand layout), then PV.
+    auto logits_softmax = [&](const uint8_t* Kb, int slot) -> bf16x8 {
+        const int32_t* trow = rows[slot];
         float x[2][4];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             f32x4 s = {0.f, 0.f, 0.f, 0.f};
-            const uint16_t* kp = Ks + (16 * tt + col) * M_KS_STRIDE + 8 * g;
 #pragma unroll
-            for (int ks = 0; ks < M_DQK / 32; ++ks)
-                s = mfma_bf16_16x16x32(as_bf16x8(*(const u32x4*)(kp + 32 * ks)), as_bf16x8(qf[ks]), s);
+            for (int ks = 0; ks < M_DQK / 32; ++ks) {
+                const u32x4 kfrag = *(const u32x4*)(Kb + qk_base[tt][ks & 1] + 128 * (ks >> 1));
+                s = mfma_bf16_16x16x32(as_bf16x8(kfrag), as_bf16x8(qf[ks]), s);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int tok = 16 * tt + 4 * g + i;
-                const bool ok = trow[tok] >= 0;
-                x[tt][i] = ok ? s[i] * zscale : -INFINITY;
+                float zs = zscale;
+                if constexpr (FP8) zs *= tscale[slot][tok];
+                x[tt][i] = trow[tok] >= 0 ? s[i] * zs : -INFINITY;
             }
         }
-        // ---- online softmax (per head = per lane column; reduce over the 4 lane groups)
         float tmax = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
                            fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
         const float m_new = fmaxf(m_run, tmax);
         float p[2][4];
-        float psum = 0.f;
-        float alpha = 1.f;
+        float psum = 0.f, alpha = 1.f;
         if (m_new != -INFINITY) {
             alpha = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
@@ -199,22 +226,74 @@ void mla_bf16_mfma(MlaArgs a, int slice) {
 #pragma unroll
             for (int ct = 0; ct < M_DL / 16; ++ct) oacc[ct] *= alpha;
         }
+        if constexpr (FP8) {   // V rows are unscaled codes: fold each token's scale into p
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) p[tt][i] *= tscale[slot][16 * tt + 4 * g + i];
+        }
         u32x4 pb;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int tt = m >> 1, i = 2 * (m & 1);
             pb[m] = f32_to_bf16(p[tt][i]) | (f32_to_bf16(p[tt][i + 1]) << 16);
         }
-        // ---- O^T += V^T P^T
-        const bf16x8 pbf = as_bf16x8(pb);
+        return as_bf16x8(pb);
+    };
+    auto pv = [&](const uint8_t* Kb, bf16x8 pbf) {
 #pragma unroll
         for (int ct = 0; ct < M_DL / 16; ++ct) {
-            const int c = 16 * ct + col;
-            const u32x4 va = *(const u32x4*)(Vt + c * M_TILE + 8 * vt_unit(c, g));
+            const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4_ptr)(Kb + pv_base[0][ct & 3] + 128 * (ct >> 2)));
+            const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4_ptr)(Kb + pv_base[1][ct & 3] + 128 * (ct >> 2)));
+            u32x4 va;
+            va[0] = (uint16_t)v0[0] | ((uint32_t)(uint16_t)v0[1] << 16);
+            va[1] = (uint16_t)v0[2] | ((uint32_t)(uint16_t)v0[3] << 16);
+            va[2] = (uint16_t)v1[0] | ((uint32_t)(uint16_t)v1[1] << 16);
+            va[3] = (uint16_t)v1[2] | ((uint32_t)(uint16_t)v1[3] << 16);
             oacc[ct] = mfma_bf16_16x16x32(as_bf16x8(va), pbf, oacc[ct]);
         }
-        if (tid < M_TILE) rows[buf ^ 1][tid] = row_of(j0 + M_TILE + tid);
-        __syncthreads();
+    };
+
+    if (tid < M_TILE) {
+        stage_rows(0, 0);
+        stage_rows(1, 1);
+    }
+    __syncthreads();
+    if constexpr (!FP8) {
+        // Row ids are staged by wave 0 two tiles ahead with a two-tile chain
+        // (the index of tile i+3 and the page-table entry of tile i+2 are
+        // loaded at the top of tile i, the row id written at its end), so no
+        // staging load is waited for while a tile's transfers are in flight.
+        const bool stager = tid < M_TILE;
+        auto sel_of = [&](int tile) { const int j = tile * M_TILE + tid; return j < nslots ? sel[j_begin + j] : -1; };
+        int sidx_q = stager ? sel_of(2) : -1;    // index for tile i+2
+        if (ntiles > 0) issue(&Ks[0][0], rows[0]);
+        for (int i = 0; i < ntiles; ++i) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();                       // tile i landed; the other buffer is free
+            int blk = 0, sidx_n = -1;
+            if (stager) {
+                if (sidx_q >= 0) blk = pt[sidx_q / G.block_size];
+                sidx_n = sel_of(i + 3);
+            }
+            if (i + 1 < ntiles) issue(&Ks[((i + 1) & 1) % (FP8 ? 1 : 2)][0], rows[(i + 1) % 3]);
+            const uint8_t* cur = &Ks[(i & 1) % (FP8 ? 1 : 2)][0];
+            pv(cur, logits_softmax(cur, i % 3));
+            if (stager) {
+                rows[(i + 2) % 3][tid] = sidx_q < 0 ? -1 : blk * G.block_size + sidx_q % G.block_size;
+                sidx_q = sidx_n;
+            }
+        }
+    } else {
+        for (int i = 0; i < ntiles; ++i) {
+            gather_fp8(rows[i % 3]);
+            __syncthreads();
+            if (tid < M_TILE) stage_rows((i + 2) % 3, i + 2);
+            pv(&Ks[0][0], logits_softmax(&Ks[0][0], i % 3));
+            __syncthreads();
+        }
     }
 
     // ---- epilogue: lane holds O^T[c = 16ct + 4g + i][head]

@@ -4,27 +4,34 @@
 // highest-scoring visible tokens, or every visible token when a query sees K
 // or fewer; equal scores go to the lower token index.
 //
-// Each score maps to an order-preserving 32-bit key.  Selection runs in three
-// kernels per query row:
-//   hist   (only when the indexer did not already build it) counts keys per
-//          bucket of their top 12 bits into a per-row histogram;
-//   filter each workgroup re-derives the threshold bucket b* from the
-//          histogram (the bucket holding the K-th largest key), then streams
-//          its chunk of the row: tokens above b* are selected outright and
-//          tokens in b* are appended to a candidate list; appends are
-//          aggregated per wavefront (one atomic per wave);
-//   refine one workgroup per row resolves the candidates exactly with an
-//          MSB-first radix select over the composite key
-//          (low 20 key bits, ~index) -- unique per token, so the lowest-index
-//          tie rule falls out of the order -- then sorts the row's K indices
-//          ascending in LDS (bitonic) and writes them with -1 padding.
+// Each score maps to an order-preserving 32-bit key.  Per query row:
+//   hist      (only when the indexer did not already build it) counts keys
+//             per bucket of their top 12 bits into a per-row histogram;
+//   threshold one workgroup per row finds the bucket b* holding the K-th
+//             largest key;
+//   filter    streams the row in 4096-score chunks, every load issued up
+//             front: tokens above b* are selected outright, tokens inside b*
+//             become candidates; each wave reserves its output slots with a
+//             single atomic after a lane prefix scan;
+//   refine    one workgroup per row loads the candidates' composite keys
+//             (low 20 key bits, ~index) into LDS -- unique per token, so the
+//             lowest-index tie rule is part of the order -- and radix-selects
+//             the remaining ones MSB first (digit found by a wave-parallel
+//             suffix scan); the K winners are marked in an LDS bitmap over
+//             the row (segment by segment for very long rows) and written
+//             out in ascending order by a block scan of the bitmap's
+//             popcounts.
 #include "dsa_kernels.h"
 
 namespace dsa {
 
 constexpr int TK_THREADS = 256;
-constexpr int TK_CHUNK = 16384;        // scores per filter / hist workgroup
-constexpr int RF_THREADS = 512;
+constexpr int TK_CHUNK = 16384;          // scores per hist workgroup
+constexpr int FL_PER_THREAD = 16;
+constexpr int FL_CHUNK = TK_THREADS * FL_PER_THREAD;   // scores per filter workgroup
+constexpr int RF_THREADS = 1024;
+constexpr int RF_LDS_CAND = 6144;        // candidates cached in LDS
+constexpr int RF_BITMAP_TOKENS = 1 << 19;  // rows up to this length use the bitmap writer
 
 __global__ void zero_u32(uint32_t* __restrict__ p, size_t n) {
     size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -60,64 +67,62 @@ __global__ __launch_bounds__(TK_THREADS) void topk_hist(TopkArgs a) {
         if (h[i]) atomicAdd(gh + i, h[i]);
 }
 
-// Threshold bucket of a row: the bucket b with count(> b) < k <= count(>= b).
-// Every thread returns b and count(> b).  256 threads, 16 buckets each.
-__device__ void find_threshold_bucket(const uint32_t* __restrict__ gh, int k, uint32_t* sh_scan,
-                                      int& bucket, uint32_t& above) {
+// Threshold bucket of each row: the bucket b with count(> b) < k <= count(>= b).
+__global__ __launch_bounds__(TK_THREADS) void topk_threshold(TopkArgs a) {
     static_assert(HIST_BINS == 16 * TK_THREADS, "bucket split");
+    const Geometry& G = a.g;
+    const int t = blockIdx.x;
+    const int r = find_request(G.qsl, G.B, t);
+    const int n = visible_count(G.ctx, G.qsl, r, t);
+    if (n <= a.k) return;
+    const uint32_t k = (uint32_t)a.k;
+    __shared__ uint32_t sh_scan[TK_THREADS];
     const int tid = threadIdx.x;
     const int hi = HIST_BINS - 16 * tid;   // this thread covers [hi-16, hi), highest first
-    const u32x4* src = (const u32x4*)(gh + hi - 16);
+    const u32x4* src = (const u32x4*)(a.hist + (size_t)t * HIST_BINS + hi - 16);
     uint32_t c[16];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-        u32x4 x = src[v];
+        const u32x4 x = src[v];
         c[4 * v] = x[0]; c[4 * v + 1] = x[1]; c[4 * v + 2] = x[2]; c[4 * v + 3] = x[3];
     }
     uint32_t sum = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) sum += c[i];
-    // inclusive scan over threads in descending-bucket order
     sh_scan[tid] = sum;
     __syncthreads();
-    for (int off = 1; off < TK_THREADS; off <<= 1) {
-        uint32_t v = tid >= off ? sh_scan[tid - off] : 0u;
+    for (int off = 1; off < TK_THREADS; off <<= 1) {   // inclusive scan, descending buckets
+        const uint32_t v = tid >= off ? sh_scan[tid - off] : 0u;
         __syncthreads();
         sh_scan[tid] += v;
         __syncthreads();
     }
-    const uint32_t incl = sh_scan[tid];
-    const uint32_t excl = incl - sum;
-    __syncthreads();
-    if (excl < (uint32_t)k && incl >= (uint32_t)k) {
+    const uint32_t incl = sh_scan[tid], excl = incl - sum;
+    if (excl < k && incl >= k) {
         uint32_t cum = excl;
         for (int i = 15; i >= 0; --i) {
-            if (cum + c[i] >= (uint32_t)k) {
-                sh_scan[0] = (uint32_t)(hi - 16 + i);
-                sh_scan[1] = cum;
+            if (cum + c[i] >= k) {
+                TopkCounters* cnt = a.counters + t;
+                cnt->bucket = (uint32_t)(hi - 16 + i);
+                cnt->above_expected = cum;
                 break;
             }
             cum += c[i];
         }
     }
-    __syncthreads();
-    bucket = (int)sh_scan[0];
-    above = sh_scan[1];
-    __syncthreads();
 }
 
-// Appends `flag` lanes to a per-row list with one atomic per wavefront;
-// returns this lane's slot (valid only where flag is set).
-__device__ __forceinline__ uint32_t wave_append(bool flag, uint32_t* counter) {
-    const unsigned long long mask = __ballot(flag);
-    if (mask == 0ull) return 0u;
+// Exclusive prefix sum over the 64 lanes of a wave; *total gets the wave sum.
+__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t* total) {
     const int lane = threadIdx.x & 63;
-    const int leader = __ffsll((long long)mask) - 1;
-    uint32_t base = 0u;
-    if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
-    base = __shfl(base, leader);
-    const unsigned long long below = lane ? (mask & ((1ull << lane) - 1ull)) : 0ull;
-    return base + (uint32_t)__popcll(below);
+    uint32_t x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    *total = __shfl(x, 63);
+    return x - v;
 }
 
 __global__ __launch_bounds__(TK_THREADS) void topk_filter(TopkArgs a) {
@@ -126,27 +131,52 @@ __global__ __launch_bounds__(TK_THREADS) void topk_filter(TopkArgs a) {
     const int r = find_request(G.qsl, G.B, t);
     const int n = visible_count(G.ctx, G.qsl, r, t);
     if (n <= a.k) return;
-    const int c0 = blockIdx.x * TK_CHUNK;
+    const int c0 = blockIdx.x * FL_CHUNK;
     if (c0 >= n) return;
-    const int c1 = min(n, c0 + TK_CHUNK);
-    __shared__ uint32_t sh_scan[TK_THREADS];
-    int bucket;
-    uint32_t above;
-    find_threshold_bucket(a.hist + (size_t)t * HIST_BINS, a.k, sh_scan, bucket, above);
+    const int c1 = min(n, c0 + FL_CHUNK);
     TopkCounters* cnt = a.counters + t;
-    if (blockIdx.x == 0 && threadIdx.x == 0) cnt->bucket = (uint32_t)bucket;
+    const uint32_t bucket = cnt->bucket;
     const float* row = a.scores + (size_t)t * a.ld;
-    int32_t* sel = a.indices + (size_t)t * a.k;
+    const int lane = threadIdx.x & 63;
+
+    // All loads first (coalesced: consecutive lanes, consecutive scores).
+    float v[FL_PER_THREAD];
+#pragma unroll
+    for (int j = 0; j < FL_PER_THREAD; ++j) {
+        const int s = c0 + j * TK_THREADS + threadIdx.x;
+        v[j] = s < c1 ? row[s] : 0.f;
+    }
+    uint32_t sel_mask = 0u, cand_mask = 0u;
+#pragma unroll
+    for (int j = 0; j < FL_PER_THREAD; ++j) {
+        const int s = c0 + j * TK_THREADS + threadIdx.x;
+        const uint32_t b = score_key(v[j]) >> HIST_SHIFT;
+        if (s < c1 && b > bucket) sel_mask |= 1u << j;
+        if (s < c1 && b == bucket) cand_mask |= 1u << j;
+    }
+    uint32_t sel_total, cand_total;
+    const uint32_t sel_off = wave_excl_scan(__popc(sel_mask), &sel_total);
+    const uint32_t cand_off = wave_excl_scan(__popc(cand_mask), &cand_total);
+    uint32_t sel_base = 0u, cand_base = 0u;
+    if (lane == 0) {
+        if (sel_total) sel_base = atomicAdd(&cnt->above, sel_total);
+        if (cand_total) cand_base = atomicAdd(&cnt->cand, cand_total);
+    }
+    sel_base = __shfl(sel_base, 0) + sel_off;
+    cand_base = __shfl(cand_base, 0) + cand_off;
+    int32_t* sel = a.above_list + (size_t)t * a.k;
     int32_t* cand = a.cand + (size_t)t * TOPK_CAND_CAP;
-    for (int base = c0; base < c1; base += TK_THREADS) {
-        const int s = base + threadIdx.x;
-        const bool valid = s < c1;
-        const int b = valid ? (int)(score_key(row[s]) >> HIST_SHIFT) : -1;
-        const bool is_sel = b > bucket, is_cand = b == bucket;
-        const uint32_t ps = wave_append(is_sel, &cnt->above);
-        if (is_sel && ps < (uint32_t)a.k) sel[ps] = s;
-        const uint32_t pc = wave_append(is_cand, &cnt->cand);
-        if (is_cand && pc < (uint32_t)TOPK_CAND_CAP) cand[pc] = s;
+#pragma unroll
+    for (int j = 0; j < FL_PER_THREAD; ++j) {
+        const int s = c0 + j * TK_THREADS + threadIdx.x;
+        if (sel_mask & (1u << j)) {
+            if (sel_base < (uint32_t)a.k) sel[sel_base] = s;
+            ++sel_base;
+        }
+        if (cand_mask & (1u << j)) {
+            if (cand_base < (uint32_t)TOPK_CAND_CAP) cand[cand_base] = s;
+            ++cand_base;
+        }
     }
 }
 
@@ -156,6 +186,10 @@ __device__ __forceinline__ uint64_t composite(uint32_t key, int s) {
     return ((uint64_t)(key & ((1u << HIST_SHIFT) - 1u)) << 32) | (uint64_t)(~(uint32_t)s);
 }
 
+__device__ __forceinline__ int composite_index(uint64_t ck) {
+    return (int)(~(uint32_t)(ck & 0xFFFFFFFFull));
+}
+
 __global__ __launch_bounds__(RF_THREADS) void topk_refine(TopkArgs a) {
     const Geometry& G = a.g;
     const int t = blockIdx.x;
@@ -163,47 +197,71 @@ __global__ __launch_bounds__(RF_THREADS) void topk_refine(TopkArgs a) {
     const int n = visible_count(G.ctx, G.qsl, r, t);
     const int K = a.k;
     int32_t* out = a.indices + (size_t)t * K;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (n <= K) {      // dense: every visible token, in order
         for (int i = tid; i < K; i += RF_THREADS) out[i] = i < n ? i : -1;
         return;
     }
-    __shared__ int32_t list[TOPK_MAX_K];
+    __shared__ uint64_t ck_lds[RF_LDS_CAND];
+    __shared__ uint32_t bitmap[RF_BITMAP_TOKENS / 32];
     __shared__ uint32_t h256[256];
     __shared__ uint32_t sh_state[4];
+    __shared__ uint32_t wave_sums[RF_THREADS / 64];
+    if (tid < 4) sh_state[tid] = 0u;
     const TopkCounters* cnt = a.counters + t;
-    const uint32_t above = cnt->above, ncand = cnt->cand;
+    const uint32_t above = min(cnt->above, (uint32_t)K), ncand = cnt->cand;
     const uint32_t bucket = cnt->bucket;
-    const bool from_list = ncand <= (uint32_t)TOPK_CAND_CAP;
-    const int32_t* cand = a.cand + (size_t)t * TOPK_CAND_CAP;
     const float* row = a.scores + (size_t)t * a.ld;
-    const int scan_n = from_list ? (int)ncand : n;
+    const int32_t* cand = a.cand + (size_t)t * TOPK_CAND_CAP;
+    const int32_t* above_list = a.above_list + (size_t)t * K;
+    // Candidate source: LDS copy, the global candidate list, or a full rescan.
+    const int mode = ncand <= (uint32_t)RF_LDS_CAND ? 0 : (ncand <= (uint32_t)TOPK_CAND_CAP ? 1 : 2);
+    const int scan_n = mode == 2 ? n : (int)ncand;
+    if (mode == 0)
+        for (int i = tid; i < scan_n; i += RF_THREADS) {
+            const int s = cand[i];
+            ck_lds[i] = composite(score_key(row[s]), s);
+        }
+    // fetch candidate i; false if it is not in the threshold bucket (rescan mode)
+    auto get = [&](int i, uint64_t& ck) -> bool {
+        if (mode == 0) { ck = ck_lds[i]; return true; }
+        const int s = mode == 1 ? cand[i] : i;
+        const uint32_t key = score_key(row[s]);
+        if (mode == 2 && (key >> HIST_SHIFT) != bucket) return false;
+        ck = composite(key, s);
+        return true;
+    };
 
-    // MSB-first radix select: find the `need`-th largest composite key.
+    // MSB-first radix select of the `need`-th largest composite key.
     uint32_t need = (uint32_t)K - above;
     uint64_t prefix = 0;
     int shift = 48;
     for (;; shift -= 8) {
-        for (int i = tid; i < 256; i += RF_THREADS) h256[i] = 0u;
+        if (tid < 256) h256[tid] = 0u;
         __syncthreads();
         for (int i = tid; i < scan_n; i += RF_THREADS) {
-            const int s = from_list ? cand[i] : i;
-            const uint32_t key = score_key(row[s]);
-            if (!from_list && (key >> HIST_SHIFT) != bucket) continue;
-            const uint64_t ck = composite(key, s);
-            if ((ck >> (shift + 8)) == prefix) atomicAdd(&h256[(ck >> shift) & 255u], 1u);
+            uint64_t ck;
+            if (get(i, ck) && (ck >> (shift + 8)) == prefix) atomicAdd(&h256[(ck >> shift) & 255u], 1u);
         }
         __syncthreads();
-        if (tid == 0) {
-            uint32_t cum = 0;
-            int d = 255;
-            for (; d > 0; --d) {
-                if (cum + h256[d] >= need) break;
-                cum += h256[d];
+        if (wave == 0) {   // digit with count(> d) < need <= count(>= d); lane l holds 255-4l .. 252-4l
+            uint32_t c[4], sum = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { c[j] = h256[255 - 4 * lane - j]; sum += c[j]; }
+            uint32_t tot;
+            const uint32_t excl = wave_excl_scan(sum, &tot);
+            if (excl < need && excl + sum >= need) {
+                uint32_t cum = excl;
+                for (int j = 0; j < 4; ++j) {
+                    if (cum + c[j] >= need) {
+                        sh_state[0] = (uint32_t)(255 - 4 * lane - j);
+                        sh_state[1] = need - cum;
+                        sh_state[2] = c[j] == need - cum ? 1u : 0u;
+                        break;
+                    }
+                    cum += c[j];
+                }
             }
-            sh_state[0] = (uint32_t)d;
-            sh_state[1] = need - cum;                 // still needed inside bucket d
-            sh_state[2] = h256[d] == need - cum ? 1u : 0u;
         }
         __syncthreads();
         const uint32_t d = sh_state[0];
@@ -214,39 +272,52 @@ __global__ __launch_bounds__(RF_THREADS) void topk_refine(TopkArgs a) {
         if (done) break;
     }
 
-    // Gather: filter's selections [0, above) plus the refined ones.
-    for (int i = tid; i < (int)above; i += RF_THREADS) list[i] = out[i];
-    if (tid == 0) sh_state[3] = 0u;
-    __syncthreads();
-    for (int i = tid; i < scan_n; i += RF_THREADS) {
-        const int s = from_list ? cand[i] : i;
-        const uint32_t key = score_key(row[s]);
-        if (!from_list && (key >> HIST_SHIFT) != bucket) continue;
-        if ((composite(key, s) >> shift) >= prefix) {
-            const uint32_t p = atomicAdd(&sh_state[3], 1u);
-            if (above + p < (uint32_t)K) list[above + p] = s;
+    // Mark the winners in a bitmap over one segment of the row at a time and
+    // write them in ascending order (block scan of per-thread popcounts).
+    uint32_t written = 0;
+    for (int seg0 = 0; seg0 < n; seg0 += RF_BITMAP_TOKENS) {
+        const int seg1 = min(n, seg0 + RF_BITMAP_TOKENS);
+        const int words = (seg1 - seg0 + 31) / 32;
+        for (int i = tid; i < words; i += RF_THREADS) bitmap[i] = 0u;
+        __syncthreads();
+        for (int i = tid; i < (int)above; i += RF_THREADS) {
+            const int s = above_list[i] - seg0;
+            if (s >= 0 && s < seg1 - seg0) atomicOr(&bitmap[s >> 5], 1u << (s & 31));
         }
-    }
-    __syncthreads();
-
-    // Ascending bitonic sort of the K indices (padded to a power of two).
-    int P = 1;
-    while (P < K) P <<= 1;
-    for (int i = K + tid; i < P; i += RF_THREADS) list[i] = 0x7FFFFFFF;
-    __syncthreads();
-    for (int size = 2; size <= P; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < P / 2; i += RF_THREADS) {
-                const int lo = 2 * i - (i & (stride - 1));
-                const int hi = lo + stride;
-                const bool asc = (lo & size) == 0;
-                const int x = list[lo], y = list[hi];
-                if ((x > y) == asc) { list[lo] = y; list[hi] = x; }
+        for (int i = tid; i < scan_n; i += RF_THREADS) {
+            uint64_t ck;
+            if (get(i, ck) && (ck >> shift) >= prefix) {
+                const int s = composite_index(ck) - seg0;
+                if (s >= 0 && s < seg1 - seg0) atomicOr(&bitmap[s >> 5], 1u << (s & 31));
             }
-            __syncthreads();
         }
+        __syncthreads();
+        const int per = (words + RF_THREADS - 1) / RF_THREADS;
+        const int w0 = min(words, tid * per), w1 = min(words, w0 + per);
+        uint32_t nbits = 0;
+        for (int w = w0; w < w1; ++w) nbits += __popc(bitmap[w]);
+        uint32_t wtot;
+        const uint32_t wexcl = wave_excl_scan(nbits, &wtot);
+        if (lane == 0) wave_sums[wave] = wtot;
+        __syncthreads();
+        uint32_t base = written, seg_total = 0;
+        for (int w = 0; w < RF_THREADS / 64; ++w) {
+            if (w < wave) base += wave_sums[w];
+            seg_total += wave_sums[w];
+        }
+        uint32_t pos = base + wexcl;
+        for (int w = w0; w < w1; ++w) {
+            uint32_t bits = bitmap[w];
+            while (bits) {
+                const int b = __ffs(bits) - 1;
+                bits &= bits - 1u;
+                if (pos < (uint32_t)K) out[pos] = seg0 + w * 32 + b;
+                ++pos;
+            }
+        }
+        written += seg_total;
+        __syncthreads();
     }
-    for (int i = tid; i < K; i += RF_THREADS) out[i] = list[i];
 }
 
 hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t s) {
@@ -256,10 +327,12 @@ hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s) {
-    dim3 grid((a.g.max_ctx + TK_CHUNK - 1) / TK_CHUNK, a.g.T);
-    hipLaunchKernelGGL(topk_filter, grid, dim3(TK_THREADS), 0, s, a);
+    hipLaunchKernelGGL(topk_threshold, dim3(a.g.T), dim3(TK_THREADS), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    dim3 grid((a.g.max_ctx + FL_CHUNK - 1) / FL_CHUNK, a.g.T);
+    hipLaunchKernelGGL(topk_filter, grid, dim3(TK_THREADS), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(topk_refine, dim3(a.g.T), dim3(RF_THREADS), 0, s, a);
     return hipGetLastError();
 }

@@ -7,9 +7,12 @@ Comparison rules:
     contain tokens whose oracle score lies within 1e-4 (relative) of the
     oracle's K-th score (tokens on the selection boundary, where fp32 and
     fp64 rounding may order them differently);
-  * outputs: max-abs <= 2e-2 for bf16 paths and <= 1e-4 for the fp32 path,
-    plus a relative Frobenius bound (1e-2 bf16, 1e-5 fp32) against the oracle
-    evaluated on the GPU's own selection.
+  * outputs: max-abs <= 2e-2 for bf16 paths and <= 1e-4 for the fp32 path
+    end to end (GPU selection vs the oracle's own selection); against the
+    oracle evaluated on the GPU's own selection additionally a relative
+    Frobenius bound (1e-2 bf16, 1e-5 fp32).  The Frobenius bound is not
+    applied end to end: one boundary token swapped at long contexts moves an
+    output by ~p*|v| ~ 5e-4 per element, about 1% of its norm.
 """
 from __future__ import annotations
 
@@ -69,13 +72,14 @@ def check_selection(sel_row, scores_orc, K, band=BAND):
     return len(diff)
 
 
-def check_out(gpu, ref, fp32):
+def check_out(gpu, ref, fp32, same_selection=True):
     atol = 1e-4 if fp32 else 2e-2
     rel_bound = 1e-5 if fp32 else 1e-2
     err = np.abs(gpu - ref).max()
     rel = np.linalg.norm(gpu - ref) / max(np.linalg.norm(ref), 1e-30)
     assert err <= atol, "max abs err %g > %g" % (err, atol)
-    assert rel <= rel_bound, "relative Frobenius err %g > %g" % (rel, rel_bound)
+    if same_selection:
+        assert rel <= rel_bound, "relative Frobenius err %g > %g" % (rel, rel_bound)
     return err, rel
 
 
@@ -86,9 +90,9 @@ def check_step_rows(wl, rows, out, lse, idx, threads=16, layer=1):
     worst = 0.0
     for t in rows:
         r = res[t]
-        check_selection(idx[t], r["scores"], wl.topk)
+        nd = check_selection(idx[t], r["scores"], wl.topk)
         # end to end against the oracle's own selection
-        check_out(out[t], r["out"], fp32)
+        check_out(out[t], r["out"], fp32, same_selection=(nd == 0))
         # and against the oracle evaluated on the GPU's selection
         sel = idx[t][idx[t] >= 0]
         o2, l2 = oracle.query_mla(wl, t, sel, layer)
