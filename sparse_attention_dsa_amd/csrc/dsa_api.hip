@@ -76,6 +76,16 @@ StepLayout step_layout(const dsa_batch* b, int k, int n_heads, bool fast_mla) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH; }
 
+// Selection from materialised scores: one kernel per row when rows fit its
+// LDS bitmap, else histogram + threshold/filter/refine kernels.
+hipError_t run_topk(const TopkArgs& a, const TopkLayout& l, hipStream_t s) {
+    if (topk_single_kernel(a.g.max_ctx, a.k)) return launch_topk_row(a, s);
+    hipError_t e = launch_zero_u32(a.hist, (l.cand - l.hist) / sizeof(uint32_t), s);
+    if (e == hipSuccess) e = launch_topk_hist(a, s);
+    if (e == hipSuccess) e = launch_topk_select(a, s);
+    return e;
+}
+
 int device_arch_ok() {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return DSA_ERR_DEVICE;
@@ -83,6 +93,23 @@ int device_arch_ok() {
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DSA_ERR_DEVICE;
     return strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? DSA_OK : DSA_ERR_DEVICE;
 }
+
+}  // namespace
+
+int dsa::device_cu_count() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        cache[dev] = cus;
+    }
+    return cache[dev];
+}
+
+namespace {
 
 int check_device_cached() {
     // Per-device result; the arch of a device never changes.
@@ -212,7 +239,7 @@ int dsa_indexer_scores(const dsa_batch* b, const dsa_index_cache* c, const void*
     a.g = geometry(b);
     a.keys = c->keys; a.key_scales = c->scales; a.key_dtype = c->dtype; a.dim = c->dim;
     a.q = q_idx; a.w = w; a.n_heads = n_heads_idx;
-    a.scores = scores; a.ld = ld; a.hist = nullptr;
+    a.scores = scores; a.ld = ld;
     return launch_status(launch_indexer(a, (hipStream_t)stream));
 }
 
@@ -233,10 +260,7 @@ int dsa_topk(const dsa_batch* b, const float* scores, int64_t ld, int32_t k, int
     a.counters = (TopkCounters*)(base + l.counters);
     a.cand = (int32_t*)(base + l.cand);
     a.above_list = (int32_t*)(base + l.above_list);
-    hipError_t e = launch_zero_u32(a.hist, (l.cand - l.hist) / sizeof(uint32_t), s);
-    if (e == hipSuccess) e = launch_topk_hist(a, s);
-    if (e == hipSuccess) e = launch_topk_select(a, s);
-    return launch_status(e);
+    return launch_status(run_topk(a, l, s));
 }
 
 static int mla_entry(const dsa_batch* b, const dsa_latent_cache* c, const void* q, int32_t n_heads,
@@ -287,15 +311,13 @@ int dsa_decode_step(const dsa_batch* b, const dsa_index_cache* ic, const void* q
     tk.counters = (TopkCounters*)(base + l.tk.counters);
     tk.cand = (int32_t*)(base + l.tk.cand);
     tk.above_list = (int32_t*)(base + l.tk.above_list);
-    hipError_t e = launch_zero_u32(tk.hist, (l.tk.cand - l.tk.hist) / sizeof(uint32_t), s);
-
     IndexerArgs ia;
     ia.g = tk.g;
     ia.keys = ic->keys; ia.key_scales = ic->scales; ia.key_dtype = ic->dtype; ia.dim = ic->dim;
     ia.q = q_idx; ia.w = w; ia.n_heads = n_heads_idx;
-    ia.scores = scores; ia.ld = l.ld; ia.hist = tk.hist;
-    if (e == hipSuccess) e = launch_indexer(ia, s);
-    if (e == hipSuccess) e = launch_topk_select(tk, s);
+    ia.scores = scores; ia.ld = l.ld;
+    hipError_t e = launch_indexer(ia, s);
+    if (e == hipSuccess) e = run_topk(tk, l.tk, s);
     if (e != hipSuccess) return DSA_ERR_LAUNCH;
     return run_mla(b, lc, q_mla, n_heads, indices, k, scale, out, lse, base, ws_bytes, l.tk.end, false, s);
 }

@@ -115,7 +115,6 @@ struct IndexerArgs {
     const void* keys; const float* key_scales; int key_dtype; int dim;
     const void* q; const float* w; int n_heads;
     float* scores; int64_t ld;
-    uint32_t* hist;     // [T][HIST_BINS] (zeroed) or nullptr
 };
 
 struct TopkArgs {
@@ -140,11 +139,18 @@ struct MlaArgs {
     int splits;
 };
 
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
 // Launchers (return hipError_t of the last launch).
 hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s);
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
 hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t s);
 hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s);
+// Whole selection in one kernel (no histogram input, no workspace) for rows
+// of up to 2^19 tokens.
+bool topk_single_kernel(int max_ctx, int k);
+hipError_t launch_topk_row(const TopkArgs& a, hipStream_t s);
 hipError_t launch_mla(const MlaArgs& a, bool prefill, hipStream_t s);
 
 // Which MLA path serves these shapes, and how many splits it uses.

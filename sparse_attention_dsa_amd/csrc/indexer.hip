@@ -5,18 +5,23 @@
 // sigma_s (per-token key scale) is applied after the head sum, exact because
 // ReLU is positively homogeneous and sigma_s >= 0.
 //
-// Fast path (e4m3 keys and queries, dim 128, heads a multiple of 16, 64-token
-// blocks): per workgroup one request, a group of NQ query rows of it and a
-// chunk of its context.  Each wave streams whole 64-token pages of keys
-// (8 KB, contiguous) straight into registers and multiplies them against the
-// register-resident queries with v_mfma_f32_16x16x128_f8f6f4: heads are the
-// M dimension, tokens the N dimension and the full 128-wide key the K
-// dimension, so one instruction covers a 16x16 head-token tile.  The ReLU,
-// the weighted head sum and the key scale are applied on the accumulators;
-// the head sum crosses the four 16-lane groups with three lane exchanges.
-// Scores are stored as 256-byte coalesced rows and counted into a per-row
-// LDS histogram of the top 12 key bits, which the top-K selection uses to
-// find the threshold bucket without a second pass over the scores.
+// Fast path (e4m3 keys and queries, dim 128, 16/32/64 heads, 64-token blocks).
+// Keys are streamed once, a 64-token page (8 KB, contiguous) at a time, and
+// multiplied against register-resident queries with
+// v_mfma_f32_16x16x128_f8f6f4: heads are the M dimension, tokens the N
+// dimension and the whole 128-wide key the K dimension, so one instruction
+// covers a 16x16 head-token tile and a page takes 16 per query row.  ReLU,
+// head weights and the key scale are applied on the accumulators; the head sum
+// crosses the four 16-lane groups with three lane exchanges, leaving lane l
+// with the score of token l of the page.
+//
+// Two launch shapes:
+//   persistent  (decode-sized batches) a fixed grid, two workgroups per CU;
+//               all (request, query group) page ranges are concatenated and
+//               each wave streams an equal contiguous share, so every wave
+//               does the same work with no per-chunk start-up;
+//   chunked     one workgroup per (request, query group, 1024-token chunk),
+//               pages fed by an LDS ring of asynchronous transfers.
 #include "dsa_kernels.h"
 
 namespace dsa {
@@ -24,29 +29,6 @@ namespace dsa {
 constexpr int IDX_D = 128;
 constexpr int IDX_PAGE = 64;
 constexpr int IDX_THREADS = 256;
-constexpr int IDX_CHUNK_PAGES = 32;   // 2048 tokens per workgroup
-
-struct KeyPage {
-    i32x8 frag[4];   // token 16*nt + (lane & 15), 32 of its 128 bytes
-    float scale;     // scale of token (lane) of the page
-};
-
-// Lane l loads bytes [16g, 16g+16) and [64+16g, 64+16g+16) of its token,
-// g = l >> 4; the query fragments use the same byte assignment.
-__device__ __forceinline__ void load_key_page(const uint8_t* __restrict__ keys,
-                                              const float* __restrict__ scales, int blk,
-                                              int lane, KeyPage& kp) {
-    const int g = lane >> 4, col = lane & 15;
-    const uint8_t* base = keys + (size_t)blk * (IDX_PAGE * IDX_D);
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-        const uint8_t* rp = base + (16 * nt + col) * IDX_D + 16 * g;
-        u32x4 lo = __builtin_nontemporal_load((const u32x4*)rp);
-        u32x4 hi = __builtin_nontemporal_load((const u32x4*)(rp + 64));
-        kp.frag[nt] = join_i32x8(lo, hi);
-    }
-    kp.scale = scales ? scales[(size_t)blk * IDX_PAGE + lane] : 1.0f;
-}
 
 // part[nt] holds, for token 16*nt + (lane & 15), the partial head sum of this
 // lane's 16-lane group g.  Returns the full sum for token `lane` of the page.
@@ -93,87 +75,6 @@ __device__ __forceinline__ void page_scores(const i32x8 (&qf)[NQ][HT], const flo
     }
 }
 
-template <int NQ, int HT, bool HIST>
-__global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_mfma(IndexerArgs a, int qgroups,
-                                                                int chunk_tokens) {
-    const Geometry& G = a.g;
-    const int r = blockIdx.y / qgroups, qg = blockIdx.y % qgroups;
-    const int L = G.ctx[r];
-    const int qs = G.qsl[r], ql = G.qsl[r + 1] - qs;
-    const int j0 = qg * NQ;
-    if (j0 >= ql) return;
-    const int nq = min(NQ, ql - j0);
-    const int n_last = L - ql + j0 + nq;          // visible count of the group's last row
-    const int tok0 = blockIdx.x * chunk_tokens;
-    if (tok0 >= n_last) return;
-    const int tok1 = min(n_last, tok0 + chunk_tokens);
-
-    __shared__ uint32_t hist[HIST ? NQ : 1][HIST ? HIST_BINS : 1];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 4, col = lane & 15;
-    constexpr bool use_hist = HIST;
-    if (use_hist)
-        for (int i = tid; i < NQ * HIST_BINS; i += IDX_THREADS) (&hist[0][0])[i] = 0u;
-
-    // Register-resident queries (A operand: head 16*ht + col) and weights of
-    // the four accumulator rows this lane owns (heads 16*ht + 4g + i).
-    i32x8 qf[NQ][HT];
-    float wv[NQ][HT][4];
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-        const int t = qs + j0 + min(j, nq - 1);
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-            const uint8_t* qp = (const uint8_t*)a.q + ((size_t)t * a.n_heads + 16 * ht + col) * IDX_D + 16 * g;
-            qf[j][ht] = join_i32x8(*(const u32x4*)qp, *(const u32x4*)(qp + 64));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) wv[j][ht][i] = a.w[(size_t)t * a.n_heads + 16 * ht + 4 * g + i];
-        }
-    }
-    if (use_hist) __syncthreads();
-
-    const int32_t* pt = G.page_table + (size_t)r * G.max_blocks;
-    const uint8_t* keys = (const uint8_t*)a.keys;
-    const int page1 = (tok1 + IDX_PAGE - 1) / IDX_PAGE;
-    int pg = tok0 / IDX_PAGE + wave;
-    KeyPage cur;
-    if (pg < page1) load_key_page(keys, a.key_scales, pt[pg], lane, cur);
-
-    for (; pg < page1; pg += 4) {
-        KeyPage nxt;
-        const bool more = pg + 4 < page1;
-        if (more) load_key_page(keys, a.key_scales, pt[pg + 4], lane, nxt);
-        const int pos = pg * IDX_PAGE + lane;
-        float ps[NQ];
-        page_scores<NQ, HT>(qf, wv, cur.frag, cur.scale, lane, nq, ps);
-#pragma unroll
-        for (int j = 0; j < NQ; ++j) {
-            if (j < nq) {
-                const float s = ps[j];
-                const int t = qs + j0 + j;
-                const int n_j = L - ql + j0 + j + 1;
-                if (pos < n_j) {
-                    a.scores[(size_t)t * a.ld + pos] = s;
-                    if (use_hist) atomicAdd(&hist[j][score_key(s) >> HIST_SHIFT], 1u);
-                }
-            }
-        }
-        if (more) cur = nxt;
-    }
-
-    if (use_hist) {
-        __syncthreads();
-        for (int j = 0; j < nq; ++j) {
-            uint32_t* gh = a.hist + (size_t)(qs + j0 + j) * HIST_BINS;
-            for (int b = tid; b < HIST_BINS; b += IDX_THREADS) {
-                const uint32_t v = hist[j][b];
-                if (v) atomicAdd(gh + b, v);
-            }
-        }
-    }
-}
-
-
 // ---------------------------------------------------------------------------
 // LDS-ring variant: each wave streams its pages through a private ring of
 // DMA_DEPTH page slots in LDS with global_load_lds_dwordx4 (one fully
@@ -191,6 +92,10 @@ __global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_mfma(IndexerArgs a, i
 constexpr int DMA_DEPTH = IDX_DMA_DEPTH;     // pages in flight per wave
 constexpr int DMA_PPW = IDX_DMA_PPW;         // pages per wave per workgroup
 constexpr int DMA_OPS_PER_PAGE = 9;          // 8 x 1 KB of keys + 256 B of scales
+#ifndef IDX_DMA_AUX
+#define IDX_DMA_AUX 3
+#endif
+constexpr int DMA_AUX = IDX_DMA_AUX;         // cache policy of the key transfers (sc0 nt: streamed once)
 
 __device__ __forceinline__ int page_swz(int t) { return (t ^ (t >> 3)) & 7; }
 
@@ -206,7 +111,7 @@ __device__ __forceinline__ void wait_vmcnt() {
     else static_assert(N == 0, "unsupported vmcnt");
 }
 
-template <int NQ, int HT, bool HIST>
+template <int NQ, int HT>
 __global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_dma(IndexerArgs a, int qgroups) {
     const Geometry& G = a.g;
     const int r = blockIdx.y / qgroups, qg = blockIdx.y % qgroups;
@@ -223,14 +128,11 @@ __global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_dma(IndexerArgs a, in
 
     __shared__ __attribute__((aligned(16))) uint8_t kbuf[4][DMA_DEPTH][IDX_PAGE * IDX_D];
     __shared__ __attribute__((aligned(16))) float sbuf[4][DMA_DEPTH][IDX_PAGE];
-    __shared__ uint32_t hist[HIST ? NQ : 1][HIST ? HIST_BINS / 2 : 1];   // two 16-bit counts per word
     const int tid = threadIdx.x, lane = tid & 63;
     // wave index in a scalar register: page ids then come from scalar loads,
     // which do not touch the vector-memory counter the ring waits on
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, col = lane & 15;
-    if constexpr (HIST)
-        for (int i = tid; i < NQ * HIST_BINS / 2; i += IDX_THREADS) (&hist[0][0])[i] = 0u;
 
     const int32_t* pt = G.page_table + (size_t)r * G.max_blocks;
     const uint8_t* keys = (const uint8_t*)a.keys;
@@ -251,7 +153,7 @@ __global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_dma(IndexerArgs a, in
         for (int c = 0; c < 8; ++c) {
             const int U = 64 * c + lane, t = U >> 3, u = (U & 7) ^ page_swz(t);
             __builtin_amdgcn_global_load_lds((const void*)(src + t * IDX_D + 16 * u), (lds_ptr_t)(dst + 1024 * c),
-                                             16, 0, 0);
+                                             16, 0, DMA_AUX);
         }
         const void* ssrc = has_scale ? (const void*)(a.key_scales + (size_t)blk * IDX_PAGE + lane)
                                      : (const void*)(src + 4 * lane);
@@ -274,7 +176,6 @@ __global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_dma(IndexerArgs a, in
             for (int i = 0; i < 4; ++i) wv[j][ht][i] = a.w[(size_t)t * a.n_heads + 16 * ht + 4 * g + i];
         }
     }
-    if constexpr (HIST) __syncthreads();
 
     float sc[NQ][DMA_PPW];
 #pragma unroll
@@ -303,32 +204,7 @@ __global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_dma(IndexerArgs a, in
             for (int j = 0; j < NQ; ++j) sc[j][i] = ps[j];
         }
     }
-    // Stores and histogram counts after the ring has drained (LDS atomics
-    // issued while transfers are pending would make the compiler wait on them).
-    // (histogram first: its barrier then has no stores to wait for)
-    if constexpr (HIST) {
-#pragma unroll
-        for (int i = 0; i < DMA_PPW; ++i) {
-            const int pos = (pfirst + 4 * i) * IDX_PAGE + lane;
-#pragma unroll
-            for (int j = 0; j < NQ; ++j) {
-                const int n_j = L - ql + j0 + j + 1;
-                if (i < npw && j < nq && pos < n_j) {
-                    const uint32_t b = score_key(sc[j][i]) >> HIST_SHIFT;
-                    atomicAdd(&hist[j][b >> 1], 1u << (16 * (b & 1)));
-                }
-            }
-        }
-        __syncthreads();
-        for (int j = 0; j < nq; ++j) {
-            uint32_t* gh = a.hist + (size_t)(qs + j0 + j) * HIST_BINS;
-            for (int w = tid; w < HIST_BINS / 2; w += IDX_THREADS) {
-                const uint32_t v = hist[j][w];
-                if (v & 0xFFFFu) atomicAdd(gh + 2 * w, v & 0xFFFFu);
-                if (v >> 16) atomicAdd(gh + 2 * w + 1, v >> 16);
-            }
-        }
-    }
+    // scores are stored after the ring has drained (stores share the counter it waits on)
 #pragma unroll
     for (int i = 0; i < DMA_PPW; ++i) {
         const int pos = (pfirst + 4 * i) * IDX_PAGE + lane;
@@ -336,6 +212,168 @@ __global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_dma(IndexerArgs a, in
         for (int j = 0; j < NQ; ++j) {
             const int n_j = L - ql + j0 + j + 1;
             if (i < npw && j < nq && pos < n_j) a.scores[(size_t)(qs + j0 + j) * a.ld + pos] = sc[j][i];
+        }
+    }
+}
+
+
+// ---------------------------------------------------------------------------
+// Staged page loads for the persistent kernel: fully contiguous loads (lane l
+// reads bytes [1024c + 16l, +16) of the page, 1 KB per instruction, like a
+// plain streaming read) into a register ring, then each page is re-laid
+// through a private 8 KB LDS buffer of the wave into the MFMA fragment layout.
+struct RawPage {
+    u32x4 v[8];      // unit (lane & 7) of token 8c + (lane >> 3), c = 0..7
+    float scale;     // scale of token (lane)
+};
+
+__device__ __forceinline__ void load_raw_page(const uint8_t* __restrict__ keys, const float* __restrict__ scales,
+                                              int blk, int lane, RawPage& p) {
+    const uint8_t* base = keys + (size_t)blk * (IDX_PAGE * IDX_D) + 16 * lane;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) p.v[c] = __builtin_nontemporal_load((const u32x4*)(base + 1024 * c));
+    p.scale = scales ? scales[(size_t)blk * IDX_PAGE + lane] : 1.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Persistent variant for decode batches: the work is the concatenation of all
+// (request, query group) page ranges; a fixed grid of workgroups splits it
+// into equal contiguous shares, one per wave, so every wave streams the same
+// number of pages with no per-chunk start-up and no tail imbalance.  Pages
+// arrive through the staged register ring (contiguous 1 KB loads, relaid
+// through the wave's LDS buffer); queries and weights are reloaded when a
+// wave's share crosses into the next request.
+#ifndef IDX_PER_PF
+#define IDX_PER_PF 2
+#endif
+constexpr int PER_PF = IDX_PER_PF;
+constexpr int PER_MAX_ITEMS = 4096;        // (request, query group) pairs per launch
+constexpr int PER_WG_PER_CU = 2;
+
+template <int NQ, int HT>
+__global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_persistent(IndexerArgs a, int qgroups) {
+    const Geometry& G = a.g;
+    const int n_items = G.B * qgroups;
+    __shared__ int item_off[PER_MAX_ITEMS + 1];
+    __shared__ int scan_tmp[IDX_THREADS];
+    __shared__ __attribute__((aligned(16))) uint8_t pbuf[4][IDX_PAGE * IDX_D];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, col = lane & 15;
+
+    // pages of each item (visible count of the group's last row), prefix-summed
+    auto item_pages = [&](int it) -> int {
+        const int r = it / qgroups, qg = it % qgroups;
+        const int qs = G.qsl[r], ql = G.qsl[r + 1] - qs;
+        const int j0 = qg * NQ;
+        if (j0 >= ql) return 0;
+        const int n_last = G.ctx[r] - ql + j0 + min(NQ, ql - j0);
+        return n_last > 0 ? (n_last + IDX_PAGE - 1) / IDX_PAGE : 0;
+    };
+    const int per = (n_items + IDX_THREADS - 1) / IDX_THREADS;
+    const int i0 = min(n_items, tid * per), i1 = min(n_items, i0 + per);
+    int local = 0;
+    for (int it = i0; it < i1; ++it) local += item_pages(it);
+    scan_tmp[tid] = local;
+    __syncthreads();
+    for (int off = 1; off < IDX_THREADS; off <<= 1) {
+        const int v = tid >= off ? scan_tmp[tid - off] : 0;
+        __syncthreads();
+        scan_tmp[tid] += v;
+        __syncthreads();
+    }
+    int run = scan_tmp[tid] - local;
+    for (int it = i0; it < i1; ++it) { item_off[it] = run; run += item_pages(it); }
+    if (tid == IDX_THREADS - 1) item_off[n_items] = scan_tmp[tid];
+    __syncthreads();
+
+    const int P = item_off[n_items];
+    const int nwaves = gridDim.x * 4;
+    const int gw = blockIdx.x * 4 + wave;
+    const int p0 = (int)(((long long)P * gw) / nwaves), p1 = (int)(((long long)P * (gw + 1)) / nwaves);
+    if (p0 >= p1) return;
+    auto find_item = [&](int p) -> int {   // largest it with item_off[it] <= p and pages > 0
+        int lo = 0, hi = n_items - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (item_off[mid] <= p) lo = mid; else hi = mid - 1;
+        }
+        while (item_off[lo + 1] <= p) ++lo;
+        return lo;
+    };
+    const uint8_t* keys = (const uint8_t*)a.keys;
+
+    // issue cursor (runs PER_PF pages ahead of the compute cursor)
+    int iss_p = p0, iss_it = __builtin_amdgcn_readfirstlane(find_item(p0));
+    auto issue_next = [&](RawPage& dst) {
+        while (item_off[iss_it + 1] <= iss_p) ++iss_it;
+        const int r = iss_it / qgroups;
+        const int blk = G.page_table[(size_t)r * G.max_blocks + (iss_p - item_off[iss_it])];
+        load_raw_page(keys, a.key_scales, __builtin_amdgcn_readfirstlane(blk), lane, dst);
+        ++iss_p;
+    };
+    RawPage ring[PER_PF];
+#pragma unroll
+    for (int d = 0; d < PER_PF; ++d)
+        if (p0 + d < p1) issue_next(ring[d]);
+
+    // compute cursor state: current item's queries
+    int cur_it = -1;
+    int r = 0, qs = 0, ql = 0, j0 = 0, nq = 0, L = 0;
+    i32x8 qf[NQ][HT];
+    float wv[NQ][HT][4];
+    auto load_item = [&](int it) {
+        cur_it = it;
+        r = it / qgroups;
+        const int qg = it % qgroups;
+        qs = G.qsl[r]; ql = G.qsl[r + 1] - qs; j0 = qg * NQ; nq = min(NQ, ql - j0); L = G.ctx[r];
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            const int t = qs + j0 + min(j, nq - 1);
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                const uint8_t* qp = (const uint8_t*)a.q + ((size_t)t * a.n_heads + 16 * ht + col) * IDX_D + 16 * g;
+                qf[j][ht] = join_i32x8(*(const u32x4*)qp, *(const u32x4*)(qp + 64));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) wv[j][ht][i] = a.w[(size_t)t * a.n_heads + 16 * ht + 4 * g + i];
+            }
+        }
+    };
+    uint8_t* pb = &pbuf[wave][0];
+    const int wt = lane >> 3, wu = lane & 7;
+    for (int base = p0; base < p1; base += PER_PF) {
+#pragma unroll
+        for (int sl = 0; sl < PER_PF; ++sl) {
+            const int p = base + sl;
+            if (p < p1) {
+                int it = cur_it < 0 ? find_item(p) : cur_it;
+                while (item_off[it + 1] <= p) ++it;
+                if (it != cur_it) load_item(__builtin_amdgcn_readfirstlane(it));
+                RawPage& cur = ring[sl];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const int t = 8 * c + wt;
+                    *(u32x4*)(pb + t * IDX_D + 16 * (wu ^ page_swz(t))) = cur.v[c];
+                }
+                i32x8 kf[4];
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    const int t = 16 * nt + col;
+                    const u32x4 lo = *(const u32x4*)(pb + t * IDX_D + 16 * (g ^ page_swz(t)));
+                    const u32x4 hi = *(const u32x4*)(pb + t * IDX_D + 16 * ((4 + g) ^ page_swz(t)));
+                    kf[nt] = join_i32x8(lo, hi);
+                }
+                const float ksc = cur.scale;
+                if (p + PER_PF < p1) issue_next(cur);
+                float ps[NQ];
+                page_scores<NQ, HT>(qf, wv, kf, ksc, lane, nq, ps);
+                const int pos = (p - item_off[cur_it]) * IDX_PAGE + lane;
+#pragma unroll
+                for (int j = 0; j < NQ; ++j) {
+                    const int n_j = L - ql + j0 + j + 1;
+                    if (j < nq && pos < n_j) a.scores[(size_t)(qs + j0 + j) * a.ld + pos] = ps[j];
+                }
+            }
         }
     }
 }
@@ -375,31 +413,20 @@ __global__ __launch_bounds__(256) void indexer_generic(IndexerArgs a) {
     const float sc = a.key_scales ? a.key_scales[row] : 1.f;
     const float score = sc * total;
     a.scores[(size_t)t * a.ld + s] = score;
-    if (a.hist) atomicAdd(a.hist + (size_t)t * HIST_BINS + (score_key(score) >> HIST_SHIFT), 1u);
 }
 
-#ifndef IDX_USE_DMA
-#define IDX_USE_DMA 1
-#endif
-
+// Generic path kernel above; launch policy below.
 template <int NQ, int HT>
 static hipError_t launch_fp8(const IndexerArgs& a, hipStream_t s) {
     const int qgroups = (a.g.max_q_len + NQ - 1) / NQ;
-    if (IDX_USE_DMA) {
-        const int chunk = 4 * DMA_PPW * IDX_PAGE;
-        dim3 grid((a.g.max_ctx + chunk - 1) / chunk, a.g.B * qgroups);
-        if (a.hist)
-            hipLaunchKernelGGL((indexer_fp8_dma<NQ, HT, true>), grid, dim3(IDX_THREADS), 0, s, a, qgroups);
-        else
-            hipLaunchKernelGGL((indexer_fp8_dma<NQ, HT, false>), grid, dim3(IDX_THREADS), 0, s, a, qgroups);
+    if (a.g.B * qgroups <= PER_MAX_ITEMS) {
+        hipLaunchKernelGGL((indexer_fp8_persistent<NQ, HT>), dim3(device_cu_count() * PER_WG_PER_CU),
+                           dim3(IDX_THREADS), 0, s, a, qgroups);
         return hipGetLastError();
     }
-    const int chunk_tokens = IDX_CHUNK_PAGES * IDX_PAGE;
-    dim3 grid((a.g.max_ctx + chunk_tokens - 1) / chunk_tokens, a.g.B * qgroups);
-    if (a.hist)
-        hipLaunchKernelGGL((indexer_fp8_mfma<NQ, HT, true>), grid, dim3(IDX_THREADS), 0, s, a, qgroups, chunk_tokens);
-    else
-        hipLaunchKernelGGL((indexer_fp8_mfma<NQ, HT, false>), grid, dim3(IDX_THREADS), 0, s, a, qgroups, chunk_tokens);
+    const int chunk = 4 * DMA_PPW * IDX_PAGE;
+    dim3 grid((a.g.max_ctx + chunk - 1) / chunk, a.g.B * qgroups);
+    hipLaunchKernelGGL((indexer_fp8_dma<NQ, HT>), grid, dim3(IDX_THREADS), 0, s, a, qgroups);
     return hipGetLastError();
 }
 

@@ -125,6 +125,20 @@ __device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t* total) 
     return x - v;
 }
 
+// Appends `flag` lanes with one atomic per wavefront; returns this lane's slot
+// (valid only where flag is set).
+__device__ __forceinline__ uint32_t wave_append(bool flag, uint32_t* counter) {
+    const unsigned long long mask = __ballot(flag);
+    if (mask == 0ull) return 0u;
+    const int lane = threadIdx.x & 63;
+    const int leader = __ffsll((long long)mask) - 1;
+    uint32_t base = 0u;
+    if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
+    base = __shfl(base, leader);
+    const unsigned long long below = lane ? (mask & ((1ull << lane) - 1ull)) : 0ull;
+    return base + (uint32_t)__popcll(below);
+}
+
 __global__ __launch_bounds__(TK_THREADS) void topk_filter(TopkArgs a) {
     const Geometry& G = a.g;
     const int t = blockIdx.y;
@@ -318,6 +332,260 @@ __global__ __launch_bounds__(RF_THREADS) void topk_refine(TopkArgs a) {
         written += seg_total;
         __syncthreads();
     }
+}
+
+
+// ---------------------------------------------------------------------------
+// One-kernel selection for rows of up to ROW_MAX_TOKENS scores: one 1024-thread
+// workgroup per row does everything in LDS.
+//   1. bucket boundaries from the row itself: min/max key of a strided sample
+//      give an offset and a shift so that the populated key range spreads over
+//      the 4096 buckets (keys outside the sample range clamp to the end
+//      buckets; the map stays monotonic).  Fixed top-bit buckets would pile
+//      most scores into a handful of buckets, and same-address LDS atomics
+//      serialize;
+//   2. histogram pass, then the threshold bucket b*;
+//   3. filter pass: winners above b* are marked in a bitmap over the row,
+//      members of b* become candidates (composite key: full score key, then
+//      the complemented index, so the lowest-index tie rule is in the order);
+//   4. the best K - count(> b*) candidates: bitonic sort in LDS when they fit,
+//      else an MSB-first radix select over the composite keys;
+//   5. ascending write-out from the bitmap.
+constexpr int ROW_THREADS = 1024;
+constexpr int ROW_MAX_TOKENS = 1 << 19;
+constexpr int ROW_CAND = 6144;
+constexpr int ROW_SORT = 4096;           // candidates sorted directly up to this many
+#ifndef TOPK_ROW_UNROLL
+#define TOPK_ROW_UNROLL 32
+#endif
+constexpr int ROW_UNROLL = TOPK_ROW_UNROLL;
+
+__device__ __forceinline__ uint64_t full_composite(uint32_t key, int s) {
+    return ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)s);
+}
+
+__global__ __launch_bounds__(ROW_THREADS) void topk_row(TopkArgs a) {
+    const Geometry& G = a.g;
+    const int t = blockIdx.x;
+    const int r = find_request(G.qsl, G.B, t);
+    const int n = visible_count(G.ctx, G.qsl, r, t);
+    const int K = a.k;
+    int32_t* out = a.indices + (size_t)t * K;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (n <= K) {
+        for (int i = tid; i < K; i += ROW_THREADS) out[i] = i < n ? i : -1;
+        return;
+    }
+    __shared__ uint32_t bitmap[ROW_MAX_TOKENS / 32];
+    __shared__ uint64_t cand[ROW_CAND];
+    __shared__ uint32_t hist[HIST_BINS];
+    __shared__ uint32_t wave_sums[ROW_THREADS / 64];
+    __shared__ uint32_t wave_mm[2][ROW_THREADS / 64];
+    __shared__ uint32_t st[8];
+    const float* row = a.scores + (size_t)t * a.ld;
+    const int words = (n + 31) / 32;
+    for (int i = tid; i < HIST_BINS; i += ROW_THREADS) hist[i] = 0u;
+    if (tid < 8) st[tid] = 0u;
+
+    // 1. key range of a strided sample -> bucket offset and shift
+    {
+        const long long idx = (long long)tid * n / ROW_THREADS;
+        const uint32_t k0 = score_key(row[idx]);
+        uint32_t mn = k0, mx = k0;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            mn = min(mn, (uint32_t)__shfl_xor((int)mn, off));
+            mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
+        }
+        if (lane == 0) { wave_mm[0][wave] = mn; wave_mm[1][wave] = mx; }
+    }
+    __syncthreads();
+    uint32_t lo = wave_mm[0][0], hi = wave_mm[1][0];
+    for (int w = 1; w < ROW_THREADS / 64; ++w) { lo = min(lo, wave_mm[0][w]); hi = max(hi, wave_mm[1][w]); }
+    int shift = 0;
+    while (shift < 32 && ((hi - lo) >> shift) >= (uint32_t)HIST_BINS) ++shift;
+    auto bucket_of = [&](uint32_t key) -> uint32_t {
+        if (key <= lo) return 0u;
+        const uint32_t b = (key - lo) >> shift;
+        return b < (uint32_t)HIST_BINS ? b : (uint32_t)HIST_BINS - 1u;
+    };
+
+    // 2. histogram pass
+    constexpr int U = ROW_UNROLL;
+    for (int base = 0; base < n; base += U * ROW_THREADS) {
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int s = base + u * ROW_THREADS + tid;
+            v[u] = s < n ? row[s] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (base + u * ROW_THREADS + tid < n) atomicAdd(&hist[bucket_of(score_key(v[u]))], 1u);
+    }
+    __syncthreads();
+    {   // threshold bucket: each thread owns 4 buckets, descending across threads
+        uint32_t c[4], sum = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { c[j] = hist[HIST_BINS - 1 - 4 * tid - j]; sum += c[j]; }
+        uint32_t wt;
+        const uint32_t wex = wave_excl_scan(sum, &wt);
+        if (lane == 0) wave_sums[wave] = wt;
+        __syncthreads();
+        uint32_t ex = wex;
+        for (int w = 0; w < wave; ++w) ex += wave_sums[w];
+        if (ex < (uint32_t)K && ex + sum >= (uint32_t)K) {
+            uint32_t cum = ex;
+            for (int j = 0; j < 4; ++j) {
+                if (cum + c[j] >= (uint32_t)K) { st[0] = HIST_BINS - 1 - 4 * tid - j; st[1] = cum; break; }
+                cum += c[j];
+            }
+        }
+        __syncthreads();
+    }
+    const uint32_t bucket = st[0], above = st[1];
+
+    // 3. filter pass.  The 64 consecutive scores of a wave at one step map to
+    // exactly two bitmap words, written whole from a ballot (every word of the
+    // row is written here, so the bitmap needs no clearing).
+    for (int base = 0; base < n; base += U * ROW_THREADS) {
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int s = base + u * ROW_THREADS + tid;
+            v[u] = s < n ? row[s] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int s0 = base + u * ROW_THREADS + wave * 64;   // first score of this wave's step
+            if (s0 < n) {
+                const int s = s0 + lane;
+                const uint32_t key = score_key(v[u]);
+                const uint32_t b = bucket_of(key);
+                const unsigned long long win = __ballot(s < n && b > bucket);
+                if (lane == 0) bitmap[s0 >> 5] = (uint32_t)win;
+                if (lane == 32 && s0 + 32 < n) bitmap[(s0 >> 5) + 1] = (uint32_t)(win >> 32);
+                const bool is_cand = s < n && b == bucket;
+                if (__ballot(is_cand)) {
+                    const uint32_t p = wave_append(is_cand, &st[2]);
+                    if (is_cand && p < (uint32_t)ROW_CAND) cand[p] = full_composite(key, s);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const uint32_t ncand = st[2];
+    const uint32_t need = (uint32_t)K - above;
+
+    // 4. the best `need` candidates
+    if (ncand <= (uint32_t)ROW_SORT) {
+        // descending bitonic sort of the candidates (zero padding sorts last)
+        int P = 1;
+        while (P < (int)ncand) P <<= 1;
+        for (int i = (int)ncand + tid; i < P; i += ROW_THREADS) cand[i] = 0ull;
+        __syncthreads();
+        for (int size = 2; size <= P; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                for (int i = tid; i < P / 2; i += ROW_THREADS) {
+                    const int l0 = 2 * i - (i & (stride - 1));
+                    const int l1 = l0 + stride;
+                    const bool desc = (l0 & size) == 0;
+                    const uint64_t x = cand[l0], y = cand[l1];
+                    if ((x < y) == desc) { cand[l0] = y; cand[l1] = x; }
+                }
+                __syncthreads();
+            }
+        }
+        for (int i = tid; i < (int)need; i += ROW_THREADS) {
+            const int sidx = composite_index(cand[i]);
+            atomicOr(&bitmap[sidx >> 5], 1u << (sidx & 31));
+        }
+    } else {
+        const bool in_lds = ncand <= (uint32_t)ROW_CAND;
+        const int scan_n = in_lds ? (int)ncand : n;
+        auto get = [&](int i, uint64_t& ck) -> bool {
+            if (in_lds) { ck = cand[i]; return true; }
+            const uint32_t key = score_key(row[i]);
+            if (bucket_of(key) != bucket) return false;
+            ck = full_composite(key, i);
+            return true;
+        };
+        uint32_t rem = need;
+        uint64_t prefix = 0;
+        int sh = 56;
+        for (;; sh -= 8) {
+            if (tid < 256) hist[tid] = 0u;
+            __syncthreads();
+            for (int i = tid; i < scan_n; i += ROW_THREADS) {
+                uint64_t ck;
+                if (get(i, ck) && (sh == 56 || (ck >> (sh + 8)) == prefix))
+                    atomicAdd(&hist[(ck >> sh) & 255u], 1u);
+            }
+            __syncthreads();
+            if (wave == 0) {
+                uint32_t c[4], sum = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) { c[j] = hist[255 - 4 * lane - j]; sum += c[j]; }
+                uint32_t tot;
+                const uint32_t excl = wave_excl_scan(sum, &tot);
+                if (excl < rem && excl + sum >= rem) {
+                    uint32_t cum = excl;
+                    for (int j = 0; j < 4; ++j) {
+                        if (cum + c[j] >= rem) {
+                            st[4] = (uint32_t)(255 - 4 * lane - j);
+                            st[5] = rem - cum;
+                            st[6] = c[j] == rem - cum ? 1u : 0u;
+                            break;
+                        }
+                        cum += c[j];
+                    }
+                }
+            }
+            __syncthreads();
+            const uint32_t d = st[4];
+            rem = st[5];
+            const bool done = st[6] != 0u || sh == 0;
+            prefix = (prefix << 8) | d;
+            __syncthreads();
+            if (done) break;
+        }
+        for (int i = tid; i < scan_n; i += ROW_THREADS) {
+            uint64_t ck;
+            if (get(i, ck) && (ck >> sh) >= prefix) {
+                const int sidx = composite_index(ck);
+                atomicOr(&bitmap[sidx >> 5], 1u << (sidx & 31));
+            }
+        }
+    }
+    __syncthreads();
+
+    // 5. ascending write-out
+    const int per = (words + ROW_THREADS - 1) / ROW_THREADS;
+    const int w0 = min(words, tid * per), w1 = min(words, w0 + per);
+    uint32_t nbits = 0;
+    for (int w = w0; w < w1; ++w) nbits += __popc(bitmap[w]);
+    uint32_t wtot;
+    const uint32_t wexcl = wave_excl_scan(nbits, &wtot);
+    if (lane == 0) wave_sums[wave] = wtot;
+    __syncthreads();
+    uint32_t pos = wexcl;
+    for (int w = 0; w < wave; ++w) pos += wave_sums[w];
+    for (int w = w0; w < w1; ++w) {
+        uint32_t bits = bitmap[w];
+        while (bits) {
+            const int b = __ffs(bits) - 1;
+            bits &= bits - 1u;
+            if (pos < (uint32_t)K) out[pos] = w * 32 + b;
+            ++pos;
+        }
+    }
+}
+
+bool topk_single_kernel(int max_ctx, int k) { return max_ctx <= ROW_MAX_TOKENS && k <= TOPK_MAX_K; }
+
+hipError_t launch_topk_row(const TopkArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(topk_row, dim3(a.g.T), dim3(ROW_THREADS), 0, s, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t s) {

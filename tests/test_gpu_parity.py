@@ -196,3 +196,28 @@ def test_band_is_rarely_used():
     for t in range(wl.total_q):
         total += check_selection(idx[t], oracle.query_scores(wl, t), wl.topk, band=BAND)
     assert total <= 4
+
+
+@pytest.mark.parametrize("dup", [False, True])
+def test_topk_rows_beyond_single_kernel(dup):
+    """Rows longer than 2^19 tokens take the histogram + threshold/filter/refine
+    path; same exact-set rule as above."""
+    lens = [600000, 530000, 5000]
+    bs = 64
+    maxb = (max(lens) + bs - 1) // bs
+    ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    qsl = torch.tensor([0, 1, 2, 3], dtype=torch.int32, device="cuda")
+    pt = torch.zeros((3, maxb), dtype=torch.int32, device="cuda")
+    batch = dsa.Batch(ctx, qsl, pt, bs, 1, max(lens))
+    rng = np.random.default_rng(9)
+    ld = maxb * bs
+    scores = np.zeros((3, ld), dtype=np.float32)
+    for t, n in enumerate(lens):
+        v = rng.standard_normal(n).astype(np.float32)
+        if dup:
+            v = np.round(v * 8).astype(np.float32) / 8
+        scores[t, :n] = v
+    idx = dsa.topk(batch, torch.from_numpy(scores).cuda(), 2048).cpu().numpy()
+    for t, n in enumerate(lens):
+        ref = oracle.topk(scores[t, :n].astype(np.float64), 2048)
+        assert sorted(ref.tolist()) == idx[t].tolist()
