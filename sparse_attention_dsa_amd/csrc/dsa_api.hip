@@ -29,6 +29,7 @@ Geometry geometry(const dsa_batch* b) {
     g.T = b->total_q;
     g.max_q_len = b->max_q_len;
     g.max_ctx = b->max_context_len;
+    g.q_uniform = (int64_t)b->total_q == (int64_t)b->num_requests * b->max_q_len ? b->max_q_len : 0;
     g.ctx = b->context_lens;
     g.qsl = b->query_start_loc;
     g.page_table = b->page_table;
@@ -38,14 +39,12 @@ Geometry geometry(const dsa_batch* b) {
 }
 
 // Workspace pieces (byte offsets from the base, each 256-aligned).
-struct TopkLayout { size_t hist, counters, cand, above_list, end; };
-TopkLayout topk_layout(size_t base, int T, int k) {
+struct TopkLayout { size_t bitmap, end; int64_t bitmap_ld; };
+TopkLayout topk_layout(size_t base, const dsa_batch* b) {
     TopkLayout l;
-    l.hist = base;
-    l.counters = align_up(l.hist + sizeof(uint32_t) * (size_t)T * HIST_BINS);
-    l.cand = align_up(l.counters + sizeof(TopkCounters) * (size_t)T);
-    l.above_list = align_up(l.cand + sizeof(int32_t) * (size_t)T * TOPK_CAND_CAP);
-    l.end = align_up(l.above_list + sizeof(int32_t) * (size_t)T * k);
+    l.bitmap_ld = round_up64(((int64_t)b->max_context_len + 31) / 32);
+    l.bitmap = base;
+    l.end = align_up(l.bitmap + sizeof(uint32_t) * (size_t)b->total_q * (size_t)l.bitmap_ld);
     return l;
 }
 
@@ -68,7 +67,7 @@ StepLayout step_layout(const dsa_batch* b, int k, int n_heads, bool fast_mla) {
     l.ld = round_up64(b->max_context_len);
     l.scores = 0;
     l.indices = align_up(sizeof(float) * (size_t)b->total_q * l.ld);
-    l.tk = topk_layout(align_up(l.indices + sizeof(int32_t) * (size_t)b->total_q * k), b->total_q, k);
+    l.tk = topk_layout(align_up(l.indices + sizeof(int32_t) * (size_t)b->total_q * k), b);
     l.ml = mla_layout(l.tk.end, b, k, n_heads, false, fast_mla);
     l.end = l.ml.end;
     return l;
@@ -76,14 +75,21 @@ StepLayout step_layout(const dsa_batch* b, int k, int n_heads, bool fast_mla) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH; }
 
-// Selection from materialised scores: one kernel per row when rows fit its
-// LDS bitmap, else histogram + threshold/filter/refine kernels.
-hipError_t run_topk(const TopkArgs& a, const TopkLayout& l, hipStream_t s) {
-    if (topk_single_kernel(a.g.max_ctx, a.k)) return launch_topk_row(a, s);
-    hipError_t e = launch_zero_u32(a.hist, (l.cand - l.hist) / sizeof(uint32_t), s);
-    if (e == hipSuccess) e = launch_topk_hist(a, s);
-    if (e == hipSuccess) e = launch_topk_select(a, s);
-    return e;
+TopkArgs topk_args(const dsa_batch* b, const float* scores, int64_t ld, int k, int32_t* indices, char* base,
+                   const TopkLayout& l) {
+    TopkArgs a;
+    a.g = geometry(b);
+    a.scores = scores; a.ld = ld; a.k = k; a.indices = indices;
+    a.bitmap = (uint32_t*)(base + l.bitmap);
+    a.bitmap_ld = l.bitmap_ld;
+    return a;
+}
+
+// Top-K grid limits: rows x chunk columns of 256-thread workgroups.
+constexpr int64_t TOPK_MAX_CONTEXT = (int64_t)65535 * TOPK_CHUNK;
+constexpr int32_t TOPK_MAX_ROWS = 1 << 24;
+bool topk_shape_ok(const dsa_batch* b, int k) {
+    return k <= TOPK_MAX_K && b->max_context_len <= TOPK_MAX_CONTEXT && b->total_q <= TOPK_MAX_ROWS;
 }
 
 int device_arch_ok() {
@@ -214,7 +220,7 @@ size_t dsa_workspace_size(int32_t op, const dsa_batch* b, int32_t k, int32_t n_h
     switch (op) {
     case DSA_OP_TOPK:
         if (k < 1 || k > TOPK_MAX_K) return 0;
-        return topk_layout(0, b->total_q, k).end;
+        return topk_layout(0, b).end;
     case DSA_OP_MLA_DECODE:
     case DSA_OP_MLA_PREFILL:
         if (k < 1 || n_heads < 1) return 0;
@@ -246,21 +252,13 @@ int dsa_indexer_scores(const dsa_batch* b, const dsa_index_cache* c, const void*
 int dsa_topk(const dsa_batch* b, const float* scores, int64_t ld, int32_t k, int32_t* indices,
              void* ws, size_t ws_bytes, dsa_stream_t stream) {
     if (!batch_ok(b) || !scores || !indices || k < 1 || ld < b->max_context_len) return DSA_ERR_INVALID_ARG;
-    if (k > TOPK_MAX_K) return DSA_ERR_UNSUPPORTED;
-    const TopkLayout l = topk_layout(0, b->total_q, k);
+    if (!topk_shape_ok(b, k)) return DSA_ERR_UNSUPPORTED;
+    const TopkLayout l = topk_layout(0, b);
     if (!ws || ws_bytes < l.end) return DSA_ERR_WORKSPACE;
     int st = check_device_cached();
     if (st != DSA_OK) return st;
-    hipStream_t s = (hipStream_t)stream;
-    char* base = (char*)ws;
-    TopkArgs a;
-    a.g = geometry(b);
-    a.scores = scores; a.ld = ld; a.k = k; a.indices = indices;
-    a.hist = (uint32_t*)(base + l.hist);
-    a.counters = (TopkCounters*)(base + l.counters);
-    a.cand = (int32_t*)(base + l.cand);
-    a.above_list = (int32_t*)(base + l.above_list);
-    return launch_status(run_topk(a, l, s));
+    const TopkArgs a = topk_args(b, scores, ld, k, indices, (char*)ws, l);
+    return launch_status(launch_topk(a, (hipStream_t)stream));
 }
 
 static int mla_entry(const dsa_batch* b, const dsa_latent_cache* c, const void* q, int32_t n_heads,
@@ -294,7 +292,7 @@ int dsa_decode_step(const dsa_batch* b, const dsa_index_cache* ic, const void* q
     int st = validate_indexer(b, ic, q_idx, w, n_heads_idx);
     if (st != DSA_OK) return st;
     if ((st = validate_mla(b, lc, q_mla, n_heads, k, out)) != DSA_OK) return st;
-    if (k > TOPK_MAX_K) return DSA_ERR_UNSUPPORTED;
+    if (!topk_shape_ok(b, k)) return DSA_ERR_UNSUPPORTED;
     const bool fast = mla_fast_path(lc->dtype, lc->d_latent, lc->d_rope, n_heads, b->block_size);
     const StepLayout l = step_layout(b, k, n_heads, fast);
     if (!ws || ws_bytes < l.end) return DSA_ERR_WORKSPACE;
@@ -304,20 +302,14 @@ int dsa_decode_step(const dsa_batch* b, const dsa_index_cache* ic, const void* q
     float* scores = (float*)(base + l.scores);
     int32_t* indices = indices_out ? indices_out : (int32_t*)(base + l.indices);
 
-    TopkArgs tk;
-    tk.g = geometry(b);
-    tk.scores = scores; tk.ld = l.ld; tk.k = k; tk.indices = indices;
-    tk.hist = (uint32_t*)(base + l.tk.hist);
-    tk.counters = (TopkCounters*)(base + l.tk.counters);
-    tk.cand = (int32_t*)(base + l.tk.cand);
-    tk.above_list = (int32_t*)(base + l.tk.above_list);
+    const TopkArgs tk = topk_args(b, scores, l.ld, k, indices, base, l.tk);
     IndexerArgs ia;
     ia.g = tk.g;
     ia.keys = ic->keys; ia.key_scales = ic->scales; ia.key_dtype = ic->dtype; ia.dim = ic->dim;
     ia.q = q_idx; ia.w = w; ia.n_heads = n_heads_idx;
     ia.scores = scores; ia.ld = l.ld;
     hipError_t e = launch_indexer(ia, s);
-    if (e == hipSuccess) e = run_topk(tk, l.tk, s);
+    if (e == hipSuccess) e = launch_topk(tk, s);
     if (e != hipSuccess) return DSA_ERR_LAUNCH;
     return run_mla(b, lc, q_mla, n_heads, indices, k, scale, out, lse, base, ws_bytes, l.tk.end, false, s);
 }

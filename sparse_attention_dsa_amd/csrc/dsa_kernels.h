@@ -14,24 +14,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-// Histogram of the top bits of the order-preserving score key, used to find
-// the bucket that holds the K-th largest score.
-constexpr int HIST_BITS = 12;
-constexpr int HIST_BINS = 1 << HIST_BITS;
-constexpr int HIST_SHIFT = 32 - HIST_BITS;
-
-// Candidates kept per query row for the exact refinement of the threshold
-// bucket; beyond this the refinement rescans the row's scores.
-constexpr int TOPK_CAND_CAP = 16384;
+// Largest supported K, and scores per workgroup of the top-K candidate pass.
 constexpr int TOPK_MAX_K = 4096;
-
-// Per-row top-K bookkeeping in the workspace.
-struct TopkCounters {
-    uint32_t above;           // tokens appended above the threshold bucket
-    uint32_t cand;            // tokens appended from the threshold bucket
-    uint32_t bucket;          // threshold bucket
-    uint32_t above_expected;  // histogram count above the threshold bucket
-};
+constexpr int TOPK_CHUNK = 8192;
 
 // ----------------------------------------------------------- conversions
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
@@ -104,11 +89,23 @@ __device__ __forceinline__ int visible_count(const int32_t* ctx, const int32_t* 
 // ------------------------------------------------------- launch helpers
 struct Geometry {
     int B, T, max_q_len, max_ctx;
+    int q_uniform;          // > 0: every request has exactly this many query rows
     const int32_t* ctx;
     const int32_t* qsl;
     const int32_t* page_table;
     int max_blocks, block_size;
 };
+
+// Visible-token count of query row t; a single load when the query rows are
+// spread uniformly over the requests.
+__device__ __forceinline__ int row_visible(const Geometry& g, int t) {
+    if (g.q_uniform > 0) {
+        const int r = t / g.q_uniform;
+        return g.ctx[r] - g.q_uniform + (t - r * g.q_uniform) + 1;
+    }
+    const int r = find_request(g.qsl, g.B, t);
+    return visible_count(g.ctx, g.qsl, r, t);
+}
 
 struct IndexerArgs {
     Geometry g;
@@ -122,10 +119,8 @@ struct TopkArgs {
     const float* scores; int64_t ld;
     int k;
     int32_t* indices;        // [T][k] result
-    int32_t* above_list;     // [T][k] tokens above the threshold bucket
-    uint32_t* hist;          // [T][HIST_BINS]
-    TopkCounters* counters;  // [T]
-    int32_t* cand;           // [T][TOPK_CAND_CAP]
+    uint32_t* bitmap;        // [T][bitmap_ld] candidate bitmap over each row
+    int64_t bitmap_ld;
 };
 
 struct MlaArgs {
@@ -143,14 +138,9 @@ struct MlaArgs {
 int device_cu_count();
 
 // Launchers (return hipError_t of the last launch).
-hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s);
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
-hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t s);
-hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s);
-// Whole selection in one kernel (no histogram input, no workspace) for rows
-// of up to 2^19 tokens.
-bool topk_single_kernel(int max_ctx, int k);
-hipError_t launch_topk_row(const TopkArgs& a, hipStream_t s);
+// Candidate pass then per-row selection.
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_mla(const MlaArgs& a, bool prefill, hipStream_t s);
 
 // Which MLA path serves these shapes, and how many splits it uses.

@@ -4,112 +4,77 @@
 // highest-scoring visible tokens, or every visible token when a query sees K
 // or fewer; equal scores go to the lower token index.
 //
-// Each score maps to an order-preserving 32-bit key.  Per query row:
-//   hist      (only when the indexer did not already build it) counts keys
-//             per bucket of their top 12 bits into a per-row histogram;
-//   threshold one workgroup per row finds the bucket b* holding the K-th
-//             largest key;
-//   filter    streams the row in 4096-score chunks, every load issued up
-//             front: tokens above b* are selected outright, tokens inside b*
-//             become candidates; each wave reserves its output slots with a
-//             single atomic after a lane prefix scan;
-//   refine    one workgroup per row loads the candidates' composite keys
-//             (low 20 key bits, ~index) into LDS -- unique per token, so the
-//             lowest-index tie rule is part of the order -- and radix-selects
-//             the remaining ones MSB first (digit found by a wave-parallel
-//             suffix scan); the K winners are marked in an LDS bitmap over
-//             the row (segment by segment for very long rows) and written
-//             out in ascending order by a block scan of the bitmap's
-//             popcounts.
+// Scores are ranked by an order-preserving 32-bit key; the composite key
+// (score key, then the complemented token index) is unique per token and puts
+// the lower index first among equal scores, so "the K largest composite keys"
+// is exactly the selection the rule asks for.
+//
+// Two kernels, one streaming pass over the scores:
+//   candidate pass   rows longer than SEL_LIST are cut into TOPK_CHUNK-score
+//                    chunks, one 256-thread workgroup each.  Every workgroup of
+//                    a row draws the same strided sample of the row and takes a
+//                    key bound X that, for any ordering that is not adversarial
+//                    to the stride, has well over K scores of the row above it
+//                    (the sample rank sits six binomial standard deviations
+//                    past the expected rank of the K-th score).  It then writes
+//                    its chunk's bitmap of "score >= X" as whole words, one
+//                    ballot per 64 scores: one compare per score, no atomics.
+//   selection        one 1024-thread workgroup per row compacts the bitmap into
+//                    an LDS list of composite keys in ascending token order
+//                    (short rows load all their scores instead).  If the list
+//                    holds at least K entries it contains the whole top K; the
+//                    K-th largest composite T* is found with a histogram over
+//                    buckets spread across the list's key range, then an exact
+//                    pass over the threshold bucket.  The entries >= T* are
+//                    written out in list order.  When the sample bound fails
+//                    (fewer than K candidates, or more than the list holds) the
+//                    same selection runs over the whole row from memory.
 #include "dsa_kernels.h"
 
 namespace dsa {
 
-constexpr int TK_THREADS = 256;
-constexpr int TK_CHUNK = 16384;          // scores per hist workgroup
-constexpr int FL_PER_THREAD = 16;
-constexpr int FL_CHUNK = TK_THREADS * FL_PER_THREAD;   // scores per filter workgroup
-constexpr int RF_THREADS = 1024;
-constexpr int RF_LDS_CAND = 6144;        // candidates cached in LDS
-constexpr int RF_BITMAP_TOKENS = 1 << 19;  // rows up to this length use the bitmap writer
+constexpr int TK_THREADS = 256;                        // candidate pass
+constexpr int TK_PER_LANE = TOPK_CHUNK / TK_THREADS;   // scores per lane
+constexpr int TK_WAVE_SPAN = 64 * TK_PER_LANE;         // contiguous scores per wave
+constexpr int TK_SAMPLE = 1024;                        // sample per 128K scores of row
+constexpr int TK_SAMPLE_MAX = 4096;
+constexpr int TK_SAMPLE_BINS = 256;
+static_assert(TK_PER_LANE == 32, "each lane ends up holding one bitmap word of its wave");
 
-__global__ void zero_u32(uint32_t* __restrict__ p, size_t n) {
-    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    for (; i < n; i += stride) p[i] = 0u;
+constexpr int SEL_THREADS = 1024;                      // selection
+constexpr int SEL_WAVES = SEL_THREADS / 64;
+constexpr int SEL_LIST = 12288;                        // candidates held in LDS
+constexpr int SEL_BINS = 4096;
+constexpr int SEL_MEMBERS = 4096;                      // threshold-bucket members sorted directly
+static_assert(SEL_LIST > TOPK_MAX_K, "short rows go straight to the list");
+static_assert(SEL_BINS == 4 * SEL_THREADS, "four buckets per thread in the threshold scan");
+
+// Order-preserving map's inverse for ">=" tests on floats: for finite v,
+// score_key(v) >= x  <=>  v >= key_floor(x)  (x a key of a finite float or
+// the unused key below +0; keys at or below that of -inf admit everything).
+__device__ __forceinline__ float key_floor(uint32_t x) {
+    if (x <= 0x007FFFFFu) return -__builtin_inff();
+    if (x >= 0x80000000u) return __uint_as_float(x & 0x7FFFFFFFu);
+    return __uint_as_float(~x);
 }
 
-hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s) {
-    if (n == 0) return hipSuccess;
-    const size_t blocks = min((n + 255) / 256, (size_t)4096);
-    hipLaunchKernelGGL(zero_u32, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
-    return hipGetLastError();
+__device__ __forceinline__ uint64_t composite(uint32_t key, int s) {
+    return ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)s);
 }
+__device__ __forceinline__ int composite_index(uint64_t ck) { return (int)(~(uint32_t)(ck & 0xFFFFFFFFull)); }
+__device__ __forceinline__ uint32_t composite_key(uint64_t ck) { return (uint32_t)(ck >> 32); }
 
-__global__ __launch_bounds__(TK_THREADS) void topk_hist(TopkArgs a) {
-    const Geometry& G = a.g;
-    const int t = blockIdx.y;
-    const int r = find_request(G.qsl, G.B, t);
-    const int n = visible_count(G.ctx, G.qsl, r, t);
-    if (n <= a.k) return;
-    const int c0 = blockIdx.x * TK_CHUNK;
-    if (c0 >= n) return;
-    const int c1 = min(n, c0 + TK_CHUNK);
-    __shared__ uint32_t h[HIST_BINS];
-    for (int i = threadIdx.x; i < HIST_BINS; i += TK_THREADS) h[i] = 0u;
-    __syncthreads();
-    const float* row = a.scores + (size_t)t * a.ld;
-    for (int s = c0 + threadIdx.x; s < c1; s += TK_THREADS)
-        atomicAdd(&h[score_key(row[s]) >> HIST_SHIFT], 1u);
-    __syncthreads();
-    uint32_t* gh = a.hist + (size_t)t * HIST_BINS;
-    for (int i = threadIdx.x; i < HIST_BINS; i += TK_THREADS)
-        if (h[i]) atomicAdd(gh + i, h[i]);
+// Bucket of key x in a map of `bins` buckets starting at lo, 2^shift keys
+// wide; keys outside clamp to the end buckets (monotonic in x).
+__device__ __forceinline__ uint32_t bucket_of(uint32_t x, uint32_t lo, uint32_t shift, uint32_t bins) {
+    if (x <= lo) return 0u;
+    const uint32_t b = (x - lo) >> shift;
+    return b < bins ? b : bins - 1u;
 }
-
-// Threshold bucket of each row: the bucket b with count(> b) < k <= count(>= b).
-__global__ __launch_bounds__(TK_THREADS) void topk_threshold(TopkArgs a) {
-    static_assert(HIST_BINS == 16 * TK_THREADS, "bucket split");
-    const Geometry& G = a.g;
-    const int t = blockIdx.x;
-    const int r = find_request(G.qsl, G.B, t);
-    const int n = visible_count(G.ctx, G.qsl, r, t);
-    if (n <= a.k) return;
-    const uint32_t k = (uint32_t)a.k;
-    __shared__ uint32_t sh_scan[TK_THREADS];
-    const int tid = threadIdx.x;
-    const int hi = HIST_BINS - 16 * tid;   // this thread covers [hi-16, hi), highest first
-    const u32x4* src = (const u32x4*)(a.hist + (size_t)t * HIST_BINS + hi - 16);
-    uint32_t c[16];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const u32x4 x = src[v];
-        c[4 * v] = x[0]; c[4 * v + 1] = x[1]; c[4 * v + 2] = x[2]; c[4 * v + 3] = x[3];
-    }
-    uint32_t sum = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sum += c[i];
-    sh_scan[tid] = sum;
-    __syncthreads();
-    for (int off = 1; off < TK_THREADS; off <<= 1) {   // inclusive scan, descending buckets
-        const uint32_t v = tid >= off ? sh_scan[tid - off] : 0u;
-        __syncthreads();
-        sh_scan[tid] += v;
-        __syncthreads();
-    }
-    const uint32_t incl = sh_scan[tid], excl = incl - sum;
-    if (excl < k && incl >= k) {
-        uint32_t cum = excl;
-        for (int i = 15; i >= 0; --i) {
-            if (cum + c[i] >= k) {
-                TopkCounters* cnt = a.counters + t;
-                cnt->bucket = (uint32_t)(hi - 16 + i);
-                cnt->above_expected = cum;
-                break;
-            }
-            cum += c[i];
-        }
-    }
+__device__ __forceinline__ uint32_t range_shift(uint32_t lo, uint32_t hi, uint32_t bins) {
+    uint32_t sh = 0;
+    while (((hi - lo) >> sh) >= bins) ++sh;
+    return sh;
 }
 
 // Exclusive prefix sum over the 64 lanes of a wave; *total gets the wave sum.
@@ -125,483 +90,381 @@ __device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t* total) 
     return x - v;
 }
 
-// Appends `flag` lanes with one atomic per wavefront; returns this lane's slot
-// (valid only where flag is set).
-__device__ __forceinline__ uint32_t wave_append(bool flag, uint32_t* counter) {
-    const unsigned long long mask = __ballot(flag);
-    if (mask == 0ull) return 0u;
+// Exclusive prefix sum over the workgroup (wsum: one slot per wave).
+template <int WAVES>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t wt;
+    const uint32_t wex = wave_excl_scan(v, &wt);
+    if (lane == 0) wsum[wave] = wt;
+    __syncthreads();
+    uint32_t ex = wex, tot = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+        const uint32_t x = wsum[w];
+        ex += w < wave ? x : 0u;
+        tot += x;
+    }
+    __syncthreads();
+    *total = tot;
+    return ex;
+}
+
+// LDS counter increment; one atomic per wave when all active lanes share the
+// bucket (rows of equal scores would otherwise serialize on one address).
+__device__ __forceinline__ void lds_count(uint32_t* h, uint32_t bin, bool active) {
+    const unsigned long long act = __ballot(active);
+    if (act == 0ull) return;
     const int lane = threadIdx.x & 63;
-    const int leader = __ffsll((long long)mask) - 1;
-    uint32_t base = 0u;
-    if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
-    base = __shfl(base, leader);
-    const unsigned long long below = lane ? (mask & ((1ull << lane) - 1ull)) : 0ull;
-    return base + (uint32_t)__popcll(below);
-}
-
-__global__ __launch_bounds__(TK_THREADS) void topk_filter(TopkArgs a) {
-    const Geometry& G = a.g;
-    const int t = blockIdx.y;
-    const int r = find_request(G.qsl, G.B, t);
-    const int n = visible_count(G.ctx, G.qsl, r, t);
-    if (n <= a.k) return;
-    const int c0 = blockIdx.x * FL_CHUNK;
-    if (c0 >= n) return;
-    const int c1 = min(n, c0 + FL_CHUNK);
-    TopkCounters* cnt = a.counters + t;
-    const uint32_t bucket = cnt->bucket;
-    const float* row = a.scores + (size_t)t * a.ld;
-    const int lane = threadIdx.x & 63;
-
-    // All loads first (coalesced: consecutive lanes, consecutive scores).
-    float v[FL_PER_THREAD];
-#pragma unroll
-    for (int j = 0; j < FL_PER_THREAD; ++j) {
-        const int s = c0 + j * TK_THREADS + threadIdx.x;
-        v[j] = s < c1 ? row[s] : 0.f;
-    }
-    uint32_t sel_mask = 0u, cand_mask = 0u;
-#pragma unroll
-    for (int j = 0; j < FL_PER_THREAD; ++j) {
-        const int s = c0 + j * TK_THREADS + threadIdx.x;
-        const uint32_t b = score_key(v[j]) >> HIST_SHIFT;
-        if (s < c1 && b > bucket) sel_mask |= 1u << j;
-        if (s < c1 && b == bucket) cand_mask |= 1u << j;
-    }
-    uint32_t sel_total, cand_total;
-    const uint32_t sel_off = wave_excl_scan(__popc(sel_mask), &sel_total);
-    const uint32_t cand_off = wave_excl_scan(__popc(cand_mask), &cand_total);
-    uint32_t sel_base = 0u, cand_base = 0u;
-    if (lane == 0) {
-        if (sel_total) sel_base = atomicAdd(&cnt->above, sel_total);
-        if (cand_total) cand_base = atomicAdd(&cnt->cand, cand_total);
-    }
-    sel_base = __shfl(sel_base, 0) + sel_off;
-    cand_base = __shfl(cand_base, 0) + cand_off;
-    int32_t* sel = a.above_list + (size_t)t * a.k;
-    int32_t* cand = a.cand + (size_t)t * TOPK_CAND_CAP;
-#pragma unroll
-    for (int j = 0; j < FL_PER_THREAD; ++j) {
-        const int s = c0 + j * TK_THREADS + threadIdx.x;
-        if (sel_mask & (1u << j)) {
-            if (sel_base < (uint32_t)a.k) sel[sel_base] = s;
-            ++sel_base;
-        }
-        if (cand_mask & (1u << j)) {
-            if (cand_base < (uint32_t)TOPK_CAND_CAP) cand[cand_base] = s;
-            ++cand_base;
-        }
+    const int first = __ffsll((long long)act) - 1;
+    const uint32_t b0 = (uint32_t)__shfl((int)bin, first);
+    if (__ballot(active && bin == b0) == act) {
+        if (lane == first) atomicAdd(&h[b0], (uint32_t)__popcll(act));
+    } else if (active) {
+        atomicAdd(&h[bin], 1u);
     }
 }
-
-// Composite selection key of a threshold-bucket token: the 20 key bits below
-// the bucket bits, then the complemented index (so lower index ranks higher).
-__device__ __forceinline__ uint64_t composite(uint32_t key, int s) {
-    return ((uint64_t)(key & ((1u << HIST_SHIFT) - 1u)) << 32) | (uint64_t)(~(uint32_t)s);
-}
-
-__device__ __forceinline__ int composite_index(uint64_t ck) {
-    return (int)(~(uint32_t)(ck & 0xFFFFFFFFull));
-}
-
-__global__ __launch_bounds__(RF_THREADS) void topk_refine(TopkArgs a) {
-    const Geometry& G = a.g;
-    const int t = blockIdx.x;
-    const int r = find_request(G.qsl, G.B, t);
-    const int n = visible_count(G.ctx, G.qsl, r, t);
-    const int K = a.k;
-    int32_t* out = a.indices + (size_t)t * K;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (n <= K) {      // dense: every visible token, in order
-        for (int i = tid; i < K; i += RF_THREADS) out[i] = i < n ? i : -1;
-        return;
-    }
-    __shared__ uint64_t ck_lds[RF_LDS_CAND];
-    __shared__ uint32_t bitmap[RF_BITMAP_TOKENS / 32];
-    __shared__ uint32_t h256[256];
-    __shared__ uint32_t sh_state[4];
-    __shared__ uint32_t wave_sums[RF_THREADS / 64];
-    if (tid < 4) sh_state[tid] = 0u;
-    const TopkCounters* cnt = a.counters + t;
-    const uint32_t above = min(cnt->above, (uint32_t)K), ncand = cnt->cand;
-    const uint32_t bucket = cnt->bucket;
-    const float* row = a.scores + (size_t)t * a.ld;
-    const int32_t* cand = a.cand + (size_t)t * TOPK_CAND_CAP;
-    const int32_t* above_list = a.above_list + (size_t)t * K;
-    // Candidate source: LDS copy, the global candidate list, or a full rescan.
-    const int mode = ncand <= (uint32_t)RF_LDS_CAND ? 0 : (ncand <= (uint32_t)TOPK_CAND_CAP ? 1 : 2);
-    const int scan_n = mode == 2 ? n : (int)ncand;
-    if (mode == 0)
-        for (int i = tid; i < scan_n; i += RF_THREADS) {
-            const int s = cand[i];
-            ck_lds[i] = composite(score_key(row[s]), s);
-        }
-    // fetch candidate i; false if it is not in the threshold bucket (rescan mode)
-    auto get = [&](int i, uint64_t& ck) -> bool {
-        if (mode == 0) { ck = ck_lds[i]; return true; }
-        const int s = mode == 1 ? cand[i] : i;
-        const uint32_t key = score_key(row[s]);
-        if (mode == 2 && (key >> HIST_SHIFT) != bucket) return false;
-        ck = composite(key, s);
-        return true;
-    };
-
-    // MSB-first radix select of the `need`-th largest composite key.
-    uint32_t need = (uint32_t)K - above;
-    uint64_t prefix = 0;
-    int shift = 48;
-    for (;; shift -= 8) {
-        if (tid < 256) h256[tid] = 0u;
-        __syncthreads();
-        for (int i = tid; i < scan_n; i += RF_THREADS) {
-            uint64_t ck;
-            if (get(i, ck) && (ck >> (shift + 8)) == prefix) atomicAdd(&h256[(ck >> shift) & 255u], 1u);
-        }
-        __syncthreads();
-        if (wave == 0) {   // digit with count(> d) < need <= count(>= d); lane l holds 255-4l .. 252-4l
-            uint32_t c[4], sum = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) { c[j] = h256[255 - 4 * lane - j]; sum += c[j]; }
-            uint32_t tot;
-            const uint32_t excl = wave_excl_scan(sum, &tot);
-            if (excl < need && excl + sum >= need) {
-                uint32_t cum = excl;
-                for (int j = 0; j < 4; ++j) {
-                    if (cum + c[j] >= need) {
-                        sh_state[0] = (uint32_t)(255 - 4 * lane - j);
-                        sh_state[1] = need - cum;
-                        sh_state[2] = c[j] == need - cum ? 1u : 0u;
-                        break;
-                    }
-                    cum += c[j];
-                }
-            }
-        }
-        __syncthreads();
-        const uint32_t d = sh_state[0];
-        need = sh_state[1];
-        const bool done = sh_state[2] != 0u || shift == 0;
-        prefix = (prefix << 8) | d;
-        __syncthreads();
-        if (done) break;
-    }
-
-    // Mark the winners in a bitmap over one segment of the row at a time and
-    // write them in ascending order (block scan of per-thread popcounts).
-    uint32_t written = 0;
-    for (int seg0 = 0; seg0 < n; seg0 += RF_BITMAP_TOKENS) {
-        const int seg1 = min(n, seg0 + RF_BITMAP_TOKENS);
-        const int words = (seg1 - seg0 + 31) / 32;
-        for (int i = tid; i < words; i += RF_THREADS) bitmap[i] = 0u;
-        __syncthreads();
-        for (int i = tid; i < (int)above; i += RF_THREADS) {
-            const int s = above_list[i] - seg0;
-            if (s >= 0 && s < seg1 - seg0) atomicOr(&bitmap[s >> 5], 1u << (s & 31));
-        }
-        for (int i = tid; i < scan_n; i += RF_THREADS) {
-            uint64_t ck;
-            if (get(i, ck) && (ck >> shift) >= prefix) {
-                const int s = composite_index(ck) - seg0;
-                if (s >= 0 && s < seg1 - seg0) atomicOr(&bitmap[s >> 5], 1u << (s & 31));
-            }
-        }
-        __syncthreads();
-        const int per = (words + RF_THREADS - 1) / RF_THREADS;
-        const int w0 = min(words, tid * per), w1 = min(words, w0 + per);
-        uint32_t nbits = 0;
-        for (int w = w0; w < w1; ++w) nbits += __popc(bitmap[w]);
-        uint32_t wtot;
-        const uint32_t wexcl = wave_excl_scan(nbits, &wtot);
-        if (lane == 0) wave_sums[wave] = wtot;
-        __syncthreads();
-        uint32_t base = written, seg_total = 0;
-        for (int w = 0; w < RF_THREADS / 64; ++w) {
-            if (w < wave) base += wave_sums[w];
-            seg_total += wave_sums[w];
-        }
-        uint32_t pos = base + wexcl;
-        for (int w = w0; w < w1; ++w) {
-            uint32_t bits = bitmap[w];
-            while (bits) {
-                const int b = __ffs(bits) - 1;
-                bits &= bits - 1u;
-                if (pos < (uint32_t)K) out[pos] = seg0 + w * 32 + b;
-                ++pos;
-            }
-        }
-        written += seg_total;
-        __syncthreads();
-    }
-}
-
 
 // ---------------------------------------------------------------------------
-// One-kernel selection for rows of up to ROW_MAX_TOKENS scores: one 1024-thread
-// workgroup per row does everything in LDS.
-//   1. bucket boundaries from the row itself: min/max key of a strided sample
-//      give an offset and a shift so that the populated key range spreads over
-//      the 4096 buckets (keys outside the sample range clamp to the end
-//      buckets; the map stays monotonic).  Fixed top-bit buckets would pile
-//      most scores into a handful of buckets, and same-address LDS atomics
-//      serialize;
-//   2. histogram pass, then the threshold bucket b*;
-//   3. filter pass: winners above b* are marked in a bitmap over the row,
-//      members of b* become candidates (composite key: full score key, then
-//      the complemented index, so the lowest-index tie rule is in the order);
-//   4. the best K - count(> b*) candidates: bitonic sort in LDS when they fit,
-//      else an MSB-first radix select over the composite keys;
-//   5. ascending write-out from the bitmap.
-constexpr int ROW_THREADS = 1024;
-constexpr int ROW_MAX_TOKENS = 1 << 19;
-constexpr int ROW_CAND = 6144;
-constexpr int ROW_SORT = 4096;           // candidates sorted directly up to this many
-#ifndef TOPK_ROW_UNROLL
-#define TOPK_ROW_UNROLL 32
-#endif
-constexpr int ROW_UNROLL = TOPK_ROW_UNROLL;
-
-__device__ __forceinline__ uint64_t full_composite(uint32_t key, int s) {
-    return ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)s);
-}
-
-__global__ __launch_bounds__(ROW_THREADS) void topk_row(TopkArgs a) {
-    const Geometry& G = a.g;
-    const int t = blockIdx.x;
-    const int r = find_request(G.qsl, G.B, t);
-    const int n = visible_count(G.ctx, G.qsl, r, t);
+// Candidate pass.
+__global__ __launch_bounds__(TK_THREADS) void topk_candidates(TopkArgs a) {
+    const int t = blockIdx.x, c = blockIdx.y;
+    const int n = row_visible(a.g, t);
+    const int c0 = c * TOPK_CHUNK;
+    if (n <= SEL_LIST || c0 >= n) return;
     const int K = a.k;
-    int32_t* out = a.indices + (size_t)t * K;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (n <= K) {
-        for (int i = tid; i < K; i += ROW_THREADS) out[i] = i < n ? i : -1;
-        return;
-    }
-    __shared__ uint32_t bitmap[ROW_MAX_TOKENS / 32];
-    __shared__ uint64_t cand[ROW_CAND];
-    __shared__ uint32_t hist[HIST_BINS];
-    __shared__ uint32_t wave_sums[ROW_THREADS / 64];
-    __shared__ uint32_t wave_mm[2][ROW_THREADS / 64];
-    __shared__ uint32_t st[8];
     const float* row = a.scores + (size_t)t * a.ld;
-    const int words = (n + 31) / 32;
-    for (int i = tid; i < HIST_BINS; i += ROW_THREADS) hist[i] = 0u;
-    if (tid < 8) st[tid] = 0u;
+    __shared__ uint32_t h[TK_SAMPLE_BINS];
+    __shared__ uint32_t red[2][TK_THREADS / 64];
+    __shared__ uint32_t bound;
 
-    // 1. key range of a strided sample -> bucket offset and shift
-    {
-        const long long idx = (long long)tid * n / ROW_THREADS;
-        const uint32_t k0 = score_key(row[idx]);
-        uint32_t mn = k0, mx = k0;
+    // the row's sample (identical in every chunk of the row), then the chunk;
+    // positions past the row read as NaN, which fails every ">=" test
+    const int m = TK_SAMPLE * min(TK_SAMPLE_MAX / TK_SAMPLE, (n + 131071) / 131072);
+    const int ns = m / TK_THREADS;
+    float smp[TK_SAMPLE_MAX / TK_THREADS];
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            mn = min(mn, (uint32_t)__shfl_xor((int)mn, off));
-            mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
-        }
-        if (lane == 0) { wave_mm[0][wave] = mn; wave_mm[1][wave] = mx; }
+    for (int i = 0; i < TK_SAMPLE_MAX / TK_THREADS; ++i)
+        if (i < ns) smp[i] = row[(int)((long long)(tid + i * TK_THREADS) * n / m)];
+    const int w0 = c0 + wave * TK_WAVE_SPAN;
+    float v[TK_PER_LANE];
+#pragma unroll
+    for (int j = 0; j < TK_PER_LANE; ++j) {
+        const int s = w0 + j * 64 + lane;
+        v[j] = s < n ? row[s] : __builtin_nanf("");
     }
-    __syncthreads();
-    uint32_t lo = wave_mm[0][0], hi = wave_mm[1][0];
-    for (int w = 1; w < ROW_THREADS / 64; ++w) { lo = min(lo, wave_mm[0][w]); hi = max(hi, wave_mm[1][w]); }
-    int shift = 0;
-    while (shift < 32 && ((hi - lo) >> shift) >= (uint32_t)HIST_BINS) ++shift;
-    auto bucket_of = [&](uint32_t key) -> uint32_t {
-        if (key <= lo) return 0u;
-        const uint32_t b = (key - lo) >> shift;
-        return b < (uint32_t)HIST_BINS ? b : (uint32_t)HIST_BINS - 1u;
-    };
-
-    // 2. histogram pass
-    constexpr int U = ROW_UNROLL;
-    for (int base = 0; base < n; base += U * ROW_THREADS) {
-        float v[U];
+    h[tid] = 0u;
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int s = base + u * ROW_THREADS + tid;
-            v[u] = s < n ? row[s] : 0.f;
+    for (int i = 0; i < TK_SAMPLE_MAX / TK_THREADS; ++i)
+        if (i < ns) {
+            const uint32_t k = score_key(smp[i]);
+            mn = min(mn, k);
+            mx = max(mx, k);
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (base + u * ROW_THREADS + tid < n) atomicAdd(&hist[bucket_of(score_key(v[u]))], 1u);
+    for (int off = 32; off > 0; off >>= 1) {
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, off));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
     }
+    if (lane == 0) { red[0][wave] = mn; red[1][wave] = mx; }
     __syncthreads();
-    {   // threshold bucket: each thread owns 4 buckets, descending across threads
-        uint32_t c[4], sum = 0;
+    uint32_t lo = red[0][0], hi = red[1][0];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) { c[j] = hist[HIST_BINS - 1 - 4 * tid - j]; sum += c[j]; }
-        uint32_t wt;
-        const uint32_t wex = wave_excl_scan(sum, &wt);
-        if (lane == 0) wave_sums[wave] = wt;
-        __syncthreads();
-        uint32_t ex = wex;
-        for (int w = 0; w < wave; ++w) ex += wave_sums[w];
-        if (ex < (uint32_t)K && ex + sum >= (uint32_t)K) {
+    for (int w = 1; w < TK_THREADS / 64; ++w) { lo = min(lo, red[0][w]); hi = max(hi, red[1][w]); }
+    const uint32_t sh = range_shift(lo, hi, TK_SAMPLE_BINS);
+#pragma unroll
+    for (int i = 0; i < TK_SAMPLE_MAX / TK_THREADS; ++i)
+        if (i < ns) atomicAdd(&h[bucket_of(score_key(smp[i]), lo, sh, TK_SAMPLE_BINS)], 1u);
+    __syncthreads();
+    // Sample rank r: the expected rank of the K-th score plus six standard
+    // deviations of a binomial count, plus a margin.  X = lower key bound of the
+    // highest bucket whose cumulative count (from the top) reaches r.
+    if (wave == 0) {
+        const float q = (float)K / (float)n, mq = (float)m * q;
+        const uint32_t r = (uint32_t)ceilf(mq + 6.f * sqrtf(mq * (1.f - q))) + 8u;
+        uint32_t c4[4], sum = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { c4[j] = h[TK_SAMPLE_BINS - 1 - 4 * lane - j]; sum += c4[j]; }
+        uint32_t tot;
+        const uint32_t ex = wave_excl_scan(sum, &tot);
+        if (lane == 0 && tot < r) bound = 0u;   // the sample never reaches r: take everything
+        if (ex < r && ex + sum >= r) {
             uint32_t cum = ex;
             for (int j = 0; j < 4; ++j) {
-                if (cum + c[j] >= (uint32_t)K) { st[0] = HIST_BINS - 1 - 4 * tid - j; st[1] = cum; break; }
-                cum += c[j];
-            }
-        }
-        __syncthreads();
-    }
-    const uint32_t bucket = st[0], above = st[1];
-
-    // 3. filter pass.  The 64 consecutive scores of a wave at one step map to
-    // exactly two bitmap words, written whole from a ballot (every word of the
-    // row is written here, so the bitmap needs no clearing).
-    for (int base = 0; base < n; base += U * ROW_THREADS) {
-        float v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int s = base + u * ROW_THREADS + tid;
-            v[u] = s < n ? row[s] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int s0 = base + u * ROW_THREADS + wave * 64;   // first score of this wave's step
-            if (s0 < n) {
-                const int s = s0 + lane;
-                const uint32_t key = score_key(v[u]);
-                const uint32_t b = bucket_of(key);
-                const unsigned long long win = __ballot(s < n && b > bucket);
-                if (lane == 0) bitmap[s0 >> 5] = (uint32_t)win;
-                if (lane == 32 && s0 + 32 < n) bitmap[(s0 >> 5) + 1] = (uint32_t)(win >> 32);
-                const bool is_cand = s < n && b == bucket;
-                if (__ballot(is_cand)) {
-                    const uint32_t p = wave_append(is_cand, &st[2]);
-                    if (is_cand && p < (uint32_t)ROW_CAND) cand[p] = full_composite(key, s);
+                cum += c4[j];
+                if (cum >= r) {
+                    const uint32_t b = (uint32_t)(TK_SAMPLE_BINS - 1 - 4 * lane - j);
+                    bound = b == 0u ? 0u : lo + (b << sh);
+                    break;
                 }
             }
         }
     }
     __syncthreads();
-    const uint32_t ncand = st[2];
-    const uint32_t need = (uint32_t)K - above;
+    const float xf = key_floor(bound);
 
-    // 4. the best `need` candidates
-    if (ncand <= (uint32_t)ROW_SORT) {
-        // descending bitonic sort of the candidates (zero padding sorts last)
+    // Step j covers scores w0 + 64j .. +63: bitmap words 2j and 2j+1 of this
+    // wave, which end up in lanes 2j and 2j+1.
+    uint32_t word = 0u;
+#pragma unroll
+    for (int j = 0; j < TK_PER_LANE; ++j) {
+        const unsigned long long mk = __ballot(v[j] >= xf);
+        if (lane == 2 * j) word = (uint32_t)mk;
+        if (lane == 2 * j + 1) word = (uint32_t)(mk >> 32);
+    }
+    if (w0 + 32 * lane < n) a.bitmap[(size_t)t * a.bitmap_ld + (w0 >> 5) + lane] = word;
+}
+
+// ---------------------------------------------------------------------------
+// Selection.
+struct SelShared {
+    uint64_t list[SEL_LIST];
+    union {
+        uint32_t hist[SEL_BINS];
+        uint64_t members[SEL_MEMBERS];
+    } r;
+    uint32_t wsum[SEL_WAVES];
+    uint32_t red[2][SEL_WAVES];
+    uint32_t st[8];
+};
+
+// The K-th largest composite key over source entries i < count (get(i, ck)
+// fetches entry i); count >= K.  Called by the whole workgroup.
+template <class Get>
+__device__ uint64_t kth_composite(int count, uint32_t K, const Get& get, SelShared& S) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // 1. key range of the entries
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    for (int i = tid; i < count; i += SEL_THREADS) {
+        const uint32_t k = composite_key(get(i));
+        mn = min(mn, k);
+        mx = max(mx, k);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, off));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
+    }
+    if (lane == 0) { S.red[0][wave] = mn; S.red[1][wave] = mx; }
+    for (int i = tid; i < SEL_BINS; i += SEL_THREADS) S.r.hist[i] = 0u;
+    __syncthreads();
+    uint32_t lo = S.red[0][0], hi = S.red[1][0];
+#pragma unroll
+    for (int w = 1; w < SEL_WAVES; ++w) { lo = min(lo, S.red[0][w]); hi = max(hi, S.red[1][w]); }
+    const uint32_t sh = range_shift(lo, hi, SEL_BINS);
+
+    // 2. histogram over SEL_BINS buckets spread across [lo, hi]
+    for (int base = 0; base < count; base += SEL_THREADS) {
+        const int i = base + tid;
+        const bool ok = i < count;
+        const uint32_t b = ok ? bucket_of(composite_key(get(i)), lo, sh, SEL_BINS) : 0u;
+        lds_count(S.r.hist, b, ok);
+    }
+    __syncthreads();
+
+    // 3. threshold bucket b*: count(> b*) < K <= count(>= b*); thread i owns
+    // buckets 4095-4i .. 4092-4i
+    uint32_t c4[4], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { c4[j] = S.r.hist[SEL_BINS - 1 - 4 * tid - j]; sum += c4[j]; }
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan<SEL_WAVES>(sum, S.wsum, &tot);
+    if (ex < K && ex + sum >= K) {
+        uint32_t cum = ex;
+        for (int j = 0; j < 4; ++j) {
+            if (cum + c4[j] >= K) {
+                S.st[0] = (uint32_t)(SEL_BINS - 1 - 4 * tid - j);
+                S.st[1] = cum;
+                S.st[2] = c4[j];
+                break;
+            }
+            cum += c4[j];
+        }
+    }
+    if (tid == 0) S.st[3] = 0u;
+    __syncthreads();
+    const uint32_t bstar = S.st[0], need = K - S.st[1], nb = S.st[2];
+    __syncthreads();   // the histogram space is reused below
+
+    if (nb <= (uint32_t)SEL_MEMBERS) {
+        // 4a. the threshold bucket's members: descending bitonic sort
+        for (int base = 0; base < count; base += SEL_THREADS) {
+            const int i = base + tid;
+            uint64_t ck = 0;
+            bool mem = false;
+            if (i < count) {
+                ck = get(i);
+                mem = bucket_of(composite_key(ck), lo, sh, SEL_BINS) == bstar;
+            }
+            const unsigned long long mk = __ballot(mem);
+            if (mk) {
+                const int first = __ffsll((long long)mk) - 1;
+                uint32_t pos = 0;
+                if (lane == first) pos = atomicAdd(&S.st[3], (uint32_t)__popcll(mk));
+                const unsigned long long below = lane ? (mk & ((1ull << lane) - 1ull)) : 0ull;
+                pos = (uint32_t)__shfl((int)pos, first) + (uint32_t)__popcll(below);
+                if (mem) S.r.members[pos] = ck;
+            }
+        }
+        __syncthreads();
         int P = 1;
-        while (P < (int)ncand) P <<= 1;
-        for (int i = (int)ncand + tid; i < P; i += ROW_THREADS) cand[i] = 0ull;
+        while (P < (int)nb) P <<= 1;
+        for (int i = (int)nb + tid; i < P; i += SEL_THREADS) S.r.members[i] = 0ull;   // sorts last
         __syncthreads();
         for (int size = 2; size <= P; size <<= 1) {
             for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                for (int i = tid; i < P / 2; i += ROW_THREADS) {
+                for (int i = tid; i < P / 2; i += SEL_THREADS) {
                     const int l0 = 2 * i - (i & (stride - 1));
                     const int l1 = l0 + stride;
                     const bool desc = (l0 & size) == 0;
-                    const uint64_t x = cand[l0], y = cand[l1];
-                    if ((x < y) == desc) { cand[l0] = y; cand[l1] = x; }
+                    const uint64_t x = S.r.members[l0], y = S.r.members[l1];
+                    if ((x < y) == desc) { S.r.members[l0] = y; S.r.members[l1] = x; }
                 }
                 __syncthreads();
             }
         }
-        for (int i = tid; i < (int)need; i += ROW_THREADS) {
-            const int sidx = composite_index(cand[i]);
-            atomicOr(&bitmap[sidx >> 5], 1u << (sidx & 31));
-        }
-    } else {
-        const bool in_lds = ncand <= (uint32_t)ROW_CAND;
-        const int scan_n = in_lds ? (int)ncand : n;
-        auto get = [&](int i, uint64_t& ck) -> bool {
-            if (in_lds) { ck = cand[i]; return true; }
-            const uint32_t key = score_key(row[i]);
-            if (bucket_of(key) != bucket) return false;
-            ck = full_composite(key, i);
-            return true;
-        };
-        uint32_t rem = need;
-        uint64_t prefix = 0;
-        int sh = 56;
-        for (;; sh -= 8) {
-            if (tid < 256) hist[tid] = 0u;
-            __syncthreads();
-            for (int i = tid; i < scan_n; i += ROW_THREADS) {
-                uint64_t ck;
-                if (get(i, ck) && (sh == 56 || (ck >> (sh + 8)) == prefix))
-                    atomicAdd(&hist[(ck >> sh) & 255u], 1u);
+        const uint64_t kth = S.r.members[need - 1];
+        __syncthreads();
+        return kth;
+    }
+
+    // 4b. many ties: MSB-first radix select of the need-th largest member
+    // composite, 8 bits at a time (unique keys: settled by the last digit)
+    uint32_t* h256 = S.r.hist;
+    uint32_t rem = need;
+    uint64_t prefix = 0;
+    for (int d = 56; d >= 0; d -= 8) {
+        if (tid < 256) h256[tid] = 0u;
+        __syncthreads();
+        for (int base = 0; base < count; base += SEL_THREADS) {
+            const int i = base + tid;
+            uint64_t ck = 0;
+            bool ok = false;
+            if (i < count) {
+                ck = get(i);
+                ok = bucket_of(composite_key(ck), lo, sh, SEL_BINS) == bstar &&
+                     (d == 56 || (ck >> (d + 8)) == prefix);
             }
-            __syncthreads();
-            if (wave == 0) {
-                uint32_t c[4], sum = 0;
+            lds_count(h256, (uint32_t)(ck >> d) & 255u, ok);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            uint32_t cc[4], s4 = 0;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) { c[j] = hist[255 - 4 * lane - j]; sum += c[j]; }
-                uint32_t tot;
-                const uint32_t excl = wave_excl_scan(sum, &tot);
-                if (excl < rem && excl + sum >= rem) {
-                    uint32_t cum = excl;
-                    for (int j = 0; j < 4; ++j) {
-                        if (cum + c[j] >= rem) {
-                            st[4] = (uint32_t)(255 - 4 * lane - j);
-                            st[5] = rem - cum;
-                            st[6] = c[j] == rem - cum ? 1u : 0u;
-                            break;
-                        }
-                        cum += c[j];
-                    }
+            for (int j = 0; j < 4; ++j) { cc[j] = h256[255 - 4 * lane - j]; s4 += cc[j]; }
+            uint32_t t4;
+            const uint32_t e4 = wave_excl_scan(s4, &t4);
+            if (e4 < rem && e4 + s4 >= rem) {
+                uint32_t cum = e4;
+                for (int j = 0; j < 4; ++j) {
+                    if (cum + cc[j] >= rem) { S.st[4] = (uint32_t)(255 - 4 * lane - j); S.st[5] = rem - cum; break; }
+                    cum += cc[j];
                 }
             }
-            __syncthreads();
-            const uint32_t d = st[4];
-            rem = st[5];
-            const bool done = st[6] != 0u || sh == 0;
-            prefix = (prefix << 8) | d;
-            __syncthreads();
-            if (done) break;
         }
-        for (int i = tid; i < scan_n; i += ROW_THREADS) {
-            uint64_t ck;
-            if (get(i, ck) && (ck >> sh) >= prefix) {
-                const int sidx = composite_index(ck);
-                atomicOr(&bitmap[sidx >> 5], 1u << (sidx & 31));
-            }
-        }
+        __syncthreads();
+        prefix = (prefix << 8) | S.st[4];
+        rem = S.st[5];
+        __syncthreads();
     }
-    __syncthreads();
+    return prefix;
+}
 
-    // 5. ascending write-out
-    const int per = (words + ROW_THREADS - 1) / ROW_THREADS;
-    const int w0 = min(words, tid * per), w1 = min(words, w0 + per);
-    uint32_t nbits = 0;
-    for (int w = w0; w < w1; ++w) nbits += __popc(bitmap[w]);
-    uint32_t wtot;
-    const uint32_t wexcl = wave_excl_scan(nbits, &wtot);
-    if (lane == 0) wave_sums[wave] = wtot;
-    __syncthreads();
-    uint32_t pos = wexcl;
-    for (int w = 0; w < wave; ++w) pos += wave_sums[w];
-    for (int w = w0; w < w1; ++w) {
-        uint32_t bits = bitmap[w];
-        while (bits) {
-            const int b = __ffs(bits) - 1;
-            bits &= bits - 1u;
-            if (pos < (uint32_t)K) out[pos] = w * 32 + b;
+// Writes the source entries with composite >= kth, in source order (which is
+// ascending token order); exactly K of them.
+template <class Get>
+__device__ void write_selected(int count, uint64_t kth, uint32_t K, const Get& get, int32_t* out, SelShared& S) {
+    const int tid = threadIdx.x;
+    const int per = (count + SEL_THREADS - 1) / SEL_THREADS;
+    const int i0 = min(count, tid * per), i1 = min(count, i0 + per);
+    uint32_t nsel = 0;
+    for (int i = i0; i < i1; ++i) nsel += get(i) >= kth ? 1u : 0u;
+    uint32_t tot;
+    uint32_t pos = block_excl_scan<SEL_WAVES>(nsel, S.wsum, &tot);
+    for (int i = i0; i < i1; ++i) {
+        const uint64_t ck = get(i);
+        if (ck >= kth) {
+            if (pos < K) out[pos] = composite_index(ck);
             ++pos;
         }
     }
 }
 
-bool topk_single_kernel(int max_ctx, int k) { return max_ctx <= ROW_MAX_TOKENS && k <= TOPK_MAX_K; }
-
-hipError_t launch_topk_row(const TopkArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(topk_row, dim3(a.g.T), dim3(ROW_THREADS), 0, s, a);
-    return hipGetLastError();
+__global__ __launch_bounds__(SEL_THREADS) void topk_select(TopkArgs a) {
+    const int t = blockIdx.x;
+    const int n = row_visible(a.g, t);
+    const uint32_t K = (uint32_t)a.k;
+    const int tid = threadIdx.x;
+    int32_t* out = a.indices + (size_t)t * K;
+    if (n <= (int)K) {   // every visible token, then -1 padding
+        for (int i = tid; i < (int)K; i += SEL_THREADS) out[i] = i < n ? i : -1;
+        return;
+    }
+    __shared__ SelShared S;
+    const float* row = a.scores + (size_t)t * a.ld;
+    int count = 0;
+    if (n <= SEL_LIST) {
+        for (int i = tid; i < n; i += SEL_THREADS) S.list[i] = composite(score_key(row[i]), i);
+        count = n;
+    } else {
+        // compact the candidate bitmap: positions by a block scan of popcounts
+        const uint32_t* bm = a.bitmap + (size_t)t * a.bitmap_ld;
+        const int words = (n + 31) >> 5;
+        const int per = (words + SEL_THREADS - 1) / SEL_THREADS;
+        const int w0 = min(words, tid * per), w1 = min(words, w0 + per);
+        uint32_t nb = 0;
+        for (int w = w0; w < w1; ++w) nb += __popc(bm[w]);
+        uint32_t tot;
+        uint32_t pos = block_excl_scan<SEL_WAVES>(nb, S.wsum, &tot);
+        count = (int)tot;
+        if (count >= (int)K && count <= SEL_LIST) {
+            for (int w = w0; w < w1; ++w) {
+                uint32_t bits = bm[w];
+                while (bits) {
+                    const int b = __ffs(bits) - 1;
+                    bits &= bits - 1u;
+                    S.list[pos++] = (uint64_t)(w * 32 + b);
+                }
+            }
+            __syncthreads();
+            constexpr int G = SEL_LIST / SEL_THREADS;
+            float sv[G];
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const int i = tid + j * SEL_THREADS;
+                sv[j] = i < count ? row[(int)S.list[i]] : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const int i = tid + j * SEL_THREADS;
+                if (i < count) S.list[i] = composite(score_key(sv[j]), (int)S.list[i]);
+            }
+        } else {
+            count = -1;   // the sample bound failed for this row
+        }
+    }
+    __syncthreads();
+    if (count >= 0) {
+        auto get = [&](int i) -> uint64_t { return S.list[i]; };
+        const uint64_t kth = kth_composite(count, K, get, S);
+        write_selected(count, kth, K, get, out, S);
+    } else {
+        auto get = [&](int i) -> uint64_t { return composite(score_key(row[i]), i); };
+        const uint64_t kth = kth_composite(n, K, get, S);
+        write_selected(n, kth, K, get, out, S);
+    }
 }
 
-hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t s) {
-    dim3 grid((a.g.max_ctx + TK_CHUNK - 1) / TK_CHUNK, a.g.T);
-    hipLaunchKernelGGL(topk_hist, grid, dim3(TK_THREADS), 0, s, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(topk_threshold, dim3(a.g.T), dim3(TK_THREADS), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    dim3 grid((a.g.max_ctx + FL_CHUNK - 1) / FL_CHUNK, a.g.T);
-    hipLaunchKernelGGL(topk_filter, grid, dim3(TK_THREADS), 0, s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_refine, dim3(a.g.T), dim3(RF_THREADS), 0, s, a);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
+    if (a.g.max_ctx > SEL_LIST) {
+        const dim3 grid(a.g.T, (a.g.max_ctx + TOPK_CHUNK - 1) / TOPK_CHUNK);
+        hipLaunchKernelGGL(topk_candidates, grid, dim3(TK_THREADS), 0, s, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(topk_select, dim3(a.g.T), dim3(SEL_THREADS), 0, s, a);
     return hipGetLastError();
 }
 

@@ -73,13 +73,15 @@ def test_topk_exact_on_identical_scores(dup):
 
 
 def test_topk_all_equal_takes_lowest_indices():
-    lens = [5000, 3000]
-    wl = workloads.make_workload("single_b1_l32768", batch=2, context_lens=lens, seed=3)
+    """One bucket holds the whole row (more members than the candidate list
+    keeps), so the selection rescans the row; one row spans 9 chunks."""
+    lens = [5000, 3000, 70000]
+    wl = workloads.make_workload("single_b1_l32768", batch=3, context_lens=lens, seed=3)
     batch, _ = upload(wl)
-    scores = torch.zeros((2, 5056), dtype=torch.float32, device="cuda")
+    scores = torch.zeros((3, 70016), dtype=torch.float32, device="cuda")
     idx = dsa.topk(batch, scores, 2048).cpu().numpy()
-    assert idx[0].tolist() == list(range(2048))
-    assert idx[1].tolist() == list(range(2048))
+    for t in range(3):
+        assert idx[t].tolist() == list(range(2048))
 
 
 def test_mla_decode_on_oracle_selection():
@@ -200,8 +202,8 @@ def test_band_is_rarely_used():
 
 @pytest.mark.parametrize("dup", [False, True])
 def test_topk_rows_beyond_single_kernel(dup):
-    """Rows longer than 2^19 tokens take the histogram + threshold/filter/refine
-    path; same exact-set rule as above."""
+    """Rows of 600000 and 530000 tokens (73 and 65 chunk workgroups per row)
+    next to a short one; same exact-set rule as above."""
     lens = [600000, 530000, 5000]
     bs = 64
     maxb = (max(lens) + bs - 1) // bs
