@@ -3,6 +3,8 @@
 // no state kept between calls.
 #include <string.h>
 
+#include <algorithm>
+
 #include "dsa.h"
 #include "dsa_kernels.h"
 
@@ -49,9 +51,9 @@ TopkLayout topk_layout(size_t base, const dsa_batch* b) {
 }
 
 struct MlaLayout { size_t part_o, part_lse, end; int splits; };
-MlaLayout mla_layout(size_t base, const dsa_batch* b, int k, int n_heads, bool prefill, bool fast) {
+MlaLayout mla_layout(size_t base, const dsa_batch* b, int k, int n_heads, bool prefill, int path) {
     MlaLayout l;
-    l.splits = (fast && !prefill) ? mla_decode_splits(b->total_q, n_heads, k) : 1;
+    l.splits = mla_splits(path, b->total_q, n_heads, k, prefill);
     l.part_o = l.part_lse = l.end = base;
     if (l.splits > 1) {
         const size_t th = (size_t)b->total_q * n_heads * l.splits;
@@ -61,14 +63,23 @@ MlaLayout mla_layout(size_t base, const dsa_batch* b, int k, int n_heads, bool p
     return l;
 }
 
+// Largest MLA workspace over the latent dtypes of the fast paths (for size
+// queries that do not name the dtype).
+size_t mla_layout_max(size_t base, const dsa_batch* b, int k, int n_heads, bool prefill) {
+    size_t end = base;
+    for (int dt = 0; dt <= 2; ++dt)
+        end = std::max(end, mla_layout(base, b, k, n_heads, prefill, mla_path(dt, 512, 64, n_heads)).end);
+    return end;
+}
+
 struct StepLayout { size_t scores, indices; TopkLayout tk; MlaLayout ml; size_t end; int64_t ld; };
-StepLayout step_layout(const dsa_batch* b, int k, int n_heads, bool fast_mla) {
+StepLayout step_layout(const dsa_batch* b, int k, int n_heads, int mla_path_id) {
     StepLayout l;
     l.ld = round_up64(b->max_context_len);
     l.scores = 0;
     l.indices = align_up(sizeof(float) * (size_t)b->total_q * l.ld);
     l.tk = topk_layout(align_up(l.indices + sizeof(int32_t) * (size_t)b->total_q * k), b);
-    l.ml = mla_layout(l.tk.end, b, k, n_heads, false, fast_mla);
+    l.ml = mla_layout(l.tk.end, b, k, n_heads, false, mla_path_id);
     l.end = l.ml.end;
     return l;
 }
@@ -174,8 +185,8 @@ MlaArgs mla_args(const dsa_batch* b, const dsa_latent_cache* c, const void* q, i
 // Workspace check for an MLA launch placed at `ws_base` (host only).
 int mla_workspace_ok(const dsa_batch* b, const dsa_latent_cache* c, int n_heads, int k, const void* ws,
                      size_t ws_bytes, size_t ws_base, bool prefill) {
-    const bool fast = mla_fast_path(c->dtype, c->d_latent, c->d_rope, n_heads, b->block_size);
-    const MlaLayout l = mla_layout(ws_base, b, k, n_heads, prefill, fast);
+    const int path = mla_path(c->dtype, c->d_latent, c->d_rope, n_heads);
+    const MlaLayout l = mla_layout(ws_base, b, k, n_heads, prefill, path);
     if (l.splits > 1 && (!ws || l.end > ws_bytes)) return DSA_ERR_WORKSPACE;
     return DSA_OK;
 }
@@ -183,8 +194,8 @@ int mla_workspace_ok(const dsa_batch* b, const dsa_latent_cache* c, int n_heads,
 int run_mla(const dsa_batch* b, const dsa_latent_cache* c, const void* q, int n_heads,
             const int32_t* indices, int k, float scale, void* out, float* lse, char* ws, size_t ws_bytes,
             size_t ws_base, bool prefill, hipStream_t s) {
-    const bool fast = mla_fast_path(c->dtype, c->d_latent, c->d_rope, n_heads, b->block_size);
-    MlaLayout l = mla_layout(ws_base, b, k, n_heads, prefill, fast);
+    const int path = mla_path(c->dtype, c->d_latent, c->d_rope, n_heads);
+    MlaLayout l = mla_layout(ws_base, b, k, n_heads, prefill, path);
     if (l.splits > 1 && (!ws || l.end > ws_bytes)) return DSA_ERR_WORKSPACE;
     MlaArgs a = mla_args(b, c, q, n_heads, indices, k, scale, out, lse);
     a.splits = l.splits;
@@ -224,12 +235,16 @@ size_t dsa_workspace_size(int32_t op, const dsa_batch* b, int32_t k, int32_t n_h
     case DSA_OP_MLA_DECODE:
     case DSA_OP_MLA_PREFILL:
         if (k < 1 || n_heads < 1) return 0;
-        // sized for the fast path; the generic path needs none
-        return mla_layout(0, b, k, n_heads, op == DSA_OP_MLA_PREFILL,
-                          n_heads % MLA_HEADS_PER_WG == 0).end;
+        // the largest over the latent dtypes; the generic path needs none
+        return mla_layout_max(0, b, k, n_heads, op == DSA_OP_MLA_PREFILL);
     case DSA_OP_DECODE_STEP:
         if (k < 1 || k > TOPK_MAX_K || n_heads < 1) return 0;
-        return step_layout(b, k, n_heads, n_heads % MLA_HEADS_PER_WG == 0).end;
+        {
+            size_t end = 0;
+            for (int dt = 0; dt <= 2; ++dt)
+                end = std::max(end, step_layout(b, k, n_heads, mla_path(dt, 512, 64, n_heads)).end);
+            return end;
+        }
     default:
         return 0;
     }
@@ -293,8 +308,7 @@ int dsa_decode_step(const dsa_batch* b, const dsa_index_cache* ic, const void* q
     if (st != DSA_OK) return st;
     if ((st = validate_mla(b, lc, q_mla, n_heads, k, out)) != DSA_OK) return st;
     if (!topk_shape_ok(b, k)) return DSA_ERR_UNSUPPORTED;
-    const bool fast = mla_fast_path(lc->dtype, lc->d_latent, lc->d_rope, n_heads, b->block_size);
-    const StepLayout l = step_layout(b, k, n_heads, fast);
+    const StepLayout l = step_layout(b, k, n_heads, mla_path(lc->dtype, lc->d_latent, lc->d_rope, n_heads));
     if (!ws || ws_bytes < l.end) return DSA_ERR_WORKSPACE;
     if ((st = check_device_cached()) != DSA_OK) return st;
     hipStream_t s = (hipStream_t)stream;

@@ -96,6 +96,11 @@ struct Geometry {
     int max_blocks, block_size;
 };
 
+// Request of query row t; no lookup when every request has q_uniform rows.
+__device__ __forceinline__ int row_request(const Geometry& g, int t) {
+    return g.q_uniform > 0 ? t / g.q_uniform : find_request(g.qsl, g.B, t);
+}
+
 // Visible-token count of query row t; a single load when the query rows are
 // spread uniformly over the requests.
 __device__ __forceinline__ int row_visible(const Geometry& g, int t) {
@@ -145,7 +150,10 @@ hipError_t launch_mla(const MlaArgs& a, bool prefill, hipStream_t s);
 
 // Which MLA path serves these shapes, and how many splits it uses.
 bool mla_fast_path(int kv_dtype, int d_latent, int d_rope, int n_heads, int block_size);
-int mla_decode_splits(int T, int n_heads, int k);
 constexpr int MLA_HEADS_PER_WG = 64;
+constexpr int MLA_PATH_GENERIC = 0, MLA_PATH_H64 = 1, MLA_PATH_H128 = 2;
+int mla_path(int kv_dtype, int d_latent, int d_rope, int n_heads);
+// Partial results per query row (1: no split, no combine pass).
+int mla_splits(int path, int T, int n_heads, int k, bool prefill);
 
 }  // namespace dsa

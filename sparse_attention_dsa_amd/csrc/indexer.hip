@@ -232,7 +232,11 @@ __device__ __forceinline__ void load_raw_page(const uint8_t* __restrict__ keys, 
     const uint8_t* base = keys + (size_t)blk * (IDX_PAGE * IDX_D) + 16 * lane;
 #pragma unroll
     for (int c = 0; c < 8; ++c) p.v[c] = __builtin_nontemporal_load((const u32x4*)(base + 1024 * c));
-    p.scale = scales ? scales[(size_t)blk * IDX_PAGE + lane] : 1.0f;
+    // without scales the load reads the page's own keys; the consumer then
+    // uses 1 instead (the same instructions issue either way, and nothing
+    // here waits for the load)
+    const float* sp = scales ? scales + (size_t)blk * IDX_PAGE : (const float*)(keys + (size_t)blk * (IDX_PAGE * IDX_D));
+    p.scale = sp[lane];
 }
 
 // ---------------------------------------------------------------------------
@@ -303,33 +307,61 @@ __global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_persistent(IndexerArg
     };
     const uint8_t* keys = (const uint8_t*)a.keys;
 
-    // issue cursor (runs PER_PF pages ahead of the compute cursor)
-    int iss_p = p0, iss_it = __builtin_amdgcn_readfirstlane(find_item(p0));
+    // Page-table entries and item ids of the share, resolved 64 pages at a
+    // time (lane l: page base + l) one batch ahead, so no page waits on a
+    // page-table load; the cursors read them with v_readlane.
+    auto load_batch = [&](int base, int& blk_v, int& item_v) {
+        const int p = base + lane;
+        int it = 0, blk = 0;
+        if (p < p1) {
+            it = find_item(p);
+            blk = G.page_table[(size_t)(it / qgroups) * G.max_blocks + (p - item_off[it])];
+        }
+        blk_v = blk;
+        item_v = it;
+    };
+    int bb = p0, cblk, citem, nblk = 0, nitem = 0;
+    load_batch(bb, cblk, citem);
+    if (bb + 64 < p1) load_batch(bb + 64, nblk, nitem);
+    auto blk_of = [&](int q) -> int {   // q in [bb, bb + 128)
+        const int d = q - bb;
+        return d < 64 ? __builtin_amdgcn_readlane(cblk, d) : __builtin_amdgcn_readlane(nblk, d - 64);
+    };
+
+    // The loop body is straight-line for the memory system: every slot
+    // issues a page (past the share it re-reads the share's last page) and
+    // stores its scores through buffer stores whose out-of-range lanes are
+    // dropped, so the compiler's load counting stays exact and the ring of
+    // PER_PF pages is never drained early.
+    const auto clampp = [&](int q) { return q < p1 ? q : p1 - 1; };
+    int iss_p = p0;
     auto issue_next = [&](RawPage& dst) {
-        while (item_off[iss_it + 1] <= iss_p) ++iss_it;
-        const int r = iss_it / qgroups;
-        const int blk = G.page_table[(size_t)r * G.max_blocks + (iss_p - item_off[iss_it])];
-        load_raw_page(keys, a.key_scales, __builtin_amdgcn_readfirstlane(blk), lane, dst);
+        load_raw_page(keys, a.key_scales, blk_of(clampp(iss_p)), lane, dst);
         ++iss_p;
     };
     RawPage ring[PER_PF];
 #pragma unroll
-    for (int d = 0; d < PER_PF; ++d)
-        if (p0 + d < p1) issue_next(ring[d]);
+    for (int d = 0; d < PER_PF; ++d) issue_next(ring[d]);
 
-    // compute cursor state: current item's queries
-    int cur_it = -1;
-    int r = 0, qs = 0, ql = 0, j0 = 0, nq = 0, L = 0;
+    // compute cursor state: current item's queries, output rows
+    int cur_it = -1, cur_base = 0;
     i32x8 qf[NQ][HT];
     float wv[NQ][HT][4];
+    __amdgpu_buffer_rsrc_t orow[NQ];   // score row of each query, sized to its visible count
     auto load_item = [&](int it) {
         cur_it = it;
-        r = it / qgroups;
+        cur_base = __builtin_amdgcn_readfirstlane(item_off[it]);
+        const int r = it / qgroups;
         const int qg = it % qgroups;
-        qs = G.qsl[r]; ql = G.qsl[r + 1] - qs; j0 = qg * NQ; nq = min(NQ, ql - j0); L = G.ctx[r];
+        const int qs = __builtin_amdgcn_readfirstlane(G.qsl[r]);
+        const int ql = __builtin_amdgcn_readfirstlane(G.qsl[r + 1]) - qs;
+        const int L = __builtin_amdgcn_readfirstlane(G.ctx[r]);
+        const int j0 = qg * NQ, nq = min(NQ, ql - j0);
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
             const int t = qs + j0 + min(j, nq - 1);
+            const int n_j = j < nq ? L - ql + j0 + j + 1 : 0;
+            orow[j] = __builtin_amdgcn_make_buffer_rsrc(a.scores + (size_t)t * a.ld, 0, 4 * max(n_j, 0), 0x00020000);
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) {
                 const uint8_t* qp = (const uint8_t*)a.q + ((size_t)t * a.n_heads + 16 * ht + col) * IDX_D + 16 * g;
@@ -338,6 +370,16 @@ __global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_persistent(IndexerArg
                 for (int i = 0; i < 4; ++i) wv[j][ht][i] = a.w[(size_t)t * a.n_heads + 16 * ht + 4 * g + i];
             }
         }
+        // Use every reloaded value here: the wait for these loads then sits
+        // in this (rare) branch, and the page ring's waits after it stay exact.
+#pragma unroll
+        for (int j = 0; j < NQ; ++j)
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                asm volatile("" ::"v"(qf[j][ht][0]), "v"(qf[j][ht][4]));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) asm volatile("" ::"v"(wv[j][ht][i]));
+            }
     };
     uint8_t* pb = &pbuf[wave][0];
     const int wt = lane >> 3, wu = lane & 7;
@@ -345,35 +387,40 @@ __global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_persistent(IndexerArg
 #pragma unroll
         for (int sl = 0; sl < PER_PF; ++sl) {
             const int p = base + sl;
-            if (p < p1) {
-                int it = cur_it < 0 ? find_item(p) : cur_it;
-                while (item_off[it + 1] <= p) ++it;
-                if (it != cur_it) load_item(__builtin_amdgcn_readfirstlane(it));
-                RawPage& cur = ring[sl];
-#pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    const int t = 8 * c + wt;
-                    *(u32x4*)(pb + t * IDX_D + 16 * (wu ^ page_swz(t))) = cur.v[c];
-                }
-                i32x8 kf[4];
-#pragma unroll
-                for (int nt = 0; nt < 4; ++nt) {
-                    const int t = 16 * nt + col;
-                    const u32x4 lo = *(const u32x4*)(pb + t * IDX_D + 16 * (g ^ page_swz(t)));
-                    const u32x4 hi = *(const u32x4*)(pb + t * IDX_D + 16 * ((4 + g) ^ page_swz(t)));
-                    kf[nt] = join_i32x8(lo, hi);
-                }
-                const float ksc = cur.scale;
-                if (p + PER_PF < p1) issue_next(cur);
-                float ps[NQ];
-                page_scores<NQ, HT>(qf, wv, kf, ksc, lane, nq, ps);
-                const int pos = (p - item_off[cur_it]) * IDX_PAGE + lane;
-#pragma unroll
-                for (int j = 0; j < NQ; ++j) {
-                    const int n_j = L - ql + j0 + j + 1;
-                    if (j < nq && pos < n_j) a.scores[(size_t)(qs + j0 + j) * a.ld + pos] = ps[j];
-                }
+            const int pc = clampp(p);
+            if (pc == bb + 64) {   // next batch becomes current; resolve the one after
+                bb += 64;
+                cblk = nblk;
+                citem = nitem;
+                if (bb + 64 < p1) load_batch(bb + 64, nblk, nitem);
             }
+            const int it = __builtin_amdgcn_readlane(citem, pc - bb);
+            if (it != cur_it) load_item(it);
+            RawPage& cur = ring[sl];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const int t = 8 * c + wt;
+                *(u32x4*)(pb + t * IDX_D + 16 * (wu ^ page_swz(t))) = cur.v[c];
+            }
+            i32x8 kf[4];
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const int t = 16 * nt + col;
+                const u32x4 lo = *(const u32x4*)(pb + t * IDX_D + 16 * (g ^ page_swz(t)));
+                const u32x4 hi = *(const u32x4*)(pb + t * IDX_D + 16 * ((4 + g) ^ page_swz(t)));
+                kf[nt] = join_i32x8(lo, hi);
+            }
+            const float ksc = a.key_scales ? cur.scale : 1.0f;
+            issue_next(cur);
+            float ps[NQ];
+            page_scores<NQ, HT>(qf, wv, kf, ksc, lane, NQ, ps);
+            // out-of-range offsets (past the row's visible count, or a page past
+            // the share) are dropped by the buffer range check
+            const int pos = (pc - cur_base) * IDX_PAGE + lane;
+            const int voff = p < p1 ? 4 * pos : 0x7FFFFFF0;
+#pragma unroll
+            for (int j = 0; j < NQ; ++j)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ps[j]), orow[j], voff, 0, 0);
         }
     }
 }

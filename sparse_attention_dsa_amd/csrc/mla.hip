@@ -422,25 +422,385 @@ __global__ __launch_bounds__(256) void mla_generic(MlaArgs a) {
         a.lse[(size_t)t * a.n_heads + h] = den > 0.f ? mx + logf(den) : -INFINITY;
 }
 
-bool mla_fast_path(int kv_dtype, int d_latent, int d_rope, int n_heads, int block_size) {
-    (void)block_size;
-    return (kv_dtype == 1 || kv_dtype == 2) && d_latent == M_DL && d_rope == M_DR &&
-           n_heads % MLA_HEADS_PER_WG == 0;
+// ---------------------------------------------------------------------------
+// 128-head path (bf16 latent, d = 512, r = 64, heads a multiple of 128): a
+// workgroup owns one query row, 128 heads (32 per wave) and a slice of the
+// row's selection, so every selected latent row is fetched once per slice
+// and each LDS fragment read feeds 32 heads.  Tiles of 32 tokens stream
+// through a 4-deep ring of LDS buffers by global_load_lds_dwordx4 (three
+// tiles in flight while one is computed); the physical row ids of the whole
+// slice are resolved through the page table once, up front.
+//   S^T = K Q^T    v_mfma_f32_32x32x16_bf16: A = 32 token rows of the tile
+//                  (LDS), B = 32 heads' queries (registers, 36 k-steps);
+//   O^T += V^T P^T  A = V^T fragments by ds_read_b64_tr_b16 from the same
+//                  rows, B = probabilities straight from S^T's accumulator
+//                  layout (token order inside each 16-token k-step permuted
+//                  alike on both sides); O^T (512 x 32 per wave) lives in
+//                  accumulation registers.
+// Softmax in the exp2 domain against a fixed reference per head: the max of
+// the first tile with a visible token.  Probabilities are exp2(z - ref), at
+// most 2^64 when no later logit exceeds the reference by more than 64 (fp32
+// and bf16 hold that range, and O^T = sum p v / sum p does not depend on the
+// reference), so the 256 accumulation registers are never rescaled.  A slice
+// where some logit does exceed it is computed again with the largest logit
+// seen as the reference.
+constexpr int M3_HEADS = 128;
+constexpr int M3_NBUF = 4;
+constexpr int M3_MAX_SLICE = 2048;
+constexpr int M3_DMA_PER_WAVE = M_TILE_BYTES / 1024 / 4;    // 9 x 1 KB per wave per tile
+constexpr int M3_KPF = 4;     // K fragments in flight
+constexpr int M3_VPF = 3;     // V^T fragments in flight
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Splits per decode row: enough workgroups to cover the chip (~2 per CU),
-// at least 128 selected tokens per split.
-int mla_decode_splits(int T, int n_heads, int k) {
-    const int units = T * (n_heads / MLA_HEADS_PER_WG);
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier that orders LDS traffic only: unlike __syncthreads() it
+// does not wait for this wave's outstanding global loads (the ring's
+// transfers in flight), which the loop accounts for with wait_vmcnt.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <bool SPLIT>
+__global__ __attribute__((amdgpu_flat_work_group_size(M_THREADS, M_THREADS), amdgpu_waves_per_eu(1, 1)))
+void mla_h128(MlaArgs a, int slice) {
+    const Geometry& G = a.g;
+    const int hgroups = a.n_heads / M3_HEADS;
+    const int unit = blockIdx.x;
+    const int t = unit / hgroups, hg = unit % hgroups;
+    const int sp = blockIdx.y;
+    const int j_begin = sp * slice;
+    const int nslots = max(0, min(a.k, j_begin + slice) - j_begin);
+    const int ntiles = (nslots + M_TILE - 1) / M_TILE;
+
+    __shared__ __attribute__((aligned(1024))) uint8_t Ks[M3_NBUF][M_TILE_BYTES];
+    __shared__ int32_t rows[M3_MAX_SLICE];                 // physical row per slot (0 for padding)
+    __shared__ uint32_t tvalid[M3_MAX_SLICE / M_TILE];     // per tile: bit s = slot s holds a token
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hh = lane >> 5, c32 = lane & 31;
+    const int head = hg * M3_HEADS + wave * 32 + c32;
+
+    // queries first (needed last), then the slice's rows: every selection
+    // index load, then every page-table load, so each waits one round trip
+    u32x4 qf[M_DQK / 16];
+    {
+        const uint16_t* qp = (const uint16_t*)a.q + ((size_t)t * a.n_heads + head) * M_DQK + 8 * hh;
+#pragma unroll
+        for (int ks = 0; ks < M_DQK / 16; ++ks) qf[ks] = *(const u32x4*)(qp + 16 * ks);
+    }
+    {
+        constexpr int PER = M3_MAX_SLICE / M_THREADS;
+        const int r = row_request(G, t);
+        const int32_t* sel = a.indices + (size_t)t * a.k + j_begin;
+        const int32_t* pt = G.page_table + (size_t)r * G.max_blocks;
+        int sj[PER], blk[PER];
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int j = tid + u * M_THREADS;
+            sj[u] = j < nslots ? sel[j] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < PER; ++u) blk[u] = sj[u] >= 0 ? pt[sj[u] / G.block_size] : 0;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int j = tid + u * M_THREADS;
+            const bool ok = sj[u] >= 0;
+            if (j < ntiles * M_TILE) rows[j] = ok ? blk[u] * G.block_size + sj[u] % G.block_size : 0;
+            const unsigned long long m = __ballot(ok);   // 64 slots = two tiles
+            if (lane == 0 && j < ntiles * M_TILE) tvalid[j / M_TILE] = (uint32_t)m;
+            if (lane == 32 && j < ntiles * M_TILE) tvalid[j / M_TILE] = (uint32_t)(m >> 32);
+        }
+    }
+    __syncthreads();
+
+    // one tile's rows into ring buffer b: instruction i of wave w moves LDS
+    // units 64(9w+i) .. +63; LDS unit (row rr, physical unit pu) holds logical
+    // unit pu ^ ks_swz(rr) of that row.  The instruction's first unit is
+    // uniform, so a lane's row is the first row or the next one.
+    auto issue = [&](int tile, int b) {
+        const int32_t* trows = rows + M_TILE * tile;
+        int ln = lane;
+        asm volatile("" : "+v"(ln));   // recomputed per tile: hoisted, these would hold 18 registers
+        int row[M3_DMA_PER_WAVE], off[M3_DMA_PER_WAVE];
+#pragma unroll
+        for (int i = 0; i < M3_DMA_PER_WAVE; ++i) {
+            const int U0 = (wave * M3_DMA_PER_WAVE + i) * 64;
+            const int rr0 = U0 / M_ROW_UNITS, pu0 = U0 - rr0 * M_ROW_UNITS;
+            int pu = pu0 + ln;
+            const bool wrap = pu >= M_ROW_UNITS;
+            const int rr = rr0 + (wrap ? 1 : 0);
+            pu -= wrap ? M_ROW_UNITS : 0;
+            off[i] = 16 * (pu ^ ks_swz(rr));
+            row[i] = trows[rr];
+        }
+#pragma unroll
+        for (int i = 0; i < M3_DMA_PER_WAVE; ++i) {
+            const uint8_t* src = (const uint8_t*)a.kv + (size_t)row[i] * M_ROW_BYTES + off[i];
+            __builtin_amdgcn_global_load_lds((const void*)src,
+                                             (lds_vptr)(&Ks[b][0] + 1024 * (wave * M3_DMA_PER_WAVE + i)), 16, 0, 0);
+        }
+    };
+
+    // per-lane LDS offsets (XOR by ks_swz(r) < 8 only touches the low 3 bits
+    // of a unit index, so fragment reads are few bases plus immediates)
+    int qk_base[4];       // S^T A operand: row c32, unit 2ks + hh; [ks % 4]
+    {
+        const int sw = ks_swz(c32);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) qk_base[m] = c32 * M_ROW_BYTES + 16 * ((2 * m + hh) ^ sw);
+    }
+    // V^T A operand by transposing reads: in 16-lane group g4 (hh = g4 >> 1,
+    // column half 16(g4 & 1)), source lane s = 4jj + q points at token
+    // 16kk + 8rd + 4hh + jj, columns 32cb + 16(g4 & 1) + 4q .. +3, and
+    // destination lane d receives column d of the half, tokens jj = 0..3.
+    int pv_base[2][2][2];   // [kk][rd][cb & 1]
+    {
+        const int s16 = lane & 15, jj = s16 >> 2, q = s16 & 3;
+        const int v = 2 * ((lane >> 4) & 1) + (q >> 1);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int rd = 0; rd < 2; ++rd) {
+                const int tok = 16 * kk + 8 * rd + 4 * hh + jj;
+#pragma unroll
+                for (int c1 = 0; c1 < 2; ++c1)
+                    pv_base[kk][rd][c1] = tok * M_ROW_BYTES + 16 * ((4 * c1 + v) ^ ks_swz(tok)) + 8 * (q & 1);
+            }
+    }
+
+    __shared__ uint32_t redo;
+    f32x16 oacc[M_DL / 32];
+    float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
+    const float zscale = a.scale * LOG2E;
+
+    for (int pass = 0;; ++pass) {
+#pragma unroll
+    for (int cb = 0; cb < M_DL / 32; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[cb][i] = 0.f;
+    l_run = 0.f;
+    bool overflow = false;
+    if (tid == 0) redo = 0u;
+
+#pragma unroll
+    for (int b = 0; b < M3_NBUF - 1; ++b)
+        if (b < ntiles) issue(b, b);
+
+    for (int i = 0; i < ntiles; ++i) {
+        // this wave's transfers of tile i are done once at most the ones of
+        // the (up to two) later tiles already issued are outstanding
+        const int later = min(M3_NBUF - 2, ntiles - 1 - i);
+        if (later >= 2) wait_vmcnt<2 * M3_DMA_PER_WAVE>();
+        else if (later == 1) wait_vmcnt<M3_DMA_PER_WAVE>();
+        else wait_vmcnt<0>();
+        lds_barrier();   // everyone's part of tile i landed; tile i-1's buffer is free
+        if (i + M3_NBUF - 1 < ntiles) issue(i + M3_NBUF - 1, (i + M3_NBUF - 1) % M3_NBUF);
+        const uint8_t* Kb = &Ks[i % M3_NBUF][0];
+
+        const uint32_t vmask = tvalid[i];   // tokens present in the tile (bit per slot)
+
+        // S^T: K fragments read M3_KPF steps ahead of their MFMA
+        f32x16 st;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) st[e] = 0.f;
+        {
+            constexpr int NK = M_DQK / 16;
+            u32x4 kb[M3_KPF];
+#pragma unroll
+            for (int j = 0; j < M3_KPF; ++j) kb[j] = *(const u32x4*)(Kb + qk_base[j & 3] + 128 * (j >> 2));
+            // scheduling groups: the prefetch reads first, then MFMA / read pairs
+            __builtin_amdgcn_sched_group_barrier(0x100, M3_KPF, 0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < NK; ++ks) {
+                st = mfma_bf16_32x32x16(as_bf16x8(kb[ks % M3_KPF]), as_bf16x8(qf[ks]), st);
+                if (ks + M3_KPF < NK) {
+                    const int kn = ks + M3_KPF;
+                    kb[ks % M3_KPF] = *(const u32x4*)(Kb + qk_base[kn & 3] + 128 * (kn >> 2));
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // then one LDS read
+            }
+        }
+        // element e of this lane: token 8(e/4) + 4hh + e%4, head c32
+        float x[16];
+        if (vmask == 0xFFFFFFFFu) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) x[e] = st[e] * zscale;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int tok = 8 * (e >> 2) + 4 * hh + (e & 3);
+                x[e] = (vmask >> tok) & 1u ? st[e] * zscale : -INFINITY;
+            }
+        }
+        float tmax;
+        {   // max and (below) sum as balanced trees
+            float m8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m8[e] = fmaxf(x[e], x[e + 8]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m8[e] = fmaxf(m8[e], m8[e + 4]);
+            tmax = fmaxf(fmaxf(m8[0], m8[2]), fmaxf(m8[1], m8[3]));
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        m_seen = fmaxf(m_seen, tmax);
+        if (m_ref == -INFINITY) m_ref = tmax;   // first visible token of this head
+        overflow |= tmax > m_ref + 64.f;
+        // every head of the wave has the same visible tokens, so m_ref is
+        // -inf in all lanes or in none
+        float p[16];
+        if (m_ref == -INFINITY) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) p[e] = 0.f;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(x[e] - m_ref);
+        }
+        {
+            float s8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s8[e] = p[e] + p[e + 8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s8[e] += s8[e + 4];
+            l_run += (s8[0] + s8[2]) + (s8[1] + s8[3]);
+        }
+        bf16x8 pb[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pb[kk][e] = (__bf16)p[8 * kk + e];
+
+        // O^T += V^T P^T: V^T fragments (two transposing reads each) read
+        // M3_VPF MFMAs ahead; the 16 accumulators rotate between dependent updates
+        {
+            constexpr int NV = 2 * (M_DL / 32);
+            auto vread = [&](int n, s16x4& v0, s16x4& v1) {
+                const int kk = n / (M_DL / 32), cb = n % (M_DL / 32);
+                v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4_ptr)(Kb + pv_base[kk][0][cb & 1] + 128 * (cb >> 1)));
+                v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4_ptr)(Kb + pv_base[kk][1][cb & 1] + 128 * (cb >> 1)));
+            };
+            s16x4 vb0[M3_VPF], vb1[M3_VPF];
+#pragma unroll
+            for (int j = 0; j < M3_VPF; ++j) vread(j, vb0[j], vb1[j]);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * M3_VPF, 0);
+#pragma unroll
+            for (int n = 0; n < NV; ++n) {
+                const int kk = n / (M_DL / 32), cb = n % (M_DL / 32);
+                const s16x4 v0 = vb0[n % M3_VPF], v1 = vb1[n % M3_VPF];
+                u32x4 va;
+                va[0] = (uint16_t)v0[0] | ((uint32_t)(uint16_t)v0[1] << 16);
+                va[1] = (uint16_t)v0[2] | ((uint32_t)(uint16_t)v0[3] << 16);
+                va[2] = (uint16_t)v1[0] | ((uint32_t)(uint16_t)v1[1] << 16);
+                va[3] = (uint16_t)v1[2] | ((uint32_t)(uint16_t)v1[3] << 16);
+                oacc[cb] = mfma_bf16_32x32x16(as_bf16x8(va), pb[kk], oacc[cb]);
+                if (n + M3_VPF < NV) vread(n + M3_VPF, vb0[n % M3_VPF], vb1[n % M3_VPF]);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // then its two reads
+            }
+        }
+    }
+    // the whole workgroup agrees on a second pass (it shares the barriers)
+    if (__ballot(overflow) && lane == 0) redo = 1u;
+    __syncthreads();
+    if (pass > 0 || redo == 0u) break;
+    m_ref = m_seen;
+    __syncthreads();
+    }
+    const float m_run = m_ref;
+
+    // ---- epilogue: element e of block cb is O^T[32cb + 8(e/4) + 4hh + e%4][head]
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const bool empty = l_tot == 0.f;
+    const float inv = empty ? 0.f : 1.f / l_tot;
+    const float lse_nat = empty ? -INFINITY : (m_run + log2f(l_tot)) * LN2;
+    if (SPLIT) {
+        float* po = a.part_o + (((size_t)t * a.n_heads + head) * a.splits + sp) * M_DL;
+#pragma unroll
+        for (int cb = 0; cb < M_DL / 32; ++cb)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                f32x4 o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = oacc[cb][4 * e4 + e] * inv;
+                *(f32x4*)(po + 32 * cb + 8 * e4 + 4 * hh) = o;
+            }
+        if (hh == 0) a.part_lse[((size_t)t * a.n_heads + head) * a.splits + sp] = lse_nat;
+    } else {
+        uint16_t* op = (uint16_t*)a.out + ((size_t)t * a.n_heads + head) * M_DL;
+#pragma unroll
+        for (int cb = 0; cb < M_DL / 32; ++cb)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                u32x2 w;
+                w[0] = f32_to_bf16(oacc[cb][4 * e4] * inv) | (f32_to_bf16(oacc[cb][4 * e4 + 1] * inv) << 16);
+                w[1] = f32_to_bf16(oacc[cb][4 * e4 + 2] * inv) | (f32_to_bf16(oacc[cb][4 * e4 + 3] * inv) << 16);
+                *(u32x2*)(op + 32 * cb + 8 * e4 + 4 * hh) = w;
+            }
+        if (a.lse && hh == 0) a.lse[(size_t)t * a.n_heads + head] = lse_nat;
+    }
+}
+
+// Which kernel serves an MLA call.
+int mla_path(int kv_dtype, int d_latent, int d_rope, int n_heads) {
+    if (d_latent != M_DL || d_rope != M_DR) return MLA_PATH_GENERIC;
+    if (kv_dtype == 1 && n_heads % M3_HEADS == 0) return MLA_PATH_H128;
+    if ((kv_dtype == 1 || kv_dtype == 2) && n_heads % MLA_HEADS_PER_WG == 0) return MLA_PATH_H64;
+    return MLA_PATH_GENERIC;
+}
+
+bool mla_fast_path(int kv_dtype, int d_latent, int d_rope, int n_heads, int block_size) {
+    (void)block_size;
+    return mla_path(kv_dtype, d_latent, d_rope, n_heads) != MLA_PATH_GENERIC;
+}
+
+// Splits per query row.  Decode: enough workgroups to cover the chip, at
+// least 128 selected tokens per split; the 128-head path also keeps each
+// slice within its row-id buffer.
+int mla_splits(int path, int T, int n_heads, int k, bool prefill) {
+    if (path == MLA_PATH_GENERIC) return 1;
+    const int min_s = path == MLA_PATH_H128 ? (k + M3_MAX_SLICE - 1) / M3_MAX_SLICE : 1;
+    if (prefill) return min_s;
+    const int per_row = n_heads / (path == MLA_PATH_H128 ? M3_HEADS : MLA_HEADS_PER_WG);
+    const int units = T * per_row;
+    const int target = path == MLA_PATH_H128 ? device_cu_count() : 2 * device_cu_count();
     int s = 1;
-    while (units * s < 512 && k / (2 * s) >= 128) s <<= 1;
-    return s;
+    while (units * s < target && k / (2 * s) >= 128) s <<= 1;
+    return max(s, min_s);
 }
 
 hipError_t launch_mla(const MlaArgs& a, bool prefill, hipStream_t s) {
-    if (mla_fast_path(a.kv_dtype, a.d_latent, a.d_rope, a.n_heads, a.g.block_size)) {
+    const int path = mla_path(a.kv_dtype, a.d_latent, a.d_rope, a.n_heads);
+    if (path == MLA_PATH_H128) {
+        const int S = a.splits;
+        int slice = (a.k + S - 1) / S;
+        slice = (slice + M_TILE - 1) / M_TILE * M_TILE;
+        if (slice > M3_MAX_SLICE) return hipErrorInvalidValue;
+        const dim3 grid(a.g.T * (a.n_heads / M3_HEADS), S);
+        if (S > 1) {
+            hipLaunchKernelGGL(mla_h128<true>, grid, dim3(M_THREADS), 0, s, a, slice);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(mla_combine, dim3(a.g.T * a.n_heads), dim3(M_DL / 4), 0, s, a);
+        } else {
+            hipLaunchKernelGGL(mla_h128<false>, grid, dim3(M_THREADS), 0, s, a, slice);
+        }
+        return hipGetLastError();
+    }
+    if (path == MLA_PATH_H64) {
         const int hgroups = a.n_heads / MLA_HEADS_PER_WG;
-        const bool split = !prefill && a.splits > 1;
+        const bool split = a.splits > 1;
         const int S = split ? a.splits : 1;
         int slice = (a.k + S - 1) / S;
         slice = (slice + M_TILE - 1) / M_TILE * M_TILE;
