@@ -10,11 +10,17 @@ batch-64 decode with per-request contexts drawn uniformly from [8K, 128K]
 Prints one JSON line.  `value` is decode tokens/s per layer (query rows per
 second).  `roofline` covers the dominant kernel -- the lightning indexer --
 with its algorithmic bytes per launch divided by its average launch time,
-timed live here with HIP events on the stream it runs on.  `step_hbm` gives
-the same ratio for the whole step.  `cpu_baseline` times the CPU oracle on a
-bounded sample of the same workload.  Inputs rotate over several device
-copies so that the 256 MB Infinity Cache cannot serve a step from the
-previous one.
+timed live here with HIP events on the stream it runs on; its `traffic` is
+the HBM bytes per launch that rocprofv3's FETCH_SIZE and WRITE_SIZE counters
+recorded (scaled by a copy-kernel calibration), read from the committed
+counter summary and reported only while the indexer source is unchanged.
+`step_hbm` gives the algorithmic-bytes ratio for the whole step.
+`indexshare` times groups of layers that share one selection (one full step,
+then sparse MLA only on the other layers' caches) and reports the amortised
+tokens/s per layer.  `all_128k` repeats the step measurement with every
+context at 131072 tokens.  `cpu_baseline` times the CPU oracle on a bounded
+sample of the same workload.  Inputs rotate over several device copies so
+that the 256 MB Infinity Cache cannot serve a step from the previous one.
 
 Algorithmic bytes of a step (what it must read or write; workspace excluded):
   sum_r  L_r*(D_idx + 4)            fp8 keys + fp32 key scale
@@ -94,6 +100,184 @@ def step_flops(wl, indices):
     return f_idx, f_mla
 
 
+def mla_layer_bytes(wl, indices):
+    """Bytes of one sparse-MLA layer that reuses a selection: distinct selected
+    latent rows, the page-table entries they need, queries and outputs."""
+    import numpy as np
+    e_q = 4 if wl.kv_dtype == "f32" else 2
+    mla_q = wl.mla_heads * (wl.d_latent + wl.d_rope) * e_q + wl.mla_heads * wl.d_latent * e_q
+    total = 0
+    for r in range(wl.batch):
+        ql = int(wl.q_lens[r])
+        q0 = int(wl.query_start_loc[r])
+        sel = indices[q0:q0 + ql]
+        u = np.unique(sel[sel >= 0])
+        total += len(u) * latent_row_bytes(wl) + 4 * len(np.unique(u // wl.block_size))
+        total += ql * mla_q
+    return total
+
+
+# ------------------------------------------------------- measured traffic
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "indexer_fp8_persistent_b64_l8k_128k_traffic.md")
+INDEXER_SOURCES = ("sparse_attention_dsa_amd/csrc/indexer.hip", "sparse_attention_dsa_amd/csrc/dsa_kernels.h")
+
+
+def indexer_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for p in INDEXER_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per indexer launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by its copy-kernel
+    calibration), or None when the summary is missing, covers another
+    workload, or was taken on a different indexer source."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            fields = dict(l.strip().strip("`").split(": ", 1) for l in f if ": " in l and l.startswith("`"))
+    except OSError:
+        return None
+    if fields.get("workload") != workload or fields.get("source-sha256") != indexer_source_hash():
+        return None
+    try:
+        return int(fields["fetch-bytes-per-launch"]) + int(fields["write-bytes-per-launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------ rig
+class Rig:
+    """One workload resident on the device in several rotating copies, with
+    prebuilt ctypes argument tuples so that timed loops only call into the
+    library."""
+
+    def __init__(self, wl, ncopies, log):
+        import ctypes as C
+        import torch
+        import sparse_attention_dsa_amd as dsa
+        from sparse_attention_dsa_amd import binding as B
+        import workloads
+
+        self.wl, self.torch, self.B = wl, torch, B
+        d0 = workloads.to_device(wl, "cuda")
+        self.batch = dsa.Batch(d0["context_lens"], d0["query_start_loc"], d0["page_table"], wl.block_size,
+                               wl.max_q_len, wl.max_context_len)
+        self.copies = [d0]
+        for _ in range(ncopies - 1):
+            dc = dict(d0)
+            for key in ("idx_keys", "idx_scales", "kv", "kv_scales", "q_mla"):
+                if d0[key] is not None:
+                    dc[key] = d0[key].clone()
+            self.copies.append(dc)
+        torch.cuda.synchronize()
+        log("[bench] %s: %d device copies ready" % (wl.name, len(self.copies)))
+
+        T, H, K = wl.total_q, wl.mla_heads, wl.topk
+        self.L = B.lib()
+        self.bst = self.batch.struct()
+        self.ws_step = dsa.workspace_size(B.OP_DECODE_STEP, self.batch, K, H)
+        self.ws_mla = dsa.workspace_size(B.OP_MLA_DECODE, self.batch, K, H)
+        self.ws = torch.empty(max(self.ws_step, self.ws_mla, 256), dtype=torch.uint8, device="cuda")
+        odt = torch.bfloat16 if wl.kv_dtype != "f32" else torch.float32
+        self.outs = [torch.empty((T, H, wl.d_latent), dtype=odt, device="cuda") for _ in self.copies]
+        self.idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+        self.stream = torch.cuda.current_stream()
+        sptr = C.c_void_p(self.stream.cuda_stream)
+        self.ld = (wl.max_context_len + 63) // 64 * 64
+        self.scores = torch.empty((T, self.ld), dtype=torch.float32, device="cuda")
+        wsp, idxp = C.c_void_p(self.ws.data_ptr()), C.c_void_p(self.idx.data_ptr())
+        self.step_args, self.mla_args, self.idx_args, self._keep = [], [], [], []
+        for ci, dc in enumerate(self.copies):
+            ic = B.index_cache(dc["idx_keys"], dc["idx_scales"])
+            lc = B.latent_cache(dc["kv"], dc["kv_scales"], wl.d_latent)
+            self._keep += [ic, lc]
+            outp, qm = C.c_void_p(self.outs[ci].data_ptr()), C.c_void_p(dc["q_mla"].data_ptr())
+            self.step_args.append((C.byref(self.bst), C.byref(ic), C.c_void_p(dc["q_idx"].data_ptr()),
+                                   C.c_void_p(dc["w"].data_ptr()), wl.idx_heads, C.byref(lc), qm, H, K,
+                                   C.c_float(wl.softmax_scale), outp, None, idxp, wsp,
+                                   C.c_size_t(self.ws_step), sptr))
+            self.mla_args.append((C.byref(self.bst), C.byref(lc), qm, H, idxp, K, C.c_float(wl.softmax_scale),
+                                  outp, None, wsp, C.c_size_t(self.ws_mla), sptr))
+            self.idx_args.append((C.byref(self.bst), C.byref(ic), C.c_void_p(dc["q_idx"].data_ptr()),
+                                  C.c_void_p(dc["w"].data_ptr()), wl.idx_heads,
+                                  C.c_void_p(self.scores.data_ptr()), self.ld, sptr))
+
+    def _ok(self, fn, st):
+        if st != 0:
+            raise self.B.DsaError(fn, st)
+
+    def step(self, i):
+        self._ok("dsa_decode_step", self.L.dsa_decode_step(*self.step_args[i % len(self.copies)]))
+
+    def group(self, i, layers):
+        """One IndexShare group: the full step on one layer's caches, then
+        `layers - 1` sparse-MLA layers on other caches reusing its indices."""
+        n = len(self.copies)
+        self.step(i)
+        for l in range(1, layers):
+            self._ok("dsa_sparse_mla_decode", self.L.dsa_sparse_mla_decode(*self.mla_args[(i + l) % n]))
+
+    def indexer(self, i):
+        self._ok("dsa_indexer_scores", self.L.dsa_indexer_scores(*self.idx_args[i % len(self.copies)]))
+
+    def time_loop(self, fn, iters, warmup):
+        """Average ms per call of fn(i) over `iters` calls, bracketed by
+        events on the library's stream after a device-wide sync."""
+        torch = self.torch
+        for i in range(warmup):
+            fn(i)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record(self.stream)
+        for i in range(iters):
+            fn(i)
+        ev1.record(self.stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / iters
+
+    def time_launches(self, fn, iters, warmup):
+        """Average µs of single launches, each bracketed by its own events."""
+        torch = self.torch
+        for i in range(warmup):
+            fn(i)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        torch.cuda.synchronize()
+        for i in range(iters):
+            evs[i][0].record(self.stream)
+            fn(i)
+            evs[i][1].record(self.stream)
+        torch.cuda.synchronize()
+        return 1e3 * sum(a.elapsed_time(b) for a, b in evs) / iters
+
+    def selection(self):
+        self.step(0)
+        self.torch.cuda.synchronize()
+        return self.idx.cpu().numpy()
+
+    def free(self):
+        self.copies = self.outs = self.step_args = self.mla_args = self.idx_args = self._keep = None
+        self.ws = self.idx = self.scores = None
+        self.torch.cuda.empty_cache()
+
+
+def summarize(rig, ms_step, indices, idx_us):
+    wl = rig.wl
+    sb = step_bytes(wl, indices)
+    ib = indexer_launch_bytes(wl)
+    return {
+        "ms_per_step": round(ms_step, 5),
+        "tokens_per_s": round(wl.total_q / (ms_step * 1e-3), 1),
+        "step_bytes": sb,
+        "step_hbm_frac": round(sb / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "indexer_us": round(idx_us, 2),
+        "indexer_hbm_frac": round(ib / (idx_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+    }
+
+
 # ------------------------------------------------------------------ main
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -102,9 +286,12 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--copies", type=int, default=4, help="rotating device copies of the caches")
-    ap.add_argument("--cpu-rows", type=int, default=24, help="query rows in the oracle CPU sample (0: skip)")
+    ap.add_argument("--cpu-rows", type=int, default=64, help="query rows in the oracle CPU sample (0: skip)")
     ap.add_argument("--cpu-threads", type=int, default=0)
-    ap.add_argument("--graph", action="store_true", help="replay the step from a captured HIP graph")
+    ap.add_argument("--share-layers", type=int, default=4,
+                    help="layers per IndexShare group for the amortised figure (0 or 1: skip)")
+    ap.add_argument("--no-128k", action="store_true",
+                    help="skip the extra measurement with every context at 131072 tokens")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -115,8 +302,6 @@ def main(argv=None):
     import numpy as np
     import torch
 
-    import sparse_attention_dsa_amd as dsa
-    from sparse_attention_dsa_amd import binding as B
     import workloads
 
     def log(*a):
@@ -127,100 +312,17 @@ def main(argv=None):
     wl = workloads.make_workload(args.workload)
     log("[bench] workload %s: B=%d T=%d sum L=%d (generated in %.1fs)" %
         (wl.name, wl.batch, wl.total_q, int(wl.context_lens.sum()), time.time() - t0))
-    d0 = workloads.to_device(wl, "cuda")
-    batch = dsa.Batch(d0["context_lens"], d0["query_start_loc"], d0["page_table"], wl.block_size,
-                      wl.max_q_len, wl.max_context_len)
-    copies = [d0]
-    for _ in range(args.copies - 1):
-        dc = dict(d0)
-        for key in ("idx_keys", "idx_scales", "kv", "kv_scales"):
-            if d0[key] is not None:
-                dc[key] = d0[key].clone()
-        copies.append(dc)
-    torch.cuda.synchronize()
-    log("[bench] %d device copies ready" % len(copies))
+    rig = Rig(wl, args.copies, log)
+    T, K = wl.total_q, wl.topk
 
-    T, H, K = wl.total_q, wl.mla_heads, wl.topk
-    L = B.lib()
-    bst = batch.struct()
-    ws_bytes = dsa.workspace_size(B.OP_DECODE_STEP, batch, K, H)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-    outs = [torch.empty((T, H, wl.d_latent), dtype=torch.bfloat16 if wl.kv_dtype != "f32" else torch.float32,
-                        device="cuda") for _ in copies]
-    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
-    stream = torch.cuda.current_stream()
-    sptr = C.c_void_p(stream.cuda_stream)
-
-    # Prebuilt ctypes arguments per copy: the timed loop only calls into the library.
-    calls = []
-    for ci, dc in enumerate(copies):
-        ic = B.index_cache(dc["idx_keys"], dc["idx_scales"])
-        lc = B.latent_cache(dc["kv"], dc["kv_scales"], wl.d_latent)
-        calls.append((C.byref(bst), C.byref(ic), C.c_void_p(dc["q_idx"].data_ptr()), C.c_void_p(dc["w"].data_ptr()),
-                      wl.idx_heads, C.byref(lc), C.c_void_p(dc["q_mla"].data_ptr()), H, K,
-                      C.c_float(wl.softmax_scale), C.c_void_p(outs[ci].data_ptr()), None,
-                      C.c_void_p(idx.data_ptr()), C.c_void_p(ws.data_ptr()), C.c_size_t(ws_bytes), sptr, ic, lc))
-
-    def step(i):
-        a = calls[i % len(calls)]
-        st = L.dsa_decode_step(*a[:16])
-        if st != 0:
-            raise B.DsaError("dsa_decode_step", st)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    graph = None
-    if args.graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(len(calls)):
-                step(i)
-        torch.cuda.synchronize()
-
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    if graph is None:
-        for i in range(args.steps):
-            step(i)
-    else:
-        reps = max(1, args.steps // len(calls))
-        for _ in range(reps):
-            graph.replay()
-        args.steps = reps * len(calls)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    # The timed region: exactly `steps` decode steps.
+    ms_per_step = rig.time_loop(rig.step, args.steps, args.warmup)
     log("[bench] step: %.1f us" % (ms_per_step * 1e3))
-
-    # Selection of the last step (for the byte accounting only).
-    step(0)
-    torch.cuda.synchronize()
-    indices = idx.cpu().numpy()
+    indices = rig.selection()
 
     # Dominant kernel: the lightning indexer, timed launch by launch.
-    ld = (wl.max_context_len + 63) // 64 * 64
-    scores = torch.empty((T, ld), dtype=torch.float32, device="cuda")
-    icalls = []
-    for dc in copies:
-        ic = B.index_cache(dc["idx_keys"], dc["idx_scales"])
-        icalls.append((C.byref(bst), C.byref(ic), C.c_void_p(dc["q_idx"].data_ptr()),
-                       C.c_void_p(dc["w"].data_ptr()), wl.idx_heads, C.c_void_p(scores.data_ptr()), ld, sptr, ic))
-    for i in range(args.warmup):
-        L.dsa_indexer_scores(*icalls[i % len(icalls)][:8])
     n_idx = max(args.steps, 20)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_idx)]
-    torch.cuda.synchronize()
-    for i in range(n_idx):
-        evs[i][0].record(stream)
-        st = L.dsa_indexer_scores(*icalls[i % len(icalls)][:8])
-        evs[i][1].record(stream)
-        if st != 0:
-            raise B.DsaError("dsa_indexer_scores", st)
-    torch.cuda.synchronize()
-    idx_us = 1e3 * sum(a.elapsed_time(b) for a, b in evs) / n_idx
+    idx_us = rig.time_launches(rig.indexer, n_idx, args.warmup)
     idx_bytes = indexer_launch_bytes(wl)
     idx_gbs = idx_bytes / (idx_us * 1e-6) / 1e9
     log("[bench] indexer kernel: %.1f us, %.1f MB -> %.0f GB/s" % (idx_us, idx_bytes / 1e6, idx_gbs))
@@ -228,7 +330,37 @@ def main(argv=None):
     sb = step_bytes(wl, indices)
     f_idx, f_mla = step_flops(wl, indices)
     step_gbs = sb / (ms_per_step * 1e-3) / 1e9
-    tokens_per_s = T / (ms_per_step * 1e-3)
+
+    # IndexShare: one full step then (layers-1) MLA-only layers on the same indices.
+    share = None
+    if args.share_layers >= 2:
+        nl = args.share_layers
+        ms_group = rig.time_loop(lambda i: rig.group(i, nl), max(4, args.steps // nl), 2)
+        gb = sb + (nl - 1) * mla_layer_bytes(wl, indices)
+        share = {"layers_per_group": nl, "ms_per_group": round(ms_group, 5),
+                 "tokens_per_s_per_layer": round(nl * T / (ms_group * 1e-3), 1),
+                 "group_bytes": gb, "hbm_frac": round(gb / (ms_group * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        log("[bench] IndexShare x%d: %.1f us per group -> %.0f tok/s/layer" %
+            (nl, ms_group * 1e3, share["tokens_per_s_per_layer"]))
+
+    traffic = measured_traffic(wl.name)
+    rig.free()
+    del rig
+
+    # Every context at 131072 tokens: the literal 128K point of the metric.
+    at128 = None
+    if not args.no_128k and args.workload == DEFAULT_WORKLOAD:
+        t0 = time.time()
+        wl2 = workloads.make_workload(DEFAULT_WORKLOAD, context_lens=[131072])
+        log("[bench] workload all-128K generated in %.1fs" % (time.time() - t0))
+        rig2 = Rig(wl2, args.copies, log)
+        ms2 = rig2.time_loop(rig2.step, args.steps, args.warmup)
+        ind2 = rig2.selection()
+        us2 = rig2.time_launches(rig2.indexer, n_idx, args.warmup)
+        at128 = dict(workload="batched_b64_l128k", **summarize(rig2, ms2, ind2, us2))
+        log("[bench] all-128K step: %.1f us" % (ms2 * 1e3))
+        rig2.free()
+        del rig2, wl2
 
     # CPU baseline: the oracle on a bounded sample of query rows.
     cpu = None
@@ -247,7 +379,7 @@ def main(argv=None):
 
     res = {
         "metric": "DSA decode tokens/s per layer at 128K ctx, batch 64; HBM GB/s as % of peak",
-        "value": round(tokens_per_s, 1),
+        "value": round(T / (ms_per_step * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -262,16 +394,18 @@ def main(argv=None):
                    "context": "L_r ~ U[8192, 131072]" if wl.name == DEFAULT_WORKLOAD else
                    "L_r = %s" % sorted(set(wl.context_lens.tolist()))[:4],
                    "mean_context": round(float(wl.context_lens.mean()), 1), "topk": K,
-                   "indexer": "%dx%d e4m3" % (wl.idx_heads, wl.idx_dim), "mla_heads": H,
+                   "indexer": "%dx%d e4m3" % (wl.idx_heads, wl.idx_dim), "mla_heads": wl.mla_heads,
                    "latent": "%d+%d %s" % (wl.d_latent, wl.d_rope, wl.kv_dtype), "block_size": wl.block_size,
-                   "input_copies": len(copies), "hip_graph": bool(graph is not None)},
-        "roofline": {"bound": "hbm", "kernel": "indexer_fp8_mfma", "achieved": round(idx_gbs, 1),
+                   "input_copies": args.copies},
+        "roofline": {"bound": "hbm", "kernel": "indexer_fp8_persistent", "achieved": round(idx_gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(idx_gbs / PEAK_HBM_GBS, 4),
-                     "traffic": None, "bytes_per_launch": idx_bytes, "us_per_launch": round(idx_us, 2)},
+                     "traffic": traffic, "bytes_per_launch": idx_bytes, "us_per_launch": round(idx_us, 2)},
         "step_hbm": {"bytes": sb, "achieved": round(step_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(step_gbs / PEAK_HBM_GBS, 4)},
         "step_tflops": {"indexer_fp8": round(f_idx / (ms_per_step * 1e-3) / 1e12, 2),
                         "mla_bf16": round(f_mla / (ms_per_step * 1e-3) / 1e12, 2)},
+        "indexshare": share,
+        "all_128k": at128,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

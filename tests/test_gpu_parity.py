@@ -223,3 +223,37 @@ def test_topk_rows_beyond_single_kernel(dup):
     for t, n in enumerate(lens):
         ref = oracle.topk(scores[t, :n].astype(np.float64), 2048)
         assert sorted(ref.tolist()) == idx[t].tolist()
+
+
+@pytest.mark.parametrize("case", ["bf16", "mtp_fp8"])
+def test_indexshare_decode_group(case):
+    """IndexShare decode: the full layer runs the whole step and hands its
+    indices to a shared layer, whose sparse MLA runs on its own latent cache
+    and queries with those indices unchanged."""
+    if case == "bf16":
+        wl = workloads.make_workload("single_b1_l32768", batch=4, context_lens=[3000, 9000, 2048, 20000],
+                                     seed=18, layers=2)
+    else:
+        wl = workloads.make_workload("mtp_b8_l202752", batch=2, context_lens=[5000, 2100], seed=19, layers=2)
+    log("indexshare", case, wl.context_lens.tolist(), "q_len", wl.q_lens.tolist())
+    batch, d = upload(wl)
+    T, H = wl.total_q, wl.mla_heads
+    idx = torch.empty((T, wl.topk), dtype=torch.int32, device="cuda")
+    lse2 = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    out1 = dsa.decode_step(batch, d["idx_keys"], d["idx_scales"], d["q_idx"], d["w"], d["kv"], d["kv_scales"],
+                           wl.d_latent, d["q_mla"], wl.topk, wl.softmax_scale, indices_out=idx)
+    out2 = dsa.sparse_mla_decode(batch, d["kv2"], d["kv2_scales"], wl.d_latent, d["q_mla2"], idx,
+                                 wl.softmax_scale, lse=lse2)
+    torch.cuda.synchronize()
+    out1, out2 = out1.float().cpu().numpy(), out2.float().cpu().numpy()
+    idx, lse2 = idx.cpu().numpy(), lse2.cpu().numpy()
+    res = oracle.run_step(wl, rows=list(range(T)), layers=2)
+    for t in range(T):
+        r = res[t]
+        nd = check_selection(idx[t], r["scores"], wl.topk)
+        sel = idx[t][idx[t] >= 0]
+        check_out(out1[t], r["out"], fp32=False, same_selection=(nd == 0))
+        check_out(out2[t], r["out2"], fp32=False, same_selection=(nd == 0))
+        ref2, rl2 = oracle.query_mla(wl, t, sel, 2)
+        check_out(out2[t], ref2, fp32=False)
+        np.testing.assert_allclose(lse2[t], rl2, rtol=0, atol=1e-3)
