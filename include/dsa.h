@@ -116,7 +116,9 @@ int dsa_indexer_scores(const dsa_batch *batch, const dsa_index_cache *cache,
  *   indices [T][k] int32: the min(k, n_t) selected logical positions of row t
  *           in ascending order, then -1 padding.  Selection rule: highest
  *           score first, lower index first among equal scores.  1 <= k <= 4096.
- *   workspace: dsa_workspace_size(DSA_OP_TOPK, batch, k, 0, 0) bytes.
+ *   workspace: dsa_workspace_size(DSA_OP_TOPK, batch, k, 0, 0) bytes
+ *           (candidate slots for rows longer than 12288 tokens, about 4 bytes
+ *           per score; 0 when no row is that long, and NULL is then accepted).
  */
 int dsa_topk(const dsa_batch *batch, const float *scores, int64_t ld_scores, int32_t k,
              int32_t *indices, void *workspace, size_t workspace_bytes, dsa_stream_t stream);
@@ -165,7 +167,9 @@ int dsa_decode_step(const dsa_batch *batch, const dsa_index_cache *index_cache,
                     void *workspace, size_t workspace_bytes, dsa_stream_t stream);
 
 /* Workspace bytes for `op` (enum dsa_op) with this batch geometry; 0 for an
- * invalid request.  Host-only, never touches the device. */
+ * invalid request and for calls that need none (top-K on rows of at most
+ * 12288 tokens, prefill MLA without splits).  Host-only, never touches the
+ * device. */
 size_t dsa_workspace_size(int32_t op, const dsa_batch *batch, int32_t k, int32_t n_heads,
                           int32_t n_heads_idx);
 

@@ -41,12 +41,19 @@ Geometry geometry(const dsa_batch* b) {
 }
 
 // Workspace pieces (byte offsets from the base, each 256-aligned).
-struct TopkLayout { size_t bitmap, end; int64_t bitmap_ld; };
+struct TopkLayout { size_t bound, count, cmax, cand, end; int nchunks; };
 TopkLayout topk_layout(size_t base, const dsa_batch* b) {
     TopkLayout l;
-    l.bitmap_ld = round_up64(((int64_t)b->max_context_len + 31) / 32);
-    l.bitmap = base;
-    l.end = align_up(l.bitmap + sizeof(uint32_t) * (size_t)b->total_q * (size_t)l.bitmap_ld);
+    l.bound = l.count = l.cmax = l.cand = l.end = base;
+    l.nchunks = 0;
+    if (b->max_context_len > TOPK_LIST) {
+        l.nchunks = (int)(((int64_t)b->max_context_len + TOPK_CHUNK - 1) / TOPK_CHUNK);
+        const size_t rc = (size_t)b->total_q * l.nchunks;
+        l.count = align_up(base + sizeof(uint32_t) * (size_t)b->total_q);
+        l.cmax = align_up(l.count + sizeof(uint32_t) * rc);
+        l.cand = align_up(l.cmax + sizeof(uint32_t) * rc);
+        l.end = align_up(l.cand + sizeof(uint64_t) * rc * TOPK_CAND_CAP);
+    }
     return l;
 }
 
@@ -72,14 +79,15 @@ size_t mla_layout_max(size_t base, const dsa_batch* b, int k, int n_heads, bool 
     return end;
 }
 
-struct StepLayout { size_t scores, indices; TopkLayout tk; MlaLayout ml; size_t end; int64_t ld; };
+struct StepLayout { size_t scores, indices, mla_base; TopkLayout tk; MlaLayout ml; size_t end; int64_t ld; };
 StepLayout step_layout(const dsa_batch* b, int k, int n_heads, int mla_path_id) {
     StepLayout l;
     l.ld = round_up64(b->max_context_len);
     l.scores = 0;
     l.indices = align_up(sizeof(float) * (size_t)b->total_q * l.ld);
     l.tk = topk_layout(align_up(l.indices + sizeof(int32_t) * (size_t)b->total_q * k), b);
-    l.ml = mla_layout(l.tk.end, b, k, n_heads, false, mla_path_id);
+    l.mla_base = l.tk.end;
+    l.ml = mla_layout(l.mla_base, b, k, n_heads, false, mla_path_id);
     l.end = l.ml.end;
     return l;
 }
@@ -91,13 +99,17 @@ TopkArgs topk_args(const dsa_batch* b, const float* scores, int64_t ld, int k, i
     TopkArgs a;
     a.g = geometry(b);
     a.scores = scores; a.ld = ld; a.k = k; a.indices = indices;
-    a.bitmap = (uint32_t*)(base + l.bitmap);
-    a.bitmap_ld = l.bitmap_ld;
+    a.bound = (uint32_t*)(base + l.bound);
+    a.cand_count = (uint32_t*)(base + l.count);
+    a.cand_max = (uint32_t*)(base + l.cmax);
+    a.cand = (uint64_t*)(base + l.cand);
+    a.nchunks = l.nchunks;
     return a;
 }
 
-// Top-K grid limits: rows x chunk columns of 256-thread workgroups.
-constexpr int64_t TOPK_MAX_CONTEXT = (int64_t)65535 * TOPK_CHUNK;
+// Top-K limits: one workgroup per row; byte offsets of the scores it reads
+// (a row plus two streaming steps) stay below 2^31.
+constexpr int64_t TOPK_MAX_CONTEXT = (int64_t)1 << 28;
 constexpr int32_t TOPK_MAX_ROWS = 1 << 24;
 bool topk_shape_ok(const dsa_batch* b, int k) {
     return k <= TOPK_MAX_K && b->max_context_len <= TOPK_MAX_CONTEXT && b->total_q <= TOPK_MAX_ROWS;
@@ -231,7 +243,7 @@ size_t dsa_workspace_size(int32_t op, const dsa_batch* b, int32_t k, int32_t n_h
     switch (op) {
     case DSA_OP_TOPK:
         if (k < 1 || k > TOPK_MAX_K) return 0;
-        return topk_layout(0, b).end;
+        return topk_layout(0, b).end;   // 0 when no row exceeds TOPK_LIST
     case DSA_OP_MLA_DECODE:
     case DSA_OP_MLA_PREFILL:
         if (k < 1 || n_heads < 1) return 0;
@@ -269,7 +281,7 @@ int dsa_topk(const dsa_batch* b, const float* scores, int64_t ld, int32_t k, int
     if (!batch_ok(b) || !scores || !indices || k < 1 || ld < b->max_context_len) return DSA_ERR_INVALID_ARG;
     if (!topk_shape_ok(b, k)) return DSA_ERR_UNSUPPORTED;
     const TopkLayout l = topk_layout(0, b);
-    if (!ws || ws_bytes < l.end) return DSA_ERR_WORKSPACE;
+    if (l.end > 0 && (!ws || ws_bytes < l.end)) return DSA_ERR_WORKSPACE;
     int st = check_device_cached();
     if (st != DSA_OK) return st;
     const TopkArgs a = topk_args(b, scores, ld, k, indices, (char*)ws, l);
@@ -325,7 +337,7 @@ int dsa_decode_step(const dsa_batch* b, const dsa_index_cache* ic, const void* q
     hipError_t e = launch_indexer(ia, s);
     if (e == hipSuccess) e = launch_topk(tk, s);
     if (e != hipSuccess) return DSA_ERR_LAUNCH;
-    return run_mla(b, lc, q_mla, n_heads, indices, k, scale, out, lse, base, ws_bytes, l.tk.end, false, s);
+    return run_mla(b, lc, q_mla, n_heads, indices, k, scale, out, lse, base, ws_bytes, l.mla_base, false, s);
 }
 
 }  // extern "C"

@@ -14,9 +14,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-// Largest supported K, and scores per workgroup of the top-K candidate pass.
+// Top-K: largest supported K; rows longer than TOPK_LIST are cut into
+// TOPK_CHUNK-score chunks whose candidates fill slots of TOPK_CAND_CAP.
 constexpr int TOPK_MAX_K = 4096;
+constexpr int TOPK_LIST = 12288;
 constexpr int TOPK_CHUNK = 8192;
+constexpr int TOPK_CAND_CAP = 4096;
 
 // ----------------------------------------------------------- conversions
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
@@ -124,8 +127,12 @@ struct TopkArgs {
     const float* scores; int64_t ld;
     int k;
     int32_t* indices;        // [T][k] result
-    uint32_t* bitmap;        // [T][bitmap_ld] candidate bitmap over each row
-    int64_t bitmap_ld;
+    // workspace (rows longer than TOPK_LIST only)
+    uint32_t* bound;         // [T] sample key bound
+    uint32_t* cand_count;    // [T][nchunks] candidates per chunk
+    uint32_t* cand_max;      // [T][nchunks] largest candidate key per chunk
+    uint64_t* cand;          // [T][nchunks][TOPK_CAND_CAP] composites in token order
+    int nchunks;
 };
 
 struct MlaArgs {
@@ -144,7 +151,7 @@ int device_cu_count();
 
 // Launchers (return hipError_t of the last launch).
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
-// Candidate pass then per-row selection.
+// Sample bound, chunk compaction, then one selection workgroup per row.
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_mla(const MlaArgs& a, bool prefill, hipStream_t s);
 

@@ -9,41 +9,42 @@
 // the lower index first among equal scores, so "the K largest composite keys"
 // is exactly the selection the rule asks for.
 //
-// Two kernels, one streaming pass over the scores:
-//   candidate pass   rows longer than SEL_LIST are cut into TOPK_CHUNK-score
-//                    chunks, one 256-thread workgroup each.  Every workgroup of
-//                    a row draws the same strided sample of the row and takes a
-//                    key bound X that, for any ordering that is not adversarial
-//                    to the stride, has well over K scores of the row above it
-//                    (the sample rank sits six binomial standard deviations
-//                    past the expected rank of the K-th score).  It then writes
-//                    its chunk's bitmap of "score >= X" as whole words, one
-//                    ballot per 64 scores: one compare per score, no atomics.
-//   selection        one 1024-thread workgroup per row compacts the bitmap into
-//                    an LDS list of composite keys in ascending token order
-//                    (short rows load all their scores instead).  If the list
-//                    holds at least K entries it contains the whole top K; the
-//                    K-th largest composite T* is found with a histogram over
-//                    buckets spread across the list's key range, then an exact
-//                    pass over the threshold bucket.  The entries >= T* are
-//                    written out in list order.  When the sample bound fails
-//                    (fewer than K candidates, or more than the list holds) the
-//                    same selection runs over the whole row from memory.
+// Rows longer than SEL_LIST take three kernels and read their scores once:
+//   bound      one workgroup per row draws a strided sample of the row and
+//              takes a key bound X that, for any ordering that is not
+//              adversarial to the stride, has well over K scores of the row at
+//              or above it (the sample rank sits six binomial standard
+//              deviations past the expected rank of the K-th score);
+//   compact    one workgroup per TOPK_CHUNK scores of a row writes the
+//              composites of its scores >= X, in token order, to the chunk's
+//              slot of the candidate buffer (the whole chip streams the rows);
+//   select     one workgroup per row gathers its chunks' candidates into an
+//              LDS list, still in ascending token order.  If the list holds at
+//              least K entries it contains the whole top K; the K-th largest
+//              composite T* is found with a histogram over buckets spread
+//              across the list's key range, then an exact pass over the
+//              threshold bucket, and the entries >= T* are written out in list
+//              order.
+// When the sample bound fails (fewer than K candidates, a chunk slot or the
+// list overflowing) the same selection runs over the whole row from memory.
+// Rows of at most SEL_LIST tokens load all their scores into the list
+// directly and skip the first two kernels.
 #include "dsa_kernels.h"
 
 namespace dsa {
 
-constexpr int TK_THREADS = 256;                        // candidate pass
-constexpr int TK_PER_LANE = TOPK_CHUNK / TK_THREADS;   // scores per lane
-constexpr int TK_WAVE_SPAN = 64 * TK_PER_LANE;         // contiguous scores per wave
 constexpr int TK_SAMPLE = 1024;                        // sample per 128K scores of row
 constexpr int TK_SAMPLE_MAX = 4096;
 constexpr int TK_SAMPLE_BINS = 256;
-static_assert(TK_PER_LANE == 32, "each lane ends up holding one bitmap word of its wave");
+constexpr int BND_THREADS = 256;                       // bound kernel
+constexpr int CMP_THREADS = 256;                       // compaction kernel
+constexpr int CMP_PER = TOPK_CHUNK / CMP_THREADS;      // scores per thread
+static_assert(CMP_PER % 4 == 0, "16-byte loads");
+static_assert(TOPK_CAND_CAP <= TOPK_CHUNK, "a chunk slot never needs more than its chunk");
 
 constexpr int SEL_THREADS = 1024;                      // selection
 constexpr int SEL_WAVES = SEL_THREADS / 64;
-constexpr int SEL_LIST = 12288;                        // candidates held in LDS
+constexpr int SEL_LIST = TOPK_LIST;                    // candidates held in LDS
 constexpr int SEL_BINS = 4096;
 constexpr int SEL_MEMBERS = 4096;                      // threshold-bucket members sorted directly
 static_assert(SEL_LIST > TOPK_MAX_K, "short rows go straight to the list");
@@ -77,17 +78,51 @@ __device__ __forceinline__ uint32_t range_shift(uint32_t lo, uint32_t hi, uint32
     return sh;
 }
 
-// Exclusive prefix sum over the 64 lanes of a wave; *total gets the wave sum.
+// ---------------------------------------------------------------- wave ops
+// Cross-lane steps use DPP (row shifts within 16-lane rows, then row
+// broadcasts), which run at ALU latency instead of through the LDS crossbar.
+constexpr int DPP_ROW_SHR1 = 0x111, DPP_ROW_SHR2 = 0x112, DPP_ROW_SHR4 = 0x114, DPP_ROW_SHR8 = 0x118;
+constexpr int DPP_ROW_BCAST15 = 0x142, DPP_ROW_BCAST31 = 0x143;
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+    v += __builtin_amdgcn_update_dpp(0u, v, DPP_ROW_SHR1, 0xF, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0u, v, DPP_ROW_SHR2, 0xF, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0u, v, DPP_ROW_SHR4, 0xF, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0u, v, DPP_ROW_SHR8, 0xF, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0u, v, DPP_ROW_BCAST15, 0xA, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0u, v, DPP_ROW_BCAST31, 0xC, 0xF, false);
+    return v;
+}
+
+// Exclusive prefix sum over the wave; *total gets the wave sum.
 __device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t* total) {
-    const int lane = threadIdx.x & 63;
-    uint32_t x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    *total = __shfl(x, 63);
-    return x - v;
+    const uint32_t inc = wave_incl_scan(v);
+    *total = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+    return inc - v;
+}
+
+// Wave-wide minimum and maximum (uniform results).  Lanes whose DPP source
+// lies outside their row keep their own value.
+__device__ __forceinline__ void wave_min_max(uint32_t& mn, uint32_t& mx) {
+#define DSA_MINMAX_STEP(ctrl, rmask)                                                               \
+    mn = min(mn, (uint32_t)__builtin_amdgcn_update_dpp((int)mn, (int)mn, ctrl, rmask, 0xF, false)); \
+    mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp((int)mx, (int)mx, ctrl, rmask, 0xF, false));
+    DSA_MINMAX_STEP(DPP_ROW_SHR1, 0xF)
+    DSA_MINMAX_STEP(DPP_ROW_SHR2, 0xF)
+    DSA_MINMAX_STEP(DPP_ROW_SHR4, 0xF)
+    DSA_MINMAX_STEP(DPP_ROW_SHR8, 0xF)
+    DSA_MINMAX_STEP(DPP_ROW_BCAST15, 0xA)
+    DSA_MINMAX_STEP(DPP_ROW_BCAST31, 0xC)
+#undef DSA_MINMAX_STEP
+    mn = (uint32_t)__builtin_amdgcn_readlane((int)mn, 63);
+    mx = (uint32_t)__builtin_amdgcn_readlane((int)mx, 63);
+}
+
+// Workgroup barrier that orders LDS traffic only: unlike __syncthreads() it
+// does not wait for this wave's global loads still in flight.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Exclusive prefix sum over the workgroup (wsum: one slot per wave).
@@ -97,7 +132,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
     uint32_t wt;
     const uint32_t wex = wave_excl_scan(v, &wt);
     if (lane == 0) wsum[wave] = wt;
-    __syncthreads();
+    lds_barrier();
     uint32_t ex = wex, tot = 0;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) {
@@ -105,9 +140,23 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
         ex += w < wave ? x : 0u;
         tot += x;
     }
-    __syncthreads();
+    lds_barrier();
     *total = tot;
     return ex;
+}
+
+// Workgroup-wide minimum and maximum (red: two slots per wave).
+template <int WAVES>
+__device__ __forceinline__ void block_min_max(uint32_t& mn, uint32_t& mx, uint32_t (*red)[WAVES]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    wave_min_max(mn, mx);
+    if (lane == 0) { red[0][wave] = mn; red[1][wave] = mx; }
+    lds_barrier();
+    mn = red[0][0];
+    mx = red[1][0];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) { mn = min(mn, red[0][w]); mx = max(mx, red[1][w]); }
+    lds_barrier();
 }
 
 // LDS counter increment; one atomic per wave when all active lanes share the
@@ -117,7 +166,7 @@ __device__ __forceinline__ void lds_count(uint32_t* h, uint32_t bin, bool active
     if (act == 0ull) return;
     const int lane = threadIdx.x & 63;
     const int first = __ffsll((long long)act) - 1;
-    const uint32_t b0 = (uint32_t)__shfl((int)bin, first);
+    const uint32_t b0 = (uint32_t)__builtin_amdgcn_readlane((int)bin, first);
     if (__ballot(active && bin == b0) == act) {
         if (lane == first) atomicAdd(&h[b0], (uint32_t)__popcll(act));
     } else if (active) {
@@ -126,61 +175,41 @@ __device__ __forceinline__ void lds_count(uint32_t* h, uint32_t bin, bool active
 }
 
 // ---------------------------------------------------------------------------
-// Candidate pass.
-__global__ __launch_bounds__(TK_THREADS) void topk_candidates(TopkArgs a) {
-    const int t = blockIdx.x, c = blockIdx.y;
+// Bound kernel.
+__global__ __launch_bounds__(BND_THREADS) void topk_bound(TopkArgs a) {
+    constexpr int WAVES = BND_THREADS / 64;
+    constexpr int NS = TK_SAMPLE_MAX / BND_THREADS;
+    const int t = blockIdx.x;
     const int n = row_visible(a.g, t);
-    const int c0 = c * TOPK_CHUNK;
-    if (n <= SEL_LIST || c0 >= n) return;
-    const int K = a.k;
+    if (n <= SEL_LIST) return;
+    const uint32_t K = (uint32_t)a.k;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float* row = a.scores + (size_t)t * a.ld;
     __shared__ uint32_t h[TK_SAMPLE_BINS];
-    __shared__ uint32_t red[2][TK_THREADS / 64];
-    __shared__ uint32_t bound;
+    __shared__ uint32_t red[2][WAVES];
+    static_assert(TK_SAMPLE_BINS == BND_THREADS, "one bucket per thread");
 
-    // the row's sample (identical in every chunk of the row), then the chunk;
-    // positions past the row read as NaN, which fails every ">=" test
     const int m = TK_SAMPLE * min(TK_SAMPLE_MAX / TK_SAMPLE, (n + 131071) / 131072);
-    const int ns = m / TK_THREADS;
-    float smp[TK_SAMPLE_MAX / TK_THREADS];
+    const int ns = m / BND_THREADS;
+    uint32_t key[NS];
 #pragma unroll
-    for (int i = 0; i < TK_SAMPLE_MAX / TK_THREADS; ++i)
-        if (i < ns) smp[i] = row[(int)((long long)(tid + i * TK_THREADS) * n / m)];
-    const int w0 = c0 + wave * TK_WAVE_SPAN;
-    float v[TK_PER_LANE];
-#pragma unroll
-    for (int j = 0; j < TK_PER_LANE; ++j) {
-        const int s = w0 + j * 64 + lane;
-        v[j] = s < n ? row[s] : __builtin_nanf("");
-    }
+    for (int i = 0; i < NS; ++i)
+        if (i < ns) key[i] = score_key(row[(int)((long long)(tid + i * BND_THREADS) * n / m)]);
     h[tid] = 0u;
-    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
-    for (int i = 0; i < TK_SAMPLE_MAX / TK_THREADS; ++i)
-        if (i < ns) {
-            const uint32_t k = score_key(smp[i]);
-            mn = min(mn, k);
-            mx = max(mx, k);
-        }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        mn = min(mn, (uint32_t)__shfl_xor((int)mn, off));
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
-    }
-    if (lane == 0) { red[0][wave] = mn; red[1][wave] = mx; }
-    __syncthreads();
-    uint32_t lo = red[0][0], hi = red[1][0];
-#pragma unroll
-    for (int w = 1; w < TK_THREADS / 64; ++w) { lo = min(lo, red[0][w]); hi = max(hi, red[1][w]); }
+    for (int i = 0; i < NS; ++i)
+        if (i < ns) { lo = min(lo, key[i]); hi = max(hi, key[i]); }
+    block_min_max<WAVES>(lo, hi, red);
     const uint32_t sh = range_shift(lo, hi, TK_SAMPLE_BINS);
 #pragma unroll
-    for (int i = 0; i < TK_SAMPLE_MAX / TK_THREADS; ++i)
-        if (i < ns) atomicAdd(&h[bucket_of(score_key(smp[i]), lo, sh, TK_SAMPLE_BINS)], 1u);
-    __syncthreads();
+    for (int i = 0; i < NS; ++i)
+        if (i < ns) atomicAdd(&h[bucket_of(key[i], lo, sh, TK_SAMPLE_BINS)], 1u);
+    lds_barrier();
     // Sample rank r: the expected rank of the K-th score plus six standard
     // deviations of a binomial count, plus a margin.  X = lower key bound of the
-    // highest bucket whose cumulative count (from the top) reaches r.
+    // highest bucket whose cumulative count (from the top) reaches r; 0 (take
+    // everything) when the sample never reaches r.
     if (wave == 0) {
         const float q = (float)K / (float)n, mq = (float)m * q;
         const uint32_t r = (uint32_t)ceilf(mq + 6.f * sqrtf(mq * (1.f - q))) + 8u;
@@ -189,32 +218,106 @@ __global__ __launch_bounds__(TK_THREADS) void topk_candidates(TopkArgs a) {
         for (int j = 0; j < 4; ++j) { c4[j] = h[TK_SAMPLE_BINS - 1 - 4 * lane - j]; sum += c4[j]; }
         uint32_t tot;
         const uint32_t ex = wave_excl_scan(sum, &tot);
-        if (lane == 0 && tot < r) bound = 0u;   // the sample never reaches r: take everything
+        if (lane == 0 && tot < r) a.bound[t] = 0u;
         if (ex < r && ex + sum >= r) {
             uint32_t cum = ex;
             for (int j = 0; j < 4; ++j) {
                 cum += c4[j];
                 if (cum >= r) {
                     const uint32_t b = (uint32_t)(TK_SAMPLE_BINS - 1 - 4 * lane - j);
-                    bound = b == 0u ? 0u : lo + (b << sh);
+                    a.bound[t] = b == 0u ? 0u : lo + (b << sh);
                     break;
                 }
             }
         }
     }
-    __syncthreads();
-    const float xf = key_floor(bound);
+}
 
-    // Step j covers scores w0 + 64j .. +63: bitmap words 2j and 2j+1 of this
-    // wave, which end up in lanes 2j and 2j+1.
-    uint32_t word = 0u;
+// ---------------------------------------------------------------------------
+// Compaction kernel.  Wave w covers scores [c0 + 2048w, +2048); its load j
+// covers 256 of them, 4 per lane, so each load is one contiguous 1 KB.  The
+// token order inside the chunk is (wave, load, lane, element), so positions
+// come from one wave scan per load plus the waves' totals.
+__global__ __launch_bounds__(CMP_THREADS) void topk_compact(TopkArgs a) {
+    constexpr int WAVES = CMP_THREADS / 64;
+    constexpr int NL = CMP_PER / 4;                 // loads per lane
+    constexpr int WSPAN = TOPK_CHUNK / WAVES;       // scores per wave
+    const int t = blockIdx.x, c = blockIdx.y;
+    const int n = row_visible(a.g, t);
+    const int c0 = c * TOPK_CHUNK;
+    if (n <= SEL_LIST || c0 >= n) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ uint32_t wsum[WAVES], wmax[WAVES];
+    const float* row = a.scores + (size_t)t * a.ld;
+    const int wbase = c0 + WSPAN * wave + 4 * lane;   // + 256 j: this lane's 4 scores of load j
+    float v[NL][4];
+    if ((reinterpret_cast<uintptr_t>(row) & 15u) == 0u) {
+        // the range check returns zeros past the row's allocation (positions
+        // past n are masked below)
+        const uint32_t bytes = (uint32_t)min<int64_t>(4 * a.ld, (int64_t)1 << 31);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)row, 0, (int)bytes, 0x00020000);
 #pragma unroll
-    for (int j = 0; j < TK_PER_LANE; ++j) {
-        const unsigned long long mk = __ballot(v[j] >= xf);
-        if (lane == 2 * j) word = (uint32_t)mk;
-        if (lane == 2 * j + 1) word = (uint32_t)(mk >> 32);
+        for (int j = 0; j < NL; ++j) {
+            const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(4u * (uint32_t)(wbase + 256 * j)), 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[j][e] = __uint_as_float(q[e]);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < NL; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int s = wbase + 256 * j + e;
+                v[j][e] = s < n ? row[s] : 0.f;
+            }
     }
-    if (w0 + 32 * lane < n) a.bitmap[(size_t)t * a.bitmap_ld + (w0 >> 5) + lane] = word;
+    const float xf = key_floor(a.bound[t]);
+    uint32_t keep[NL], pos[NL];
+    uint32_t wtot = 0;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+        keep[j] = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int s = wbase + 256 * j + e;
+            keep[j] |= (s < n && v[j][e] >= xf ? 1u : 0u) << e;
+        }
+        uint32_t tj;
+        pos[j] = wtot + wave_excl_scan((uint32_t)__popc(keep[j]), &tj);
+        wtot += tj;
+    }
+    // largest kept key (0 when none is kept)
+    uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < NL; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if ((keep[j] >> e) & 1u) kmax = max(kmax, score_key(v[j][e]));
+    wave_min_max(kmin, kmax);
+    if (lane == 0) { wsum[wave] = wtot; wmax[wave] = kmax; }
+    lds_barrier();
+    uint32_t woff = 0, tot = 0, cmax = 0u;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+        const uint32_t x = wsum[w];
+        woff += w < wave ? x : 0u;
+        tot += x;
+        cmax = max(cmax, wmax[w]);
+    }
+    const size_t slot = (size_t)t * a.nchunks + c;
+    if (tid == 0) {
+        a.cand_count[slot] = tot;   // above the cap: the slot overflowed
+        a.cand_max[slot] = cmax;
+    }
+    if (tot > (uint32_t)TOPK_CAND_CAP) return;
+    uint64_t* dst = a.cand + slot * TOPK_CAND_CAP + woff;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+        uint32_t p = pos[j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if ((keep[j] >> e) & 1u) dst[p++] = composite(score_key(v[j][e]), wbase + 256 * j + e);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -225,34 +328,29 @@ struct SelShared {
         uint32_t hist[SEL_BINS];
         uint64_t members[SEL_MEMBERS];
     } r;
+    uint32_t off[SEL_THREADS];   // list offset of each chunk's candidates
     uint32_t wsum[SEL_WAVES];
     uint32_t red[2][SEL_WAVES];
     uint32_t st[8];
 };
 
-// The K-th largest composite key over source entries i < count (get(i, ck)
+template <class Get>
+__device__ uint64_t kth_from_hist(int count, uint32_t K, const Get& get, SelShared& S, uint32_t lo, uint32_t sh);
+
+// The K-th largest composite key over source entries i < count (get(i)
 // fetches entry i); count >= K.  Called by the whole workgroup.
 template <class Get>
 __device__ uint64_t kth_composite(int count, uint32_t K, const Get& get, SelShared& S) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x;
     // 1. key range of the entries
-    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
     for (int i = tid; i < count; i += SEL_THREADS) {
         const uint32_t k = composite_key(get(i));
-        mn = min(mn, k);
-        mx = max(mx, k);
+        lo = min(lo, k);
+        hi = max(hi, k);
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        mn = min(mn, (uint32_t)__shfl_xor((int)mn, off));
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
-    }
-    if (lane == 0) { S.red[0][wave] = mn; S.red[1][wave] = mx; }
     for (int i = tid; i < SEL_BINS; i += SEL_THREADS) S.r.hist[i] = 0u;
-    __syncthreads();
-    uint32_t lo = S.red[0][0], hi = S.red[1][0];
-#pragma unroll
-    for (int w = 1; w < SEL_WAVES; ++w) { lo = min(lo, S.red[0][w]); hi = max(hi, S.red[1][w]); }
+    block_min_max<SEL_WAVES>(lo, hi, S.red);
     const uint32_t sh = range_shift(lo, hi, SEL_BINS);
 
     // 2. histogram over SEL_BINS buckets spread across [lo, hi]
@@ -262,8 +360,15 @@ __device__ uint64_t kth_composite(int count, uint32_t K, const Get& get, SelShar
         const uint32_t b = ok ? bucket_of(composite_key(get(i)), lo, sh, SEL_BINS) : 0u;
         lds_count(S.r.hist, b, ok);
     }
-    __syncthreads();
+    lds_barrier();
+    return kth_from_hist(count, K, get, S, lo, sh);
+}
 
+// Steps 3 and 4 of the above, given the histogram of the entries over
+// SEL_BINS buckets of 2^sh keys from lo (in S.r.hist).
+template <class Get>
+__device__ uint64_t kth_from_hist(int count, uint32_t K, const Get& get, SelShared& S, uint32_t lo, uint32_t sh) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // 3. threshold bucket b*: count(> b*) < K <= count(>= b*); thread i owns
     // buckets 4095-4i .. 4092-4i
     uint32_t c4[4], sum = 0;
@@ -284,9 +389,9 @@ __device__ uint64_t kth_composite(int count, uint32_t K, const Get& get, SelShar
         }
     }
     if (tid == 0) S.st[3] = 0u;
-    __syncthreads();
+    lds_barrier();
     const uint32_t bstar = S.st[0], need = K - S.st[1], nb = S.st[2];
-    __syncthreads();   // the histogram space is reused below
+    lds_barrier();   // the histogram space is reused below
 
     if (nb <= (uint32_t)SEL_MEMBERS) {
         // 4a. the threshold bucket's members: descending bitonic sort
@@ -304,15 +409,15 @@ __device__ uint64_t kth_composite(int count, uint32_t K, const Get& get, SelShar
                 uint32_t pos = 0;
                 if (lane == first) pos = atomicAdd(&S.st[3], (uint32_t)__popcll(mk));
                 const unsigned long long below = lane ? (mk & ((1ull << lane) - 1ull)) : 0ull;
-                pos = (uint32_t)__shfl((int)pos, first) + (uint32_t)__popcll(below);
+                pos = (uint32_t)__builtin_amdgcn_readlane((int)pos, first) + (uint32_t)__popcll(below);
                 if (mem) S.r.members[pos] = ck;
             }
         }
-        __syncthreads();
+        lds_barrier();
         int P = 1;
         while (P < (int)nb) P <<= 1;
         for (int i = (int)nb + tid; i < P; i += SEL_THREADS) S.r.members[i] = 0ull;   // sorts last
-        __syncthreads();
+        lds_barrier();
         for (int size = 2; size <= P; size <<= 1) {
             for (int stride = size >> 1; stride > 0; stride >>= 1) {
                 for (int i = tid; i < P / 2; i += SEL_THREADS) {
@@ -322,11 +427,11 @@ __device__ uint64_t kth_composite(int count, uint32_t K, const Get& get, SelShar
                     const uint64_t x = S.r.members[l0], y = S.r.members[l1];
                     if ((x < y) == desc) { S.r.members[l0] = y; S.r.members[l1] = x; }
                 }
-                __syncthreads();
+                lds_barrier();
             }
         }
         const uint64_t kth = S.r.members[need - 1];
-        __syncthreads();
+        lds_barrier();
         return kth;
     }
 
@@ -337,7 +442,7 @@ __device__ uint64_t kth_composite(int count, uint32_t K, const Get& get, SelShar
     uint64_t prefix = 0;
     for (int d = 56; d >= 0; d -= 8) {
         if (tid < 256) h256[tid] = 0u;
-        __syncthreads();
+        lds_barrier();
         for (int base = 0; base < count; base += SEL_THREADS) {
             const int i = base + tid;
             uint64_t ck = 0;
@@ -349,7 +454,7 @@ __device__ uint64_t kth_composite(int count, uint32_t K, const Get& get, SelShar
             }
             lds_count(h256, (uint32_t)(ck >> d) & 255u, ok);
         }
-        __syncthreads();
+        lds_barrier();
         if (wave == 0) {
             uint32_t cc[4], s4 = 0;
 #pragma unroll
@@ -364,10 +469,10 @@ __device__ uint64_t kth_composite(int count, uint32_t K, const Get& get, SelShar
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
         prefix = (prefix << 8) | S.st[4];
         rem = S.st[5];
-        __syncthreads();
+        lds_barrier();
     }
     return prefix;
 }
@@ -392,6 +497,57 @@ __device__ void write_selected(int count, uint64_t kth, uint32_t K, const Get& g
     }
 }
 
+// Gathers row t's chunk candidates into S.list in chunk order and counts
+// them into the SEL_BINS-bucket histogram over [bound, largest candidate key]
+// (*lo, *sh); returns the entry count, or -1 when a chunk slot overflowed or
+// the list would.  Every thread fetches list positions tid, tid + SEL_THREADS,
+// ... (all its loads issued before any of its LDS stores).
+__device__ int gather_candidates(const TopkArgs& a, int t, int n, SelShared& S, uint32_t* lo_out,
+                                 uint32_t* sh_out) {
+    constexpr int PER = SEL_LIST / SEL_THREADS;
+    const int tid = threadIdx.x;
+    const int nc = (n + TOPK_CHUNK - 1) / TOPK_CHUNK;
+    if (nc > SEL_THREADS) return -1;   // rows of over 8M tokens: the whole-row path
+    const size_t row0 = (size_t)t * a.nchunks;
+    const uint32_t k = tid < nc ? a.cand_count[row0 + tid] : 0u;
+    uint32_t hi = tid < nc ? a.cand_max[row0 + tid] : 0u, mn = 0xFFFFFFFFu;
+    for (int i = tid; i < SEL_BINS; i += SEL_THREADS) S.r.hist[i] = 0u;
+    if (__syncthreads_or(k > (uint32_t)TOPK_CAND_CAP)) return -1;
+    block_min_max<SEL_WAVES>(mn, hi, S.red);
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan<SEL_WAVES>(k, S.wsum, &tot);
+    if ((int)tot > SEL_LIST) return -1;   // uniform
+    const uint32_t lo = a.bound[t], sh = range_shift(lo, max(hi, lo), SEL_BINS);
+    uint32_t* off = S.off;
+    if (tid < nc) off[tid] = ex;
+    lds_barrier();
+    const uint64_t* base = a.cand + row0 * TOPK_CAND_CAP;
+    uint64_t v[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const uint32_t p = (uint32_t)(tid + j * SEL_THREADS);
+        v[j] = 0ull;
+        if (p < tot) {
+            int l = 0, h = nc - 1;   // last chunk whose offset is <= p
+            while (l < h) {
+                const int mid = (l + h + 1) >> 1;
+                if (off[mid] <= p) l = mid; else h = mid - 1;
+            }
+            v[j] = base[(size_t)l * TOPK_CAND_CAP + (p - off[l])];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const uint32_t p = (uint32_t)(tid + j * SEL_THREADS);
+        if (p < tot) S.list[p] = v[j];
+        lds_count(S.r.hist, p < tot ? bucket_of(composite_key(v[j]), lo, sh, SEL_BINS) : 0u, p < tot);
+    }
+    lds_barrier();
+    *lo_out = lo;
+    *sh_out = sh;
+    return (int)tot;
+}
+
 __global__ __launch_bounds__(SEL_THREADS) void topk_select(TopkArgs a) {
     const int t = blockIdx.x;
     const int n = row_visible(a.g, t);
@@ -404,64 +560,34 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_select(TopkArgs a) {
     }
     __shared__ SelShared S;
     const float* row = a.scores + (size_t)t * a.ld;
-    int count = 0;
+    auto get = [&](int i) -> uint64_t { return S.list[i]; };
     if (n <= SEL_LIST) {
         for (int i = tid; i < n; i += SEL_THREADS) S.list[i] = composite(score_key(row[i]), i);
-        count = n;
-    } else {
-        // compact the candidate bitmap: positions by a block scan of popcounts
-        const uint32_t* bm = a.bitmap + (size_t)t * a.bitmap_ld;
-        const int words = (n + 31) >> 5;
-        const int per = (words + SEL_THREADS - 1) / SEL_THREADS;
-        const int w0 = min(words, tid * per), w1 = min(words, w0 + per);
-        uint32_t nb = 0;
-        for (int w = w0; w < w1; ++w) nb += __popc(bm[w]);
-        uint32_t tot;
-        uint32_t pos = block_excl_scan<SEL_WAVES>(nb, S.wsum, &tot);
-        count = (int)tot;
-        if (count >= (int)K && count <= SEL_LIST) {
-            for (int w = w0; w < w1; ++w) {
-                uint32_t bits = bm[w];
-                while (bits) {
-                    const int b = __ffs(bits) - 1;
-                    bits &= bits - 1u;
-                    S.list[pos++] = (uint64_t)(w * 32 + b);
-                }
-            }
-            __syncthreads();
-            constexpr int G = SEL_LIST / SEL_THREADS;
-            float sv[G];
-#pragma unroll
-            for (int j = 0; j < G; ++j) {
-                const int i = tid + j * SEL_THREADS;
-                sv[j] = i < count ? row[(int)S.list[i]] : 0.f;
-            }
-#pragma unroll
-            for (int j = 0; j < G; ++j) {
-                const int i = tid + j * SEL_THREADS;
-                if (i < count) S.list[i] = composite(score_key(sv[j]), (int)S.list[i]);
-            }
-        } else {
-            count = -1;   // the sample bound failed for this row
-        }
-    }
-    __syncthreads();
-    if (count >= 0) {
-        auto get = [&](int i) -> uint64_t { return S.list[i]; };
-        const uint64_t kth = kth_composite(count, K, get, S);
-        write_selected(count, kth, K, get, out, S);
-    } else {
-        auto get = [&](int i) -> uint64_t { return composite(score_key(row[i]), i); };
+        __syncthreads();
         const uint64_t kth = kth_composite(n, K, get, S);
         write_selected(n, kth, K, get, out, S);
+        return;
+    }
+    uint32_t lo, sh;
+    const int count = gather_candidates(a, t, n, S, &lo, &sh);
+    if (count >= (int)K) {
+        const uint64_t kth = kth_from_hist(count, K, get, S, lo, sh);
+        write_selected(count, kth, K, get, out, S);
+    } else {   // the sample bound failed for this row
+        __syncthreads();
+        auto from_row = [&](int i) -> uint64_t { return composite(score_key(row[i]), i); };
+        const uint64_t kth = kth_composite(n, K, from_row, S);
+        write_selected(n, kth, K, from_row, out, S);
     }
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
     if (a.g.max_ctx > SEL_LIST) {
-        const dim3 grid(a.g.T, (a.g.max_ctx + TOPK_CHUNK - 1) / TOPK_CHUNK);
-        hipLaunchKernelGGL(topk_candidates, grid, dim3(TK_THREADS), 0, s, a);
-        const hipError_t e = hipGetLastError();
+        hipLaunchKernelGGL(topk_bound, dim3(a.g.T), dim3(BND_THREADS), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(topk_compact, dim3(a.g.T, a.nchunks), dim3(CMP_THREADS), 0, s, a);
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(topk_select, dim3(a.g.T), dim3(SEL_THREADS), 0, s, a);

@@ -44,13 +44,15 @@ def _batch(B_=2, T=2, maxq=1, maxctx=1000, bs=64, maxblocks=16):
 
 def test_workspace_size_host_only(L):
     b = _batch()
-    ws_topk = L.dsa_workspace_size(B.OP_TOPK, C.byref(b), 2048, 0, 0)
-    assert ws_topk >= 2 * ((1000 + 31) // 32) * 4     # one candidate bit per visible token and row
-    assert L.dsa_workspace_size(B.OP_TOPK, C.byref(b), 0, 0, 0) == 0
-    assert L.dsa_workspace_size(B.OP_TOPK, C.byref(b), 5000, 0, 0) == 0
+    assert L.dsa_workspace_size(B.OP_TOPK, C.byref(b), 2048, 0, 0) == 0     # rows too short to need slots
+    long_ = _batch(maxctx=100000, maxblocks=1600)
+    ws_topk = L.dsa_workspace_size(B.OP_TOPK, C.byref(long_), 2048, 0, 0)
+    assert ws_topk >= 2 * 13 * 4096 * 8                # 13 chunks of candidate slots per row
+    assert L.dsa_workspace_size(B.OP_TOPK, C.byref(long_), 0, 0, 0) == 0
+    assert L.dsa_workspace_size(B.OP_TOPK, C.byref(long_), 5000, 0, 0) == 0
     assert L.dsa_workspace_size(99, C.byref(b), 16, 0, 0) == 0
-    step = L.dsa_workspace_size(B.OP_DECODE_STEP, C.byref(b), 2048, 128, 64)
-    assert step >= 2 * 1000 * 4 + 2 * 2048 * 4 + ws_topk     # scores + indices + selection bitmap
+    step = L.dsa_workspace_size(B.OP_DECODE_STEP, C.byref(long_), 2048, 128, 64)
+    assert step >= 2 * 100000 * 4 + 2 * 2048 * 4 + ws_topk     # scores + indices + candidate slots
     bad = _batch(maxctx=5000)                   # 16 blocks * 64 < 5000
     assert L.dsa_workspace_size(B.OP_TOPK, C.byref(bad), 16, 0, 0) == 0
 
@@ -65,7 +67,8 @@ def test_invalid_arguments_rejected_before_device(L):
     assert L.dsa_indexer_scores(C.byref(b), C.byref(bad_dt), 0x1, 0x1, 64, 0x1, 1024, None) == -2
     assert L.dsa_topk(C.byref(b), 0x1, 1024, 0, 0x1, 0x1, 1 << 30, None) == -1
     assert L.dsa_topk(C.byref(b), 0x1, 1024, 5000, 0x1, 0x1, 1 << 30, None) == -2
-    assert L.dsa_topk(C.byref(b), 0x1, 1024, 16, 0x1, 0x1, 8, None) == -3
+    assert L.dsa_topk(C.byref(long_b := _batch(maxctx=100000, maxblocks=1600)), 0x1, 100000, 16, 0x1, 0x1, 8,
+                      None) == -3                   # workspace too small
     lc = B.DsaLatentCache(0x10, None, B.E4M3, 512, 64)      # fp8 latent needs scales
     assert L.dsa_sparse_mla_decode(C.byref(b), C.byref(lc), 0x1, 128, 0x1, 2048, 0.1, 0x1, None,
                                    0x1, 1 << 30, None) == -2
