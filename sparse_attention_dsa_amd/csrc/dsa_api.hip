@@ -64,8 +64,8 @@ MlaLayout mla_layout(size_t base, const dsa_batch* b, int k, int n_heads, bool p
     l.part_o = l.part_lse = l.end = base;
     if (l.splits > 1) {
         const size_t th = (size_t)b->total_q * n_heads * l.splits;
-        l.part_lse = align_up(base + sizeof(float) * th * 512);
-        l.end = align_up(l.part_lse + sizeof(float) * th);
+        l.part_lse = align_up(base + sizeof(uint16_t) * th * 512);
+        l.end = align_up(l.part_lse + 2 * sizeof(float) * th);
     }
     return l;
 }
@@ -213,7 +213,7 @@ int run_mla(const dsa_batch* b, const dsa_latent_cache* c, const void* q, int n_
     a.splits = l.splits;
     if (l.splits > 1) {
         if (!ws) return DSA_ERR_WORKSPACE;
-        a.part_o = (float*)(ws + l.part_o);
+        a.part_o = (uint16_t*)(ws + l.part_o);
         a.part_lse = (float*)(ws + l.part_lse);
     }
     return launch_status(launch_mla(a, prefill, s));

@@ -142,7 +142,8 @@ struct MlaArgs {
     const int32_t* indices; int k;
     float scale;
     void* out; float* lse;
-    float* part_o; float* part_lse;   // split partials or nullptr
+    uint16_t* part_o;                 // split partials: fp16 [T][H][S][d], or nullptr
+    float* part_lse;                  // [T][H][S][2]: lse and the partial's scale 2^-k
     int splits;
 };
 

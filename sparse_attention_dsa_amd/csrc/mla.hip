@@ -41,6 +41,22 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Split partials are stored as fp16 with one power-of-two scale per (query
+// row, head, slice): the head's largest |value| times 2^k lies in
+// [2^14, 2^15), so every value keeps 11 significant bits relative to it and
+// none overflows.  The combine multiplies by 2^-k.
+__device__ __forceinline__ int part_exponent(float amax) {
+    if (!(amax > 0.f)) return 0;
+    const int e = (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 126;   // amax in [2^(e-1), 2^e)
+    return max(-100, min(100, 15 - e));
+}
+__device__ __forceinline__ float pow2i(int k) { return __uint_as_float((uint32_t)(127 + k) << 23); }
+__device__ __forceinline__ uint32_t pack_f16x2(float x, float y) {
+    const _Float16 hx = (_Float16)x, hy = (_Float16)y;
+    return (uint32_t)__builtin_bit_cast(uint16_t, hx) | ((uint32_t)__builtin_bit_cast(uint16_t, hy) << 16);
+}
+
 typedef __attribute__((address_space(3))) void* lds_vptr;
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 
@@ -301,11 +317,30 @@ void mla_bf16_mfma(MlaArgs a, int slice) {
     const float inv = empty ? 0.f : 1.f / l_run;
     const float lse_nat = empty ? -INFINITY : (m_run + log2f(l_run)) * LN2;
     if (SPLIT) {
-        float* po = a.part_o + (((size_t)t * a.n_heads + head) * a.splits + sp) * M_DL;
+        // the head's values sit in lanes col, col + 16, col + 32, col + 48
+        float amax = 0.f;
 #pragma unroll
         for (int ct = 0; ct < M_DL / 16; ++ct)
-            *(f32x4*)(po + 16 * ct + 4 * g) = oacc[ct] * inv;
-        if (g == 0) a.part_lse[((size_t)t * a.n_heads + head) * a.splits + sp] = lse_nat;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(oacc[ct][i]));
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        const int k = part_exponent(amax * inv);
+        const float sc = inv * pow2i(k);
+        const size_t pidx = ((size_t)t * a.n_heads + head) * a.splits + sp;
+        uint16_t* po = a.part_o + pidx * M_DL;
+#pragma unroll
+        for (int ct = 0; ct < M_DL / 16; ++ct) {
+            const f32x4 o = oacc[ct] * sc;
+            u32x2 w;
+            w[0] = pack_f16x2(o[0], o[1]);
+            w[1] = pack_f16x2(o[2], o[3]);
+            *(u32x2*)(po + 16 * ct + 4 * g) = w;
+        }
+        if (g == 0) {
+            a.part_lse[2 * pidx] = lse_nat;
+            a.part_lse[2 * pidx + 1] = pow2i(-k);
+        }
     } else {
         uint16_t* op = (uint16_t*)a.out + ((size_t)t * a.n_heads + head) * M_DL;
 #pragma unroll
@@ -325,16 +360,23 @@ __global__ __launch_bounds__(128) void mla_combine(MlaArgs a) {
     const size_t th = blockIdx.x;             // (t, h)
     const int c4 = threadIdx.x;               // 4 columns each
     const int S = a.splits;
-    const float* pl = a.part_lse + th * S;
+    const float* pl = a.part_lse + 2 * th * S;   // per slice: lse, 2^-k
+    const uint16_t* po = a.part_o + th * S * M_DL + 4 * c4;
     float mx = -INFINITY;
-    for (int s = 0; s < S; ++s) mx = fmaxf(mx, pl[s]);
+    for (int s = 0; s < S; ++s) mx = fmaxf(mx, pl[2 * s]);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float den = 0.f;
     if (mx != -INFINITY) {
         for (int s = 0; s < S; ++s) {
-            const float wgt = __expf(pl[s] - mx);
+            const float wgt = __expf(pl[2 * s] - mx);
             den += wgt;
-            acc += wgt * *(const f32x4*)(a.part_o + (th * S + s) * M_DL + 4 * c4);
+            const float ws = wgt * pl[2 * s + 1];
+            const u32x2 h = *(const u32x2*)(po + (size_t)s * M_DL);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint16_t b = (uint16_t)(h[i >> 1] >> (16 * (i & 1)));
+                acc[i] += ws * (float)__builtin_bit_cast(_Float16, b);
+            }
         }
         acc *= 1.f / den;
     }
@@ -726,17 +768,30 @@ void mla_h128(MlaArgs a, int slice) {
     const float inv = empty ? 0.f : 1.f / l_tot;
     const float lse_nat = empty ? -INFINITY : (m_run + log2f(l_tot)) * LN2;
     if (SPLIT) {
-        float* po = a.part_o + (((size_t)t * a.n_heads + head) * a.splits + sp) * M_DL;
+        // the head's values sit in lanes c32 and c32 + 32
+        float amax = 0.f;
+#pragma unroll
+        for (int cb = 0; cb < M_DL / 32; ++cb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(oacc[cb][e]));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        const int k = part_exponent(amax * inv);
+        const float sc = inv * pow2i(k);
+        const size_t pidx = ((size_t)t * a.n_heads + head) * a.splits + sp;
+        uint16_t* po = a.part_o + pidx * M_DL;
 #pragma unroll
         for (int cb = 0; cb < M_DL / 32; ++cb)
 #pragma unroll
             for (int e4 = 0; e4 < 4; ++e4) {
-                f32x4 o;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = oacc[cb][4 * e4 + e] * inv;
-                *(f32x4*)(po + 32 * cb + 8 * e4 + 4 * hh) = o;
+                u32x2 w;
+                w[0] = pack_f16x2(oacc[cb][4 * e4] * sc, oacc[cb][4 * e4 + 1] * sc);
+                w[1] = pack_f16x2(oacc[cb][4 * e4 + 2] * sc, oacc[cb][4 * e4 + 3] * sc);
+                *(u32x2*)(po + 32 * cb + 8 * e4 + 4 * hh) = w;
             }
-        if (hh == 0) a.part_lse[((size_t)t * a.n_heads + head) * a.splits + sp] = lse_nat;
+        if (hh == 0) {
+            a.part_lse[2 * pidx] = lse_nat;
+            a.part_lse[2 * pidx + 1] = pow2i(-k);
+        }
     } else {
         uint16_t* op = (uint16_t*)a.out + ((size_t)t * a.n_heads + head) * M_DL;
 #pragma unroll
