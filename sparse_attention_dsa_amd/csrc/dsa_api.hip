@@ -79,20 +79,43 @@ size_t mla_layout_max(size_t base, const dsa_batch* b, int k, int n_heads, bool 
     return end;
 }
 
-struct StepLayout { size_t scores, indices, mla_base; TopkLayout tk; MlaLayout ml; size_t end; int64_t ld; };
+// Decode-step workspace: score rows (written by the indexer, or by the
+// selection's recompute path), indices, the top-K slots of the score-writing
+// path, the candidate lists of the emitting path (bound, count, TOPK_LIST
+// composites per query row), then the MLA partials.
+struct StepLayout {
+    size_t scores, indices, bound, count, cand, mla_base;
+    TopkLayout tk; MlaLayout ml; size_t end; int64_t ld;
+};
 StepLayout step_layout(const dsa_batch* b, int k, int n_heads, int mla_path_id) {
     StepLayout l;
+    const size_t T = (size_t)b->total_q;
     l.ld = round_up64(b->max_context_len);
     l.scores = 0;
-    l.indices = align_up(sizeof(float) * (size_t)b->total_q * l.ld);
-    l.tk = topk_layout(align_up(l.indices + sizeof(int32_t) * (size_t)b->total_q * k), b);
-    l.mla_base = l.tk.end;
+    l.indices = align_up(sizeof(float) * T * l.ld);
+    l.tk = topk_layout(align_up(l.indices + sizeof(int32_t) * T * k), b);
+    l.bound = l.tk.end;
+    l.count = align_up(l.bound + sizeof(uint32_t) * T);
+    l.cand = align_up(l.count + sizeof(uint32_t) * T);
+    l.mla_base = align_up(l.cand + sizeof(uint64_t) * T * TOPK_LIST);
     l.ml = mla_layout(l.mla_base, b, k, n_heads, false, mla_path_id);
     l.end = l.ml.end;
     return l;
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH; }
+
+// Indexer arguments that write score rows (no candidate emission).
+IndexerArgs indexer_args(const dsa_batch* b, const dsa_index_cache* c, const void* q_idx, const float* w,
+                         int n_heads_idx, float* scores, int64_t ld) {
+    IndexerArgs a;
+    a.g = geometry(b);
+    a.keys = c->keys; a.key_scales = c->scales; a.key_dtype = c->dtype; a.dim = c->dim;
+    a.q = q_idx; a.w = w; a.n_heads = n_heads_idx;
+    a.scores = scores; a.ld = ld;
+    a.bound = nullptr; a.row_count = nullptr; a.cand = nullptr; a.k = 0;
+    return a;
+}
 
 TopkArgs topk_args(const dsa_batch* b, const float* scores, int64_t ld, int k, int32_t* indices, char* base,
                    const TopkLayout& l) {
@@ -268,11 +291,7 @@ int dsa_indexer_scores(const dsa_batch* b, const dsa_index_cache* c, const void*
     if (st != DSA_OK) return st;
     if (!scores || ld < b->max_context_len) return DSA_ERR_INVALID_ARG;
     if ((st = check_device_cached()) != DSA_OK) return st;
-    IndexerArgs a;
-    a.g = geometry(b);
-    a.keys = c->keys; a.key_scales = c->scales; a.key_dtype = c->dtype; a.dim = c->dim;
-    a.q = q_idx; a.w = w; a.n_heads = n_heads_idx;
-    a.scores = scores; a.ld = ld;
+    const IndexerArgs a = indexer_args(b, c, q_idx, w, n_heads_idx, scores, ld);
     return launch_status(launch_indexer(a, (hipStream_t)stream));
 }
 
@@ -329,13 +348,18 @@ int dsa_decode_step(const dsa_batch* b, const dsa_index_cache* ic, const void* q
     int32_t* indices = indices_out ? indices_out : (int32_t*)(base + l.indices);
 
     const TopkArgs tk = topk_args(b, scores, l.ld, k, indices, base, l.tk);
-    IndexerArgs ia;
-    ia.g = tk.g;
-    ia.keys = ic->keys; ia.key_scales = ic->scales; ia.key_dtype = ic->dtype; ia.dim = ic->dim;
-    ia.q = q_idx; ia.w = w; ia.n_heads = n_heads_idx;
-    ia.scores = scores; ia.ld = l.ld;
-    hipError_t e = launch_indexer(ia, s);
-    if (e == hipSuccess) e = launch_topk(tk, s);
+    IndexerArgs ia = indexer_args(b, ic, q_idx, w, n_heads_idx, scores, l.ld);
+    hipError_t e;
+    if (indexer_emit_ok(ia)) {   // candidates straight from the indexer, no score rows
+        ia.bound = (uint32_t*)(base + l.bound);
+        ia.row_count = (uint32_t*)(base + l.count);
+        ia.cand = (uint64_t*)(base + l.cand);
+        ia.k = k;
+        e = launch_emit_step(ia, tk, s);
+    } else {
+        e = launch_indexer(ia, s);
+        if (e == hipSuccess) e = launch_topk(tk, s);
+    }
     if (e != hipSuccess) return DSA_ERR_LAUNCH;
     return run_mla(b, lc, q_mla, n_heads, indices, k, scale, out, lse, base, ws_bytes, l.mla_base, false, s);
 }

@@ -120,6 +120,13 @@ struct IndexerArgs {
     const void* keys; const float* key_scales; int key_dtype; int dim;
     const void* q; const float* w; int n_heads;
     float* scores; int64_t ld;
+    // candidate emission (fused decode step; cand == nullptr: write scores):
+    // per query row, the composites of the scores at or above the key bound
+    // go to an unordered list of TOPK_LIST slots instead of the score rows
+    uint32_t* bound;         // [T] key bound (written by the sample kernel)
+    uint32_t* row_count;     // [T] candidates appended (may exceed TOPK_LIST)
+    uint64_t* cand;          // [T][TOPK_LIST]
+    int k;                   // top-K size the bound is drawn for
 };
 
 struct TopkArgs {
@@ -152,6 +159,14 @@ int device_cu_count();
 
 // Launchers (return hipError_t of the last launch).
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
+// Whether the decode step can take the candidate-emission path for this
+// shape (e4m3 keys, dim 128, 16/32/64 heads, 64-token blocks, persistent grid).
+bool indexer_emit_ok(const IndexerArgs& a);
+hipError_t launch_sample_bound(const IndexerArgs& a, hipStream_t s);
+// Sample bound per query row (and zeroed candidate counters), then the
+// indexer emitting candidates, then the selection from the candidate lists
+// (recomputing a row's scores into a.scores where its bound fails).
+hipError_t launch_emit_step(const IndexerArgs& ia, const TopkArgs& ta, hipStream_t s);
 // Sample bound, chunk compaction, then one selection workgroup per row.
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_mla(const MlaArgs& a, bool prefill, hipStream_t s);

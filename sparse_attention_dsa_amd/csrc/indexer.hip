@@ -22,58 +22,10 @@
 //               does the same work with no per-chunk start-up;
 //   chunked     one workgroup per (request, query group, 1024-token chunk),
 //               pages fed by an LDS ring of asynchronous transfers.
-#include "dsa_kernels.h"
+#include "indexer_dev.h"
+#include "topk_dev.h"
 
 namespace dsa {
-
-constexpr int IDX_D = 128;
-constexpr int IDX_PAGE = 64;
-constexpr int IDX_THREADS = 256;
-
-// part[nt] holds, for token 16*nt + (lane & 15), the partial head sum of this
-// lane's 16-lane group g.  Returns the full sum for token `lane` of the page.
-__device__ __forceinline__ float head_sum_transpose(const float part[4], int lane) {
-    const int b1 = (lane >> 5) & 1, b0 = (lane >> 4) & 1;
-    const float send0 = b1 ? part[0] : part[2];
-    const float send1 = b1 ? part[1] : part[3];
-    const float keep0 = b1 ? part[2] : part[0];
-    const float keep1 = b1 ? part[3] : part[1];
-    const float a0 = keep0 + __shfl_xor(send0, 32);
-    const float a1 = keep1 + __shfl_xor(send1, 32);
-    const float send = b0 ? a0 : a1;
-    const float keep = b0 ? a1 : a0;
-    return keep + __shfl_xor(send, 16);
-}
-
-// Scores of one 64-token page for the NQ query rows: 16 MFMAs per row (heads x
-// tokens x full key), ReLU, head weights, head sum across the lane groups, key
-// scale.  Lane l returns the score of token l of the page.
-template <int NQ, int HT>
-__device__ __forceinline__ void page_scores(const i32x8 (&qf)[NQ][HT], const float (&wv)[NQ][HT][4],
-                                            const i32x8 (&kf)[4], float ksc, int lane, int nq,
-                                            float (&out)[NQ]) {
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-        if (j < nq) {
-            float part[4];
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                float acc = 0.f;
-#pragma unroll
-                for (int ht = 0; ht < HT; ++ht) {
-                    const f32x4 c = mfma_fp8_16x16x128(qf[j][ht], kf[nt], zero);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc += wv[j][ht][i] * fmaxf(c[i], 0.f);
-                }
-                part[nt] = acc;
-            }
-            out[j] = head_sum_transpose(part, lane) * ksc;
-        } else {
-            out[j] = 0.f;
-        }
-    }
-}
 
 // ---------------------------------------------------------------------------
 // LDS-ring variant: each wave streams its pages through a private ring of
@@ -254,13 +206,20 @@ constexpr int PER_PF = IDX_PER_PF;
 constexpr int PER_MAX_ITEMS = 4096;        // (request, query group) pairs per launch
 constexpr int PER_WG_PER_CU = 2;
 
-template <int NQ, int HT>
+// EMIT: instead of storing the scores, each wave stages the composites of its
+// scores at or above the row's key bound in LDS and appends them to the row's
+// candidate list with one atomic per flush (at a request change, when the
+// stage fills, and at the end of the share).
+constexpr int STAGE_CAP = 256;     // staged candidates per wave and query row
+
+template <int NQ, int HT, bool EMIT>
 __global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_persistent(IndexerArgs a, int qgroups) {
     const Geometry& G = a.g;
     const int n_items = G.B * qgroups;
     __shared__ int item_off[PER_MAX_ITEMS + 1];
     __shared__ int scan_tmp[IDX_THREADS];
     __shared__ __attribute__((aligned(16))) uint8_t pbuf[4][IDX_PAGE * IDX_D];
+    __shared__ uint64_t stage[EMIT ? 4 : 1][EMIT ? NQ : 1][EMIT ? STAGE_CAP : 1];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, col = lane & 15;
@@ -348,6 +307,22 @@ __global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_persistent(IndexerArg
     i32x8 qf[NQ][HT];
     float wv[NQ][HT][4];
     __amdgpu_buffer_rsrc_t orow[NQ];   // score row of each query, sized to its visible count
+    // EMIT state per query row of the item: row index, visible count, bound,
+    // staged count (all wave-uniform)
+    int trow[NQ], nvis[NQ], nst[NQ];
+    float xf[NQ];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) { trow[j] = 0; nvis[j] = 0; nst[j] = 0; xf[j] = 0.f; }
+    auto flush = [&](int j) {
+        if (nst[j] == 0) return;
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&a.row_count[trow[j]], (uint32_t)nst[j]);
+        base = (uint32_t)__builtin_amdgcn_readlane((int)base, 0);
+        uint64_t* dst = a.cand + (size_t)trow[j] * TOPK_LIST;
+        for (int i = lane; i < nst[j]; i += 64)
+            if (base + (uint32_t)i < (uint32_t)TOPK_LIST) dst[base + i] = stage[wave][j][i];
+        nst[j] = 0;
+    };
     auto load_item = [&](int it) {
         cur_it = it;
         cur_base = __builtin_amdgcn_readfirstlane(item_off[it]);
@@ -361,7 +336,14 @@ __global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_persistent(IndexerArg
         for (int j = 0; j < NQ; ++j) {
             const int t = qs + j0 + min(j, nq - 1);
             const int n_j = j < nq ? L - ql + j0 + j + 1 : 0;
-            orow[j] = __builtin_amdgcn_make_buffer_rsrc(a.scores + (size_t)t * a.ld, 0, 4 * max(n_j, 0), 0x00020000);
+            if constexpr (EMIT) {
+                trow[j] = t;
+                nvis[j] = n_j;
+                xf[j] = key_floor(a.bound[t]);
+            } else {
+                orow[j] = __builtin_amdgcn_make_buffer_rsrc(a.scores + (size_t)t * a.ld, 0, 4 * max(n_j, 0),
+                                                            0x00020000);
+            }
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) {
                 const uint8_t* qp = (const uint8_t*)a.q + ((size_t)t * a.n_heads + 16 * ht + col) * IDX_D + 16 * g;
@@ -373,13 +355,15 @@ __global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_persistent(IndexerArg
         // Use every reloaded value here: the wait for these loads then sits
         // in this (rare) branch, and the page ring's waits after it stay exact.
 #pragma unroll
-        for (int j = 0; j < NQ; ++j)
+        for (int j = 0; j < NQ; ++j) {
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) {
                 asm volatile("" ::"v"(qf[j][ht][0]), "v"(qf[j][ht][4]));
 #pragma unroll
                 for (int i = 0; i < 4; ++i) asm volatile("" ::"v"(wv[j][ht][i]));
             }
+            if constexpr (EMIT) asm volatile("" ::"v"(xf[j]));
+        }
     };
     uint8_t* pb = &pbuf[wave][0];
     const int wt = lane >> 3, wu = lane & 7;
@@ -395,7 +379,13 @@ __global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_persistent(IndexerArg
                 if (bb + 64 < p1) load_batch(bb + 64, nblk, nitem);
             }
             const int it = __builtin_amdgcn_readlane(citem, pc - bb);
-            if (it != cur_it) load_item(it);
+            if (it != cur_it) {
+                if constexpr (EMIT) {
+#pragma unroll
+                    for (int j = 0; j < NQ; ++j) flush(j);
+                }
+                load_item(it);
+            }
             RawPage& cur = ring[sl];
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
@@ -417,12 +407,91 @@ __global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_persistent(IndexerArg
             // out-of-range offsets (past the row's visible count, or a page past
             // the share) are dropped by the buffer range check
             const int pos = (pc - cur_base) * IDX_PAGE + lane;
-            const int voff = p < p1 ? 4 * pos : 0x7FFFFFF0;
+            if constexpr (EMIT) {
 #pragma unroll
-            for (int j = 0; j < NQ; ++j)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ps[j]), orow[j], voff, 0, 0);
+                for (int j = 0; j < NQ; ++j) {
+                    const bool keep = p < p1 && pos < nvis[j] && ps[j] >= xf[j];
+                    const unsigned long long mk = __ballot(keep);
+                    if (mk != 0ull) {
+                        const unsigned long long below = lane ? (mk & ((1ull << lane) - 1ull)) : 0ull;
+                        if (keep) stage[wave][j][nst[j] + __popcll(below)] = composite(score_key(ps[j]), pos);
+                        nst[j] += __popcll(mk);
+                        if (nst[j] > STAGE_CAP - 64) flush(j);
+                    }
+                }
+            } else {
+                const int voff = p < p1 ? 4 * pos : 0x7FFFFFF0;
+#pragma unroll
+                for (int j = 0; j < NQ; ++j)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ps[j]), orow[j], voff, 0, 0);
+            }
         }
     }
+    if constexpr (EMIT) {
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) flush(j);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Sample bound for candidate emission: one 1024-thread workgroup per query
+// row scores the row's strided sample of tokens (same MFMA page scoring, 16
+// tokens per fragment) and writes the key bound the indexer filters with.  It
+// also zeroes the row's candidate counter.  Rows of at most TOPK_LIST tokens
+// take every token (bound 0).
+constexpr int SB_THREADS = 1024;
+constexpr int SB_BATCH = 4;                                        // key fragments in flight per lane
+
+template <int HT>
+__global__ __launch_bounds__(SB_THREADS) void indexer_sample_bound(IndexerArgs a) {
+    const Geometry& G = a.g;
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = row_visible(G, t);
+    if (tid == 0) a.row_count[t] = 0u;
+    if (n <= TOPK_LIST) {
+        if (tid == 0) a.bound[t] = 0u;
+        return;
+    }
+    __shared__ uint32_t skeys[TK_SAMPLE_MAX];
+    __shared__ uint32_t h[256], res;
+    __shared__ uint32_t red[2][SB_THREADS / 64];
+    const int r = G.q_uniform > 0 ? t / G.q_uniform : find_request(G.qsl, G.B, t);
+    const int32_t* pt = G.page_table + (size_t)r * G.max_blocks;
+    const int m = sample_size(n);
+    const int per_wave = m / (SB_THREADS / 64);          // 64 .. 256 samples
+    const int nfrag = per_wave / 16;
+    i32x8 qf[HT];
+    float wv[HT][4];
+    load_query<HT>(a, t, lane, qf, wv);
+    // lane (g, col) of fragment f handles sample i = i0 + 16 f + col; four
+    // fragments in flight at a time (1024 threads leave 128 registers a lane)
+    const int i0 = wave * per_wave + (lane & 15);
+    for (int f0 = 0; f0 < nfrag; f0 += SB_BATCH) {
+        int blk[SB_BATCH], row[SB_BATCH];
+#pragma unroll
+        for (int b = 0; b < SB_BATCH; ++b) {
+            const int s = sample_pos(i0 + 16 * min(f0 + b, nfrag - 1), n, m);
+            blk[b] = pt[s / IDX_PAGE];
+            row[b] = s % IDX_PAGE;
+        }
+        i32x8 kf[SB_BATCH];
+        float ksc[SB_BATCH];
+#pragma unroll
+        for (int b = 0; b < SB_BATCH; ++b) {
+            kf[b] = load_key_fragment(a, blk[b], row[b], lane);
+            ksc[b] = a.key_scales ? a.key_scales[(size_t)blk[b] * IDX_PAGE + row[b]] : 1.f;
+        }
+#pragma unroll
+        for (int b = 0; b < SB_BATCH; ++b) {
+            const float sc = token_head_sum<HT>(qf, wv, kf[b]) * ksc[b];
+            if (lane < 16 && f0 + b < nfrag) skeys[i0 + 16 * (f0 + b)] = score_key(sc);
+        }
+    }
+    lds_barrier();
+    const uint32_t x = sample_key_bound<SB_THREADS>(skeys, m, n, (uint32_t)a.k, h, red, &res);
+    if (tid == 0) a.bound[t] = x;
 }
 
 // Generic path: any head count / dim, fp32 or e4m3 keys and queries, any block
@@ -467,13 +536,33 @@ template <int NQ, int HT>
 static hipError_t launch_fp8(const IndexerArgs& a, hipStream_t s) {
     const int qgroups = (a.g.max_q_len + NQ - 1) / NQ;
     if (a.g.B * qgroups <= PER_MAX_ITEMS) {
-        hipLaunchKernelGGL((indexer_fp8_persistent<NQ, HT>), dim3(device_cu_count() * PER_WG_PER_CU),
-                           dim3(IDX_THREADS), 0, s, a, qgroups);
+        if (a.cand)
+            hipLaunchKernelGGL((indexer_fp8_persistent<NQ, HT, true>), dim3(device_cu_count() * PER_WG_PER_CU),
+                               dim3(IDX_THREADS), 0, s, a, qgroups);
+        else
+            hipLaunchKernelGGL((indexer_fp8_persistent<NQ, HT, false>), dim3(device_cu_count() * PER_WG_PER_CU),
+                               dim3(IDX_THREADS), 0, s, a, qgroups);
         return hipGetLastError();
     }
     const int chunk = 4 * DMA_PPW * IDX_PAGE;
     dim3 grid((a.g.max_ctx + chunk - 1) / chunk, a.g.B * qgroups);
     hipLaunchKernelGGL((indexer_fp8_dma<NQ, HT>), grid, dim3(IDX_THREADS), 0, s, a, qgroups);
+    return hipGetLastError();
+}
+
+bool indexer_emit_ok(const IndexerArgs& a) {
+    const int qg = (a.g.max_q_len + 1) / 2;
+    const int items = a.g.B * (a.g.max_q_len >= 2 ? qg : a.g.max_q_len);
+    return a.key_dtype == 2 && a.dim == IDX_D && a.g.block_size == IDX_PAGE &&
+           (a.n_heads == 64 || a.n_heads == 32 || a.n_heads == 16) && items <= PER_MAX_ITEMS;
+}
+
+hipError_t launch_sample_bound(const IndexerArgs& a, hipStream_t s) {
+    switch (a.n_heads) {
+    case 64: hipLaunchKernelGGL(indexer_sample_bound<4>, dim3(a.g.T), dim3(SB_THREADS), 0, s, a); break;
+    case 32: hipLaunchKernelGGL(indexer_sample_bound<2>, dim3(a.g.T), dim3(SB_THREADS), 0, s, a); break;
+    default: hipLaunchKernelGGL(indexer_sample_bound<1>, dim3(a.g.T), dim3(SB_THREADS), 0, s, a); break;
+    }
     return hipGetLastError();
 }
 

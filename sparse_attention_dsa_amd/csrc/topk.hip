@@ -29,13 +29,11 @@
 // list overflowing) the same selection runs over the whole row from memory.
 // Rows of at most SEL_LIST tokens load all their scores into the list
 // directly and skip the first two kernels.
-#include "dsa_kernels.h"
+#include "indexer_dev.h"
+#include "topk_dev.h"
 
 namespace dsa {
 
-constexpr int TK_SAMPLE = 1024;                        // sample per 128K scores of row
-constexpr int TK_SAMPLE_MAX = 4096;
-constexpr int TK_SAMPLE_BINS = 256;
 constexpr int BND_THREADS = 256;                       // bound kernel
 constexpr int CMP_THREADS = 256;                       // compaction kernel
 constexpr int CMP_PER = TOPK_CHUNK / CMP_THREADS;      // scores per thread
@@ -50,187 +48,29 @@ constexpr int SEL_MEMBERS = 4096;                      // threshold-bucket membe
 static_assert(SEL_LIST > TOPK_MAX_K, "short rows go straight to the list");
 static_assert(SEL_BINS == 4 * SEL_THREADS, "four buckets per thread in the threshold scan");
 
-// Order-preserving map's inverse for ">=" tests on floats: for finite v,
-// score_key(v) >= x  <=>  v >= key_floor(x)  (x a key of a finite float or
-// the unused key below +0; keys at or below that of -inf admit everything).
-__device__ __forceinline__ float key_floor(uint32_t x) {
-    if (x <= 0x007FFFFFu) return -__builtin_inff();
-    if (x >= 0x80000000u) return __uint_as_float(x & 0x7FFFFFFFu);
-    return __uint_as_float(~x);
-}
-
-__device__ __forceinline__ uint64_t composite(uint32_t key, int s) {
-    return ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)s);
-}
-__device__ __forceinline__ int composite_index(uint64_t ck) { return (int)(~(uint32_t)(ck & 0xFFFFFFFFull)); }
-__device__ __forceinline__ uint32_t composite_key(uint64_t ck) { return (uint32_t)(ck >> 32); }
-
-// Bucket of key x in a map of `bins` buckets starting at lo, 2^shift keys
-// wide; keys outside clamp to the end buckets (monotonic in x).
-__device__ __forceinline__ uint32_t bucket_of(uint32_t x, uint32_t lo, uint32_t shift, uint32_t bins) {
-    if (x <= lo) return 0u;
-    const uint32_t b = (x - lo) >> shift;
-    return b < bins ? b : bins - 1u;
-}
-__device__ __forceinline__ uint32_t range_shift(uint32_t lo, uint32_t hi, uint32_t bins) {
-    uint32_t sh = 0;
-    while (((hi - lo) >> sh) >= bins) ++sh;
-    return sh;
-}
-
-// ---------------------------------------------------------------- wave ops
-// Cross-lane steps use DPP (row shifts within 16-lane rows, then row
-// broadcasts), which run at ALU latency instead of through the LDS crossbar.
-constexpr int DPP_ROW_SHR1 = 0x111, DPP_ROW_SHR2 = 0x112, DPP_ROW_SHR4 = 0x114, DPP_ROW_SHR8 = 0x118;
-constexpr int DPP_ROW_BCAST15 = 0x142, DPP_ROW_BCAST31 = 0x143;
-
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-    v += __builtin_amdgcn_update_dpp(0u, v, DPP_ROW_SHR1, 0xF, 0xF, false);
-    v += __builtin_amdgcn_update_dpp(0u, v, DPP_ROW_SHR2, 0xF, 0xF, false);
-    v += __builtin_amdgcn_update_dpp(0u, v, DPP_ROW_SHR4, 0xF, 0xF, false);
-    v += __builtin_amdgcn_update_dpp(0u, v, DPP_ROW_SHR8, 0xF, 0xF, false);
-    v += __builtin_amdgcn_update_dpp(0u, v, DPP_ROW_BCAST15, 0xA, 0xF, false);
-    v += __builtin_amdgcn_update_dpp(0u, v, DPP_ROW_BCAST31, 0xC, 0xF, false);
-    return v;
-}
-
-// Exclusive prefix sum over the wave; *total gets the wave sum.
-__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t* total) {
-    const uint32_t inc = wave_incl_scan(v);
-    *total = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
-    return inc - v;
-}
-
-// Wave-wide minimum and maximum (uniform results).  Lanes whose DPP source
-// lies outside their row keep their own value.
-__device__ __forceinline__ void wave_min_max(uint32_t& mn, uint32_t& mx) {
-#define DSA_MINMAX_STEP(ctrl, rmask)                                                               \
-    mn = min(mn, (uint32_t)__builtin_amdgcn_update_dpp((int)mn, (int)mn, ctrl, rmask, 0xF, false)); \
-    mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp((int)mx, (int)mx, ctrl, rmask, 0xF, false));
-    DSA_MINMAX_STEP(DPP_ROW_SHR1, 0xF)
-    DSA_MINMAX_STEP(DPP_ROW_SHR2, 0xF)
-    DSA_MINMAX_STEP(DPP_ROW_SHR4, 0xF)
-    DSA_MINMAX_STEP(DPP_ROW_SHR8, 0xF)
-    DSA_MINMAX_STEP(DPP_ROW_BCAST15, 0xA)
-    DSA_MINMAX_STEP(DPP_ROW_BCAST31, 0xC)
-#undef DSA_MINMAX_STEP
-    mn = (uint32_t)__builtin_amdgcn_readlane((int)mn, 63);
-    mx = (uint32_t)__builtin_amdgcn_readlane((int)mx, 63);
-}
-
-// Workgroup barrier that orders LDS traffic only: unlike __syncthreads() it
-// does not wait for this wave's global loads still in flight.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Exclusive prefix sum over the workgroup (wsum: one slot per wave).
-template <int WAVES>
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t wt;
-    const uint32_t wex = wave_excl_scan(v, &wt);
-    if (lane == 0) wsum[wave] = wt;
-    lds_barrier();
-    uint32_t ex = wex, tot = 0;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) {
-        const uint32_t x = wsum[w];
-        ex += w < wave ? x : 0u;
-        tot += x;
-    }
-    lds_barrier();
-    *total = tot;
-    return ex;
-}
-
-// Workgroup-wide minimum and maximum (red: two slots per wave).
-template <int WAVES>
-__device__ __forceinline__ void block_min_max(uint32_t& mn, uint32_t& mx, uint32_t (*red)[WAVES]) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    wave_min_max(mn, mx);
-    if (lane == 0) { red[0][wave] = mn; red[1][wave] = mx; }
-    lds_barrier();
-    mn = red[0][0];
-    mx = red[1][0];
-#pragma unroll
-    for (int w = 1; w < WAVES; ++w) { mn = min(mn, red[0][w]); mx = max(mx, red[1][w]); }
-    lds_barrier();
-}
-
-// LDS counter increment; one atomic per wave when all active lanes share the
-// bucket (rows of equal scores would otherwise serialize on one address).
-__device__ __forceinline__ void lds_count(uint32_t* h, uint32_t bin, bool active) {
-    const unsigned long long act = __ballot(active);
-    if (act == 0ull) return;
-    const int lane = threadIdx.x & 63;
-    const int first = __ffsll((long long)act) - 1;
-    const uint32_t b0 = (uint32_t)__builtin_amdgcn_readlane((int)bin, first);
-    if (__ballot(active && bin == b0) == act) {
-        if (lane == first) atomicAdd(&h[b0], (uint32_t)__popcll(act));
-    } else if (active) {
-        atomicAdd(&h[bin], 1u);
-    }
-}
-
 // ---------------------------------------------------------------------------
-// Bound kernel.
+// Bound kernel: the row's strided sample of scores, then its key bound.
 __global__ __launch_bounds__(BND_THREADS) void topk_bound(TopkArgs a) {
-    constexpr int WAVES = BND_THREADS / 64;
     constexpr int NS = TK_SAMPLE_MAX / BND_THREADS;
     const int t = blockIdx.x;
     const int n = row_visible(a.g, t);
     if (n <= SEL_LIST) return;
-    const uint32_t K = (uint32_t)a.k;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x;
     const float* row = a.scores + (size_t)t * a.ld;
-    __shared__ uint32_t h[TK_SAMPLE_BINS];
-    __shared__ uint32_t red[2][WAVES];
-    static_assert(TK_SAMPLE_BINS == BND_THREADS, "one bucket per thread");
-
-    const int m = TK_SAMPLE * min(TK_SAMPLE_MAX / TK_SAMPLE, (n + 131071) / 131072);
-    const int ns = m / BND_THREADS;
-    uint32_t key[NS];
+    __shared__ uint32_t skeys[TK_SAMPLE_MAX];
+    __shared__ uint32_t h[256], res;
+    __shared__ uint32_t red[2][BND_THREADS / 64];
+    const int m = sample_size(n);
+    float v[NS];
 #pragma unroll
     for (int i = 0; i < NS; ++i)
-        if (i < ns) key[i] = score_key(row[(int)((long long)(tid + i * BND_THREADS) * n / m)]);
-    h[tid] = 0u;
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+        if (tid + i * BND_THREADS < m) v[i] = row[sample_pos(tid + i * BND_THREADS, n, m)];
 #pragma unroll
     for (int i = 0; i < NS; ++i)
-        if (i < ns) { lo = min(lo, key[i]); hi = max(hi, key[i]); }
-    block_min_max<WAVES>(lo, hi, red);
-    const uint32_t sh = range_shift(lo, hi, TK_SAMPLE_BINS);
-#pragma unroll
-    for (int i = 0; i < NS; ++i)
-        if (i < ns) atomicAdd(&h[bucket_of(key[i], lo, sh, TK_SAMPLE_BINS)], 1u);
+        if (tid + i * BND_THREADS < m) skeys[tid + i * BND_THREADS] = score_key(v[i]);
     lds_barrier();
-    // Sample rank r: the expected rank of the K-th score plus six standard
-    // deviations of a binomial count, plus a margin.  X = lower key bound of the
-    // highest bucket whose cumulative count (from the top) reaches r; 0 (take
-    // everything) when the sample never reaches r.
-    if (wave == 0) {
-        const float q = (float)K / (float)n, mq = (float)m * q;
-        const uint32_t r = (uint32_t)ceilf(mq + 6.f * sqrtf(mq * (1.f - q))) + 8u;
-        uint32_t c4[4], sum = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) { c4[j] = h[TK_SAMPLE_BINS - 1 - 4 * lane - j]; sum += c4[j]; }
-        uint32_t tot;
-        const uint32_t ex = wave_excl_scan(sum, &tot);
-        if (lane == 0 && tot < r) a.bound[t] = 0u;
-        if (ex < r && ex + sum >= r) {
-            uint32_t cum = ex;
-            for (int j = 0; j < 4; ++j) {
-                cum += c4[j];
-                if (cum >= r) {
-                    const uint32_t b = (uint32_t)(TK_SAMPLE_BINS - 1 - 4 * lane - j);
-                    a.bound[t] = b == 0u ? 0u : lo + (b << sh);
-                    break;
-                }
-            }
-        }
-    }
+    const uint32_t x = sample_key_bound<BND_THREADS>(skeys, m, n, (uint32_t)a.k, h, red, &res);
+    if (tid == 0) a.bound[t] = x;
 }
 
 // ---------------------------------------------------------------------------
@@ -579,6 +419,184 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_select(TopkArgs a) {
         const uint64_t kth = kth_composite(n, K, from_row, S);
         write_selected(n, kth, K, from_row, out, S);
     }
+}
+
+// ---------------------------------------------------------------------------
+// Selection from the indexer's candidate lists (fused decode step).  A row's
+// list holds, in no particular order, the composites of its scores at or
+// above the sample bound (every score when the row has at most SEL_LIST
+// tokens).  The selected entries are written in ascending token order after
+// a bitonic sort of their indices.  When the list is short of K entries or
+// overflowed, the workgroup computes the row's scores itself (same page
+// scoring as the indexer) into the score rows and selects from them.
+
+// Writes the K entries with composite >= kth, sorted by token index.  Rows
+// of at most SEL_BITMAP tokens mark the selected tokens in an LDS bitmap and
+// read it back in order (one block scan); longer rows sort the indices with
+// a bitonic network.
+constexpr int SEL_BITMAP = SEL_MEMBERS * 64;   // bits in the members space
+template <class Get>
+__device__ void write_selected_sorted(int count, int n, uint64_t kth, uint32_t K, const Get& get, int32_t* out,
+                                      SelShared& S) {
+    constexpr int PER = SEL_LIST / SEL_THREADS;
+    const int tid = threadIdx.x;
+    if (n <= SEL_BITMAP) {
+        uint32_t* bm = reinterpret_cast<uint32_t*>(S.r.members);
+        const int nw = (n + 31) >> 5;
+        for (int i = tid; i < nw; i += SEL_THREADS) bm[i] = 0u;
+        lds_barrier();
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int i = tid + j * SEL_THREADS;
+            if (i < count) {
+                const uint64_t ck = get(i);
+                if (ck >= kth) {
+                    const int x = composite_index(ck);
+                    atomicOr(&bm[x >> 5], 1u << (x & 31));
+                }
+            }
+        }
+        lds_barrier();
+        // thread tid owns words [w0, w1)
+        const int per = (nw + SEL_THREADS - 1) / SEL_THREADS;
+        const int w0 = min(nw, tid * per), w1 = min(nw, w0 + per);
+        uint32_t c = 0;
+        for (int w = w0; w < w1; ++w) c += (uint32_t)__popc(bm[w]);
+        uint32_t tot;
+        uint32_t pos = block_excl_scan<SEL_WAVES>(c, S.wsum, &tot);
+        for (int w = w0; w < w1; ++w) {
+            uint32_t bits = bm[w];
+            while (bits) {
+                const int bit = __ffs(bits) - 1;
+                bits &= bits - 1u;
+                out[pos++] = 32 * w + bit;
+            }
+        }
+        return;
+    }
+    int32_t* sel = reinterpret_cast<int32_t*>(S.r.members);   // 2 * SEL_MEMBERS slots
+    uint32_t flags = 0u;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int i = tid + j * SEL_THREADS;
+        if (i < count && get(i) >= kth) flags |= 1u << j;
+    }
+    uint32_t tot;
+    uint32_t pos = block_excl_scan<SEL_WAVES>((uint32_t)__popc(flags), S.wsum, &tot);
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+        if ((flags >> j) & 1u) sel[pos++] = composite_index(get(tid + j * SEL_THREADS));
+    int P = 1;
+    while (P < (int)K) P <<= 1;
+    for (int i = (int)K + tid; i < P; i += SEL_THREADS) sel[i] = 0x7FFFFFFF;   // sorts last
+    lds_barrier();
+    for (int size = 2; size <= P; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = tid; i < P / 2; i += SEL_THREADS) {
+                const int l0 = 2 * i - (i & (stride - 1));
+                const int l1 = l0 + stride;
+                const bool asc = (l0 & size) == 0;
+                const int32_t x = sel[l0], y = sel[l1];
+                if ((x > y) == asc) { sel[l0] = y; sel[l1] = x; }
+            }
+            lds_barrier();
+        }
+    }
+    for (int i = tid; i < (int)K; i += SEL_THREADS) out[i] = sel[i];
+}
+static_assert(2 * SEL_MEMBERS >= TOPK_MAX_K, "sorted selection fits the members space");
+
+// The scores of query row t (n visible tokens) into row, by the indexer's
+// page scoring; pages are spread over the workgroup's waves.
+template <int HT>
+__device__ void recompute_row(const IndexerArgs& ia, int t, int n, float* row) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const Geometry& G = ia.g;
+    const int r = G.q_uniform > 0 ? t / G.q_uniform : find_request(G.qsl, G.B, t);
+    const int32_t* pt = G.page_table + (size_t)r * G.max_blocks;
+    i32x8 qf[1][HT];
+    float wv[1][HT][4];
+    load_query<HT>(ia, t, lane, qf[0], wv[0]);
+    const int npages = (n + IDX_PAGE - 1) / IDX_PAGE;
+    for (int pg = wave; pg < npages; pg += SEL_WAVES) {
+        const int blk = __builtin_amdgcn_readfirstlane(pt[pg]);
+        i32x8 kf[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) kf[nt] = load_key_fragment(ia, blk, 16 * nt + (lane & 15), lane);
+        const float ksc = ia.key_scales ? ia.key_scales[(size_t)blk * IDX_PAGE + lane] : 1.f;
+        float ps[1];
+        page_scores<1, HT>(qf, wv, kf, ksc, lane, 1, ps);
+        const int sidx = pg * IDX_PAGE + lane;
+        if (sidx < n) row[sidx] = ps[0];
+    }
+}
+
+template <int HT>
+__global__ __launch_bounds__(SEL_THREADS) void topk_select_cand(TopkArgs a, IndexerArgs ia) {
+    constexpr int PER = SEL_LIST / SEL_THREADS;
+    const int t = blockIdx.x;
+    const int n = row_visible(a.g, t);
+    const uint32_t K = (uint32_t)a.k;
+    const int tid = threadIdx.x;
+    int32_t* out = a.indices + (size_t)t * K;
+    if (n <= (int)K) {   // every visible token, then -1 padding
+        for (int i = tid; i < (int)K; i += SEL_THREADS) out[i] = i < n ? i : -1;
+        return;
+    }
+    __shared__ SelShared S;
+    const uint32_t cnt = ia.row_count[t];
+    if (cnt >= K && cnt <= (uint32_t)SEL_LIST) {
+        const int count = (int)cnt;
+        const uint64_t* src = ia.cand + (size_t)t * TOPK_LIST;
+        for (int i = tid; i < SEL_BINS; i += SEL_THREADS) S.r.hist[i] = 0u;
+        uint64_t v[PER];
+        uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int i = tid + j * SEL_THREADS;
+            v[j] = i < count ? src[i] : 0ull;
+        }
+#pragma unroll
+        for (int j = 0; j < PER; ++j)
+            if (tid + j * SEL_THREADS < count) {
+                S.list[tid + j * SEL_THREADS] = v[j];
+                lo = min(lo, composite_key(v[j]));
+                hi = max(hi, composite_key(v[j]));
+            }
+        block_min_max<SEL_WAVES>(lo, hi, S.red);
+        const uint32_t sh = range_shift(lo, hi, SEL_BINS);
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const bool ok = tid + j * SEL_THREADS < count;
+            lds_count(S.r.hist, ok ? bucket_of(composite_key(v[j]), lo, sh, SEL_BINS) : 0u, ok);
+        }
+        lds_barrier();
+        auto get = [&](int i) -> uint64_t { return S.list[i]; };
+        const uint64_t kth = kth_from_hist(count, K, get, S, lo, sh);
+        write_selected_sorted(count, n, kth, K, get, out, S);
+        return;
+    }
+    // the bound failed for this row: its scores from the keys, then the
+    // whole-row selection
+    float* row = ia.scores + (size_t)t * ia.ld;
+    recompute_row<HT>(ia, t, n, row);
+    __syncthreads();
+    auto from_row = [&](int i) -> uint64_t { return composite(score_key(row[i]), i); };
+    const uint64_t kth = kth_composite(n, K, from_row, S);
+    write_selected(n, kth, K, from_row, out, S);
+}
+
+hipError_t launch_emit_step(const IndexerArgs& ia, const TopkArgs& ta, hipStream_t s) {
+    hipError_t e = launch_sample_bound(ia, s);
+    if (e == hipSuccess) e = launch_indexer(ia, s);
+    if (e != hipSuccess) return e;
+    switch (ia.n_heads) {
+    case 64: hipLaunchKernelGGL(topk_select_cand<4>, dim3(ta.g.T), dim3(SEL_THREADS), 0, s, ta, ia); break;
+    case 32: hipLaunchKernelGGL(topk_select_cand<2>, dim3(ta.g.T), dim3(SEL_THREADS), 0, s, ta, ia); break;
+    default: hipLaunchKernelGGL(topk_select_cand<1>, dim3(ta.g.T), dim3(SEL_THREADS), 0, s, ta, ia); break;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {

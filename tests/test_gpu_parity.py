@@ -257,3 +257,26 @@ def test_indexshare_decode_group(case):
         ref2, rl2 = oracle.query_mla(wl, t, sel, 2)
         check_out(out2[t], ref2, fp32=False)
         np.testing.assert_allclose(lse2[t], rl2, rtol=0, atol=1e-3)
+
+
+def _sample_positions(n, m=1024):
+    """Token positions of the strided sample the top-K bound is drawn from
+    (m per 128K tokens of the row): floor(i n / m)."""
+    return [i * n // m for i in range(m)]
+
+
+def test_decode_step_bound_fallbacks():
+    """Rows where the sample bound cannot hold the top K: one whose scores all
+    tie (every token is a candidate: the list overflows) and one whose sampled
+    tokens score far above the rest (the bound leaves fewer than K
+    candidates).  Both must still match the oracle exactly."""
+    wl = workloads.make_workload("single_b1_l32768", batch=3, context_lens=[20000, 30000, 9000], seed=21)
+    wl.q_idx[0] = 0                                   # row 0: all scores 0
+    n1 = 30000
+    for s in _sample_positions(n1):                  # row 1: sampled tokens x1000
+        blk = int(wl.page_table[1, s // wl.block_size])
+        wl.idx_scales[blk, s % wl.block_size] *= 1000.0
+    batch, d = upload(wl)
+    out, lse, idx = gpu_step(wl, batch, d)
+    assert idx[0].tolist() == list(range(2048))
+    check_step_rows(wl, [0, 1, 2], out, lse, idx)
