@@ -209,17 +209,22 @@ constexpr int PER_WG_PER_CU = 2;
 // EMIT: instead of storing the scores, each wave stages the composites of its
 // scores at or above the row's key bound in LDS and appends them to the row's
 // candidate list with one atomic per flush (at a request change, when the
-// stage fills, and at the end of the share).
-constexpr int STAGE_CAP = 256;     // staged candidates per wave and query row
+// stage fills, and at the end of the share).  The stage is double-buffered
+// and a flush completes one page later: the atomic's returned base is used
+// only then, so waiting for it never drains the page ring.
+template <int NQ>
+constexpr int stage_cap() { return NQ == 1 ? 256 : 128; }   // per wave, query row and half
 
 template <int NQ, int HT, bool EMIT>
-__global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_persistent(IndexerArgs a, int qgroups) {
+__global__ __launch_bounds__(IDX_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
+void indexer_fp8_persistent(IndexerArgs a, int qgroups) {
     const Geometry& G = a.g;
     const int n_items = G.B * qgroups;
     __shared__ int item_off[PER_MAX_ITEMS + 1];
     __shared__ int scan_tmp[IDX_THREADS];
     __shared__ __attribute__((aligned(16))) uint8_t pbuf[4][IDX_PAGE * IDX_D];
-    __shared__ uint64_t stage[EMIT ? 4 : 1][EMIT ? NQ : 1][EMIT ? STAGE_CAP : 1];
+    constexpr int STAGE_CAP = stage_cap<NQ>();
+    __shared__ uint64_t stage[EMIT ? 4 : 1][EMIT ? NQ : 1][EMIT ? 2 : 1][EMIT ? STAGE_CAP : 1];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, col = lane & 15;
@@ -309,18 +314,32 @@ __global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_persistent(IndexerArg
     __amdgpu_buffer_rsrc_t orow[NQ];   // score row of each query, sized to its visible count
     // EMIT state per query row of the item: row index, visible count, bound,
     // staged count (all wave-uniform)
-    int trow[NQ], nvis[NQ], nst[NQ];
+    // stage half in use, staged count; pending flush: count, half, row and the
+    // atomic's returned base (lane 0)
+    int trow[NQ], nvis[NQ], nst[NQ], half[NQ], pn[NQ], ph[NQ], prow[NQ];
+    uint32_t pbase[NQ];
     float xf[NQ];
 #pragma unroll
-    for (int j = 0; j < NQ; ++j) { trow[j] = 0; nvis[j] = 0; nst[j] = 0; xf[j] = 0.f; }
-    auto flush = [&](int j) {
+    for (int j = 0; j < NQ; ++j) {
+        trow[j] = 0; nvis[j] = 0; nst[j] = 0; half[j] = 0; pn[j] = 0; ph[j] = 0; prow[j] = 0; pbase[j] = 0u;
+        xf[j] = 0.f;
+    }
+    auto complete = [&](int j) {   // copy a pending flush's entries to the row's list
+        if (pn[j] == 0) return;
+        const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)pbase[j], 0);
+        uint64_t* dst = a.cand + (size_t)prow[j] * TOPK_LIST;
+        for (int i = lane; i < pn[j]; i += 64)
+            if (base + (uint32_t)i < (uint32_t)TOPK_LIST) dst[base + i] = stage[wave][j][ph[j]][i];
+        pn[j] = 0;
+    };
+    auto flush = [&](int j) {      // reserve list space; the copy happens in complete()
+        complete(j);
         if (nst[j] == 0) return;
-        uint32_t base = 0;
-        if (lane == 0) base = atomicAdd(&a.row_count[trow[j]], (uint32_t)nst[j]);
-        base = (uint32_t)__builtin_amdgcn_readlane((int)base, 0);
-        uint64_t* dst = a.cand + (size_t)trow[j] * TOPK_LIST;
-        for (int i = lane; i < nst[j]; i += 64)
-            if (base + (uint32_t)i < (uint32_t)TOPK_LIST) dst[base + i] = stage[wave][j][i];
+        if (lane == 0) pbase[j] = atomicAdd(&a.row_count[trow[j]], (uint32_t)nst[j]);
+        pn[j] = nst[j];
+        ph[j] = half[j];
+        prow[j] = trow[j];
+        half[j] ^= 1;
         nst[j] = 0;
     };
     auto load_item = [&](int it) {
@@ -410,11 +429,13 @@ __global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_persistent(IndexerArg
             if constexpr (EMIT) {
 #pragma unroll
                 for (int j = 0; j < NQ; ++j) {
+                    complete(j);   // a flush issued one page ago
                     const bool keep = p < p1 && pos < nvis[j] && ps[j] >= xf[j];
                     const unsigned long long mk = __ballot(keep);
                     if (mk != 0ull) {
                         const unsigned long long below = lane ? (mk & ((1ull << lane) - 1ull)) : 0ull;
-                        if (keep) stage[wave][j][nst[j] + __popcll(below)] = composite(score_key(ps[j]), pos);
+                        if (keep)
+                            stage[wave][j][half[j]][nst[j] + __popcll(below)] = composite(score_key(ps[j]), pos);
                         nst[j] += __popcll(mk);
                         if (nst[j] > STAGE_CAP - 64) flush(j);
                     }
@@ -429,7 +450,10 @@ __global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_persistent(IndexerArg
     }
     if constexpr (EMIT) {
 #pragma unroll
-        for (int j = 0; j < NQ; ++j) flush(j);
+        for (int j = 0; j < NQ; ++j) {
+            flush(j);
+            complete(j);
+        }
     }
 }
 
@@ -448,6 +472,9 @@ __global__ __launch_bounds__(SB_THREADS) void indexer_sample_bound(IndexerArgs a
     const int t = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    i32x8 qf[HT];
+    float wv[HT][4];
+    load_query<HT>(a, t, lane, qf, wv);   // in flight while the row's length arrives
     const int n = row_visible(G, t);
     if (tid == 0) a.row_count[t] = 0u;
     if (n <= TOPK_LIST) {
@@ -462,9 +489,6 @@ __global__ __launch_bounds__(SB_THREADS) void indexer_sample_bound(IndexerArgs a
     const int m = sample_size(n);
     const int per_wave = m / (SB_THREADS / 64);          // 64 .. 256 samples
     const int nfrag = per_wave / 16;
-    i32x8 qf[HT];
-    float wv[HT][4];
-    load_query<HT>(a, t, lane, qf, wv);
     // lane (g, col) of fragment f handles sample i = i0 + 16 f + col; four
     // fragments in flight at a time (1024 threads leave 128 registers a lane)
     const int i0 = wave * per_wave + (lane & 15);
