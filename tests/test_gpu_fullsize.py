@@ -44,6 +44,17 @@ def test_decode_full_size(name, rows):
     log("  rows", rows, "worst abs err", worst)
 
 
+def test_decode_all_128k_full_size():
+    """Batch 64 with every context at 131072 tokens (10.8 GB latent pool)."""
+    wl = workloads.make_workload("batched_b64_l8k_128k", context_lens=[131072])
+    log("all-128K T", wl.total_q, "sum L", int(wl.context_lens.sum()))
+    batch, d = upload(wl)
+    out, lse, idx = gpu_step(wl, batch, d)
+    _structural(wl, idx)
+    worst = check_step_rows(wl, [0, 31, 63], out, lse, idx)
+    log("  worst abs err", worst)
+
+
 def test_chunked_prefill_full_size():
     wl = workloads.make_workload("prefill_q4096_l131072")
     log("prefill T", wl.total_q, "L", int(wl.context_lens[0]))
