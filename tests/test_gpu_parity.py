@@ -280,3 +280,23 @@ def test_decode_step_bound_fallbacks():
     out, lse, idx = gpu_step(wl, batch, d)
     assert idx[0].tolist() == list(range(2048))
     check_step_rows(wl, [0, 1, 2], out, lse, idx)
+
+
+@pytest.mark.parametrize("case", ["list_edge", "k4096", "idx32", "idx16_h64"])
+def test_decode_step_shapes(case):
+    """The candidate-emitting step across its shape switches: rows exactly at
+    and one past the length where the sample bound starts (12288), the
+    largest K, 32- and 16-head indexers, and 64 MLA heads (the GLM-5 shape)."""
+    if case == "list_edge":
+        wl = workloads.make_workload("single_b1_l32768", batch=3, context_lens=[12288, 12289, 12352], seed=22)
+    elif case == "k4096":
+        wl = workloads.make_workload("single_b1_l32768", batch=2, context_lens=[4096, 30000], topk=4096, seed=23)
+    elif case == "idx32":
+        wl = workloads.make_workload("single_b1_l32768", batch=2, context_lens=[20000, 3000], idx_heads=32, seed=24)
+    else:
+        wl = workloads.make_workload("single_b1_l32768", batch=2, context_lens=[15000, 2500], idx_heads=16,
+                                     mla_heads=64, seed=25)
+    log("decode_step shape", case, wl.context_lens.tolist(), "K", wl.topk, "H_idx", wl.idx_heads, "H", wl.mla_heads)
+    batch, d = upload(wl)
+    out, lse, idx = gpu_step(wl, batch, d)
+    check_step_rows(wl, list(range(wl.total_q)), out, lse, idx)
