@@ -180,15 +180,24 @@ struct RawPage {
 };
 
 __device__ __forceinline__ void load_raw_page(const uint8_t* __restrict__ keys, const float* __restrict__ scales,
-                                              int blk, int lane, RawPage& p) {
-    const uint8_t* base = keys + (size_t)blk * (IDX_PAGE * IDX_D) + 16 * lane;
+                                              int blk, bool live, int lane, RawPage& p) {
+    // Buffer loads through a descriptor of the page (block id and liveness
+    // are wave-uniform).  A slot past the wave's share still issues the same
+    // instructions, so the ring's load counting stays exact, but its
+    // descriptor holds no records: the range check returns zeros and nothing
+    // is read from memory.
+    const uint8_t* page = keys + (size_t)blk * (IDX_PAGE * IDX_D);
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)page, 0, live ? IDX_PAGE * IDX_D : 0, 0x00020000);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) p.v[c] = __builtin_nontemporal_load((const u32x4*)(base + 1024 * c));
+    for (int c = 0; c < 8; ++c) p.v[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, 16 * lane + 1024 * c, 0, 2);
     // without scales the load reads the page's own keys; the consumer then
     // uses 1 instead (the same instructions issue either way, and nothing
     // here waits for the load)
-    const float* sp = scales ? scales + (size_t)blk * IDX_PAGE : (const float*)(keys + (size_t)blk * (IDX_PAGE * IDX_D));
-    p.scale = sp[lane];
+    const void* sp = scales ? (const void*)(scales + (size_t)blk * IDX_PAGE) : (const void*)page;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)sp, 0, live ? 4 * IDX_PAGE : 0, 0x00020000);
+    p.scale = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, 4 * lane, 0, 0));
 }
 
 // ---------------------------------------------------------------------------
@@ -300,7 +309,7 @@ void indexer_fp8_persistent(IndexerArgs a, int qgroups) {
     const auto clampp = [&](int q) { return q < p1 ? q : p1 - 1; };
     int iss_p = p0;
     auto issue_next = [&](RawPage& dst) {
-        load_raw_page(keys, a.key_scales, blk_of(clampp(iss_p)), lane, dst);
+        load_raw_page(keys, a.key_scales, blk_of(clampp(iss_p)), iss_p < p1, lane, dst);
         ++iss_p;
     };
     RawPage ring[PER_PF];
