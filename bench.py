@@ -15,6 +15,11 @@ the HBM bytes per launch that rocprofv3's FETCH_SIZE and WRITE_SIZE counters
 recorded (scaled by a copy-kernel calibration), read from the committed
 counter summary and reported only while the indexer source is unchanged.
 `step_hbm` gives the algorithmic-bytes ratio for the whole step.
+`prefill` times the chunked prefill (4096 new query tokens on a 131072-token
+context: indexer scores, top-K, then sparse MLA prefill on two layers that
+share the selection) call by call, and reports each contraction as MFMA
+utilisation (achieved FLOP/s over the dense fp8 / bf16 peak), since at that
+shape both are compute-bound; the top-K time is reported on its own.
 `indexshare` times groups of layers that share one selection (one full step,
 then sparse MLA only on the other layers' caches) and reports the amortised
 tokens/s per layer.  `all_128k` repeats the step measurement with every
@@ -44,7 +49,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, published
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 DEFAULT_WORKLOAD = "batched_b64_l8k_128k"
+PREFILL_WORKLOAD = "prefill_q4096_l131072"
 
 
 # ------------------------------------------------------------ accounting
@@ -278,6 +286,87 @@ def summarize(rig, ms_step, indices, idx_us):
     }
 
 
+def prefill_flops(wl):
+    """(indexer fp8 FLOPs, sparse-MLA bf16 FLOPs per layer) of one chunked
+    prefill: query j of a request with context L and q new tokens sees
+    L - q + j + 1 tokens and selects min(K, that) of them."""
+    f_idx = f_mla = 0
+    for L, q in zip(wl.context_lens.tolist(), wl.q_lens.tolist()):
+        for j in range(q):
+            n = L - q + j + 1
+            f_idx += 2 * wl.idx_heads * wl.idx_dim * n
+            f_mla += 2 * wl.mla_heads * min(wl.topk, n) * (wl.d_latent + wl.d_rope + wl.d_latent)
+    return f_idx, f_mla
+
+
+def prefill_leg(iters, warmup, log):
+    """Chunked prefill, one call at a time: indexer scores, top-K, sparse MLA
+    prefill on layer 1 and on layer 2 with layer 1's selection."""
+    import torch
+    import sparse_attention_dsa_amd as dsa
+    import workloads
+
+    t0 = time.time()
+    wl = workloads.make_workload(PREFILL_WORKLOAD)
+    d = workloads.to_device(wl, "cuda")
+    log("[bench] workload %s: T=%d L=%d (generated in %.1fs)" %
+        (wl.name, wl.total_q, int(wl.context_lens.max()), time.time() - t0))
+    batch = dsa.Batch(d["context_lens"], d["query_start_loc"], d["page_table"], wl.block_size,
+                      wl.max_q_len, wl.max_context_len)
+    T, H, K = wl.total_q, wl.mla_heads, wl.topk
+    ld = (wl.max_context_len + 63) // 64 * 64
+    stream = torch.cuda.current_stream()
+    scores = torch.empty((T, ld), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    out = torch.empty((T, H, wl.d_latent), dtype=torch.bfloat16, device="cuda")
+    from sparse_attention_dsa_amd import binding as B
+    ws_tk = torch.empty(max(dsa.workspace_size(B.OP_TOPK, batch, K, 0), 256), dtype=torch.uint8, device="cuda")
+    ws_ml = torch.empty(max(dsa.workspace_size(B.OP_MLA_PREFILL, batch, K, H), 256), dtype=torch.uint8,
+                        device="cuda")
+    calls = [
+        lambda: dsa.indexer_scores(batch, d["idx_keys"], d["idx_scales"], d["q_idx"], d["w"], scores=scores,
+                                   ld=ld, stream=stream),
+        lambda: dsa.topk(batch, scores, K, indices=idx, workspace=ws_tk, stream=stream),
+        lambda: dsa.sparse_mla_prefill(batch, d["kv"], d["kv_scales"], wl.d_latent, d["q_mla"], idx,
+                                       wl.softmax_scale, out=out, workspace=ws_ml, stream=stream),
+        lambda: dsa.sparse_mla_prefill(batch, d["kv2"], d["kv2_scales"], wl.d_latent, d["q_mla2"], idx,
+                                       wl.softmax_scale, out=out, workspace=ws_ml, stream=stream),
+    ]
+    for _ in range(warmup):
+        for c in calls:
+            c()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(iters)]
+    torch.cuda.synchronize()
+    for it in range(iters):
+        evs[it][0].record(stream)
+        for k, c in enumerate(calls):
+            c()
+            evs[it][k + 1].record(stream)
+    torch.cuda.synchronize()
+    us = [1e3 * sum(e[k].elapsed_time(e[k + 1]) for e in evs) / iters for k in range(len(calls))]
+    step_us = 1e3 * sum(e[0].elapsed_time(e[-1]) for e in evs) / iters
+    f_idx, f_mla = prefill_flops(wl)
+    mla_us = (us[2] + us[3]) / 2
+    res = {
+        "workload": wl.name, "query_rows": T, "context": int(wl.context_lens.max()), "topk": K, "layers": 2,
+        "ms_per_step": round(step_us * 1e-3, 4),
+        "tokens_per_s": round(T / (step_us * 1e-6), 1),
+        "indexer": {"us": round(us[0], 1), "tflops": round(f_idx / us[0] * 1e-6, 1),
+                    "peak": PEAK_FP8_TFLOPS, "mfma_frac": round(f_idx / us[0] * 1e-6 / PEAK_FP8_TFLOPS, 4)},
+        "topk": {"us": round(us[1], 1), "scores": T * int(wl.context_lens.max()) - T * (T - 1) // 2},
+        "mla_prefill": {"us_per_layer": round(mla_us, 1), "tflops": round(f_mla / mla_us * 1e-6, 1),
+                        "peak": PEAK_BF16_TFLOPS,
+                        "mfma_frac": round(f_mla / mla_us * 1e-6 / PEAK_BF16_TFLOPS, 4)},
+    }
+    log("[bench] prefill: %.2f ms per step; indexer %.0f us (%.1f%% of fp8 peak), top-K %.0f us, "
+        "MLA %.0f us per layer (%.1f%% of bf16 peak)" %
+        (step_us * 1e-3, us[0], 100 * res["indexer"]["mfma_frac"], us[1], mla_us,
+         100 * res["mla_prefill"]["mfma_frac"]))
+    del d, scores, idx, out, ws_tk, ws_ml, calls
+    torch.cuda.empty_cache()
+    return res
+
+
 # ------------------------------------------------------------------ main
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -292,6 +381,8 @@ def main(argv=None):
                     help="layers per IndexShare group for the amortised figure (0 or 1: skip)")
     ap.add_argument("--no-128k", action="store_true",
                     help="skip the extra measurement with every context at 131072 tokens")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the chunked-prefill measurement (4096 queries on a 131072-token context)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -362,6 +453,11 @@ def main(argv=None):
         rig2.free()
         del rig2, wl2
 
+    # Chunked prefill: MFMA-bound, reported as utilisation per contraction.
+    prefill = None
+    if not args.no_prefill and args.workload == DEFAULT_WORKLOAD:
+        prefill = prefill_leg(max(3, min(args.steps, 10)), 2, log)
+
     # CPU baseline: the oracle on a bounded sample of query rows.
     cpu = None
     if args.cpu_rows > 0:
@@ -406,6 +502,7 @@ def main(argv=None):
                         "mla_bf16": round(f_mla / (ms_per_step * 1e-3) / 1e12, 2)},
         "indexshare": share,
         "all_128k": at128,
+        "prefill": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

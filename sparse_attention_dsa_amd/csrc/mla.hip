@@ -531,32 +531,35 @@ void mla_h128(MlaArgs a, int slice) {
     const int hh = lane >> 5, c32 = lane & 31;
     const int head = hg * M3_HEADS + wave * 32 + c32;
 
-    // queries first (needed last), then the slice's rows: every selection
-    // index load, then every page-table load, so each waits one round trip
-    u32x4 qf[M_DQK / 16];
-    {
-        const uint16_t* qp = (const uint16_t*)a.q + ((size_t)t * a.n_heads + head) * M_DQK + 8 * hh;
-#pragma unroll
-        for (int ks = 0; ks < M_DQK / 16; ++ks) qf[ks] = *(const u32x4*)(qp + 16 * ks);
-    }
+    // the slice's rows first: every selection index load, then every
+    // page-table load, so each waits one round trip; the queries are loaded
+    // after the first tile's transfers are on their way
     {
         constexpr int PER = M3_MAX_SLICE / M_THREADS;
         const int r = row_request(G, t);
         const int32_t* sel = a.indices + (size_t)t * a.k + j_begin;
         const int32_t* pt = G.page_table + (size_t)r * G.max_blocks;
-        int sj[PER], blk[PER];
+        const int bs = G.block_size;
+        const bool pow2 = (bs & (bs - 1)) == 0;
+        const int bsh = __builtin_ctz((unsigned)bs);
+        int sj[PER], blk[PER], slot[PER];
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
             const int j = tid + u * M_THREADS;
             sj[u] = j < nslots ? sel[j] : -1;
         }
 #pragma unroll
-        for (int u = 0; u < PER; ++u) blk[u] = sj[u] >= 0 ? pt[sj[u] / G.block_size] : 0;
+        for (int u = 0; u < PER; ++u) {
+            const int s = max(sj[u], 0);
+            const int b = pow2 ? s >> bsh : s / bs;
+            slot[u] = s - b * bs;
+            blk[u] = sj[u] >= 0 ? pt[b] : 0;
+        }
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
             const int j = tid + u * M_THREADS;
             const bool ok = sj[u] >= 0;
-            if (j < ntiles * M_TILE) rows[j] = ok ? blk[u] * G.block_size + sj[u] % G.block_size : 0;
+            if (j < ntiles * M_TILE) rows[j] = ok ? blk[u] * bs + slot[u] : 0;
             const unsigned long long m = __ballot(ok);   // 64 slots = two tiles
             if (lane == 0 && j < ntiles * M_TILE) tvalid[j / M_TILE] = (uint32_t)m;
             if (lane == 32 && j < ntiles * M_TILE) tvalid[j / M_TILE] = (uint32_t)(m >> 32);
@@ -624,6 +627,22 @@ void mla_h128(MlaArgs a, int slice) {
     float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
     const float zscale = a.scale * LOG2E;
 
+    // first pass: tile 0's transfers, the queries (needed at the first
+    // MFMA), then the next tiles; the first wait of the loop covers the
+    // queries as well, since they were issued before the later tiles
+    u32x4 qf[M_DQK / 16];
+    if (0 < ntiles) issue(0, 0);
+    asm volatile("" ::: "memory");
+    {
+        const uint16_t* qp = (const uint16_t*)a.q + ((size_t)t * a.n_heads + head) * M_DQK + 8 * hh;
+#pragma unroll
+        for (int ks = 0; ks < M_DQK / 16; ++ks) qf[ks] = *(const u32x4*)(qp + 16 * ks);
+    }
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int b = 1; b < M3_NBUF - 1; ++b)
+        if (b < ntiles) issue(b, b);
+
     for (int pass = 0;; ++pass) {
 #pragma unroll
     for (int cb = 0; cb < M_DL / 32; ++cb)
@@ -633,9 +652,11 @@ void mla_h128(MlaArgs a, int slice) {
     bool overflow = false;
     if (tid == 0) redo = 0u;
 
+    if (pass > 0) {
 #pragma unroll
-    for (int b = 0; b < M3_NBUF - 1; ++b)
-        if (b < ntiles) issue(b, b);
+        for (int b = 0; b < M3_NBUF - 1; ++b)
+            if (b < ntiles) issue(b, b);
+    }
 
     for (int i = 0; i < ntiles; ++i) {
         // this wave's transfers of tile i are done once at most the ones of
