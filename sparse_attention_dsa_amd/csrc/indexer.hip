@@ -57,7 +57,9 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
     else if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
     else if constexpr (N == 18) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
     else if constexpr (N == 27) asm volatile("s_waitcnt vmcnt(27)" ::: "memory");
     else static_assert(N == 0, "unsupported vmcnt");
@@ -168,6 +170,194 @@ __global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_dma(IndexerArgs a, in
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Query-blocked variant for long query chunks (chunked prefill), where the
+// indexer is a dense fp8 product with a causal epilogue.  A workgroup owns
+// PF_QB query rows of one request (PF_QW per wave, queries and weights in
+// registers) and a range of PF_CHUNK pages.  Each page (8 KB of keys and
+// 256 B of scales) enters an LDS ring once per workgroup, by asynchronous
+// transfers split evenly over the waves, and is read by every wave, so a key
+// byte brought from L2 feeds PF_QB query rows.  Workgroups are numbered
+// page-range-major: the ones resident together work on the same pages.
+//
+// Every wave issues exactly three transfers per page (two 1 KB key units and
+// the page's scales) and two score stores per page (buffer stores whose descriptors
+// are sized to each row's visible count, so positions past it are dropped),
+// which keeps the vector-memory counts of the ring's waits exact.
+// Scores of one page for PF_QW query rows with the MFMAs of the next token
+// tile in flight while the current one's results are reduced (two sets of
+// accumulators), so the matrix core does not wait for the vector ALU.
+template <int NQ, int HT>
+__device__ __forceinline__ void page_scores_ilp(const i32x8 (&qf)[NQ][HT], const float (&wv)[NQ][HT][4],
+                                                const i32x8 (&kf)[4], float ksc, int lane, float (&out)[NQ]) {
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 c[2][NQ][HT];
+    float part[NQ][4];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j)
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) c[0][j][ht] = mfma_fp8_16x16x128(qf[j][ht], kf[0], zero);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+        if (nt + 1 < 4) {
+#pragma unroll
+            for (int j = 0; j < NQ; ++j)
+#pragma unroll
+                for (int ht = 0; ht < HT; ++ht)
+                    c[(nt + 1) & 1][j][ht] = mfma_fp8_16x16x128(qf[j][ht], kf[nt + 1], zero);
+        }
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            float acc = 0.f;
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc += wv[j][ht][i] * fmaxf(c[nt & 1][j][ht][i], 0.f);
+            part[j][nt] = acc;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) out[j] = head_sum_transpose(part[j], lane) * ksc;
+}
+
+constexpr int PF_WAVES = 4;
+constexpr int PF_QW = 2;                       // query rows per wave
+constexpr int PF_QB = PF_WAVES * PF_QW;        // query rows per workgroup
+constexpr int PF_CHUNK = 128;                  // pages per workgroup
+constexpr int PF_RING = 4;                     // page slots
+constexpr int PF_MIN_Q = 8;                    // longest query chunk from which it is used
+
+template <int HT>
+__global__ __launch_bounds__(PF_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2))) void indexer_fp8_prefill(IndexerArgs a, int qblocks) {
+    const Geometry& G = a.g;
+    const int r = blockIdx.x / qblocks, jb = blockIdx.x % qblocks;
+    const int qs = G.qsl[r], ql = G.qsl[r + 1] - qs;
+    const int j0 = jb * PF_QB;
+    if (j0 >= ql) return;
+    const int L = G.ctx[r];
+    const int n_last = L - ql + min(ql, j0 + PF_QB);      // visible tokens of the block's last row
+    const int p0 = blockIdx.y * PF_CHUNK;
+    const int np_all = (n_last + IDX_PAGE - 1) / IDX_PAGE;
+    if (p0 >= np_all) return;
+    const int np = min(PF_CHUNK, np_all - p0);
+
+    // a slot: the page's keys, then four copies of its 64 scales
+    constexpr int SLOT = IDX_PAGE * IDX_D + 16 * IDX_PAGE;
+    __shared__ __attribute__((aligned(16))) uint8_t kbuf[PF_RING][SLOT];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, col = lane & 15;
+
+    // this wave's query rows; a row past the request repeats its last row
+    // and stores nothing
+    const int jw = j0 + PF_QW * wave;
+    const int nq = min(PF_QW, ql - jw);
+    i32x8 qf[PF_QW][HT];
+    float wv[PF_QW][HT][4];
+    __amdgpu_buffer_rsrc_t orow[PF_QW];
+#pragma unroll
+    for (int j = 0; j < PF_QW; ++j) {
+        const int jj = min(jw + j, ql - 1);
+        const int t = qs + jj;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            const uint8_t* qp = (const uint8_t*)a.q + ((size_t)t * a.n_heads + 16 * ht + col) * IDX_D + 16 * g;
+            qf[j][ht] = join_i32x8(*(const u32x4*)qp, *(const u32x4*)(qp + 64));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wv[j][ht][i] = a.w[(size_t)t * a.n_heads + 16 * ht + 4 * g + i];
+        }
+        const int nvis = j < nq ? L - ql + jj + 1 : 0;
+        orow[j] = __builtin_amdgcn_make_buffer_rsrc((void*)(a.scores + (size_t)t * a.ld), 0, 4 * nvis, 0x00020000);
+    }
+    // physical block of chunk page 64b + l in lane l of blkv[b]
+    const int32_t* pt = G.page_table + (size_t)r * G.max_blocks;
+    int blkv[PF_CHUNK / 64];
+#pragma unroll
+    for (int b = 0; b < PF_CHUNK / 64; ++b) blkv[b] = 64 * b + lane < np ? pt[p0 + 64 * b + lane] : 0;
+    // consume the loads above here, so that no wait for them lands inside
+    // the ring (whose waits count only its own transfers and stores)
+#pragma unroll
+    for (int j = 0; j < PF_QW; ++j)
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            const u32x4 lo = (u32x4)__builtin_shufflevector(qf[j][ht], qf[j][ht], 0, 1, 2, 3);
+            const u32x4 hi = (u32x4)__builtin_shufflevector(qf[j][ht], qf[j][ht], 4, 5, 6, 7);
+            asm volatile("" ::"v"(lo), "v"(hi));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) asm volatile("" ::"v"(wv[j][ht][i]));
+        }
+#pragma unroll
+    for (int b = 0; b < PF_CHUNK / 64; ++b) asm volatile("" ::"v"(blkv[b]));
+
+    const uint8_t* keys = (const uint8_t*)a.keys;
+    const bool has_scale = a.key_scales != nullptr;
+    // chunk page p into the slot at dst: key units 2w, 2w+1 and the page's
+    // 64 scales (every wave writes the same scale values)
+    auto issue = [&](int p, uint8_t* dst) {
+        int bv = blkv[0];
+#pragma unroll
+        for (int b = 1; b < PF_CHUNK / 64; ++b) bv = (p >> 6) == b ? blkv[b] : bv;
+        const int blk = __builtin_amdgcn_readlane(bv, p & 63);
+        const uint8_t* src = keys + (size_t)blk * (IDX_PAGE * IDX_D);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int U = 64 * (2 * wave + c) + lane, t = U >> 3, u = (U & 7) ^ page_swz(t);
+            __builtin_amdgcn_global_load_lds((const void*)(src + t * IDX_D + 16 * u),
+                                             (lds_ptr_t)(dst + 1024 * (2 * wave + c)), 16, 0, DMA_AUX);
+        }
+        // the 256 B of scales as 16-byte units: lane l moves unit l & 15, so
+        // the slot holds four copies
+        const uint8_t* ssrc = has_scale ? (const uint8_t*)(a.key_scales + (size_t)blk * IDX_PAGE) : src;
+        __builtin_amdgcn_global_load_lds((const void*)(ssrc + 16 * (lane & 15)),
+                                         (lds_ptr_t)(dst + IDX_PAGE * IDX_D), 16, 0, 0);
+    };
+#pragma unroll
+    for (int d = 0; d < PF_RING - 1; ++d)
+        if (d < np) issue(d, &kbuf[d][0]);
+
+    for (int p = 0; p < np; ++p) {
+        // page p's transfers of this wave are done once at most the younger
+        // operations are pending: in steady state the stores of the three
+        // previous pages (2 each) and the transfers of the next two (3 each)
+        if (p >= PF_RING - 1 && p + 2 < np) wait_vmcnt<12>();
+        else if (p + 2 < np) wait_vmcnt<6>();
+        else wait_vmcnt<0>();
+        lds_barrier();   // every wave's part of page p landed; the slot of page p - 1 is free
+        // the slot read and the slot refilled are passed as __restrict__
+        // pointers: the compiler then knows the transfers in flight cannot
+        // alias the reads and does not wait for them before each read
+        auto body = [&](const uint8_t* __restrict__ pb, uint8_t* __restrict__ dst) {
+            if (p + PF_RING - 1 < np) issue(p + PF_RING - 1, dst);
+            i32x8 kf[4];
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const int t = 16 * nt + col;
+                const u32x4 lo = *(const u32x4*)(pb + t * IDX_D + 16 * (g ^ page_swz(t)));
+                const u32x4 hi = *(const u32x4*)(pb + t * IDX_D + 16 * ((4 + g) ^ page_swz(t)));
+                kf[nt] = join_i32x8(lo, hi);
+            }
+            const float ksc = has_scale ? ((const float*)(pb + IDX_PAGE * IDX_D))[lane] : 1.f;
+            float ps[PF_QW];
+            page_scores_ilp<PF_QW, HT>(qf, wv, kf, ksc, lane, ps);
+            const int voff = 4 * ((p0 + p) * IDX_PAGE + lane);
+#pragma unroll
+            for (int j = 0; j < PF_QW; ++j)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ps[j]), orow[j], voff, 0, 0);
+        };
+        const int nx = (p + PF_RING - 1) % PF_RING;
+        body(&kbuf[p % PF_RING][0], &kbuf[nx][0]);
+    }
+}
+
+template <int HT>
+static hipError_t launch_fp8_prefill(const IndexerArgs& a, hipStream_t s) {
+    const int qblocks = (a.g.max_q_len + PF_QB - 1) / PF_QB;
+    const int chunks = ((a.g.max_ctx + IDX_PAGE - 1) / IDX_PAGE + PF_CHUNK - 1) / PF_CHUNK;
+    hipLaunchKernelGGL(indexer_fp8_prefill<HT>, dim3(a.g.B * qblocks, chunks), dim3(PF_WAVES * 64), 0, s, a,
+                       qblocks);
+    return hipGetLastError();
+}
 
 // ---------------------------------------------------------------------------
 // Staged page loads for the persistent kernel: fully contiguous loads (lane l
@@ -602,6 +792,13 @@ hipError_t launch_sample_bound(const IndexerArgs& a, hipStream_t s) {
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
     const bool fast = a.key_dtype == 2 && a.dim == IDX_D && a.g.block_size == IDX_PAGE &&
                       (a.n_heads == 64 || a.n_heads == 32 || a.n_heads == 16);
+    if (fast && a.g.max_q_len >= PF_MIN_Q) {
+        switch (a.n_heads) {
+        case 64: return launch_fp8_prefill<4>(a, s);
+        case 32: return launch_fp8_prefill<2>(a, s);
+        default: return launch_fp8_prefill<1>(a, s);
+        }
+    }
     if (fast) {
         const bool two = a.g.max_q_len >= 2;
         switch (a.n_heads) {

@@ -531,9 +531,14 @@ void mla_h128(MlaArgs a, int slice) {
     const int hh = lane >> 5, c32 = lane & 31;
     const int head = hg * M3_HEADS + wave * 32 + c32;
 
-    // the slice's rows first: every selection index load, then every
-    // page-table load, so each waits one round trip; the queries are loaded
-    // after the first tile's transfers are on their way
+    // queries first (needed last), then the slice's rows: every selection
+    // index load, then every page-table load, so each waits one round trip
+    u32x4 qf[M_DQK / 16];
+    {
+        const uint16_t* qp = (const uint16_t*)a.q + ((size_t)t * a.n_heads + head) * M_DQK + 8 * hh;
+#pragma unroll
+        for (int ks = 0; ks < M_DQK / 16; ++ks) qf[ks] = *(const u32x4*)(qp + 16 * ks);
+    }
     {
         constexpr int PER = M3_MAX_SLICE / M_THREADS;
         const int r = row_request(G, t);
@@ -627,22 +632,6 @@ void mla_h128(MlaArgs a, int slice) {
     float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
     const float zscale = a.scale * LOG2E;
 
-    // first pass: tile 0's transfers, the queries (needed at the first
-    // MFMA), then the next tiles; the first wait of the loop covers the
-    // queries as well, since they were issued before the later tiles
-    u32x4 qf[M_DQK / 16];
-    if (0 < ntiles) issue(0, 0);
-    asm volatile("" ::: "memory");
-    {
-        const uint16_t* qp = (const uint16_t*)a.q + ((size_t)t * a.n_heads + head) * M_DQK + 8 * hh;
-#pragma unroll
-        for (int ks = 0; ks < M_DQK / 16; ++ks) qf[ks] = *(const u32x4*)(qp + 16 * ks);
-    }
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int b = 1; b < M3_NBUF - 1; ++b)
-        if (b < ntiles) issue(b, b);
-
     for (int pass = 0;; ++pass) {
 #pragma unroll
     for (int cb = 0; cb < M_DL / 32; ++cb)
@@ -652,11 +641,9 @@ void mla_h128(MlaArgs a, int slice) {
     bool overflow = false;
     if (tid == 0) redo = 0u;
 
-    if (pass > 0) {
 #pragma unroll
-        for (int b = 0; b < M3_NBUF - 1; ++b)
-            if (b < ntiles) issue(b, b);
-    }
+    for (int b = 0; b < M3_NBUF - 1; ++b)
+        if (b < ntiles) issue(b, b);
 
     for (int i = 0; i < ntiles; ++i) {
         // this wave's transfers of tile i are done once at most the ones of

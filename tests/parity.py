@@ -28,6 +28,40 @@ import workloads
 BAND = 1e-4
 
 
+def score_bound(wl, t):
+    """Rounding bound of query row t's indexer scores computed in fp32.
+
+    A score is a sum over heads of w_h * ReLU(q_h . k_s) times sigma_s: a
+    dot of `dim` exact products, a head sum of `heads` terms and two
+    products, i.e. at most n = dim + heads + 2 fp32 roundings in any order.
+    Its error is then at most gamma_n = n u / (1 - n u) (u = 2^-24) times
+    the same expression on absolute values, sigma_s * sum_h |w_h| sum_d
+    |q_hd k_sd|, which the oracle evaluates on the inputs' magnitudes
+    (sign bit cleared in the e4m3 codes)."""
+    r, p, n = wl.query_positions()[t]
+    if wl.idx_dtype == "f32":
+        keys, q = np.abs(wl.idx_keys), np.abs(wl.q_idx[t])
+    else:
+        keys, q = wl.idx_keys & np.uint8(0x7F), wl.q_idx[t] & np.uint8(0x7F)
+    mag = oracle.indexer_scores(keys, wl.idx_scales, wl.idx_dtype, wl.page_table[r], wl.block_size, q,
+                                "f32" if wl.idx_dtype == "f32" else "e4m3", np.abs(wl.w[t]), n)
+    m = wl.idx_dim + wl.idx_heads + 2
+    u = 2.0 ** -24
+    return m * u / (1.0 - m * u) * mag
+
+
+def check_scores(wl, t, got):
+    """GPU scores of row t (its first n entries) against the oracle, within
+    the fp32 rounding bound of each score."""
+    ref = oracle.query_scores(wl, t)
+    assert got.shape == ref.shape
+    err = np.abs(got.astype(np.float64) - ref)
+    bound = score_bound(wl, t)
+    bad = np.nonzero(err > bound)[0]
+    assert bad.size == 0, "row %d: %d scores outside the fp32 bound, first at %d: got %r ref %r bound %r" % (
+        t, bad.size, bad[0], float(got[bad[0]]), float(ref[bad[0]]), float(bound[bad[0]]))
+
+
 def log(*a):
     print(*a, flush=True)
     sys.stdout.flush()

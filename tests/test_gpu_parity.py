@@ -9,7 +9,7 @@ import torch
 import oracle
 import sparse_attention_dsa_amd as dsa
 import workloads
-from parity import BAND, check_out, check_selection, check_step_rows, gpu_step, log, upload
+from parity import BAND, check_out, check_scores, check_selection, check_step_rows, gpu_step, log, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -37,8 +37,25 @@ def test_indexer_scores_fp8_ragged():
     torch.cuda.synchronize()
     sc = sc.cpu().numpy()
     for t, (r, p, n) in enumerate(wl.query_positions()):
-        ref = oracle.query_scores(wl, t)
-        np.testing.assert_allclose(sc[t, :n], ref, rtol=1e-5, atol=1e-5 * np.abs(ref).max())
+        check_scores(wl, t, sc[t, :n])
+
+
+@pytest.mark.parametrize("heads,scaled", [(64, True), (32, True), (16, True), (64, False)])
+def test_indexer_scores_query_blocks(heads, scaled):
+    """Long query chunks take the query-blocked indexer (8 rows per
+    workgroup, 128-page ranges): ragged query counts (one row, a block plus
+    one row, several blocks), contexts across a page range, causal rows."""
+    wl = workloads.make_workload("single_b1_l32768", batch=4, seed=21, idx_heads=heads,
+                                 context_lens=[70, 700, 3000, 8300], q_len=[1, 9, 17, 40])
+    if not scaled:
+        wl.idx_scales = None
+    log("indexer query blocks", heads, scaled, wl.context_lens.tolist(), wl.q_lens.tolist())
+    batch, d = upload(wl)
+    sc = dsa.indexer_scores(batch, d["idx_keys"], d["idx_scales"] if scaled else None, d["q_idx"], d["w"])
+    torch.cuda.synchronize()
+    sc = sc.cpu().numpy()
+    for t, (r, p, n) in enumerate(wl.query_positions()):
+        check_scores(wl, t, sc[t, :n])
 
 
 def test_indexer_scores_f32_tiny():
