@@ -54,6 +54,12 @@ __device__ __forceinline__ int page_swz(int t) { return (t ^ (t >> 3)) & 7; }
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 template <int N>
+__device__ __forceinline__ void wait_vmcnt_n() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -181,8 +187,8 @@ __global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_dma(IndexerArgs a, in
 // byte brought from L2 feeds PF_QB query rows.  Workgroups are numbered
 // page-range-major: the ones resident together work on the same pages.
 //
-// Every wave issues exactly three transfers per page (two 1 KB key units and
-// the page's scales) and two score stores per page (buffer stores whose descriptors
+// Every wave issues the same transfers for every page (its 1 KB key units and
+// the page's scales) and one score store per query row and page (buffer stores whose descriptors
 // are sized to each row's visible count, so positions past it are dropped),
 // which keeps the vector-memory counts of the ring's waits exact.
 // Scores of one page for PF_QW query rows with the MFMAs of the next token
@@ -221,15 +227,27 @@ __device__ __forceinline__ void page_scores_ilp(const i32x8 (&qf)[NQ][HT], const
     for (int j = 0; j < NQ; ++j) out[j] = head_sum_transpose(part[j], lane) * ksc;
 }
 
-constexpr int PF_WAVES = 4;
-constexpr int PF_QW = 2;                       // query rows per wave
+#ifndef IDX_PF_WAVES
+#define IDX_PF_WAVES 4
+#endif
+#ifndef IDX_PF_QW
+#define IDX_PF_QW 2
+#endif
+constexpr int PF_WAVES = IDX_PF_WAVES;
+constexpr int PF_QW = IDX_PF_QW;               // query rows per wave
 constexpr int PF_QB = PF_WAVES * PF_QW;        // query rows per workgroup
+constexpr int PF_KU = 8 / PF_WAVES;            // 1 KB key units each wave moves per page
+constexpr int PF_OPS = PF_KU + 1;              // transfers per wave per page (keys, scales)
 constexpr int PF_CHUNK = 128;                  // pages per workgroup
 constexpr int PF_RING = 4;                     // page slots
 constexpr int PF_MIN_Q = 8;                    // longest query chunk from which it is used
 
 template <int HT>
-__global__ __launch_bounds__(PF_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2))) void indexer_fp8_prefill(IndexerArgs a, int qblocks) {
+#ifndef IDX_PF_WPE
+#define IDX_PF_WPE 2
+#endif
+__global__ __launch_bounds__(PF_WAVES * 64) __attribute__((amdgpu_waves_per_eu(IDX_PF_WPE)))
+void indexer_fp8_prefill(IndexerArgs a, int qblocks) {
     const Geometry& G = a.g;
     const int r = blockIdx.x / qblocks, jb = blockIdx.x % qblocks;
     const int qs = G.qsl[r], ql = G.qsl[r + 1] - qs;
@@ -301,10 +319,10 @@ __global__ __launch_bounds__(PF_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2
         const int blk = __builtin_amdgcn_readlane(bv, p & 63);
         const uint8_t* src = keys + (size_t)blk * (IDX_PAGE * IDX_D);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int U = 64 * (2 * wave + c) + lane, t = U >> 3, u = (U & 7) ^ page_swz(t);
+        for (int c = 0; c < PF_KU; ++c) {
+            const int U = 64 * (PF_KU * wave + c) + lane, t = U >> 3, u = (U & 7) ^ page_swz(t);
             __builtin_amdgcn_global_load_lds((const void*)(src + t * IDX_D + 16 * u),
-                                             (lds_ptr_t)(dst + 1024 * (2 * wave + c)), 16, 0, DMA_AUX);
+                                             (lds_ptr_t)(dst + 1024 * (PF_KU * wave + c)), 16, 0, DMA_AUX);
         }
         // the 256 B of scales as 16-byte units: lane l moves unit l & 15, so
         // the slot holds four copies
@@ -319,10 +337,11 @@ __global__ __launch_bounds__(PF_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2
     for (int p = 0; p < np; ++p) {
         // page p's transfers of this wave are done once at most the younger
         // operations are pending: in steady state the stores of the three
-        // previous pages (2 each) and the transfers of the next two (3 each)
-        if (p >= PF_RING - 1 && p + 2 < np) wait_vmcnt<12>();
-        else if (p + 2 < np) wait_vmcnt<6>();
-        else wait_vmcnt<0>();
+        // previous pages and the transfers of the next two; before that, at
+        // least the next two pages' transfers
+        if (p >= PF_RING - 1 && p + 2 < np) wait_vmcnt_n<3 * PF_QW + 2 * PF_OPS>();
+        else if (p + 2 < np) wait_vmcnt_n<2 * PF_OPS>();
+        else wait_vmcnt_n<0>();
         lds_barrier();   // every wave's part of page p landed; the slot of page p - 1 is free
         // the slot read and the slot refilled are passed as __restrict__
         // pointers: the compiler then knows the transfers in flight cannot

@@ -572,47 +572,42 @@ void mla_h128(MlaArgs a, int slice) {
     }
     __syncthreads();
 
-    // one tile's rows into ring buffer b: instruction i of wave w moves LDS
-    // units 64(9w+i) .. +63; LDS unit (row rr, physical unit pu) holds logical
-    // unit pu ^ ks_swz(rr) of that row.  The instruction's first unit is
-    // uniform, so a lane's row is the first row or the next one.
+    // Tile layout in LDS (32 rows of 72 16-byte units): the 1 KB block
+    // (r >> 3, u >> 3) sits at 1024 (9 (r >> 3) + (u >> 3)); inside it row
+    // r & 7 takes 128 B and holds its units u & 7 XOR-permuted by r & 7, so
+    // that one unit of the block's 8 rows covers all banks:
+    //   tile_off(r, u) = 1024 (9 (r >> 3) + (u >> 3)) + 16 (8 (r & 7) + ((u & 7) ^ (r & 7))).
+    // Wave w moves rows 8w .. 8w+7: its instruction i covers units 8i .. 8i+7
+    // of each, lane l taking row 8w + (l >> 3) and unit 8i + ((l & 7) ^ (l >> 3)),
+    // which the transfer writes at 16 l of the instruction's 1 KB block, i.e.
+    // at tile_off.  All nine instructions of a lane read the same row, so a
+    // tile costs one row id per lane and immediate offsets.
+    static_assert(M_TILE == 32 && M_THREADS == 256 && M_ROW_UNITS == 72 && M3_DMA_PER_WAVE == 9,
+                  "tile layout: 4 waves x 8 rows, 9 blocks of 8 units per row");
+    const int dma_col = 16 * ((lane & 7) ^ (lane >> 3));
     auto issue = [&](int tile, int b) {
-        const int32_t* trows = rows + M_TILE * tile;
-        int ln = lane;
-        asm volatile("" : "+v"(ln));   // recomputed per tile: hoisted, these would hold 18 registers
-        int row[M3_DMA_PER_WAVE], off[M3_DMA_PER_WAVE];
+        const int row = rows[M_TILE * tile + 8 * wave + (lane >> 3)];
+        const uint8_t* src = (const uint8_t*)a.kv + (size_t)row * M_ROW_BYTES + dma_col;
+        uint8_t* dst = &Ks[b][0] + 1024 * M3_DMA_PER_WAVE * wave;
 #pragma unroll
-        for (int i = 0; i < M3_DMA_PER_WAVE; ++i) {
-            const int U0 = (wave * M3_DMA_PER_WAVE + i) * 64;
-            const int rr0 = U0 / M_ROW_UNITS, pu0 = U0 - rr0 * M_ROW_UNITS;
-            int pu = pu0 + ln;
-            const bool wrap = pu >= M_ROW_UNITS;
-            const int rr = rr0 + (wrap ? 1 : 0);
-            pu -= wrap ? M_ROW_UNITS : 0;
-            off[i] = 16 * (pu ^ ks_swz(rr));
-            row[i] = trows[rr];
-        }
-#pragma unroll
-        for (int i = 0; i < M3_DMA_PER_WAVE; ++i) {
-            const uint8_t* src = (const uint8_t*)a.kv + (size_t)row[i] * M_ROW_BYTES + off[i];
-            __builtin_amdgcn_global_load_lds((const void*)src,
-                                             (lds_vptr)(&Ks[b][0] + 1024 * (wave * M3_DMA_PER_WAVE + i)), 16, 0, 0);
-        }
+        for (int i = 0; i < M3_DMA_PER_WAVE; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(src + 128 * i), (lds_vptr)(dst + 1024 * i), 16, 0, 0);
     };
 
-    // per-lane LDS offsets (XOR by ks_swz(r) < 8 only touches the low 3 bits
-    // of a unit index, so fragment reads are few bases plus immediates)
-    int qk_base[4];       // S^T A operand: row c32, unit 2ks + hh; [ks % 4]
+    // per-lane LDS offsets: unit 8m + e of row r is at the offset of unit e
+    // plus 1024 m, so fragment reads are few bases plus immediates
+    int qk_base[4];       // S^T A operand: row c32, unit 2ks + hh; [ks % 4], + 1024 (ks / 4)
     {
-        const int sw = ks_swz(c32);
+        const int rb = 9216 * (c32 >> 3) + 128 * (c32 & 7), sw = c32 & 7;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) qk_base[m] = c32 * M_ROW_BYTES + 16 * ((2 * m + hh) ^ sw);
+        for (int m = 0; m < 4; ++m) qk_base[m] = rb + 16 * ((2 * m + hh) ^ sw);
     }
     // V^T A operand by transposing reads: in 16-lane group g4 (hh = g4 >> 1,
     // column half 16(g4 & 1)), source lane s = 4jj + q points at token
-    // 16kk + 8rd + 4hh + jj, columns 32cb + 16(g4 & 1) + 4q .. +3, and
-    // destination lane d receives column d of the half, tokens jj = 0..3.
-    int pv_base[2][2][2];   // [kk][rd][cb & 1]
+    // 16kk + 8rd + 4hh + jj, columns 32cb + 16(g4 & 1) + 4q .. +3 (unit
+    // 4cb + v, v = 2(g4 & 1) + (q >> 1)), and destination lane d receives
+    // column d of the half, tokens jj = 0..3.
+    int pv_base[2][2][2];   // [kk][rd][cb & 1], + 1024 (cb / 2)
     {
         const int s16 = lane & 15, jj = s16 >> 2, q = s16 & 3;
         const int v = 2 * ((lane >> 4) & 1) + (q >> 1);
@@ -623,7 +618,8 @@ void mla_h128(MlaArgs a, int slice) {
                 const int tok = 16 * kk + 8 * rd + 4 * hh + jj;
 #pragma unroll
                 for (int c1 = 0; c1 < 2; ++c1)
-                    pv_base[kk][rd][c1] = tok * M_ROW_BYTES + 16 * ((4 * c1 + v) ^ ks_swz(tok)) + 8 * (q & 1);
+                    pv_base[kk][rd][c1] = 9216 * (tok >> 3) + 128 * (tok & 7) + 16 * ((4 * c1 + v) ^ (tok & 7)) +
+                                          8 * (q & 1);
             }
     }
 
@@ -666,7 +662,7 @@ void mla_h128(MlaArgs a, int slice) {
             constexpr int NK = M_DQK / 16;
             u32x4 kb[M3_KPF];
 #pragma unroll
-            for (int j = 0; j < M3_KPF; ++j) kb[j] = *(const u32x4*)(Kb + qk_base[j & 3] + 128 * (j >> 2));
+            for (int j = 0; j < M3_KPF; ++j) kb[j] = *(const u32x4*)(Kb + qk_base[j & 3] + 1024 * (j >> 2));
             // scheduling groups: the prefetch reads first, then MFMA / read pairs
             __builtin_amdgcn_sched_group_barrier(0x100, M3_KPF, 0);
             __builtin_amdgcn_sched_barrier(0);
@@ -675,7 +671,7 @@ void mla_h128(MlaArgs a, int slice) {
                 st = mfma_bf16_32x32x16(as_bf16x8(kb[ks % M3_KPF]), as_bf16x8(qf[ks]), st);
                 if (ks + M3_KPF < NK) {
                     const int kn = ks + M3_KPF;
-                    kb[ks % M3_KPF] = *(const u32x4*)(Kb + qk_base[kn & 3] + 128 * (kn >> 2));
+                    kb[ks % M3_KPF] = *(const u32x4*)(Kb + qk_base[kn & 3] + 1024 * (kn >> 2));
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // then one LDS read
@@ -737,9 +733,9 @@ void mla_h128(MlaArgs a, int slice) {
             auto vread = [&](int n, s16x4& v0, s16x4& v1) {
                 const int kk = n / (M_DL / 32), cb = n % (M_DL / 32);
                 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4_ptr)(Kb + pv_base[kk][0][cb & 1] + 128 * (cb >> 1)));
+                    (lds_s16x4_ptr)(Kb + pv_base[kk][0][cb & 1] + 1024 * (cb >> 1)));
                 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4_ptr)(Kb + pv_base[kk][1][cb & 1] + 128 * (cb >> 1)));
+                    (lds_s16x4_ptr)(Kb + pv_base[kk][1][cb & 1] + 1024 * (cb >> 1)));
             };
             s16x4 vb0[M3_VPF], vb1[M3_VPF];
 #pragma unroll
