@@ -65,6 +65,22 @@ __device__ __forceinline__ f32x4 mfma_bf16_16x16x32(bf16x8 a, bf16x8 b, f32x4 c)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Value held by lane (lane ^ 32), exchanged with v_permlane32_swap (the
+// upper half of the first operand trades places with the lower half of the
+// second; with both operands x, lane l < 32 finds x[l + 32] in the second
+// result and lane l >= 32 finds x[l - 32] in the first), no LDS round trip.
+__device__ __forceinline__ float lane_xor32(float x, int lane) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(lane < 32 ? r[1] : r[0]);
+}
+
+// Value held by lane (lane ^ 16), by v_permlane16_swap (odd 16-lane rows of
+// the first operand trade places with even rows of the second).
+__device__ __forceinline__ float lane_xor16(float x, int lane) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float((lane & 16) ? r[0] : r[1]);
+}
+
 __device__ __forceinline__ i32x8 join_i32x8(u32x4 lo, u32x4 hi) {
     i32x8 r;
     r[0] = (int)lo[0]; r[1] = (int)lo[1]; r[2] = (int)lo[2]; r[3] = (int)lo[3];

@@ -19,22 +19,6 @@ constexpr int IDX_D = 128;
 constexpr int IDX_PAGE = 64;
 constexpr int IDX_THREADS = 256;
 
-// Value held by lane (lane ^ 32), exchanged with v_permlane32_swap (the
-// upper half of the first operand trades places with the lower half of the
-// second; with both operands x, lane l < 32 finds x[l + 32] in the second
-// result and lane l >= 32 finds x[l - 32] in the first), no LDS round trip.
-__device__ __forceinline__ float lane_xor32(float x, int lane) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(lane < 32 ? r[1] : r[0]);
-}
-
-// Value held by lane (lane ^ 16), by v_permlane16_swap (odd 16-lane rows of
-// the first operand trade places with even rows of the second).
-__device__ __forceinline__ float lane_xor16(float x, int lane) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float((lane & 16) ? r[0] : r[1]);
-}
-
 // part[nt] holds, for token 16*nt + (lane & 15), the partial head sum of this
 // lane's 16-lane group g.  Returns the full sum for token `lane` of the page.
 __device__ __forceinline__ float head_sum_transpose(const float part[4], int lane) {

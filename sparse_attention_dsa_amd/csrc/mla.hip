@@ -498,6 +498,19 @@ __device__ __forceinline__ f32x16 mfma_bf16_32x32x16(bf16x8 a, bf16x8 b, f32x16 
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// 32-bit LDS address of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// max(a, b, c) in one instruction (fmaxf would first canonicalize every
+// input it cannot prove canonical; no NaN reaches these)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -649,68 +662,97 @@ void mla_h128(MlaArgs a, int slice) {
         else if (later == 1) wait_vmcnt<M3_DMA_PER_WAVE>();
         else wait_vmcnt<0>();
         lds_barrier();   // everyone's part of tile i landed; tile i-1's buffer is free
-        if (i + M3_NBUF - 1 < ntiles) issue(i + M3_NBUF - 1, (i + M3_NBUF - 1) % M3_NBUF);
         const uint8_t* Kb = &Ks[i % M3_NBUF][0];
 
         const uint32_t vmask = tvalid[i];   // tokens present in the tile (bit per slot)
 
-        // S^T: K fragments read M3_KPF steps ahead of their MFMA
+        // S^T: K fragments read M3_KPF steps ahead of their MFMA; the nine
+        // transfers of tile i+3 (into the buffer tile i-1 has left) are
+        // spread over the MFMAs, one after every fourth, so that issuing them
+        // never holds up the matrix core for long
         f32x16 st;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) st[e] = 0.f;
         {
             constexpr int NK = M_DQK / 16;
-            u32x4 kb[M3_KPF];
+            const int nt = i + M3_NBUF - 1;
+            const bool iss = nt < ntiles;
+            const uint8_t* dsrc = (const uint8_t*)a.kv +
+                                  (size_t)rows[M_TILE * min(nt, ntiles - 1) + 8 * wave + (lane >> 3)] * M_ROW_BYTES +
+                                  dma_col;
+            auto qk = [&](const uint8_t* kbuf, uint8_t* dst, bool dma) {
+                u32x4 kb[M3_KPF];
 #pragma unroll
-            for (int j = 0; j < M3_KPF; ++j) kb[j] = *(const u32x4*)(Kb + qk_base[j & 3] + 1024 * (j >> 2));
-            // scheduling groups: the prefetch reads first, then MFMA / read pairs
-            __builtin_amdgcn_sched_group_barrier(0x100, M3_KPF, 0);
-            __builtin_amdgcn_sched_barrier(0);
+                for (int j = 0; j < M3_KPF; ++j) kb[j] = *(const u32x4*)(kbuf + qk_base[j & 3] + 1024 * (j >> 2));
+                __builtin_amdgcn_sched_group_barrier(0x100, M3_KPF, 0);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int ks = 0; ks < NK; ++ks) {
-                st = mfma_bf16_32x32x16(as_bf16x8(kb[ks % M3_KPF]), as_bf16x8(qf[ks]), st);
-                if (ks + M3_KPF < NK) {
-                    const int kn = ks + M3_KPF;
-                    kb[ks % M3_KPF] = *(const u32x4*)(Kb + qk_base[kn & 3] + 1024 * (kn >> 2));
+                for (int ks = 0; ks < NK; ++ks) {
+                    if (ks == 0) st = mfma_bf16_32x32x16(as_bf16x8(kb[0]), as_bf16x8(qf[0]), f32x16{});
+                    else st = mfma_bf16_32x32x16(as_bf16x8(kb[ks % M3_KPF]), as_bf16x8(qf[ks]), st);
+                    if (ks + M3_KPF < NK) {
+                        const int kn = ks + M3_KPF;
+                        kb[ks % M3_KPF] = *(const u32x4*)(kbuf + qk_base[kn & 3] + 1024 * (kn >> 2));
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // then one LDS read
+                    if (dma && (ks & 3) == 1) {
+                        // Issued by inline asm: the compiler does not track it as an
+                        // LDS write, so it puts no wait for it before the fragment
+                        // reads of tile i, which use another buffer (the loop's own
+                        // vector-memory waits count these transfers).  M0 holds the
+                        // LDS address and is restored afterwards; no immediate
+                        // offset, which the LDS destination would include as well.
+                        const uint32_t m0v = lds_addr(dst + 1024 * (ks >> 2));
+                        const uint8_t* gsrc = dsrc + 128 * (ks >> 2);
+                        uint32_t saved;
+                        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                                     "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+                                     : "=&s"(saved) : "v"(gsrc), "s"(m0v));
+                    }
                 }
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // then one LDS read
-            }
+            };
+            uint8_t* ddst = &Ks[nt % M3_NBUF][0] + 1024 * M3_DMA_PER_WAVE * wave;
+            if (iss) qk(Kb, ddst, true);
+            else qk(Kb, ddst, false);
         }
-        // element e of this lane: token 8(e/4) + 4hh + e%4, head c32
-        float x[16];
-        if (vmask == 0xFFFFFFFFu) {
+        // element e of this lane: token 8(e/4) + 4hh + e%4, head c32.
+        // The tile's largest logit comes from the raw scores' extreme in the
+        // direction of the scale's sign, slots without a token excluded (the
+        // tiles with padding only); probabilities are exp2(s * zscale - ref)
+        // by one fused multiply-add, zero for those slots.
+        const bool full = vmask == 0xFFFFFFFFu;
+        float ext;
+        if (zscale >= 0.f) {
+            float sm[16];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) x[e] = st[e] * zscale;
+            for (int e = 0; e < 16; ++e) sm[e] = st[e];
+            if (!full) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    sm[e] = (vmask >> (8 * (e >> 2) + 4 * hh + (e & 3))) & 1u ? sm[e] : -INFINITY;
+            }
+            ext = fmaxf(max3f(max3f(sm[0], sm[1], sm[2]), max3f(sm[3], sm[4], sm[5]), max3f(sm[6], sm[7], sm[8])),
+                        max3f(max3f(sm[9], sm[10], sm[11]), max3f(sm[12], sm[13], sm[14]), sm[15]));
         } else {
+            ext = INFINITY;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int tok = 8 * (e >> 2) + 4 * hh + (e & 3);
-                x[e] = (vmask >> tok) & 1u ? st[e] * zscale : -INFINITY;
-            }
+            for (int e = 0; e < 16; ++e)
+                if (full || ((vmask >> (8 * (e >> 2) + 4 * hh + (e & 3))) & 1u)) ext = fminf(ext, st[e]);
         }
-        float tmax;
-        {   // max and (below) sum as balanced trees
-            float m8[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) m8[e] = fmaxf(x[e], x[e + 8]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) m8[e] = fmaxf(m8[e], m8[e + 4]);
-            tmax = fmaxf(fmaxf(m8[0], m8[2]), fmaxf(m8[1], m8[3]));
-        }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        float tmax = vmask ? ext * zscale : -INFINITY;
+        tmax = fmaxf(tmax, lane_xor32(tmax, lane));
         m_seen = fmaxf(m_seen, tmax);
         if (m_ref == -INFINITY) m_ref = tmax;   // first visible token of this head
         overflow |= tmax > m_ref + 64.f;
-        // every head of the wave has the same visible tokens, so m_ref is
-        // -inf in all lanes or in none
+        // before the first visible token (m_ref = -inf in all lanes of the
+        // wave, whose heads share their tokens) every probability is 0
+        const float mre = m_ref == -INFINITY ? INFINITY : m_ref;
         float p[16];
-        if (m_ref == -INFINITY) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) p[e] = 0.f;
-        } else {
+        for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(st[e], zscale, -mre));
+        if (!full) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(x[e] - m_ref);
+            for (int e = 0; e < 16; ++e)
+                p[e] = (vmask >> (8 * (e >> 2) + 4 * hh + (e & 3))) & 1u ? p[e] : 0.f;
         }
         {
             float s8[8];
@@ -767,7 +809,7 @@ void mla_h128(MlaArgs a, int slice) {
     const float m_run = m_ref;
 
     // ---- epilogue: element e of block cb is O^T[32cb + 8(e/4) + 4hh + e%4][head]
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = l_run + lane_xor32(l_run, lane);
     const bool empty = l_tot == 0.f;
     const float inv = empty ? 0.f : 1.f / l_tot;
     const float lse_nat = empty ? -INFINITY : (m_run + log2f(l_tot)) * LN2;
