@@ -707,16 +707,22 @@ __global__ __launch_bounds__(SB_THREADS) void indexer_sample_bound(IndexerArgs a
     const int m = sample_size(n);
     const int per_wave = m / (SB_THREADS / 64);          // 64 .. 256 samples
     const int nfrag = per_wave / 16;
-    // lane (g, col) of fragment f handles sample i = i0 + 16 f + col; four
-    // fragments in flight at a time (1024 threads leave 128 registers a lane)
+    const int nrun = m / 16;
+    // The sample is m / 16 runs of 16 consecutive tokens at evenly spaced,
+    // 16-aligned starts, so a run lies in one page: one page-table entry and
+    // one contiguous 2 KB of keys.  Fragment f of wave w is run w nfrag + f,
+    // lane (g, col) taking its token col (sample i0 + 16 f); four fragments
+    // in flight at a time (1024 threads leave 128 registers a lane).
     const int i0 = wave * per_wave + (lane & 15);
+    const int last = (n - 16) & ~15;
     for (int f0 = 0; f0 < nfrag; f0 += SB_BATCH) {
         int blk[SB_BATCH], row[SB_BATCH];
 #pragma unroll
         for (int b = 0; b < SB_BATCH; ++b) {
-            const int s = sample_pos(i0 + 16 * min(f0 + b, nfrag - 1), n, m);
-            blk[b] = pt[s / IDX_PAGE];
-            row[b] = s % IDX_PAGE;
+            const int run = wave * nfrag + min(f0 + b, nfrag - 1);
+            const int start = min((int)((long long)run * n / nrun) & ~15, last);
+            blk[b] = pt[start / IDX_PAGE];
+            row[b] = start % IDX_PAGE + (lane & 15);
         }
         i32x8 kf[SB_BATCH];
         float ksc[SB_BATCH];

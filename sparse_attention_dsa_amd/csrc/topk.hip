@@ -60,11 +60,17 @@ __global__ __launch_bounds__(BND_THREADS) void topk_bound(TopkArgs a) {
     __shared__ uint32_t skeys[TK_SAMPLE_MAX];
     __shared__ uint32_t h[256], res;
     __shared__ uint32_t red[2][BND_THREADS / 64];
+    // the sample as m / 16 runs of 16 consecutive scores at evenly spaced
+    // starts: each run is one 64-byte segment of the row, so the sample
+    // touches m / 16 segments instead of m
     const int m = sample_size(n);
+    const int nrun = m / 16;
     float v[NS];
 #pragma unroll
-    for (int i = 0; i < NS; ++i)
-        if (tid + i * BND_THREADS < m) v[i] = row[sample_pos(tid + i * BND_THREADS, n, m)];
+    for (int i = 0; i < NS; ++i) {
+        const int j = tid + i * BND_THREADS;
+        if (j < m) v[i] = row[min((int)((long long)(j >> 4) * n / nrun), n - 16) + (j & 15)];
+    }
 #pragma unroll
     for (int i = 0; i < NS; ++i)
         if (tid + i * BND_THREADS < m) skeys[tid + i * BND_THREADS] = score_key(v[i]);

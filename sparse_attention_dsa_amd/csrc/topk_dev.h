@@ -7,12 +7,12 @@
 
 namespace dsa {
 
-// Strided sample of a long row: TK_SAMPLE positions per 128K tokens, at most
-// TK_SAMPLE_MAX; sample i sits at floor(i n / m).
+// Sample of a long row: TK_SAMPLE positions per 128K tokens, at most
+// TK_SAMPLE_MAX, taken as m / 16 runs of 16 consecutive positions at evenly
+// spaced starts (each kernel that draws one states its starts).
 constexpr int TK_SAMPLE = 1024;
 constexpr int TK_SAMPLE_MAX = 4096;
 __device__ __forceinline__ int sample_size(int n) { return TK_SAMPLE * min(TK_SAMPLE_MAX / TK_SAMPLE, (n + 131071) / 131072); }
-__device__ __forceinline__ int sample_pos(int i, int n, int m) { return (int)((long long)i * n / m); }
 
 // Order-preserving map's inverse for ">=" tests on floats: for finite v,
 // score_key(v) >= x  <=>  v >= key_floor(x)  (x a key of a finite float or

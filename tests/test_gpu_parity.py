@@ -277,9 +277,12 @@ def test_indexshare_decode_group(case):
 
 
 def _sample_positions(n, m=1024):
-    """Token positions of the strided sample the top-K bound is drawn from
-    (m per 128K tokens of the row): floor(i n / m)."""
-    return [i * n // m for i in range(m)]
+    """Token positions of the sample the decode step's top-K bound is drawn
+    from (m per 128K tokens of the row): m / 16 runs of 16 consecutive tokens,
+    run j starting at floor(j n / (m / 16)) rounded down to a multiple of 16,
+    at most n - 16 rounded down likewise."""
+    nrun, last = m // 16, (n - 16) & ~15
+    return [min((j * n // nrun) & ~15, last) + c for j in range(nrun) for c in range(16)]
 
 
 def test_decode_step_bound_fallbacks():
