@@ -162,6 +162,26 @@ def test_decode_step(case):
     log("  worst abs err", worst)
 
 
+@pytest.mark.parametrize("q_len", [[2, 0, 1], [0, 9, 1]])
+def test_decode_step_request_without_queries(q_len):
+    """A request with no new query rows in the batch (its pages are in the
+    page table but nothing reads them) between requests that have some: every
+    row still matches the oracle.  The second case also takes the
+    query-blocked indexer (9 rows in one request)."""
+    wl = workloads.make_workload("single_b1_l32768", batch=3, context_lens=[5000, 14000, 3000], q_len=q_len,
+                                 seed=23)
+    assert wl.total_q == sum(q_len)
+    log("decode_step request without queries", wl.context_lens.tolist(), wl.q_lens.tolist())
+    batch, d = upload(wl)
+    out, lse, idx = gpu_step(wl, batch, d)
+    check_step_rows(wl, list(range(wl.total_q)), out, lse, idx)
+    sc = dsa.indexer_scores(batch, d["idx_keys"], d["idx_scales"], d["q_idx"], d["w"])
+    torch.cuda.synchronize()
+    sc = sc.cpu().numpy()
+    for t, (r, p, n) in enumerate(wl.query_positions()):
+        check_scores(wl, t, sc[t, :n])
+
+
 def test_decode_step_zero_query_ties():
     """All indexer scores tie at 0 -> the lowest K indices, bit-exact."""
     wl = workloads.make_workload("single_b1_l32768", batch=2, context_lens=[4000, 2100], seed=15)
