@@ -20,6 +20,8 @@ context: indexer scores, top-K, then sparse MLA prefill on two layers that
 share the selection) call by call, and reports each contraction as MFMA
 utilisation (achieved FLOP/s over the dense fp8 / bf16 peak), since at that
 shape both are compute-bound; the top-K time is reported on its own.
+`other_configs` gives the step on the other decode configurations, and
+`hbm_ceiling` a plain 2 GiB streaming read as the practical bandwidth ceiling.
 `indexshare` times groups of layers that share one selection (one full step,
 then sparse MLA only on the other layers' caches) and reports the amortised
 tokens/s per layer.  `all_128k` repeats the step measurement with every
@@ -367,6 +369,54 @@ def prefill_leg(iters, warmup, log):
     return res
 
 
+OTHER_WORKLOADS = ("tiny_fp32_l4096", "single_b1_l32768", "mtp_b8_l202752")
+
+
+def other_configs(steps, warmup, log):
+    """The decode step on the other decode configurations (one request at
+    4096 fp32 / 32768 tokens; 8 requests at 202752 tokens with two MTP query
+    rows and an e4m3 latent cache): step time, tokens/s and the step's
+    algorithmic bytes over its time."""
+    import workloads
+    res = {}
+    for name in OTHER_WORKLOADS:
+        wl = workloads.make_workload(name)
+        rig = Rig(wl, 4, lambda *a: None)
+        ms = rig.time_loop(rig.step, steps, warmup)
+        sb = step_bytes(wl, rig.selection())
+        res[name] = {"ms_per_step": round(ms, 5), "tokens_per_s": round(wl.total_q / (ms * 1e-3), 1),
+                     "step_bytes": sb, "step_hbm_frac": round(sb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        log("[bench] %s: step %.1f us" % (name, ms * 1e3))
+        rig.free()
+        del rig
+    return res
+
+
+def read_ceiling(log, nbytes=1 << 31, iters=20):
+    """The library's streaming-read probe over 2 GiB (every byte read once
+    with 16-byte non-temporal loads): the practical HBM read ceiling next to
+    the 8 TB/s peak."""
+    import torch
+    from sparse_attention_dsa_amd import binding as B
+    x = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    sink = B.read_probe(x)
+    for _ in range(3):
+        B.read_probe(x, sink)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(iters):
+        B.read_probe(x, sink)
+    ev1.record()
+    torch.cuda.synchronize()
+    gbs = nbytes * iters / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    log("[bench] streaming read: %.0f GB/s" % gbs)
+    del x, sink
+    torch.cuda.empty_cache()
+    return {"kernel": "dsa_read_probe over 2 GiB", "achieved": round(gbs, 1), "unit": "GB/s",
+            "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 # ------------------------------------------------------------------ main
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -383,6 +433,8 @@ def main(argv=None):
                     help="skip the extra measurement with every context at 131072 tokens")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the chunked-prefill measurement (4096 queries on a 131072-token context)")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the other decode configurations and the streaming-read ceiling")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -458,6 +510,12 @@ def main(argv=None):
     if not args.no_prefill and args.workload == DEFAULT_WORKLOAD:
         prefill = prefill_leg(max(3, min(args.steps, 10)), 2, log)
 
+    # Other decode configurations, and a plain streaming read as the practical HBM ceiling.
+    others = ceiling = None
+    if not args.no_others and args.workload == DEFAULT_WORKLOAD:
+        others = other_configs(max(10, min(args.steps, 50)), 5, log)
+        ceiling = read_ceiling(log)
+
     # CPU baseline: the oracle on a bounded sample of query rows.
     cpu = None
     if args.cpu_rows > 0:
@@ -503,6 +561,8 @@ def main(argv=None):
         "indexshare": share,
         "all_128k": at128,
         "prefill": prefill,
+        "other_configs": others,
+        "hbm_ceiling": ceiling,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

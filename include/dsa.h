@@ -179,6 +179,20 @@ const char *dsa_status_string(int32_t status);
 /* DSA_OK if the current HIP device is gfx950, else DSA_ERR_DEVICE. */
 int dsa_check_device(void);
 
+/* Measurement helper, not a step of the method: the practical HBM read
+ * bandwidth that the library's streaming kernels are compared against.
+ * dsa_read_probe reads every byte of `buf` (device memory, 16-byte aligned,
+ * nbytes a positive multiple of 16, caller-owned) exactly once with 16-byte
+ * non-temporal loads, and writes one 32-bit word per workgroup to `sink`
+ * (device, caller-owned, at least dsa_read_probe_sink_size() bytes; its
+ * contents are meaningless), asynchronously on `stream`; time it with events
+ * around the call.  DSA_ERR_INVALID_ARG for a null, misaligned or
+ * wrongly sized buffer, DSA_ERR_WORKSPACE for a small sink, DSA_ERR_LAUNCH if
+ * the launch fails.  dsa_read_probe_sink_size queries the current device's
+ * CU count. */
+size_t dsa_read_probe_sink_size(void);
+int dsa_read_probe(const void *buf, int64_t nbytes, void *sink, size_t sink_bytes, dsa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

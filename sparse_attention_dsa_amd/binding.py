@@ -20,7 +20,8 @@ F32, BF16, E4M3 = 0, 1, 2
 OP_TOPK, OP_MLA_DECODE, OP_MLA_PREFILL, OP_DECODE_STEP = 1, 2, 3, 4
 
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
-           "dsa_decode_step", "dsa_workspace_size", "dsa_status_string", "dsa_check_device")
+           "dsa_decode_step", "dsa_workspace_size", "dsa_status_string", "dsa_check_device",
+           "dsa_read_probe_sink_size", "dsa_read_probe")
 
 
 class DsaBatch(C.Structure):
@@ -63,8 +64,11 @@ def lib():
         L.dsa_status_string.argtypes = [i32]
         L.dsa_status_string.restype = C.c_char_p
         L.dsa_check_device.argtypes = []
+        L.dsa_read_probe_sink_size.argtypes = []
+        L.dsa_read_probe_sink_size.restype = sz
+        L.dsa_read_probe.argtypes = [vp, i64, vp, sz, vp]
         for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
-                     "dsa_decode_step", "dsa_check_device"):
+                     "dsa_decode_step", "dsa_check_device", "dsa_read_probe"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -208,6 +212,15 @@ def decode_step(batch: Batch, keys, key_scales, q_idx, w, kv, kv_scales, d_laten
         q_mla.shape[1], k, float(scale), _ptr(out), _ptr(lse), _ptr(indices_out), _ptr(ws), ws.numel(),
         _stream(stream)))
     return out
+
+
+def read_probe(buf: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Read every byte of a device buffer once (bandwidth measurement helper)."""
+    n = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.empty(max(int(lib().dsa_read_probe_sink_size()), 4), dtype=torch.uint8, device=buf.device)
+    _check("dsa_read_probe", lib().dsa_read_probe(_ptr(buf), n, _ptr(sink), sink.numel(), _stream(stream)))
+    return sink
 
 
 def check_device() -> int:

@@ -198,8 +198,9 @@ int validate_mla(const dsa_batch* b, const dsa_latent_cache* c, const void* q, i
     if (!c || !c->kv) return DSA_ERR_INVALID_ARG;
     if (!latent_cache_ok(c)) return DSA_ERR_UNSUPPORTED;
     if (!mla_fast_path(c->dtype, c->d_latent, c->d_rope, n_heads, b->block_size)) {
-        // generic path keeps q row and logits in LDS
-        if ((size_t)(c->d_latent + c->d_rope + k) * sizeof(float) > 60 * 1024) return DSA_ERR_UNSUPPORTED;
+        // generic path keeps the selection's rows, the q row and the logits in LDS
+        if ((size_t)k * sizeof(int64_t) + (size_t)(c->d_latent + c->d_rope + k) * sizeof(float) > 60 * 1024)
+            return DSA_ERR_UNSUPPORTED;
     }
     return DSA_OK;
 }

@@ -395,14 +395,23 @@ __global__ __launch_bounds__(256) void mla_generic(MlaArgs a) {
     const int t = blockIdx.x / a.n_heads, h = blockIdx.x % a.n_heads;
     const int r = find_request(G.qsl, G.B, t);
     const int W = a.d_latent + a.d_rope, D = a.d_latent;
-    extern __shared__ float smem[];
-    float* qv = smem;            // [W]
-    float* z = smem + W;         // [k]
+    extern __shared__ int64_t smem64[];
+    int64_t* rows = smem64;                       // [k] physical row of each slot (-1: padding)
+    float* qv = (float*)(smem64 + a.k);           // [W]
+    float* z = qv + W;                            // [k]
     __shared__ float red[256];
     const bool f32 = a.kv_dtype == 0;
+    const int32_t* sel = a.indices + (size_t)t * a.k;
+    const int32_t* pt = G.page_table + (size_t)r * G.max_blocks;
+    const int bs = G.block_size;
     for (int c = threadIdx.x; c < W; c += blockDim.x) {
         const size_t off = ((size_t)t * a.n_heads + h) * W + c;
         qv[c] = f32 ? ((const float*)a.q)[off] : bf16_to_f32(((const uint16_t*)a.q)[off]);
+    }
+    // the selection's rows through the page table, once
+    for (int j = threadIdx.x; j < a.k; j += blockDim.x) {
+        const int s = sel[j];
+        rows[j] = s >= 0 ? (int64_t)pt[s / bs] * bs + s % bs : -1;
     }
     __syncthreads();
     auto elem = [&](int64_t row, int c) -> float {
@@ -411,16 +420,13 @@ __global__ __launch_bounds__(256) void mla_generic(MlaArgs a) {
         if (a.kv_dtype == 1) return bf16_to_f32(((const uint16_t*)a.kv)[off]);
         return e4m3_to_f32(((const uint8_t*)a.kv)[off]) * a.kv_scales[row];
     };
-    const int32_t* sel = a.indices + (size_t)t * a.k;
-    const int32_t* pt = G.page_table + (size_t)r * G.max_blocks;
-    const int bs = G.block_size;
     float lmax = -INFINITY;
     for (int j = threadIdx.x; j < a.k; j += blockDim.x) {
-        const int s = sel[j];
+        const int64_t row = rows[j];
         float zj = -INFINITY;
-        if (s >= 0) {
-            const int64_t row = (int64_t)pt[s / bs] * bs + s % bs;
+        if (row >= 0) {
             float dot = 0.f;
+#pragma unroll 8
             for (int c = 0; c < W; ++c) dot = fmaf(qv[c], elem(row, c), dot);
             zj = dot * a.scale;
         }
@@ -437,7 +443,7 @@ __global__ __launch_bounds__(256) void mla_generic(MlaArgs a) {
     __syncthreads();
     float lsum = 0.f;
     for (int j = threadIdx.x; j < a.k; j += blockDim.x) {
-        const float p = mx == -INFINITY ? 0.f : __expf(z[j] - mx);
+        const float p = mx == -INFINITY || rows[j] < 0 ? 0.f : __expf(z[j] - mx);
         z[j] = p;
         lsum += p;
     }
@@ -451,10 +457,10 @@ __global__ __launch_bounds__(256) void mla_generic(MlaArgs a) {
     const float inv = den > 0.f ? 1.f / den : 0.f;
     for (int c = threadIdx.x; c < D; c += blockDim.x) {
         float acc = 0.f;
+#pragma unroll 8
         for (int j = 0; j < a.k; ++j) {
-            const int s = sel[j];
-            if (s < 0) continue;
-            acc = fmaf(z[j], elem((int64_t)pt[s / bs] * bs + s % bs, c), acc);
+            const int64_t row = rows[j];   // padding has p = 0: read row 0 instead
+            acc = fmaf(z[j], elem(row < 0 ? 0 : row, c), acc);
         }
         const size_t off = ((size_t)t * a.n_heads + h) * D + c;
         if (f32) ((float*)a.out)[off] = acc * inv;
@@ -866,6 +872,9 @@ bool mla_fast_path(int kv_dtype, int d_latent, int d_rope, int n_heads, int bloc
     return mla_path(kv_dtype, d_latent, d_rope, n_heads) != MLA_PATH_GENERIC;
 }
 
+#ifndef MLA_MIN_SLICE
+#define MLA_MIN_SLICE 128
+#endif
 // Splits per query row.  Decode: enough workgroups to cover the chip, at
 // least 128 selected tokens per split; the 128-head path also keeps each
 // slice within its row-id buffer.
@@ -877,7 +886,7 @@ int mla_splits(int path, int T, int n_heads, int k, bool prefill) {
     const int units = T * per_row;
     const int target = path == MLA_PATH_H128 ? device_cu_count() : 2 * device_cu_count();
     int s = 1;
-    while (units * s < target && k / (2 * s) >= 128) s <<= 1;
+    while (units * s < target && k / (2 * s) >= MLA_MIN_SLICE) s <<= 1;
     return max(s, min_s);
 }
 
@@ -919,7 +928,7 @@ hipError_t launch_mla(const MlaArgs& a, bool prefill, hipStream_t s) {
         }
         return hipGetLastError();
     }
-    const size_t shm = sizeof(float) * ((size_t)a.d_latent + a.d_rope + a.k);
+    const size_t shm = sizeof(int64_t) * (size_t)a.k + sizeof(float) * ((size_t)a.d_latent + a.d_rope + a.k);
     hipLaunchKernelGGL(mla_generic, dim3(a.g.T * a.n_heads), dim3(256), shm, s, a);
     return hipGetLastError();
 }

@@ -77,6 +77,11 @@ def test_invalid_arguments_rejected_before_device(L):
                                    0x1, 1 << 30, None) == -1
     assert L.dsa_sparse_mla_decode(C.byref(b), C.byref(lc_ok), 0x1, 128, 0x1, 2048, 0.1, 0x1, None,
                                    0x1, 16, None) == -3
+    # the read-bandwidth probe: null or misaligned buffer, size not a multiple of 16, null sink
+    assert L.dsa_read_probe(None, 1024, 0x100, 1 << 20, None) == -1
+    assert L.dsa_read_probe(0x108, 1024, 0x100, 1 << 20, None) == -1
+    assert L.dsa_read_probe(0x100, 1000, 0x100, 1 << 20, None) == -1
+    assert L.dsa_read_probe(0x100, 1024, None, 1 << 20, None) == -1
 
 
 def test_valid_call_without_gpu_reports_device(L):
