@@ -179,6 +179,68 @@ const char *dsa_status_string(int32_t status);
 /* DSA_OK if the current HIP device is gfx950, else DSA_ERR_DEVICE. */
 int dsa_check_device(void);
 
+/*
+ * Two-tier latent cache (HiSparse design, SemiAnalysis GLM-5.3 article,
+ * "HiSparse"): a bounded hot set of latent rows in device memory in front of
+ * the full paged latent cache, which stays in pinned host memory.  All
+ * buffers are caller-owned device memory:
+ *   kv        [capacity][d_latent + d_rope] in the host cache's dtype;
+ *   scales    [capacity] fp32 (DSA_E4M3 caches), NULL otherwise;
+ *   slot_of   [num_requests][max_context_len] int32: slot of token s of
+ *             request r, -1 if not resident;
+ *   owner     [capacity] int64: (r << 32) | s of the slot's token, -1 if free;
+ *   last_use  [capacity] int32: step of the slot's last use, -1 if never;
+ *   clock     [1] int32: the last step (fetches number themselves).
+ * The state is bound to one batch layout (num_requests, max_context_len):
+ * reset it when that layout changes.
+ */
+typedef struct {
+    void *kv;
+    float *scales;
+    int32_t capacity;
+    int32_t *slot_of;
+    int64_t *owner;
+    int32_t *last_use;
+    int32_t *clock;
+} dsa_hot_cache;
+
+/* Empties a hot cache (no token resident, no slot used, clock 0). */
+int dsa_hot_cache_reset(const dsa_batch *batch, dsa_hot_cache *hot, dsa_stream_t stream);
+
+/* Workspace bytes of dsa_hot_cache_fetch for this batch, k and capacity (0
+ * for an invalid request).  Host-only. */
+size_t dsa_hot_cache_workspace_size(const dsa_batch *batch, int32_t k, int32_t capacity);
+
+/*
+ * One step of the two-tier cache for a selection `indices` [T][k] (logical
+ * positions, -1 padding, as written by dsa_topk / dsa_decode_step): makes
+ * every selected token resident in the hot set.
+ *  1. selected tokens already resident are hits: their slot's last use
+ *     becomes this step (clock + 1);
+ *  2. the distinct selected tokens not resident are the misses, in
+ *     (request, token) order;
+ *  3. victims: the slots not used in this step with the greatest age
+ *     (step - last use, saturated at 65535; never used = 65535), ties to the
+ *     lower slot, as many as misses; taken as every victim older than the
+ *     last one's age in slot order, then those of that age in slot order;
+ *  4. miss i moves into victim i: the slot's previous token loses it, the
+ *     row (and scale) is read from the host cache (batch->page_table,
+ *     block_size layout; `host->kv` and `host->scales` in pinned host memory
+ *     that the device can address) and written to the slot.
+ * Afterwards sparse MLA over the hot set is dsa_sparse_mla_decode with the
+ * batch's page_table = slot_of, max_blocks = max_context_len, block_size = 1,
+ * and the latent cache {hot->kv, hot->scales}: the same rows, so the same
+ * output as over the full cache.  counts (device int32 [2] or NULL): misses,
+ * evictions.  capacity must be >= total_q * k (every selected token of the
+ * step fits); DSA_ERR_INVALID_ARG otherwise or for null pointers,
+ * DSA_ERR_UNSUPPORTED for an unsupported cache, DSA_ERR_WORKSPACE for a small
+ * workspace.  Asynchronous on `stream`; calls on one hot cache must be
+ * ordered on one stream.
+ */
+int dsa_hot_cache_fetch(const dsa_batch *batch, const dsa_latent_cache *host, const int32_t *indices, int32_t k,
+                        dsa_hot_cache *hot, int32_t *counts, void *workspace, size_t workspace_bytes,
+                        dsa_stream_t stream);
+
 /* Measurement helper, not a step of the method: the practical HBM read
  * bandwidth that the library's streaming kernels are compared against.
  * dsa_read_probe reads every byte of `buf` (device memory, 16-byte aligned,

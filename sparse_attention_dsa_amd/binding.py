@@ -21,7 +21,13 @@ OP_TOPK, OP_MLA_DECODE, OP_MLA_PREFILL, OP_DECODE_STEP = 1, 2, 3, 4
 
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
            "dsa_decode_step", "dsa_workspace_size", "dsa_status_string", "dsa_check_device",
-           "dsa_read_probe_sink_size", "dsa_read_probe")
+           "dsa_read_probe_sink_size", "dsa_read_probe", "dsa_hot_cache_reset", "dsa_hot_cache_workspace_size",
+           "dsa_hot_cache_fetch")
+
+
+class DsaHotCache(C.Structure):
+    _fields_ = [("kv", C.c_void_p), ("scales", C.c_void_p), ("capacity", C.c_int32), ("slot_of", C.c_void_p),
+                ("owner", C.c_void_p), ("last_use", C.c_void_p), ("clock", C.c_void_p)]
 
 
 class DsaBatch(C.Structure):
@@ -67,8 +73,13 @@ def lib():
         L.dsa_read_probe_sink_size.argtypes = []
         L.dsa_read_probe_sink_size.restype = sz
         L.dsa_read_probe.argtypes = [vp, i64, vp, sz, vp]
+        L.dsa_hot_cache_reset.argtypes = [P(DsaBatch), P(DsaHotCache), vp]
+        L.dsa_hot_cache_workspace_size.argtypes = [P(DsaBatch), i32, i32]
+        L.dsa_hot_cache_workspace_size.restype = sz
+        L.dsa_hot_cache_fetch.argtypes = [P(DsaBatch), P(DsaLatentCache), vp, i32, P(DsaHotCache), vp, vp, sz, vp]
         for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
-                     "dsa_decode_step", "dsa_check_device", "dsa_read_probe"):
+                     "dsa_decode_step", "dsa_check_device", "dsa_read_probe", "dsa_hot_cache_reset",
+                     "dsa_hot_cache_fetch"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -212,6 +223,55 @@ def decode_step(batch: Batch, keys, key_scales, q_idx, w, kv, kv_scales, d_laten
         q_mla.shape[1], k, float(scale), _ptr(out), _ptr(lse), _ptr(indices_out), _ptr(ws), ws.numel(),
         _stream(stream)))
     return out
+
+
+class HotCache:
+    """Device state of a two-tier latent cache: `capacity` slots of latent
+    rows (dtype and width of the host cache) in front of a paged latent cache
+    kept in pinned host memory, for batches of `num_requests` requests of at
+    most `max_context_len` tokens."""
+
+    def __init__(self, capacity, num_requests, max_context_len, row_width, dtype, device="cuda"):
+        self.capacity = int(capacity)
+        self.kv = torch.empty((self.capacity, row_width), dtype=dtype, device=device)
+        self.scales = (torch.empty(self.capacity, dtype=torch.float32, device=device)
+                       if dtype in (torch.uint8, torch.float8_e4m3fn) else None)
+        self.slot_of = torch.empty((num_requests, max_context_len), dtype=torch.int32, device=device)
+        self.owner = torch.empty(self.capacity, dtype=torch.int64, device=device)
+        self.last_use = torch.empty(self.capacity, dtype=torch.int32, device=device)
+        self.clock = torch.zeros(1, dtype=torch.int32, device=device)
+
+    def struct(self):
+        return DsaHotCache(self.kv.data_ptr(), None if self.scales is None else self.scales.data_ptr(),
+                           self.capacity, self.slot_of.data_ptr(), self.owner.data_ptr(),
+                           self.last_use.data_ptr(), self.clock.data_ptr())
+
+    def batch(self, batch: "Batch") -> "Batch":
+        """The geometry of MLA over the hot set: one token per block, the slot
+        table as page table."""
+        return Batch(batch.context_lens, batch.query_start_loc, self.slot_of, 1, batch.max_q_len,
+                     batch.max_context_len)
+
+
+def hot_cache_reset(batch: "Batch", hot: HotCache, stream=None):
+    b, h = batch.struct(), hot.struct()
+    _check("dsa_hot_cache_reset", lib().dsa_hot_cache_reset(C.byref(b), C.byref(h), _stream(stream)))
+
+
+def hot_cache_fetch(batch: "Batch", host_kv, host_scales, d_latent, indices, hot: HotCache, counts=None,
+                    workspace=None, stream=None):
+    """Make every token of `indices` resident in `hot` (host_kv / host_scales:
+    the paged latent cache in pinned host memory)."""
+    k = indices.shape[1]
+    b = batch.struct()
+    need = int(lib().dsa_hot_cache_workspace_size(C.byref(b), k, hot.capacity))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=indices.device)
+    c, h = latent_cache(host_kv, host_scales, d_latent), hot.struct()
+    _check("dsa_hot_cache_fetch", lib().dsa_hot_cache_fetch(C.byref(b), C.byref(c), _ptr(indices), k, C.byref(h),
+                                                            _ptr(counts), _ptr(workspace), workspace.numel(),
+                                                            _stream(stream)))
+    return workspace
 
 
 def read_probe(buf: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:

@@ -1,0 +1,443 @@
+// Two-tier latent cache on gfx950: a bounded hot set of latent rows in HBM in
+// front of the full history, which stays in pinned host memory (the HiSparse
+// design of the SemiAnalysis GLM-5.3 article, "HiSparse": an LRU-like device
+// cache that loads the tokens a top-K selection misses from host DRAM and
+// evicts the least recently used ones).  The output of sparse MLA is unchanged:
+// the selected rows are the same bytes, only their placement differs, and the
+// MLA reads them through a token-granular slot table (page table with one
+// token per block).
+//
+// Policy, per fetch (one step; the step counter lives on the device):
+//  1. every selected token that is resident is a hit: its slot's last use
+//     becomes this step;
+//  2. the distinct selected tokens that are not resident are the misses,
+//     ordered by (request, token);
+//  3. the victims are the M slots (M = number of misses) not used in this
+//     step with the greatest age (step - last use, saturated at 65535; a slot
+//     never used has age 65535), ties to the lower slot; they are taken in
+//     the order: every victim older than the M-th one by slot, then those of
+//     its age by slot;
+//  4. miss i moves into victim i: the victim's previous token loses its slot,
+//     the row (and its e4m3 scale) is copied from host memory by the GPU
+//     (zero-copy reads of pinned memory), and the slot's last use becomes
+//     this step.
+// The capacity is at least T x K (every distinct selected token of a step
+// fits), so there are always enough slots not used in the step.
+#include "dsa_kernels.h"
+#include "topk_dev.h"
+#include "dsa.h"
+
+#include <algorithm>
+
+namespace dsa {
+
+constexpr int HC_THREADS = 256;
+constexpr int HC_WAVES = HC_THREADS / 64;
+constexpr int HC_PER = 4;                         // items per thread in the scans
+constexpr int HC_ITEMS = HC_THREADS * HC_PER;     // items per workgroup in the scans
+constexpr int HC_AGE_BINS = 65536;
+constexpr int HC_MAX_AGE = HC_AGE_BINS - 1;
+
+// scalars in the workspace
+enum { HS_MISSES = 0, HS_OLDER = 1, HS_AGE = 2, HS_NEED = 3, HS_EVICT = 4, HS_STEP = 5, HS_VICTIMS = 6, HS_N = 16 };
+
+struct HotArgs {
+    Geometry g;
+    int k;
+    const int32_t* indices;
+    int32_t* slot_of;        // [B][maxctx]
+    int64_t* owner;          // [capacity]
+    int32_t* last_use;       // [capacity]
+    int32_t* clock;          // [1]
+    int capacity, maxctx, wpr;
+    uint32_t* scal;          // [HS_N]
+    uint32_t* hist;          // [HC_AGE_BINS]
+    uint32_t* bitmap;        // [B][wpr]
+    uint32_t* wsum;          // per-workgroup word sums, then offsets
+    uint32_t* csum;          // per-workgroup (older, equal) counts, then offsets
+    int64_t* miss;           // [T k]
+    int32_t* victims;        // [T k]
+    const uint8_t* host_kv;
+    const float* host_scales;
+    const int32_t* host_pt;  // the batch's page table (host cache layout)
+    uint8_t* hot_kv;
+    float* hot_scales;
+    int row_bytes;
+    int32_t* counts;         // [2] misses, evictions (or null)
+};
+
+__device__ __forceinline__ int slot_age(int32_t lu, int step) {
+    return lu < 0 ? HC_MAX_AGE : max(0, min(step - lu, HC_MAX_AGE));
+}
+
+// Clears the per-step scalars, age histogram and miss bitmap, and fixes this
+// step's number (device clock + 1).
+__global__ __launch_bounds__(HC_THREADS) void hc_clear(HotArgs a, int64_t nwords) {
+    const int64_t i = (int64_t)blockIdx.x * HC_THREADS + threadIdx.x;
+    if (i < HS_N) a.scal[i] = i == HS_STEP ? (uint32_t)(*a.clock + 1) : 0u;
+    if (i < HC_AGE_BINS) a.hist[i] = 0u;
+    if (i < nwords) a.bitmap[i] = 0u;
+}
+
+// Hits stamp their slot; misses set their bit in the request's bitmap.
+__global__ __launch_bounds__(HC_THREADS) void hc_mark(HotArgs a) {
+    const int t = blockIdx.y, j = blockIdx.x * HC_THREADS + threadIdx.x;
+    if (j >= a.k) return;
+    const int s = a.indices[(size_t)t * a.k + j];
+    if (s < 0 || s >= a.maxctx) return;
+    const int r = row_request(a.g, t);
+    const int slot = a.slot_of[(size_t)r * a.maxctx + s];
+    if (slot >= 0 && slot < a.capacity) a.last_use[slot] = (int32_t)a.scal[HS_STEP];
+    else atomicOr(&a.bitmap[(size_t)r * a.wpr + (s >> 5)], 1u << (s & 31));
+}
+
+// Per-workgroup population count of HC_ITEMS consecutive items (bitmap words,
+// or (older, equal) slot flags).
+__global__ __launch_bounds__(HC_THREADS) void hc_count_words(HotArgs a, int64_t nwords) {
+    __shared__ uint32_t wsum[HC_WAVES];
+    const int64_t w0 = (int64_t)blockIdx.x * HC_ITEMS + HC_PER * threadIdx.x;
+    uint32_t c = 0;
+#pragma unroll
+    for (int u = 0; u < HC_PER; ++u)
+        if (w0 + u < nwords) c += __popc(a.bitmap[w0 + u]);
+    uint32_t tot;
+    block_excl_scan<HC_WAVES>(c, wsum, &tot);
+    if (threadIdx.x == 0) a.wsum[blockIdx.x] = tot;
+}
+
+__global__ __launch_bounds__(HC_THREADS) void hc_count_slots(HotArgs a) {
+    __shared__ uint32_t wsum[HC_WAVES];
+    const int step = (int)a.scal[HS_STEP], astar = (int)a.scal[HS_AGE];
+    const int64_t s0 = (int64_t)blockIdx.x * HC_ITEMS + HC_PER * threadIdx.x;
+    uint32_t older = 0, equal = 0;
+#pragma unroll
+    for (int u = 0; u < HC_PER; ++u) {
+        if (s0 + u >= a.capacity) break;
+        const int32_t lu = a.last_use[s0 + u];
+        if (lu == step) continue;
+        const int age = slot_age(lu, step);
+        older += age > astar;
+        equal += age == astar;
+    }
+    uint32_t to, te;
+    block_excl_scan<HC_WAVES>(older, wsum, &to);
+    block_excl_scan<HC_WAVES>(equal, wsum, &te);
+    if (threadIdx.x == 0) {
+        a.csum[2 * blockIdx.x] = to;
+        a.csum[2 * blockIdx.x + 1] = te;
+    }
+}
+
+// One workgroup: exclusive prefix sums, in place, of `n` counts spaced by
+// `stride` (components 0 .. stride-1 scanned independently); the totals go to
+// out[0 .. stride-1].
+__global__ __launch_bounds__(HC_THREADS) void hc_scan(uint32_t* v, int n, int stride, uint32_t* out) {
+    __shared__ uint32_t wsum[HC_WAVES];
+    for (int c = 0; c < stride; ++c) {
+        uint32_t carry = 0;
+        for (int base = 0; base < n; base += HC_THREADS) {
+            const int i = base + threadIdx.x;
+            const uint32_t x = i < n ? v[(size_t)i * stride + c] : 0u;
+            uint32_t tot;
+            const uint32_t ex = block_excl_scan<HC_WAVES>(x, wsum, &tot);
+            if (i < n) v[(size_t)i * stride + c] = carry + ex;
+            carry += tot;
+        }
+        if (threadIdx.x == 0) out[c] = carry;
+    }
+}
+
+// The misses in (request, token) order.
+__global__ __launch_bounds__(HC_THREADS) void hc_write_misses(HotArgs a, int64_t nwords) {
+    __shared__ uint32_t wsum[HC_WAVES];
+    const int64_t w0 = (int64_t)blockIdx.x * HC_ITEMS + HC_PER * threadIdx.x;
+    uint32_t words[HC_PER], c = 0;
+#pragma unroll
+    for (int u = 0; u < HC_PER; ++u) {
+        words[u] = w0 + u < nwords ? a.bitmap[w0 + u] : 0u;
+        c += __popc(words[u]);
+    }
+    uint32_t tot;
+    uint32_t pos = a.wsum[blockIdx.x] + block_excl_scan<HC_WAVES>(c, wsum, &tot);
+#pragma unroll
+    for (int u = 0; u < HC_PER; ++u) {
+        uint32_t m = words[u];
+        const int64_t w = w0 + u;
+        const int r = (int)(w / a.wpr), sb = 32 * (int)(w % a.wpr);
+        while (m) {
+            const int b = __builtin_ctz(m);
+            m &= m - 1;
+            a.miss[pos++] = ((int64_t)r << 32) | (uint32_t)(sb + b);
+        }
+    }
+}
+
+// Age histogram of the slots not used in this step.  A thread takes a run of
+// HC_RUN consecutive slots and adds one count per run of equal ages, so that
+// slots filled together (or never used) do not all hit one counter.
+constexpr int HC_RUN = 32;
+__global__ __launch_bounds__(HC_THREADS) void hc_age_hist(HotArgs a) {
+    const int step = (int)a.scal[HS_STEP];
+    const int64_t s0 = ((int64_t)blockIdx.x * HC_THREADS + threadIdx.x) * HC_RUN;
+    int cur = -1;
+    uint32_t n = 0;
+    for (int u = 0; u < HC_RUN && s0 + u < a.capacity; ++u) {
+        const int32_t lu = a.last_use[s0 + u];
+        if (lu == step) continue;
+        const int age = slot_age(lu, step);
+        if (age != cur) {
+            if (n) atomicAdd(&a.hist[cur], n);
+            cur = age;
+            n = 0;
+        }
+        ++n;
+    }
+    if (n) atomicAdd(&a.hist[cur], n);
+}
+
+// One workgroup: the age a* of the M-th oldest eligible slot, the number of
+// eligible slots older than a*, and how many of age a* are needed.
+__global__ __launch_bounds__(HC_THREADS) void hc_pick(HotArgs a) {
+    __shared__ uint32_t wsum[HC_WAVES];
+    constexpr int PER = HC_AGE_BINS / HC_THREADS;            // 256 bins a thread, oldest first
+    const uint32_t M = a.scal[HS_MISSES];
+    // thread i owns ages [HC_MAX_AGE - PER (i + 1) + 1, HC_MAX_AGE - PER i]
+    uint32_t c = 0;
+    for (int q = 0; q < PER; ++q) c += a.hist[HC_MAX_AGE - PER * threadIdx.x - q];
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan<HC_WAVES>(c, wsum, &tot);
+    if (threadIdx.x == 0) a.scal[HS_VICTIMS] = min(M, tot);
+    if (M == 0) {
+        if (threadIdx.x == 0) { a.scal[HS_AGE] = HC_AGE_BINS; a.scal[HS_OLDER] = 0; a.scal[HS_NEED] = 0; }
+        return;
+    }
+    const uint32_t want = min(M, tot);   // fewer only if the capacity contract is broken
+    if (ex < want && ex + c >= want) {
+        uint32_t cum = ex;
+        for (int q = 0; q < PER; ++q) {
+            const int age = HC_MAX_AGE - PER * threadIdx.x - q;
+            const uint32_t h = a.hist[age];
+            if (cum + h >= want) {
+                a.scal[HS_AGE] = (uint32_t)age;
+                a.scal[HS_OLDER] = cum;
+                a.scal[HS_NEED] = want - cum;
+                break;
+            }
+            cum += h;
+        }
+    }
+}
+
+// The victims: every eligible slot older than a* (slot order), then the first
+// `need` of age a* (slot order).
+__global__ __launch_bounds__(HC_THREADS) void hc_write_victims(HotArgs a) {
+    __shared__ uint32_t wsum[HC_WAVES];
+    const int step = (int)a.scal[HS_STEP], astar = (int)a.scal[HS_AGE];
+    const uint32_t n_older = a.scal[HS_OLDER], need = a.scal[HS_NEED];
+    const int64_t s0 = (int64_t)blockIdx.x * HC_ITEMS + HC_PER * threadIdx.x;
+    uint32_t fo = 0, fe = 0;   // flag bits per item
+#pragma unroll
+    for (int u = 0; u < HC_PER; ++u) {
+        if (s0 + u >= a.capacity) break;
+        const int32_t lu = a.last_use[s0 + u];
+        if (lu == step) continue;
+        const int age = slot_age(lu, step);
+        fo |= (age > astar ? 1u : 0u) << u;
+        fe |= (age == astar ? 1u : 0u) << u;
+    }
+    uint32_t to, te;
+    uint32_t po = a.csum[2 * blockIdx.x] + block_excl_scan<HC_WAVES>(__popc(fo), wsum, &to);
+    uint32_t pe = a.csum[2 * blockIdx.x + 1] + block_excl_scan<HC_WAVES>(__popc(fe), wsum, &te);
+#pragma unroll
+    for (int u = 0; u < HC_PER; ++u) {
+        if ((fo >> u) & 1u) a.victims[po++] = (int32_t)(s0 + u);
+        if ((fe >> u) & 1u) {
+            if (pe < need) a.victims[n_older + pe] = (int32_t)(s0 + u);
+            ++pe;
+        }
+    }
+}
+
+// One wave per miss: evict the victim's token, claim the slot, copy the row
+// (and scale) from host memory.
+__global__ __launch_bounds__(HC_THREADS) void hc_assign(HotArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int i = blockIdx.x * HC_WAVES + (threadIdx.x >> 6);
+    const uint32_t M = a.scal[HS_MISSES], nv = a.scal[HS_VICTIMS];
+    const int step = (int)a.scal[HS_STEP];
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        *a.clock = step;
+        if (a.counts) a.counts[0] = (int32_t)M;
+    }
+    if ((uint32_t)i >= M || (uint32_t)i >= nv) return;
+    const int64_t rs = a.miss[i];
+    const int r = (int)(rs >> 32), s = (int)(rs & 0xFFFFFFFF);
+    const int v = a.victims[i];
+    if (lane == 0) {
+        const int64_t old = a.owner[v];
+        if (old >= 0) {
+            const int orq = (int)(old >> 32), osl = (int)(old & 0xFFFFFFFF);
+            if (orq < a.g.B && osl < a.maxctx) a.slot_of[(size_t)orq * a.maxctx + osl] = -1;
+            atomicAdd(&a.scal[HS_EVICT], 1u);
+        }
+        a.owner[v] = rs;
+        a.last_use[v] = step;
+        a.slot_of[(size_t)r * a.maxctx + s] = v;
+    }
+    const int bs = a.g.block_size;
+    const int64_t row = (int64_t)a.host_pt[(size_t)r * a.g.max_blocks + s / bs] * bs + s % bs;
+    const uint8_t* src = a.host_kv + row * a.row_bytes;
+    uint8_t* dst = a.hot_kv + (int64_t)v * a.row_bytes;
+    for (int o = 16 * lane; o < a.row_bytes; o += 16 * 64) *(u32x4*)(dst + o) = *(const u32x4*)(src + o);
+    if (a.hot_scales && lane == 0) a.hot_scales[v] = a.host_scales[row];
+}
+
+__global__ void hc_finish(HotArgs a) {
+    if (a.counts) a.counts[1] = (int32_t)a.scal[HS_EVICT];
+}
+
+// Resets a hot cache to empty: no token resident, no slot used, clock 0.
+__global__ __launch_bounds__(HC_THREADS) void hc_reset(int32_t* slot_of, int64_t n_map, int64_t* owner,
+                                                       int32_t* last_use, int capacity, int32_t* clock) {
+    const int64_t i = (int64_t)blockIdx.x * HC_THREADS + threadIdx.x;
+    if (i < n_map) slot_of[i] = -1;
+    if (i < capacity) { owner[i] = -1; last_use[i] = -1; }
+    if (i == 0) *clock = 0;
+}
+
+struct HotLayout {
+    size_t scal, hist, bitmap, wsum, csum, miss, victims, end;
+    int64_t nwords;
+    int nwg_words, nwg_slots;
+};
+
+HotLayout hot_layout(const dsa_batch* b, int k, int capacity) {
+    HotLayout l;
+    const int wpr = (b->max_context_len + 31) / 32;
+    l.nwords = (int64_t)b->num_requests * wpr;
+    l.nwg_words = (int)((l.nwords + HC_ITEMS - 1) / HC_ITEMS);
+    l.nwg_slots = (capacity + HC_ITEMS - 1) / HC_ITEMS;
+    auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+    l.scal = 0;
+    l.hist = al(l.scal + sizeof(uint32_t) * HS_N);
+    l.bitmap = l.hist + sizeof(uint32_t) * HC_AGE_BINS;     // contiguous with hist: one clear
+    l.wsum = al(l.bitmap + sizeof(uint32_t) * (size_t)l.nwords);
+    l.csum = al(l.wsum + sizeof(uint32_t) * ((size_t)l.nwg_words + 1));
+    l.miss = al(l.csum + sizeof(uint32_t) * (2 * (size_t)l.nwg_slots + 2));
+    l.victims = al(l.miss + sizeof(int64_t) * (size_t)b->total_q * k);
+    l.end = al(l.victims + sizeof(int32_t) * (size_t)b->total_q * k);
+    return l;
+}
+
+}  // namespace dsa
+
+namespace {
+
+bool hot_ok(const dsa_hot_cache* h) {
+    return h && h->kv && h->slot_of && h->owner && h->last_use && h->clock && h->capacity >= 1;
+}
+
+int latent_row_bytes(const dsa_latent_cache* c) {
+    const int W = c->d_latent + c->d_rope;
+    return c->dtype == DSA_F32 ? 4 * W : c->dtype == DSA_BF16 ? 2 * W : W;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dsa_hot_cache_workspace_size(const dsa_batch* batch, int32_t k, int32_t capacity) {
+    if (!batch || batch->num_requests < 1 || batch->total_q < 1 || batch->max_context_len < 1 || k < 1 ||
+        capacity < 1)
+        return 0;
+    return dsa::hot_layout(batch, k, capacity).end;
+}
+
+int dsa_hot_cache_reset(const dsa_batch* batch, dsa_hot_cache* hot, dsa_stream_t stream) {
+    if (!batch || batch->num_requests < 1 || batch->max_context_len < 1 || !hot_ok(hot)) return DSA_ERR_INVALID_ARG;
+    const int64_t n_map = (int64_t)batch->num_requests * batch->max_context_len;
+    const int64_t n = std::max<int64_t>(n_map, hot->capacity);
+    hipLaunchKernelGGL(dsa::hc_reset, dim3((unsigned)((n + dsa::HC_THREADS - 1) / dsa::HC_THREADS)),
+                       dim3(dsa::HC_THREADS), 0, (hipStream_t)stream, hot->slot_of, n_map, hot->owner, hot->last_use,
+                       hot->capacity, hot->clock);
+    return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
+}
+
+int dsa_hot_cache_fetch(const dsa_batch* b, const dsa_latent_cache* host, const int32_t* indices, int32_t k,
+                        dsa_hot_cache* hot, int32_t* counts, void* workspace, size_t workspace_bytes,
+                        dsa_stream_t stream) {
+    using namespace dsa;
+    if (!b || b->num_requests < 1 || b->total_q < 1 || b->max_q_len < 1 || b->max_context_len < 1 ||
+        !b->context_lens || !b->query_start_loc || !b->page_table || b->block_size < 1 || b->max_blocks < 1 ||
+        (int64_t)b->max_blocks * b->block_size < b->max_context_len || !host || !host->kv || !indices || k < 1 ||
+        !hot_ok(hot))
+        return DSA_ERR_INVALID_ARG;
+    if (!(host->dtype == DSA_F32 || host->dtype == DSA_BF16 || host->dtype == DSA_E4M3) || host->d_latent < 1 ||
+        host->d_rope < 0 || (host->dtype == DSA_E4M3) != (host->scales != nullptr) ||
+        (host->dtype == DSA_E4M3) != (hot->scales != nullptr))
+        return DSA_ERR_UNSUPPORTED;
+    const int row_bytes = latent_row_bytes(host);
+    if (row_bytes % 16) return DSA_ERR_UNSUPPORTED;
+    if ((int64_t)hot->capacity < (int64_t)b->total_q * k) return DSA_ERR_INVALID_ARG;
+    const HotLayout l = hot_layout(b, k, hot->capacity);
+    if (!workspace || workspace_bytes < l.end) return DSA_ERR_WORKSPACE;
+
+    uint8_t* base = (uint8_t*)workspace;
+    HotArgs a;
+    a.g.B = b->num_requests;
+    a.g.T = b->total_q;
+    a.g.max_q_len = b->max_q_len;
+    a.g.max_ctx = b->max_context_len;
+    a.g.q_uniform = (int64_t)b->total_q == (int64_t)b->num_requests * b->max_q_len ? b->max_q_len : 0;
+    a.g.ctx = b->context_lens;
+    a.g.qsl = b->query_start_loc;
+    a.g.page_table = b->page_table;
+    a.g.max_blocks = b->max_blocks;
+    a.g.block_size = b->block_size;
+    a.k = k;
+    a.indices = indices;
+    a.slot_of = hot->slot_of;
+    a.owner = hot->owner;
+    a.last_use = hot->last_use;
+    a.clock = hot->clock;
+    a.capacity = hot->capacity;
+    a.maxctx = b->max_context_len;
+    a.wpr = (b->max_context_len + 31) / 32;
+    a.scal = (uint32_t*)(base + l.scal);
+    a.hist = (uint32_t*)(base + l.hist);
+    a.bitmap = (uint32_t*)(base + l.bitmap);
+    a.wsum = (uint32_t*)(base + l.wsum);
+    a.csum = (uint32_t*)(base + l.csum);
+    a.miss = (int64_t*)(base + l.miss);
+    a.victims = (int32_t*)(base + l.victims);
+    a.host_kv = (const uint8_t*)host->kv;
+    a.host_scales = host->scales;
+    a.host_pt = b->page_table;
+    a.hot_kv = (uint8_t*)hot->kv;
+    a.hot_scales = hot->scales;
+    a.row_bytes = row_bytes;
+    a.counts = counts;
+
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t nclear = std::max<int64_t>(HC_AGE_BINS, l.nwords);
+    hipLaunchKernelGGL(hc_clear, dim3((unsigned)((nclear + HC_THREADS - 1) / HC_THREADS)), dim3(HC_THREADS), 0, s, a,
+                       l.nwords);
+    hipLaunchKernelGGL(hc_mark, dim3((k + HC_THREADS - 1) / HC_THREADS, b->total_q), dim3(HC_THREADS), 0, s, a);
+    hipLaunchKernelGGL(hc_count_words, dim3(l.nwg_words), dim3(HC_THREADS), 0, s, a, l.nwords);
+    hipLaunchKernelGGL(hc_scan, dim3(1), dim3(HC_THREADS), 0, s, a.wsum, l.nwg_words, 1, a.scal + HS_MISSES);
+    hipLaunchKernelGGL(hc_write_misses, dim3(l.nwg_words), dim3(HC_THREADS), 0, s, a, l.nwords);
+    const int64_t runs = ((int64_t)hot->capacity + HC_RUN - 1) / HC_RUN;
+    hipLaunchKernelGGL(hc_age_hist, dim3((unsigned)((runs + HC_THREADS - 1) / HC_THREADS)), dim3(HC_THREADS), 0, s,
+                       a);
+    hipLaunchKernelGGL(hc_pick, dim3(1), dim3(HC_THREADS), 0, s, a);
+    hipLaunchKernelGGL(hc_count_slots, dim3(l.nwg_slots), dim3(HC_THREADS), 0, s, a);
+    hipLaunchKernelGGL(hc_scan, dim3(1), dim3(HC_THREADS), 0, s, a.csum, l.nwg_slots, 2,
+                       a.csum + 2 * (size_t)l.nwg_slots);
+    hipLaunchKernelGGL(hc_write_victims, dim3(l.nwg_slots), dim3(HC_THREADS), 0, s, a);
+    const int64_t tk = (int64_t)b->total_q * k;
+    hipLaunchKernelGGL(hc_assign, dim3((unsigned)((tk + HC_WAVES - 1) / HC_WAVES)), dim3(HC_THREADS), 0, s, a);
+    hipLaunchKernelGGL(hc_finish, dim3(1), dim3(1), 0, s, a);
+    return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
+}
+
+}  // extern "C"
