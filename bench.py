@@ -20,6 +20,9 @@ context: indexer scores, top-K, then sparse MLA prefill on two layers that
 share the selection) call by call, and reports each contraction as MFMA
 utilisation (achieved FLOP/s over the dense fp8 / bf16 peak), since at that
 shape both are compute-bound; the top-K time is reported on its own.
+`hot_cache` times the two-tier latent cache (hot set in HBM, full history in
+pinned host memory) on selections that drift from step to step: the fetch of
+the missing rows and sparse MLA over the hot set.
 `other_configs` gives the step on the other decode configurations, and
 `hbm_ceiling` a plain 2 GiB streaming read as the practical bandwidth ceiling.
 `indexshare` times groups of layers that share one selection (one full step,
@@ -369,6 +372,91 @@ def prefill_leg(iters, warmup, log):
     return res
 
 
+def hot_cache_leg(steps, warmup, log, capacity_mult=4, keep=0.8):
+    """Two-tier latent cache on the batch-64 workload: a hot set of
+    capacity_mult x T x K slots in HBM in front of the full latent pool in
+    pinned host memory.  Each decode step's selection keeps `keep` of every
+    row's previous selection and draws the rest anew among the row's visible
+    tokens (synthetic drift; random N(0,1) data has no temporal locality of
+    its own).  Per step: the fetch (hits, misses, LRU victims, host reads of
+    the missing rows) and sparse MLA over the hot set, timed separately."""
+    import numpy as np
+    import torch
+    import sparse_attention_dsa_amd as dsa
+    from sparse_attention_dsa_amd import binding as B
+    import workloads
+
+    wl = workloads.make_workload(DEFAULT_WORKLOAD)
+    d = workloads.to_device(wl, "cuda")
+    batch = dsa.Batch(d["context_lens"], d["query_start_loc"], d["page_table"], wl.block_size, wl.max_q_len,
+                      wl.max_context_len)
+    T, K = wl.total_q, wl.topk
+    host_kv = d["kv"].cpu().pin_memory()
+    cap = capacity_mult * T * K
+    hot = B.HotCache(cap, wl.batch, wl.max_context_len, d["kv"].shape[-1], d["kv"].dtype)
+    B.hot_cache_reset(batch, hot)
+    rng = np.random.default_rng(7)
+    pos = wl.query_positions()
+    prev = [rng.choice(n, size=K, replace=False) for (_, _, n) in pos]
+    sels = []
+    # warm-up until the hot set is full, so that the timed steps evict
+    warmup += int(np.ceil((capacity_mult - 1) / (1.0 - keep))) + 2
+    for _ in range(warmup + steps):
+        cur = []
+        for t, (_, _, n) in enumerate(pos):
+            kept = rng.choice(prev[t], size=int(keep * K), replace=False)
+            new = rng.choice(n, size=2 * (K - len(kept)), replace=True)
+            new = np.setdiff1d(np.unique(new), kept)[:K - len(kept)]
+            while len(new) < K - len(kept):
+                extra = np.setdiff1d(rng.choice(n, size=K, replace=False), np.concatenate([kept, new]))
+                new = np.concatenate([new, extra])[:K - len(kept)]
+            cur.append(np.concatenate([kept, new]))
+        prev = cur
+        sels.append(torch.from_numpy(np.sort(np.stack(cur)).astype(np.int32)).cuda())
+    counts = torch.zeros(2, dtype=torch.int32, device="cuda")
+    out = torch.empty((T, wl.mla_heads, wl.d_latent), dtype=torch.bfloat16, device="cuda")
+    ws_f = None
+    ws_m = torch.empty(max(dsa.workspace_size(B.OP_MLA_DECODE, batch, K, wl.mla_heads), 256), dtype=torch.uint8,
+                       device="cuda")
+    hb = hot.batch(batch)
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        ws_f = B.hot_cache_fetch(batch, host_kv, None, wl.d_latent, sels[i], hot, counts=counts, workspace=ws_f)
+        dsa.sparse_mla_decode(hb, hot.kv, None, wl.d_latent, d["q_mla"], sels[i], wl.softmax_scale, out=out,
+                              workspace=ws_m)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    miss, evict = [], []
+    for j in range(steps):
+        i = warmup + j
+        ev[j][0].record(stream)
+        B.hot_cache_fetch(batch, host_kv, None, wl.d_latent, sels[i], hot, counts=counts, workspace=ws_f)
+        ev[j][1].record(stream)
+        dsa.sparse_mla_decode(hb, hot.kv, None, wl.d_latent, d["q_mla"], sels[i], wl.softmax_scale, out=out,
+                              workspace=ws_m)
+        ev[j][2].record(stream)
+        miss.append(counts[0].clone())
+        evict.append(counts[1].clone())
+    torch.cuda.synchronize()
+    f_us = 1e3 * sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    m_us = 1e3 * sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    misses = float(torch.stack(miss).float().mean().item())
+    evictions = float(torch.stack(evict).float().mean().item())
+    row = d["kv"].shape[-1] * d["kv"].element_size()
+    res = {"workload": wl.name, "capacity_slots": cap, "hot_bytes": cap * row,
+           "full_pool_bytes": int(d["kv"].numel() * d["kv"].element_size()), "selection_kept_per_step": keep,
+           "fetch_us": round(f_us, 1), "mla_us": round(m_us, 1), "misses_per_step": round(misses, 1),
+           "evictions_per_step": round(evictions, 1),
+           "hit_rate": round(1.0 - misses / (T * K), 4),
+           "host_read_gbs": round(misses * row / (f_us * 1e-6) / 1e9, 1)}
+    log("[bench] two-tier cache: hot set %.2f GB of %.2f GB; fetch %.0f us (%.0f misses, %.0f evictions a step, %.1f "
+        "GB/s from host), MLA %.1f us" % (res["hot_bytes"] / 1e9, res["full_pool_bytes"] / 1e9, f_us, misses,
+                                          evictions, res["host_read_gbs"], m_us))
+    del d, host_kv, hot, sels, out, ws_f, ws_m
+    torch.cuda.empty_cache()
+    return res
+
+
 OTHER_WORKLOADS = ("tiny_fp32_l4096", "single_b1_l32768", "mtp_b8_l202752")
 
 
@@ -435,6 +523,8 @@ def main(argv=None):
                     help="skip the chunked-prefill measurement (4096 queries on a 131072-token context)")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the other decode configurations and the streaming-read ceiling")
+    ap.add_argument("--no-hot-cache", action="store_true",
+                    help="skip the two-tier latent cache measurement")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -516,6 +606,11 @@ def main(argv=None):
         others = other_configs(max(10, min(args.steps, 50)), 5, log)
         ceiling = read_ceiling(log)
 
+    # Two-tier latent cache: fetch + MLA over the hot set on drifting selections.
+    hot = None
+    if not args.no_hot_cache and args.workload == DEFAULT_WORKLOAD:
+        hot = hot_cache_leg(max(5, min(args.steps, 20)), 10, log)
+
     # CPU baseline: the oracle on a bounded sample of query rows.
     cpu = None
     if args.cpu_rows > 0:
@@ -562,6 +657,7 @@ def main(argv=None):
         "all_128k": at128,
         "prefill": prefill,
         "other_configs": others,
+        "hot_cache": hot,
         "hbm_ceiling": ceiling,
         "cpu_baseline": cpu,
     }

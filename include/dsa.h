@@ -233,8 +233,8 @@ size_t dsa_hot_cache_workspace_size(const dsa_batch *batch, int32_t k, int32_t c
  * output as over the full cache.  counts (device int32 [2] or NULL): misses,
  * evictions.  capacity must be >= total_q * k (every selected token of the
  * step fits); DSA_ERR_INVALID_ARG otherwise or for null pointers,
- * DSA_ERR_UNSUPPORTED for an unsupported cache, DSA_ERR_WORKSPACE for a small
- * workspace.  Asynchronous on `stream`; calls on one hot cache must be
+ * DSA_ERR_UNSUPPORTED for a cache whose rows are not a multiple of 16 bytes
+ * or exceed 2 KB, DSA_ERR_WORKSPACE for a small workspace.  Asynchronous on `stream`; calls on one hot cache must be
  * ordered on one stream.
  */
 int dsa_hot_cache_fetch(const dsa_batch *batch, const dsa_latent_cache *host, const int32_t *indices, int32_t k,

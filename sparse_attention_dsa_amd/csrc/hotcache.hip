@@ -172,19 +172,31 @@ __global__ __launch_bounds__(HC_THREADS) void hc_write_misses(HotArgs a, int64_t
     }
 }
 
-// Age histogram of the slots not used in this step.  A thread takes a run of
-// HC_RUN consecutive slots and adds one count per run of equal ages, so that
-// slots filled together (or never used) do not all hit one counter.
+// Age histogram of the slots not used in this step.  Ages below HC_LDS_AGES
+// (the recent steps, where almost every slot is) and the saturated age (every
+// never-used slot) are counted in LDS and flushed once per workgroup; the
+// other old ones go to the global histogram, one count per run of equal ages
+// among a thread's HC_RUN slots.
 constexpr int HC_RUN = 32;
+constexpr int HC_LDS_AGES = 4096;
 __global__ __launch_bounds__(HC_THREADS) void hc_age_hist(HotArgs a) {
+    __shared__ uint32_t h[HC_LDS_AGES + 1];                   // last bin: HC_MAX_AGE
+    for (int i = threadIdx.x; i <= HC_LDS_AGES; i += HC_THREADS) h[i] = 0u;
+    __syncthreads();
     const int step = (int)a.scal[HS_STEP];
-    const int64_t s0 = ((int64_t)blockIdx.x * HC_THREADS + threadIdx.x) * HC_RUN;
+    // the workgroup covers HC_THREADS * HC_RUN consecutive slots; lane-
+    // consecutive loads (coalesced), each thread HC_RUN slots HC_THREADS apart
+    const int64_t s0 = (int64_t)blockIdx.x * HC_THREADS * HC_RUN + threadIdx.x;
     int cur = -1;
     uint32_t n = 0;
-    for (int u = 0; u < HC_RUN && s0 + u < a.capacity; ++u) {
-        const int32_t lu = a.last_use[s0 + u];
+    for (int u = 0; u < HC_RUN && s0 + (int64_t)u * HC_THREADS < a.capacity; ++u) {
+        const int32_t lu = a.last_use[s0 + (int64_t)u * HC_THREADS];
         if (lu == step) continue;
         const int age = slot_age(lu, step);
+        if (age < HC_LDS_AGES || age == HC_MAX_AGE) {
+            atomicAdd(&h[age < HC_LDS_AGES ? age : HC_LDS_AGES], 1u);
+            continue;
+        }
         if (age != cur) {
             if (n) atomicAdd(&a.hist[cur], n);
             cur = age;
@@ -193,6 +205,9 @@ __global__ __launch_bounds__(HC_THREADS) void hc_age_hist(HotArgs a) {
         ++n;
     }
     if (n) atomicAdd(&a.hist[cur], n);
+    __syncthreads();
+    for (int i = threadIdx.x; i <= HC_LDS_AGES; i += HC_THREADS)
+        if (h[i]) atomicAdd(&a.hist[i < HC_LDS_AGES ? i : HC_MAX_AGE], h[i]);
 }
 
 // One workgroup: the age a* of the M-th oldest eligible slot, the number of
@@ -258,6 +273,18 @@ __global__ __launch_bounds__(HC_THREADS) void hc_write_victims(HotArgs a) {
     }
 }
 
+// One row of up to 2 KB by one wave, every load issued before the first store
+// (host reads are long round trips).
+__device__ __forceinline__ void copy_row(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int bytes,
+                                         int lane) {
+    const int o0 = 16 * lane, o1 = 16 * (lane + 64);
+    u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
+    if (o0 < bytes) v0 = *(const u32x4*)(src + o0);
+    if (o1 < bytes) v1 = *(const u32x4*)(src + o1);
+    if (o0 < bytes) *(u32x4*)(dst + o0) = v0;
+    if (o1 < bytes) *(u32x4*)(dst + o1) = v1;
+}
+
 // One wave per miss: evict the victim's token, claim the slot, copy the row
 // (and scale) from host memory.
 __global__ __launch_bounds__(HC_THREADS) void hc_assign(HotArgs a) {
@@ -286,9 +313,7 @@ __global__ __launch_bounds__(HC_THREADS) void hc_assign(HotArgs a) {
     }
     const int bs = a.g.block_size;
     const int64_t row = (int64_t)a.host_pt[(size_t)r * a.g.max_blocks + s / bs] * bs + s % bs;
-    const uint8_t* src = a.host_kv + row * a.row_bytes;
-    uint8_t* dst = a.hot_kv + (int64_t)v * a.row_bytes;
-    for (int o = 16 * lane; o < a.row_bytes; o += 16 * 64) *(u32x4*)(dst + o) = *(const u32x4*)(src + o);
+    copy_row(a.host_kv + row * a.row_bytes, a.hot_kv + (int64_t)v * a.row_bytes, a.row_bytes, lane);
     if (a.hot_scales && lane == 0) a.hot_scales[v] = a.host_scales[row];
 }
 
@@ -377,7 +402,7 @@ int dsa_hot_cache_fetch(const dsa_batch* b, const dsa_latent_cache* host, const 
         (host->dtype == DSA_E4M3) != (hot->scales != nullptr))
         return DSA_ERR_UNSUPPORTED;
     const int row_bytes = latent_row_bytes(host);
-    if (row_bytes % 16) return DSA_ERR_UNSUPPORTED;
+    if (row_bytes % 16 || row_bytes > 2048) return DSA_ERR_UNSUPPORTED;
     if ((int64_t)hot->capacity < (int64_t)b->total_q * k) return DSA_ERR_INVALID_ARG;
     const HotLayout l = hot_layout(b, k, hot->capacity);
     if (!workspace || workspace_bytes < l.end) return DSA_ERR_WORKSPACE;
