@@ -180,8 +180,10 @@ const char *dsa_status_string(int32_t status);
 int dsa_check_device(void);
 
 /*
- * Two-tier latent cache (HiSparse design, SemiAnalysis GLM-5.3 article,
- * "HiSparse"): a bounded hot set of latent rows in device memory in front of
+ * Two-tier latent cache (HiSparse design: SemiAnalysis, "Sparse Savings,
+ * Persistent Demand: inside GLM-5.3", section "How Sparse Attention Affects
+ * DRAM/NAND Memory"; remio.ai, section "HiSparse Move o Histórico Completo
+ * para Fora da GPU"): a bounded hot set of latent rows in device memory in front of
  * the full paged latent cache, which stays in pinned host memory.  All
  * buffers are caller-owned device memory:
  *   kv        [capacity][d_latent + d_rope] in the host cache's dtype;

@@ -3,7 +3,9 @@
 TEST INFRASTRUCTURE ONLY (like the rest of ``oracle/``): the product library
 never imports it, and it imports nothing from the product library.
 
-Source: SemiAnalysis GLM-5.3 article, section "HiSparse" -- a bounded device
+Sources: SemiAnalysis, "Sparse Savings, Persistent Demand: inside GLM-5.3",
+section "How Sparse Attention Affects DRAM/NAND Memory", and remio.ai, section
+"HiSparse Move o Histórico Completo para Fora da GPU" -- a bounded device
 cache in front of the full history in host memory that behaves like an LRU
 cache: tokens a top-K selection misses are loaded from host memory, the least
 recently used entries are evicted.  The pages fix no tie rule, age unit or

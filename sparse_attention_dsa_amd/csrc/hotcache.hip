@@ -1,6 +1,8 @@
 // Two-tier latent cache on gfx950: a bounded hot set of latent rows in HBM in
 // front of the full history, which stays in pinned host memory (the HiSparse
-// design of the SemiAnalysis GLM-5.3 article, "HiSparse": an LRU-like device
+// design: SemiAnalysis, "Sparse Savings, Persistent Demand: inside GLM-5.3",
+// section "How Sparse Attention Affects DRAM/NAND Memory"; remio.ai, section
+// "HiSparse Move o Histórico Completo para Fora da GPU" -- an LRU-like device
 // cache that loads the tokens a top-K selection misses from host DRAM and
 // evicts the least recently used ones).  The output of sparse MLA is unchanged:
 // the selected rows are the same bytes, only their placement differs, and the
