@@ -28,6 +28,8 @@
  *     cache of row width W is laid out [num_blocks][block_size][W].
  *   - Token indices are LOGICAL positions within the request (so a second
  *     layer with its own latent pool can reuse them: "IndexShare").
+ *   - Device tensors start 16-byte aligned (as device allocators return
+ *     them); the kernels use 16-byte vector loads and stores.
  *   - Workspaces: pass at least dsa_workspace_size(op, ...) bytes, 256-byte
  *     aligned.  Contents on entry are ignored; on return they are garbage.
  *     Calls that share a workspace must be ordered on one stream.

@@ -356,36 +356,46 @@ void mla_bf16_mfma(MlaArgs a, int slice) {
 }
 
 // Merge split partials: out = sum_s e^{lse_s - L} o_s with L = log-sum-exp.
-__global__ __launch_bounds__(128) void mla_combine(MlaArgs a) {
-    const size_t th = blockIdx.x;             // (t, h)
-    const int c4 = threadIdx.x;               // 4 columns each
+__global__ __launch_bounds__(256) void mla_combine(MlaArgs a) {
+    const int lane = threadIdx.x & 63;
+    const size_t th = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (t, h), one wave each
+    if (th >= (size_t)a.g.T * a.n_heads) return;
     const int S = a.splits;
     const float* pl = a.part_lse + 2 * th * S;   // per slice: lse, 2^-k
-    const uint16_t* po = a.part_o + th * S * M_DL + 4 * c4;
+    const uint16_t* po = a.part_o + th * S * M_DL + 8 * lane;
     float mx = -INFINITY;
     for (int s = 0; s < S; ++s) mx = fmaxf(mx, pl[2 * s]);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float den = 0.f;
     if (mx != -INFINITY) {
-        for (int s = 0; s < S; ++s) {
-            const float wgt = __expf(pl[2 * s] - mx);
-            den += wgt;
-            const float ws = wgt * pl[2 * s + 1];
-            const u32x2 h = *(const u32x2*)(po + (size_t)s * M_DL);
+        for (int s0 = 0; s0 < S; s0 += 4) {
+            u32x4 h[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint16_t b = (uint16_t)(h[i >> 1] >> (16 * (i & 1)));
-                acc[i] += ws * (float)__builtin_bit_cast(_Float16, b);
+            for (int u = 0; u < 4; ++u)
+                if (s0 + u < S) h[u] = *(const u32x4*)(po + (size_t)(s0 + u) * M_DL);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (s0 + u >= S) break;
+                const float wgt = __expf(pl[2 * (s0 + u)] - mx);
+                den += wgt;
+                const float ws = wgt * pl[2 * (s0 + u) + 1];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint16_t b = (uint16_t)(h[u][i >> 1] >> (16 * (i & 1)));
+                    acc[i] += ws * (float)__builtin_bit_cast(_Float16, b);
+                }
             }
         }
-        acc *= 1.f / den;
+        const float inv = 1.f / den;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] *= inv;
     }
-    uint16_t* op = (uint16_t*)a.out + th * M_DL + 4 * c4;
-    u32x2 w;
-    w[0] = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
-    w[1] = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
-    *(u32x2*)op = w;
-    if (a.lse && c4 == 0) a.lse[th] = mx == -INFINITY ? -INFINITY : mx + logf(den);
+    uint16_t* op = (uint16_t*)a.out + th * M_DL + 8 * lane;
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = f32_to_bf16(acc[2 * i]) | (f32_to_bf16(acc[2 * i + 1]) << 16);
+    *(u32x4*)op = w;
+    if (a.lse && lane == 0) a.lse[th] = mx == -INFINITY ? -INFINITY : mx + logf(den);
 }
 
 // Generic path: any dims and head counts, fp32 / bf16 / e4m3 latent.  One
@@ -902,7 +912,7 @@ hipError_t launch_mla(const MlaArgs& a, bool prefill, hipStream_t s) {
             hipLaunchKernelGGL(mla_h128<true>, grid, dim3(M_THREADS), 0, s, a, slice);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
-            hipLaunchKernelGGL(mla_combine, dim3(a.g.T * a.n_heads), dim3(M_DL / 4), 0, s, a);
+            hipLaunchKernelGGL(mla_combine, dim3((a.g.T * a.n_heads + 3) / 4), dim3(256), 0, s, a);
         } else {
             hipLaunchKernelGGL(mla_h128<false>, grid, dim3(M_THREADS), 0, s, a, slice);
         }
@@ -921,7 +931,7 @@ hipError_t launch_mla(const MlaArgs& a, bool prefill, hipStream_t s) {
             else hipLaunchKernelGGL((mla_bf16_mfma<false, true>), grid, dim3(M_THREADS), 0, s, a, slice);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
-            hipLaunchKernelGGL(mla_combine, dim3(a.g.T * a.n_heads), dim3(M_DL / 4), 0, s, a);
+            hipLaunchKernelGGL(mla_combine, dim3((a.g.T * a.n_heads + 3) / 4), dim3(256), 0, s, a);
         } else {
             if (fp8) hipLaunchKernelGGL((mla_bf16_mfma<true, false>), grid, dim3(M_THREADS), 0, s, a, slice);
             else hipLaunchKernelGGL((mla_bf16_mfma<false, false>), grid, dim3(M_THREADS), 0, s, a, slice);
