@@ -382,6 +382,7 @@ size_t dsa_hot_cache_workspace_size(const dsa_batch* batch, int32_t k, int32_t c
 
 int dsa_hot_cache_reset(const dsa_batch* batch, dsa_hot_cache* hot, dsa_stream_t stream) {
     if (!batch || batch->num_requests < 1 || batch->max_context_len < 1 || !hot_ok(hot)) return DSA_ERR_INVALID_ARG;
+    if (const int st = dsa_check_device(); st != DSA_OK) return st;
     const int64_t n_map = (int64_t)batch->num_requests * batch->max_context_len;
     const int64_t n = std::max<int64_t>(n_map, hot->capacity);
     hipLaunchKernelGGL(dsa::hc_reset, dim3((unsigned)((n + dsa::HC_THREADS - 1) / dsa::HC_THREADS)),
@@ -408,6 +409,7 @@ int dsa_hot_cache_fetch(const dsa_batch* b, const dsa_latent_cache* host, const 
     if ((int64_t)hot->capacity < (int64_t)b->total_q * k) return DSA_ERR_INVALID_ARG;
     const HotLayout l = hot_layout(b, k, hot->capacity);
     if (!workspace || workspace_bytes < l.end) return DSA_ERR_WORKSPACE;
+    if (const int st = dsa_check_device(); st != DSA_OK) return st;
 
     uint8_t* base = (uint8_t*)workspace;
     HotArgs a;

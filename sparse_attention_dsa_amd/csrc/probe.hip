@@ -53,6 +53,7 @@ size_t dsa_read_probe_sink_size(void) { return sizeof(uint32_t) * (size_t)dsa::p
 
 int dsa_read_probe(const void* buf, int64_t nbytes, void* sink, size_t sink_bytes, dsa_stream_t stream) {
     if (!buf || nbytes < 16 || (nbytes & 15) || ((uintptr_t)buf & 15) || !sink) return DSA_ERR_INVALID_ARG;
+    if (const int st = dsa_check_device(); st != DSA_OK) return st;
     const int grid = dsa::probe_grid();
     if (sink_bytes < sizeof(uint32_t) * (size_t)grid) return DSA_ERR_WORKSPACE;
     hipLaunchKernelGGL(dsa::stream_read, dim3(grid), dim3(dsa::PR_THREADS), 0, (hipStream_t)stream, (const uint8_t*)buf, nbytes,

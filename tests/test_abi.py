@@ -84,6 +84,30 @@ def test_invalid_arguments_rejected_before_device(L):
     assert L.dsa_read_probe(0x100, 1024, None, 1 << 20, None) == -1
 
 
+def test_hot_cache_arguments_rejected_before_device(L):
+    b = _batch(T=2)
+    assert L.dsa_hot_cache_workspace_size(None, 16, 64) == 0
+    assert L.dsa_hot_cache_workspace_size(C.byref(b), 0, 64) == 0
+    assert L.dsa_hot_cache_workspace_size(C.byref(b), 16, 0) == 0
+    small = L.dsa_hot_cache_workspace_size(C.byref(b), 16, 64)
+    assert 0 < small < L.dsa_hot_cache_workspace_size(C.byref(b), 16, 1 << 20)   # grows with the hot set
+    hot = B.DsaHotCache(0x100, None, 64, 0x200, 0x300, 0x400, 0x500)
+    bf = B.DsaLatentCache(0x10, None, B.BF16, 512, 64)
+    ws = 1 << 30
+    assert L.dsa_hot_cache_reset(C.byref(b), None, None) == -1
+    no_clock = B.DsaHotCache(0x100, None, 64, 0x200, 0x300, 0x400, None)
+    assert L.dsa_hot_cache_reset(C.byref(b), C.byref(no_clock), None) == -1
+    assert L.dsa_hot_cache_fetch(C.byref(b), C.byref(bf), None, 16, C.byref(hot), None, 0x1, ws, None) == -1
+    assert L.dsa_hot_cache_fetch(C.byref(b), C.byref(bf), 0x1, 33, C.byref(hot), None, 0x1, ws, None) == -1  # 2 x 33 > 64 slots
+    odd = B.DsaLatentCache(0x10, None, B.BF16, 7, 0)                           # 14-byte rows
+    assert L.dsa_hot_cache_fetch(C.byref(b), C.byref(odd), 0x1, 16, C.byref(hot), None, 0x1, ws, None) == -2
+    wide = B.DsaLatentCache(0x10, None, B.F32, 512, 64)                        # 2304-byte rows
+    assert L.dsa_hot_cache_fetch(C.byref(b), C.byref(wide), 0x1, 16, C.byref(hot), None, 0x1, ws, None) == -2
+    fp8 = B.DsaLatentCache(0x10, 0x20, B.E4M3, 512, 64)                        # hot set without scales
+    assert L.dsa_hot_cache_fetch(C.byref(b), C.byref(fp8), 0x1, 16, C.byref(hot), None, 0x1, ws, None) == -2
+    assert L.dsa_hot_cache_fetch(C.byref(b), C.byref(bf), 0x1, 16, C.byref(hot), None, 0x1, small - 1, None) == -3
+
+
 def test_valid_call_without_gpu_reports_device(L):
     import torch
     if torch.cuda.is_available():
@@ -92,3 +116,8 @@ def test_valid_call_without_gpu_reports_device(L):
     ic = B.DsaIndexCache(0x10, None, B.E4M3, 128)
     assert L.dsa_indexer_scores(C.byref(b), C.byref(ic), 0x1, 0x1, 64, 0x1, 1024, None) == -4
     assert L.dsa_check_device() == -4
+    hot = B.DsaHotCache(0x100, None, 64, 0x200, 0x300, 0x400, 0x500)
+    bf = B.DsaLatentCache(0x10, None, B.BF16, 512, 64)
+    assert L.dsa_hot_cache_reset(C.byref(b), C.byref(hot), None) == -4
+    assert L.dsa_hot_cache_fetch(C.byref(b), C.byref(bf), 0x1, 16, C.byref(hot), None, 0x1, 1 << 30, None) == -4
+    assert L.dsa_read_probe(0x100, 1024, 0x100, 1 << 20, None) == -4
