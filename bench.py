@@ -8,12 +8,18 @@ batch-64 decode with per-request contexts drawn uniformly from [8K, 128K]
 (64-token pages, shuffled page tables, fp8 index keys, bf16 latent cache).
 
 Prints one JSON line.  `value` is decode tokens/s per layer (query rows per
-second).  `roofline` covers the dominant kernel -- the lightning indexer --
-with its algorithmic bytes per launch divided by its average launch time,
-timed live here with HIP events on the stream it runs on; its `traffic` is
-the HBM bytes per launch that rocprofv3's FETCH_SIZE and WRITE_SIZE counters
+second).  `roofline` covers the dominant kernel of the step -- the lightning
+indexer as the step runs it (emitting top-K candidates instead of score
+rows) -- with its algorithmic bytes per launch (the keys, scales, page-table
+entries, queries and weights it must read) divided by its average launch
+time, timed live here by events that dsa_decode_step_timed records on the
+library's stream right before and after that launch; its `traffic` is the
+HBM bytes per launch that rocprofv3's FETCH_SIZE and WRITE_SIZE counters
 recorded (scaled by a copy-kernel calibration), read from the committed
 counter summary and reported only while the indexer source is unchanged.
+`step_phases_us` splits the step the same way (bound sampling, indexer,
+selection, attention), and `indexer_scores_kernel` gives the standalone,
+score-writing indexer (dsa_indexer_scores) timed launch by launch.
 `step_hbm` gives the algorithmic-bytes ratio for the whole step.
 `prefill` times the chunked prefill (4096 new query tokens on a 131072-token
 context: indexer scores, top-K, then sparse MLA prefill on two layers that
@@ -86,6 +92,13 @@ def indexer_launch_bytes(wl):
     return total
 
 
+def indexer_read_bytes(wl):
+    """Bytes the candidate-emitting indexer must read: indexer_launch_bytes
+    without the score rows (its candidate appends, about 8 bytes for each of a
+    few thousand tokens per row, are left out)."""
+    return indexer_launch_bytes(wl) - sum(4 * n for (_, _, n) in wl.query_positions())
+
+
 def step_bytes(wl, indices):
     """Algorithmic bytes of one whole step (formula in the module docstring)."""
     import numpy as np
@@ -144,11 +157,12 @@ def indexer_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, prefix=""):
     """HBM bytes per indexer launch from the committed rocprofv3 counter
     summary (FETCH_SIZE + WRITE_SIZE, each scaled by its copy-kernel
     calibration), or None when the summary is missing, covers another
-    workload, or was taken on a different indexer source."""
+    workload, or was taken on a different indexer source.  prefix "" is the
+    score-writing instance, "emit-" the candidate-emitting one."""
     try:
         with open(TRAFFIC_SUMMARY) as f:
             fields = dict(l.strip().strip("`").split(": ", 1) for l in f if ": " in l and l.startswith("`"))
@@ -157,7 +171,7 @@ def measured_traffic(workload):
     if fields.get("workload") != workload or fields.get("source-sha256") != indexer_source_hash():
         return None
     try:
-        return int(fields["fetch-bytes-per-launch"]) + int(fields["write-bytes-per-launch"])
+        return int(fields[prefix + "fetch-bytes-per-launch"]) + int(fields[prefix + "write-bytes-per-launch"])
     except (KeyError, ValueError):
         return None
 
@@ -233,6 +247,27 @@ class Rig:
         self.step(i)
         for l in range(1, layers):
             self._ok("dsa_sparse_mla_decode", self.L.dsa_sparse_mla_decode(*self.mla_args[(i + l) % n]))
+
+    def step_phases(self, iters, warmup):
+        """Average µs of the step's phases (bound sampling, indexer, selection,
+        attention) and of the whole step, from the events that
+        dsa_decode_step_timed records on the library's stream."""
+        import ctypes as C
+        torch, B = self.torch, self.B
+        n = len(self.copies)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(B.STEP_EVENTS)] for _ in range(iters)]
+        handles = [B.event_handles(e, self.stream) for e in evs]
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        for i in range(iters):
+            self._ok("dsa_decode_step_timed",
+                     self.L.dsa_decode_step_timed(*self.step_args[i % n], handles[i], B.STEP_EVENTS))
+        torch.cuda.synchronize()
+        names = ("sampling", "indexer", "selection", "attention")
+        out = {k: 1e3 * sum(e[j].elapsed_time(e[j + 1]) for e in evs) / iters for j, k in enumerate(names)}
+        out["step"] = 1e3 * sum(e[0].elapsed_time(e[-1]) for e in evs) / iters
+        return out
 
     def indexer(self, i):
         self._ok("dsa_indexer_scores", self.L.dsa_indexer_scores(*self.idx_args[i % len(self.copies)]))
@@ -553,12 +588,19 @@ def main(argv=None):
     log("[bench] step: %.1f us" % (ms_per_step * 1e3))
     indices = rig.selection()
 
-    # Dominant kernel: the lightning indexer, timed launch by launch.
+    # Dominant kernel: the lightning indexer as the step runs it, timed by the
+    # events the library records around its launch.
     n_idx = max(args.steps, 20)
+    phases = rig.step_phases(n_idx, args.warmup)
+    emit_us, emit_bytes = phases["indexer"], indexer_read_bytes(wl)
+    emit_gbs = emit_bytes / (emit_us * 1e-6) / 1e9
+    log("[bench] step phases (us): " + ", ".join("%s %.1f" % kv for kv in phases.items()))
+    log("[bench] indexer in the step: %.1f us, %.1f MB -> %.0f GB/s" % (emit_us, emit_bytes / 1e6, emit_gbs))
+    # The standalone, score-writing indexer, timed launch by launch.
     idx_us = rig.time_launches(rig.indexer, n_idx, args.warmup)
     idx_bytes = indexer_launch_bytes(wl)
     idx_gbs = idx_bytes / (idx_us * 1e-6) / 1e9
-    log("[bench] indexer kernel: %.1f us, %.1f MB -> %.0f GB/s" % (idx_us, idx_bytes / 1e6, idx_gbs))
+    log("[bench] standalone indexer: %.1f us, %.1f MB -> %.0f GB/s" % (idx_us, idx_bytes / 1e6, idx_gbs))
 
     sb = step_bytes(wl, indices)
     f_idx, f_mla = step_flops(wl, indices)
@@ -577,6 +619,7 @@ def main(argv=None):
             (nl, ms_group * 1e3, share["tokens_per_s_per_layer"]))
 
     traffic = measured_traffic(wl.name)
+    emit_traffic = measured_traffic(wl.name, "emit-")
     rig.free()
     del rig
 
@@ -646,9 +689,15 @@ def main(argv=None):
                    "indexer": "%dx%d e4m3" % (wl.idx_heads, wl.idx_dim), "mla_heads": wl.mla_heads,
                    "latent": "%d+%d %s" % (wl.d_latent, wl.d_rope, wl.kv_dtype), "block_size": wl.block_size,
                    "input_copies": args.copies},
-        "roofline": {"bound": "hbm", "kernel": "indexer_fp8_persistent", "achieved": round(idx_gbs, 1),
-                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(idx_gbs / PEAK_HBM_GBS, 4),
-                     "traffic": traffic, "bytes_per_launch": idx_bytes, "us_per_launch": round(idx_us, 2)},
+        "roofline": {"bound": "hbm", "kernel": "indexer_fp8_persistent<1, 4, true> (in dsa_decode_step)",
+                     "achieved": round(emit_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(emit_gbs / PEAK_HBM_GBS, 4), "traffic": emit_traffic,
+                     "bytes_per_launch": emit_bytes, "us_per_launch": round(emit_us, 2)},
+        "step_phases_us": {k: round(v, 2) for k, v in phases.items()},
+        "indexer_scores_kernel": {"kernel": "indexer_fp8_persistent<1, 4, false> (dsa_indexer_scores)",
+                                  "achieved": round(idx_gbs, 1), "frac": round(idx_gbs / PEAK_HBM_GBS, 4),
+                                  "traffic": traffic, "bytes_per_launch": idx_bytes,
+                                  "us_per_launch": round(idx_us, 2)},
         "step_hbm": {"bytes": sb, "achieved": round(step_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(step_gbs / PEAK_HBM_GBS, 4)},
         "step_tflops": {"indexer_fp8": round(f_idx / (ms_per_step * 1e-3) / 1e12, 2),

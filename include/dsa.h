@@ -168,6 +168,26 @@ int dsa_decode_step(const dsa_batch *batch, const dsa_index_cache *index_cache,
                     int32_t k, float softmax_scale, void *out, float *lse, int32_t *indices_out,
                     void *workspace, size_t workspace_bytes, dsa_stream_t stream);
 
+/*
+ * Measurement variant of dsa_decode_step: the same launches and results,
+ * plus DSA_STEP_EVENTS events recorded on `stream` at the step's phase
+ * boundaries, so that a caller can time each phase on the stream it runs on:
+ *   events[0] before the first launch, events[1] after the top-K bound
+ *   sampling (at once when the step takes no sample), events[2] after the
+ *   lightning indexer, events[3] after the top-K selection, events[4] after
+ *   sparse MLA (and its split combine).
+ *   events: DSA_STEP_EVENTS caller-created hipEvent_t handles (as void*);
+ *           recording allocates nothing.  n_events >= DSA_STEP_EVENTS, else
+ *           DSA_ERR_INVALID_ARG (also for a NULL handle).
+ */
+#define DSA_STEP_EVENTS 5
+int dsa_decode_step_timed(const dsa_batch *batch, const dsa_index_cache *index_cache,
+                          const void *q_idx, const float *w, int32_t n_heads_idx,
+                          const dsa_latent_cache *latent_cache, const void *q_mla, int32_t n_heads,
+                          int32_t k, float softmax_scale, void *out, float *lse, int32_t *indices_out,
+                          void *workspace, size_t workspace_bytes, dsa_stream_t stream,
+                          void *const *events, int32_t n_events);
+
 /* Workspace bytes for `op` (enum dsa_op) with this batch geometry; 0 for an
  * invalid request and for calls that need none (top-K on rows of at most
  * 12288 tokens, prefill MLA without splits).  Host-only, never touches the

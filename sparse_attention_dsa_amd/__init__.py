@@ -4,5 +4,5 @@ Lightning-indexer scores, top-K selection and sparse MQA-mode MLA over a
 paged latent / indexer-key cache, as hand-written HIP kernels behind the C ABI
 in ``include/dsa.h``.  ``binding`` is the thin Python front end.
 """
-from .binding import (Batch, DsaError, decode_step, indexer_scores, lib, sparse_mla_decode,  # noqa: F401
-                      sparse_mla_prefill, topk, workspace_size)
+from .binding import (Batch, DsaError, decode_step, decode_step_timed, indexer_scores, lib,  # noqa: F401
+                      sparse_mla_decode, sparse_mla_prefill, topk, workspace_size)

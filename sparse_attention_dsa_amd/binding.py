@@ -22,7 +22,8 @@ OP_TOPK, OP_MLA_DECODE, OP_MLA_PREFILL, OP_DECODE_STEP = 1, 2, 3, 4
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
            "dsa_decode_step", "dsa_workspace_size", "dsa_status_string", "dsa_check_device",
            "dsa_read_probe_sink_size", "dsa_read_probe", "dsa_hot_cache_reset", "dsa_hot_cache_workspace_size",
-           "dsa_hot_cache_fetch")
+           "dsa_hot_cache_fetch", "dsa_decode_step_timed")
+STEP_EVENTS = 5   # events of dsa_decode_step_timed: start, after sampling, indexer, selection, attention
 
 
 class DsaHotCache(C.Structure):
@@ -77,9 +78,11 @@ def lib():
         L.dsa_hot_cache_workspace_size.argtypes = [P(DsaBatch), i32, i32]
         L.dsa_hot_cache_workspace_size.restype = sz
         L.dsa_hot_cache_fetch.argtypes = [P(DsaBatch), P(DsaLatentCache), vp, i32, P(DsaHotCache), vp, vp, sz, vp]
+        L.dsa_decode_step_timed.argtypes = [P(DsaBatch), P(DsaIndexCache), vp, vp, i32, P(DsaLatentCache), vp, i32,
+                                            i32, f32, vp, vp, vp, vp, sz, vp, P(vp), i32]
         for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
                      "dsa_decode_step", "dsa_check_device", "dsa_read_probe", "dsa_hot_cache_reset",
-                     "dsa_hot_cache_fetch"):
+                     "dsa_hot_cache_fetch", "dsa_decode_step_timed"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -222,6 +225,33 @@ def decode_step(batch: Batch, keys, key_scales, q_idx, w, kv, kv_scales, d_laten
         C.byref(b), C.byref(ic), _ptr(q_idx), _ptr(w), q_idx.shape[1], C.byref(lc), _ptr(q_mla),
         q_mla.shape[1], k, float(scale), _ptr(out), _ptr(lse), _ptr(indices_out), _ptr(ws), ws.numel(),
         _stream(stream)))
+    return out
+
+
+def event_handles(events, stream=None):
+    """ctypes array of the raw hipEvent_t handles of torch.cuda.Event objects
+    (created with enable_timing=True); torch creates an event on its first
+    record, so one not yet recorded is recorded once on the stream first."""
+    s = stream or torch.cuda.current_stream()
+    for e in events:
+        if not e.cuda_event:
+            e.record(s)
+    return (C.c_void_p * len(events))(*[C.c_void_p(e.cuda_event) for e in events])
+
+
+def decode_step_timed(batch: Batch, keys, key_scales, q_idx, w, kv, kv_scales, d_latent, q_mla, k, scale, events,
+                      out=None, lse=None, indices_out=None, workspace=None, stream=None):
+    """decode_step that also records `events` (STEP_EVENTS torch.cuda.Event) at
+    its phase boundaries: start, after sampling, indexer, selection, attention."""
+    if out is None:
+        out = _out_like(kv, q_mla, d_latent)
+    ws = _workspace(OP_DECODE_STEP, batch, k, q_mla.shape[1], q_mla.device, workspace)
+    b, ic, lc = batch.struct(), index_cache(keys, key_scales), latent_cache(kv, kv_scales, d_latent)
+    h = event_handles(events, stream)
+    _check("dsa_decode_step_timed", lib().dsa_decode_step_timed(
+        C.byref(b), C.byref(ic), _ptr(q_idx), _ptr(w), q_idx.shape[1], C.byref(lc), _ptr(q_mla),
+        q_mla.shape[1], k, float(scale), _ptr(out), _ptr(lse), _ptr(indices_out), _ptr(ws), ws.numel(),
+        _stream(stream), h, len(events)))
     return out
 
 

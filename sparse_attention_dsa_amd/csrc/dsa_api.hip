@@ -332,10 +332,18 @@ int dsa_sparse_mla_prefill(const dsa_batch* b, const dsa_latent_cache* c, const 
     return mla_entry(b, c, q, n_heads, indices, k, scale, out, lse, ws, ws_bytes, stream, true);
 }
 
-int dsa_decode_step(const dsa_batch* b, const dsa_index_cache* ic, const void* q_idx, const float* w,
-                    int32_t n_heads_idx, const dsa_latent_cache* lc, const void* q_mla, int32_t n_heads,
-                    int32_t k, float scale, void* out, float* lse, int32_t* indices_out, void* ws,
-                    size_t ws_bytes, dsa_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The decode step; with `ev` (DSA_STEP_EVENTS events) it records ev[0] before
+// its first launch, ev[1] after the bound sampling (at once when there is
+// none), ev[2] after the indexer, ev[3] after the top-K selection and ev[4]
+// after attention.
+int decode_step(const dsa_batch* b, const dsa_index_cache* ic, const void* q_idx, const float* w,
+                int32_t n_heads_idx, const dsa_latent_cache* lc, const void* q_mla, int32_t n_heads, int32_t k,
+                float scale, void* out, float* lse, int32_t* indices_out, void* ws, size_t ws_bytes,
+                dsa_stream_t stream, const hipEvent_t* ev) {
     int st = validate_indexer(b, ic, q_idx, w, n_heads_idx);
     if (st != DSA_OK) return st;
     if ((st = validate_mla(b, lc, q_mla, n_heads, k, out)) != DSA_OK) return st;
@@ -350,19 +358,51 @@ int dsa_decode_step(const dsa_batch* b, const dsa_index_cache* ic, const void* q
 
     const TopkArgs tk = topk_args(b, scores, l.ld, k, indices, base, l.tk);
     IndexerArgs ia = indexer_args(b, ic, q_idx, w, n_heads_idx, scores, l.ld);
-    hipError_t e;
+    hipError_t e = ev ? hipEventRecord(ev[0], s) : hipSuccess;
+    if (e != hipSuccess) return DSA_ERR_LAUNCH;
     if (indexer_emit_ok(ia)) {   // candidates straight from the indexer, no score rows
         ia.bound = (uint32_t*)(base + l.bound);
         ia.row_count = (uint32_t*)(base + l.count);
         ia.cand = (uint64_t*)(base + l.cand);
         ia.k = k;
-        e = launch_emit_step(ia, tk, s);
+        e = launch_emit_step(ia, tk, s, ev);
     } else {
-        e = launch_indexer(ia, s);
+        if (ev) e = hipEventRecord(ev[1], s);
+        if (e == hipSuccess) e = launch_indexer(ia, s);
+        if (e == hipSuccess && ev) e = hipEventRecord(ev[2], s);
         if (e == hipSuccess) e = launch_topk(tk, s);
     }
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[3], s);
     if (e != hipSuccess) return DSA_ERR_LAUNCH;
-    return run_mla(b, lc, q_mla, n_heads, indices, k, scale, out, lse, base, ws_bytes, l.mla_base, false, s);
+    st = run_mla(b, lc, q_mla, n_heads, indices, k, scale, out, lse, base, ws_bytes, l.mla_base, false, s);
+    if (st == DSA_OK && ev && hipEventRecord(ev[4], s) != hipSuccess) return DSA_ERR_LAUNCH;
+    return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_decode_step(const dsa_batch* b, const dsa_index_cache* ic, const void* q_idx, const float* w,
+                    int32_t n_heads_idx, const dsa_latent_cache* lc, const void* q_mla, int32_t n_heads,
+                    int32_t k, float scale, void* out, float* lse, int32_t* indices_out, void* ws,
+                    size_t ws_bytes, dsa_stream_t stream) {
+    return decode_step(b, ic, q_idx, w, n_heads_idx, lc, q_mla, n_heads, k, scale, out, lse, indices_out, ws,
+                       ws_bytes, stream, nullptr);
+}
+
+int dsa_decode_step_timed(const dsa_batch* b, const dsa_index_cache* ic, const void* q_idx, const float* w,
+                          int32_t n_heads_idx, const dsa_latent_cache* lc, const void* q_mla, int32_t n_heads,
+                          int32_t k, float scale, void* out, float* lse, int32_t* indices_out, void* ws,
+                          size_t ws_bytes, dsa_stream_t stream, void* const* events, int32_t n_events) {
+    if (!events || n_events < DSA_STEP_EVENTS) return DSA_ERR_INVALID_ARG;
+    hipEvent_t ev[DSA_STEP_EVENTS];
+    for (int i = 0; i < DSA_STEP_EVENTS; ++i) {
+        if (!events[i]) return DSA_ERR_INVALID_ARG;
+        ev[i] = (hipEvent_t)events[i];
+    }
+    return decode_step(b, ic, q_idx, w, n_heads_idx, lc, q_mla, n_heads, k, scale, out, lse, indices_out, ws,
+                       ws_bytes, stream, ev);
 }
 
 }  // extern "C"

@@ -182,7 +182,10 @@ hipError_t launch_sample_bound(const IndexerArgs& a, hipStream_t s);
 // Sample bound per query row (and zeroed candidate counters), then the
 // indexer emitting candidates, then the selection from the candidate lists
 // (recomputing a row's scores into a.scores where its bound fails).
-hipError_t launch_emit_step(const IndexerArgs& ia, const TopkArgs& ta, hipStream_t s);
+// With `ev`, ev[1] is recorded after the sample bound and ev[2] after the
+// indexer (the measurement variant of the decode step).
+hipError_t launch_emit_step(const IndexerArgs& ia, const TopkArgs& ta, hipStream_t s,
+                            const hipEvent_t* ev = nullptr);
 // Sample bound, chunk compaction, then one selection workgroup per row.
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_mla(const MlaArgs& a, bool prefill, hipStream_t s);

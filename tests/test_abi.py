@@ -77,6 +77,14 @@ def test_invalid_arguments_rejected_before_device(L):
                                    0x1, 1 << 30, None) == -1
     assert L.dsa_sparse_mla_decode(C.byref(b), C.byref(lc_ok), 0x1, 128, 0x1, 2048, 0.1, 0x1, None,
                                    0x1, 16, None) == -3
+    # the measurement variant of the decode step: too few or null event handles
+    ev = (C.c_void_p * 5)(*[C.c_void_p(0x100 + i) for i in range(5)])
+    args = (C.byref(b), C.byref(ic), 0x1, 0x1, 64, C.byref(lc_ok), 0x1, 128, 2048, 0.1, 0x1, None, None, 0x1,
+            1 << 30, None)
+    assert L.dsa_decode_step_timed(*args, ev, 4) == -1
+    assert L.dsa_decode_step_timed(*args, None, 5) == -1
+    ev_null = (C.c_void_p * 5)(0x100, 0x101, None, 0x103, 0x104)
+    assert L.dsa_decode_step_timed(*args, ev_null, 5) == -1
     # the read-bandwidth probe: null or misaligned buffer, size not a multiple of 16, null sink
     assert L.dsa_read_probe(None, 1024, 0x100, 1 << 20, None) == -1
     assert L.dsa_read_probe(0x108, 1024, 0x100, 1 << 20, None) == -1
