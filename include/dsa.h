@@ -172,10 +172,12 @@ int dsa_decode_step(const dsa_batch *batch, const dsa_index_cache *index_cache,
  * Measurement variant of dsa_decode_step: the same launches and results,
  * plus DSA_STEP_EVENTS events recorded on `stream` at the step's phase
  * boundaries, so that a caller can time each phase on the stream it runs on:
- *   events[0] before the first launch, events[1] after the top-K bound
- *   sampling (at once when the step takes no sample), events[2] after the
- *   lightning indexer, events[3] after the top-K selection, events[4] after
- *   sparse MLA (and its split combine).
+ *   events[0] before the first launch (so events[0..1] span the top-K bound
+ *   sampling, empty when the step takes none), events[1] and events[2] at
+ *   the start and end of the lightning indexer (taken by the kernel launch
+ *   itself for the persistent decode indexer, so they span the kernel
+ *   alone), events[3] after the top-K selection, events[4] after sparse MLA
+ *   (and its split combine).
  *   events: DSA_STEP_EVENTS caller-created hipEvent_t handles (as void*);
  *           recording allocates nothing.  n_events >= DSA_STEP_EVENTS, else
  *           DSA_ERR_INVALID_ARG (also for a NULL handle).

@@ -337,9 +337,8 @@ int dsa_sparse_mla_prefill(const dsa_batch* b, const dsa_latent_cache* c, const 
 namespace {
 
 // The decode step; with `ev` (DSA_STEP_EVENTS events) it records ev[0] before
-// its first launch, ev[1] after the bound sampling (at once when there is
-// none), ev[2] after the indexer, ev[3] after the top-K selection and ev[4]
-// after attention.
+// its first launch, ev[1] and ev[2] at the start and end of the indexer,
+// ev[3] after the top-K selection and ev[4] after attention.
 int decode_step(const dsa_batch* b, const dsa_index_cache* ic, const void* q_idx, const float* w,
                 int32_t n_heads_idx, const dsa_latent_cache* lc, const void* q_mla, int32_t n_heads, int32_t k,
                 float scale, void* out, float* lse, int32_t* indices_out, void* ws, size_t ws_bytes,
@@ -367,9 +366,7 @@ int decode_step(const dsa_batch* b, const dsa_index_cache* ic, const void* q_idx
         ia.k = k;
         e = launch_emit_step(ia, tk, s, ev);
     } else {
-        if (ev) e = hipEventRecord(ev[1], s);
-        if (e == hipSuccess) e = launch_indexer(ia, s);
-        if (e == hipSuccess && ev) e = hipEventRecord(ev[2], s);
+        e = launch_indexer(ia, s, ev ? ev + 1 : nullptr);
         if (e == hipSuccess) e = launch_topk(tk, s);
     }
     if (e == hipSuccess && ev) e = hipEventRecord(ev[3], s);

@@ -174,7 +174,9 @@ struct MlaArgs {
 int device_cu_count();
 
 // Launchers (return hipError_t of the last launch).
-hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
+// With `se`, se[0] and se[1] mark the indexer's start and end (for the
+// persistent kernel, taken by its launch itself).
+hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s, const hipEvent_t* se = nullptr);
 // Whether the decode step can take the candidate-emission path for this
 // shape (e4m3 keys, dim 128, 16/32/64 heads, 64-token blocks, persistent grid).
 bool indexer_emit_ok(const IndexerArgs& a);
@@ -182,8 +184,8 @@ hipError_t launch_sample_bound(const IndexerArgs& a, hipStream_t s);
 // Sample bound per query row (and zeroed candidate counters), then the
 // indexer emitting candidates, then the selection from the candidate lists
 // (recomputing a row's scores into a.scores where its bound fails).
-// With `ev`, ev[1] is recorded after the sample bound and ev[2] after the
-// indexer (the measurement variant of the decode step).
+// With `ev`, ev[1] and ev[2] mark the start and end of the indexer (the
+// measurement variant of the decode step).
 hipError_t launch_emit_step(const IndexerArgs& ia, const TopkArgs& ta, hipStream_t s,
                             const hipEvent_t* ev = nullptr);
 // Sample bound, chunk compaction, then one selection workgroup per row.

@@ -22,6 +22,8 @@
 //               does the same work with no per-chunk start-up;
 //   chunked     one workgroup per (request, query group, 1024-token chunk),
 //               pages fed by an LDS ring of asynchronous transfers.
+#include <hip/hip_ext.h>
+
 #include "indexer_dev.h"
 #include "topk_dev.h"
 
@@ -781,21 +783,33 @@ __global__ __launch_bounds__(256) void indexer_generic(IndexerArgs a) {
 
 // Generic path kernel above; launch policy below.
 template <int NQ, int HT>
-static hipError_t launch_fp8(const IndexerArgs& a, hipStream_t s) {
+static hipError_t launch_fp8(const IndexerArgs& a, hipStream_t s, const hipEvent_t* se) {
     const int qgroups = (a.g.max_q_len + NQ - 1) / NQ;
     if (a.g.B * qgroups <= PER_MAX_ITEMS) {
-        if (a.cand)
-            hipLaunchKernelGGL((indexer_fp8_persistent<NQ, HT, true>), dim3(device_cu_count() * PER_WG_PER_CU),
-                               dim3(IDX_THREADS), 0, s, a, qgroups);
-        else
-            hipLaunchKernelGGL((indexer_fp8_persistent<NQ, HT, false>), dim3(device_cu_count() * PER_WG_PER_CU),
-                               dim3(IDX_THREADS), 0, s, a, qgroups);
+        const dim3 grid(device_cu_count() * PER_WG_PER_CU);
+        if (se) {   // start and stop events taken by the launch itself: the kernel's own duration
+            if (a.cand)
+                hipExtLaunchKernelGGL((indexer_fp8_persistent<NQ, HT, true>), grid, dim3(IDX_THREADS), 0, s, se[0],
+                                      se[1], 0, a, qgroups);
+            else
+                hipExtLaunchKernelGGL((indexer_fp8_persistent<NQ, HT, false>), grid, dim3(IDX_THREADS), 0, s, se[0],
+                                      se[1], 0, a, qgroups);
+        } else if (a.cand) {
+            hipLaunchKernelGGL((indexer_fp8_persistent<NQ, HT, true>), grid, dim3(IDX_THREADS), 0, s, a, qgroups);
+        } else {
+            hipLaunchKernelGGL((indexer_fp8_persistent<NQ, HT, false>), grid, dim3(IDX_THREADS), 0, s, a, qgroups);
+        }
         return hipGetLastError();
+    }
+    if (se) {
+        const hipError_t e = hipEventRecord(se[0], s);
+        if (e != hipSuccess) return e;
     }
     const int chunk = 4 * DMA_PPW * IDX_PAGE;
     dim3 grid((a.g.max_ctx + chunk - 1) / chunk, a.g.B * qgroups);
     hipLaunchKernelGGL((indexer_fp8_dma<NQ, HT>), grid, dim3(IDX_THREADS), 0, s, a, qgroups);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess && se ? hipEventRecord(se[1], s) : e;
 }
 
 bool indexer_emit_ok(const IndexerArgs& a) {
@@ -814,28 +828,32 @@ hipError_t launch_sample_bound(const IndexerArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
+hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s, const hipEvent_t* se) {
     const bool fast = a.key_dtype == 2 && a.dim == IDX_D && a.g.block_size == IDX_PAGE &&
                       (a.n_heads == 64 || a.n_heads == 32 || a.n_heads == 16);
-    if (fast && a.g.max_q_len >= PF_MIN_Q) {
-        switch (a.n_heads) {
-        case 64: return launch_fp8_prefill<4>(a, s);
-        case 32: return launch_fp8_prefill<2>(a, s);
-        default: return launch_fp8_prefill<1>(a, s);
-        }
-    }
-    if (fast) {
+    if (fast && a.g.max_q_len < PF_MIN_Q) {
         const bool two = a.g.max_q_len >= 2;
         switch (a.n_heads) {
-        case 64: return two ? launch_fp8<2, 4>(a, s) : launch_fp8<1, 4>(a, s);
-        case 32: return two ? launch_fp8<2, 2>(a, s) : launch_fp8<1, 2>(a, s);
-        default: return two ? launch_fp8<2, 1>(a, s) : launch_fp8<1, 1>(a, s);
+        case 64: return two ? launch_fp8<2, 4>(a, s, se) : launch_fp8<1, 4>(a, s, se);
+        case 32: return two ? launch_fp8<2, 2>(a, s, se) : launch_fp8<1, 2>(a, s, se);
+        default: return two ? launch_fp8<2, 1>(a, s, se) : launch_fp8<1, 1>(a, s, se);
         }
     }
-    dim3 grid((a.g.max_ctx + 255) / 256, a.g.T);
-    const size_t shm = sizeof(float) * ((size_t)a.n_heads * a.dim + a.n_heads);
-    hipLaunchKernelGGL(indexer_generic, grid, dim3(256), shm, s, a);
-    return hipGetLastError();
+    hipError_t e = se ? hipEventRecord(se[0], s) : hipSuccess;
+    if (e != hipSuccess) return e;
+    if (fast) {
+        switch (a.n_heads) {
+        case 64: e = launch_fp8_prefill<4>(a, s); break;
+        case 32: e = launch_fp8_prefill<2>(a, s); break;
+        default: e = launch_fp8_prefill<1>(a, s); break;
+        }
+    } else {
+        dim3 grid((a.g.max_ctx + 255) / 256, a.g.T);
+        const size_t shm = sizeof(float) * ((size_t)a.n_heads * a.dim + a.n_heads);
+        hipLaunchKernelGGL(indexer_generic, grid, dim3(256), shm, s, a);
+        e = hipGetLastError();
+    }
+    return e == hipSuccess && se ? hipEventRecord(se[1], s) : e;
 }
 
 }  // namespace dsa

@@ -595,9 +595,7 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_select_cand(TopkArgs a, Inde
 
 hipError_t launch_emit_step(const IndexerArgs& ia, const TopkArgs& ta, hipStream_t s, const hipEvent_t* ev) {
     hipError_t e = launch_sample_bound(ia, s);
-    if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);
-    if (e == hipSuccess) e = launch_indexer(ia, s);
-    if (e == hipSuccess && ev) e = hipEventRecord(ev[2], s);
+    if (e == hipSuccess) e = launch_indexer(ia, s, ev ? ev + 1 : nullptr);
     if (e != hipSuccess) return e;
     switch (ia.n_heads) {
     case 64: hipLaunchKernelGGL(topk_select_cand<4>, dim3(ta.g.T), dim3(SEL_THREADS), 0, s, ta, ia); break;
