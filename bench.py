@@ -12,8 +12,8 @@ second).  `roofline` covers the dominant kernel of the step -- the lightning
 indexer as the step runs it (emitting top-K candidates instead of score
 rows) -- with its algorithmic bytes per launch (the keys, scales, page-table
 entries, queries and weights it must read) divided by its average launch
-time, timed live here by events that dsa_decode_step_timed records on the
-library's stream right before and after that launch; its `traffic` is the
+time, timed live here by the start and stop events that
+dsa_decode_step_timed has that launch itself take; its `traffic` is the
 HBM bytes per launch that rocprofv3's FETCH_SIZE and WRITE_SIZE counters
 recorded (scaled by a copy-kernel calibration), read from the committed
 counter summary and reported only while the indexer source is unchanged.
