@@ -145,16 +145,45 @@ def _qm_code(wl):
     return "f32" if wl.kv_dtype == "f32" else "bf16"
 
 
+def query_positions(wl):
+    """(request r, position p, visible count n) of every query row, in row order.
+
+    Reading of the pages (section "DeepSeek Sparse Attention": each query
+    token is scored against the tokens before it; the MTP workload's two
+    query tokens are causal among themselves): a request's context length L
+    counts its q_len new query tokens, which are its last q_len positions;
+    query j (0-based) sits at p = L - q_len + j and sees tokens [0, p], so
+    n = p + 1.  Pinned by tests/golden/positions_hand.json."""
+    out = []
+    for r in range(len(wl.context_lens)):
+        L, ql = int(wl.context_lens[r]), int(wl.q_lens[r])
+        for j in range(ql):
+            p = L - ql + j
+            out.append((r, p, p + 1))
+    return out
+
+
+def row_position(wl, t):
+    """query_positions(wl)[t] for one row, without listing every row."""
+    qsl = np.asarray(wl.query_start_loc)
+    r = int(np.searchsorted(qsl, t, side="right")) - 1
+    while int(qsl[r + 1]) <= t:                  # requests with no query rows
+        r += 1
+    L, ql = int(wl.context_lens[r]), int(wl.q_lens[r])
+    p = L - ql + (t - int(qsl[r]))
+    return r, p, p + 1
+
+
 def query_scores(wl, t):
     """Indexer scores of query row t of a workload (float64 [n_t])."""
-    r, p, n = wl.query_positions()[t]
+    r, p, n = row_position(wl, t)
     return indexer_scores(wl.idx_keys, wl.idx_scales, wl.idx_dtype, wl.page_table[r],
                           wl.block_size, wl.q_idx[t], _q_code(wl), wl.w[t], n)
 
 
 def query_mla(wl, t, sel, layer=1):
     """Sparse MLA of query row t over `sel` on layer 1 or 2's latent cache."""
-    r, p, n = wl.query_positions()[t]
+    r, p, n = row_position(wl, t)
     kv, ks, q = (wl.kv, wl.kv_scales, wl.q_mla) if layer == 1 else (wl.kv2, wl.kv2_scales, wl.q_mla2)
     return sparse_mla(kv, ks, wl.kv_dtype, wl.d_latent, wl.d_rope, wl.page_table[r],
                       wl.block_size, q[t], _qm_code(wl), sel, wl.softmax_scale)

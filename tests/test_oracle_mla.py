@@ -14,6 +14,8 @@ import math
 import os
 
 import numpy as np
+
+import oracle
 import pytest
 import torch
 
@@ -161,7 +163,7 @@ def test_page_table_invariance(orc):
 def test_mtp_queries_are_causal(orc):
     wl = workloads.make_workload("single_b1_l32768", context_lens=[90], q_len=2, idx_heads=4,
                                  mla_heads=2, d_latent=16, d_rope=8, topk=200)
-    pos = wl.query_positions()
+    pos = oracle.query_positions(wl)
     assert [p for (_, p, _) in pos] == [88, 89]
     res = orc.run_step(wl, threads=1)
     assert res[0]["indices"].tolist() == list(range(89))

@@ -60,3 +60,24 @@ def test_duplicate_scores(orc):
     scores = np.array([1.0, 5.0, 2.0, 5.0, 2.0, 2.0, 0.0])
     assert sorted(orc.topk(scores, 3).tolist()) == [1, 2, 3]
     assert sorted(orc.topk(scores, 4).tolist()) == [1, 2, 3, 4]
+
+
+def test_query_positions_hand_worked():
+    """The causal visibility reading against hand-worked rows (request,
+    position, visible count), requests with no query rows included."""
+    import json
+    import os
+    import types
+
+    import numpy as np
+
+    import oracle
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "positions_hand.json")
+    for case in json.load(open(path))["cases"]:
+        ql = np.asarray(case["q_lens"], dtype=np.int32)
+        qsl = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+        wl = types.SimpleNamespace(context_lens=np.asarray(case["context_lens"], dtype=np.int32), q_lens=ql,
+                                   query_start_loc=qsl)
+        want = [tuple(r) for r in case["rows"]]
+        assert oracle.query_positions(wl) == want
+        assert [oracle.row_position(wl, t) for t in range(len(want))] == want

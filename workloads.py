@@ -134,16 +134,6 @@ class Workload:
     def d_qk(self) -> int:
         return self.d_latent + self.d_rope
 
-    def query_positions(self):
-        """(request, position p, visible count n=p+1) of every query row."""
-        out = []
-        for r in range(self.batch):
-            L, ql = int(self.context_lens[r]), int(self.q_lens[r])
-            for j in range(ql):
-                p = L - ql + j
-                out.append((r, p, p + 1))
-        return out
-
 
 # ----------------------------------------------------------------- encoders
 def bf16_bits(x: np.ndarray) -> np.ndarray:
