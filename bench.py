@@ -67,6 +67,22 @@ PREFILL_WORKLOAD = "prefill_q4096_l131072"
 
 
 # ------------------------------------------------------------ accounting
+def visible_counts(wl):
+    """Visible-token count of every query row, in row order: query j of a
+    request with context L (new query tokens included) and q_len rows sees
+    L - q_len + j + 1 tokens (inclusive causal)."""
+    out = []
+    for L, ql in zip(wl.context_lens.tolist(), wl.q_lens.tolist()):
+        out.extend(L - ql + j + 1 for j in range(ql))
+    return out
+
+
+def h800_ridge():
+    """The H800's practical ridge point the MLA Modifications section quotes:
+    865 TFLOP/s over 3.35 TB/s, in FLOP per byte."""
+    return 865e12 / 3.35e12
+
+
 def mla_arithmetic_intensity(H, d, r, b):
     """FLOP per byte of MQA-mode MLA decode for L >> H (MLA Modifications
     section of the GLM-5.3 article): 2H(2d+r) / (b(d+r))."""
@@ -87,7 +103,7 @@ def indexer_launch_bytes(wl):
     for r in range(wl.batch):
         L, ql = int(wl.context_lens[r]), int(wl.q_lens[r])
         total += L * key_row + 4 * math.ceil(L / wl.block_size) + ql * q_row
-    for (_, _, n) in wl.query_positions():
+    for n in visible_counts(wl):
         total += 4 * n
     return total
 
@@ -96,7 +112,7 @@ def indexer_read_bytes(wl):
     """Bytes the candidate-emitting indexer must read: indexer_launch_bytes
     without the score rows (its candidate appends, about 8 bytes for each of a
     few thousand tokens per row, are left out)."""
-    return indexer_launch_bytes(wl) - sum(4 * n for (_, _, n) in wl.query_positions())
+    return indexer_launch_bytes(wl) - sum(4 * n for n in visible_counts(wl))
 
 
 def step_bytes(wl, indices):
@@ -120,7 +136,7 @@ def step_bytes(wl, indices):
 def step_flops(wl, indices):
     """Indexer (2*H_idx*D_idx per visible token) + MLA (2*H*(576+512) per
     selected token) floating-point operations of one step."""
-    f_idx = sum(2 * wl.idx_heads * wl.idx_dim * n for (_, _, n) in wl.query_positions())
+    f_idx = sum(2 * wl.idx_heads * wl.idx_dim * n for n in visible_counts(wl))
     n_sel = int((indices >= 0).sum())
     f_mla = 2 * wl.mla_heads * ((wl.d_latent + wl.d_rope) + wl.d_latent) * n_sel
     return f_idx, f_mla
@@ -141,6 +157,36 @@ def mla_layer_bytes(wl, indices):
         total += len(u) * latent_row_bytes(wl) + 4 * len(np.unique(u // wl.block_size))
         total += ql * mla_q
     return total
+
+
+def check_against_oracle(wl, rows, ref, indices, out, oracle):
+    """The timed step's selection and output for `rows` against the oracle's
+    results for them: every selection holds min(K, n) distinct visible
+    tokens and differs from the oracle's only at scores within 1e-4
+    (relative) of the oracle's K-th score; every output is within 2e-2 max-abs
+    (1e-4 for fp32) of the oracle's sparse MLA on the step's own selection."""
+    import numpy as np
+    atol = 1e-4 if wl.kv_dtype == "f32" else 2e-2
+    diffs, worst, ok = 0, 0.0, True
+    for t in rows:
+        r = ref[t]
+        sc, osel = r["scores"], r["indices"]
+        n = len(sc)
+        m = min(wl.topk, n)
+        sel = indices[t][:m]
+        ok &= bool((sel >= 0).all() and (indices[t][m:] == -1).all() and (np.diff(sel) > 0).all()
+                   and sel[-1] < n)
+        d = set(sel.tolist()) ^ set(osel.tolist())
+        if d:
+            kth = float(sc[osel[-1]])
+            ok &= all(abs(float(sc[x]) - kth) <= 1e-4 * abs(kth) for x in d)
+        diffs += len(d)
+        o_ref = r["out"] if not d else oracle.query_mla(wl, t, sel)[0]
+        err = float(np.abs(out[t] - o_ref).max())
+        worst = max(worst, err)
+        ok &= err <= atol
+    return {"rows": len(rows), "selection_diffs": diffs, "max_abs_err": round(worst, 6), "atol": atol,
+            "ok": bool(ok)}
 
 
 # ------------------------------------------------------- measured traffic
@@ -431,14 +477,14 @@ def hot_cache_leg(steps, warmup, log, capacity_mult=4, keep=0.8):
     hot = B.HotCache(cap, wl.batch, wl.max_context_len, d["kv"].shape[-1], d["kv"].dtype)
     B.hot_cache_reset(batch, hot)
     rng = np.random.default_rng(7)
-    pos = wl.query_positions()
-    prev = [rng.choice(n, size=K, replace=False) for (_, _, n) in pos]
+    vis = visible_counts(wl)
+    prev = [rng.choice(n, size=K, replace=False) for n in vis]
     sels = []
     # warm-up until the hot set is full, so that the timed steps evict
     warmup += int(np.ceil((capacity_mult - 1) / (1.0 - keep))) + 2
     for _ in range(warmup + steps):
         cur = []
-        for t, (_, _, n) in enumerate(pos):
+        for t, n in enumerate(vis):
             kept = rng.choice(prev[t], size=int(keep * K), replace=False)
             new = rng.choice(n, size=2 * (K - len(kept)), replace=True)
             new = np.setdiff1d(np.unique(new), kept)[:K - len(kept)]
@@ -587,6 +633,7 @@ def main(argv=None):
     ms_per_step = rig.time_loop(rig.step, args.steps, args.warmup)
     log("[bench] step: %.1f us" % (ms_per_step * 1e3))
     indices = rig.selection()
+    out_first = rig.outs[0].float().cpu().numpy()      # the step's output on copy 0 (same inputs as every copy)
 
     # Dominant kernel: the lightning indexer as the step runs it, timed by the
     # events the library records around its launch.
@@ -654,20 +701,23 @@ def main(argv=None):
     if not args.no_hot_cache and args.workload == DEFAULT_WORKLOAD:
         hot = hot_cache_leg(max(5, min(args.steps, 20)), 10, log)
 
-    # CPU baseline: the oracle on a bounded sample of query rows.
-    cpu = None
+    # CPU baseline: the oracle on a bounded sample of query rows; its results
+    # also check the timed step's selection and output for those rows.
+    cpu = parity = None
     if args.cpu_rows > 0:
         import oracle
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         rng = np.random.default_rng(0)
         rows = sorted(rng.choice(T, size=min(args.cpu_rows, T), replace=False).tolist())
         tc = time.time()
-        oracle.run_step(wl, rows=rows, threads=threads, keep_scores=False)
+        ref = oracle.run_step(wl, rows=rows, threads=threads)
         dt = time.time() - tc
         cpu = {"value": round(len(rows) / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
                "sample": "%d of %d query rows of the same workload (full contexts, fp64 C oracle), %.1f s wall"
                          % (len(rows), T, dt)}
         log("[bench] oracle: %d rows in %.1fs" % (len(rows), dt))
+        parity = check_against_oracle(wl, rows, ref, indices, out_first, oracle)
+        log("[bench] parity of the timed step on %d rows: %s" % (len(rows), parity))
 
     res = {
         "metric": "DSA decode tokens/s per layer at 128K ctx, batch 64; HBM GB/s as % of peak",
@@ -700,8 +750,9 @@ def main(argv=None):
                                   "us_per_launch": round(idx_us, 2)},
         "step_hbm": {"bytes": sb, "achieved": round(step_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(step_gbs / PEAK_HBM_GBS, 4)},
-        "step_tflops": {"indexer_fp8": round(f_idx / (ms_per_step * 1e-3) / 1e12, 2),
-                        "mla_bf16": round(f_mla / (ms_per_step * 1e-3) / 1e12, 2)},
+        "kernel_tflops": {"indexer_fp8": round(f_idx / (phases["indexer"] * 1e-6) / 1e12, 1),
+                          "mla_bf16": round(f_mla / (phases["attention"] * 1e-6) / 1e12, 1),
+                          "basis": "each contraction's FLOPs over its own phase time"},
         "indexshare": share,
         "all_128k": at128,
         "prefill": prefill,
@@ -709,6 +760,7 @@ def main(argv=None):
         "hot_cache": hot,
         "hbm_ceiling": ceiling,
         "cpu_baseline": cpu,
+        "parity": parity,
     }
     print(json.dumps(res), flush=True)
     return 0

@@ -106,8 +106,9 @@ typedef struct {
  *   q_idx  [T][n_heads_idx][dim], same dtype as the key cache (fp32 or e4m3;
  *          a per-(t,h) query scale is folded into w by the caller).
  *   w      [T][n_heads_idx] fp32 head weights.
- *   scores [T][ld_scores] fp32: scores[t][s] for s < n_t; entries s >= n_t
- *          are not written.  ld_scores >= max_context_len.
+ *   scores [T][ld_scores] fp32: scores[t][s] for s < n_t, and -inf for
+ *          n_t <= s < ld_scores (positions a query does not see).
+ *          ld_scores >= max_context_len.
  */
 int dsa_indexer_scores(const dsa_batch *batch, const dsa_index_cache *cache,
                        const void *q_idx, const float *w, int32_t n_heads_idx,
@@ -118,7 +119,7 @@ int dsa_indexer_scores(const dsa_batch *batch, const dsa_index_cache *cache,
  *   indices [T][k] int32: the min(k, n_t) selected logical positions of row t
  *           in ascending order, then -1 padding.  Selection rule: highest
  *           score first, lower index first among equal scores.  1 <= k <= 4096.
- *   workspace: dsa_workspace_size(DSA_OP_TOPK, batch, k, 0, 0) bytes
+ *   workspace: dsa_workspace_size(DSA_OP_TOPK, batch, k, 0) bytes
  *           (candidate slots for rows longer than 12288 tokens, about 4 bytes
  *           per score; 0 when no row is that long, and NULL is then accepted).
  */
@@ -135,7 +136,7 @@ int dsa_topk(const dsa_batch *batch, const float *scores, int64_t ld_scores, int
  *   out     [T][n_heads][d_latent]: fp32 for an fp32 cache, bf16 otherwise.
  *   lse     [T][n_heads] fp32 natural-log log-sum-exp of the scaled logits,
  *           or NULL.  A row with no valid index gets out = 0, lse = -inf.
- *   workspace: dsa_workspace_size(DSA_OP_MLA_DECODE, batch, k, n_heads, 0).
+ *   workspace: dsa_workspace_size(DSA_OP_MLA_DECODE, batch, k, n_heads).
  */
 int dsa_sparse_mla_decode(const dsa_batch *batch, const dsa_latent_cache *cache,
                           const void *q, int32_t n_heads, const int32_t *indices, int32_t k,
@@ -160,7 +161,7 @@ int dsa_sparse_mla_prefill(const dsa_batch *batch, const dsa_latent_cache *cache
  * kept in the workspace.  Arguments as in the three calls above.
  *   indices_out  [T][k] or NULL: when given, the selection is also returned
  *                (for reuse by layers that share this layer's indexer).
- *   workspace: dsa_workspace_size(DSA_OP_DECODE_STEP, batch, k, n_heads, 0).
+ *   workspace: dsa_workspace_size(DSA_OP_DECODE_STEP, batch, k, n_heads).
  */
 int dsa_decode_step(const dsa_batch *batch, const dsa_index_cache *index_cache,
                     const void *q_idx, const float *w, int32_t n_heads_idx,
@@ -194,8 +195,7 @@ int dsa_decode_step_timed(const dsa_batch *batch, const dsa_index_cache *index_c
  * invalid request and for calls that need none (top-K on rows of at most
  * 12288 tokens, prefill MLA without splits).  Host-only, never touches the
  * device. */
-size_t dsa_workspace_size(int32_t op, const dsa_batch *batch, int32_t k, int32_t n_heads,
-                          int32_t n_heads_idx);
+size_t dsa_workspace_size(int32_t op, const dsa_batch *batch, int32_t k, int32_t n_heads);
 
 /* Static text for a status code. */
 const char *dsa_status_string(int32_t status);

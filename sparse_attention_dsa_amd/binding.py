@@ -66,7 +66,7 @@ def lib():
         L.dsa_sparse_mla_prefill.argtypes = mla
         L.dsa_decode_step.argtypes = [P(DsaBatch), P(DsaIndexCache), vp, vp, i32, P(DsaLatentCache), vp, i32,
                                       i32, f32, vp, vp, vp, vp, sz, vp]
-        L.dsa_workspace_size.argtypes = [i32, P(DsaBatch), i32, i32, i32]
+        L.dsa_workspace_size.argtypes = [i32, P(DsaBatch), i32, i32]
         L.dsa_workspace_size.restype = sz
         L.dsa_status_string.argtypes = [i32]
         L.dsa_status_string.restype = C.c_char_p
@@ -152,9 +152,9 @@ def latent_cache(kv: torch.Tensor, scales: Optional[torch.Tensor], d_latent: int
                           dtype_code(kv), d_latent, kv.shape[-1] - d_latent)
 
 
-def workspace_size(op: int, batch: Batch, k: int, n_heads: int = 0, n_heads_idx: int = 0) -> int:
+def workspace_size(op: int, batch: Batch, k: int, n_heads: int = 0) -> int:
     b = batch.struct()
-    return int(lib().dsa_workspace_size(op, C.byref(b), k, n_heads, n_heads_idx))
+    return int(lib().dsa_workspace_size(op, C.byref(b), k, n_heads))
 
 
 def _workspace(op, batch, k, n_heads, device, workspace):
@@ -165,7 +165,7 @@ def _workspace(op, batch, k, n_heads, device, workspace):
 
 
 def indexer_scores(batch: Batch, keys, key_scales, q_idx, w, scores=None, ld=None, stream=None):
-    """Scores [T][ld] fp32 (entries past each row's visible count are untouched)."""
+    """Scores [T][ld] fp32 (-inf past each row's visible count)."""
     ld = ld or ((batch.max_context_len + 63) // 64 * 64)
     if scores is None:
         scores = torch.empty((batch.total_q, ld), dtype=torch.float32, device=q_idx.device)

@@ -261,8 +261,7 @@ const char* dsa_status_string(int32_t status) {
 
 int dsa_check_device(void) { return check_device_cached(); }
 
-size_t dsa_workspace_size(int32_t op, const dsa_batch* b, int32_t k, int32_t n_heads, int32_t n_heads_idx) {
-    (void)n_heads_idx;
+size_t dsa_workspace_size(int32_t op, const dsa_batch* b, int32_t k, int32_t n_heads) {
     if (!batch_ok(b)) return 0;
     switch (op) {
     case DSA_OP_TOPK:
@@ -293,7 +292,9 @@ int dsa_indexer_scores(const dsa_batch* b, const dsa_index_cache* c, const void*
     if (!scores || ld < b->max_context_len) return DSA_ERR_INVALID_ARG;
     if ((st = check_device_cached()) != DSA_OK) return st;
     const IndexerArgs a = indexer_args(b, c, q_idx, w, n_heads_idx, scores, ld);
-    return launch_status(launch_indexer(a, (hipStream_t)stream));
+    hipError_t e = launch_indexer(a, (hipStream_t)stream);
+    if (e == hipSuccess) e = launch_score_tail(a, (hipStream_t)stream);
+    return launch_status(e);
 }
 
 int dsa_topk(const dsa_batch* b, const float* scores, int64_t ld, int32_t k, int32_t* indices,

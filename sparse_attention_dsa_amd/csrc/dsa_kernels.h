@@ -88,6 +88,21 @@ __device__ __forceinline__ i32x8 join_i32x8(u32x4 lo, u32x4 hi) {
     return r;
 }
 
+// ------------------------------------------------------ waits and barriers
+// Wait until at most N of this wave's vector-memory operations are pending.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier that orders LDS traffic only: unlike __syncthreads() it
+// does not wait for this wave's outstanding global loads (asynchronous
+// transfers in flight), which the callers account for with wait_vmcnt.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ----------------------------------------------------------- batch maps
 // Request owning query row t: the largest r with qsl[r] <= t.
 __device__ __forceinline__ int find_request(const int32_t* qsl, int B, int t) {
@@ -177,6 +192,8 @@ int device_cu_count();
 // With `se`, se[0] and se[1] mark the indexer's start and end (for the
 // persistent kernel, taken by its launch itself).
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s, const hipEvent_t* se = nullptr);
+// -inf over every score row's entries past its visible tokens, [n_t, ld).
+hipError_t launch_score_tail(const IndexerArgs& a, hipStream_t s);
 // Whether the decode step can take the candidate-emission path for this
 // shape (e4m3 keys, dim 128, 16/32/64 heads, 64-token blocks, persistent grid).
 bool indexer_emit_ok(const IndexerArgs& a);

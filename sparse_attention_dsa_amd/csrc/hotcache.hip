@@ -13,16 +13,19 @@
 //  1. every selected token that is resident is a hit: its slot's last use
 //     becomes this step;
 //  2. the distinct selected tokens that are not resident are the misses,
-//     ordered by (request, token);
+//     listed in (request, token) order;
 //  3. the victims are the M slots (M = number of misses) not used in this
-//     step with the greatest age (step - last use, saturated at 65535; a slot
-//     never used has age 65535), ties to the lower slot; they are taken in
-//     the order: every victim older than the M-th one by slot, then those of
-//     its age by slot;
-//  4. miss i moves into victim i: the victim's previous token loses its slot,
-//     the row (and its e4m3 scale) is copied from host memory by the GPU
-//     (zero-copy reads of pinned memory), and the slot's last use becomes
-//     this step.
+//     step that were used least recently: a never-used slot ranks before any
+//     used one, otherwise the earlier last use first, equal ranks to the
+//     lower slot.  Ages are exact 32-bit step counts (never capped): the
+//     M-th oldest age is found by a two-level selection, first over the high
+//     16 bits of the ages, then over the low 16 bits within that bucket;
+//  4. each miss moves into one victim (the misses in order take every victim
+//     older than the M-th one in slot order, then those of its age in slot
+//     order; which victim a miss takes does not change the resident set or
+//     any slot's age): the victim's previous token loses its slot, the row
+//     (and its e4m3 scale) is copied from host memory by the GPU (zero-copy
+//     reads of pinned memory), and the slot's last use becomes this step.
 // The capacity is at least T x K (every distinct selected token of a step
 // fits), so there are always enough slots not used in the step.
 #include "dsa_kernels.h"
@@ -37,11 +40,13 @@ constexpr int HC_THREADS = 256;
 constexpr int HC_WAVES = HC_THREADS / 64;
 constexpr int HC_PER = 4;                         // items per thread in the scans
 constexpr int HC_ITEMS = HC_THREADS * HC_PER;     // items per workgroup in the scans
-constexpr int HC_AGE_BINS = 65536;
-constexpr int HC_MAX_AGE = HC_AGE_BINS - 1;
+constexpr int HC_AGE_BINS = 65536;             // one 16-bit half of an age
 
-// scalars in the workspace
-enum { HS_MISSES = 0, HS_OLDER = 1, HS_AGE = 2, HS_NEED = 3, HS_EVICT = 4, HS_STEP = 5, HS_VICTIMS = 6, HS_N = 16 };
+// scalars in the workspace: misses, slots older than a*, a*, how many of age
+// a* are taken, evictions, this step, victims, the high half of a* and the
+// count of slots whose high half is above it
+enum { HS_MISSES = 0, HS_OLDER = 1, HS_AGE = 2, HS_NEED = 3, HS_EVICT = 4, HS_STEP = 5, HS_VICTIMS = 6,
+       HS_HI = 7, HS_OLDER_HI = 8, HS_N = 16 };
 
 struct HotArgs {
     Geometry g;
@@ -53,7 +58,7 @@ struct HotArgs {
     int32_t* clock;          // [1]
     int capacity, maxctx, wpr;
     uint32_t* scal;          // [HS_N]
-    uint32_t* hist;          // [HC_AGE_BINS]
+    uint32_t* hist;          // [2][HC_AGE_BINS]: high halves, then low halves within one high bucket
     uint32_t* bitmap;        // [B][wpr]
     uint32_t* wsum;          // per-workgroup word sums, then offsets
     uint32_t* csum;          // per-workgroup (older, equal) counts, then offsets
@@ -68,8 +73,11 @@ struct HotArgs {
     int32_t* counts;         // [2] misses, evictions (or null)
 };
 
-__device__ __forceinline__ int slot_age(int32_t lu, int step) {
-    return lu < 0 ? HC_MAX_AGE : max(0, min(step - lu, HC_MAX_AGE));
+// Age of a slot not used in this step: steps since its last use, minus one
+// (0 for a slot used in the previous step); a never-used slot gets `step`,
+// above every used slot's age (last uses are steps >= 1).
+__device__ __forceinline__ uint32_t slot_age(int32_t lu, int step) {
+    return lu < 0 ? (uint32_t)step : (uint32_t)(step - lu - 1);
 }
 
 // Clears the per-step scalars, age histogram and miss bitmap, and fixes this
@@ -77,7 +85,7 @@ __device__ __forceinline__ int slot_age(int32_t lu, int step) {
 __global__ __launch_bounds__(HC_THREADS) void hc_clear(HotArgs a, int64_t nwords) {
     const int64_t i = (int64_t)blockIdx.x * HC_THREADS + threadIdx.x;
     if (i < HS_N) a.scal[i] = i == HS_STEP ? (uint32_t)(*a.clock + 1) : 0u;
-    if (i < HC_AGE_BINS) a.hist[i] = 0u;
+    if (i < 2 * HC_AGE_BINS) a.hist[i] = 0u;
     if (i < nwords) a.bitmap[i] = 0u;
 }
 
@@ -109,7 +117,8 @@ __global__ __launch_bounds__(HC_THREADS) void hc_count_words(HotArgs a, int64_t 
 
 __global__ __launch_bounds__(HC_THREADS) void hc_count_slots(HotArgs a) {
     __shared__ uint32_t wsum[HC_WAVES];
-    const int step = (int)a.scal[HS_STEP], astar = (int)a.scal[HS_AGE];
+    const int step = (int)a.scal[HS_STEP];
+    const uint32_t astar = a.scal[HS_AGE];
     const int64_t s0 = (int64_t)blockIdx.x * HC_ITEMS + HC_PER * threadIdx.x;
     uint32_t older = 0, equal = 0;
 #pragma unroll
@@ -117,7 +126,7 @@ __global__ __launch_bounds__(HC_THREADS) void hc_count_slots(HotArgs a) {
         if (s0 + u >= a.capacity) break;
         const int32_t lu = a.last_use[s0 + u];
         if (lu == step) continue;
-        const int age = slot_age(lu, step);
+        const uint32_t age = slot_age(lu, step);
         older += age > astar;
         equal += age == astar;
     }
@@ -174,73 +183,102 @@ __global__ __launch_bounds__(HC_THREADS) void hc_write_misses(HotArgs a, int64_t
     }
 }
 
-// Age histogram of the slots not used in this step.  Ages below HC_LDS_AGES
-// (the recent steps, where almost every slot is) and the saturated age (every
-// never-used slot) are counted in LDS and flushed once per workgroup; the
-// other old ones go to the global histogram, one count per run of equal ages
-// among a thread's HC_RUN slots.
+// Age histogram of the slots not used in this step, one 16-bit half at a
+// time.  Level 0 counts the high halves of all their ages; level 1 counts
+// the low halves of the ages whose high half is scal[HS_HI].  The common
+// bins (high half 0 at level 0; recent ages and the never-used age at level
+// 1) are counted in LDS and flushed once per workgroup; the other ones go to
+// the global histogram, one count per run of equal bins among a thread's
+// HC_RUN slots.
 constexpr int HC_RUN = 32;
-constexpr int HC_LDS_AGES = 4096;
-__global__ __launch_bounds__(HC_THREADS) void hc_age_hist(HotArgs a) {
-    __shared__ uint32_t h[HC_LDS_AGES + 1];                   // last bin: HC_MAX_AGE
-    for (int i = threadIdx.x; i <= HC_LDS_AGES; i += HC_THREADS) h[i] = 0u;
+constexpr int HC_LDS_BINS = 4096;
+__global__ __launch_bounds__(HC_THREADS) void hc_age_hist(HotArgs a, int level) {
+    __shared__ uint32_t h[HC_LDS_BINS + 1];                   // last bin: the never-used age (level 1)
+    for (int i = threadIdx.x; i <= HC_LDS_BINS; i += HC_THREADS) h[i] = 0u;
     __syncthreads();
     const int step = (int)a.scal[HS_STEP];
+    const uint32_t hi = a.scal[HS_HI];
+    const uint32_t never = (uint32_t)step;                    // age of a never-used slot
+    const bool never_here = level == 1 && (never >> 16) == hi;
+    uint32_t* gh = a.hist + (level ? HC_AGE_BINS : 0);
     // the workgroup covers HC_THREADS * HC_RUN consecutive slots; lane-
     // consecutive loads (coalesced), each thread HC_RUN slots HC_THREADS apart
     const int64_t s0 = (int64_t)blockIdx.x * HC_THREADS * HC_RUN + threadIdx.x;
     int cur = -1;
     uint32_t n = 0;
-    for (int u = 0; u < HC_RUN && s0 + (int64_t)u * HC_THREADS < a.capacity; ++u) {
-        const int32_t lu = a.last_use[s0 + (int64_t)u * HC_THREADS];
-        if (lu == step) continue;
-        const int age = slot_age(lu, step);
-        if (age < HC_LDS_AGES || age == HC_MAX_AGE) {
-            atomicAdd(&h[age < HC_LDS_AGES ? age : HC_LDS_AGES], 1u);
-            continue;
+    for (int u = 0; u < HC_RUN; ++u) {
+        const int64_t slot = s0 + (int64_t)u * HC_THREADS;
+        bool elig = slot < a.capacity;
+        uint32_t age = 0;
+        if (elig) {
+            const int32_t lu = a.last_use[slot];
+            age = slot_age(lu, step);
+            elig = lu != step && (level == 0 || (age >> 16) == hi);
         }
-        if (age != cur) {
-            if (n) atomicAdd(&a.hist[cur], n);
-            cur = age;
+        const int bin = level ? (int)(age & 0xFFFFu) : (int)(age >> 16);
+        const bool is_never = never_here && age == never;
+        const bool in_lds = elig && (is_never || bin < HC_LDS_BINS);
+        // one LDS atomic per wave when its lanes share the bin (the usual case)
+        lds_count(h, is_never ? (uint32_t)HC_LDS_BINS : (uint32_t)min(bin, HC_LDS_BINS - 1), in_lds);
+        if (!elig || in_lds) continue;
+        if (bin != cur) {
+            if (n) atomicAdd(&gh[cur], n);
+            cur = bin;
             n = 0;
         }
         ++n;
     }
-    if (n) atomicAdd(&a.hist[cur], n);
+    if (n) atomicAdd(&gh[cur], n);
     __syncthreads();
-    for (int i = threadIdx.x; i <= HC_LDS_AGES; i += HC_THREADS)
-        if (h[i]) atomicAdd(&a.hist[i < HC_LDS_AGES ? i : HC_MAX_AGE], h[i]);
+    for (int i = threadIdx.x; i < HC_LDS_BINS; i += HC_THREADS)
+        if (h[i]) atomicAdd(&gh[i], h[i]);
+    if (threadIdx.x == 0 && h[HC_LDS_BINS]) atomicAdd(&gh[never & 0xFFFFu], h[HC_LDS_BINS]);
 }
 
-// One workgroup: the age a* of the M-th oldest eligible slot, the number of
-// eligible slots older than a*, and how many of age a* are needed.
-__global__ __launch_bounds__(HC_THREADS) void hc_pick(HotArgs a) {
+// One workgroup, per level: the bucket holding the M-th oldest eligible slot
+// (scanning from the oldest bucket down).  Level 0 records the high half and
+// the count of slots in older high buckets; level 1 completes a* = (high <<
+// 16) | low, the number of eligible slots older than a*, and how many of age
+// a* are taken.
+__global__ __launch_bounds__(HC_THREADS) void hc_pick(HotArgs a, int level) {
     __shared__ uint32_t wsum[HC_WAVES];
     constexpr int PER = HC_AGE_BINS / HC_THREADS;            // 256 bins a thread, oldest first
     const uint32_t M = a.scal[HS_MISSES];
-    // thread i owns ages [HC_MAX_AGE - PER (i + 1) + 1, HC_MAX_AGE - PER i]
+    const uint32_t* h = a.hist + (level ? HC_AGE_BINS : 0);
+    const uint32_t base = level ? a.scal[HS_OLDER_HI] : 0u;
+    // thread i owns bins [HC_AGE_BINS - PER (i + 1), HC_AGE_BINS - 1 - PER i]
     uint32_t c = 0;
-    for (int q = 0; q < PER; ++q) c += a.hist[HC_MAX_AGE - PER * threadIdx.x - q];
+    for (int q = 0; q < PER; ++q) c += h[HC_AGE_BINS - 1 - PER * threadIdx.x - q];
     uint32_t tot;
     const uint32_t ex = block_excl_scan<HC_WAVES>(c, wsum, &tot);
-    if (threadIdx.x == 0) a.scal[HS_VICTIMS] = min(M, tot);
-    if (M == 0) {
-        if (threadIdx.x == 0) { a.scal[HS_AGE] = HC_AGE_BINS; a.scal[HS_OLDER] = 0; a.scal[HS_NEED] = 0; }
+    if (level == 0 && threadIdx.x == 0) a.scal[HS_VICTIMS] = min(M, tot);
+    const uint32_t want = min(M, level ? a.scal[HS_VICTIMS] : tot);   // fewer only if the capacity contract is broken
+    if (want == 0u) {
+        if (threadIdx.x == 0) {
+            a.scal[HS_HI] = 0xFFFFu;
+            a.scal[HS_AGE] = 0xFFFFFFFFu;   // no slot is that old
+            a.scal[HS_OLDER] = 0u;
+            a.scal[HS_NEED] = 0u;
+        }
         return;
     }
-    const uint32_t want = min(M, tot);   // fewer only if the capacity contract is broken
-    if (ex < want && ex + c >= want) {
-        uint32_t cum = ex;
+    if (base + ex < want && base + ex + c >= want) {
+        uint32_t cum = base + ex;
         for (int q = 0; q < PER; ++q) {
-            const int age = HC_MAX_AGE - PER * threadIdx.x - q;
-            const uint32_t h = a.hist[age];
-            if (cum + h >= want) {
-                a.scal[HS_AGE] = (uint32_t)age;
-                a.scal[HS_OLDER] = cum;
-                a.scal[HS_NEED] = want - cum;
+            const uint32_t bin = (uint32_t)(HC_AGE_BINS - 1 - PER * threadIdx.x - q);
+            const uint32_t hb = h[bin];
+            if (cum + hb >= want) {
+                if (level == 0) {
+                    a.scal[HS_HI] = bin;
+                    a.scal[HS_OLDER_HI] = cum;
+                } else {
+                    a.scal[HS_AGE] = (a.scal[HS_HI] << 16) | bin;
+                    a.scal[HS_OLDER] = cum;
+                    a.scal[HS_NEED] = want - cum;
+                }
                 break;
             }
-            cum += h;
+            cum += hb;
         }
     }
 }
@@ -249,7 +287,8 @@ __global__ __launch_bounds__(HC_THREADS) void hc_pick(HotArgs a) {
 // `need` of age a* (slot order).
 __global__ __launch_bounds__(HC_THREADS) void hc_write_victims(HotArgs a) {
     __shared__ uint32_t wsum[HC_WAVES];
-    const int step = (int)a.scal[HS_STEP], astar = (int)a.scal[HS_AGE];
+    const int step = (int)a.scal[HS_STEP];
+    const uint32_t astar = a.scal[HS_AGE];
     const uint32_t n_older = a.scal[HS_OLDER], need = a.scal[HS_NEED];
     const int64_t s0 = (int64_t)blockIdx.x * HC_ITEMS + HC_PER * threadIdx.x;
     uint32_t fo = 0, fe = 0;   // flag bits per item
@@ -258,7 +297,7 @@ __global__ __launch_bounds__(HC_THREADS) void hc_write_victims(HotArgs a) {
         if (s0 + u >= a.capacity) break;
         const int32_t lu = a.last_use[s0 + u];
         if (lu == step) continue;
-        const int age = slot_age(lu, step);
+        const uint32_t age = slot_age(lu, step);
         fo |= (age > astar ? 1u : 0u) << u;
         fe |= (age == astar ? 1u : 0u) << u;
     }
@@ -347,7 +386,7 @@ HotLayout hot_layout(const dsa_batch* b, int k, int capacity) {
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
     l.scal = 0;
     l.hist = al(l.scal + sizeof(uint32_t) * HS_N);
-    l.bitmap = l.hist + sizeof(uint32_t) * HC_AGE_BINS;     // contiguous with hist: one clear
+    l.bitmap = l.hist + sizeof(uint32_t) * 2 * HC_AGE_BINS;   // contiguous with hist: one clear
     l.wsum = al(l.bitmap + sizeof(uint32_t) * (size_t)l.nwords);
     l.csum = al(l.wsum + sizeof(uint32_t) * ((size_t)l.nwg_words + 1));
     l.miss = al(l.csum + sizeof(uint32_t) * (2 * (size_t)l.nwg_slots + 2));
@@ -448,7 +487,7 @@ int dsa_hot_cache_fetch(const dsa_batch* b, const dsa_latent_cache* host, const 
     a.counts = counts;
 
     hipStream_t s = (hipStream_t)stream;
-    const int64_t nclear = std::max<int64_t>(HC_AGE_BINS, l.nwords);
+    const int64_t nclear = std::max<int64_t>(2 * HC_AGE_BINS, l.nwords);
     hipLaunchKernelGGL(hc_clear, dim3((unsigned)((nclear + HC_THREADS - 1) / HC_THREADS)), dim3(HC_THREADS), 0, s, a,
                        l.nwords);
     hipLaunchKernelGGL(hc_mark, dim3((k + HC_THREADS - 1) / HC_THREADS, b->total_q), dim3(HC_THREADS), 0, s, a);
@@ -456,9 +495,11 @@ int dsa_hot_cache_fetch(const dsa_batch* b, const dsa_latent_cache* host, const 
     hipLaunchKernelGGL(hc_scan, dim3(1), dim3(HC_THREADS), 0, s, a.wsum, l.nwg_words, 1, a.scal + HS_MISSES);
     hipLaunchKernelGGL(hc_write_misses, dim3(l.nwg_words), dim3(HC_THREADS), 0, s, a, l.nwords);
     const int64_t runs = ((int64_t)hot->capacity + HC_RUN - 1) / HC_RUN;
-    hipLaunchKernelGGL(hc_age_hist, dim3((unsigned)((runs + HC_THREADS - 1) / HC_THREADS)), dim3(HC_THREADS), 0, s,
-                       a);
-    hipLaunchKernelGGL(hc_pick, dim3(1), dim3(HC_THREADS), 0, s, a);
+    const dim3 hgrid((unsigned)((runs + HC_THREADS - 1) / HC_THREADS));
+    for (int level = 0; level < 2; ++level) {
+        hipLaunchKernelGGL(hc_age_hist, hgrid, dim3(HC_THREADS), 0, s, a, level);
+        hipLaunchKernelGGL(hc_pick, dim3(1), dim3(HC_THREADS), 0, s, a, level);
+    }
     hipLaunchKernelGGL(hc_count_slots, dim3(l.nwg_slots), dim3(HC_THREADS), 0, s, a);
     hipLaunchKernelGGL(hc_scan, dim3(1), dim3(HC_THREADS), 0, s, a.csum, l.nwg_slots, 2,
                        a.csum + 2 * (size_t)l.nwg_slots);

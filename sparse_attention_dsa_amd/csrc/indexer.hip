@@ -37,41 +37,14 @@ namespace dsa {
 // page_swz(t) so that the MFMA fragment reads of 16 tokens hit distinct banks.
 // Scores stay in registers until the wave's pages are done: global stores in
 // the loop would share the vector-memory counter the ring waits on.
-#ifndef IDX_DMA_DEPTH
-#define IDX_DMA_DEPTH 2
-#endif
-#ifndef IDX_DMA_PPW
-#define IDX_DMA_PPW 4
-#endif
-constexpr int DMA_DEPTH = IDX_DMA_DEPTH;     // pages in flight per wave
-constexpr int DMA_PPW = IDX_DMA_PPW;         // pages per wave per workgroup
+constexpr int DMA_DEPTH = 2;                 // pages in flight per wave
+constexpr int DMA_PPW = 4;                   // pages per wave per workgroup
 constexpr int DMA_OPS_PER_PAGE = 9;          // 8 x 1 KB of keys + 256 B of scales
-#ifndef IDX_DMA_AUX
-#define IDX_DMA_AUX 3
-#endif
-constexpr int DMA_AUX = IDX_DMA_AUX;         // cache policy of the key transfers (sc0 nt: streamed once)
+constexpr int DMA_AUX = 3;                   // cache policy of the key transfers (sc0 nt: streamed once)
 
 __device__ __forceinline__ int page_swz(int t) { return (t ^ (t >> 3)) & 7; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_n() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    else if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-    else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-    else if constexpr (N == 18) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-    else if constexpr (N == 27) asm volatile("s_waitcnt vmcnt(27)" ::: "memory");
-    else static_assert(N == 0, "unsupported vmcnt");
-}
 
 template <int NQ, int HT>
 __global__ __launch_bounds__(IDX_THREADS) void indexer_fp8_dma(IndexerArgs a, int qgroups) {
@@ -229,14 +202,8 @@ __device__ __forceinline__ void page_scores_ilp(const i32x8 (&qf)[NQ][HT], const
     for (int j = 0; j < NQ; ++j) out[j] = head_sum_transpose(part[j], lane) * ksc;
 }
 
-#ifndef IDX_PF_WAVES
-#define IDX_PF_WAVES 4
-#endif
-#ifndef IDX_PF_QW
-#define IDX_PF_QW 2
-#endif
-constexpr int PF_WAVES = IDX_PF_WAVES;
-constexpr int PF_QW = IDX_PF_QW;               // query rows per wave
+constexpr int PF_WAVES = 4;
+constexpr int PF_QW = 2;                       // query rows per wave
 constexpr int PF_QB = PF_WAVES * PF_QW;        // query rows per workgroup
 constexpr int PF_KU = 8 / PF_WAVES;            // 1 KB key units each wave moves per page
 constexpr int PF_OPS = PF_KU + 1;              // transfers per wave per page (keys, scales)
@@ -245,10 +212,7 @@ constexpr int PF_RING = 4;                     // page slots
 constexpr int PF_MIN_Q = 8;                    // longest query chunk from which it is used
 
 template <int HT>
-#ifndef IDX_PF_WPE
-#define IDX_PF_WPE 2
-#endif
-__global__ __launch_bounds__(PF_WAVES * 64) __attribute__((amdgpu_waves_per_eu(IDX_PF_WPE)))
+__global__ __launch_bounds__(PF_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void indexer_fp8_prefill(IndexerArgs a, int qblocks) {
     const Geometry& G = a.g;
     const int r = blockIdx.x / qblocks, jb = blockIdx.x % qblocks;
@@ -341,9 +305,9 @@ void indexer_fp8_prefill(IndexerArgs a, int qblocks) {
         // operations are pending: in steady state the stores of the three
         // previous pages and the transfers of the next two; before that, at
         // least the next two pages' transfers
-        if (p >= PF_RING - 1 && p + 2 < np) wait_vmcnt_n<3 * PF_QW + 2 * PF_OPS>();
-        else if (p + 2 < np) wait_vmcnt_n<2 * PF_OPS>();
-        else wait_vmcnt_n<0>();
+        if (p >= PF_RING - 1 && p + 2 < np) wait_vmcnt<3 * PF_QW + 2 * PF_OPS>();
+        else if (p + 2 < np) wait_vmcnt<2 * PF_OPS>();
+        else wait_vmcnt<0>();
         lds_barrier();   // every wave's part of page p landed; the slot of page p - 1 is free
         // the slot read and the slot refilled are passed as __restrict__
         // pointers: the compiler then knows the transfers in flight cannot
@@ -419,10 +383,7 @@ __device__ __forceinline__ void load_raw_page(const uint8_t* __restrict__ keys, 
 // arrive through the staged register ring (contiguous 1 KB loads, relaid
 // through the wave's LDS buffer); queries and weights are reloaded when a
 // wave's share crosses into the next request.
-#ifndef IDX_PER_PF
-#define IDX_PER_PF 2
-#endif
-constexpr int PER_PF = IDX_PER_PF;
+constexpr int PER_PF = 2;                  // pages in flight per wave
 constexpr int PER_MAX_ITEMS = 4096;        // (request, query group) pairs per launch
 constexpr int PER_WG_PER_CU = 2;
 
@@ -815,8 +776,11 @@ static hipError_t launch_fp8(const IndexerArgs& a, hipStream_t s, const hipEvent
 bool indexer_emit_ok(const IndexerArgs& a) {
     const int qg = (a.g.max_q_len + 1) / 2;
     const int items = a.g.B * (a.g.max_q_len >= 2 ? qg : a.g.max_q_len);
+    // batches with long query chunks take the query-blocked indexer, which
+    // writes score rows (launch_indexer + launch_topk)
     return a.key_dtype == 2 && a.dim == IDX_D && a.g.block_size == IDX_PAGE &&
-           (a.n_heads == 64 || a.n_heads == 32 || a.n_heads == 16) && items <= PER_MAX_ITEMS;
+           (a.n_heads == 64 || a.n_heads == 32 || a.n_heads == 16) && items <= PER_MAX_ITEMS &&
+           a.g.max_q_len < PF_MIN_Q;
 }
 
 hipError_t launch_sample_bound(const IndexerArgs& a, hipStream_t s) {
@@ -825,6 +789,37 @@ hipError_t launch_sample_bound(const IndexerArgs& a, hipStream_t s) {
     case 32: hipLaunchKernelGGL(indexer_sample_bound<2>, dim3(a.g.T), dim3(SB_THREADS), 0, s, a); break;
     default: hipLaunchKernelGGL(indexer_sample_bound<1>, dim3(a.g.T), dim3(SB_THREADS), 0, s, a); break;
     }
+    return hipGetLastError();
+}
+
+// -inf over the part of each score row past its visible tokens, [n_t, ld):
+// workgroup (x, t) covers an eighth of row t's tail with 16-byte stores.
+constexpr int TAIL_SPLIT = 8;
+__global__ __launch_bounds__(256) void score_tail_fill(IndexerArgs a) {
+    const int t = blockIdx.y;
+    const int n = row_visible(a.g, t);
+    const int64_t tail = a.ld - n;
+    if (tail <= 0) return;
+    float* row = a.scores + (size_t)t * a.ld;
+    const int64_t per = (tail + TAIL_SPLIT - 1) / TAIL_SPLIT;
+    const int64_t b0 = n + per * blockIdx.x, b1 = min<int64_t>(a.ld, b0 + per);
+    const float ninf = -__builtin_inff();
+    int64_t i = b0 + threadIdx.x;
+    // scalar stores up to a 16-byte boundary of the row, then float4 stores
+    const int64_t head = min<int64_t>(b1, (b0 + 3) & ~(int64_t)3);
+    if (i < head) row[i] = ninf;
+    const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0u;
+    if (aligned) {
+        for (int64_t v = head + 4 * (int64_t)threadIdx.x; v + 4 <= b1; v += 4 * 256)
+            *(f32x4*)(row + v) = (f32x4){ninf, ninf, ninf, ninf};
+        for (int64_t v = max(head, b1 & ~(int64_t)3) + threadIdx.x; v < b1; v += 256) row[v] = ninf;
+    } else {
+        for (int64_t v = head + threadIdx.x; v < b1; v += 256) row[v] = ninf;
+    }
+}
+
+hipError_t launch_score_tail(const IndexerArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(score_tail_fill, dim3(TAIL_SPLIT, a.g.T), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

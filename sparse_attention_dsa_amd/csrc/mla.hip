@@ -527,17 +527,6 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
     return r;
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Workgroup barrier that orders LDS traffic only: unlike __syncthreads() it
-// does not wait for this wave's outstanding global loads (the ring's
-// transfers in flight), which the loop accounts for with wait_vmcnt.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 template <bool SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(M_THREADS, M_THREADS), amdgpu_waves_per_eu(1, 1)))
@@ -882,9 +871,7 @@ bool mla_fast_path(int kv_dtype, int d_latent, int d_rope, int n_heads, int bloc
     return mla_path(kv_dtype, d_latent, d_rope, n_heads) != MLA_PATH_GENERIC;
 }
 
-#ifndef MLA_MIN_SLICE
-#define MLA_MIN_SLICE 128
-#endif
+constexpr int MLA_MIN_SLICE = 128;   // fewest selected tokens per split
 // Splits per query row.  Decode: enough workgroups to cover the chip, at
 // least 128 selected tokens per split; the 128-head path also keeps each
 // slice within its row-id buffer.

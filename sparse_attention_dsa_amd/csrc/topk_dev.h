@@ -83,12 +83,6 @@ __device__ __forceinline__ void wave_min_max(uint32_t& mn, uint32_t& mx) {
     mx = (uint32_t)__builtin_amdgcn_readlane((int)mx, 63);
 }
 
-// Workgroup barrier that orders LDS traffic only: unlike __syncthreads() it
-// does not wait for this wave's global loads still in flight.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 // Exclusive prefix sum over the workgroup (wsum: one slot per wave).
 template <int WAVES>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {

@@ -38,7 +38,7 @@ def score_bound(wl, t):
     the same expression on absolute values, sigma_s * sum_h |w_h| sum_d
     |q_hd k_sd|, which the oracle evaluates on the inputs' magnitudes
     (sign bit cleared in the e4m3 codes)."""
-    r, p, n = wl.query_positions()[t]
+    r, p, n = oracle.query_positions(wl)[t]
     if wl.idx_dtype == "f32":
         keys, q = np.abs(wl.idx_keys), np.abs(wl.q_idx[t])
     else:

@@ -44,17 +44,17 @@ def _batch(B_=2, T=2, maxq=1, maxctx=1000, bs=64, maxblocks=16):
 
 def test_workspace_size_host_only(L):
     b = _batch()
-    assert L.dsa_workspace_size(B.OP_TOPK, C.byref(b), 2048, 0, 0) == 0     # rows too short to need slots
+    assert L.dsa_workspace_size(B.OP_TOPK, C.byref(b), 2048, 0) == 0     # rows too short to need slots
     long_ = _batch(maxctx=100000, maxblocks=1600)
-    ws_topk = L.dsa_workspace_size(B.OP_TOPK, C.byref(long_), 2048, 0, 0)
+    ws_topk = L.dsa_workspace_size(B.OP_TOPK, C.byref(long_), 2048, 0)
     assert ws_topk >= 2 * 13 * 4096 * 8                # 13 chunks of candidate slots per row
-    assert L.dsa_workspace_size(B.OP_TOPK, C.byref(long_), 0, 0, 0) == 0
-    assert L.dsa_workspace_size(B.OP_TOPK, C.byref(long_), 5000, 0, 0) == 0
-    assert L.dsa_workspace_size(99, C.byref(b), 16, 0, 0) == 0
-    step = L.dsa_workspace_size(B.OP_DECODE_STEP, C.byref(long_), 2048, 128, 64)
+    assert L.dsa_workspace_size(B.OP_TOPK, C.byref(long_), 0, 0) == 0
+    assert L.dsa_workspace_size(B.OP_TOPK, C.byref(long_), 5000, 0) == 0
+    assert L.dsa_workspace_size(99, C.byref(b), 16, 0) == 0
+    step = L.dsa_workspace_size(B.OP_DECODE_STEP, C.byref(long_), 2048, 128)
     assert step >= 2 * 100000 * 4 + 2 * 2048 * 4 + ws_topk     # scores + indices + candidate slots
     bad = _batch(maxctx=5000)                   # 16 blocks * 64 < 5000
-    assert L.dsa_workspace_size(B.OP_TOPK, C.byref(bad), 16, 0, 0) == 0
+    assert L.dsa_workspace_size(B.OP_TOPK, C.byref(bad), 16, 0) == 0
 
 
 def test_invalid_arguments_rejected_before_device(L):

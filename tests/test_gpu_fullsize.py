@@ -22,7 +22,7 @@ def _device():
 
 
 def _structural(wl, idx):
-    for t, (r, p, n) in enumerate(wl.query_positions()):
+    for t, (r, p, n) in enumerate(oracle.query_positions(wl)):
         m = min(n, wl.topk)
         s = idx[t, :m]
         assert (s >= 0).all() and (idx[t, m:] == -1).all()

@@ -1,15 +1,19 @@
-"""GPU parity of the two-tier latent cache: after every fetch the device state
-(slot table, owners, last uses, clock, counts) equals the reference model's
-(oracle/hot_cache.py) exactly, and sparse MLA over the hot set gives the same
-output and LSE bit for bit as over the full cache."""
+"""GPU parity of the two-tier latent cache against the LRU model
+(oracle/hot_cache.py): after every fetch the misses and victims are the
+model's, the kernel's placement of misses into victims is a one-to-one map
+(the model then takes it over: the pages leave placement open), and the whole
+device state (slot table, owners, last uses, clock, counts) equals the
+model's.  Sparse MLA over the hot set matches the CPU oracle on the full
+cache, and the full-cache MLA bit for bit."""
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import sparse_attention_dsa_amd as dsa
 import workloads
 from oracle.hot_cache import HotCacheModel
-from parity import log, upload
+from parity import check_out, log, upload
 from sparse_attention_dsa_amd import binding as B
 
 pytestmark = pytest.mark.gpu
@@ -27,7 +31,7 @@ def _selections(wl, K, steps, keep, seed):
     carried over from the row's previous selection (a decode sequence whose
     selection drifts)."""
     rng = np.random.default_rng(seed)
-    pos = wl.query_positions()
+    pos = oracle.query_positions(wl)
     prev = [rng.choice(n, size=K, replace=False) for (_, _, n) in pos]
     out = []
     for _ in range(steps):
@@ -41,8 +45,22 @@ def _selections(wl, K, steps, keep, seed):
     return out
 
 
-@pytest.mark.parametrize("case,capacity_extra", [("bf16", 0), ("bf16", 300), ("e4m3", 64)])
-def test_hot_cache_matches_model_and_full_cache(case, capacity_extra):
+def _state_matches(hot, model, step):
+    slot_of = hot.slot_of.cpu().numpy()
+    want = np.full_like(slot_of, -1)
+    for (r, s), v in model.slot_of.items():
+        want[r, s] = v
+    assert np.array_equal(slot_of, want), step
+    owner = hot.owner.cpu().numpy()
+    want_owner = np.array([-1 if o is None else (o[0] << 32) | o[1] for o in model.owner], dtype=np.int64)
+    assert np.array_equal(owner, want_owner), step
+    assert hot.last_use.cpu().tolist() == model.last_use, step
+    assert int(hot.clock.item()) == model.clock
+
+
+@pytest.mark.parametrize("case,capacity_extra,jumps", [("bf16", 0, False), ("bf16", 300, False),
+                                                       ("e4m3", 64, False), ("bf16", 500, True)])
+def test_hot_cache_matches_model_and_oracle(case, capacity_extra, jumps):
     if case == "bf16":
         wl = workloads.make_workload("single_b1_l32768", batch=3, context_lens=[3000, 5000, 2000], q_len=[1, 2, 1],
                                      topk=256, seed=31)
@@ -50,7 +68,7 @@ def test_hot_cache_matches_model_and_full_cache(case, capacity_extra):
         wl = workloads.make_workload("mtp_b8_l202752", batch=3, context_lens=[3000, 5000, 2000], topk=256, seed=32)
     K, T = wl.topk, wl.total_q
     cap = T * K + capacity_extra
-    log("hot cache", case, "capacity", cap, "T", T, "K", K)
+    log("hot cache", case, "capacity", cap, "T", T, "K", K, "clock jumps", jumps)
     batch, d = upload(wl)
     host_kv = d["kv"].cpu().pin_memory()
     host_sc = d["kv_scales"].cpu().pin_memory() if d["kv_scales"] is not None else None
@@ -59,24 +77,27 @@ def test_hot_cache_matches_model_and_full_cache(case, capacity_extra):
     model = HotCacheModel(cap)
     counts = torch.zeros(2, dtype=torch.int32, device="cuda")
     ws = None
-    req = [r for (r, _, _) in wl.query_positions()]
-    for step, sel in enumerate(_selections(wl, K, steps=6, keep=0.6, seed=33)):
+    pos = oracle.query_positions(wl)
+    req = [r for (r, _, _) in pos]
+    sels = _selections(wl, K, steps=8, keep=0.6, seed=33)
+    for step, sel in enumerate(sels):
+        if jumps and step in (3, 5):
+            # ages beyond 16 bits: the clock moves 70000 steps on (the slots
+            # keep their last uses), on the device and in the model alike
+            model.clock += 70000
+            hot.clock.fill_(model.clock)
         idx = torch.from_numpy(sel).cuda()
         ws = B.hot_cache_fetch(batch, host_kv, host_sc, wl.d_latent, idx, hot, counts=counts, workspace=ws)
-        misses, victims, evicted = model.step({(req[t], int(s)) for t in range(T) for s in sel[t]})
         torch.cuda.synchronize()
-        assert counts.tolist() == [len(misses), len(evicted)], step
+        selected = {(req[t], int(s)) for t in range(T) for s in sel[t]}
+        before = set(model.slot_of)
         slot_of = hot.slot_of.cpu().numpy()
-        want = np.full_like(slot_of, -1)
-        for (r, s), v in model.slot_of.items():
-            want[r, s] = v
-        assert np.array_equal(slot_of, want), step
-        owner = hot.owner.cpu().numpy()
-        want_owner = np.array([-1 if o is None else (o[0] << 32) | o[1] for o in model.owner], dtype=np.int64)
-        assert np.array_equal(owner, want_owner), step
-        assert hot.last_use.cpu().tolist() == model.last_use, step
-        assert int(hot.clock.item()) == model.clock
-        # MLA over the hot set == MLA over the full cache, bit for bit
+        # the kernel's placement of this step's misses, checked and adopted by the model
+        assign = {(r, s): int(slot_of[r, s]) for (r, s) in selected if (r, s) not in before}
+        misses, victims, evicted = model.step(selected, assign=assign)
+        assert counts.tolist() == [len(misses), len(evicted)], step
+        _state_matches(hot, model, step)
+        # MLA over the hot set: the oracle on the full cache, and the full-cache MLA bit for bit
         lse_h = torch.empty((T, wl.mla_heads), dtype=torch.float32, device="cuda")
         lse_f = torch.empty_like(lse_h)
         out_h = dsa.sparse_mla_decode(hot.batch(batch), hot.kv, hot.scales, wl.d_latent, d["q_mla"], idx,
@@ -86,6 +107,12 @@ def test_hot_cache_matches_model_and_full_cache(case, capacity_extra):
         torch.cuda.synchronize()
         assert torch.equal(out_h, out_f), step
         assert torch.equal(lse_h, lse_f), step
+        if step in (0, len(sels) - 1):
+            oh, lh = out_h.float().cpu().numpy(), lse_h.cpu().numpy()
+            for t in range(T):
+                ref, rlse = oracle.query_mla(wl, t, sel[t])
+                check_out(oh[t], ref, fp32=False)
+                np.testing.assert_allclose(lh[t], rlse, rtol=0, atol=1e-3)
         log("  step", step + 1, "misses", len(misses), "evictions", len(evicted))
 
 

@@ -33,11 +33,14 @@ def test_indexer_scores_fp8_ragged():
     wl = _ragged()
     log("indexer fp8 ragged", wl.context_lens.tolist())
     batch, d = upload(wl)
-    sc = dsa.indexer_scores(batch, d["idx_keys"], d["idx_scales"], d["q_idx"], d["w"])
+    # a row stride past the longest row: every row has a tail of -inf
+    ld = 5000 + 200
+    sc = dsa.indexer_scores(batch, d["idx_keys"], d["idx_scales"], d["q_idx"], d["w"], ld=ld)
     torch.cuda.synchronize()
     sc = sc.cpu().numpy()
-    for t, (r, p, n) in enumerate(wl.query_positions()):
+    for t, (r, p, n) in enumerate(oracle.query_positions(wl)):
         check_scores(wl, t, sc[t, :n])
+        assert np.all(np.isneginf(sc[t, n:])), "row %d: entries past the visible tokens must be -inf" % t
 
 
 @pytest.mark.parametrize("heads,scaled", [(64, True), (32, True), (16, True), (64, False)])
@@ -54,16 +57,18 @@ def test_indexer_scores_query_blocks(heads, scaled):
     sc = dsa.indexer_scores(batch, d["idx_keys"], d["idx_scales"] if scaled else None, d["q_idx"], d["w"])
     torch.cuda.synchronize()
     sc = sc.cpu().numpy()
-    for t, (r, p, n) in enumerate(wl.query_positions()):
+    for t, (r, p, n) in enumerate(oracle.query_positions(wl)):
         check_scores(wl, t, sc[t, :n])
+        assert np.all(np.isneginf(sc[t, n:]))
 
 
 def test_indexer_scores_f32_tiny():
     wl = workloads.make_workload("tiny_fp32_l4096")
     batch, d = upload(wl)
-    sc = dsa.indexer_scores(batch, d["idx_keys"], None, d["q_idx"], d["w"]).cpu().numpy()
+    sc = dsa.indexer_scores(batch, d["idx_keys"], None, d["q_idx"], d["w"], ld=4096 + 37).cpu().numpy()
     ref = oracle.query_scores(wl, 0)
     np.testing.assert_allclose(sc[0, :4096], ref, rtol=1e-5, atol=1e-5 * np.abs(ref).max())
+    assert np.all(np.isneginf(sc[0, 4096:]))
 
 
 @pytest.mark.parametrize("dup", [False, True])
@@ -178,7 +183,7 @@ def test_decode_step_request_without_queries(q_len):
     sc = dsa.indexer_scores(batch, d["idx_keys"], d["idx_scales"], d["q_idx"], d["w"])
     torch.cuda.synchronize()
     sc = sc.cpu().numpy()
-    for t, (r, p, n) in enumerate(wl.query_positions()):
+    for t, (r, p, n) in enumerate(oracle.query_positions(wl)):
         check_scores(wl, t, sc[t, :n])
 
 
@@ -340,3 +345,31 @@ def test_decode_step_shapes(case):
     batch, d = upload(wl)
     out, lse, idx = gpu_step(wl, batch, d)
     check_step_rows(wl, list(range(wl.total_q)), out, lse, idx)
+
+
+@pytest.mark.parametrize("q_len", [1, 2])
+def test_many_requests(q_len):
+    """More than 4096 (request, query-group) items: 4200 short requests (16 to
+    300 tokens) plus a few long ones.  Standalone scores on sampled rows
+    element by element (with the -inf tail), and the whole decode step's
+    selections and outputs on sampled rows."""
+    rng = np.random.default_rng(77)
+    lens = rng.integers(16, 300, size=4200).tolist() + [3000, 9000, 14000, 20000, 2049, 2500]
+    kw = dict(batch=len(lens), context_lens=lens, q_len=q_len, seed=78)
+    if q_len == 2:   # the indexer with two query rows per item; small MLA shapes keep the arrays small
+        kw.update(mla_heads=16, d_latent=64, d_rope=16, kv_dtype="f32")
+    wl = workloads.make_workload("single_b1_l32768", **kw)
+    T = wl.total_q
+    log("many requests: B", wl.batch, "T", T, "q_len", q_len, "sum L", int(wl.context_lens.sum()))
+    batch, d = upload(wl)
+    ld = (max(lens) + 63) // 64 * 64
+    sc = dsa.indexer_scores(batch, d["idx_keys"], d["idx_scales"], d["q_idx"], d["w"], ld=ld)
+    out, lse, idx = gpu_step(wl, batch, d)
+    pos = oracle.query_positions(wl)
+    rows = sorted(set(list(range(12)) + list(range(T - 2 * 6 - 4, T)) + rng.choice(T, 24, replace=False).tolist()))
+    sc_rows = sc[rows].cpu().numpy()
+    for i, t in enumerate(rows):
+        n = pos[t][2]
+        check_scores(wl, t, sc_rows[i, :n])
+        assert np.all(np.isneginf(sc_rows[i, n:]))
+    check_step_rows(wl, rows, out, lse, idx)
