@@ -52,7 +52,8 @@ enum dsa_status {
     DSA_ERR_UNSUPPORTED = -2,   /* dtype or shape combination not implemented */
     DSA_ERR_WORKSPACE = -3,     /* workspace smaller than dsa_workspace_size() */
     DSA_ERR_DEVICE = -4,        /* current device is not gfx950 */
-    DSA_ERR_LAUNCH = -5         /* a HIP launch returned an error */
+    DSA_ERR_LAUNCH = -5,        /* a HIP launch returned an error */
+    DSA_ERR_TOO_LARGE = -6      /* batch beyond dsa_decode_step_noalloc's built-in scratch */
 };
 
 /* Storage formats.  DSA_E4M3 is the OCP e4m3fn fp8 format (max 448). */
@@ -190,6 +191,30 @@ int dsa_decode_step_timed(const dsa_batch *batch, const dsa_index_cache *index_c
                           int32_t k, float softmax_scale, void *out, float *lse, int32_t *indices_out,
                           void *workspace, size_t workspace_bytes, dsa_stream_t stream,
                           void *const *events, int32_t n_events);
+
+/*
+ * dsa_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments (minus the workspace)
+ * and the same results as dsa_decode_step.  It allocates nothing: its
+ * workspace is a scratch array of DSA_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends (its device address is
+ * looked up on the first call on each device).
+ *   A batch whose dsa_workspace_size(DSA_OP_DECODE_STEP, ...) exceeds the
+ *   scratch is rejected with DSA_ERR_TOO_LARGE before anything is launched
+ *   (128 MiB covers, e.g., 64 query rows at 128K context, K = 2048, 128 MLA
+ *   heads).  Other errors as dsa_decode_step.
+ *   All calls on one GPU share that GPU's scratch, which keeps the last
+ *   call's contents (the step initialises what it needs): calls that may
+ *   overlap on one GPU (different streams, different host threads) race and
+ *   must be ordered by the caller.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int dsa_decode_step_noalloc(const dsa_batch *batch, const dsa_index_cache *index_cache,
+                            const void *q_idx, const float *w, int32_t n_heads_idx,
+                            const dsa_latent_cache *latent_cache, const void *q_mla, int32_t n_heads,
+                            int32_t k, float softmax_scale, void *out, float *lse, int32_t *indices_out,
+                            dsa_stream_t stream);
 
 /* Workspace bytes for `op` (enum dsa_op) with this batch geometry; 0 for an
  * invalid request and for calls that need none (top-K on rows of at most

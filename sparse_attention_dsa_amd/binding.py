@@ -22,7 +22,7 @@ OP_TOPK, OP_MLA_DECODE, OP_MLA_PREFILL, OP_DECODE_STEP = 1, 2, 3, 4
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
            "dsa_decode_step", "dsa_workspace_size", "dsa_status_string", "dsa_check_device",
            "dsa_read_probe_sink_size", "dsa_read_probe", "dsa_hot_cache_reset", "dsa_hot_cache_workspace_size",
-           "dsa_hot_cache_fetch", "dsa_decode_step_timed")
+           "dsa_hot_cache_fetch", "dsa_decode_step_timed", "dsa_decode_step_noalloc")
 STEP_EVENTS = 5   # events of dsa_decode_step_timed: start, after sampling, indexer, selection, attention
 
 
@@ -80,9 +80,11 @@ def lib():
         L.dsa_hot_cache_fetch.argtypes = [P(DsaBatch), P(DsaLatentCache), vp, i32, P(DsaHotCache), vp, vp, sz, vp]
         L.dsa_decode_step_timed.argtypes = [P(DsaBatch), P(DsaIndexCache), vp, vp, i32, P(DsaLatentCache), vp, i32,
                                             i32, f32, vp, vp, vp, vp, sz, vp, P(vp), i32]
+        L.dsa_decode_step_noalloc.argtypes = [P(DsaBatch), P(DsaIndexCache), vp, vp, i32, P(DsaLatentCache), vp,
+                                              i32, i32, f32, vp, vp, vp, vp]
         for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
                      "dsa_decode_step", "dsa_check_device", "dsa_read_probe", "dsa_hot_cache_reset",
-                     "dsa_hot_cache_fetch", "dsa_decode_step_timed"):
+                     "dsa_hot_cache_fetch", "dsa_decode_step_timed", "dsa_decode_step_noalloc"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -225,6 +227,19 @@ def decode_step(batch: Batch, keys, key_scales, q_idx, w, kv, kv_scales, d_laten
         C.byref(b), C.byref(ic), _ptr(q_idx), _ptr(w), q_idx.shape[1], C.byref(lc), _ptr(q_mla),
         q_mla.shape[1], k, float(scale), _ptr(out), _ptr(lse), _ptr(indices_out), _ptr(ws), ws.numel(),
         _stream(stream)))
+    return out
+
+
+def decode_step_noalloc(batch: Batch, keys, key_scales, q_idx, w, kv, kv_scales, d_latent, q_mla, k, scale,
+                        out=None, lse=None, indices_out=None, stream=None):
+    """decode_step through the entry point that allocates nothing (its
+    workspace is the library's per-GPU scratch)."""
+    if out is None:
+        out = _out_like(kv, q_mla, d_latent)
+    b, ic, lc = batch.struct(), index_cache(keys, key_scales), latent_cache(kv, kv_scales, d_latent)
+    _check("dsa_decode_step_noalloc", lib().dsa_decode_step_noalloc(
+        C.byref(b), C.byref(ic), _ptr(q_idx), _ptr(w), q_idx.shape[1], C.byref(lc), _ptr(q_mla), q_mla.shape[1],
+        k, float(scale), _ptr(out), _ptr(lse), _ptr(indices_out), _stream(stream)))
     return out
 
 

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "dsa.h"
 #include "dsa_kernels.h"
@@ -255,6 +256,7 @@ const char* dsa_status_string(int32_t status) {
     case DSA_ERR_WORKSPACE: return "workspace too small";
     case DSA_ERR_DEVICE: return "current device is not gfx950";
     case DSA_ERR_LAUNCH: return "kernel launch failed";
+    case DSA_ERR_TOO_LARGE: return "batch needs more than the no-allocation entry point's scratch";
     default: return "unknown status";
     }
 }
@@ -401,6 +403,57 @@ int dsa_decode_step_timed(const dsa_batch* b, const dsa_index_cache* ic, const v
     }
     return decode_step(b, ic, q_idx, w, n_heads_idx, lc, q_mla, n_heads, k, scale, out, lse, indices_out, ws,
                        ws_bytes, stream, ev);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// No-allocation decode step.  Its workspace is a file-scope device array;
+// host code never passes the array's name to a kernel (in host code that
+// name is only a stand-in for the symbol): the device address of each GPU's
+// copy is looked up once per device with hipGetSymbolAddress and used
+// instead.
+static __device__ __align__(256) uint8_t scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex noalloc_mutex;
+void* noalloc_ptr[NOALLOC_MAX_DEVICES];
+
+// Device address of the current device's scratch (looked up on the first
+// call on that device, with the device current), or nullptr.
+void* noalloc_scratch() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NOALLOC_MAX_DEVICES) return nullptr;
+    std::lock_guard<std::mutex> lock(noalloc_mutex);
+    if (!noalloc_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        noalloc_ptr[dev] = p;
+    }
+    return noalloc_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_decode_step_noalloc(const dsa_batch* b, const dsa_index_cache* ic, const void* q_idx, const float* w,
+                            int32_t n_heads_idx, const dsa_latent_cache* lc, const void* q_mla, int32_t n_heads,
+                            int32_t k, float scale, void* out, float* lse, int32_t* indices_out,
+                            dsa_stream_t stream) {
+    int st = validate_indexer(b, ic, q_idx, w, n_heads_idx);
+    if (st != DSA_OK) return st;
+    if ((st = validate_mla(b, lc, q_mla, n_heads, k, out)) != DSA_OK) return st;
+    if (!topk_shape_ok(b, k)) return DSA_ERR_UNSUPPORTED;
+    const StepLayout l = step_layout(b, k, n_heads, mla_path(lc->dtype, lc->d_latent, lc->d_rope, n_heads));
+    if (l.end > DSA_NOALLOC_SCRATCH_BYTES) return DSA_ERR_TOO_LARGE;
+    if ((st = check_device_cached()) != DSA_OK) return st;
+    void* ws = noalloc_scratch();
+    if (!ws) return DSA_ERR_LAUNCH;
+    return decode_step(b, ic, q_idx, w, n_heads_idx, lc, q_mla, n_heads, k, scale, out, lse, indices_out, ws,
+                       DSA_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 }  // extern "C"

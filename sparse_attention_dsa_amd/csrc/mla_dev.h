@@ -1,0 +1,575 @@
+// Sparse MQA-mode MLA, 128-head slice (gfx950): the device code shared by the
+// standalone sparse-MLA kernels and the fused decode step.
+//
+// Per query row t and head h (SemiAnalysis GLM-5.3 article, "MLA
+// Modifications"): logits z_j = scale * q[t,h,:] . kv[s_j, 0:d+r] over the
+// selected tokens s_j, out[t,h,:] = softmax(z) . kv[s_j, 0:d]; K and V are the
+// same cached latent row, V being its first d = 512 columns.
+//
+// A workgroup of 4 waves owns one query row, 128 heads (32 per wave) and a
+// contiguous slice of the row's selection, so every selected latent row is
+// fetched once per slice and each LDS fragment read feeds 32 heads.  Tiles of
+// 32 tokens stream through a ring of LDS buffers by global_load_lds_dwordx4
+// (three tiles in flight while one is computed); the physical rows of the
+// slice are resolved through the page table once, up front.
+//   S^T = K Q^T    v_mfma_f32_32x32x16_bf16: A = 32 token rows of the tile
+//                  (LDS), B = 32 heads' queries (registers, 36 k-steps);
+//   O^T += V^T P^T  A = V^T fragments by ds_read_b64_tr_b16 from the same
+//                  rows, B = probabilities straight from S^T's accumulator
+//                  layout (token order inside each 16-token k-step permuted
+//                  alike on both sides); O^T (512 x 32 per wave) lives in the
+//                  accumulation registers.
+// e4m3 latent rows (576 codes + one fp32 scale per token) arrive in an fp8
+// staging ring and are widened exactly to bf16 in LDS (every e4m3 value is a
+// bf16 value); the token's scale multiplies its logit and its probability.
+//
+// Softmax in the exp2 domain against a fixed reference per head: the largest
+// logit of the first tile with a visible token.  Probabilities are
+// exp2(z - ref), at most 2^64 while no later logit exceeds the reference by
+// more than 64 (fp32 and bf16 hold that range; O^T = sum p v / sum p does not
+// depend on the reference), so the accumulators are never rescaled.  A slice
+// where some logit does exceed it is computed again with the largest logit
+// seen as the reference.  The logit scale enters as a positive factor: for a
+// negative scale the queries' signs are flipped when they are loaded (exact),
+// which gives the same logits.  (A zero scale takes the generic path.)
+#pragma once
+
+#include "dsa_kernels.h"
+
+namespace dsa {
+
+constexpr int M_DL = 512, M_DR = 64, M_DQK = M_DL + M_DR;
+constexpr int M_TILE = 32;                 // selected tokens per tile
+constexpr int M_ROW_BYTES = 2 * M_DQK;     // 1152: one bf16 row in LDS
+constexpr int M_ROW_UNITS = M_ROW_BYTES / 16;
+constexpr int M_TILE_BYTES = M_TILE * M_ROW_BYTES;
+constexpr int M_THREADS = 256;
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+constexpr int M3_HEADS = 128;
+constexpr int M3_NBUF = 4;                             // bf16 ring: tiles in LDS
+constexpr int M3_FP8_NBUF = 3;                         // e4m3 staging ring
+constexpr int M3_FP8_TILE = M_TILE * M_DQK;            // 18432 B of codes per tile
+constexpr int M3_MAX_SLICE = 2048;
+constexpr int M3_DMA_PER_WAVE = M_TILE_BYTES / 1024 / 4;    // 9 x 1 KB per wave per tile (bf16)
+constexpr int M3_KPF = 3;     // K fragments in flight
+constexpr int M3_VPF = 2;     // V^T fragments in flight
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_vptr;
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+
+// LDS of one slice.  The bf16 ring holds M3_NBUF tiles; an e4m3 slice uses
+// the first two as its widened tiles and the rest of the space as its
+// staging ring of codes.
+struct MlaSliceLds {
+    uint8_t ks[M3_NBUF][M_TILE_BYTES];
+    int32_t rows[M3_MAX_SLICE];                 // physical row per slot (0 for padding)
+    uint32_t tvalid[M3_MAX_SLICE / M_TILE];     // per tile: bit s = slot s holds a token
+    uint32_t redo;
+};
+static_assert(2 * M_TILE_BYTES + M3_FP8_NBUF * M3_FP8_TILE <= M3_NBUF * M_TILE_BYTES, "e4m3 staging fits");
+
+// Split partials are stored as fp16 with one power-of-two scale per (query
+// row, head, slice): the head's largest |value| times 2^k lies in
+// [2^14, 2^15), so every value keeps 11 significant bits relative to it and
+// none overflows.  The merge multiplies by 2^-k.
+__device__ __forceinline__ int part_exponent(float amax) {
+    if (!(amax > 0.f)) return 0;
+    const int e = (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 126;   // amax in [2^(e-1), 2^e)
+    return max(-100, min(100, 15 - e));
+}
+__device__ __forceinline__ float pow2i(int k) { return __uint_as_float((uint32_t)(127 + k) << 23); }
+__device__ __forceinline__ uint32_t pack_f16x2(float x, float y) {
+    const _Float16 hx = (_Float16)x, hy = (_Float16)y;
+    return (uint32_t)__builtin_bit_cast(uint16_t, hx) | ((uint32_t)__builtin_bit_cast(uint16_t, hy) << 16);
+}
+
+__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 32-bit LDS address of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// max(a, b, c) in one instruction (fmaxf would first canonicalize every
+// input it cannot prove canonical; no NaN reaches these)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// Two e4m3 codes (bytes 0 and 1 of w when hi is false, bytes 2 and 3
+// otherwise) widened to two packed bf16 values, exactly: e4m3 normals are
+// (1 + m/8) 2^(e-7), subnormals m 2^-9, all representable in bf16.
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w, bool hi) {
+    const uint32_t c0 = (w >> (hi ? 16 : 0)) & 0xFFu, c1 = (w >> (hi ? 24 : 8)) & 0xFFu;
+    return (__float_as_uint(e4m3_to_f32(c0)) >> 16) | (__float_as_uint(e4m3_to_f32(c1)) & 0xFFFF0000u);
+}
+
+// Tile layout in LDS (32 rows of 72 16-byte units, bf16): the 1 KB block
+// (r >> 3, u >> 3) sits at 1024 (9 (r >> 3) + (u >> 3)); inside it row r & 7
+// takes 128 B and holds its units u & 7 XOR-permuted by r & 7, so that one
+// unit of the block's 8 rows covers all banks:
+//   tile_off(r, u) = 1024 (9 (r >> 3) + (u >> 3)) + 16 (8 (r & 7) + ((u & 7) ^ (r & 7))).
+// bf16 rows: wave w moves rows 8w .. 8w+7; its transfer i covers units
+// 8i .. 8i+7 of each, lane l taking row 8w + (l >> 3) and unit
+// 8i + ((l & 7) ^ (l >> 3)), which the transfer writes at 16 l of the
+// instruction's 1 KB block, i.e. at tile_off.  All nine transfers of a lane
+// read the same row, so a tile costs one row id per lane.
+__device__ __forceinline__ int tile_off(int r, int u) {
+    return 1024 * (9 * (r >> 3) + (u >> 3)) + 16 * (8 * (r & 7) + ((u & 7) ^ (r & 7)));
+}
+
+// e4m3 staging layout (32 rows of 36 16-byte units of codes): transfer
+// (g, i), g = r >> 4, i = u >> 2, is 1 KB at 1024 (9 g + i), lane l of it
+// taking row 16 g + (l >> 2) and unit 4 i + (l & 3).  A lane reads one row
+// for all its transfers.
+__device__ __forceinline__ int fp8_stage_off(int r, int u) {
+    return 1024 * (9 * (r >> 4) + (u >> 2)) + 16 * (4 * (r & 15) + (u & 3));
+}
+
+// Result of a slice, per lane: element e of block cb is O^T[32 cb + 8 (e/4) +
+// 4 hh + e % 4][head] (unnormalised), with the reference m_ref (log2 domain)
+// and the row sum l_tot of the probabilities.
+struct MlaAcc {
+    f32x16 o[M_DL / 32];
+    float m_ref, l_tot;
+};
+
+// Slice [j_begin, j_begin + nslots) of query row t's selection `sel` (logical
+// positions, -1 skipped) through page-table row `pt`, heads [hbase, hbase +
+// 128).  `rows_phys`: the selection already holds physical rows.  Called by
+// all M_THREADS threads; uses L exclusively until it returns.
+template <bool FP8>
+__device__ __forceinline__ void mla_slice(const MlaArgs& a, int t, int hbase, const int32_t* sel, const int32_t* pt,
+                                          int nslots, MlaSliceLds& L, MlaAcc& acc) {
+    const Geometry& G = a.g;
+    const int ntiles = (nslots + M_TILE - 1) / M_TILE;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hh = lane >> 5, c32 = lane & 31;
+    const int head = hbase + wave * 32 + c32;
+    const uint8_t* kvb = (const uint8_t*)a.kv;
+    const float zscale = fabsf(a.scale) * LOG2E;
+    const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
+
+    // queries first (needed last), then the slice's rows: every selection
+    // index load, then every page-table load, so each waits one round trip
+    u32x4 qf[M_DQK / 16];
+    {
+        const uint16_t* qp = (const uint16_t*)a.q + ((size_t)t * a.n_heads + head) * M_DQK + 8 * hh;
+#pragma unroll
+        for (int ks = 0; ks < M_DQK / 16; ++ks) qf[ks] = *(const u32x4*)(qp + 16 * ks) ^ qsign;
+    }
+    {
+        constexpr int PER = M3_MAX_SLICE / M_THREADS;
+        const int bs = G.block_size;
+        const bool pow2 = (bs & (bs - 1)) == 0;
+        const int bsh = __builtin_ctz((unsigned)bs);
+        int sj[PER], blk[PER], slot[PER];
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int j = tid + u * M_THREADS;
+            sj[u] = j < nslots ? sel[j] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int s = max(sj[u], 0);
+            const int b = pow2 ? s >> bsh : s / bs;
+            slot[u] = s - b * bs;
+            blk[u] = sj[u] >= 0 ? pt[b] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int j = tid + u * M_THREADS;
+            const bool ok = sj[u] >= 0;
+            if (j < ntiles * M_TILE) L.rows[j] = ok ? blk[u] * bs + slot[u] : 0;
+            const unsigned long long m = __ballot(ok);   // 64 slots = two tiles
+            if (lane == 0 && j < ntiles * M_TILE) L.tvalid[j / M_TILE] = (uint32_t)m;
+            if (lane == 32 && j < ntiles * M_TILE) L.tvalid[j / M_TILE] = (uint32_t)(m >> 32);
+        }
+    }
+    __syncthreads();
+
+    // per-wave transfers of one tile (bf16: 9 x 1 KB into ring buffer b;
+    // e4m3: the wave's 4 or 5 staging transfers into staging slot b)
+    constexpr int FP8_OPS = 5;                 // staging transfers of waves 0 and 1 (waves 2, 3: 4)
+    const int dma_col = FP8 ? 16 * (lane & 3) : 16 * ((lane & 7) ^ (lane >> 3));
+    const int f8_g = wave >> 1, f8_i0 = (wave & 1) ? 5 : 0, f8_n = (wave & 1) ? 4 : 5;
+    uint8_t* const f8_stage = &L.ks[0][0] + 2 * M_TILE_BYTES;
+    auto tile_row = [&](int tile) -> int {
+        return FP8 ? L.rows[M_TILE * tile + 16 * f8_g + (lane >> 2)] : L.rows[M_TILE * tile + 8 * wave + (lane >> 3)];
+    };
+    auto issue = [&](int tile, int b) {
+        const int row = tile_row(tile);
+        if constexpr (!FP8) {
+            const uint8_t* src = kvb + (size_t)row * M_ROW_BYTES + dma_col;
+            uint8_t* dst = &L.ks[b][0] + 1024 * M3_DMA_PER_WAVE * wave;
+#pragma unroll
+            for (int i = 0; i < M3_DMA_PER_WAVE; ++i)
+                __builtin_amdgcn_global_load_lds((const void*)(src + 128 * i), (lds_vptr)(dst + 1024 * i), 16, 0, 0);
+        } else {
+            const uint8_t* src = kvb + (size_t)row * M_DQK + 64 * f8_i0 + dma_col;
+            uint8_t* dst = f8_stage + M3_FP8_TILE * b + 1024 * (9 * f8_g + f8_i0);
+#pragma unroll
+            for (int i = 0; i < FP8_OPS; ++i)
+                if (i < f8_n)
+                    __builtin_amdgcn_global_load_lds((const void*)(src + 64 * i), (lds_vptr)(dst + 1024 * i), 16, 0, 0);
+        }
+    };
+    constexpr int NRING = FP8 ? M3_FP8_NBUF : M3_NBUF;
+    // e4m3: staging slot -> widened tile (two buffers), 9 units of 8 columns a thread
+    auto widen = [&](int slot, int b) {
+        const uint8_t* st8 = f8_stage + M3_FP8_TILE * slot;
+        uint8_t* dst = &L.ks[b][0];
+#pragma unroll
+        for (int i = 0; i < M_TILE * M_ROW_UNITS / M_THREADS; ++i) {
+            const int U = tid + M_THREADS * i;
+            const int r = U / M_ROW_UNITS, u = U % M_ROW_UNITS;   // bf16 unit u = codes [8u, 8u + 8)
+            const u32x2 c = *(const u32x2*)(st8 + fp8_stage_off(r, u >> 1) + 8 * (u & 1));
+            u32x4 o;
+            o[0] = e4m3x2_to_bf16x2(c[0], false);
+            o[1] = e4m3x2_to_bf16x2(c[0], true);
+            o[2] = e4m3x2_to_bf16x2(c[1], false);
+            o[3] = e4m3x2_to_bf16x2(c[1], true);
+            *(u32x4*)(dst + tile_off(r, u)) = o;
+        }
+    };
+
+    // per-lane LDS offsets: unit 8m + e of row r is at the offset of unit e
+    // plus 1024 m, so fragment reads are few bases plus immediates
+    int qk_base[4];       // S^T A operand: row c32, unit 2ks + hh; [ks % 4], + 1024 (ks / 4)
+    {
+        const int rb = 9216 * (c32 >> 3) + 128 * (c32 & 7), sw = c32 & 7;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) qk_base[m] = rb + 16 * ((2 * m + hh) ^ sw);
+    }
+    // V^T A operand by transposing reads: in 16-lane group g4 (hh = g4 >> 1,
+    // column half 16(g4 & 1)), source lane s = 4jj + q points at token
+    // 16kk + 8rd + 4hh + jj, columns 32cb + 16(g4 & 1) + 4q .. +3 (unit
+    // 4cb + v, v = 2(g4 & 1) + (q >> 1)), and destination lane d receives
+    // column d of the half, tokens jj = 0..3.
+    int pv_base[2][2][2];   // [kk][rd][cb & 1], + 1024 (cb / 2)
+    {
+        const int s16 = lane & 15, jj = s16 >> 2, q = s16 & 3;
+        const int v = 2 * ((lane >> 4) & 1) + (q >> 1);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int rd = 0; rd < 2; ++rd) {
+                const int tok = 16 * kk + 8 * rd + 4 * hh + jj;
+#pragma unroll
+                for (int c1 = 0; c1 < 2; ++c1)
+                    pv_base[kk][rd][c1] = 9216 * (tok >> 3) + 128 * (tok & 7) + 16 * ((4 * c1 + v) ^ (tok & 7)) +
+                                          8 * (q & 1);
+            }
+    }
+
+    f32x16* oacc = acc.o;
+    float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
+
+    for (int pass = 0;; ++pass) {
+#pragma unroll
+    for (int cb = 0; cb < M_DL / 32; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[cb][i] = 0.f;
+    l_run = 0.f;
+    bool overflow = false;
+    if (tid == 0) L.redo = 0u;
+
+#pragma unroll
+    for (int b = 0; b < NRING - 1; ++b)
+        if (b < ntiles) issue(b, b);
+
+    for (int i = 0; i < ntiles; ++i) {
+        // this wave's transfers of tile i are done once at most the ones of
+        // the (up to NRING - 2) later tiles already issued are outstanding
+        const int later = min(NRING - 2, ntiles - 1 - i);
+        if constexpr (!FP8) {
+            if (later >= 2) wait_vmcnt<2 * M3_DMA_PER_WAVE>();
+            else if (later == 1) wait_vmcnt<M3_DMA_PER_WAVE>();
+            else wait_vmcnt<0>();
+        } else {
+            // waves 2 and 3 issue one transfer fewer per tile; the count
+            // below is the larger one, so those waves may also wait for part
+            // of tile i + 1 (never for less than tile i)
+            if (later >= 1) { if (f8_n == FP8_OPS) wait_vmcnt<FP8_OPS>(); else wait_vmcnt<FP8_OPS - 1>(); }
+            else wait_vmcnt<0>();
+        }
+        lds_barrier();   // everyone's part of tile i landed; tile i-1's buffer is free
+        uint8_t* Kb;
+        if constexpr (FP8) {
+            widen(i % M3_FP8_NBUF, i & 1);
+            lds_barrier();   // tile i widened
+            Kb = &L.ks[i & 1][0];
+        } else {
+            Kb = &L.ks[i % M3_NBUF][0];
+        }
+
+        const uint32_t vmask = L.tvalid[i];   // tokens present in the tile (bit per slot)
+        const bool full = vmask == 0xFFFFFFFFu;
+
+        // S^T: K fragments read M3_KPF steps ahead of their MFMA; the
+        // transfers of tile i + NRING - 1 (into the buffer tile i - 1 has
+        // left) are spread over the MFMAs, one after every fourth, so that
+        // issuing them never holds up the matrix core for long
+        f32x16 st;
+        {
+            constexpr int NK = M_DQK / 16;
+            const int nt = i + NRING - 1;
+            const bool iss = nt < ntiles;
+            const int srow = tile_row(min(nt, ntiles - 1));
+            const uint8_t* dsrc = FP8 ? kvb + (size_t)srow * M_DQK + 64 * f8_i0 + dma_col
+                                      : kvb + (size_t)srow * M_ROW_BYTES + dma_col;
+            uint8_t* ddst = FP8 ? f8_stage + M3_FP8_TILE * (nt % M3_FP8_NBUF) + 1024 * (9 * f8_g + f8_i0)
+                                : &L.ks[nt % M3_NBUF][0] + 1024 * M3_DMA_PER_WAVE * wave;
+            auto qk = [&](bool dma) {
+                u32x4 kb[M3_KPF];
+#pragma unroll
+                for (int j = 0; j < M3_KPF; ++j) kb[j] = *(const u32x4*)(Kb + qk_base[j & 3] + 1024 * (j >> 2));
+                __builtin_amdgcn_sched_group_barrier(0x100, M3_KPF, 0);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int ks = 0; ks < NK; ++ks) {
+                    if (ks == 0) st = mfma_bf16_32x32x16(as_bf16x8(kb[0]), as_bf16x8(qf[0]), f32x16{});
+                    else st = mfma_bf16_32x32x16(as_bf16x8(kb[ks % M3_KPF]), as_bf16x8(qf[ks]), st);
+                    if (ks + M3_KPF < NK) {
+                        const int kn = ks + M3_KPF;
+                        kb[ks % M3_KPF] = *(const u32x4*)(Kb + qk_base[kn & 3] + 1024 * (kn >> 2));
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // then one LDS read
+                    const int di = ks >> 2;
+                    if (dma && (ks & 3) == 1 && di < (FP8 ? FP8_OPS : M3_DMA_PER_WAVE) && (!FP8 || di < f8_n)) {
+                        // Issued by inline asm: the compiler does not track it as an
+                        // LDS write, so it puts no wait for it before the fragment
+                        // reads of tile i, which use another buffer (the loop's own
+                        // vector-memory waits count these transfers).  M0 holds the
+                        // LDS address and is restored afterwards; no immediate
+                        // offset, which the LDS destination would include as well.
+                        const uint32_t m0v = lds_addr(ddst + 1024 * di);
+                        const uint8_t* gsrc = dsrc + (FP8 ? 64 : 128) * di;
+                        uint32_t saved;
+                        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                                     "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+                                     : "=&s"(saved) : "v"(gsrc), "s"(m0v));
+                    }
+                }
+            };
+            if (iss) qk(true);
+            else qk(false);
+        }
+        // element e of this lane: token 8(e/4) + 4hh + e%4, head c32.
+        float tsc[16];
+        if constexpr (FP8) {
+            // the tokens' scales multiply their logits (and, below, their
+            // probabilities, as V rows are unscaled codes)
+            const float* ts = a.kv_scales;
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int tok = 8 * e4 + 4 * hh + e;
+                    tsc[4 * e4 + e] = ts[L.rows[M_TILE * i + tok]];
+                }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) st[e] *= tsc[e];
+        }
+        if (!full) {   // slots without a token take no part
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                st[e] = (vmask >> (8 * (e >> 2) + 4 * hh + (e & 3))) & 1u ? st[e] : -INFINITY;
+        }
+        // the tile's largest logit (zscale > 0) and the fixed reference
+        float tmax = max3f(max3f(max3f(st[0], st[1], st[2]), max3f(st[3], st[4], st[5]),
+                                 max3f(st[6], st[7], st[8])),
+                           max3f(st[9], st[10], st[11]), max3f(st[12], st[13], fmaxf(st[14], st[15])));
+        tmax *= zscale;
+        tmax = fmaxf(tmax, lane_xor32(tmax, lane));
+        m_seen = fmaxf(m_seen, tmax);
+        if (m_ref == -INFINITY) m_ref = tmax;   // first visible token of this head
+        overflow |= tmax > m_ref + 64.f;
+        // before the first visible token (m_ref = -inf in all lanes of the
+        // wave, whose heads share their tokens) every probability is 0
+        const float mre = m_ref == -INFINITY ? INFINITY : m_ref;
+        float p[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(st[e], zscale, -mre));
+        {
+            float s8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s8[e] = p[e] + p[e + 8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s8[e] += s8[e + 4];
+            l_run += (s8[0] + s8[2]) + (s8[1] + s8[3]);
+        }
+        if constexpr (FP8) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) p[e] *= tsc[e];
+        }
+        bf16x8 pb[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pb[kk][e] = (__bf16)p[8 * kk + e];
+
+        // O^T += V^T P^T: V^T fragments (two transposing reads each) read
+        // M3_VPF MFMAs ahead; the 16 accumulators rotate between dependent updates
+        {
+            constexpr int NV = 2 * (M_DL / 32);
+            auto vread = [&](int n, s16x4& v0, s16x4& v1) {
+                const int kk = n / (M_DL / 32), cb = n % (M_DL / 32);
+                v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4_ptr)(Kb + pv_base[kk][0][cb & 1] + 1024 * (cb >> 1)));
+                v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4_ptr)(Kb + pv_base[kk][1][cb & 1] + 1024 * (cb >> 1)));
+            };
+            s16x4 vb0[M3_VPF], vb1[M3_VPF];
+#pragma unroll
+            for (int j = 0; j < M3_VPF; ++j) vread(j, vb0[j], vb1[j]);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * M3_VPF, 0);
+#pragma unroll
+            for (int n = 0; n < NV; ++n) {
+                const int kk = n / (M_DL / 32), cb = n % (M_DL / 32);
+                const s16x4 v0 = vb0[n % M3_VPF], v1 = vb1[n % M3_VPF];
+                u32x4 va;
+                va[0] = (uint16_t)v0[0] | ((uint32_t)(uint16_t)v0[1] << 16);
+                va[1] = (uint16_t)v0[2] | ((uint32_t)(uint16_t)v0[3] << 16);
+                va[2] = (uint16_t)v1[0] | ((uint32_t)(uint16_t)v1[1] << 16);
+                va[3] = (uint16_t)v1[2] | ((uint32_t)(uint16_t)v1[3] << 16);
+                oacc[cb] = mfma_bf16_32x32x16(as_bf16x8(va), pb[kk], oacc[cb]);
+                if (n + M3_VPF < NV) vread(n + M3_VPF, vb0[n % M3_VPF], vb1[n % M3_VPF]);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // then its two reads
+            }
+        }
+    }
+    // the whole workgroup agrees on a second pass (it shares the barriers)
+    if (__ballot(overflow) && lane == 0) L.redo = 1u;
+    __syncthreads();
+    if (pass > 0 || L.redo == 0u) break;
+    m_ref = m_seen;
+    __syncthreads();
+    }
+    acc.m_ref = m_ref;
+    acc.l_tot = l_run + lane_xor32(l_run, lane);
+}
+
+// Normalised bf16 output and natural-log lse of a finished slice that covers
+// the whole selection.
+__device__ __forceinline__ void mla_store_final(const MlaArgs& a, int t, int head, const MlaAcc& acc) {
+    const int hh = (threadIdx.x & 63) >> 5;
+    const bool empty = acc.l_tot == 0.f;
+    const float inv = empty ? 0.f : 1.f / acc.l_tot;
+    uint16_t* op = (uint16_t*)a.out + ((size_t)t * a.n_heads + head) * M_DL;
+#pragma unroll
+    for (int cb = 0; cb < M_DL / 32; ++cb)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            u32x2 w;
+            w[0] = f32_to_bf16(acc.o[cb][4 * e4] * inv) | (f32_to_bf16(acc.o[cb][4 * e4 + 1] * inv) << 16);
+            w[1] = f32_to_bf16(acc.o[cb][4 * e4 + 2] * inv) | (f32_to_bf16(acc.o[cb][4 * e4 + 3] * inv) << 16);
+            *(u32x2*)(op + 32 * cb + 8 * e4 + 4 * hh) = w;
+        }
+    if (a.lse && hh == 0)
+        a.lse[(size_t)t * a.n_heads + head] = empty ? -INFINITY : (acc.m_ref + log2f(acc.l_tot)) * LN2;
+}
+
+// A slice's normalised partial output as fp16 with its power-of-two scale,
+// and its natural-log lse, at partial index pidx (row, head, slot).
+__device__ __forceinline__ void mla_store_partial(const MlaArgs& a, size_t pidx, const MlaAcc& acc) {
+    const int hh = (threadIdx.x & 63) >> 5;
+    const bool empty = acc.l_tot == 0.f;
+    const float inv = empty ? 0.f : 1.f / acc.l_tot;
+    const float lse_nat = empty ? -INFINITY : (acc.m_ref + log2f(acc.l_tot)) * LN2;
+    // the head's values sit in lanes c32 and c32 + 32
+    float amax = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < M_DL / 32; ++cb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(acc.o[cb][e]));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    const int k = part_exponent(amax * inv);
+    const float sc = inv * pow2i(k);
+    uint16_t* po = a.part_o + pidx * M_DL;
+#pragma unroll
+    for (int cb = 0; cb < M_DL / 32; ++cb)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            u32x2 w;
+            w[0] = pack_f16x2(acc.o[cb][4 * e4] * sc, acc.o[cb][4 * e4 + 1] * sc);
+            w[1] = pack_f16x2(acc.o[cb][4 * e4 + 2] * sc, acc.o[cb][4 * e4 + 3] * sc);
+            *(u32x2*)(po + 32 * cb + 8 * e4 + 4 * hh) = w;
+        }
+    if (hh == 0) {
+        a.part_lse[2 * pidx] = lse_nat;
+        a.part_lse[2 * pidx + 1] = pow2i(-k);
+    }
+}
+
+// The last slice of a row to finish: merges the other slices' partials
+// (indices pbase + s, s < nparts) with its own registers by their
+// log-sum-exp and writes the bf16 output and lse.
+__device__ __forceinline__ void mla_merge_final(const MlaArgs& a, int t, int head, const MlaAcc& acc, size_t pbase,
+                                                int nparts) {
+    const int hh = (threadIdx.x & 63) >> 5;
+    const bool own_empty = acc.l_tot == 0.f;
+    const float own_lse = own_empty ? -INFINITY : (acc.m_ref + log2f(acc.l_tot)) * LN2;
+    float mx = own_lse;
+    for (int s = 0; s < nparts; ++s) mx = fmaxf(mx, a.part_lse[2 * (pbase + s)]);
+    if (mx == -INFINITY) {   // no token in any slice
+        uint16_t* op = (uint16_t*)a.out + ((size_t)t * a.n_heads + head) * M_DL;
+#pragma unroll
+        for (int cb = 0; cb < M_DL / 32; ++cb)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) *(u32x2*)(op + 32 * cb + 8 * e4 + 4 * hh) = (u32x2){0u, 0u};
+        if (a.lse && hh == 0) a.lse[(size_t)t * a.n_heads + head] = -INFINITY;
+        return;
+    }
+    // own weight: e^(own_lse - mx) on the normalised own output
+    const float w_own = own_empty ? 0.f : __expf(own_lse - mx) / acc.l_tot;
+    float den = own_empty ? 0.f : __expf(own_lse - mx);
+    f32x16 o[M_DL / 32];
+#pragma unroll
+    for (int cb = 0; cb < M_DL / 32; ++cb) o[cb] = acc.o[cb] * w_own;
+    for (int s = 0; s < nparts; ++s) {
+        const size_t pidx = pbase + s;
+        const float ls = a.part_lse[2 * pidx];
+        if (ls == -INFINITY) continue;
+        const float wgt = __expf(ls - mx);
+        den += wgt;
+        const float ws = wgt * a.part_lse[2 * pidx + 1];
+        const uint16_t* po = a.part_o + pidx * M_DL;
+#pragma unroll
+        for (int cb = 0; cb < M_DL / 32; ++cb)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const u32x2 w = *(const u32x2*)(po + 32 * cb + 8 * e4 + 4 * hh);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint16_t b = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
+                    o[cb][4 * e4 + q] += ws * (float)__builtin_bit_cast(_Float16, b);
+                }
+            }
+    }
+    const float inv = 1.f / den;
+    uint16_t* op = (uint16_t*)a.out + ((size_t)t * a.n_heads + head) * M_DL;
+#pragma unroll
+    for (int cb = 0; cb < M_DL / 32; ++cb)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            u32x2 w;
+            w[0] = f32_to_bf16(o[cb][4 * e4] * inv) | (f32_to_bf16(o[cb][4 * e4 + 1] * inv) << 16);
+            w[1] = f32_to_bf16(o[cb][4 * e4 + 2] * inv) | (f32_to_bf16(o[cb][4 * e4 + 3] * inv) << 16);
+            *(u32x2*)(op + 32 * cb + 8 * e4 + 4 * hh) = w;
+        }
+    if (a.lse && hh == 0) a.lse[(size_t)t * a.n_heads + head] = mx + logf(den);
+}
+
+}  // namespace dsa

@@ -129,3 +129,16 @@ def test_valid_call_without_gpu_reports_device(L):
     assert L.dsa_hot_cache_reset(C.byref(b), C.byref(hot), None) == -4
     assert L.dsa_hot_cache_fetch(C.byref(b), C.byref(bf), 0x1, 16, C.byref(hot), None, 0x1, 1 << 30, None) == -4
     assert L.dsa_read_probe(0x100, 1024, 0x100, 1 << 20, None) == -4
+
+
+def test_noalloc_rejects_batches_beyond_its_scratch(L):
+    """The no-allocation entry point refuses a batch whose workspace would not
+    fit its built-in scratch, before touching a device."""
+    ic = B.DsaIndexCache(0x10, 0x20, B.E4M3, 128)
+    lc = B.DsaLatentCache(0x10, None, B.BF16, 512, 64)
+    huge = _batch(B_=64, T=64, maxctx=1 << 20, maxblocks=(1 << 20) // 64)
+    st = L.dsa_decode_step_noalloc(C.byref(huge), C.byref(ic), 0x1, 0x1, 64, C.byref(lc), 0x1, 128, 2048,
+                                   0.04, 0x1, None, None, None)
+    assert st == -6
+    assert L.dsa_status_string(-6).startswith(b"batch needs more than")
+    assert L.dsa_workspace_size(B.OP_DECODE_STEP, C.byref(huge), 2048, 128) > (128 << 20)
