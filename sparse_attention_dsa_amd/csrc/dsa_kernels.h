@@ -182,6 +182,7 @@ struct MlaArgs {
     void* out; float* lse;
     uint16_t* part_o;                 // split partials: fp16 [T][H][S][d], or nullptr
     float* part_lse;                  // [T][H][S][2]: lse and the partial's scale 2^-k
+    uint32_t* arrive;                 // [T * H / 128]: slices finished (128-head path)
     int splits;
 };
 

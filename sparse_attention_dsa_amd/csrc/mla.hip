@@ -27,38 +27,9 @@
 // online-softmax rescale is a per-lane scalar.  Decode rows split their
 // selection across workgroups and a second kernel merges the partial results
 // by their log-sum-exp; prefill rows have enough parallelism without it.
-#include "dsa_kernels.h"
+#include "mla_dev.h"
 
 namespace dsa {
-
-constexpr int M_DL = 512, M_DR = 64, M_DQK = M_DL + M_DR;
-constexpr int M_TILE = 32;                 // selected tokens per tile
-constexpr int M_ROW_BYTES = 2 * M_DQK;     // 1152: one bf16 row in LDS
-constexpr int M_ROW_UNITS = M_ROW_BYTES / 16;
-constexpr int M_TILE_BYTES = M_TILE * M_ROW_BYTES;
-constexpr int M_THREADS = 256;
-constexpr float LOG2E = 1.4426950408889634f;
-constexpr float LN2 = 0.6931471805599453f;
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-// Split partials are stored as fp16 with one power-of-two scale per (query
-// row, head, slice): the head's largest |value| times 2^k lies in
-// [2^14, 2^15), so every value keeps 11 significant bits relative to it and
-// none overflows.  The combine multiplies by 2^-k.
-__device__ __forceinline__ int part_exponent(float amax) {
-    if (!(amax > 0.f)) return 0;
-    const int e = (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 126;   // amax in [2^(e-1), 2^e)
-    return max(-100, min(100, 15 - e));
-}
-__device__ __forceinline__ float pow2i(int k) { return __uint_as_float((uint32_t)(127 + k) << 23); }
-__device__ __forceinline__ uint32_t pack_f16x2(float x, float y) {
-    const _Float16 hx = (_Float16)x, hy = (_Float16)y;
-    return (uint32_t)__builtin_bit_cast(uint16_t, hx) | ((uint32_t)__builtin_bit_cast(uint16_t, hy) << 16);
-}
-
-typedef __attribute__((address_space(3))) void* lds_vptr;
-typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 
 // Slot order inside a 32-token tile: k-slot 8g + j of lane group g holds token
 // slot_token(g, j); lane group g's logit accumulators hold tokens 4g..4g+3 of
@@ -481,387 +452,34 @@ __global__ __launch_bounds__(256) void mla_generic(MlaArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 128-head path (bf16 latent, d = 512, r = 64, heads a multiple of 128): a
-// workgroup owns one query row, 128 heads (32 per wave) and a slice of the
-// row's selection, so every selected latent row is fetched once per slice
-// and each LDS fragment read feeds 32 heads.  Tiles of 32 tokens stream
-// through a 4-deep ring of LDS buffers by global_load_lds_dwordx4 (three
-// tiles in flight while one is computed); the physical row ids of the whole
-// slice are resolved through the page table once, up front.
-//   S^T = K Q^T    v_mfma_f32_32x32x16_bf16: A = 32 token rows of the tile
-//                  (LDS), B = 32 heads' queries (registers, 36 k-steps);
-//   O^T += V^T P^T  A = V^T fragments by ds_read_b64_tr_b16 from the same
-//                  rows, B = probabilities straight from S^T's accumulator
-//                  layout (token order inside each 16-token k-step permuted
-//                  alike on both sides); O^T (512 x 32 per wave) lives in
-//                  accumulation registers.
-// Softmax in the exp2 domain against a fixed reference per head: the max of
-// the first tile with a visible token.  Probabilities are exp2(z - ref), at
-// most 2^64 when no later logit exceeds the reference by more than 64 (fp32
-// and bf16 hold that range, and O^T = sum p v / sum p does not depend on the
-// reference), so the 256 accumulation registers are never rescaled.  A slice
-// where some logit does exceed it is computed again with the largest logit
-// seen as the reference.
-constexpr int M3_HEADS = 128;
-constexpr int M3_NBUF = 4;
-constexpr int M3_MAX_SLICE = 2048;
-constexpr int M3_DMA_PER_WAVE = M_TILE_BYTES / 1024 / 4;    // 9 x 1 KB per wave per tile
-constexpr int M3_KPF = 4;     // K fragments in flight
-constexpr int M3_VPF = 3;     // V^T fragments in flight
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// 32-bit LDS address of a pointer into a __shared__ array
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
-}
-
-// max(a, b, c) in one instruction (fmaxf would first canonicalize every
-// input it cannot prove canonical; no NaN reaches these)
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-}
-
-
-template <bool SPLIT>
+// 128-head path (bf16 or e4m3 latent, d = 512, r = 64, heads a multiple of
+// 128): one workgroup per (query row, 128 heads, slice of the selection),
+// the slice computed by mla_slice (mla_dev.h).  With several slices per row,
+// each stores its normalised partial (fp16 with a power-of-two scale) and
+// its log-sum-exp at its slice index, and mla_combine merges them.
+template <bool FP8>
 __global__ __attribute__((amdgpu_flat_work_group_size(M_THREADS, M_THREADS), amdgpu_waves_per_eu(1, 1)))
 void mla_h128(MlaArgs a, int slice) {
     const Geometry& G = a.g;
     const int hgroups = a.n_heads / M3_HEADS;
     const int unit = blockIdx.x;
     const int t = unit / hgroups, hg = unit % hgroups;
-    const int sp = blockIdx.y;
+    const int sp = blockIdx.y, S = a.splits;
     const int j_begin = sp * slice;
     const int nslots = max(0, min(a.k, j_begin + slice) - j_begin);
-    const int ntiles = (nslots + M_TILE - 1) / M_TILE;
-
-    __shared__ __attribute__((aligned(1024))) uint8_t Ks[M3_NBUF][M_TILE_BYTES];
-    __shared__ int32_t rows[M3_MAX_SLICE];                 // physical row per slot (0 for padding)
-    __shared__ uint32_t tvalid[M3_MAX_SLICE / M_TILE];     // per tile: bit s = slot s holds a token
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int hh = lane >> 5, c32 = lane & 31;
-    const int head = hg * M3_HEADS + wave * 32 + c32;
-
-    // queries first (needed last), then the slice's rows: every selection
-    // index load, then every page-table load, so each waits one round trip
-    u32x4 qf[M_DQK / 16];
-    {
-        const uint16_t* qp = (const uint16_t*)a.q + ((size_t)t * a.n_heads + head) * M_DQK + 8 * hh;
-#pragma unroll
-        for (int ks = 0; ks < M_DQK / 16; ++ks) qf[ks] = *(const u32x4*)(qp + 16 * ks);
-    }
-    {
-        constexpr int PER = M3_MAX_SLICE / M_THREADS;
-        const int r = row_request(G, t);
-        const int32_t* sel = a.indices + (size_t)t * a.k + j_begin;
-        const int32_t* pt = G.page_table + (size_t)r * G.max_blocks;
-        const int bs = G.block_size;
-        const bool pow2 = (bs & (bs - 1)) == 0;
-        const int bsh = __builtin_ctz((unsigned)bs);
-        int sj[PER], blk[PER], slot[PER];
-#pragma unroll
-        for (int u = 0; u < PER; ++u) {
-            const int j = tid + u * M_THREADS;
-            sj[u] = j < nslots ? sel[j] : -1;
-        }
-#pragma unroll
-        for (int u = 0; u < PER; ++u) {
-            const int s = max(sj[u], 0);
-            const int b = pow2 ? s >> bsh : s / bs;
-            slot[u] = s - b * bs;
-            blk[u] = sj[u] >= 0 ? pt[b] : 0;
-        }
-#pragma unroll
-        for (int u = 0; u < PER; ++u) {
-            const int j = tid + u * M_THREADS;
-            const bool ok = sj[u] >= 0;
-            if (j < ntiles * M_TILE) rows[j] = ok ? blk[u] * bs + slot[u] : 0;
-            const unsigned long long m = __ballot(ok);   // 64 slots = two tiles
-            if (lane == 0 && j < ntiles * M_TILE) tvalid[j / M_TILE] = (uint32_t)m;
-            if (lane == 32 && j < ntiles * M_TILE) tvalid[j / M_TILE] = (uint32_t)(m >> 32);
-        }
-    }
-    __syncthreads();
-
-    // Tile layout in LDS (32 rows of 72 16-byte units): the 1 KB block
-    // (r >> 3, u >> 3) sits at 1024 (9 (r >> 3) + (u >> 3)); inside it row
-    // r & 7 takes 128 B and holds its units u & 7 XOR-permuted by r & 7, so
-    // that one unit of the block's 8 rows covers all banks:
-    //   tile_off(r, u) = 1024 (9 (r >> 3) + (u >> 3)) + 16 (8 (r & 7) + ((u & 7) ^ (r & 7))).
-    // Wave w moves rows 8w .. 8w+7: its instruction i covers units 8i .. 8i+7
-    // of each, lane l taking row 8w + (l >> 3) and unit 8i + ((l & 7) ^ (l >> 3)),
-    // which the transfer writes at 16 l of the instruction's 1 KB block, i.e.
-    // at tile_off.  All nine instructions of a lane read the same row, so a
-    // tile costs one row id per lane and immediate offsets.
-    static_assert(M_TILE == 32 && M_THREADS == 256 && M_ROW_UNITS == 72 && M3_DMA_PER_WAVE == 9,
-                  "tile layout: 4 waves x 8 rows, 9 blocks of 8 units per row");
-    const int dma_col = 16 * ((lane & 7) ^ (lane >> 3));
-    auto issue = [&](int tile, int b) {
-        const int row = rows[M_TILE * tile + 8 * wave + (lane >> 3)];
-        const uint8_t* src = (const uint8_t*)a.kv + (size_t)row * M_ROW_BYTES + dma_col;
-        uint8_t* dst = &Ks[b][0] + 1024 * M3_DMA_PER_WAVE * wave;
-#pragma unroll
-        for (int i = 0; i < M3_DMA_PER_WAVE; ++i)
-            __builtin_amdgcn_global_load_lds((const void*)(src + 128 * i), (lds_vptr)(dst + 1024 * i), 16, 0, 0);
-    };
-
-    // per-lane LDS offsets: unit 8m + e of row r is at the offset of unit e
-    // plus 1024 m, so fragment reads are few bases plus immediates
-    int qk_base[4];       // S^T A operand: row c32, unit 2ks + hh; [ks % 4], + 1024 (ks / 4)
-    {
-        const int rb = 9216 * (c32 >> 3) + 128 * (c32 & 7), sw = c32 & 7;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) qk_base[m] = rb + 16 * ((2 * m + hh) ^ sw);
-    }
-    // V^T A operand by transposing reads: in 16-lane group g4 (hh = g4 >> 1,
-    // column half 16(g4 & 1)), source lane s = 4jj + q points at token
-    // 16kk + 8rd + 4hh + jj, columns 32cb + 16(g4 & 1) + 4q .. +3 (unit
-    // 4cb + v, v = 2(g4 & 1) + (q >> 1)), and destination lane d receives
-    // column d of the half, tokens jj = 0..3.
-    int pv_base[2][2][2];   // [kk][rd][cb & 1], + 1024 (cb / 2)
-    {
-        const int s16 = lane & 15, jj = s16 >> 2, q = s16 & 3;
-        const int v = 2 * ((lane >> 4) & 1) + (q >> 1);
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int rd = 0; rd < 2; ++rd) {
-                const int tok = 16 * kk + 8 * rd + 4 * hh + jj;
-#pragma unroll
-                for (int c1 = 0; c1 < 2; ++c1)
-                    pv_base[kk][rd][c1] = 9216 * (tok >> 3) + 128 * (tok & 7) + 16 * ((4 * c1 + v) ^ (tok & 7)) +
-                                          8 * (q & 1);
-            }
-    }
-
-    __shared__ uint32_t redo;
-    f32x16 oacc[M_DL / 32];
-    float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
-    const float zscale = a.scale * LOG2E;
-
-    for (int pass = 0;; ++pass) {
-#pragma unroll
-    for (int cb = 0; cb < M_DL / 32; ++cb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[cb][i] = 0.f;
-    l_run = 0.f;
-    bool overflow = false;
-    if (tid == 0) redo = 0u;
-
-#pragma unroll
-    for (int b = 0; b < M3_NBUF - 1; ++b)
-        if (b < ntiles) issue(b, b);
-
-    for (int i = 0; i < ntiles; ++i) {
-        // this wave's transfers of tile i are done once at most the ones of
-        // the (up to two) later tiles already issued are outstanding
-        const int later = min(M3_NBUF - 2, ntiles - 1 - i);
-        if (later >= 2) wait_vmcnt<2 * M3_DMA_PER_WAVE>();
-        else if (later == 1) wait_vmcnt<M3_DMA_PER_WAVE>();
-        else wait_vmcnt<0>();
-        lds_barrier();   // everyone's part of tile i landed; tile i-1's buffer is free
-        const uint8_t* Kb = &Ks[i % M3_NBUF][0];
-
-        const uint32_t vmask = tvalid[i];   // tokens present in the tile (bit per slot)
-
-        // S^T: K fragments read M3_KPF steps ahead of their MFMA; the nine
-        // transfers of tile i+3 (into the buffer tile i-1 has left) are
-        // spread over the MFMAs, one after every fourth, so that issuing them
-        // never holds up the matrix core for long
-        f32x16 st;
-        {
-            constexpr int NK = M_DQK / 16;
-            const int nt = i + M3_NBUF - 1;
-            const bool iss = nt < ntiles;
-            const uint8_t* dsrc = (const uint8_t*)a.kv +
-                                  (size_t)rows[M_TILE * min(nt, ntiles - 1) + 8 * wave + (lane >> 3)] * M_ROW_BYTES +
-                                  dma_col;
-            auto qk = [&](const uint8_t* kbuf, uint8_t* dst, bool dma) {
-                u32x4 kb[M3_KPF];
-#pragma unroll
-                for (int j = 0; j < M3_KPF; ++j) kb[j] = *(const u32x4*)(kbuf + qk_base[j & 3] + 1024 * (j >> 2));
-                __builtin_amdgcn_sched_group_barrier(0x100, M3_KPF, 0);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int ks = 0; ks < NK; ++ks) {
-                    if (ks == 0) st = mfma_bf16_32x32x16(as_bf16x8(kb[0]), as_bf16x8(qf[0]), f32x16{});
-                    else st = mfma_bf16_32x32x16(as_bf16x8(kb[ks % M3_KPF]), as_bf16x8(qf[ks]), st);
-                    if (ks + M3_KPF < NK) {
-                        const int kn = ks + M3_KPF;
-                        kb[ks % M3_KPF] = *(const u32x4*)(kbuf + qk_base[kn & 3] + 1024 * (kn >> 2));
-                    }
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // then one LDS read
-                    if (dma && (ks & 3) == 1) {
-                        // Issued by inline asm: the compiler does not track it as an
-                        // LDS write, so it puts no wait for it before the fragment
-                        // reads of tile i, which use another buffer (the loop's own
-                        // vector-memory waits count these transfers).  M0 holds the
-                        // LDS address and is restored afterwards; no immediate
-                        // offset, which the LDS destination would include as well.
-                        const uint32_t m0v = lds_addr(dst + 1024 * (ks >> 2));
-                        const uint8_t* gsrc = dsrc + 128 * (ks >> 2);
-                        uint32_t saved;
-                        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
-                                     "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
-                                     : "=&s"(saved) : "v"(gsrc), "s"(m0v));
-                    }
-                }
-            };
-            uint8_t* ddst = &Ks[nt % M3_NBUF][0] + 1024 * M3_DMA_PER_WAVE * wave;
-            if (iss) qk(Kb, ddst, true);
-            else qk(Kb, ddst, false);
-        }
-        // element e of this lane: token 8(e/4) + 4hh + e%4, head c32.
-        // The tile's largest logit comes from the raw scores' extreme in the
-        // direction of the scale's sign, slots without a token excluded (the
-        // tiles with padding only); probabilities are exp2(s * zscale - ref)
-        // by one fused multiply-add, zero for those slots.
-        const bool full = vmask == 0xFFFFFFFFu;
-        float ext;
-        if (zscale >= 0.f) {
-            float sm[16];
-#pragma unroll
-            for (int e = 0; e < 16; ++e) sm[e] = st[e];
-            if (!full) {
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    sm[e] = (vmask >> (8 * (e >> 2) + 4 * hh + (e & 3))) & 1u ? sm[e] : -INFINITY;
-            }
-            ext = fmaxf(max3f(max3f(sm[0], sm[1], sm[2]), max3f(sm[3], sm[4], sm[5]), max3f(sm[6], sm[7], sm[8])),
-                        max3f(max3f(sm[9], sm[10], sm[11]), max3f(sm[12], sm[13], sm[14]), sm[15]));
-        } else {
-            ext = INFINITY;
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                if (full || ((vmask >> (8 * (e >> 2) + 4 * hh + (e & 3))) & 1u)) ext = fminf(ext, st[e]);
-        }
-        float tmax = vmask ? ext * zscale : -INFINITY;
-        tmax = fmaxf(tmax, lane_xor32(tmax, lane));
-        m_seen = fmaxf(m_seen, tmax);
-        if (m_ref == -INFINITY) m_ref = tmax;   // first visible token of this head
-        overflow |= tmax > m_ref + 64.f;
-        // before the first visible token (m_ref = -inf in all lanes of the
-        // wave, whose heads share their tokens) every probability is 0
-        const float mre = m_ref == -INFINITY ? INFINITY : m_ref;
-        float p[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(st[e], zscale, -mre));
-        if (!full) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                p[e] = (vmask >> (8 * (e >> 2) + 4 * hh + (e & 3))) & 1u ? p[e] : 0.f;
-        }
-        {
-            float s8[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s8[e] = p[e] + p[e + 8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) s8[e] += s8[e + 4];
-            l_run += (s8[0] + s8[2]) + (s8[1] + s8[3]);
-        }
-        bf16x8 pb[2];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pb[kk][e] = (__bf16)p[8 * kk + e];
-
-        // O^T += V^T P^T: V^T fragments (two transposing reads each) read
-        // M3_VPF MFMAs ahead; the 16 accumulators rotate between dependent updates
-        {
-            constexpr int NV = 2 * (M_DL / 32);
-            auto vread = [&](int n, s16x4& v0, s16x4& v1) {
-                const int kk = n / (M_DL / 32), cb = n % (M_DL / 32);
-                v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4_ptr)(Kb + pv_base[kk][0][cb & 1] + 1024 * (cb >> 1)));
-                v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4_ptr)(Kb + pv_base[kk][1][cb & 1] + 1024 * (cb >> 1)));
-            };
-            s16x4 vb0[M3_VPF], vb1[M3_VPF];
-#pragma unroll
-            for (int j = 0; j < M3_VPF; ++j) vread(j, vb0[j], vb1[j]);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * M3_VPF, 0);
-#pragma unroll
-            for (int n = 0; n < NV; ++n) {
-                const int kk = n / (M_DL / 32), cb = n % (M_DL / 32);
-                const s16x4 v0 = vb0[n % M3_VPF], v1 = vb1[n % M3_VPF];
-                u32x4 va;
-                va[0] = (uint16_t)v0[0] | ((uint32_t)(uint16_t)v0[1] << 16);
-                va[1] = (uint16_t)v0[2] | ((uint32_t)(uint16_t)v0[3] << 16);
-                va[2] = (uint16_t)v1[0] | ((uint32_t)(uint16_t)v1[1] << 16);
-                va[3] = (uint16_t)v1[2] | ((uint32_t)(uint16_t)v1[3] << 16);
-                oacc[cb] = mfma_bf16_32x32x16(as_bf16x8(va), pb[kk], oacc[cb]);
-                if (n + M3_VPF < NV) vread(n + M3_VPF, vb0[n % M3_VPF], vb1[n % M3_VPF]);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // then its two reads
-            }
-        }
-    }
-    // the whole workgroup agrees on a second pass (it shares the barriers)
-    if (__ballot(overflow) && lane == 0) redo = 1u;
-    __syncthreads();
-    if (pass > 0 || redo == 0u) break;
-    m_ref = m_seen;
-    __syncthreads();
-    }
-    const float m_run = m_ref;
-
-    // ---- epilogue: element e of block cb is O^T[32cb + 8(e/4) + 4hh + e%4][head]
-    const float l_tot = l_run + lane_xor32(l_run, lane);
-    const bool empty = l_tot == 0.f;
-    const float inv = empty ? 0.f : 1.f / l_tot;
-    const float lse_nat = empty ? -INFINITY : (m_run + log2f(l_tot)) * LN2;
-    if (SPLIT) {
-        // the head's values sit in lanes c32 and c32 + 32
-        float amax = 0.f;
-#pragma unroll
-        for (int cb = 0; cb < M_DL / 32; ++cb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(oacc[cb][e]));
-        amax = fmaxf(amax, __shfl_xor(amax, 32));
-        const int k = part_exponent(amax * inv);
-        const float sc = inv * pow2i(k);
-        const size_t pidx = ((size_t)t * a.n_heads + head) * a.splits + sp;
-        uint16_t* po = a.part_o + pidx * M_DL;
-#pragma unroll
-        for (int cb = 0; cb < M_DL / 32; ++cb)
-#pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) {
-                u32x2 w;
-                w[0] = pack_f16x2(oacc[cb][4 * e4] * sc, oacc[cb][4 * e4 + 1] * sc);
-                w[1] = pack_f16x2(oacc[cb][4 * e4 + 2] * sc, oacc[cb][4 * e4 + 3] * sc);
-                *(u32x2*)(po + 32 * cb + 8 * e4 + 4 * hh) = w;
-            }
-        if (hh == 0) {
-            a.part_lse[2 * pidx] = lse_nat;
-            a.part_lse[2 * pidx + 1] = pow2i(-k);
-        }
-    } else {
-        uint16_t* op = (uint16_t*)a.out + ((size_t)t * a.n_heads + head) * M_DL;
-#pragma unroll
-        for (int cb = 0; cb < M_DL / 32; ++cb)
-#pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) {
-                u32x2 w;
-                w[0] = f32_to_bf16(oacc[cb][4 * e4] * inv) | (f32_to_bf16(oacc[cb][4 * e4 + 1] * inv) << 16);
-                w[1] = f32_to_bf16(oacc[cb][4 * e4 + 2] * inv) | (f32_to_bf16(oacc[cb][4 * e4 + 3] * inv) << 16);
-                *(u32x2*)(op + 32 * cb + 8 * e4 + 4 * hh) = w;
-            }
-        if (a.lse && hh == 0) a.lse[(size_t)t * a.n_heads + head] = lse_nat;
-    }
+    __shared__ MlaSliceLds L;
+    const int r = row_request(G, t);
+    MlaAcc acc;
+    mla_slice<FP8>(a, t, hg * M3_HEADS, a.indices + (size_t)t * a.k + j_begin,
+                   G.page_table + (size_t)r * G.max_blocks, nslots, L, acc);
+    if (S == 1) mla_store_final(a, t, hg * M3_HEADS, acc, L);
+    else mla_store_partial(a, t, hg * M3_HEADS, sp, acc, L);
 }
 
 // Which kernel serves an MLA call.
 int mla_path(int kv_dtype, int d_latent, int d_rope, int n_heads) {
     if (d_latent != M_DL || d_rope != M_DR) return MLA_PATH_GENERIC;
-    if (kv_dtype == 1 && n_heads % M3_HEADS == 0) return MLA_PATH_H128;
+    if ((kv_dtype == 1 || kv_dtype == 2) && n_heads % M3_HEADS == 0) return MLA_PATH_H128;
     if ((kv_dtype == 1 || kv_dtype == 2) && n_heads % MLA_HEADS_PER_WG == 0) return MLA_PATH_H64;
     return MLA_PATH_GENERIC;
 }
@@ -888,22 +506,23 @@ int mla_splits(int path, int T, int n_heads, int k, bool prefill) {
 }
 
 hipError_t launch_mla(const MlaArgs& a, bool prefill, hipStream_t s) {
-    const int path = mla_path(a.kv_dtype, a.d_latent, a.d_rope, a.n_heads);
+    // a zero logit scale takes the generic kernel (the 128-head tile folds
+    // the scale's sign into the queries and needs it nonzero)
+    const int path = a.scale == 0.f ? MLA_PATH_GENERIC : mla_path(a.kv_dtype, a.d_latent, a.d_rope, a.n_heads);
     if (path == MLA_PATH_H128) {
         const int S = a.splits;
         int slice = (a.k + S - 1) / S;
         slice = (slice + M_TILE - 1) / M_TILE * M_TILE;
         if (slice > M3_MAX_SLICE) return hipErrorInvalidValue;
         const dim3 grid(a.g.T * (a.n_heads / M3_HEADS), S);
-        if (S > 1) {
-            hipLaunchKernelGGL(mla_h128<true>, grid, dim3(M_THREADS), 0, s, a, slice);
-            const hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
+        if (a.kv_dtype == 2) hipLaunchKernelGGL(mla_h128<true>, grid, dim3(M_THREADS), 0, s, a, slice);
+        else hipLaunchKernelGGL(mla_h128<false>, grid, dim3(M_THREADS), 0, s, a, slice);
+        hipError_t e = hipGetLastError();
+        if (e == hipSuccess && S > 1) {
             hipLaunchKernelGGL(mla_combine, dim3((a.g.T * a.n_heads + 3) / 4), dim3(256), 0, s, a);
-        } else {
-            hipLaunchKernelGGL(mla_h128<false>, grid, dim3(M_THREADS), 0, s, a, slice);
+            e = hipGetLastError();
         }
-        return hipGetLastError();
+        return e;
     }
     if (path == MLA_PATH_H64) {
         const int hgroups = a.n_heads / MLA_HEADS_PER_WG;
@@ -925,6 +544,7 @@ hipError_t launch_mla(const MlaArgs& a, bool prefill, hipStream_t s) {
         }
         return hipGetLastError();
     }
+    if (path != MLA_PATH_GENERIC) return hipErrorInvalidValue;
     const size_t shm = sizeof(int64_t) * (size_t)a.k + sizeof(float) * ((size_t)a.d_latent + a.d_rope + a.k);
     hipLaunchKernelGGL(mla_generic, dim3(a.g.T * a.n_heads), dim3(256), shm, s, a);
     return hipGetLastError();

@@ -68,6 +68,7 @@ struct MlaSliceLds {
     uint8_t ks[M3_NBUF][M_TILE_BYTES];
     int32_t rows[M3_MAX_SLICE];                 // physical row per slot (0 for padding)
     uint32_t tvalid[M3_MAX_SLICE / M_TILE];     // per tile: bit s = slot s holds a token
+    float tscale[M3_FP8_NBUF][2 * M_TILE];      // e4m3: the staged tiles' token scales (twice)
     uint32_t redo;
 };
 static_assert(2 * M_TILE_BYTES + M3_FP8_NBUF * M3_FP8_TILE <= M3_NBUF * M_TILE_BYTES, "e4m3 staging fits");
@@ -82,9 +83,17 @@ __device__ __forceinline__ int part_exponent(float amax) {
     return max(-100, min(100, 15 - e));
 }
 __device__ __forceinline__ float pow2i(int k) { return __uint_as_float((uint32_t)(127 + k) << 23); }
+// Two floats to packed fp16, round to nearest even (one instruction).
 __device__ __forceinline__ uint32_t pack_f16x2(float x, float y) {
-    const _Float16 hx = (_Float16)x, hy = (_Float16)y;
-    return (uint32_t)__builtin_bit_cast(uint16_t, hx) | ((uint32_t)__builtin_bit_cast(uint16_t, hy) << 16);
+    typedef _Float16 f16x2_v __attribute__((ext_vector_type(2)));
+    const f16x2_v v = {(_Float16)x, (_Float16)y};
+    return __builtin_bit_cast(uint32_t, v);
+}
+// Two finite floats to packed bf16, round to nearest even (one instruction).
+__device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
+    typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+    const bf16x2_v v = {(__bf16)x, (__bf16)y};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ f32x16 mfma_bf16_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -105,17 +114,21 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 }
 
 // Two e4m3 codes (bytes 0 and 1 of w when hi is false, bytes 2 and 3
-// otherwise) widened to two packed bf16 values, exactly: e4m3 normals are
-// (1 + m/8) 2^(e-7), subnormals m 2^-9, all representable in bf16.
+// otherwise) widened to two packed bf16 values by the hardware conversion
+// with a unit scale, exactly: e4m3 normals are (1 + m/8) 2^(e-7), subnormals
+// m 2^-9, all representable in bf16.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w, bool hi) {
-    const uint32_t c0 = (w >> (hi ? 16 : 0)) & 0xFFu, c1 = (w >> (hi ? 24 : 8)) & 0xFFu;
-    return (__float_as_uint(e4m3_to_f32(c0)) >> 16) | (__float_as_uint(e4m3_to_f32(c1)) & 0xFFFF0000u);
+    const bf16x2_t v = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                          : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // Tile layout in LDS (32 rows of 72 16-byte units, bf16): the 1 KB block
 // (r >> 3, u >> 3) sits at 1024 (9 (r >> 3) + (u >> 3)); inside it row r & 7
 // takes 128 B and holds its units u & 7 XOR-permuted by r & 7, so that one
-// unit of the block's 8 rows covers all banks:
+// unit of the block's 8 rows covers all banks (the S^T fragment reads run
+// at the full LDS rate):
 //   tile_off(r, u) = 1024 (9 (r >> 3) + (u >> 3)) + 16 (8 (r & 7) + ((u & 7) ^ (r & 7))).
 // bf16 rows: wave w moves rows 8w .. 8w+7; its transfer i covers units
 // 8i .. 8i+7 of each, lane l taking row 8w + (l >> 3) and unit
@@ -159,14 +172,10 @@ __device__ __forceinline__ void mla_slice(const MlaArgs& a, int t, int hbase, co
     const float zscale = fabsf(a.scale) * LOG2E;
     const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
 
-    // queries first (needed last), then the slice's rows: every selection
-    // index load, then every page-table load, so each waits one round trip
-    u32x4 qf[M_DQK / 16];
-    {
-        const uint16_t* qp = (const uint16_t*)a.q + ((size_t)t * a.n_heads + head) * M_DQK + 8 * hh;
-#pragma unroll
-        for (int ks = 0; ks < M_DQK / 16; ++ks) qf[ks] = *(const u32x4*)(qp + 16 * ks) ^ qsign;
-    }
+    // the slice's rows first (every selection index load, then every
+    // page-table load, so each waits one round trip); the queries are loaded
+    // after the ring's first transfers are issued, so that waiting for them
+    // never delays the row chain
     {
         constexpr int PER = M3_MAX_SLICE / M_THREADS;
         const int bs = G.block_size;
@@ -198,14 +207,19 @@ __device__ __forceinline__ void mla_slice(const MlaArgs& a, int t, int hbase, co
     __syncthreads();
 
     // per-wave transfers of one tile (bf16: 9 x 1 KB into ring buffer b;
-    // e4m3: the wave's 4 or 5 staging transfers into staging slot b)
-    constexpr int FP8_OPS = 5;                 // staging transfers of waves 0 and 1 (waves 2, 3: 4)
+    // e4m3: the wave's 5 or 4 staging transfers into staging slot b, and for
+    // wave 1 a fifth: the tile's 32 token scales, 4 B per lane, lanes 32..63
+    // repeating lanes 0..31)
+    constexpr int FP8_OPS = 5;                 // transfers of waves 0, 1 and 2 (wave 3: 4)
     const int dma_col = FP8 ? 16 * (lane & 3) : 16 * ((lane & 7) ^ (lane >> 3));
     const int f8_g = wave >> 1, f8_i0 = (wave & 1) ? 5 : 0, f8_n = (wave & 1) ? 4 : 5;
+    const bool f8_sc = wave == 1;
+    const int f8_ops = f8_n + (f8_sc ? 1 : 0);
     uint8_t* const f8_stage = &L.ks[0][0] + 2 * M_TILE_BYTES;
     auto tile_row = [&](int tile) -> int {
         return FP8 ? L.rows[M_TILE * tile + 16 * f8_g + (lane >> 2)] : L.rows[M_TILE * tile + 8 * wave + (lane >> 3)];
     };
+    auto scale_src = [&](int tile) -> const float* { return a.kv_scales + L.rows[M_TILE * tile + (lane & 31)]; };
     auto issue = [&](int tile, int b) {
         const int row = tile_row(tile);
         if constexpr (!FP8) {
@@ -221,6 +235,8 @@ __device__ __forceinline__ void mla_slice(const MlaArgs& a, int t, int hbase, co
             for (int i = 0; i < FP8_OPS; ++i)
                 if (i < f8_n)
                     __builtin_amdgcn_global_load_lds((const void*)(src + 64 * i), (lds_vptr)(dst + 1024 * i), 16, 0, 0);
+            if (f8_sc)
+                __builtin_amdgcn_global_load_lds((const void*)scale_src(tile), (lds_vptr)&L.tscale[b][0], 4, 0, 0);
         }
     };
     constexpr int NRING = FP8 ? M3_FP8_NBUF : M3_NBUF;
@@ -266,13 +282,14 @@ __device__ __forceinline__ void mla_slice(const MlaArgs& a, int t, int hbase, co
                 const int tok = 16 * kk + 8 * rd + 4 * hh + jj;
 #pragma unroll
                 for (int c1 = 0; c1 < 2; ++c1)
-                    pv_base[kk][rd][c1] = 9216 * (tok >> 3) + 128 * (tok & 7) + 16 * ((4 * c1 + v) ^ (tok & 7)) +
-                                          8 * (q & 1);
+                    pv_base[kk][rd][c1] = 9216 * (tok >> 3) + 128 * (tok & 7) +
+                                          16 * ((4 * c1 + v) ^ (tok & 7)) + 8 * (q & 1);
             }
     }
 
     f32x16* oacc = acc.o;
     float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
+    u32x4 qf[M_DQK / 16];   // B operand of S^T = K Q^T, one 16-byte fragment per 16-wide k step
 
     for (int pass = 0;; ++pass) {
 #pragma unroll
@@ -286,6 +303,11 @@ __device__ __forceinline__ void mla_slice(const MlaArgs& a, int t, int hbase, co
 #pragma unroll
     for (int b = 0; b < NRING - 1; ++b)
         if (b < ntiles) issue(b, b);
+    if (pass == 0) {
+        const uint16_t* qp = (const uint16_t*)a.q + ((size_t)t * a.n_heads + head) * M_DQK + 8 * hh;
+#pragma unroll
+        for (int ks = 0; ks < M_DQK / 16; ++ks) qf[ks] = *(const u32x4*)(qp + 16 * ks) ^ qsign;
+    }
 
     for (int i = 0; i < ntiles; ++i) {
         // this wave's transfers of tile i are done once at most the ones of
@@ -296,10 +318,7 @@ __device__ __forceinline__ void mla_slice(const MlaArgs& a, int t, int hbase, co
             else if (later == 1) wait_vmcnt<M3_DMA_PER_WAVE>();
             else wait_vmcnt<0>();
         } else {
-            // waves 2 and 3 issue one transfer fewer per tile; the count
-            // below is the larger one, so those waves may also wait for part
-            // of tile i + 1 (never for less than tile i)
-            if (later >= 1) { if (f8_n == FP8_OPS) wait_vmcnt<FP8_OPS>(); else wait_vmcnt<FP8_OPS - 1>(); }
+            if (later >= 1) { if (f8_ops == FP8_OPS) wait_vmcnt<FP8_OPS>(); else wait_vmcnt<FP8_OPS - 1>(); }
             else wait_vmcnt<0>();
         }
         lds_barrier();   // everyone's part of tile i landed; tile i-1's buffer is free
@@ -346,6 +365,17 @@ __device__ __forceinline__ void mla_slice(const MlaArgs& a, int t, int hbase, co
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // then one LDS read
                     const int di = ks >> 2;
+                    if constexpr (FP8) {
+                        if (dma && (ks & 3) == 1 && di == FP8_OPS - 1 && f8_sc) {
+                            // the tile's token scales (4-byte transfer), as in issue()
+                            const uint32_t m0v = lds_addr(&L.tscale[nt % M3_FP8_NBUF][0]);
+                            const float* gsrc = scale_src(min(nt, ntiles - 1));
+                            uint32_t saved;
+                            asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                                         "global_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+                                         : "=&s"(saved) : "v"(gsrc), "s"(m0v));
+                        }
+                    }
                     if (dma && (ks & 3) == 1 && di < (FP8 ? FP8_OPS : M3_DMA_PER_WAVE) && (!FP8 || di < f8_n)) {
                         // Issued by inline asm: the compiler does not track it as an
                         // LDS write, so it puts no wait for it before the fragment
@@ -366,20 +396,16 @@ __device__ __forceinline__ void mla_slice(const MlaArgs& a, int t, int hbase, co
             else qk(false);
         }
         // element e of this lane: token 8(e/4) + 4hh + e%4, head c32.
-        float tsc[16];
+        // e4m3: the tokens' scales multiply their logits (and, below, their
+        // probabilities, as V rows are unscaled codes)
+        const float* tsl = &L.tscale[i % M3_FP8_NBUF][4 * hh];
         if constexpr (FP8) {
-            // the tokens' scales multiply their logits (and, below, their
-            // probabilities, as V rows are unscaled codes)
-            const float* ts = a.kv_scales;
 #pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4)
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const f32x4 sc4 = *(const f32x4*)(tsl + 8 * e4);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int tok = 8 * e4 + 4 * hh + e;
-                    tsc[4 * e4 + e] = ts[L.rows[M_TILE * i + tok]];
-                }
-#pragma unroll
-            for (int e = 0; e < 16; ++e) st[e] *= tsc[e];
+                for (int e = 0; e < 4; ++e) st[4 * e4 + e] *= sc4[e];
+            }
         }
         if (!full) {   // slots without a token take no part
 #pragma unroll
@@ -411,7 +437,11 @@ __device__ __forceinline__ void mla_slice(const MlaArgs& a, int t, int hbase, co
         }
         if constexpr (FP8) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) p[e] *= tsc[e];
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const f32x4 sc4 = *(const f32x4*)(tsl + 8 * e4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) p[4 * e4 + e] *= sc4[e];
+            }
         }
         bf16x8 pb[2];
 #pragma unroll
@@ -461,30 +491,72 @@ __device__ __forceinline__ void mla_slice(const MlaArgs& a, int t, int hbase, co
     acc.l_tot = l_run + lane_xor32(l_run, lane);
 }
 
-// Normalised bf16 output and natural-log lse of a finished slice that covers
-// the whole selection.
-__device__ __forceinline__ void mla_store_final(const MlaArgs& a, int t, int head, const MlaAcc& acc) {
-    const int hh = (threadIdx.x & 63) >> 5;
-    const bool empty = acc.l_tot == 0.f;
-    const float inv = empty ? 0.f : 1.f / acc.l_tot;
-    uint16_t* op = (uint16_t*)a.out + ((size_t)t * a.n_heads + head) * M_DL;
+// Output of a finished slice, staged through LDS so that every global store
+// writes one whole 1 KB head row.  Each wave owns 32 KB of the (now idle)
+// ring: its 32 heads x 512 columns of 16-bit values, row c (head) at 1024 c.
+// The 16-byte unit u of row c sits at unit u ^ c, its two 8-byte halves
+// swapped when bit 3 of c is set, so that the lanes of a 16-lane group write
+// distinct banks and a row is read back by 64 lanes without conflicts.
+template <bool HALF>   // HALF: fp16 values, else bf16
+__device__ __forceinline__ void mla_stage_rows(const MlaAcc& acc, float sc, MlaSliceLds& L) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int hh = lane >> 5, c = lane & 31;
+    uint8_t* base = &L.ks[0][0] + 32768 * wave + 1024 * c + 8 * (hh ^ ((c >> 3) & 1));
 #pragma unroll
     for (int cb = 0; cb < M_DL / 32; ++cb)
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
+            const float x0 = acc.o[cb][4 * e4] * sc, x1 = acc.o[cb][4 * e4 + 1] * sc;
+            const float x2 = acc.o[cb][4 * e4 + 2] * sc, x3 = acc.o[cb][4 * e4 + 3] * sc;
             u32x2 w;
-            w[0] = f32_to_bf16(acc.o[cb][4 * e4] * inv) | (f32_to_bf16(acc.o[cb][4 * e4 + 1] * inv) << 16);
-            w[1] = f32_to_bf16(acc.o[cb][4 * e4 + 2] * inv) | (f32_to_bf16(acc.o[cb][4 * e4 + 3] * inv) << 16);
-            *(u32x2*)(op + 32 * cb + 8 * e4 + 4 * hh) = w;
+            if constexpr (HALF) {
+                w[0] = pack_f16x2(x0, x1);
+                w[1] = pack_f16x2(x2, x3);
+            } else {
+                w[0] = pack_bf16x2(x0, x1);
+                w[1] = pack_bf16x2(x2, x3);
+            }
+            const int u = 4 * cb + e4;   // 16-byte unit of the row: columns 8u .. 8u + 7
+            *(u32x2*)(base + 16 * (u ^ c)) = w;
         }
+}
+
+// Stores the wave's 32 staged rows: row j (head hfirst + j of the wave) to
+// dst + row_stride * j, 16 bytes a lane.
+__device__ __forceinline__ void mla_flush_rows(const MlaSliceLds& L, uint16_t* dst, size_t row_stride) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint8_t* base = &L.ks[0][0] + 32768 * wave;
+#pragma unroll 8
+    for (int j = 0; j < 32; ++j) {
+        u32x4 v = *(const u32x4*)(base + 1024 * j + 16 * (lane ^ j));
+        if ((j >> 3) & 1) v = (u32x4){v[2], v[3], v[0], v[1]};
+        *(u32x4*)(dst + row_stride * j + 8 * lane) = v;
+    }
+}
+
+// Normalised bf16 output and natural-log lse of a finished slice that covers
+// the whole selection.  Called by the whole workgroup after mla_slice (which
+// ends with a barrier, so the ring is idle).
+__device__ __forceinline__ void mla_store_final(const MlaArgs& a, int t, int hbase, const MlaAcc& acc,
+                                                MlaSliceLds& L) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int hh = lane >> 5, head = hbase + 32 * wave + (lane & 31);
+    const bool empty = acc.l_tot == 0.f;
+    const float inv = empty ? 0.f : 1.f / acc.l_tot;
+    mla_stage_rows<false>(acc, inv, L);
     if (a.lse && hh == 0)
         a.lse[(size_t)t * a.n_heads + head] = empty ? -INFINITY : (acc.m_ref + log2f(acc.l_tot)) * LN2;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's rows written (a wave reads only its own)
+    mla_flush_rows(L, (uint16_t*)a.out + ((size_t)t * a.n_heads + hbase + 32 * wave) * M_DL, M_DL);
 }
 
 // A slice's normalised partial output as fp16 with its power-of-two scale,
-// and its natural-log lse, at partial index pidx (row, head, slot).
-__device__ __forceinline__ void mla_store_partial(const MlaArgs& a, size_t pidx, const MlaAcc& acc) {
-    const int hh = (threadIdx.x & 63) >> 5;
+// and its natural-log lse, at partial index ((t * H + head) * S + sp).
+__device__ __forceinline__ void mla_store_partial(const MlaArgs& a, int t, int hbase, int sp, const MlaAcc& acc,
+                                                  MlaSliceLds& L) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int hh = lane >> 5, head = hbase + 32 * wave + (lane & 31);
+    const int S = a.splits;
     const bool empty = acc.l_tot == 0.f;
     const float inv = empty ? 0.f : 1.f / acc.l_tot;
     const float lse_nat = empty ? -INFINITY : (acc.m_ref + log2f(acc.l_tot)) * LN2;
@@ -494,71 +566,54 @@ __device__ __forceinline__ void mla_store_partial(const MlaArgs& a, size_t pidx,
     for (int cb = 0; cb < M_DL / 32; ++cb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(acc.o[cb][e]));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    amax = fmaxf(amax, lane_xor32(amax, lane));
     const int k = part_exponent(amax * inv);
-    const float sc = inv * pow2i(k);
-    uint16_t* po = a.part_o + pidx * M_DL;
-#pragma unroll
-    for (int cb = 0; cb < M_DL / 32; ++cb)
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-            u32x2 w;
-            w[0] = pack_f16x2(acc.o[cb][4 * e4] * sc, acc.o[cb][4 * e4 + 1] * sc);
-            w[1] = pack_f16x2(acc.o[cb][4 * e4 + 2] * sc, acc.o[cb][4 * e4 + 3] * sc);
-            *(u32x2*)(po + 32 * cb + 8 * e4 + 4 * hh) = w;
-        }
+    mla_stage_rows<true>(acc, inv * pow2i(k), L);
+    const size_t pidx = ((size_t)t * a.n_heads + head) * S + sp;
     if (hh == 0) {
         a.part_lse[2 * pidx] = lse_nat;
         a.part_lse[2 * pidx + 1] = pow2i(-k);
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's rows written
+    mla_flush_rows(L, a.part_o + (((size_t)t * a.n_heads + hbase + 32 * wave) * S + sp) * M_DL, (size_t)S * M_DL);
 }
 
-// The last slice of a row to finish: merges the other slices' partials
-// (indices pbase + s, s < nparts) with its own registers by their
-// log-sum-exp and writes the bf16 output and lse.
-__device__ __forceinline__ void mla_merge_final(const MlaArgs& a, int t, int head, const MlaAcc& acc, size_t pbase,
-                                                int nparts) {
+// The last slice of a row to finish: merges the S slices' partials (indices
+// pbase + s, in slice order, so the result does not depend on which slice
+// finished last) by their log-sum-exp and writes the bf16 output and lse.
+__device__ __forceinline__ void mla_merge_final(const MlaArgs& a, int t, int head, size_t pbase, int S) {
     const int hh = (threadIdx.x & 63) >> 5;
-    const bool own_empty = acc.l_tot == 0.f;
-    const float own_lse = own_empty ? -INFINITY : (acc.m_ref + log2f(acc.l_tot)) * LN2;
-    float mx = own_lse;
-    for (int s = 0; s < nparts; ++s) mx = fmaxf(mx, a.part_lse[2 * (pbase + s)]);
-    if (mx == -INFINITY) {   // no token in any slice
-        uint16_t* op = (uint16_t*)a.out + ((size_t)t * a.n_heads + head) * M_DL;
-#pragma unroll
-        for (int cb = 0; cb < M_DL / 32; ++cb)
-#pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) *(u32x2*)(op + 32 * cb + 8 * e4 + 4 * hh) = (u32x2){0u, 0u};
-        if (a.lse && hh == 0) a.lse[(size_t)t * a.n_heads + head] = -INFINITY;
-        return;
-    }
-    // own weight: e^(own_lse - mx) on the normalised own output
-    const float w_own = own_empty ? 0.f : __expf(own_lse - mx) / acc.l_tot;
-    float den = own_empty ? 0.f : __expf(own_lse - mx);
+    float mx = -INFINITY;
+    for (int s = 0; s < S; ++s) mx = fmaxf(mx, a.part_lse[2 * (pbase + s)]);
     f32x16 o[M_DL / 32];
 #pragma unroll
-    for (int cb = 0; cb < M_DL / 32; ++cb) o[cb] = acc.o[cb] * w_own;
-    for (int s = 0; s < nparts; ++s) {
-        const size_t pidx = pbase + s;
-        const float ls = a.part_lse[2 * pidx];
-        if (ls == -INFINITY) continue;
-        const float wgt = __expf(ls - mx);
-        den += wgt;
-        const float ws = wgt * a.part_lse[2 * pidx + 1];
-        const uint16_t* po = a.part_o + pidx * M_DL;
+    for (int cb = 0; cb < M_DL / 32; ++cb)
 #pragma unroll
-        for (int cb = 0; cb < M_DL / 32; ++cb)
+        for (int e = 0; e < 16; ++e) o[cb][e] = 0.f;
+    float den = 0.f;
+    if (mx != -INFINITY) {
+        for (int s = 0; s < S; ++s) {
+            const size_t pidx = pbase + s;
+            const float ls = a.part_lse[2 * pidx];
+            if (ls == -INFINITY) continue;
+            const float wgt = __expf(ls - mx);
+            den += wgt;
+            const float ws = wgt * a.part_lse[2 * pidx + 1];
+            const uint16_t* po = a.part_o + pidx * M_DL;
 #pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) {
-                const u32x2 w = *(const u32x2*)(po + 32 * cb + 8 * e4 + 4 * hh);
+            for (int cb = 0; cb < M_DL / 32; ++cb)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint16_t b = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
-                    o[cb][4 * e4 + q] += ws * (float)__builtin_bit_cast(_Float16, b);
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const u32x2 w = *(const u32x2*)(po + 32 * cb + 8 * e4 + 4 * hh);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint16_t b = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
+                        o[cb][4 * e4 + q] += ws * (float)__builtin_bit_cast(_Float16, b);
+                    }
                 }
-            }
+        }
     }
-    const float inv = 1.f / den;
+    const float inv = den > 0.f ? 1.f / den : 0.f;
     uint16_t* op = (uint16_t*)a.out + ((size_t)t * a.n_heads + head) * M_DL;
 #pragma unroll
     for (int cb = 0; cb < M_DL / 32; ++cb)
@@ -569,7 +624,7 @@ __device__ __forceinline__ void mla_merge_final(const MlaArgs& a, int t, int hea
             w[1] = f32_to_bf16(o[cb][4 * e4 + 2] * inv) | (f32_to_bf16(o[cb][4 * e4 + 3] * inv) << 16);
             *(u32x2*)(op + 32 * cb + 8 * e4 + 4 * hh) = w;
         }
-    if (a.lse && hh == 0) a.lse[(size_t)t * a.n_heads + head] = mx + logf(den);
+    if (a.lse && hh == 0) a.lse[(size_t)t * a.n_heads + head] = mx == -INFINITY ? -INFINITY : mx + logf(den);
 }
 
 }  // namespace dsa
