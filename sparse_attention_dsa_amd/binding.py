@@ -22,7 +22,8 @@ OP_TOPK, OP_MLA_DECODE, OP_MLA_PREFILL, OP_DECODE_STEP = 1, 2, 3, 4
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
            "dsa_decode_step", "dsa_workspace_size", "dsa_status_string", "dsa_check_device",
            "dsa_read_probe_sink_size", "dsa_read_probe", "dsa_hot_cache_reset", "dsa_hot_cache_workspace_size",
-           "dsa_hot_cache_fetch", "dsa_decode_step_timed", "dsa_decode_step_noalloc")
+           "dsa_hot_cache_fetch", "dsa_decode_step_timed", "dsa_decode_step_noalloc",
+           "dsa_decode_step_fused")
 STEP_EVENTS = 5   # events of dsa_decode_step_timed: start, after sampling, indexer, selection, attention
 
 
@@ -82,9 +83,12 @@ def lib():
                                             i32, f32, vp, vp, vp, vp, sz, vp, P(vp), i32]
         L.dsa_decode_step_noalloc.argtypes = [P(DsaBatch), P(DsaIndexCache), vp, vp, i32, P(DsaLatentCache), vp,
                                               i32, i32, f32, vp, vp, vp, vp]
+        L.dsa_decode_step_fused.argtypes = [P(DsaBatch), P(DsaIndexCache), vp, vp, i32, P(DsaLatentCache), vp, i32,
+                                            i32, f32, vp, vp, vp, vp, sz, vp, P(vp), i32]
         for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
                      "dsa_decode_step", "dsa_check_device", "dsa_read_probe", "dsa_hot_cache_reset",
-                     "dsa_hot_cache_fetch", "dsa_decode_step_timed", "dsa_decode_step_noalloc"):
+                     "dsa_hot_cache_fetch", "dsa_decode_step_timed", "dsa_decode_step_noalloc",
+                     "dsa_decode_step_fused"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -227,6 +231,23 @@ def decode_step(batch: Batch, keys, key_scales, q_idx, w, kv, kv_scales, d_laten
         C.byref(b), C.byref(ic), _ptr(q_idx), _ptr(w), q_idx.shape[1], C.byref(lc), _ptr(q_mla),
         q_mla.shape[1], k, float(scale), _ptr(out), _ptr(lse), _ptr(indices_out), _ptr(ws), ws.numel(),
         _stream(stream)))
+    return out
+
+
+def decode_step_fused(batch: Batch, keys, key_scales, q_idx, w, kv, kv_scales, d_latent, q_mla, k, scale,
+                      out=None, lse=None, indices_out=None, workspace=None, stream=None, events=None):
+    """The step as one persistent kernel (dsa_decode_step_fused); `events`
+    (STEP_EVENTS torch.cuda.Event, optional) are recorded at its boundaries:
+    start, persistent kernel start and end, after it, after the merge."""
+    if out is None:
+        out = _out_like(kv, q_mla, d_latent)
+    ws = _workspace(OP_DECODE_STEP, batch, k, q_mla.shape[1], q_mla.device, workspace)
+    b, ic, lc = batch.struct(), index_cache(keys, key_scales), latent_cache(kv, kv_scales, d_latent)
+    h = event_handles(events, stream) if events is not None else None
+    _check("dsa_decode_step_fused", lib().dsa_decode_step_fused(
+        C.byref(b), C.byref(ic), _ptr(q_idx), _ptr(w), q_idx.shape[1], C.byref(lc), _ptr(q_mla),
+        q_mla.shape[1], k, float(scale), _ptr(out), _ptr(lse), _ptr(indices_out), _ptr(ws), ws.numel(),
+        _stream(stream), h, len(events) if events is not None else 0))
     return out
 
 

@@ -106,7 +106,57 @@ StepLayout step_layout(const dsa_batch* b, int k, int n_heads, int mla_path_id) 
     return l;
 }
 
+// Fused decode-step workspace: score rows (for rows whose chunk quotas fail),
+// indices, candidate lists and counts, the per-row and per-request
+// bookkeeping, the ready queue, and the partial slots of split attention.
+struct FusedLayout {
+    size_t scores, indices, cand, count, excl, req_done, prefix, chunk_req, slot, splits, ctr, rq, part_o, part_lse, end;
+    int64_t ld;
+    int rq_cap, part_slots;
+};
+// Partial slots: a pool of 8 per query row plus 32 (so one or two rows can
+// always take 16 slices), then a reserve of 2 per row.
+constexpr int FUSED_SLOTS_PER_ROW = 8, FUSED_SLOTS_EXTRA = 32, FUSED_SLOTS_RESERVE = 2;
+FusedLayout fused_layout(const dsa_batch* b, int k, int n_heads) {
+    FusedLayout l;
+    const size_t T = (size_t)b->total_q, B = (size_t)b->num_requests;
+    l.ld = round_up64(b->max_context_len);
+    l.rq_cap = (int)(B + T * FU_MAX_SPLITS);
+    l.part_slots = (int)(T * FUSED_SLOTS_PER_ROW + FUSED_SLOTS_EXTRA);
+    const size_t slots = (size_t)l.part_slots + FUSED_SLOTS_RESERVE * T;
+    l.scores = 0;
+    l.indices = align_up(sizeof(float) * T * l.ld);
+    l.cand = align_up(l.indices + sizeof(int32_t) * T * k);
+    l.count = align_up(l.cand + sizeof(uint64_t) * T * TOPK_LIST);
+    l.excl = align_up(l.count + sizeof(uint32_t) * T);
+    l.req_done = align_up(l.excl + sizeof(uint64_t) * T);
+    l.prefix = align_up(l.req_done + sizeof(uint32_t) * B);
+    // chunks of 64 pages of 64 tokens: at most this many per request
+    const size_t max_chunks = B * (size_t)((b->max_context_len + 64 * 64 - 1) / (64 * 64));
+    l.chunk_req = align_up(l.prefix + sizeof(uint32_t) * (B + 1));
+    l.slot = align_up(l.chunk_req + 2 * sizeof(uint32_t) * max_chunks);
+    l.splits = align_up(l.slot + sizeof(uint32_t) * T);
+    l.ctr = align_up(l.splits + sizeof(uint32_t) * T);
+    l.rq = align_up(l.ctr + sizeof(uint32_t) * FC_N);
+    l.part_o = align_up(l.rq + 4 * sizeof(uint32_t) * (size_t)l.rq_cap);
+    l.part_lse = align_up(l.part_o + sizeof(uint16_t) * 512 * (size_t)n_heads * slots);
+    l.end = align_up(l.part_lse + 2 * sizeof(float) * (size_t)n_heads * slots);
+    return l;
+}
+
 int launch_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH; }
+
+// Workspace of the multi-kernel decode step for any latent dtype.
+size_t step_workspace(const dsa_batch* b, int k, int n_heads) {
+    size_t end = 0;
+    for (int dt = 0; dt <= 2; ++dt) end = std::max(end, step_layout(b, k, n_heads, mla_path(dt, 512, 64, n_heads)).end);
+    return end;
+}
+// Decode-step workspace that serves both entry points (the multi-kernel step
+// and the one-launch step).
+size_t decode_step_workspace(const dsa_batch* b, int k, int n_heads) {
+    return std::max(step_workspace(b, k, n_heads), fused_layout(b, k, n_heads).end);
+}
 
 // Indexer arguments that write score rows (no candidate emission).
 IndexerArgs indexer_args(const dsa_batch* b, const dsa_index_cache* c, const void* q_idx, const float* w,
@@ -278,12 +328,7 @@ size_t dsa_workspace_size(int32_t op, const dsa_batch* b, int32_t k, int32_t n_h
         return mla_layout_max(0, b, k, n_heads, op == DSA_OP_MLA_PREFILL);
     case DSA_OP_DECODE_STEP:
         if (k < 1 || k > TOPK_MAX_K || n_heads < 1) return 0;
-        {
-            size_t end = 0;
-            for (int dt = 0; dt <= 2; ++dt)
-                end = std::max(end, step_layout(b, k, n_heads, mla_path(dt, 512, 64, n_heads)).end);
-            return end;
-        }
+        return decode_step_workspace(b, k, n_heads);
     default:
         return 0;
     }
@@ -352,11 +397,11 @@ int decode_step(const dsa_batch* b, const dsa_index_cache* ic, const void* q_idx
     if (st != DSA_OK) return st;
     if ((st = validate_mla(b, lc, q_mla, n_heads, k, out)) != DSA_OK) return st;
     if (!topk_shape_ok(b, k)) return DSA_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    char* base = (char*)ws;
     const StepLayout l = step_layout(b, k, n_heads, mla_path(lc->dtype, lc->d_latent, lc->d_rope, n_heads));
     if (!ws || ws_bytes < l.end) return DSA_ERR_WORKSPACE;
     if ((st = check_device_cached()) != DSA_OK) return st;
-    hipStream_t s = (hipStream_t)stream;
-    char* base = (char*)ws;
     float* scores = (float*)(base + l.scores);
     int32_t* indices = indices_out ? indices_out : (int32_t*)(base + l.indices);
 
@@ -379,6 +424,53 @@ int decode_step(const dsa_batch* b, const dsa_index_cache* ic, const void* q_idx
     st = run_mla(b, lc, q_mla, n_heads, indices, k, scale, out, lse, base, ws_bytes, l.mla_base, false, s);
     if (st == DSA_OK && ev && hipEventRecord(ev[4], s) != hipSuccess) return DSA_ERR_LAUNCH;
     return st;
+}
+
+// The step in one persistent launch (plus its init and merge kernels); with
+// `ev` it records ev[0] before the first launch, ev[1] and ev[2] at the start
+// and end of the persistent kernel (taken by its launch), ev[3] before the
+// merge of split partials and ev[4] after it.
+int decode_step_fused(const dsa_batch* b, const dsa_index_cache* ic, const void* q_idx, const float* w,
+                      int32_t n_heads_idx, const dsa_latent_cache* lc, const void* q_mla, int32_t n_heads, int32_t k,
+                      float scale, void* out, float* lse, int32_t* indices_out, void* ws, size_t ws_bytes,
+                      dsa_stream_t stream, const hipEvent_t* ev) {
+    int st = validate_indexer(b, ic, q_idx, w, n_heads_idx);
+    if (st != DSA_OK) return st;
+    if ((st = validate_mla(b, lc, q_mla, n_heads, k, out)) != DSA_OK) return st;
+    if (!topk_shape_ok(b, k)) return DSA_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    char* base = (char*)ws;
+    const FusedLayout fl = fused_layout(b, k, n_heads);
+    IndexerArgs ia = indexer_args(b, ic, q_idx, w, n_heads_idx, (float*)(base + fl.scores), fl.ld);
+    ia.k = k;
+    MlaArgs ma = mla_args(b, lc, q_mla, n_heads, nullptr, k, scale, out, lse);
+    if (!fused_ok(ia, ma)) return DSA_ERR_UNSUPPORTED;
+    if (!ws || ws_bytes < fl.end) return DSA_ERR_WORKSPACE;
+    if ((st = check_device_cached()) != DSA_OK) return st;
+    FusedArgs f;
+    f.indices = indices_out ? indices_out : (int32_t*)(base + fl.indices);
+    ia.cand = (uint64_t*)(base + fl.cand);
+    ia.row_count = (uint32_t*)(base + fl.count);
+    ma.indices = f.indices;
+    ma.part_o = (uint16_t*)(base + fl.part_o);
+    ma.part_lse = (float*)(base + fl.part_lse);
+    f.ia = ia;
+    f.ma = ma;
+    f.ctr = (uint32_t*)(base + fl.ctr);
+    f.chunk_prefix = (uint32_t*)(base + fl.prefix);
+    f.chunk_req = (uint32_t*)(base + fl.chunk_req);
+    f.req_done = (uint32_t*)(base + fl.req_done);
+    f.row_excl = (unsigned long long*)(base + fl.excl);
+    f.row_slot = (uint32_t*)(base + fl.slot);
+    f.row_splits = (uint32_t*)(base + fl.splits);
+    f.rq = (uint32_t*)(base + fl.rq);
+    f.rq_cap = fl.rq_cap;
+    f.sq_cap = b->num_requests;
+    f.part_slots = fl.part_slots;
+    hipError_t e = ev ? hipEventRecord(ev[0], s) : hipSuccess;
+    if (e == hipSuccess) e = launch_fused(f, s, ev ? ev + 1 : nullptr);
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[4], s);
+    return launch_status(e);
 }
 
 }  // namespace
@@ -405,6 +497,22 @@ int dsa_decode_step_timed(const dsa_batch* b, const dsa_index_cache* ic, const v
     }
     return decode_step(b, ic, q_idx, w, n_heads_idx, lc, q_mla, n_heads, k, scale, out, lse, indices_out, ws,
                        ws_bytes, stream, ev);
+}
+
+int dsa_decode_step_fused(const dsa_batch* b, const dsa_index_cache* ic, const void* q_idx, const float* w,
+                          int32_t n_heads_idx, const dsa_latent_cache* lc, const void* q_mla, int32_t n_heads,
+                          int32_t k, float scale, void* out, float* lse, int32_t* indices_out, void* ws,
+                          size_t ws_bytes, dsa_stream_t stream, void* const* events, int32_t n_events) {
+    hipEvent_t ev[DSA_STEP_EVENTS];
+    if (events) {
+        if (n_events < DSA_STEP_EVENTS) return DSA_ERR_INVALID_ARG;
+        for (int i = 0; i < DSA_STEP_EVENTS; ++i) {
+            if (!events[i]) return DSA_ERR_INVALID_ARG;
+            ev[i] = (hipEvent_t)events[i];
+        }
+    }
+    return decode_step_fused(b, ic, q_idx, w, n_heads_idx, lc, q_mla, n_heads, k, scale, out, lse, indices_out, ws,
+                             ws_bytes, stream, events ? ev : nullptr);
 }
 
 }  // extern "C"
@@ -449,8 +557,7 @@ int dsa_decode_step_noalloc(const dsa_batch* b, const dsa_index_cache* ic, const
     if (st != DSA_OK) return st;
     if ((st = validate_mla(b, lc, q_mla, n_heads, k, out)) != DSA_OK) return st;
     if (!topk_shape_ok(b, k)) return DSA_ERR_UNSUPPORTED;
-    const StepLayout l = step_layout(b, k, n_heads, mla_path(lc->dtype, lc->d_latent, lc->d_rope, n_heads));
-    if (l.end > DSA_NOALLOC_SCRATCH_BYTES) return DSA_ERR_TOO_LARGE;
+    if (step_workspace(b, k, n_heads) > DSA_NOALLOC_SCRATCH_BYTES) return DSA_ERR_TOO_LARGE;
     if ((st = check_device_cached()) != DSA_OK) return st;
     void* ws = noalloc_scratch();
     if (!ws) return DSA_ERR_LAUNCH;

@@ -88,6 +88,61 @@ __device__ __forceinline__ i32x8 join_i32x8(u32x4 lo, u32x4 hi) {
     return r;
 }
 
+// Work-item id x through an opaque move.  Values derived from it cannot be
+// hoisted out of a persistent kernel's item loop, where they would stay live
+// across every kind of item (and spill); each device routine takes it once.
+__device__ __forceinline__ int tid_x() {
+    int r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"((int)threadIdx.x));
+    return r;
+}
+
+// Accesses to data that one workgroup hands to another inside a launch.
+// Agent-scope atomic accesses are coherent across the device by themselves
+// (they do not stop in an XCD's own L2), so a writer that waits for its
+// stores (vmcnt 0) before it sets a flag, and a reader that loads the data
+// after it has seen the flag, need no L2 write-back or invalidate: those are
+// what agent-scope release and acquire add for ordinary accesses, and they
+// cost the whole device's streaming bandwidth when issued often.
+template <class T>
+__device__ __forceinline__ void st_agent(T* p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ T ld_agent(const T* p) {
+    return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------ asynchronous LDS fills
+// One 64-lane transfer global -> LDS at LDS address m0v (wave-uniform; lane
+// l's bytes land at m0v + l * size): 16 B a lane (plain, or streamed: not
+// kept in the caches), or 4 B a lane.  Issued by inline asm, so the compiler
+// neither counts these transfers nor waits for them before LDS reads (it
+// would otherwise wait for every transfer in flight, the prefetched ones
+// too); the caller waits for them with wait_vmcnt.  M0 is restored.
+__device__ __forceinline__ void dma16(const void* g, uint32_t m0v) {
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(g), "s"(m0v));
+}
+__device__ __forceinline__ void dma16_stream(const void* g, uint32_t m0v) {
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, off sc0 nt\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(g), "s"(m0v));
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t m0v) {
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                 "global_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(g), "s"(m0v));
+}
+// 32-bit LDS address of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
 // ------------------------------------------------------ waits and barriers
 // Wait until at most N of this wave's vector-memory operations are pending.
 template <int N>
@@ -185,6 +240,38 @@ struct MlaArgs {
     uint32_t* arrive;                 // [T * H / 128]: slices finished (128-head path)
     int splits;
 };
+
+// The fused decode step's arguments (one persistent launch; see fused.hip).
+// Counters in ctr[]: head and tail of the selection queue and of the
+// attention queue, the next chunk of the key stream, the attention slices not
+// yet finished, an error word, the number of chunks, and the number of
+// selection items (requests with query rows).
+enum { FC_SQ_HEAD = 0, FC_SQ_TAIL, FC_MQ_HEAD, FC_MQ_TAIL, FC_TICKET, FC_WORK, FC_ERROR, FC_NCHUNKS, FC_NSEL, FC_N = 16 };
+enum { RQ_EMPTY = 0, RQ_SEL = 1, RQ_MLA = 2 };
+struct FusedArgs {
+    IndexerArgs ia;                  // keys, queries, weights, k; cand/row_count: candidate lists;
+                                     // scores/ld: rows scored again when a chunk quota failed
+    MlaArgs ma;                      // latent cache, MLA queries, out/lse, part_o/part_lse by slot
+    int32_t* indices;                // [T][k] selection (ascending, -1 padded)
+    uint32_t* ctr;                   // [FC_N]
+    uint32_t* chunk_prefix;          // [B] stream position of request r's first chunk
+    uint32_t* chunk_req;             // [chunks][2] request and first page of each chunk of the stream
+    uint32_t* req_done;              // [B] waves done with the request's pages
+    unsigned long long* row_excl;    // [T] largest composite a chunk left out (0: none)
+    uint32_t* row_slot;              // [T] first partial slot of the row's slices
+    uint32_t* row_splits;            // [T] slices of the row's attention
+    uint32_t* rq;                    // [rq_cap][4] queued items: kind, then three words; slots
+                                     // [0, sq_cap) the selection queue, the rest the attention queue
+    int rq_cap, sq_cap;
+    int part_slots;                  // shared partial slots (each: n_heads partials); a
+                                     // reserve of 2 per row follows them
+};
+constexpr int FU_MAX_SPLITS = 16;    // attention slices per row at most
+bool fused_ok(const IndexerArgs& ia, const MlaArgs& ma);
+// Init kernel, the persistent step (with `ev`: ev[0] and ev[1] its start and
+// stop, taken by the launch; ev[2] recorded before the merge), then the merge
+// of split partials.
+hipError_t launch_fused(const FusedArgs& f, hipStream_t s, const hipEvent_t* ev = nullptr);
 
 // Compute units of the current device (cached per device).
 int device_cu_count();

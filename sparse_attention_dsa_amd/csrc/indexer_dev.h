@@ -19,6 +19,41 @@ constexpr int IDX_D = 128;
 constexpr int IDX_PAGE = 64;
 constexpr int IDX_THREADS = 256;
 
+// XOR permutation of the 16-byte units of token t inside an LDS key page
+// (fragment reads of 16 tokens then hit distinct banks).
+__device__ __forceinline__ int page_swz(int t) { return (t ^ (t >> 3)) & 7; }
+
+// Staged page loads for the persistent kernel: fully contiguous loads (lane l
+// reads bytes [1024c + 16l, +16) of the page, 1 KB per instruction, like a
+// plain streaming read) into a register ring, then each page is re-laid
+// through a private 8 KB LDS buffer of the wave into the MFMA fragment layout.
+struct RawPage {
+    u32x4 v[8];      // unit (lane & 7) of token 8c + (lane >> 3), c = 0..7
+    float scale;     // scale of token (lane)
+};
+
+__device__ __forceinline__ void load_raw_page(const uint8_t* __restrict__ keys, const float* __restrict__ scales,
+                                              int blk, bool live, int lane, RawPage& p) {
+    // Buffer loads through a descriptor of the page (block id and liveness
+    // are wave-uniform).  A slot past the wave's share still issues the same
+    // instructions, so the ring's load counting stays exact, but its
+    // descriptor holds no records: the range check returns zeros and nothing
+    // is read from memory.
+    const uint8_t* page = keys + (size_t)blk * (IDX_PAGE * IDX_D);
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)page, 0, live ? IDX_PAGE * IDX_D : 0, 0x00020000);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) p.v[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, 16 * lane + 1024 * c, 0, 2);
+    // without scales the load reads the page's own keys; the consumer then
+    // uses 1 instead (the same instructions issue either way, and nothing
+    // here waits for the load)
+    const void* sp = scales ? (const void*)(scales + (size_t)blk * IDX_PAGE) : (const void*)page;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)sp, 0, live ? 4 * IDX_PAGE : 0, 0x00020000);
+    p.scale = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, 4 * lane, 0, 0));
+}
+
+
 // part[nt] holds, for token 16*nt + (lane & 15), the partial head sum of this
 // lane's 16-lane group g.  Returns the full sum for token `lane` of the page.
 __device__ __forceinline__ float head_sum_transpose(const float part[4], int lane) {

@@ -100,11 +100,6 @@ __device__ __forceinline__ f32x16 mfma_bf16_32x32x16(bf16x8 a, bf16x8 b, f32x16 
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// 32-bit LDS address of a pointer into a __shared__ array
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
-}
-
 // max(a, b, c) in one instruction (fmaxf would first canonicalize every
 // input it cannot prove canonical; no NaN reaches these)
 __device__ __forceinline__ float max3f(float a, float b, float c) {
@@ -164,7 +159,7 @@ __device__ __forceinline__ void mla_slice(const MlaArgs& a, int t, int hbase, co
                                           int nslots, MlaSliceLds& L, MlaAcc& acc) {
     const Geometry& G = a.g;
     const int ntiles = (nslots + M_TILE - 1) / M_TILE;
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = tid_x(), lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hh = lane >> 5, c32 = lane & 31;
     const int head = hbase + wave * 32 + c32;
@@ -185,7 +180,7 @@ __device__ __forceinline__ void mla_slice(const MlaArgs& a, int t, int hbase, co
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
             const int j = tid + u * M_THREADS;
-            sj[u] = j < nslots ? sel[j] : -1;
+            sj[u] = j < nslots ? ld_agent(sel + j) : -1;   // may come from this launch
         }
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
@@ -224,19 +219,16 @@ __device__ __forceinline__ void mla_slice(const MlaArgs& a, int t, int hbase, co
         const int row = tile_row(tile);
         if constexpr (!FP8) {
             const uint8_t* src = kvb + (size_t)row * M_ROW_BYTES + dma_col;
-            uint8_t* dst = &L.ks[b][0] + 1024 * M3_DMA_PER_WAVE * wave;
+            const uint32_t dst = lds_addr(&L.ks[b][0] + 1024 * M3_DMA_PER_WAVE * wave);
 #pragma unroll
-            for (int i = 0; i < M3_DMA_PER_WAVE; ++i)
-                __builtin_amdgcn_global_load_lds((const void*)(src + 128 * i), (lds_vptr)(dst + 1024 * i), 16, 0, 0);
+            for (int i = 0; i < M3_DMA_PER_WAVE; ++i) dma16(src + 128 * i, dst + 1024u * i);
         } else {
             const uint8_t* src = kvb + (size_t)row * M_DQK + 64 * f8_i0 + dma_col;
-            uint8_t* dst = f8_stage + M3_FP8_TILE * b + 1024 * (9 * f8_g + f8_i0);
+            const uint32_t dst = lds_addr(f8_stage + M3_FP8_TILE * b + 1024 * (9 * f8_g + f8_i0));
 #pragma unroll
             for (int i = 0; i < FP8_OPS; ++i)
-                if (i < f8_n)
-                    __builtin_amdgcn_global_load_lds((const void*)(src + 64 * i), (lds_vptr)(dst + 1024 * i), 16, 0, 0);
-            if (f8_sc)
-                __builtin_amdgcn_global_load_lds((const void*)scale_src(tile), (lds_vptr)&L.tscale[b][0], 4, 0, 0);
+                if (i < f8_n) dma16(src + 64 * i, dst + 1024u * i);
+            if (f8_sc) dma4(scale_src(tile), lds_addr(&L.tscale[b][0]));
         }
     };
     constexpr int NRING = FP8 ? M3_FP8_NBUF : M3_NBUF;
@@ -368,27 +360,15 @@ __device__ __forceinline__ void mla_slice(const MlaArgs& a, int t, int hbase, co
                     if constexpr (FP8) {
                         if (dma && (ks & 3) == 1 && di == FP8_OPS - 1 && f8_sc) {
                             // the tile's token scales (4-byte transfer), as in issue()
-                            const uint32_t m0v = lds_addr(&L.tscale[nt % M3_FP8_NBUF][0]);
-                            const float* gsrc = scale_src(min(nt, ntiles - 1));
-                            uint32_t saved;
-                            asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
-                                         "global_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
-                                         : "=&s"(saved) : "v"(gsrc), "s"(m0v));
+                            dma4(scale_src(min(nt, ntiles - 1)), lds_addr(&L.tscale[nt % M3_FP8_NBUF][0]));
                         }
                     }
                     if (dma && (ks & 3) == 1 && di < (FP8 ? FP8_OPS : M3_DMA_PER_WAVE) && (!FP8 || di < f8_n)) {
-                        // Issued by inline asm: the compiler does not track it as an
-                        // LDS write, so it puts no wait for it before the fragment
-                        // reads of tile i, which use another buffer (the loop's own
-                        // vector-memory waits count these transfers).  M0 holds the
-                        // LDS address and is restored afterwards; no immediate
-                        // offset, which the LDS destination would include as well.
-                        const uint32_t m0v = lds_addr(ddst + 1024 * di);
-                        const uint8_t* gsrc = dsrc + (FP8 ? 64 : 128) * di;
-                        uint32_t saved;
-                        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
-                                     "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
-                                     : "=&s"(saved) : "v"(gsrc), "s"(m0v));
+                        // dma16 is not counted by the compiler: it puts no wait for
+                        // it before the fragment reads of tile i, which use another
+                        // buffer (the loop's own vector-memory waits count these
+                        // transfers)
+                        dma16(dsrc + (FP8 ? 64 : 128) * di, lds_addr(ddst + 1024 * di));
                     }
                 }
             };
@@ -499,7 +479,7 @@ __device__ __forceinline__ void mla_slice(const MlaArgs& a, int t, int hbase, co
 // distinct banks and a row is read back by 64 lanes without conflicts.
 template <bool HALF>   // HALF: fp16 values, else bf16
 __device__ __forceinline__ void mla_stage_rows(const MlaAcc& acc, float sc, MlaSliceLds& L) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = tid_x(), lane = tid & 63, wave = tid >> 6;
     const int hh = lane >> 5, c = lane & 31;
     uint8_t* base = &L.ks[0][0] + 32768 * wave + 1024 * c + 8 * (hh ^ ((c >> 3) & 1));
 #pragma unroll
@@ -524,7 +504,7 @@ __device__ __forceinline__ void mla_stage_rows(const MlaAcc& acc, float sc, MlaS
 // Stores the wave's 32 staged rows: row j (head hfirst + j of the wave) to
 // dst + row_stride * j, 16 bytes a lane.
 __device__ __forceinline__ void mla_flush_rows(const MlaSliceLds& L, uint16_t* dst, size_t row_stride) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = tid_x(), lane = tid & 63, wave = tid >> 6;
     const uint8_t* base = &L.ks[0][0] + 32768 * wave;
 #pragma unroll 8
     for (int j = 0; j < 32; ++j) {
@@ -539,7 +519,7 @@ __device__ __forceinline__ void mla_flush_rows(const MlaSliceLds& L, uint16_t* d
 // ends with a barrier, so the ring is idle).
 __device__ __forceinline__ void mla_store_final(const MlaArgs& a, int t, int hbase, const MlaAcc& acc,
                                                 MlaSliceLds& L) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = tid_x(), lane = tid & 63, wave = tid >> 6;
     const int hh = lane >> 5, head = hbase + 32 * wave + (lane & 31);
     const bool empty = acc.l_tot == 0.f;
     const float inv = empty ? 0.f : 1.f / acc.l_tot;
@@ -551,12 +531,12 @@ __device__ __forceinline__ void mla_store_final(const MlaArgs& a, int t, int hba
 }
 
 // A slice's normalised partial output as fp16 with its power-of-two scale,
-// and its natural-log lse, at partial index ((t * H + head) * S + sp).
-__device__ __forceinline__ void mla_store_partial(const MlaArgs& a, int t, int hbase, int sp, const MlaAcc& acc,
-                                                  MlaSliceLds& L) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int hh = lane >> 5, head = hbase + 32 * wave + (lane & 31);
-    const int S = a.splits;
+// and its natural-log lse: head hbase + i of the slice goes to partial index
+// pfirst + pstride i (partial p: part_o[p][512], part_lse[p][2]).
+__device__ __forceinline__ void mla_store_partial_at(const MlaArgs& a, size_t pfirst, size_t pstride,
+                                                     const MlaAcc& acc, MlaSliceLds& L) {
+    const int tid = tid_x(), lane = tid & 63, wave = tid >> 6;
+    const int hh = lane >> 5, hl = 32 * wave + (lane & 31);
     const bool empty = acc.l_tot == 0.f;
     const float inv = empty ? 0.f : 1.f / acc.l_tot;
     const float lse_nat = empty ? -INFINITY : (acc.m_ref + log2f(acc.l_tot)) * LN2;
@@ -569,20 +549,27 @@ __device__ __forceinline__ void mla_store_partial(const MlaArgs& a, int t, int h
     amax = fmaxf(amax, lane_xor32(amax, lane));
     const int k = part_exponent(amax * inv);
     mla_stage_rows<true>(acc, inv * pow2i(k), L);
-    const size_t pidx = ((size_t)t * a.n_heads + head) * S + sp;
+    const size_t pidx = pfirst + pstride * hl;
     if (hh == 0) {
         a.part_lse[2 * pidx] = lse_nat;
         a.part_lse[2 * pidx + 1] = pow2i(-k);
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's rows written
-    mla_flush_rows(L, a.part_o + (((size_t)t * a.n_heads + hbase + 32 * wave) * S + sp) * M_DL, (size_t)S * M_DL);
+    mla_flush_rows(L, a.part_o + (pfirst + pstride * 32 * wave) * M_DL, pstride * M_DL);
+}
+
+// ... at partial index ((t * H + head) * S + sp) (slices of a row adjacent).
+__device__ __forceinline__ void mla_store_partial(const MlaArgs& a, int t, int hbase, int sp, const MlaAcc& acc,
+                                                  MlaSliceLds& L) {
+    const int S = a.splits;
+    mla_store_partial_at(a, ((size_t)t * a.n_heads + hbase) * S + sp, (size_t)S, acc, L);
 }
 
 // The last slice of a row to finish: merges the S slices' partials (indices
 // pbase + s, in slice order, so the result does not depend on which slice
 // finished last) by their log-sum-exp and writes the bf16 output and lse.
 __device__ __forceinline__ void mla_merge_final(const MlaArgs& a, int t, int head, size_t pbase, int S) {
-    const int hh = (threadIdx.x & 63) >> 5;
+    const int hh = (tid_x() & 63) >> 5;
     float mx = -INFINITY;
     for (int s = 0; s < S; ++s) mx = fmaxf(mx, a.part_lse[2 * (pbase + s)]);
     f32x16 o[M_DL / 32];

@@ -29,8 +29,7 @@
 // list overflowing) the same selection runs over the whole row from memory.
 // Rows of at most SEL_LIST tokens load all their scores into the list
 // directly and skip the first two kernels.
-#include "indexer_dev.h"
-#include "topk_dev.h"
+#include "select_dev.h"
 
 namespace dsa {
 
@@ -42,11 +41,6 @@ static_assert(TOPK_CAND_CAP <= TOPK_CHUNK, "a chunk slot never needs more than i
 
 constexpr int SEL_THREADS = 1024;                      // selection
 constexpr int SEL_WAVES = SEL_THREADS / 64;
-constexpr int SEL_LIST = TOPK_LIST;                    // candidates held in LDS
-constexpr int SEL_BINS = 4096;
-constexpr int SEL_MEMBERS = 4096;                      // threshold-bucket members sorted directly
-static_assert(SEL_LIST > TOPK_MAX_K, "short rows go straight to the list");
-static_assert(SEL_BINS == 4 * SEL_THREADS, "four buckets per thread in the threshold scan");
 
 // ---------------------------------------------------------------------------
 // Bound kernel: the row's strided sample of scores, then its key bound.
@@ -166,189 +160,12 @@ __global__ __launch_bounds__(CMP_THREADS) void topk_compact(TopkArgs a) {
     }
 }
 
-// ---------------------------------------------------------------------------
-// Selection.
-struct SelShared {
-    uint64_t list[SEL_LIST];
-    union {
-        uint32_t hist[SEL_BINS];
-        uint64_t members[SEL_MEMBERS];
-    } r;
-    uint32_t off[SEL_THREADS];   // list offset of each chunk's candidates
-    uint32_t wsum[SEL_WAVES];
-    uint32_t red[2][SEL_WAVES];
-    uint32_t st[8];
-};
-
-template <class Get>
-__device__ uint64_t kth_from_hist(int count, uint32_t K, const Get& get, SelShared& S, uint32_t lo, uint32_t sh);
-
-// The K-th largest composite key over source entries i < count (get(i)
-// fetches entry i); count >= K.  Called by the whole workgroup.
-template <class Get>
-__device__ uint64_t kth_composite(int count, uint32_t K, const Get& get, SelShared& S) {
-    const int tid = threadIdx.x;
-    // 1. key range of the entries
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-    for (int i = tid; i < count; i += SEL_THREADS) {
-        const uint32_t k = composite_key(get(i));
-        lo = min(lo, k);
-        hi = max(hi, k);
-    }
-    for (int i = tid; i < SEL_BINS; i += SEL_THREADS) S.r.hist[i] = 0u;
-    block_min_max<SEL_WAVES>(lo, hi, S.red);
-    const uint32_t sh = range_shift(lo, hi, SEL_BINS);
-
-    // 2. histogram over SEL_BINS buckets spread across [lo, hi]
-    for (int base = 0; base < count; base += SEL_THREADS) {
-        const int i = base + tid;
-        const bool ok = i < count;
-        const uint32_t b = ok ? bucket_of(composite_key(get(i)), lo, sh, SEL_BINS) : 0u;
-        lds_count(S.r.hist, b, ok);
-    }
-    lds_barrier();
-    return kth_from_hist(count, K, get, S, lo, sh);
-}
-
-// Steps 3 and 4 of the above, given the histogram of the entries over
-// SEL_BINS buckets of 2^sh keys from lo (in S.r.hist).
-template <class Get>
-__device__ uint64_t kth_from_hist(int count, uint32_t K, const Get& get, SelShared& S, uint32_t lo, uint32_t sh) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // 3. threshold bucket b*: count(> b*) < K <= count(>= b*); thread i owns
-    // buckets 4095-4i .. 4092-4i
-    uint32_t c4[4], sum = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) { c4[j] = S.r.hist[SEL_BINS - 1 - 4 * tid - j]; sum += c4[j]; }
-    uint32_t tot;
-    const uint32_t ex = block_excl_scan<SEL_WAVES>(sum, S.wsum, &tot);
-    if (ex < K && ex + sum >= K) {
-        uint32_t cum = ex;
-        for (int j = 0; j < 4; ++j) {
-            if (cum + c4[j] >= K) {
-                S.st[0] = (uint32_t)(SEL_BINS - 1 - 4 * tid - j);
-                S.st[1] = cum;
-                S.st[2] = c4[j];
-                break;
-            }
-            cum += c4[j];
-        }
-    }
-    if (tid == 0) S.st[3] = 0u;
-    lds_barrier();
-    const uint32_t bstar = S.st[0], need = K - S.st[1], nb = S.st[2];
-    lds_barrier();   // the histogram space is reused below
-
-    if (nb <= (uint32_t)SEL_MEMBERS) {
-        // 4a. the threshold bucket's members: descending bitonic sort
-        for (int base = 0; base < count; base += SEL_THREADS) {
-            const int i = base + tid;
-            uint64_t ck = 0;
-            bool mem = false;
-            if (i < count) {
-                ck = get(i);
-                mem = bucket_of(composite_key(ck), lo, sh, SEL_BINS) == bstar;
-            }
-            const unsigned long long mk = __ballot(mem);
-            if (mk) {
-                const int first = __ffsll((long long)mk) - 1;
-                uint32_t pos = 0;
-                if (lane == first) pos = atomicAdd(&S.st[3], (uint32_t)__popcll(mk));
-                const unsigned long long below = lane ? (mk & ((1ull << lane) - 1ull)) : 0ull;
-                pos = (uint32_t)__builtin_amdgcn_readlane((int)pos, first) + (uint32_t)__popcll(below);
-                if (mem) S.r.members[pos] = ck;
-            }
-        }
-        lds_barrier();
-        int P = 1;
-        while (P < (int)nb) P <<= 1;
-        for (int i = (int)nb + tid; i < P; i += SEL_THREADS) S.r.members[i] = 0ull;   // sorts last
-        lds_barrier();
-        for (int size = 2; size <= P; size <<= 1) {
-            for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                for (int i = tid; i < P / 2; i += SEL_THREADS) {
-                    const int l0 = 2 * i - (i & (stride - 1));
-                    const int l1 = l0 + stride;
-                    const bool desc = (l0 & size) == 0;
-                    const uint64_t x = S.r.members[l0], y = S.r.members[l1];
-                    if ((x < y) == desc) { S.r.members[l0] = y; S.r.members[l1] = x; }
-                }
-                lds_barrier();
-            }
-        }
-        const uint64_t kth = S.r.members[need - 1];
-        lds_barrier();
-        return kth;
-    }
-
-    // 4b. many ties: MSB-first radix select of the need-th largest member
-    // composite, 8 bits at a time (unique keys: settled by the last digit)
-    uint32_t* h256 = S.r.hist;
-    uint32_t rem = need;
-    uint64_t prefix = 0;
-    for (int d = 56; d >= 0; d -= 8) {
-        if (tid < 256) h256[tid] = 0u;
-        lds_barrier();
-        for (int base = 0; base < count; base += SEL_THREADS) {
-            const int i = base + tid;
-            uint64_t ck = 0;
-            bool ok = false;
-            if (i < count) {
-                ck = get(i);
-                ok = bucket_of(composite_key(ck), lo, sh, SEL_BINS) == bstar &&
-                     (d == 56 || (ck >> (d + 8)) == prefix);
-            }
-            lds_count(h256, (uint32_t)(ck >> d) & 255u, ok);
-        }
-        lds_barrier();
-        if (wave == 0) {
-            uint32_t cc[4], s4 = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) { cc[j] = h256[255 - 4 * lane - j]; s4 += cc[j]; }
-            uint32_t t4;
-            const uint32_t e4 = wave_excl_scan(s4, &t4);
-            if (e4 < rem && e4 + s4 >= rem) {
-                uint32_t cum = e4;
-                for (int j = 0; j < 4; ++j) {
-                    if (cum + cc[j] >= rem) { S.st[4] = (uint32_t)(255 - 4 * lane - j); S.st[5] = rem - cum; break; }
-                    cum += cc[j];
-                }
-            }
-        }
-        lds_barrier();
-        prefix = (prefix << 8) | S.st[4];
-        rem = S.st[5];
-        lds_barrier();
-    }
-    return prefix;
-}
-
-// Writes the source entries with composite >= kth, in source order (which is
-// ascending token order); exactly K of them.
-template <class Get>
-__device__ void write_selected(int count, uint64_t kth, uint32_t K, const Get& get, int32_t* out, SelShared& S) {
-    const int tid = threadIdx.x;
-    const int per = (count + SEL_THREADS - 1) / SEL_THREADS;
-    const int i0 = min(count, tid * per), i1 = min(count, i0 + per);
-    uint32_t nsel = 0;
-    for (int i = i0; i < i1; ++i) nsel += get(i) >= kth ? 1u : 0u;
-    uint32_t tot;
-    uint32_t pos = block_excl_scan<SEL_WAVES>(nsel, S.wsum, &tot);
-    for (int i = i0; i < i1; ++i) {
-        const uint64_t ck = get(i);
-        if (ck >= kth) {
-            if (pos < K) out[pos] = composite_index(ck);
-            ++pos;
-        }
-    }
-}
-
 // Gathers row t's chunk candidates into S.list in chunk order and counts
 // them into the SEL_BINS-bucket histogram over [bound, largest candidate key]
 // (*lo, *sh); returns the entry count, or -1 when a chunk slot overflowed or
 // the list would.  Every thread fetches list positions tid, tid + SEL_THREADS,
 // ... (all its loads issued before any of its LDS stores).
-__device__ int gather_candidates(const TopkArgs& a, int t, int n, SelShared& S, uint32_t* lo_out,
+__device__ int gather_candidates(const TopkArgs& a, int t, int n, SelShared<SEL_THREADS>& S, uint32_t* lo_out,
                                  uint32_t* sh_out) {
     constexpr int PER = SEL_LIST / SEL_THREADS;
     const int tid = threadIdx.x;
@@ -404,26 +221,26 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_select(TopkArgs a) {
         for (int i = tid; i < (int)K; i += SEL_THREADS) out[i] = i < n ? i : -1;
         return;
     }
-    __shared__ SelShared S;
+    __shared__ SelShared<SEL_THREADS> S;
     const float* row = a.scores + (size_t)t * a.ld;
     auto get = [&](int i) -> uint64_t { return S.list[i]; };
     if (n <= SEL_LIST) {
         for (int i = tid; i < n; i += SEL_THREADS) S.list[i] = composite(score_key(row[i]), i);
         __syncthreads();
-        const uint64_t kth = kth_composite(n, K, get, S);
-        write_selected(n, kth, K, get, out, S);
+        const uint64_t kth = kth_composite<SEL_THREADS>(n, K, get, S);
+        write_selected<SEL_THREADS>(n, kth, K, get, out, S);
         return;
     }
     uint32_t lo, sh;
     const int count = gather_candidates(a, t, n, S, &lo, &sh);
     if (count >= (int)K) {
-        const uint64_t kth = kth_from_hist(count, K, get, S, lo, sh);
-        write_selected(count, kth, K, get, out, S);
+        const uint64_t kth = kth_from_hist<SEL_THREADS>(count, K, get, S, lo, sh);
+        write_selected<SEL_THREADS>(count, kth, K, get, out, S);
     } else {   // the sample bound failed for this row
         __syncthreads();
         auto from_row = [&](int i) -> uint64_t { return composite(score_key(row[i]), i); };
-        const uint64_t kth = kth_composite(n, K, from_row, S);
-        write_selected(n, kth, K, from_row, out, S);
+        const uint64_t kth = kth_composite<SEL_THREADS>(n, K, from_row, S);
+        write_selected<SEL_THREADS>(n, kth, K, from_row, out, S);
     }
 }
 
@@ -435,108 +252,6 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_select(TopkArgs a) {
 // a bitonic sort of their indices.  When the list is short of K entries or
 // overflowed, the workgroup computes the row's scores itself (same page
 // scoring as the indexer) into the score rows and selects from them.
-
-// Writes the K entries with composite >= kth, sorted by token index.  Rows
-// of at most SEL_BITMAP tokens mark the selected tokens in an LDS bitmap and
-// read it back in order (one block scan); longer rows sort the indices with
-// a bitonic network.
-constexpr int SEL_BITMAP = SEL_MEMBERS * 64;   // bits in the members space
-template <class Get>
-__device__ void write_selected_sorted(int count, int n, uint64_t kth, uint32_t K, const Get& get, int32_t* out,
-                                      SelShared& S) {
-    constexpr int PER = SEL_LIST / SEL_THREADS;
-    const int tid = threadIdx.x;
-    if (n <= SEL_BITMAP) {
-        uint32_t* bm = reinterpret_cast<uint32_t*>(S.r.members);
-        const int nw = (n + 31) >> 5;
-        for (int i = tid; i < nw; i += SEL_THREADS) bm[i] = 0u;
-        lds_barrier();
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const int i = tid + j * SEL_THREADS;
-            if (i < count) {
-                const uint64_t ck = get(i);
-                if (ck >= kth) {
-                    const int x = composite_index(ck);
-                    atomicOr(&bm[x >> 5], 1u << (x & 31));
-                }
-            }
-        }
-        lds_barrier();
-        // thread tid owns words [w0, w1)
-        const int per = (nw + SEL_THREADS - 1) / SEL_THREADS;
-        const int w0 = min(nw, tid * per), w1 = min(nw, w0 + per);
-        uint32_t c = 0;
-        for (int w = w0; w < w1; ++w) c += (uint32_t)__popc(bm[w]);
-        uint32_t tot;
-        uint32_t pos = block_excl_scan<SEL_WAVES>(c, S.wsum, &tot);
-        for (int w = w0; w < w1; ++w) {
-            uint32_t bits = bm[w];
-            while (bits) {
-                const int bit = __ffs(bits) - 1;
-                bits &= bits - 1u;
-                out[pos++] = 32 * w + bit;
-            }
-        }
-        return;
-    }
-    int32_t* sel = reinterpret_cast<int32_t*>(S.r.members);   // 2 * SEL_MEMBERS slots
-    uint32_t flags = 0u;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        const int i = tid + j * SEL_THREADS;
-        if (i < count && get(i) >= kth) flags |= 1u << j;
-    }
-    uint32_t tot;
-    uint32_t pos = block_excl_scan<SEL_WAVES>((uint32_t)__popc(flags), S.wsum, &tot);
-#pragma unroll
-    for (int j = 0; j < PER; ++j)
-        if ((flags >> j) & 1u) sel[pos++] = composite_index(get(tid + j * SEL_THREADS));
-    int P = 1;
-    while (P < (int)K) P <<= 1;
-    for (int i = (int)K + tid; i < P; i += SEL_THREADS) sel[i] = 0x7FFFFFFF;   // sorts last
-    lds_barrier();
-    for (int size = 2; size <= P; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < P / 2; i += SEL_THREADS) {
-                const int l0 = 2 * i - (i & (stride - 1));
-                const int l1 = l0 + stride;
-                const bool asc = (l0 & size) == 0;
-                const int32_t x = sel[l0], y = sel[l1];
-                if ((x > y) == asc) { sel[l0] = y; sel[l1] = x; }
-            }
-            lds_barrier();
-        }
-    }
-    for (int i = tid; i < (int)K; i += SEL_THREADS) out[i] = sel[i];
-}
-static_assert(2 * SEL_MEMBERS >= TOPK_MAX_K, "sorted selection fits the members space");
-
-// The scores of query row t (n visible tokens) into row, by the indexer's
-// page scoring; pages are spread over the workgroup's waves.
-template <int HT>
-__device__ void recompute_row(const IndexerArgs& ia, int t, int n, float* row) {
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const Geometry& G = ia.g;
-    const int r = G.q_uniform > 0 ? t / G.q_uniform : find_request(G.qsl, G.B, t);
-    const int32_t* pt = G.page_table + (size_t)r * G.max_blocks;
-    i32x8 qf[1][HT];
-    float wv[1][HT][4];
-    load_query<HT>(ia, t, lane, qf[0], wv[0]);
-    const int npages = (n + IDX_PAGE - 1) / IDX_PAGE;
-    for (int pg = wave; pg < npages; pg += SEL_WAVES) {
-        const int blk = __builtin_amdgcn_readfirstlane(pt[pg]);
-        i32x8 kf[4];
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) kf[nt] = load_key_fragment(ia, blk, 16 * nt + (lane & 15), lane);
-        const float ksc = ia.key_scales ? ia.key_scales[(size_t)blk * IDX_PAGE + lane] : 1.f;
-        float ps[1];
-        page_scores<1, HT>(qf, wv, kf, ksc, lane, 1, ps);
-        const int sidx = pg * IDX_PAGE + lane;
-        if (sidx < n) row[sidx] = ps[0];
-    }
-}
 
 template <int HT>
 __global__ __launch_bounds__(SEL_THREADS) void topk_select_cand(TopkArgs a, IndexerArgs ia) {
@@ -550,7 +265,7 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_select_cand(TopkArgs a, Inde
         for (int i = tid; i < (int)K; i += SEL_THREADS) out[i] = i < n ? i : -1;
         return;
     }
-    __shared__ SelShared S;
+    __shared__ SelShared<SEL_THREADS> S;
     const uint32_t cnt = ia.row_count[t];
     if (cnt >= K && cnt <= (uint32_t)SEL_LIST) {
         const int count = (int)cnt;
@@ -579,18 +294,18 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_select_cand(TopkArgs a, Inde
         }
         lds_barrier();
         auto get = [&](int i) -> uint64_t { return S.list[i]; };
-        const uint64_t kth = kth_from_hist(count, K, get, S, lo, sh);
-        write_selected_sorted(count, n, kth, K, get, out, S);
+        const uint64_t kth = kth_from_hist<SEL_THREADS>(count, K, get, S, lo, sh);
+        write_selected_sorted<SEL_THREADS>(count, n, kth, K, get, out, S);
         return;
     }
     // the bound failed for this row: its scores from the keys, then the
     // whole-row selection
     float* row = ia.scores + (size_t)t * ia.ld;
-    recompute_row<HT>(ia, t, n, row);
+    recompute_row<SEL_THREADS, HT>(ia, t, n, row);
     __syncthreads();
     auto from_row = [&](int i) -> uint64_t { return composite(score_key(row[i]), i); };
-    const uint64_t kth = kth_composite(n, K, from_row, S);
-    write_selected(n, kth, K, from_row, out, S);
+    const uint64_t kth = kth_composite<SEL_THREADS>(n, K, from_row, S);
+    write_selected<SEL_THREADS>(n, kth, K, from_row, out, S);
 }
 
 hipError_t launch_emit_step(const IndexerArgs& ia, const TopkArgs& ta, hipStream_t s, const hipEvent_t* ev) {

@@ -86,7 +86,7 @@ __device__ __forceinline__ void wave_min_max(uint32_t& mn, uint32_t& mx) {
 // Exclusive prefix sum over the workgroup (wsum: one slot per wave).
 template <int WAVES>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = tid_x(), lane = tid & 63, wave = tid >> 6;
     uint32_t wt;
     const uint32_t wex = wave_excl_scan(v, &wt);
     if (lane == 0) wsum[wave] = wt;
@@ -106,7 +106,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
 // Workgroup-wide minimum and maximum (red: two slots per wave).
 template <int WAVES>
 __device__ __forceinline__ void block_min_max(uint32_t& mn, uint32_t& mx, uint32_t (*red)[WAVES]) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = tid_x(), lane = tid & 63, wave = tid >> 6;
     wave_min_max(mn, mx);
     if (lane == 0) { red[0][wave] = mn; red[1][wave] = mx; }
     lds_barrier();
@@ -122,7 +122,7 @@ __device__ __forceinline__ void block_min_max(uint32_t& mn, uint32_t& mx, uint32
 __device__ __forceinline__ void lds_count(uint32_t* h, uint32_t bin, bool active) {
     const unsigned long long act = __ballot(active);
     if (act == 0ull) return;
-    const int lane = threadIdx.x & 63;
+    const int lane = tid_x() & 63;
     const int first = __ffsll((long long)act) - 1;
     const uint32_t b0 = (uint32_t)__builtin_amdgcn_readlane((int)bin, first);
     if (__ballot(active && bin == b0) == act) {
@@ -143,7 +143,7 @@ template <int THREADS>
 __device__ uint32_t sample_key_bound(const uint32_t* skeys, int m, int n, uint32_t K, uint32_t* h,
                                      uint32_t (*red)[THREADS / 64], uint32_t* result) {
     constexpr int WAVES = THREADS / 64;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = tid_x(), lane = tid & 63, wave = tid >> 6;
     for (int i = tid; i < 256; i += THREADS) h[i] = 0u;
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
     for (int i = tid; i < m; i += THREADS) { lo = min(lo, skeys[i]); hi = max(hi, skeys[i]); }

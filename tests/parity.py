@@ -74,13 +74,18 @@ def upload(wl, dev="cuda"):
     return batch, d
 
 
-def gpu_step(wl, batch, d, lse=True):
-    """dsa_decode_step on the device; returns (out f32 numpy, lse, indices)."""
+def gpu_step(wl, batch, d, lse=True, fused=False, events=None):
+    """dsa_decode_step (or, with fused, dsa_decode_step_fused) on the device;
+    returns (out f32 numpy, lse, indices)."""
     T, H = wl.total_q, wl.mla_heads
     idx = torch.empty((T, wl.topk), dtype=torch.int32, device="cuda")
     lse_t = torch.empty((T, H), dtype=torch.float32, device="cuda") if lse else None
-    out = dsa.decode_step(batch, d["idx_keys"], d["idx_scales"], d["q_idx"], d["w"], d["kv"], d["kv_scales"],
-                          wl.d_latent, d["q_mla"], wl.topk, wl.softmax_scale, lse=lse_t, indices_out=idx)
+    args = (batch, d["idx_keys"], d["idx_scales"], d["q_idx"], d["w"], d["kv"], d["kv_scales"], wl.d_latent,
+            d["q_mla"], wl.topk, wl.softmax_scale)
+    if fused:
+        out = dsa.decode_step_fused(*args, lse=lse_t, indices_out=idx, events=events)
+    else:
+        out = dsa.decode_step(*args, lse=lse_t, indices_out=idx)
     torch.cuda.synchronize()
     return (out.float().cpu().numpy(), None if lse_t is None else lse_t.cpu().numpy(), idx.cpu().numpy())
 
