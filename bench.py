@@ -286,6 +286,33 @@ class Rig:
     def step(self, i):
         self._ok("dsa_decode_step", self.L.dsa_decode_step(*self.step_args[i % len(self.copies)]))
 
+    def fused_ok(self):
+        """Whether dsa_decode_step_fused takes this workload's shapes."""
+        st = self.L.dsa_decode_step_fused(*self.step_args[0], None, 0)
+        self.torch.cuda.synchronize()
+        return st == 0
+
+    def step_fused(self, i):
+        self._ok("dsa_decode_step_fused", self.L.dsa_decode_step_fused(*self.step_args[i % len(self.copies)],
+                                                                       None, 0))
+
+    def fused_phases(self, iters, warmup):
+        """Average µs of the one-launch step's persistent kernel (events taken
+        by its launch), of its merge, and of the whole call."""
+        torch, B = self.torch, self.B
+        n = len(self.copies)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(B.STEP_EVENTS)] for _ in range(iters)]
+        handles = [B.event_handles(e, self.stream) for e in evs]
+        for i in range(warmup):
+            self.step_fused(i)
+        torch.cuda.synchronize()
+        for i in range(iters):
+            self._ok("dsa_decode_step_fused",
+                     self.L.dsa_decode_step_fused(*self.step_args[i % n], handles[i], B.STEP_EVENTS))
+        torch.cuda.synchronize()
+        avg = lambda a, b: 1e3 * sum(e[a].elapsed_time(e[b]) for e in evs) / iters
+        return {"init": avg(0, 1), "kernel": avg(1, 2), "merge": avg(3, 4), "step": avg(0, 4)}
+
     def group(self, i, layers):
         """One IndexShare group: the full step on one layer's caches, then
         `layers - 1` sparse-MLA layers on other caches reusing its indices."""
@@ -555,7 +582,12 @@ def other_configs(steps, warmup, log):
         sb = step_bytes(wl, rig.selection())
         res[name] = {"ms_per_step": round(ms, 5), "tokens_per_s": round(wl.total_q / (ms * 1e-3), 1),
                      "step_bytes": sb, "step_hbm_frac": round(sb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-        log("[bench] %s: step %.1f us" % (name, ms * 1e3))
+        if rig.fused_ok():
+            msf = rig.time_loop(rig.step_fused, steps, warmup)
+            res[name]["fused_ms_per_step"] = round(msf, 5)
+            log("[bench] %s: step %.1f us, one-launch step %.1f us" % (name, ms * 1e3, msf * 1e3))
+        else:
+            log("[bench] %s: step %.1f us" % (name, ms * 1e3))
         rig.free()
         del rig
     return res
@@ -652,6 +684,21 @@ def main(argv=None):
     sb = step_bytes(wl, indices)
     f_idx, f_mla = step_flops(wl, indices)
     step_gbs = sb / (ms_per_step * 1e-3) / 1e9
+
+    # The same step as one persistent kernel (dsa_decode_step_fused).
+    fused = None
+    if rig.fused_ok():
+        ms_f = rig.time_loop(rig.step_fused, args.steps, args.warmup)
+        fp = rig.fused_phases(n_idx, args.warmup)
+        k_gbs = sb / (fp["kernel"] * 1e-6) / 1e9
+        fused = {"ms_per_step": round(ms_f, 5), "tokens_per_s": round(T / (ms_f * 1e-3), 1),
+                 "step_hbm_frac": round(sb / (ms_f * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                 "phases_us": {k: round(v, 2) for k, v in fp.items()},
+                 "kernel": "fused_decode<1, 4, false>", "kernel_achieved": round(k_gbs, 1),
+                 "kernel_frac": round(k_gbs / PEAK_HBM_GBS, 4),
+                 "basis": "the step's algorithmic bytes over the persistent kernel's own duration"}
+        log("[bench] one-launch step: %.1f us (persistent kernel %.1f us, merge %.1f us)" %
+            (ms_f * 1e3, fp["kernel"], fp["merge"]))
 
     # IndexShare: one full step then (layers-1) MLA-only layers on the same indices.
     share = None
@@ -753,6 +800,7 @@ def main(argv=None):
         "kernel_tflops": {"indexer_fp8": round(f_idx / (phases["indexer"] * 1e-6) / 1e12, 1),
                           "mla_bf16": round(f_mla / (phases["attention"] * 1e-6) / 1e12, 1),
                           "basis": "each contraction's FLOPs over its own phase time"},
+        "fused_step": fused,
         "indexshare": share,
         "all_128k": at128,
         "prefill": prefill,
