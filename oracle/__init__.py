@@ -30,7 +30,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "dsa_oracle.c")
 _LIB = os.path.join(_HERE, "libdsa_oracle.so")
 
-CODE = {"f32": 0, "bf16": 1, "e4m3": 2}
+CODE = {"f32": 0, "bf16": 1, "e4m3": 2, "mxfp4": 3}
 
 _lib = None
 
@@ -56,6 +56,10 @@ def lib():
         L.orc_bf16_to_f64.restype = C.c_double
         L.orc_e4m3_to_f64.argtypes = [C.c_uint8]
         L.orc_e4m3_to_f64.restype = C.c_double
+        L.orc_e2m1_to_f64.argtypes = [C.c_uint8]
+        L.orc_e2m1_to_f64.restype = C.c_double
+        L.orc_e8m0_to_f64.argtypes = [C.c_uint8]
+        L.orc_e8m0_to_f64.restype = C.c_double
         L.orc_indexer_scores.argtypes = [vp, f32p, C.c_int, C.c_int, i32p, C.c_int,
                                          vp, C.c_int, f32p, C.c_int, C.c_int, f64p]
         L.orc_indexer_scores.restype = None
@@ -89,10 +93,26 @@ def decode_e4m3(codes) -> np.ndarray:
     return np.array([L.orc_e4m3_to_f64(int(x)) for x in c], dtype=np.float64)
 
 
+def decode_e2m1(codes) -> np.ndarray:
+    """OCP FP4 E2M1 codes (low 4 bits of each value) to float64."""
+    L = lib()
+    c = np.asarray(codes, dtype=np.uint8).ravel()
+    return np.array([L.orc_e2m1_to_f64(int(x) & 0xF) for x in c], dtype=np.float64)
+
+
+def decode_e8m0(exps) -> np.ndarray:
+    """OCP E8M0 scale bytes to float64 (2^(e-127), NaN for 255)."""
+    L = lib()
+    e = np.asarray(exps, dtype=np.uint8).ravel()
+    return np.array([L.orc_e8m0_to_f64(int(x)) for x in e], dtype=np.float64)
+
+
 def indexer_scores(keys, key_scales, key_code, page_row, block_size, q, q_code, w, n):
     """Scores of one query over its visible tokens [0, n) (float64 [n]).
 
-    keys [nblk][bs][dim]; key_scales [nblk][bs] or None; q [H][dim]; w [H].
+    keys [nblk][bs][dim] (MXFP4: [nblk][bs * (dim/2 + dim/32)] bytes, codes
+    then E8M0 scales per block); key_scales [nblk][bs] or None; q [H][dim];
+    w [H].
     """
     keys = np.ascontiguousarray(keys)
     q = np.ascontiguousarray(q)
@@ -100,7 +120,11 @@ def indexer_scores(keys, key_scales, key_code, page_row, block_size, q, q_code, 
     page_row = np.ascontiguousarray(page_row, dtype=np.int32)
     ks = None if key_scales is None else np.ascontiguousarray(key_scales, dtype=np.float32)
     H, dim = q.shape
-    assert keys.shape[-1] == dim and w.shape == (H,)
+    if key_code == "mxfp4":
+        assert dim % 32 == 0 and keys.shape[-1] == block_size * (dim // 2 + dim // 32)
+    else:
+        assert keys.shape[-1] == dim
+    assert w.shape == (H,)
     out = np.empty(max(n, 1), dtype=np.float64)
     lib().orc_indexer_scores(_v(keys), _p(ks, C.c_float), CODE[key_code], dim,
                              _p(page_row, C.c_int32), block_size, _v(q), CODE[q_code],

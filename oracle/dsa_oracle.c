@@ -25,7 +25,13 @@
  *   - the fp8 latent scale covers all d+r columns of the row;
  *   - softmax uses the given scale on the logits; lse is in natural log.
  *
- * Storage codes: 0 = fp32, 1 = bf16 bit patterns, 2 = OCP e4m3fn codes.
+ * Storage codes: 0 = fp32, 1 = bf16 bit patterns, 2 = OCP e4m3fn codes,
+ * 3 = MXFP4 index keys (OCP Microscaling Formats v1.0: blocks of 32 FP4
+ * E2M1 elements sharing one E8M0 power-of-two scale).  An MXFP4 key cache
+ * stores each block of block_size tokens as block_size x dim/2 bytes of
+ * packed E2M1 codes (element 2i in the low nibble of byte i, 2i+1 in the
+ * high nibble), then block_size x dim/32 E8M0 bytes (scale b of a token
+ * covers its elements [32b, 32b + 32)).
  * Paged addressing: logical token s of a request lives in physical block
  * page_row[s / block_size], slot s % block_size; a cache of row width W is
  * stored as [num_blocks][block_size][W].
@@ -35,7 +41,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_E4M3 = 2 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_E4M3 = 2, ORC_MXFP4 = 3 };
 
 /* bf16 is the high half of an IEEE binary32. */
 double orc_bf16_to_f64(uint16_t bits)
@@ -61,6 +67,29 @@ double orc_e4m3_to_f64(uint8_t code)
     else
         v = ldexp((double)(8 + m), e - 10);   /* (1 + m/8) * 2^(e-7) */
     return sign ? -v : v;
+}
+
+/* OCP FP4 E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa bit; exponent 0
+ * is subnormal; no infinities or NaN. */
+double orc_e2m1_to_f64(uint8_t code)
+{
+    int sign = (code >> 3) & 1;
+    int e = (code >> 1) & 3;
+    int m = code & 1;
+    double v;
+    if (e == 0)
+        v = 0.5 * (double)m;                  /* (m/2) * 2^(1-1) */
+    else
+        v = ldexp(1.0 + 0.5 * (double)m, e - 1);
+    return sign ? -v : v;
+}
+
+/* OCP E8M0 scale: 2^(e - 127); 255 is NaN. */
+double orc_e8m0_to_f64(uint8_t e)
+{
+    if (e == 255)
+        return NAN;
+    return ldexp(1.0, (int)e - 127);
 }
 
 static double load_elem(const void *base, int code, size_t i)
@@ -89,11 +118,28 @@ static void load_row(const void *cache, const float *scales, int code, int W,
         out[c] = sc * load_elem(cache, code, row * (size_t)W + (size_t)c);
 }
 
+/* Decode the MXFP4 key of logical token s (dim elements) into out[dim]:
+ * element d = E2M1(code d) * E8M0(scale d / 32) of its block. */
+static void load_mxfp4_key(const void *keys, int dim, const int32_t *page_row, int block_size, int s,
+                           double *out)
+{
+    const uint8_t *blk = (const uint8_t *)keys +
+                         (size_t)page_row[s / block_size] * (size_t)block_size * (size_t)(dim / 2 + dim / 32);
+    int slot = s % block_size;
+    const uint8_t *codes = blk + (size_t)slot * (size_t)(dim / 2);
+    const uint8_t *exps = blk + (size_t)block_size * (size_t)(dim / 2) + (size_t)slot * (size_t)(dim / 32);
+    for (int d = 0; d < dim; ++d) {
+        uint8_t code = (uint8_t)((codes[d / 2] >> (4 * (d & 1))) & 0xF);
+        out[d] = orc_e2m1_to_f64(code) * orc_e8m0_to_f64(exps[d / 32]);
+    }
+}
+
 /*
  * Lightning-indexer scores of one query token over its visible tokens
  * [0, n):  I[s] = sigma_s * sum_h w[h] * max(0, sum_d q[h][d] * k_s[d]).
- * keys: [nblk][block_size][dim] in code key_code, key_scales [nblk][block_size]
- * or NULL (sigma = 1).  q: [n_heads][dim] in code q_code.  w: [n_heads].
+ * keys: [nblk][block_size][dim] in code key_code (or the MXFP4 block layout
+ * above), key_scales [nblk][block_size] or NULL (sigma = 1).  q: [n_heads][dim]
+ * in code q_code.  w: [n_heads].
  */
 void orc_indexer_scores(const void *keys, const float *key_scales, int key_code, int dim,
                         const int32_t *page_row, int block_size,
@@ -109,7 +155,10 @@ void orc_indexer_scores(const void *keys, const float *key_scales, int key_code,
     for (int s = 0; s < n; ++s) {
         size_t row = phys_row(page_row, block_size, s);
         double sigma = key_scales ? (double)key_scales[row] : 1.0;
-        load_row(keys, NULL, key_code, dim, row, kd);   /* raw key, scale below */
+        if (key_code == ORC_MXFP4)
+            load_mxfp4_key(keys, dim, page_row, block_size, s, kd);
+        else
+            load_row(keys, NULL, key_code, dim, row, kd);   /* raw key, scale below */
         double total = 0.0;
         for (int h = 0; h < n_heads; ++h) {
             double dot = 0.0;

@@ -95,8 +95,8 @@ class Workload:
     num_blocks: int
     idx_heads: int
     idx_dim: int
-    idx_dtype: str                # "f32" | "e4m3"
-    idx_keys: np.ndarray          # [nblk][bs][dim]  float32 or uint8 codes
+    idx_dtype: str                # "f32" | "e4m3" | "mxfp4"
+    idx_keys: np.ndarray          # [nblk][bs][dim] float32 or uint8 codes; mxfp4: [nblk][bs*(dim/2+dim/32)]
     idx_scales: Optional[np.ndarray]  # float32 [nblk][bs] or None
     q_idx: np.ndarray             # [T][H_idx][dim] float32 or uint8 codes
     w: np.ndarray                 # float32 [T][H_idx]
@@ -158,6 +158,31 @@ def _rowwise_e4m3(x: np.ndarray):
 
 
 # ------------------------------------------------------------ pool drawing
+# Non-negative FP4 E2M1 magnitudes in code order (OCP Microscaling Formats
+# v1.0), for quantising synthetic keys: codes are the generator's output,
+# their decoding belongs to the oracle.
+_E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float32)
+
+
+def _mxfp4_block_codes(x: np.ndarray):
+    """MX quantisation of x [..., dim] (dim % 32 == 0): per 32-element block
+    a power-of-two scale 2^E with E = floor(log2 amax) - 2 (the largest E2M1
+    exponent), elements rounded to the nearest E2M1 value (saturating at 6).
+    Returns (packed codes [..., dim/2] uint8, E8M0 bytes [..., dim/32])."""
+    sh = x.shape
+    blk = x.reshape(sh[:-1] + (sh[-1] // 32, 32))
+    amax = np.abs(blk).max(axis=-1)
+    e = np.where(amax > 0, np.floor(np.log2(np.maximum(amax, 1e-30))) - 2, 0).astype(np.int32)
+    e = np.clip(e, -126, 127)
+    y = np.abs(blk) / np.exp2(e)[..., None].astype(np.float32)
+    mid = (_E2M1_GRID[1:] + _E2M1_GRID[:-1]) / 2
+    mag = np.searchsorted(mid, np.minimum(y, 6.0), side="left").astype(np.uint8)
+    code = mag | np.where(blk < 0, 8, 0).astype(np.uint8)
+    code = code.reshape(sh)
+    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
+    return packed, (e + 127).astype(np.uint8)
+
+
 def _draw_slab(seed, tag, slab, nblk_total, bs, width, enc):
     b0 = slab * SLAB_BLOCKS
     nb = min(SLAB_BLOCKS, nblk_total - b0)
@@ -165,6 +190,11 @@ def _draw_slab(seed, tag, slab, nblk_total, bs, width, enc):
     x = rng.standard_normal((nb, bs, width), dtype=np.float32)
     if enc == "f32":
         return b0, x, None
+    if enc == "mxfp4":   # per block: bs rows of codes, then bs rows of E8M0 scales
+        packed, exps = _mxfp4_block_codes(x)
+        data = np.concatenate([packed.reshape(nb, -1), exps.reshape(nb, -1)], axis=1)
+        sigma = rng.uniform(0.5, 2.0, size=(nb, bs)).astype(np.float32)
+        return b0, data, sigma
     if enc == "bf16":
         return b0, bf16_bits(x), None
     codes, scale = _rowwise_e4m3(x)
@@ -173,9 +203,10 @@ def _draw_slab(seed, tag, slab, nblk_total, bs, width, enc):
 
 def draw_pool(seed, tag, nblk, bs, width, enc, threads=None):
     """Draw a [nblk][bs][width] pool in the given encoding, slab by slab."""
-    dt = {"f32": np.float32, "bf16": np.uint16, "e4m3": np.uint8}[enc]
-    data = np.empty((nblk, bs, width), dtype=dt)
-    scales = np.empty((nblk, bs), dtype=np.float32) if enc == "e4m3" else None
+    dt = {"f32": np.float32, "bf16": np.uint16, "e4m3": np.uint8, "mxfp4": np.uint8}[enc]
+    shape = (nblk, bs * (width // 2 + width // 32)) if enc == "mxfp4" else (nblk, bs, width)
+    data = np.empty(shape, dtype=dt)
+    scales = np.empty((nblk, bs), dtype=np.float32) if enc in ("e4m3", "mxfp4") else None
     nslab = (nblk + SLAB_BLOCKS - 1) // SLAB_BLOCKS
     threads = threads or min(16, os.cpu_count() or 1)
 
@@ -239,7 +270,7 @@ def make_workload(name: str = "tiny_fp32_l4096", **overrides) -> Workload:
 
     Hi, Di = int(cfg["idx_heads"]), int(cfg["idx_dim"])
     idt = cfg["idx_dtype"]
-    keys, kscales = draw_pool(seed, _TAG_KEYS, nblk, bs, Di, "f32" if idt == "f32" else "e4m3")
+    keys, kscales = draw_pool(seed, _TAG_KEYS, nblk, bs, Di, idt)
 
     qf = rng.standard_normal((T, Hi, Di), dtype=np.float32)
     w = rng.uniform(0.0, 1.0, size=(T, Hi)).astype(np.float32)
