@@ -94,11 +94,24 @@ def latent_row_bytes(wl):
     return {"f32": 4 * W, "bf16": 2 * W, "e4m3": W + 4}[wl.kv_dtype]
 
 
+def key_row_bytes(wl):
+    """Bytes of one token's index key: fp32 or e4m3 elements, or MXFP4 (half
+    a byte an element plus one E8M0 byte per 32), and its fp32 sigma."""
+    D = wl.idx_dim
+    elems = {"f32": 4 * D, "e4m3": D, "mxfp4": D // 2 + D // 32}[wl.idx_dtype]
+    return elems + (4 if wl.idx_scales is not None else 0)
+
+
+def query_row_bytes(wl):
+    """Bytes of one indexer query row (fp32, or e4m3 for e4m3 and MXFP4 keys)
+    and its fp32 head weights."""
+    return wl.idx_heads * wl.idx_dim * (4 if wl.idx_dtype == "f32" else 1) + 4 * wl.idx_heads
+
+
 def indexer_launch_bytes(wl):
     """Bytes one indexer launch must move: keys + scales + page table per
     visible token range, queries and weights, and the fp32 scores it writes."""
-    key_row = wl.idx_dim * (1 if wl.idx_dtype == "e4m3" else 4) + (4 if wl.idx_scales is not None else 0)
-    q_row = wl.idx_heads * wl.idx_dim * (1 if wl.idx_dtype == "e4m3" else 4) + 4 * wl.idx_heads
+    key_row, q_row = key_row_bytes(wl), query_row_bytes(wl)
     total = 0
     for r in range(wl.batch):
         L, ql = int(wl.context_lens[r]), int(wl.q_lens[r])
@@ -118,8 +131,7 @@ def indexer_read_bytes(wl):
 def step_bytes(wl, indices):
     """Algorithmic bytes of one whole step (formula in the module docstring)."""
     import numpy as np
-    key_row = wl.idx_dim * (1 if wl.idx_dtype == "e4m3" else 4) + (4 if wl.idx_scales is not None else 0)
-    q_row = wl.idx_heads * wl.idx_dim * (1 if wl.idx_dtype == "e4m3" else 4) + 4 * wl.idx_heads
+    key_row, q_row = key_row_bytes(wl), query_row_bytes(wl)
     e_q = 4 if wl.kv_dtype == "f32" else 2
     mla_q = wl.mla_heads * (wl.d_latent + wl.d_rope) * e_q + wl.mla_heads * wl.d_latent * e_q
     total = 0
@@ -265,7 +277,8 @@ class Rig:
         wsp, idxp = C.c_void_p(self.ws.data_ptr()), C.c_void_p(self.idx.data_ptr())
         self.step_args, self.mla_args, self.idx_args, self._keep = [], [], [], []
         for ci, dc in enumerate(self.copies):
-            ic = B.index_cache(dc["idx_keys"], dc["idx_scales"])
+            keys = B.MxFp4Keys(dc["idx_keys"], wl.idx_dim) if wl.idx_dtype == "mxfp4" else dc["idx_keys"]
+            ic = B.index_cache(keys, dc["idx_scales"])
             lc = B.latent_cache(dc["kv"], dc["kv_scales"], wl.d_latent)
             self._keep += [ic, lc]
             outp, qm = C.c_void_p(self.outs[ci].data_ptr()), C.c_void_p(dc["q_mla"].data_ptr())
@@ -593,6 +606,29 @@ def other_configs(steps, warmup, log):
     return res
 
 
+def mxfp4_leg(steps, warmup, log):
+    """The default decode workload with MXFP4 index keys (E2M1 elements, one
+    E8M0 scale per 32; e4m3 queries): the score-writing indexer launch and
+    the decode step (which takes MXFP4 keys through score rows and the
+    top-K selection)."""
+    import workloads
+    wl = workloads.make_workload(DEFAULT_WORKLOAD, idx_dtype="mxfp4")
+    rig = Rig(wl, 4, lambda *a: None)
+    ms = rig.time_loop(rig.step, steps, warmup)
+    sb = step_bytes(wl, rig.selection())
+    us = rig.time_launches(rig.indexer, max(steps, 20), warmup)
+    ib = indexer_launch_bytes(wl)
+    res = {"workload": wl.name + " (MXFP4 keys)", "key_bytes_per_token": key_row_bytes(wl),
+           "ms_per_step": round(ms, 5), "tokens_per_s": round(wl.total_q / (ms * 1e-3), 1), "step_bytes": sb,
+           "step_hbm_frac": round(sb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+           "indexer_kernel": "indexer_mxfp4<1, 4> (dsa_indexer_scores)", "indexer_us": round(us, 2),
+           "indexer_bytes": ib, "indexer_hbm_frac": round(ib / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    log("[bench] MXFP4 keys: step %.1f us, indexer %.1f us (%.0f GB/s)" % (ms * 1e3, us, ib / (us * 1e-6) / 1e9))
+    rig.free()
+    del rig
+    return res
+
+
 def read_ceiling(log, nbytes=1 << 31, iters=20):
     """The library's streaming-read probe over 2 GiB (every byte read once
     with 16-byte non-temporal loads): the practical HBM read ceiling next to
@@ -743,6 +779,11 @@ def main(argv=None):
         others = other_configs(max(10, min(args.steps, 50)), 5, log)
         ceiling = read_ceiling(log)
 
+    # MXFP4 index keys on the same workload.
+    fp4 = None
+    if not args.no_others and args.workload == DEFAULT_WORKLOAD:
+        fp4 = mxfp4_leg(max(10, min(args.steps, 50)), 5, log)
+
     # Two-tier latent cache: fetch + MLA over the hot set on drifting selections.
     hot = None
     if not args.no_hot_cache and args.workload == DEFAULT_WORKLOAD:
@@ -801,6 +842,7 @@ def main(argv=None):
                           "mla_bf16": round(f_mla / (phases["attention"] * 1e-6) / 1e12, 1),
                           "basis": "each contraction's FLOPs over its own phase time"},
         "fused_step": fused,
+        "mxfp4_keys": fp4,
         "indexshare": share,
         "all_128k": at128,
         "prefill": prefill,

@@ -148,9 +148,28 @@ class Batch:
                         self.page_table.data_ptr(), self.page_table.shape[1], self.block_size)
 
 
-def index_cache(keys: torch.Tensor, scales: Optional[torch.Tensor]) -> DsaIndexCache:
-    return DsaIndexCache(keys.data_ptr(), scales.data_ptr() if scales is not None else None,
-                         dtype_code(keys), keys.shape[-1])
+DSA_MXFP4 = 3
+
+
+class MxFp4Keys:
+    """An MXFP4 index-key cache: `data` uint8 [num_blocks][block_size *
+    (dim/2 + dim/32)] (per block: packed E2M1 codes, then E8M0 scales) and
+    the key dimension `dim` (a multiple of 32)."""
+
+    def __init__(self, data: torch.Tensor, dim: int):
+        if data.dtype != torch.uint8 or dim % 32:
+            raise ValueError("MXFP4 keys are uint8 bytes with dim a multiple of 32")
+        self.data, self.dim = data, dim
+
+    def data_ptr(self):
+        return self.data.data_ptr()
+
+
+def index_cache(keys, scales: Optional[torch.Tensor]) -> DsaIndexCache:
+    sp = scales.data_ptr() if scales is not None else None
+    if isinstance(keys, MxFp4Keys):
+        return DsaIndexCache(keys.data_ptr(), sp, DSA_MXFP4, keys.dim)
+    return DsaIndexCache(keys.data_ptr(), sp, dtype_code(keys), keys.shape[-1])
 
 
 def latent_cache(kv: torch.Tensor, scales: Optional[torch.Tensor], d_latent: int) -> DsaLatentCache:

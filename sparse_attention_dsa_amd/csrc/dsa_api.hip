@@ -228,7 +228,9 @@ int check_device_cached() {
 }
 
 bool index_cache_ok(const dsa_index_cache* c) {
-    return c && c->keys && c->dim >= 1 && (c->dtype == DSA_F32 || c->dtype == DSA_E4M3);
+    if (!c || !c->keys || c->dim < 1) return false;
+    if (c->dtype == DSA_MXFP4) return c->dim % 32 == 0;
+    return c->dtype == DSA_F32 || c->dtype == DSA_E4M3;
 }
 
 bool latent_cache_ok(const dsa_latent_cache* c) {

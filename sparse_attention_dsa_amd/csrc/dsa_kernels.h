@@ -113,6 +113,14 @@ __device__ __forceinline__ T ld_agent(const T* p) {
     return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// max(x, 0) in one instruction: fmaxf would first canonicalize an input it
+// cannot prove canonical (an MFMA result, for one); x is never NaN here.
+__device__ __forceinline__ float relu(float x) {
+    float r;
+    asm("v_max_f32 %0, 0, %1" : "=v"(r) : "v"(x));
+    return r;
+}
+
 // ------------------------------------------------ asynchronous LDS fills
 // One 64-lane transfer global -> LDS at LDS address m0v (wave-uniform; lane
 // l's bytes land at m0v + l * size): 16 B a lane (plain, or streamed: not
@@ -281,6 +289,9 @@ int device_cu_count();
 // persistent kernel, taken by its launch itself).
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s, const hipEvent_t* se = nullptr);
 // -inf over every score row's entries past its visible tokens, [n_t, ld).
+// MXFP4 index keys (key_dtype 3): the fast kernel's shapes, and its launch.
+bool mxfp4_fast(const IndexerArgs& a);
+hipError_t launch_indexer_mxfp4(const IndexerArgs& a, hipStream_t s);
 hipError_t launch_score_tail(const IndexerArgs& a, hipStream_t s);
 // Whether the decode step can take the candidate-emission path for this
 // shape (e4m3 keys, dim 128, 16/32/64 heads, 64-token blocks, persistent grid).

@@ -672,8 +672,22 @@ __global__ __launch_bounds__(SB_THREADS) void indexer_sample_bound(IndexerArgs a
     if (tid == 0) a.bound[t] = x;
 }
 
-// Generic path: any head count / dim, fp32 or e4m3 keys and queries, any block
-// size.  One thread per (query row, token); the query and weights sit in LDS.
+// FP4 E2M1 code (low 4 bits) and E8M0 scale byte to float (OCP Microscaling
+// Formats v1.0: E2M1 has exponent bias 1 and one mantissa bit, exponent 0 is
+// subnormal; E8M0 is 2^(e - 127), 255 is NaN).
+__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
+    const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+    const float mag = e == 0u ? 0.5f * (float)m : __uint_as_float((126u + e) << 23) * (1.0f + 0.5f * (float)m);
+    return (c & 8u) ? -mag : mag;
+}
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+    if (e == 255u) return __builtin_nanf("");
+    return e == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(e << 23);
+}
+
+// Generic path: any head count / dim, fp32, e4m3 or MXFP4 keys (fp32 or e4m3
+// queries), any block size.  One thread per (query row, token); the query and
+// weights sit in LDS.
 __global__ __launch_bounds__(256) void indexer_generic(IndexerArgs a) {
     const Geometry& G = a.g;
     const int t = blockIdx.y;
@@ -683,7 +697,8 @@ __global__ __launch_bounds__(256) void indexer_generic(IndexerArgs a) {
     extern __shared__ float smem[];
     float* qv = smem;            // [H][D]
     float* wv = smem + H * D;    // [H]
-    const bool f8 = a.key_dtype == 2;
+    const bool f8 = a.key_dtype == 2 || a.key_dtype == 3;   // e4m3 queries
+    const bool f4 = a.key_dtype == 3;
     for (int i = threadIdx.x; i < H * D; i += blockDim.x) {
         const size_t off = (size_t)t * H * D + i;
         qv[i] = f8 ? e4m3_to_f32(((const uint8_t*)a.q)[off]) : ((const float*)a.q)[off];
@@ -693,13 +708,20 @@ __global__ __launch_bounds__(256) void indexer_generic(IndexerArgs a) {
     const int s = blockIdx.x * blockDim.x + threadIdx.x;
     if (s >= n) return;
     const int bs = G.block_size;
-    const size_t row = (size_t)G.page_table[(size_t)r * G.max_blocks + s / bs] * bs + s % bs;
+    const size_t blk = (size_t)G.page_table[(size_t)r * G.max_blocks + s / bs];
+    const size_t row = blk * bs + s % bs;
+    // MXFP4: this token's codes and block scales inside its block
+    const uint8_t* f4c = (const uint8_t*)a.keys + blk * bs * (size_t)(D / 2 + D / 32) + (size_t)(s % bs) * (D / 2);
+    const uint8_t* f4e = (const uint8_t*)a.keys + blk * bs * (size_t)(D / 2 + D / 32) + (size_t)bs * (D / 2) +
+                         (size_t)(s % bs) * (D / 32);
     float total = 0.f;
     for (int h = 0; h < H; ++h) {
         float dot = 0.f;
         for (int d = 0; d < D; ++d) {
             const size_t off = row * D + d;
-            const float k = f8 ? e4m3_to_f32(((const uint8_t*)a.keys)[off]) : ((const float*)a.keys)[off];
+            float k;
+            if (f4) k = e2m1_to_f32((uint32_t)(f4c[d >> 1] >> (4 * (d & 1)))) * e8m0_to_f32(f4e[d >> 5]);
+            else k = f8 ? e4m3_to_f32(((const uint8_t*)a.keys)[off]) : ((const float*)a.keys)[off];
             dot = fmaf(qv[h * D + d], k, dot);
         }
         total = fmaf(wv[h], fmaxf(dot, 0.f), total);
@@ -791,6 +813,11 @@ hipError_t launch_score_tail(const IndexerArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s, const hipEvent_t* se) {
+    if (a.key_dtype == 3 && mxfp4_fast(a)) {
+        hipError_t e = se ? hipEventRecord(se[0], s) : hipSuccess;
+        if (e == hipSuccess) e = launch_indexer_mxfp4(a, s);
+        return e == hipSuccess && se ? hipEventRecord(se[1], s) : e;
+    }
     const bool fast = a.key_dtype == 2 && a.dim == IDX_D && a.g.block_size == IDX_PAGE &&
                       (a.n_heads == 64 || a.n_heads == 32 || a.n_heads == 16);
     if (fast && a.g.max_q_len < PF_MIN_Q) {

@@ -41,6 +41,10 @@ def score_bound(wl, t):
     r, p, n = oracle.query_positions(wl)[t]
     if wl.idx_dtype == "f32":
         keys, q = np.abs(wl.idx_keys), np.abs(wl.q_idx[t])
+    elif wl.idx_dtype == "mxfp4":   # both nibbles' sign bits cleared; the E8M0 bytes kept
+        keys, q = wl.idx_keys.copy(), wl.q_idx[t] & np.uint8(0x7F)
+        nc = wl.block_size * wl.idx_dim // 2
+        keys[:, :nc] &= np.uint8(0x77)
     else:
         keys, q = wl.idx_keys & np.uint8(0x7F), wl.q_idx[t] & np.uint8(0x7F)
     mag = oracle.indexer_scores(keys, wl.idx_scales, wl.idx_dtype, wl.page_table[r], wl.block_size, q,
@@ -69,6 +73,8 @@ def log(*a):
 
 def upload(wl, dev="cuda"):
     d = workloads.to_device(wl, dev)
+    if wl.idx_dtype == "mxfp4":
+        d["idx_keys"] = dsa.binding.MxFp4Keys(d["idx_keys"], wl.idx_dim)
     batch = dsa.Batch(d["context_lens"], d["query_start_loc"], d["page_table"], wl.block_size,
                       wl.max_q_len, wl.max_context_len)
     return batch, d

@@ -65,6 +65,8 @@ def test_invalid_arguments_rejected_before_device(L):
     assert L.dsa_indexer_scores(C.byref(b), C.byref(ic), 0x1, 0x1, 64, 0x1, 10, None) == -1  # ld < ctx
     bad_dt = B.DsaIndexCache(0x10, None, B.BF16, 128)
     assert L.dsa_indexer_scores(C.byref(b), C.byref(bad_dt), 0x1, 0x1, 64, 0x1, 1024, None) == -2
+    bad_f4 = B.DsaIndexCache(0x10, None, B.DSA_MXFP4, 48)   # MXFP4 blocks of 32 need dim % 32 == 0
+    assert L.dsa_indexer_scores(C.byref(b), C.byref(bad_f4), 0x1, 0x1, 64, 0x1, 1024, None) == -2
     assert L.dsa_topk(C.byref(b), 0x1, 1024, 0, 0x1, 0x1, 1 << 30, None) == -1
     assert L.dsa_topk(C.byref(b), 0x1, 1024, 5000, 0x1, 0x1, 1 << 30, None) == -2
     assert L.dsa_topk(C.byref(long_b := _batch(maxctx=100000, maxblocks=1600)), 0x1, 100000, 16, 0x1, 0x1, 8,

@@ -7,6 +7,7 @@ import types
 import numpy as np
 
 import bench
+import workloads
 
 
 def test_mla_intensity_matches_the_printed_values():
@@ -70,3 +71,13 @@ def test_step_flops_hand_count():
     assert f_idx == 16384 * 6099
     # MLA: 2 x 128 x (576 + 512) = 278528 FLOP per selected token, 500 of them
     assert f_mla == 278528 * 500
+
+
+def test_mxfp4_key_bytes_hand_count():
+    """MXFP4 keys: 128 elements x half a byte + 4 E8M0 bytes + 4 B sigma = 72
+    bytes a token; queries stay e4m3 (64 x 128 B + 64 x 4 B of w = 8448)."""
+    wl = workloads.make_workload("single_b1_l32768", batch=1, context_lens=[100], idx_dtype="mxfp4", seed=1)
+    assert bench.key_row_bytes(wl) == 64 + 4 + 4 == 72
+    assert bench.query_row_bytes(wl) == 8448
+    # 100 keys x 72 + 2 page-table entries x 4 + one query row
+    assert bench.indexer_read_bytes(wl) == 7200 + 8 + 8448
