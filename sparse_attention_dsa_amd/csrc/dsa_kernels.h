@@ -113,13 +113,10 @@ __device__ __forceinline__ T ld_agent(const T* p) {
     return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// max(x, 0) in one instruction: fmaxf would first canonicalize an input it
-// cannot prove canonical (an MFMA result, for one); x is never NaN here.
-__device__ __forceinline__ float relu(float x) {
-    float r;
-    asm("v_max_f32 %0, 0, %1" : "=v"(r) : "v"(x));
-    return r;
-}
+// max(x, 0).  (Inline asm would drop the canonicalizing v_max that fmaxf
+// puts before it, but inline asm is outside the compiler's hazard tracking:
+// a VALU read of an MFMA result then loses the wait states it needs.)
+__device__ __forceinline__ float relu(float x) { return fmaxf(x, 0.f); }
 
 // ------------------------------------------------ asynchronous LDS fills
 // One 64-lane transfer global -> LDS at LDS address m0v (wave-uniform; lane

@@ -192,7 +192,7 @@ __device__ __forceinline__ void page_scores_ilp(const i32x8 (&qf)[NQ][HT], const
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc += wv[j][ht][i] * fmaxf(c[nt & 1][j][ht][i], 0.f);
+                for (int i = 0; i < 4; ++i) acc = fmaf(wv[j][ht][i], relu(c[nt & 1][j][ht][i]), acc);
             part[j][nt] = acc;
         }
     }

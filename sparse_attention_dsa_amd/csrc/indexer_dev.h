@@ -83,13 +83,16 @@ __device__ __forceinline__ void page_scores(const i32x8 (&qf)[NQ][HT], const flo
             float part[4];
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
+                // the tile's MFMAs first (distinct results, issued back to
+                // back), then their weighted ReLU sum in the same order
+                f32x4 c[HT];
+#pragma unroll
+                for (int ht = 0; ht < HT; ++ht) c[ht] = mfma_fp8_16x16x128(qf[j][ht], kf[nt], zero);
                 float acc = 0.f;
 #pragma unroll
-                for (int ht = 0; ht < HT; ++ht) {
-                    const f32x4 c = mfma_fp8_16x16x128(qf[j][ht], kf[nt], zero);
+                for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) acc += wv[j][ht][i] * fmaxf(c[i], 0.f);
-                }
+                    for (int i = 0; i < 4; ++i) acc = fmaf(wv[j][ht][i], relu(c[ht][i]), acc);
                 part[nt] = acc;
             }
             out[j] = head_sum_transpose(part, lane) * ksc;
@@ -125,13 +128,14 @@ __device__ __forceinline__ i32x8 load_key_fragment(const IndexerArgs& a, int blk
 template <int HT>
 __device__ __forceinline__ float token_head_sum(const i32x8 (&qf)[HT], const float (&wv)[HT][4], i32x8 kf) {
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 c[HT];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) c[ht] = mfma_fp8_16x16x128(qf[ht], kf, zero);
     float acc = 0.f;
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-        const f32x4 c = mfma_fp8_16x16x128(qf[ht], kf, zero);
+    for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc += wv[ht][i] * fmaxf(c[i], 0.f);
-    }
+        for (int i = 0; i < 4; ++i) acc = fmaf(wv[ht][i], relu(c[ht][i]), acc);
     acc += __shfl_xor(acc, 16);
     acc += __shfl_xor(acc, 32);
     return acc;
