@@ -662,6 +662,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--copies", type=int, default=4, help="rotating device copies of the caches")
+    ap.add_argument("--idx-dtype", default=None, choices=["e4m3", "mxfp4"],
+                    help="index-key encoding of the workload (default: the workload's own)")
     ap.add_argument("--cpu-rows", type=int, default=64, help="query rows in the oracle CPU sample (0: skip)")
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--share-layers", type=int, default=4,
@@ -691,7 +693,8 @@ def main(argv=None):
 
     torch.cuda.set_device(0)
     t0 = time.time()
-    wl = workloads.make_workload(args.workload)
+    wl = (workloads.make_workload(args.workload, idx_dtype=args.idx_dtype) if args.idx_dtype
+          else workloads.make_workload(args.workload))
     log("[bench] workload %s: B=%d T=%d sum L=%d (generated in %.1fs)" %
         (wl.name, wl.batch, wl.total_q, int(wl.context_lens.sum()), time.time() - t0))
     rig = Rig(wl, args.copies, log)
@@ -707,7 +710,9 @@ def main(argv=None):
     # events the library records around its launch.
     n_idx = max(args.steps, 20)
     phases = rig.step_phases(n_idx, args.warmup)
-    emit_us, emit_bytes = phases["indexer"], indexer_read_bytes(wl)
+    # MXFP4 keys take the score-writing indexer inside the step
+    emit = wl.idx_dtype == "e4m3"
+    emit_us, emit_bytes = phases["indexer"], indexer_read_bytes(wl) if emit else indexer_launch_bytes(wl)
     emit_gbs = emit_bytes / (emit_us * 1e-6) / 1e9
     log("[bench] step phases (us): " + ", ".join("%s %.1f" % kv for kv in phases.items()))
     log("[bench] indexer in the step: %.1f us, %.1f MB -> %.0f GB/s" % (emit_us, emit_bytes / 1e6, emit_gbs))
@@ -824,10 +829,12 @@ def main(argv=None):
                    "context": "L_r ~ U[8192, 131072]" if wl.name == DEFAULT_WORKLOAD else
                    "L_r = %s" % sorted(set(wl.context_lens.tolist()))[:4],
                    "mean_context": round(float(wl.context_lens.mean()), 1), "topk": K,
-                   "indexer": "%dx%d e4m3" % (wl.idx_heads, wl.idx_dim), "mla_heads": wl.mla_heads,
+                   "indexer": "%dx%d %s" % (wl.idx_heads, wl.idx_dim, wl.idx_dtype), "mla_heads": wl.mla_heads,
                    "latent": "%d+%d %s" % (wl.d_latent, wl.d_rope, wl.kv_dtype), "block_size": wl.block_size,
                    "input_copies": args.copies},
-        "roofline": {"bound": "hbm", "kernel": "indexer_fp8_persistent<1, 4, true> (in dsa_decode_step)",
+        "roofline": {"bound": "hbm",
+                     "kernel": ("indexer_fp8_persistent<1, 4, true>" if emit else "indexer_%s" % wl.idx_dtype)
+                               + " (in dsa_decode_step)",
                      "achieved": round(emit_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(emit_gbs / PEAK_HBM_GBS, 4), "traffic": emit_traffic,
                      "bytes_per_launch": emit_bytes, "us_per_launch": round(emit_us, 2)},

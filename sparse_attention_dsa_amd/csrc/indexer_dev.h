@@ -83,16 +83,26 @@ __device__ __forceinline__ void page_scores(const i32x8 (&qf)[NQ][HT], const flo
             float part[4];
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
-                // the tile's MFMAs first (distinct results, issued back to
-                // back), then their weighted ReLU sum in the same order
-                f32x4 c[HT];
-#pragma unroll
-                for (int ht = 0; ht < HT; ++ht) c[ht] = mfma_fp8_16x16x128(qf[j][ht], kf[nt], zero);
                 float acc = 0.f;
+                if constexpr (NQ == 1) {
+                    // the tile's MFMAs first (distinct results, issued back to
+                    // back), then their weighted ReLU sum in the same order;
+                    // two query rows keep one result at a time (registers)
+                    f32x4 c[HT];
 #pragma unroll
-                for (int ht = 0; ht < HT; ++ht)
+                    for (int ht = 0; ht < HT; ++ht) c[ht] = mfma_fp8_16x16x128(qf[j][ht], kf[nt], zero);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) acc = fmaf(wv[j][ht][i], relu(c[ht][i]), acc);
+                    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc = fmaf(wv[j][ht][i], relu(c[ht][i]), acc);
+                } else {
+#pragma unroll
+                    for (int ht = 0; ht < HT; ++ht) {
+                        const f32x4 c = mfma_fp8_16x16x128(qf[j][ht], kf[nt], zero);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc = fmaf(wv[j][ht][i], relu(c[i]), acc);
+                    }
+                }
                 part[nt] = acc;
             }
             out[j] = head_sum_transpose(part, lane) * ksc;
