@@ -15,12 +15,22 @@
  *
  * Conventions shared by every entry point
  *   - All array arguments are DEVICE pointers unless marked "host".  The
- *     caller owns every buffer; the library never allocates, frees or
- *     synchronises, keeps no state between calls, and is reentrant.
+ *     caller owns every buffer; the library never allocates or frees, does
+ *     not synchronise (outside the debug check below), keeps no state
+ *     between calls, and is reentrant.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
  *     default stream).  Only host-visible arguments are validated; a bad
  *     device value (page id, index) is undefined behaviour and surfaces at
  *     the caller's next synchronisation.
+ *   - Debug mode: with DSA_DEBUG set in the environment (to anything but ""
+ *     or "0"; read on every call), each entry point first runs the check of
+ *     dsa_check_batch on the device values it will read (page ids against
+ *     the caches' num_blocks when given, selections against their rows'
+ *     visible counts) and returns DSA_ERR_BAD_DEVICE_ARG, with nothing else
+ *     launched, when one is out of range; after launching it waits for
+ *     `stream` and returns DSA_ERR_LAUNCH if the work failed.  So in debug
+ *     mode every call synchronises, and calls under stream capture return
+ *     DSA_ERR_UNSUPPORTED.
  *   - Return value: DSA_OK (0) or a negative dsa_status; nothing is printed
  *     and no exception crosses the ABI.  On error nothing was launched.
  *   - Paged caches: logical token s of request r lives in physical block
@@ -53,7 +63,8 @@ enum dsa_status {
     DSA_ERR_WORKSPACE = -3,     /* workspace smaller than dsa_workspace_size() */
     DSA_ERR_DEVICE = -4,        /* current device is not gfx950 */
     DSA_ERR_LAUNCH = -5,        /* a HIP launch returned an error */
-    DSA_ERR_TOO_LARGE = -6      /* batch beyond dsa_decode_step_noalloc's built-in scratch */
+    DSA_ERR_TOO_LARGE = -6,     /* batch beyond dsa_decode_step_noalloc's built-in scratch */
+    DSA_ERR_BAD_DEVICE_ARG = -7 /* a device value out of range (dsa_check_batch, DSA_DEBUG) */
 };
 
 /* Storage formats.  DSA_E4M3 is the OCP e4m3fn fp8 format (max 448). */
@@ -97,6 +108,7 @@ typedef struct {
     const float *scales;
     int32_t dtype;
     int32_t dim;
+    int32_t num_blocks;   /* blocks in the pool, or 0 if not stated (read only by the debug check) */
 } dsa_index_cache;
 
 /* MLA latent cache: kv [num_blocks][block_size][d_latent + d_rope] in
@@ -109,6 +121,7 @@ typedef struct {
     int32_t dtype;
     int32_t d_latent;
     int32_t d_rope;
+    int32_t num_blocks;   /* blocks in the pool, or 0 if not stated (read only by the debug check) */
 } dsa_latent_cache;
 
 /*
@@ -266,6 +279,29 @@ size_t dsa_workspace_size(int32_t op, const dsa_batch *batch, int32_t k, int32_t
 
 /* Static text for a status code. */
 const char *dsa_status_string(int32_t status);
+
+/*
+ * Synchronous check of the device-side batch values the entry points trust
+ * (the check that DSA_DEBUG adds to every call).  Per request r:
+ *   DSA_CHECK_QUERY_START  query_start_loc starts at 0, ends at total_q and
+ *                          does not decrease, each q_len_r <= max_q_len;
+ *   DSA_CHECK_CONTEXT      q_len_r <= L_r <= max_context_len;
+ *   DSA_CHECK_PAGE         the ceil(L_r / block_size) page ids the request
+ *                          uses are >= 0 and, when num_blocks > 0, below it;
+ *   DSA_CHECK_INDEX        (when indices [total_q][k] is given) every entry
+ *                          of row t is < n_t (negative entries are padding).
+ * Page ids and indices of a request are checked only when its query range
+ * and length hold.  failed (host, may be NULL) receives the OR of the bits
+ * that failed.  Waits for `stream`.  Returns DSA_OK, DSA_ERR_BAD_DEVICE_ARG
+ * (some check failed), DSA_ERR_INVALID_ARG for host-visible errors,
+ * DSA_ERR_UNSUPPORTED while `stream` is being captured, DSA_ERR_LAUNCH.
+ */
+#define DSA_CHECK_QUERY_START 1u
+#define DSA_CHECK_CONTEXT 2u
+#define DSA_CHECK_PAGE 4u
+#define DSA_CHECK_INDEX 8u
+int dsa_check_batch(const dsa_batch *batch, int32_t num_blocks, const int32_t *indices, int32_t k,
+                    uint32_t *failed, dsa_stream_t stream);
 
 /* DSA_OK if the current HIP device is gfx950, else DSA_ERR_DEVICE. */
 int dsa_check_device(void);

@@ -23,7 +23,9 @@ EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_spars
            "dsa_decode_step", "dsa_workspace_size", "dsa_status_string", "dsa_check_device",
            "dsa_read_probe_sink_size", "dsa_read_probe", "dsa_hot_cache_reset", "dsa_hot_cache_workspace_size",
            "dsa_hot_cache_fetch", "dsa_decode_step_timed", "dsa_decode_step_noalloc",
-           "dsa_decode_step_fused")
+           "dsa_decode_step_fused", "dsa_check_batch")
+CHECK_QUERY_START, CHECK_CONTEXT, CHECK_PAGE, CHECK_INDEX = 1, 2, 4, 8   # dsa_check_batch's bits
+ERR_BAD_DEVICE_ARG = -7
 STEP_EVENTS = 5   # events of dsa_decode_step_timed: start, after sampling, indexer, selection, attention
 
 
@@ -40,12 +42,13 @@ class DsaBatch(C.Structure):
 
 
 class DsaIndexCache(C.Structure):
-    _fields_ = [("keys", C.c_void_p), ("scales", C.c_void_p), ("dtype", C.c_int32), ("dim", C.c_int32)]
+    _fields_ = [("keys", C.c_void_p), ("scales", C.c_void_p), ("dtype", C.c_int32), ("dim", C.c_int32),
+                ("num_blocks", C.c_int32)]
 
 
 class DsaLatentCache(C.Structure):
     _fields_ = [("kv", C.c_void_p), ("scales", C.c_void_p), ("dtype", C.c_int32),
-                ("d_latent", C.c_int32), ("d_rope", C.c_int32)]
+                ("d_latent", C.c_int32), ("d_rope", C.c_int32), ("num_blocks", C.c_int32)]
 
 
 _lib = None
@@ -85,7 +88,8 @@ def lib():
                                               i32, i32, f32, vp, vp, vp, vp]
         L.dsa_decode_step_fused.argtypes = [P(DsaBatch), P(DsaIndexCache), vp, vp, i32, P(DsaLatentCache), vp, i32,
                                             i32, f32, vp, vp, vp, vp, sz, vp, P(vp), i32]
-        for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
+        L.dsa_check_batch.argtypes = [P(DsaBatch), i32, vp, i32, P(C.c_uint32), vp]
+        for name in ("dsa_check_batch", "dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
                      "dsa_decode_step", "dsa_check_device", "dsa_read_probe", "dsa_hot_cache_reset",
                      "dsa_hot_cache_fetch", "dsa_decode_step_timed", "dsa_decode_step_noalloc",
                      "dsa_decode_step_fused"):
@@ -168,13 +172,19 @@ class MxFp4Keys:
 def index_cache(keys, scales: Optional[torch.Tensor]) -> DsaIndexCache:
     sp = scales.data_ptr() if scales is not None else None
     if isinstance(keys, MxFp4Keys):
-        return DsaIndexCache(keys.data_ptr(), sp, DSA_MXFP4, keys.dim)
-    return DsaIndexCache(keys.data_ptr(), sp, dtype_code(keys), keys.shape[-1])
+        return DsaIndexCache(keys.data_ptr(), sp, DSA_MXFP4, keys.dim, keys.data.shape[0])
+    return DsaIndexCache(keys.data_ptr(), sp, dtype_code(keys), keys.shape[-1], _pool_blocks(keys))
+
+
+def _pool_blocks(t: torch.Tensor) -> int:
+    # [num_blocks][block_size][width] pools state their block count (read by
+    # the library's debug check); other views leave it unstated (0)
+    return int(t.shape[0]) if t.dim() == 3 else 0
 
 
 def latent_cache(kv: torch.Tensor, scales: Optional[torch.Tensor], d_latent: int) -> DsaLatentCache:
     return DsaLatentCache(kv.data_ptr(), scales.data_ptr() if scales is not None else None,
-                          dtype_code(kv), d_latent, kv.shape[-1] - d_latent)
+                          dtype_code(kv), d_latent, kv.shape[-1] - d_latent, _pool_blocks(kv))
 
 
 def workspace_size(op: int, batch: Batch, k: int, n_heads: int = 0) -> int:
@@ -370,3 +380,17 @@ def read_probe(buf: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=No
 
 def check_device() -> int:
     return int(lib().dsa_check_device())
+
+
+def check_batch(batch: "Batch", num_blocks: int = 0, indices: Optional[torch.Tensor] = None, k: int = 0,
+                stream=None) -> int:
+    """dsa_check_batch: waits for `stream` and returns the OR of the
+    CHECK_* bits that failed (0 when the batch's device values hold)."""
+    b = batch.struct()
+    if indices is not None:
+        k = k or indices.shape[-1]
+    failed = C.c_uint32(0)
+    st = lib().dsa_check_batch(C.byref(b), num_blocks, _ptr(indices), k, C.byref(failed), _stream(stream))
+    if st not in (DSA_OK, ERR_BAD_DEVICE_ARG):
+        raise DsaError("dsa_check_batch", st)
+    return int(failed.value)

@@ -146,6 +146,13 @@ FusedLayout fused_layout(const dsa_batch* b, int k, int n_heads) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH; }
 
+// Pool size for the debug check's page-id bound: the smaller stated one of
+// two caches that share the page table, 0 when neither states it.
+int pool_blocks(int a, int b) {
+    if (a > 0 && b > 0) return std::min(a, b);
+    return a > 0 ? a : (b > 0 ? b : 0);
+}
+
 // Workspace of the multi-kernel decode step for any latent dtype.
 size_t step_workspace(const dsa_batch* b, int k, int n_heads) {
     size_t end = 0;
@@ -311,11 +318,21 @@ const char* dsa_status_string(int32_t status) {
     case DSA_ERR_DEVICE: return "current device is not gfx950";
     case DSA_ERR_LAUNCH: return "kernel launch failed";
     case DSA_ERR_TOO_LARGE: return "batch needs more than the no-allocation entry point's scratch";
+    case DSA_ERR_BAD_DEVICE_ARG: return "a device-side size, page id or index is out of range";
     default: return "unknown status";
     }
 }
 
 int dsa_check_device(void) { return check_device_cached(); }
+
+int dsa_check_batch(const dsa_batch* b, int32_t num_blocks, const int32_t* indices, int32_t k, uint32_t* failed,
+                    dsa_stream_t stream) {
+    if (failed) *failed = 0;
+    if (!batch_ok(b) || (indices && k < 1)) return DSA_ERR_INVALID_ARG;
+    int st = check_device_cached();
+    if (st != DSA_OK) return st;
+    return run_batch_check(geometry(b), num_blocks, true, indices, k, failed, (hipStream_t)stream);
+}
 
 size_t dsa_workspace_size(int32_t op, const dsa_batch* b, int32_t k, int32_t n_heads) {
     if (!batch_ok(b)) return 0;
@@ -342,10 +359,13 @@ int dsa_indexer_scores(const dsa_batch* b, const dsa_index_cache* c, const void*
     if (st != DSA_OK) return st;
     if (!scores || ld < b->max_context_len) return DSA_ERR_INVALID_ARG;
     if ((st = check_device_cached()) != DSA_OK) return st;
+    const bool dbg = debug_mode();
+    if (dbg && (st = run_batch_check(geometry(b), c->num_blocks, true, nullptr, 0, nullptr, (hipStream_t)stream)))
+        return st;
     const IndexerArgs a = indexer_args(b, c, q_idx, w, n_heads_idx, scores, ld);
     hipError_t e = launch_indexer(a, (hipStream_t)stream);
     if (e == hipSuccess) e = launch_score_tail(a, (hipStream_t)stream);
-    return launch_status(e);
+    return debug_finish(dbg, launch_status(e), (hipStream_t)stream);
 }
 
 int dsa_topk(const dsa_batch* b, const float* scores, int64_t ld, int32_t k, int32_t* indices,
@@ -356,8 +376,10 @@ int dsa_topk(const dsa_batch* b, const float* scores, int64_t ld, int32_t k, int
     if (l.end > 0 && (!ws || ws_bytes < l.end)) return DSA_ERR_WORKSPACE;
     int st = check_device_cached();
     if (st != DSA_OK) return st;
+    const bool dbg = debug_mode();
+    if (dbg && (st = run_batch_check(geometry(b), 0, false, nullptr, 0, nullptr, (hipStream_t)stream))) return st;
     const TopkArgs a = topk_args(b, scores, ld, k, indices, (char*)ws, l);
-    return launch_status(launch_topk(a, (hipStream_t)stream));
+    return debug_finish(dbg, launch_status(launch_topk(a, (hipStream_t)stream)), (hipStream_t)stream);
 }
 
 static int mla_entry(const dsa_batch* b, const dsa_latent_cache* c, const void* q, int32_t n_heads,
@@ -368,8 +390,12 @@ static int mla_entry(const dsa_batch* b, const dsa_latent_cache* c, const void* 
     if (!indices) return DSA_ERR_INVALID_ARG;
     if ((st = mla_workspace_ok(b, c, n_heads, k, ws, ws ? ws_bytes : 0, 0, prefill)) != DSA_OK) return st;
     if ((st = check_device_cached()) != DSA_OK) return st;
-    return run_mla(b, c, q, n_heads, indices, k, scale, out, lse, (char*)ws, ws ? ws_bytes : 0, 0, prefill,
-                   (hipStream_t)stream);
+    const bool dbg = debug_mode();
+    if (dbg && (st = run_batch_check(geometry(b), c->num_blocks, true, indices, k, nullptr, (hipStream_t)stream)))
+        return st;
+    st = run_mla(b, c, q, n_heads, indices, k, scale, out, lse, (char*)ws, ws ? ws_bytes : 0, 0, prefill,
+                 (hipStream_t)stream);
+    return debug_finish(dbg, st, (hipStream_t)stream);
 }
 
 int dsa_sparse_mla_decode(const dsa_batch* b, const dsa_latent_cache* c, const void* q, int32_t n_heads,
@@ -404,6 +430,10 @@ int decode_step(const dsa_batch* b, const dsa_index_cache* ic, const void* q_idx
     const StepLayout l = step_layout(b, k, n_heads, mla_path(lc->dtype, lc->d_latent, lc->d_rope, n_heads));
     if (!ws || ws_bytes < l.end) return DSA_ERR_WORKSPACE;
     if ((st = check_device_cached()) != DSA_OK) return st;
+    const bool dbg = debug_mode();
+    if (dbg && (st = run_batch_check(geometry(b), pool_blocks(ic->num_blocks, lc->num_blocks), true, nullptr, 0,
+                                     nullptr, s)))
+        return st;
     float* scores = (float*)(base + l.scores);
     int32_t* indices = indices_out ? indices_out : (int32_t*)(base + l.indices);
 
@@ -425,7 +455,7 @@ int decode_step(const dsa_batch* b, const dsa_index_cache* ic, const void* q_idx
     if (e != hipSuccess) return DSA_ERR_LAUNCH;
     st = run_mla(b, lc, q_mla, n_heads, indices, k, scale, out, lse, base, ws_bytes, l.mla_base, false, s);
     if (st == DSA_OK && ev && hipEventRecord(ev[4], s) != hipSuccess) return DSA_ERR_LAUNCH;
-    return st;
+    return debug_finish(dbg, st, s);
 }
 
 // The step in one persistent launch (plus its init and merge kernels); with
@@ -449,6 +479,10 @@ int decode_step_fused(const dsa_batch* b, const dsa_index_cache* ic, const void*
     if (!fused_ok(ia, ma)) return DSA_ERR_UNSUPPORTED;
     if (!ws || ws_bytes < fl.end) return DSA_ERR_WORKSPACE;
     if ((st = check_device_cached()) != DSA_OK) return st;
+    const bool dbg = debug_mode();
+    if (dbg && (st = run_batch_check(geometry(b), pool_blocks(ic->num_blocks, lc->num_blocks), true, nullptr, 0,
+                                     nullptr, s)))
+        return st;
     FusedArgs f;
     f.indices = indices_out ? indices_out : (int32_t*)(base + fl.indices);
     ia.cand = (uint64_t*)(base + fl.cand);
@@ -472,7 +506,7 @@ int decode_step_fused(const dsa_batch* b, const dsa_index_cache* ic, const void*
     hipError_t e = ev ? hipEventRecord(ev[0], s) : hipSuccess;
     if (e == hipSuccess) e = launch_fused(f, s, ev ? ev + 1 : nullptr);
     if (e == hipSuccess && ev) e = hipEventRecord(ev[4], s);
-    return launch_status(e);
+    return debug_finish(dbg, launch_status(e), s);
 }
 
 }  // namespace

@@ -305,6 +305,19 @@ hipError_t launch_emit_step(const IndexerArgs& ia, const TopkArgs& ta, hipStream
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_mla(const MlaArgs& a, bool prefill, hipStream_t s);
 
+// DSA_DEBUG set in the environment (to anything but "" or "0").
+bool debug_mode();
+// Checks the batch's device-side values (query starts, context lengths, page
+// ids below num_blocks when pages and num_blocks > 0, selection entries below
+// their row's visible count when indices != nullptr) and waits for the
+// result: DSA_OK, or DSA_ERR_BAD_DEVICE_ARG with the DSA_CHECK_* bits in
+// *failed (may be nullptr); DSA_ERR_UNSUPPORTED while `s` is being captured.
+int run_batch_check(const Geometry& g, int num_blocks, bool pages, const int32_t* indices, int k,
+                    uint32_t* failed, hipStream_t s);
+// In debug mode, waits for a successful call's launches and reports a failed
+// one as DSA_ERR_LAUNCH; otherwise returns st.
+int debug_finish(bool dbg, int st, hipStream_t s);
+
 // Which MLA path serves these shapes, and how many splits it uses.
 bool mla_fast_path(int kv_dtype, int d_latent, int d_rope, int n_heads, int block_size);
 constexpr int MLA_HEADS_PER_WG = 64;

@@ -487,6 +487,11 @@ int dsa_hot_cache_fetch(const dsa_batch* b, const dsa_latent_cache* host, const 
     a.counts = counts;
 
     hipStream_t s = (hipStream_t)stream;
+    const bool dbg = debug_mode();
+    if (dbg) {
+        if (const int st = run_batch_check(a.g, host->num_blocks, true, indices, k, nullptr, s); st != DSA_OK)
+            return st;
+    }
     const int64_t nclear = std::max<int64_t>(2 * HC_AGE_BINS, l.nwords);
     hipLaunchKernelGGL(hc_clear, dim3((unsigned)((nclear + HC_THREADS - 1) / HC_THREADS)), dim3(HC_THREADS), 0, s, a,
                        l.nwords);
@@ -507,7 +512,7 @@ int dsa_hot_cache_fetch(const dsa_batch* b, const dsa_latent_cache* host, const 
     const int64_t tk = (int64_t)b->total_q * k;
     hipLaunchKernelGGL(hc_assign, dim3((unsigned)((tk + HC_WAVES - 1) / HC_WAVES)), dim3(HC_THREADS), 0, s, a);
     hipLaunchKernelGGL(hc_finish, dim3(1), dim3(1), 0, s, a);
-    return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
+    return debug_finish(dbg, hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH, s);
 }
 
 }  // extern "C"

@@ -144,3 +144,40 @@ def test_noalloc_rejects_batches_beyond_its_scratch(L):
     assert st == -6
     assert L.dsa_status_string(-6).startswith(b"batch needs more than")
     assert L.dsa_workspace_size(B.OP_DECODE_STEP, C.byref(huge), 2048, 128) > (128 << 20)
+
+
+def test_check_batch_host_arguments(L):
+    b = _batch()
+    failed = C.c_uint32(99)
+    assert L.dsa_check_batch(None, 0, None, 0, C.byref(failed), None) == -1
+    assert failed.value == 0
+    assert L.dsa_check_batch(C.byref(b), 0, 0x1, 0, None, None) == -1      # indices without k
+    assert L.dsa_check_batch(C.byref(_batch(maxctx=5000)), 0, None, 0, None, None) == -1   # pages cannot hold it
+    assert L.dsa_status_string(-7) == b"a device-side size, page id or index is out of range"
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """The ctypes structures have the sizes and field offsets that a C
+    compiler gives the header's structs."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no host C compiler")
+    structs = {"dsa_batch": B.DsaBatch, "dsa_index_cache": B.DsaIndexCache,
+               "dsa_latent_cache": B.DsaLatentCache, "dsa_hot_cache": B.DsaHotCache}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "dsa.h"', "int main(void) {"]
+    for name, cls in structs.items():
+        lines.append('printf("%s %%zu\\n", sizeof(%s));' % (name, name))
+        for f, _ in cls._fields_:
+            lines.append('printf("%s.%s %%zu\\n", offsetof(%s, %s));' % (name, f, name, f))
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = str(tmp_path / "layout")
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", exe], check=True)
+    got = dict(l.split() for l in subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
+               if l)
+    for name, cls in structs.items():
+        assert int(got[name]) == C.sizeof(cls), name
+        for f, _ in cls._fields_:
+            assert int(got["%s.%s" % (name, f)]) == getattr(cls, f).offset, (name, f)
