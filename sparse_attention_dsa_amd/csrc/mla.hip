@@ -470,7 +470,7 @@ void mla_h128(MlaArgs a, int slice) {
     __shared__ MlaSliceLds L;
     const int r = row_request(G, t);
     MlaAcc acc;
-    mla_slice<FP8>(a, t, hg * M3_HEADS, a.indices + (size_t)t * a.k + j_begin,
+    mla_slice<FP8, !FP8>(a, t, hg * M3_HEADS, a.indices + (size_t)t * a.k + j_begin,
                    G.page_table + (size_t)r * G.max_blocks, nslots, L, acc);
     if (S == 1) mla_store_final(a, t, hg * M3_HEADS, acc, L);
     else mla_store_partial(a, t, hg * M3_HEADS, sp, acc, L);

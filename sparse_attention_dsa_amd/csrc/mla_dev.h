@@ -152,9 +152,11 @@ struct MlaAcc {
 
 // Slice [j_begin, j_begin + nslots) of query row t's selection `sel` (logical
 // positions, -1 skipped) through page-table row `pt`, heads [hbase, hbase +
-// 128).  `rows_phys`: the selection already holds physical rows.  Called by
-// all M_THREADS threads; uses L exclusively until it returns.
-template <bool FP8>
+// 128).  Called by all M_THREADS threads; uses L exclusively until it
+// returns.  PIPE (bf16 rows): overlap each tile's softmax with the previous
+// tile's PV; it needs more registers than a kernel with other live state
+// (the fused step) or the e4m3 widening can spare.
+template <bool FP8, bool PIPE = false>
 __device__ __forceinline__ void mla_slice(const MlaArgs& a, int t, int hbase, const int32_t* sel, const int32_t* pt,
                                           int nslots, MlaSliceLds& L, MlaAcc& acc) {
     const Geometry& G = a.g;
@@ -263,135 +265,35 @@ __device__ __forceinline__ void mla_slice(const MlaArgs& a, int t, int hbase, co
     // 16kk + 8rd + 4hh + jj, columns 32cb + 16(g4 & 1) + 4q .. +3 (unit
     // 4cb + v, v = 2(g4 & 1) + (q >> 1)), and destination lane d receives
     // column d of the half, tokens jj = 0..3.
-    int pv_base[2][2][2];   // [kk][rd][cb & 1], + 1024 (cb / 2)
+    // (token 16kk + 8rd + tl, tl = 4hh + jj < 8: block row 2kk + rd, row tl
+    // inside it, so kk and rd enter as the immediate 9216 (2kk + rd))
+    int pv_base[2];   // [cb & 1], + 9216 (2kk + rd) + 1024 (cb / 2)
     {
         const int s16 = lane & 15, jj = s16 >> 2, q = s16 & 3;
         const int v = 2 * ((lane >> 4) & 1) + (q >> 1);
+        const int tl = 4 * hh + jj;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int rd = 0; rd < 2; ++rd) {
-                const int tok = 16 * kk + 8 * rd + 4 * hh + jj;
-#pragma unroll
-                for (int c1 = 0; c1 < 2; ++c1)
-                    pv_base[kk][rd][c1] = 9216 * (tok >> 3) + 128 * (tok & 7) +
-                                          16 * ((4 * c1 + v) ^ (tok & 7)) + 8 * (q & 1);
-            }
+        for (int c1 = 0; c1 < 2; ++c1) pv_base[c1] = 128 * tl + 16 * ((4 * c1 + v) ^ tl) + 8 * (q & 1);
     }
 
     f32x16* oacc = acc.o;
     float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
+    bool overflow = false;
     u32x4 qf[M_DQK / 16];   // B operand of S^T = K Q^T, one 16-byte fragment per 16-wide k step
 
-    for (int pass = 0;; ++pass) {
+    // Masks the slots of tile i that hold no token (their logits take no part).
+    auto mask_tile = [&](f32x16& st, uint32_t vmask) {
+        const uint32_t vm = vmask >> (4 * hh);
 #pragma unroll
-    for (int cb = 0; cb < M_DL / 32; ++cb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[cb][i] = 0.f;
-    l_run = 0.f;
-    bool overflow = false;
-    if (tid == 0) L.redo = 0u;
-
-#pragma unroll
-    for (int b = 0; b < NRING - 1; ++b)
-        if (b < ntiles) issue(b, b);
-    if (pass == 0) {
-        const uint16_t* qp = (const uint16_t*)a.q + ((size_t)t * a.n_heads + head) * M_DQK + 8 * hh;
-#pragma unroll
-        for (int ks = 0; ks < M_DQK / 16; ++ks) qf[ks] = *(const u32x4*)(qp + 16 * ks) ^ qsign;
-    }
-
-    for (int i = 0; i < ntiles; ++i) {
-        // this wave's transfers of tile i are done once at most the ones of
-        // the (up to NRING - 2) later tiles already issued are outstanding
-        const int later = min(NRING - 2, ntiles - 1 - i);
-        if constexpr (!FP8) {
-            if (later >= 2) wait_vmcnt<2 * M3_DMA_PER_WAVE>();
-            else if (later == 1) wait_vmcnt<M3_DMA_PER_WAVE>();
-            else wait_vmcnt<0>();
-        } else {
-            if (later >= 1) { if (f8_ops == FP8_OPS) wait_vmcnt<FP8_OPS>(); else wait_vmcnt<FP8_OPS - 1>(); }
-            else wait_vmcnt<0>();
-        }
-        lds_barrier();   // everyone's part of tile i landed; tile i-1's buffer is free
-        uint8_t* Kb;
-        if constexpr (FP8) {
-            widen(i % M3_FP8_NBUF, i & 1);
-            lds_barrier();   // tile i widened
-            Kb = &L.ks[i & 1][0];
-        } else {
-            Kb = &L.ks[i % M3_NBUF][0];
-        }
-
-        const uint32_t vmask = L.tvalid[i];   // tokens present in the tile (bit per slot)
-        const bool full = vmask == 0xFFFFFFFFu;
-
-        // S^T: K fragments read M3_KPF steps ahead of their MFMA; the
-        // transfers of tile i + NRING - 1 (into the buffer tile i - 1 has
-        // left) are spread over the MFMAs, one after every fourth, so that
-        // issuing them never holds up the matrix core for long
-        f32x16 st;
-        {
-            constexpr int NK = M_DQK / 16;
-            const int nt = i + NRING - 1;
-            const bool iss = nt < ntiles;
-            const int srow = tile_row(min(nt, ntiles - 1));
-            const uint8_t* dsrc = FP8 ? kvb + (size_t)srow * M_DQK + 64 * f8_i0 + dma_col
-                                      : kvb + (size_t)srow * M_ROW_BYTES + dma_col;
-            uint8_t* ddst = FP8 ? f8_stage + M3_FP8_TILE * (nt % M3_FP8_NBUF) + 1024 * (9 * f8_g + f8_i0)
-                                : &L.ks[nt % M3_NBUF][0] + 1024 * M3_DMA_PER_WAVE * wave;
-            auto qk = [&](bool dma) {
-                u32x4 kb[M3_KPF];
-#pragma unroll
-                for (int j = 0; j < M3_KPF; ++j) kb[j] = *(const u32x4*)(Kb + qk_base[j & 3] + 1024 * (j >> 2));
-                __builtin_amdgcn_sched_group_barrier(0x100, M3_KPF, 0);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int ks = 0; ks < NK; ++ks) {
-                    if (ks == 0) st = mfma_bf16_32x32x16(as_bf16x8(kb[0]), as_bf16x8(qf[0]), f32x16{});
-                    else st = mfma_bf16_32x32x16(as_bf16x8(kb[ks % M3_KPF]), as_bf16x8(qf[ks]), st);
-                    if (ks + M3_KPF < NK) {
-                        const int kn = ks + M3_KPF;
-                        kb[ks % M3_KPF] = *(const u32x4*)(Kb + qk_base[kn & 3] + 1024 * (kn >> 2));
-                    }
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // then one LDS read
-                    const int di = ks >> 2;
-                    if constexpr (FP8) {
-                        if (dma && (ks & 3) == 1 && di == FP8_OPS - 1 && f8_sc) {
-                            // the tile's token scales (4-byte transfer), as in issue()
-                            dma4(scale_src(min(nt, ntiles - 1)), lds_addr(&L.tscale[nt % M3_FP8_NBUF][0]));
-                        }
-                    }
-                    if (dma && (ks & 3) == 1 && di < (FP8 ? FP8_OPS : M3_DMA_PER_WAVE) && (!FP8 || di < f8_n)) {
-                        // dma16 is not counted by the compiler: it puts no wait for
-                        // it before the fragment reads of tile i, which use another
-                        // buffer (the loop's own vector-memory waits count these
-                        // transfers)
-                        dma16(dsrc + (FP8 ? 64 : 128) * di, lds_addr(ddst + 1024 * di));
-                    }
-                }
-            };
-            if (iss) qk(true);
-            else qk(false);
-        }
-        // element e of this lane: token 8(e/4) + 4hh + e%4, head c32.
-        // e4m3: the tokens' scales multiply their logits (and, below, their
-        // probabilities, as V rows are unscaled codes)
+        for (int e = 0; e < 16; ++e) st[e] = (vm >> (8 * (e >> 2) + (e & 3))) & 1u ? st[e] : -INFINITY;
+    };
+    // Softmax of tile i's (masked, and for e4m3 scaled) logits against the
+    // fixed reference: the probabilities as the PV operand (bf16) and the
+    // running row sum.  Element e of this lane: token 8(e/4) + 4hh + e%4,
+    // head c32; e4m3: the tokens' scales also multiply their probabilities
+    // (V rows are unscaled codes).
+    auto softmax = [&](f32x16& st, int i, bf16x8 (&pb)[2]) {
         const float* tsl = &L.tscale[i % M3_FP8_NBUF][4 * hh];
-        if constexpr (FP8) {
-#pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) {
-                const f32x4 sc4 = *(const f32x4*)(tsl + 8 * e4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) st[4 * e4 + e] *= sc4[e];
-            }
-        }
-        if (!full) {   // slots without a token take no part
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                st[e] = (vmask >> (8 * (e >> 2) + 4 * hh + (e & 3))) & 1u ? st[e] : -INFINITY;
-        }
         // the tile's largest logit (zscale > 0) and the fixed reference
         float tmax = max3f(max3f(max3f(st[0], st[1], st[2]), max3f(st[3], st[4], st[5]),
                                  max3f(st[6], st[7], st[8])),
@@ -423,41 +325,227 @@ __device__ __forceinline__ void mla_slice(const MlaArgs& a, int t, int hbase, co
                 for (int e = 0; e < 4; ++e) p[4 * e4 + e] *= sc4[e];
             }
         }
-        bf16x8 pb[2];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int e = 0; e < 8; ++e) pb[kk][e] = (__bf16)p[8 * kk + e];
-
-        // O^T += V^T P^T: V^T fragments (two transposing reads each) read
-        // M3_VPF MFMAs ahead; the 16 accumulators rotate between dependent updates
-        {
-            constexpr int NV = 2 * (M_DL / 32);
-            auto vread = [&](int n, s16x4& v0, s16x4& v1) {
-                const int kk = n / (M_DL / 32), cb = n % (M_DL / 32);
-                v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4_ptr)(Kb + pv_base[kk][0][cb & 1] + 1024 * (cb >> 1)));
-                v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4_ptr)(Kb + pv_base[kk][1][cb & 1] + 1024 * (cb >> 1)));
-            };
-            s16x4 vb0[M3_VPF], vb1[M3_VPF];
+    };
+    // O^T += V^T P^T over tile buffer Kb: V^T fragments (two transposing
+    // reads each) read M3_VPF MFMAs ahead; the 16 accumulators rotate
+    // between dependent updates
+    auto pv = [&](const uint8_t* Kb, const bf16x8 (&pb)[2]) {
+        constexpr int NV = 2 * (M_DL / 32);
+        auto vread = [&](int n, s16x4& v0, s16x4& v1) {
+            const int kk = n / (M_DL / 32), cb = n % (M_DL / 32);
+            v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4_ptr)(Kb + pv_base[cb & 1] + 9216 * (2 * kk) + 1024 * (cb >> 1)));
+            v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4_ptr)(Kb + pv_base[cb & 1] + 9216 * (2 * kk + 1) + 1024 * (cb >> 1)));
+        };
+        s16x4 vb0[M3_VPF], vb1[M3_VPF];
 #pragma unroll
-            for (int j = 0; j < M3_VPF; ++j) vread(j, vb0[j], vb1[j]);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * M3_VPF, 0);
+        for (int j = 0; j < M3_VPF; ++j) vread(j, vb0[j], vb1[j]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * M3_VPF, 0);
 #pragma unroll
-            for (int n = 0; n < NV; ++n) {
-                const int kk = n / (M_DL / 32), cb = n % (M_DL / 32);
-                const s16x4 v0 = vb0[n % M3_VPF], v1 = vb1[n % M3_VPF];
-                u32x4 va;
-                va[0] = (uint16_t)v0[0] | ((uint32_t)(uint16_t)v0[1] << 16);
-                va[1] = (uint16_t)v0[2] | ((uint32_t)(uint16_t)v0[3] << 16);
-                va[2] = (uint16_t)v1[0] | ((uint32_t)(uint16_t)v1[1] << 16);
-                va[3] = (uint16_t)v1[2] | ((uint32_t)(uint16_t)v1[3] << 16);
-                oacc[cb] = mfma_bf16_32x32x16(as_bf16x8(va), pb[kk], oacc[cb]);
-                if (n + M3_VPF < NV) vread(n + M3_VPF, vb0[n % M3_VPF], vb1[n % M3_VPF]);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // then its two reads
+        for (int n = 0; n < NV; ++n) {
+            const int kk = n / (M_DL / 32), cb = n % (M_DL / 32);
+            const s16x4 v0 = vb0[n % M3_VPF], v1 = vb1[n % M3_VPF];
+            u32x4 va;
+            va[0] = (uint16_t)v0[0] | ((uint32_t)(uint16_t)v0[1] << 16);
+            va[1] = (uint16_t)v0[2] | ((uint32_t)(uint16_t)v0[3] << 16);
+            va[2] = (uint16_t)v1[0] | ((uint32_t)(uint16_t)v1[1] << 16);
+            va[3] = (uint16_t)v1[2] | ((uint32_t)(uint16_t)v1[3] << 16);
+            oacc[cb] = mfma_bf16_32x32x16(as_bf16x8(va), pb[kk], oacc[cb]);
+            if (n + M3_VPF < NV) vread(n + M3_VPF, vb0[n % M3_VPF], vb1[n % M3_VPF]);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // then its two reads
+        }
+    };
+    // PV of the previous tile (buffer Kb, probabilities pbp) with the
+    // softmax of the current tile (logits sc, tile index ic, result pbc) in
+    // the same stretch of code: its vector instructions are scheduled
+    // between the MFMAs, which do not depend on them.
+    auto pv_soft = [&](const uint8_t* Kb, const bf16x8 (&pbp)[2], f32x16& sc, int ic, bf16x8 (&pbc)[2]) {
+        constexpr int NV = 2 * (M_DL / 32);
+        auto vread = [&](int n, s16x4& v0, s16x4& v1) {
+            const int kk = n / (M_DL / 32), cb = n % (M_DL / 32);
+            v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4_ptr)(Kb + pv_base[cb & 1] + 9216 * (2 * kk) + 1024 * (cb >> 1)));
+            v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4_ptr)(Kb + pv_base[cb & 1] + 9216 * (2 * kk + 1) + 1024 * (cb >> 1)));
+        };
+        s16x4 vb0[M3_VPF], vb1[M3_VPF];
+#pragma unroll
+        for (int j = 0; j < M3_VPF; ++j) vread(j, vb0[j], vb1[j]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * M3_VPF, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        softmax(sc, ic, pbc);
+#pragma unroll
+        for (int n = 0; n < NV; ++n) {
+            const int kk = n / (M_DL / 32), cb = n % (M_DL / 32);
+            const s16x4 v0 = vb0[n % M3_VPF], v1 = vb1[n % M3_VPF];
+            u32x4 va;
+            va[0] = (uint16_t)v0[0] | ((uint32_t)(uint16_t)v0[1] << 16);
+            va[1] = (uint16_t)v0[2] | ((uint32_t)(uint16_t)v0[3] << 16);
+            va[2] = (uint16_t)v1[0] | ((uint32_t)(uint16_t)v1[1] << 16);
+            va[3] = (uint16_t)v1[2] | ((uint32_t)(uint16_t)v1[3] << 16);
+            oacc[cb] = mfma_bf16_32x32x16(as_bf16x8(va), pbp[kk], oacc[cb]);
+            if (n + M3_VPF < NV) vread(n + M3_VPF, vb0[n % M3_VPF], vb1[n % M3_VPF]);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // its two reads
+        }
+    };
+    // S^T of the tile in buffer Kb: K fragments read M3_KPF steps ahead of
+    // their MFMA.  With dma, this wave's transfers of another tile (source
+    // row dsrc, destination ddst) are spread over the MFMAs, one after every
+    // fourth, so that issuing them never holds up the matrix core for long.
+    auto qk = [&](const uint8_t* Kb, bool dma, const uint8_t* dsrc, uint8_t* ddst, f32x16& st) {
+        constexpr int NK = M_DQK / 16;
+        u32x4 kb[M3_KPF];
+#pragma unroll
+        for (int j = 0; j < M3_KPF; ++j) kb[j] = *(const u32x4*)(Kb + qk_base[j & 3] + 1024 * (j >> 2));
+        __builtin_amdgcn_sched_group_barrier(0x100, M3_KPF, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks) {
+            if (ks == 0) st = mfma_bf16_32x32x16(as_bf16x8(kb[0]), as_bf16x8(qf[0]), f32x16{});
+            else st = mfma_bf16_32x32x16(as_bf16x8(kb[ks % M3_KPF]), as_bf16x8(qf[ks]), st);
+            if (ks + M3_KPF < NK) {
+                const int kn = ks + M3_KPF;
+                kb[ks % M3_KPF] = *(const u32x4*)(Kb + qk_base[kn & 3] + 1024 * (kn >> 2));
             }
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // then one LDS read
+            const int di = ks >> 2;
+            if (dma && (ks & 3) == 1 && di < (FP8 ? FP8_OPS : M3_DMA_PER_WAVE) && (!FP8 || di < f8_n)) {
+                // dma16 is not counted by the compiler: it puts no wait for
+                // it before the fragment reads of tile i, which use another
+                // buffer (the loop's own vector-memory waits count these
+                // transfers)
+                dma16(dsrc + (FP8 ? 64 : 128) * di, lds_addr(ddst + 1024 * di));
+            }
+        }
+    };
+
+    for (int pass = 0;; ++pass) {
+#pragma unroll
+    for (int cb = 0; cb < M_DL / 32; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[cb][i] = 0.f;
+    l_run = 0.f;
+    overflow = false;
+    if (tid == 0) L.redo = 0u;
+
+    if constexpr (PIPE) {
+        // Software-pipelined over tiles: tile i's S^T, then tile i's softmax
+        // on the vector unit while the MFMAs of tile i-1's PV run.  Ring use
+        // at step i: tile i-1 (PV), tile i (S^T), tile i+1 in flight, tile
+        // i+2 issued during tile i's S^T into the buffer tile i-2 has left.
+        static_assert(!FP8, "e4m3 rows take the one-tile-at-a-time loop (the pipelined one spills)");
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+            if (b < ntiles) issue(b, b);
+        if (pass == 0) {
+            const uint16_t* qp = (const uint16_t*)a.q + ((size_t)t * a.n_heads + head) * M_DQK + 8 * hh;
+#pragma unroll
+            for (int ks = 0; ks < M_DQK / 16; ++ks) qf[ks] = *(const u32x4*)(qp + 16 * ks) ^ qsign;
+        }
+        bf16x8 pb_prev[2];
+        for (int i = 0; i < ntiles; ++i) {
+            // tile i landed (tile i+1's transfers may be outstanding), and
+            // every wave is done with tile i-2's buffer
+            if (i + 1 < ntiles) wait_vmcnt<M3_DMA_PER_WAVE>();
+            else wait_vmcnt<0>();
+            lds_barrier();
+            const uint8_t* Kb = &L.ks[i % M3_NBUF][0];
+            const uint32_t vmask = L.tvalid[i];
+            f32x16 st;
+            bf16x8 pb[2];
+            {
+                const int nt = i + 2;
+                if (nt < ntiles) {
+                    const int srow = tile_row(nt);
+                    qk(Kb, true, kvb + (size_t)srow * M_ROW_BYTES + dma_col,
+                       &L.ks[nt % M3_NBUF][0] + 1024 * M3_DMA_PER_WAVE * wave, st);
+                } else {
+                    qk(Kb, false, nullptr, nullptr, st);
+                }
+            }
+            if (vmask != 0xFFFFFFFFu) mask_tile(st, vmask);
+            if (i == 0) softmax(st, i, pb);
+            else pv_soft(&L.ks[(i - 1) % M3_NBUF][0], pb_prev, st, i, pb);
+            pb_prev[0] = pb[0];
+            pb_prev[1] = pb[1];
+        }
+        if (ntiles > 0) pv(&L.ks[(ntiles - 1) % M3_NBUF][0], pb_prev);
+    } else {
+        // One tile at a time: S^T, softmax, PV; up to NRING - 1 tiles in
+        // flight, the next one's transfers spread over the S^T MFMAs.
+#pragma unroll
+        for (int b = 0; b < NRING - 1; ++b)
+            if (b < ntiles) issue(b, b);
+        if (pass == 0) {
+            const uint16_t* qp = (const uint16_t*)a.q + ((size_t)t * a.n_heads + head) * M_DQK + 8 * hh;
+#pragma unroll
+            for (int ks = 0; ks < M_DQK / 16; ++ks) qf[ks] = *(const u32x4*)(qp + 16 * ks) ^ qsign;
+        }
+        for (int i = 0; i < ntiles; ++i) {
+            // this wave's transfers of tile i are done once at most the ones
+            // of the (up to NRING - 2) later tiles already issued are outstanding
+            const int later = min(NRING - 2, ntiles - 1 - i);
+            if constexpr (!FP8) {
+                if (later >= 2) wait_vmcnt<2 * M3_DMA_PER_WAVE>();
+                else if (later == 1) wait_vmcnt<M3_DMA_PER_WAVE>();
+                else wait_vmcnt<0>();
+            } else {
+                if (later >= 1) { if (f8_ops == FP8_OPS) wait_vmcnt<FP8_OPS>(); else wait_vmcnt<FP8_OPS - 1>(); }
+                else wait_vmcnt<0>();
+            }
+            lds_barrier();   // everyone's part of tile i landed; tile i-1's buffer is free
+            const uint8_t* Kb;
+            if constexpr (FP8) {
+                widen(i % M3_FP8_NBUF, i & 1);
+                lds_barrier();   // tile i widened
+                Kb = &L.ks[i & 1][0];
+            } else {
+                Kb = &L.ks[i % M3_NBUF][0];
+            }
+            const uint32_t vmask = L.tvalid[i];   // tokens present in the tile (bit per slot)
+
+            // S^T, with the transfers of tile i + NRING - 1 (into the buffer
+            // or staging slot tile i - 1 has left)
+            f32x16 st;
+            bf16x8 pb[2];
+            {
+                const int nt = i + NRING - 1;
+                const bool iss = nt < ntiles;
+                const int ntc = min(nt, ntiles - 1);
+                const int srow = tile_row(ntc);
+                const uint8_t* dsrc = FP8 ? kvb + (size_t)srow * M_DQK + 64 * f8_i0 + dma_col
+                                          : kvb + (size_t)srow * M_ROW_BYTES + dma_col;
+                uint8_t* ddst = FP8 ? f8_stage + M3_FP8_TILE * (nt % M3_FP8_NBUF) + 1024 * (9 * f8_g + f8_i0)
+                                    : &L.ks[nt % M3_NBUF][0] + 1024 * M3_DMA_PER_WAVE * wave;
+                if (iss) {
+                    qk(Kb, true, dsrc, ddst, st);
+                    if constexpr (FP8) {
+                        if (f8_sc) dma4(scale_src(ntc), lds_addr(&L.tscale[nt % M3_FP8_NBUF][0]));
+                    }
+                } else {
+                    qk(Kb, false, dsrc, ddst, st);
+                }
+            }
+            if constexpr (FP8) {   // the tokens' scales multiply their logits
+                const float* tsl = &L.tscale[i % M3_FP8_NBUF][4 * hh];
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const f32x4 sc4 = *(const f32x4*)(tsl + 8 * e4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) st[4 * e4 + e] *= sc4[e];
+                }
+            }
+            if (vmask != 0xFFFFFFFFu) mask_tile(st, vmask);
+            softmax(st, i, pb);
+            pv(Kb, pb);
         }
     }
     // the whole workgroup agrees on a second pass (it shares the barriers)
