@@ -516,24 +516,9 @@ def hot_cache_leg(steps, warmup, log, capacity_mult=4, keep=0.8):
     cap = capacity_mult * T * K
     hot = B.HotCache(cap, wl.batch, wl.max_context_len, d["kv"].shape[-1], d["kv"].dtype)
     B.hot_cache_reset(batch, hot)
-    rng = np.random.default_rng(7)
-    vis = visible_counts(wl)
-    prev = [rng.choice(n, size=K, replace=False) for n in vis]
-    sels = []
     # warm-up until the hot set is full, so that the timed steps evict
     warmup += int(np.ceil((capacity_mult - 1) / (1.0 - keep))) + 2
-    for _ in range(warmup + steps):
-        cur = []
-        for t, n in enumerate(vis):
-            kept = rng.choice(prev[t], size=int(keep * K), replace=False)
-            new = rng.choice(n, size=2 * (K - len(kept)), replace=True)
-            new = np.setdiff1d(np.unique(new), kept)[:K - len(kept)]
-            while len(new) < K - len(kept):
-                extra = np.setdiff1d(rng.choice(n, size=K, replace=False), np.concatenate([kept, new]))
-                new = np.concatenate([new, extra])[:K - len(kept)]
-            cur.append(np.concatenate([kept, new]))
-        prev = cur
-        sels.append(torch.from_numpy(np.sort(np.stack(cur)).astype(np.int32)).cuda())
+    sels = drifting_selections(wl, warmup + steps, keep)
     counts = torch.zeros(2, dtype=torch.int32, device="cuda")
     out = torch.empty((T, wl.mla_heads, wl.d_latent), dtype=torch.bfloat16, device="cuda")
     ws_f = None
@@ -574,6 +559,113 @@ def hot_cache_leg(steps, warmup, log, capacity_mult=4, keep=0.8):
         "GB/s from host), MLA %.1f us" % (res["hot_bytes"] / 1e9, res["full_pool_bytes"] / 1e9, f_us, misses,
                                           evictions, res["host_read_gbs"], m_us))
     del d, host_kv, hot, sels, out, ws_f, ws_m
+    torch.cuda.empty_cache()
+    return res
+
+
+def drifting_selections(wl, nsteps, keep, seed=7):
+    """Per step, K distinct visible tokens per query row of which `keep` of
+    the row's previous selection are kept and the rest drawn anew (sorted,
+    int32 on the device)."""
+    import numpy as np
+    import torch
+    K = wl.topk
+    rng = np.random.default_rng(seed)
+    vis = visible_counts(wl)
+    prev = [rng.choice(n, size=K, replace=False) for n in vis]
+    sels = []
+    for _ in range(nsteps):
+        cur = []
+        for t, n in enumerate(vis):
+            kept = rng.choice(prev[t], size=int(keep * K), replace=False)
+            new = rng.choice(n, size=2 * (K - len(kept)), replace=True)
+            new = np.setdiff1d(np.unique(new), kept)[:K - len(kept)]
+            while len(new) < K - len(kept):
+                extra = np.setdiff1d(rng.choice(n, size=K, replace=False), np.concatenate([kept, new]))
+                new = np.concatenate([new, extra])[:K - len(kept)]
+            cur.append(np.concatenate([kept, new]))
+        prev = cur
+        sels.append(torch.from_numpy(np.sort(np.stack(cur)).astype(np.int32)).cuda())
+    return sels
+
+
+def hot_cache_layers_leg(steps, warmup, log, layers=4, capacity_mult=4, keep=0.8):
+    """Layer-wise overlap of the two-tier cache on the batch-64 workload: a
+    group of `layers` layers sharing one selection (IndexShare), each layer
+    with its own hot set and its own page table into the pinned host pool (a
+    permutation of the blocks, so that every layer misses on other host
+    rows).  The group's step is timed with fetch and attention alternating
+    on one stream, and with layer l+1's fetch on a second stream during layer
+    l's attention (sparse_attention_dsa_amd.hot_layers).  Also the GPU's read
+    rate from pinned host memory (dsa_read_probe over a pinned buffer), the
+    floor of the fetches' host reads."""
+    import torch
+    import sparse_attention_dsa_amd as dsa
+    from sparse_attention_dsa_amd import binding as B
+    from sparse_attention_dsa_amd.hot_layers import HotLayerGroup
+    import workloads
+
+    wl = workloads.make_workload(DEFAULT_WORKLOAD)
+    d = workloads.to_device(wl, "cuda")
+    T, K, H = wl.total_q, wl.topk, wl.mla_heads
+    nblk = d["kv"].shape[0]
+    host_kv = d["kv"].cpu().pin_memory()
+    g = torch.Generator().manual_seed(11)
+    batches, hots = [], []
+    cap = capacity_mult * T * K
+    for l in range(layers):
+        perm = torch.randperm(nblk, generator=g).to(torch.int32).cuda()
+        pt = perm[d["page_table"].long()].contiguous()
+        batches.append(dsa.Batch(d["context_lens"], d["query_start_loc"], pt, wl.block_size, wl.max_q_len,
+                                 wl.max_context_len))
+        hots.append(B.HotCache(cap, wl.batch, wl.max_context_len, d["kv"].shape[-1], d["kv"].dtype))
+    grp = HotLayerGroup(batches, [host_kv] * layers, [None] * layers, hots, wl.d_latent, K, H)
+    grp.reset()
+    warmup += int(math.ceil((capacity_mult - 1) / (1.0 - keep))) + 2
+    sels = drifting_selections(wl, warmup + 2 * steps, keep)
+    outs = [torch.empty((T, H, wl.d_latent), dtype=torch.bfloat16, device="cuda") for _ in range(layers)]
+    qs = [d["q_mla"]] * layers
+    counts = [torch.zeros(2, dtype=torch.int32, device="cuda") for _ in range(layers)]
+    for i in range(warmup):
+        grp.step(sels[i], qs, wl.softmax_scale, outs, counts=counts, overlap=(i % 2 == 0))
+    torch.cuda.synchronize()
+    res = {"workload": wl.name, "layers": layers, "capacity_slots": cap}
+    main = torch.cuda.current_stream()
+    i = warmup
+    for mode in ("serial", "overlapped"):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(main)
+        for j in range(steps):
+            grp.step(sels[i], qs, wl.softmax_scale, outs, counts=counts, overlap=(mode == "overlapped"))
+            ev[j + 1].record(main)
+            i += 1
+        torch.cuda.synchronize()
+        res[mode + "_us_per_group"] = round(1e3 * ev[0].elapsed_time(ev[steps]) / steps, 1)
+    misses = sum(float(c[0].item()) for c in counts) / layers
+    row = d["kv"].shape[-1] * d["kv"].element_size()
+    # read rate from pinned host memory: the library's streaming-read probe over a pinned buffer
+    pin = torch.empty(256 << 20, dtype=torch.uint8).pin_memory()
+    sink = torch.empty(max(int(B.lib().dsa_read_probe_sink_size()), 4), dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        B.read_probe(pin, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(main)
+    for _ in range(5):
+        B.read_probe(pin, sink)
+    e1.record(main)
+    torch.cuda.synchronize()
+    host_gbs = 5 * pin.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    floor_us = misses * row / (host_gbs * 1e9) * 1e6
+    ser, ovl = res["serial_us_per_group"], res["overlapped_us_per_group"]
+    res.update({"misses_per_layer_step": round(misses, 1), "hit_rate": round(1.0 - misses / (T * K), 4),
+                "host_read_probe_gbs": round(host_gbs, 1),
+                "host_read_floor_us_per_layer": round(floor_us, 1),
+                "overlap_saving_us_per_group": round(ser - ovl, 1),
+                "overlapped_us_per_layer": round(ovl / layers, 1)})
+    log("[bench] two-tier cache, %d layers sharing a selection: %.0f us per group serial, %.0f us overlapped "
+        "(%.0f us per layer; host-read floor %.0f us per layer at %.1f GB/s from pinned memory)" % (
+            layers, ser, ovl, ovl / layers, floor_us, host_gbs))
+    del d, host_kv, hots, grp, outs, sels, pin
     torch.cuda.empty_cache()
     return res
 
@@ -793,6 +885,7 @@ def main(argv=None):
     hot = None
     if not args.no_hot_cache and args.workload == DEFAULT_WORKLOAD:
         hot = hot_cache_leg(max(5, min(args.steps, 20)), 10, log)
+        hot["layers"] = hot_cache_layers_leg(max(4, min(args.steps, 10)), 4, log)
 
     # CPU baseline: the oracle on a bounded sample of query rows; its results
     # also check the timed step's selection and output for those rows.

@@ -124,3 +124,47 @@ def test_hot_cache_rejects_small_capacity():
     idx = torch.zeros((wl.total_q, wl.topk), dtype=torch.int32, device="cuda")
     with pytest.raises(B.DsaError):
         B.hot_cache_fetch(batch, d["kv"].cpu().pin_memory(), None, wl.d_latent, idx, hot)
+
+
+def test_layer_group_overlap_matches_serial_and_full_cache():
+    """Three layers sharing a selection, each with its own page table into
+    the pinned pool and its own hot set: with layer l+1's fetch on a second
+    stream during layer l's attention, every layer's output equals the
+    serial schedule's and the full-cache MLA of that layer, bit for bit,
+    step after step."""
+    from sparse_attention_dsa_amd.hot_layers import HotLayerGroup
+    wl = workloads.make_workload("single_b1_l32768", batch=3, context_lens=[3000, 5000, 2000], q_len=[1, 2, 1],
+                                 topk=256, seed=41)
+    K, T, H, L = wl.topk, wl.total_q, wl.mla_heads, 3
+    batch, d = upload(wl)
+    nblk = d["kv"].shape[0]
+    host_kv = d["kv"].cpu().pin_memory()
+    g = torch.Generator().manual_seed(5)
+    batches = []
+    for _ in range(L):
+        perm = torch.randperm(nblk, generator=g).to(torch.int32).cuda()
+        batches.append(dsa.Batch(d["context_lens"], d["query_start_loc"], perm[d["page_table"].long()].contiguous(),
+                                 wl.block_size, wl.max_q_len, wl.max_context_len))
+    qs = [d["q_mla"].roll(l, dims=1).contiguous() for l in range(L)]
+
+    def group():
+        hots = [B.HotCache(T * K + 100, wl.batch, wl.max_context_len, d["kv"].shape[-1], d["kv"].dtype)
+                for _ in range(L)]
+        grp = HotLayerGroup(batches, [host_kv] * L, [None] * L, hots, wl.d_latent, K, H)
+        grp.reset()
+        return grp
+
+    ovl, ser = group(), group()
+    for step, sel in enumerate(_selections(wl, K, steps=6, keep=0.5, seed=42)):
+        idx = torch.from_numpy(sel).cuda()
+        out_o = [torch.empty((T, H, wl.d_latent), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+        out_s = [torch.empty_like(o) for o in out_o]
+        ovl.step(idx, qs, wl.softmax_scale, out_o, overlap=True)
+        ser.step(idx, qs, wl.softmax_scale, out_s, overlap=False)
+        full = [dsa.sparse_mla_decode(batches[l], d["kv"], None, wl.d_latent, qs[l], idx, wl.softmax_scale)
+                for l in range(L)]
+        torch.cuda.synchronize()
+        for l in range(L):
+            assert torch.equal(out_o[l], out_s[l]), (step, l)
+            assert torch.equal(out_o[l], full[l]), (step, l)
+        log("  layer group step", step + 1, "ok")
