@@ -370,6 +370,26 @@ int dsa_hot_cache_fetch(const dsa_batch *batch, const dsa_latent_cache *host, co
                         dsa_hot_cache *hot, int32_t *counts, void *workspace, size_t workspace_bytes,
                         dsa_stream_t stream);
 
+/*
+ * The two phases of dsa_hot_cache_fetch as separate calls (same arguments;
+ * dsa_hot_cache_fetch = plan, then copy, with the same workspace):
+ *   dsa_hot_cache_plan  steps 1-3: hits (their last use becomes this step),
+ *                       the misses and the victims, kept in the workspace;
+ *   dsa_hot_cache_copy  step 4: each miss into its victim slot, the rows read
+ *                       from host memory; advances the clock, writes counts.
+ * For the layer-wise overlap of the same design (while layer N attends over
+ * its hot set, later layers' rows are read from host memory): the plans of
+ * later layers, short kernels, can run beside a layer's copies, which take
+ * a few compute units and the host link.  A copy must follow its own plan on
+ * the same workspace, with no other call on that workspace or hot cache in
+ * between.  Errors as dsa_hot_cache_fetch.
+ */
+int dsa_hot_cache_plan(const dsa_batch *batch, const dsa_latent_cache *host, const int32_t *indices, int32_t k,
+                       dsa_hot_cache *hot, void *workspace, size_t workspace_bytes, dsa_stream_t stream);
+int dsa_hot_cache_copy(const dsa_batch *batch, const dsa_latent_cache *host, const int32_t *indices, int32_t k,
+                       dsa_hot_cache *hot, int32_t *counts, void *workspace, size_t workspace_bytes,
+                       dsa_stream_t stream);
+
 /* Measurement helper, not a step of the method: the practical HBM read
  * bandwidth that the library's streaming kernels are compared against.
  * dsa_read_probe reads every byte of `buf` (device memory, 16-byte aligned,

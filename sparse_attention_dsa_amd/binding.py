@@ -23,7 +23,7 @@ EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_spars
            "dsa_decode_step", "dsa_workspace_size", "dsa_status_string", "dsa_check_device",
            "dsa_read_probe_sink_size", "dsa_read_probe", "dsa_hot_cache_reset", "dsa_hot_cache_workspace_size",
            "dsa_hot_cache_fetch", "dsa_decode_step_timed", "dsa_decode_step_noalloc",
-           "dsa_decode_step_fused", "dsa_check_batch")
+           "dsa_decode_step_fused", "dsa_check_batch", "dsa_hot_cache_plan", "dsa_hot_cache_copy")
 CHECK_QUERY_START, CHECK_CONTEXT, CHECK_PAGE, CHECK_INDEX = 1, 2, 4, 8   # dsa_check_batch's bits
 ERR_BAD_DEVICE_ARG = -7
 STEP_EVENTS = 5   # events of dsa_decode_step_timed: start, after sampling, indexer, selection, attention
@@ -82,6 +82,8 @@ def lib():
         L.dsa_hot_cache_workspace_size.argtypes = [P(DsaBatch), i32, i32]
         L.dsa_hot_cache_workspace_size.restype = sz
         L.dsa_hot_cache_fetch.argtypes = [P(DsaBatch), P(DsaLatentCache), vp, i32, P(DsaHotCache), vp, vp, sz, vp]
+        L.dsa_hot_cache_plan.argtypes = [P(DsaBatch), P(DsaLatentCache), vp, i32, P(DsaHotCache), vp, sz, vp]
+        L.dsa_hot_cache_copy.argtypes = [P(DsaBatch), P(DsaLatentCache), vp, i32, P(DsaHotCache), vp, vp, sz, vp]
         L.dsa_decode_step_timed.argtypes = [P(DsaBatch), P(DsaIndexCache), vp, vp, i32, P(DsaLatentCache), vp, i32,
                                             i32, f32, vp, vp, vp, vp, sz, vp, P(vp), i32]
         L.dsa_decode_step_noalloc.argtypes = [P(DsaBatch), P(DsaIndexCache), vp, vp, i32, P(DsaLatentCache), vp,
@@ -91,7 +93,7 @@ def lib():
         L.dsa_check_batch.argtypes = [P(DsaBatch), i32, vp, i32, P(C.c_uint32), vp]
         for name in ("dsa_check_batch", "dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
                      "dsa_decode_step", "dsa_check_device", "dsa_read_probe", "dsa_hot_cache_reset",
-                     "dsa_hot_cache_fetch", "dsa_decode_step_timed", "dsa_decode_step_noalloc",
+                     "dsa_hot_cache_fetch", "dsa_hot_cache_plan", "dsa_hot_cache_copy", "dsa_decode_step_timed", "dsa_decode_step_noalloc",
                      "dsa_decode_step_fused"):
             getattr(L, name).restype = C.c_int
         _lib = L
@@ -353,19 +355,31 @@ def hot_cache_reset(batch: "Batch", hot: HotCache, stream=None):
     _check("dsa_hot_cache_reset", lib().dsa_hot_cache_reset(C.byref(b), C.byref(h), _stream(stream)))
 
 
-def hot_cache_fetch(batch: "Batch", host_kv, host_scales, d_latent, indices, hot: HotCache, counts=None,
-                    workspace=None, stream=None):
-    """Make every token of `indices` resident in `hot` (host_kv / host_scales:
-    the paged latent cache in pinned host memory)."""
-    k = indices.shape[1]
+def hot_cache_workspace(batch: "Batch", k: int, hot: HotCache, device="cuda") -> torch.Tensor:
     b = batch.struct()
     need = int(lib().dsa_hot_cache_workspace_size(C.byref(b), k, hot.capacity))
+    return torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+
+
+def hot_cache_fetch(batch: "Batch", host_kv, host_scales, d_latent, indices, hot: HotCache, counts=None,
+                    workspace=None, stream=None, phase="fetch"):
+    """Make every token of `indices` resident in `hot` (host_kv / host_scales:
+    the paged latent cache in pinned host memory).  phase "plan" or "copy"
+    runs one half (dsa_hot_cache_plan / dsa_hot_cache_copy)."""
+    k = indices.shape[1]
+    b = batch.struct()
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=indices.device)
+        workspace = hot_cache_workspace(batch, k, hot, indices.device)
     c, h = latent_cache(host_kv, host_scales, d_latent), hot.struct()
-    _check("dsa_hot_cache_fetch", lib().dsa_hot_cache_fetch(C.byref(b), C.byref(c), _ptr(indices), k, C.byref(h),
-                                                            _ptr(counts), _ptr(workspace), workspace.numel(),
-                                                            _stream(stream)))
+    if phase == "plan":
+        _check("dsa_hot_cache_plan", lib().dsa_hot_cache_plan(C.byref(b), C.byref(c), _ptr(indices), k, C.byref(h),
+                                                              _ptr(workspace), workspace.numel(), _stream(stream)))
+    else:
+        fn = "dsa_hot_cache_fetch" if phase == "fetch" else "dsa_hot_cache_copy"
+        if phase not in ("fetch", "copy"):
+            raise ValueError("phase is fetch, plan or copy")
+        _check(fn, getattr(lib(), fn)(C.byref(b), C.byref(c), _ptr(indices), k, C.byref(h), _ptr(counts),
+                                      _ptr(workspace), workspace.numel(), _stream(stream)))
     return workspace
 
 

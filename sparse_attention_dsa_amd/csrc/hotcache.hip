@@ -41,6 +41,8 @@ constexpr int HC_WAVES = HC_THREADS / 64;
 constexpr int HC_PER = 4;                         // items per thread in the scans
 constexpr int HC_ITEMS = HC_THREADS * HC_PER;     // items per workgroup in the scans
 constexpr int HC_AGE_BINS = 65536;             // one 16-bit half of an age
+constexpr int HC_COARSE = 256;                 // coarse bins of a level: the half's top 8 bits
+constexpr int HC_HIST_WORDS = 2 * (HC_AGE_BINS + HC_COARSE);
 
 // scalars in the workspace: misses, slots older than a*, a*, how many of age
 // a* are taken, evictions, this step, victims, the high half of a* and the
@@ -58,7 +60,8 @@ struct HotArgs {
     int32_t* clock;          // [1]
     int capacity, maxctx, wpr;
     uint32_t* scal;          // [HS_N]
-    uint32_t* hist;          // [2][HC_AGE_BINS]: high halves, then low halves within one high bucket
+    uint32_t* hist;          // [2][HC_AGE_BINS]: high halves, then low halves within one high bucket;
+                             // then [2][HC_COARSE]: the same counts by the half's top 8 bits
     uint32_t* bitmap;        // [B][wpr]
     uint32_t* wsum;          // per-workgroup word sums, then offsets
     uint32_t* csum;          // per-workgroup (older, equal) counts, then offsets
@@ -85,7 +88,7 @@ __device__ __forceinline__ uint32_t slot_age(int32_t lu, int step) {
 __global__ __launch_bounds__(HC_THREADS) void hc_clear(HotArgs a, int64_t nwords) {
     const int64_t i = (int64_t)blockIdx.x * HC_THREADS + threadIdx.x;
     if (i < HS_N) a.scal[i] = i == HS_STEP ? (uint32_t)(*a.clock + 1) : 0u;
-    if (i < 2 * HC_AGE_BINS) a.hist[i] = 0u;
+    if (i < HC_HIST_WORDS) a.hist[i] = 0u;
     if (i < nwords) a.bitmap[i] = 0u;
 }
 
@@ -191,10 +194,13 @@ __global__ __launch_bounds__(HC_THREADS) void hc_write_misses(HotArgs a, int64_t
 // the global histogram, one count per run of equal bins among a thread's
 // HC_RUN slots.
 constexpr int HC_RUN = 32;
+constexpr int HC_COPY_WGS = 64;   // workgroups of the row copies
 constexpr int HC_LDS_BINS = 4096;
 __global__ __launch_bounds__(HC_THREADS) void hc_age_hist(HotArgs a, int level) {
     __shared__ uint32_t h[HC_LDS_BINS + 1];                   // last bin: the never-used age (level 1)
+    __shared__ uint32_t hc[HC_COARSE];
     for (int i = threadIdx.x; i <= HC_LDS_BINS; i += HC_THREADS) h[i] = 0u;
+    for (int i = threadIdx.x; i < HC_COARSE; i += HC_THREADS) hc[i] = 0u;
     __syncthreads();
     const int step = (int)a.scal[HS_STEP];
     const uint32_t hi = a.scal[HS_HI];
@@ -220,6 +226,7 @@ __global__ __launch_bounds__(HC_THREADS) void hc_age_hist(HotArgs a, int level) 
         const bool in_lds = elig && (is_never || bin < HC_LDS_BINS);
         // one LDS atomic per wave when its lanes share the bin (the usual case)
         lds_count(h, is_never ? (uint32_t)HC_LDS_BINS : (uint32_t)min(bin, HC_LDS_BINS - 1), in_lds);
+        lds_count(hc, (uint32_t)bin >> 8, elig);
         if (!elig || in_lds) continue;
         if (bin != cur) {
             if (n) atomicAdd(&gh[cur], n);
@@ -233,6 +240,9 @@ __global__ __launch_bounds__(HC_THREADS) void hc_age_hist(HotArgs a, int level) 
     for (int i = threadIdx.x; i < HC_LDS_BINS; i += HC_THREADS)
         if (h[i]) atomicAdd(&gh[i], h[i]);
     if (threadIdx.x == 0 && h[HC_LDS_BINS]) atomicAdd(&gh[never & 0xFFFFu], h[HC_LDS_BINS]);
+    uint32_t* gc = a.hist + 2 * HC_AGE_BINS + (level ? HC_COARSE : 0);
+    for (int i = threadIdx.x; i < HC_COARSE; i += HC_THREADS)
+        if (hc[i]) atomicAdd(&gc[i], hc[i]);
 }
 
 // One workgroup, per level: the bucket holding the M-th oldest eligible slot
@@ -241,14 +251,17 @@ __global__ __launch_bounds__(HC_THREADS) void hc_age_hist(HotArgs a, int level) 
 // 16) | low, the number of eligible slots older than a*, and how many of age
 // a* are taken.
 __global__ __launch_bounds__(HC_THREADS) void hc_pick(HotArgs a, int level) {
+    static_assert(HC_THREADS == HC_COARSE && HC_AGE_BINS == 256 * HC_COARSE, "one coarse bin a thread");
     __shared__ uint32_t wsum[HC_WAVES];
-    constexpr int PER = HC_AGE_BINS / HC_THREADS;            // 256 bins a thread, oldest first
+    __shared__ uint32_t s_cb, s_cum;
     const uint32_t M = a.scal[HS_MISSES];
     const uint32_t* h = a.hist + (level ? HC_AGE_BINS : 0);
+    const uint32_t* hcs = a.hist + 2 * HC_AGE_BINS + (level ? HC_COARSE : 0);
     const uint32_t base = level ? a.scal[HS_OLDER_HI] : 0u;
-    // thread i owns bins [HC_AGE_BINS - PER (i + 1), HC_AGE_BINS - 1 - PER i]
-    uint32_t c = 0;
-    for (int q = 0; q < PER; ++q) c += h[HC_AGE_BINS - 1 - PER * threadIdx.x - q];
+    if (threadIdx.x == 0) s_cb = 0xFFFFFFFFu;
+    // coarse bins oldest first (thread i: coarse bin 255 - i), then the 256
+    // bins of the one where the count reaches `want`
+    const uint32_t c = hcs[HC_COARSE - 1 - threadIdx.x];
     uint32_t tot;
     const uint32_t ex = block_excl_scan<HC_WAVES>(c, wsum, &tot);
     if (level == 0 && threadIdx.x == 0) a.scal[HS_VICTIMS] = min(M, tot);
@@ -263,22 +276,24 @@ __global__ __launch_bounds__(HC_THREADS) void hc_pick(HotArgs a, int level) {
         return;
     }
     if (base + ex < want && base + ex + c >= want) {
-        uint32_t cum = base + ex;
-        for (int q = 0; q < PER; ++q) {
-            const uint32_t bin = (uint32_t)(HC_AGE_BINS - 1 - PER * threadIdx.x - q);
-            const uint32_t hb = h[bin];
-            if (cum + hb >= want) {
-                if (level == 0) {
-                    a.scal[HS_HI] = bin;
-                    a.scal[HS_OLDER_HI] = cum;
-                } else {
-                    a.scal[HS_AGE] = (a.scal[HS_HI] << 16) | bin;
-                    a.scal[HS_OLDER] = cum;
-                    a.scal[HS_NEED] = want - cum;
-                }
-                break;
-            }
-            cum += hb;
+        s_cb = HC_COARSE - 1 - threadIdx.x;
+        s_cum = base + ex;
+    }
+    __syncthreads();
+    const uint32_t cb = s_cb;
+    if (cb >= (uint32_t)HC_COARSE) return;   // counts inconsistent with `want`: nothing chosen
+    const uint32_t bin = 256u * cb + 255u - threadIdx.x;
+    const uint32_t hb = h[bin];
+    uint32_t tot2;
+    const uint32_t cum = s_cum + block_excl_scan<HC_WAVES>(hb, wsum, &tot2);
+    if (cum < want && cum + hb >= want) {
+        if (level == 0) {
+            a.scal[HS_HI] = bin;
+            a.scal[HS_OLDER_HI] = cum;
+        } else {
+            a.scal[HS_AGE] = (a.scal[HS_HI] << 16) | bin;
+            a.scal[HS_OLDER] = cum;
+            a.scal[HS_NEED] = want - cum;
         }
     }
 }
@@ -326,18 +341,7 @@ __device__ __forceinline__ void copy_row(const uint8_t* __restrict__ src, uint8_
     if (o1 < bytes) *(u32x4*)(dst + o1) = v1;
 }
 
-// One wave per miss: evict the victim's token, claim the slot, copy the row
-// (and scale) from host memory.
-__global__ __launch_bounds__(HC_THREADS) void hc_assign(HotArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int i = blockIdx.x * HC_WAVES + (threadIdx.x >> 6);
-    const uint32_t M = a.scal[HS_MISSES], nv = a.scal[HS_VICTIMS];
-    const int step = (int)a.scal[HS_STEP];
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        *a.clock = step;
-        if (a.counts) a.counts[0] = (int32_t)M;
-    }
-    if ((uint32_t)i >= M || (uint32_t)i >= nv) return;
+__device__ __forceinline__ void hc_assign_one(const HotArgs& a, uint32_t i, int step, int lane) {
     const int64_t rs = a.miss[i];
     const int r = (int)(rs >> 32), s = (int)(rs & 0xFFFFFFFF);
     const int v = a.victims[i];
@@ -356,6 +360,24 @@ __global__ __launch_bounds__(HC_THREADS) void hc_assign(HotArgs a) {
     const int64_t row = (int64_t)a.host_pt[(size_t)r * a.g.max_blocks + s / bs] * bs + s % bs;
     copy_row(a.host_kv + row * a.row_bytes, a.hot_kv + (int64_t)v * a.row_bytes, a.row_bytes, lane);
     if (a.hot_scales && lane == 0) a.hot_scales[v] = a.host_scales[row];
+}
+
+// Per miss, one wave: evict the victim's token, claim the slot, copy the row
+// (and scale) from host memory.  A fixed number of workgroups (HC_COPY_WGS)
+// takes the misses in turn: enough rows in flight for the host link, while
+// the other compute units stay free for kernels that run beside the copy
+// (the next layer's attention).
+__global__ __launch_bounds__(HC_THREADS) void hc_assign(HotArgs a) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t M = a.scal[HS_MISSES], nv = a.scal[HS_VICTIMS];
+    const int step = (int)a.scal[HS_STEP];
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        *a.clock = step;
+        if (a.counts) a.counts[0] = (int32_t)M;
+    }
+    const uint32_t n = min(M, nv), nw = gridDim.x * HC_WAVES;
+    for (uint32_t i = blockIdx.x * HC_WAVES + (threadIdx.x >> 6); i < n; i += nw)
+        hc_assign_one(a, i, step, lane);
 }
 
 __global__ void hc_finish(HotArgs a) {
@@ -386,7 +408,7 @@ HotLayout hot_layout(const dsa_batch* b, int k, int capacity) {
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
     l.scal = 0;
     l.hist = al(l.scal + sizeof(uint32_t) * HS_N);
-    l.bitmap = l.hist + sizeof(uint32_t) * 2 * HC_AGE_BINS;   // contiguous with hist: one clear
+    l.bitmap = l.hist + sizeof(uint32_t) * HC_HIST_WORDS;   // contiguous with hist: one clear
     l.wsum = al(l.bitmap + sizeof(uint32_t) * (size_t)l.nwords);
     l.csum = al(l.wsum + sizeof(uint32_t) * ((size_t)l.nwg_words + 1));
     l.miss = al(l.csum + sizeof(uint32_t) * (2 * (size_t)l.nwg_slots + 2));
@@ -430,9 +452,13 @@ int dsa_hot_cache_reset(const dsa_batch* batch, dsa_hot_cache* hot, dsa_stream_t
     return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
 }
 
-int dsa_hot_cache_fetch(const dsa_batch* b, const dsa_latent_cache* host, const int32_t* indices, int32_t k,
-                        dsa_hot_cache* hot, int32_t* counts, void* workspace, size_t workspace_bytes,
-                        dsa_stream_t stream) {
+// Phases of a fetch: the plan (hits, misses, victims) and the copy (misses
+// into victims, rows from host memory, clock and counts).
+enum { HOT_PLAN = 1, HOT_COPY = 2 };
+
+static int hot_cache_run(const dsa_batch* b, const dsa_latent_cache* host, const int32_t* indices, int32_t k,
+                         dsa_hot_cache* hot, int32_t* counts, void* workspace, size_t workspace_bytes,
+                         dsa_stream_t stream, int phases) {
     using namespace dsa;
     if (!b || b->num_requests < 1 || b->total_q < 1 || b->max_q_len < 1 || b->max_context_len < 1 ||
         !b->context_lens || !b->query_start_loc || !b->page_table || b->block_size < 1 || b->max_blocks < 1 ||
@@ -488,11 +514,12 @@ int dsa_hot_cache_fetch(const dsa_batch* b, const dsa_latent_cache* host, const 
 
     hipStream_t s = (hipStream_t)stream;
     const bool dbg = debug_mode();
-    if (dbg) {
+    if (dbg && (phases & HOT_PLAN)) {
         if (const int st = run_batch_check(a.g, host->num_blocks, true, indices, k, nullptr, s); st != DSA_OK)
             return st;
     }
-    const int64_t nclear = std::max<int64_t>(2 * HC_AGE_BINS, l.nwords);
+    if (phases & HOT_PLAN) {
+    const int64_t nclear = std::max<int64_t>(HC_HIST_WORDS, l.nwords);
     hipLaunchKernelGGL(hc_clear, dim3((unsigned)((nclear + HC_THREADS - 1) / HC_THREADS)), dim3(HC_THREADS), 0, s, a,
                        l.nwords);
     hipLaunchKernelGGL(hc_mark, dim3((k + HC_THREADS - 1) / HC_THREADS, b->total_q), dim3(HC_THREADS), 0, s, a);
@@ -509,10 +536,31 @@ int dsa_hot_cache_fetch(const dsa_batch* b, const dsa_latent_cache* host, const 
     hipLaunchKernelGGL(hc_scan, dim3(1), dim3(HC_THREADS), 0, s, a.csum, l.nwg_slots, 2,
                        a.csum + 2 * (size_t)l.nwg_slots);
     hipLaunchKernelGGL(hc_write_victims, dim3(l.nwg_slots), dim3(HC_THREADS), 0, s, a);
-    const int64_t tk = (int64_t)b->total_q * k;
-    hipLaunchKernelGGL(hc_assign, dim3((unsigned)((tk + HC_WAVES - 1) / HC_WAVES)), dim3(HC_THREADS), 0, s, a);
-    hipLaunchKernelGGL(hc_finish, dim3(1), dim3(1), 0, s, a);
+    }
+    if (phases & HOT_COPY) {
+        const int64_t tk = (int64_t)b->total_q * k;
+        hipLaunchKernelGGL(hc_assign, dim3((unsigned)std::min<int64_t>(HC_COPY_WGS, (tk + HC_WAVES - 1) / HC_WAVES)),
+                           dim3(HC_THREADS), 0, s, a);
+        hipLaunchKernelGGL(hc_finish, dim3(1), dim3(1), 0, s, a);
+    }
     return debug_finish(dbg, hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH, s);
+}
+
+int dsa_hot_cache_fetch(const dsa_batch* b, const dsa_latent_cache* host, const int32_t* indices, int32_t k,
+                        dsa_hot_cache* hot, int32_t* counts, void* workspace, size_t workspace_bytes,
+                        dsa_stream_t stream) {
+    return hot_cache_run(b, host, indices, k, hot, counts, workspace, workspace_bytes, stream, HOT_PLAN | HOT_COPY);
+}
+
+int dsa_hot_cache_plan(const dsa_batch* b, const dsa_latent_cache* host, const int32_t* indices, int32_t k,
+                       dsa_hot_cache* hot, void* workspace, size_t workspace_bytes, dsa_stream_t stream) {
+    return hot_cache_run(b, host, indices, k, hot, nullptr, workspace, workspace_bytes, stream, HOT_PLAN);
+}
+
+int dsa_hot_cache_copy(const dsa_batch* b, const dsa_latent_cache* host, const int32_t* indices, int32_t k,
+                       dsa_hot_cache* hot, int32_t* counts, void* workspace, size_t workspace_bytes,
+                       dsa_stream_t stream) {
+    return hot_cache_run(b, host, indices, k, hot, counts, workspace, workspace_bytes, stream, HOT_COPY);
 }
 
 }  // extern "C"

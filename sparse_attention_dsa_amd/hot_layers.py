@@ -6,17 +6,17 @@ hot set, the host reads of layer N+1's missing rows are already running.
 
 A group of layers shares one selection (the IndexShare pattern: the indices
 of the group's first layer serve the others), so every layer's fetch can
-start as soon as the selection exists.  Fetches run in layer order on one
-stream and attention in layer order on a second one, each attention waiting
-for its own layer's fetch, each fetch waiting for the previous step's
-attention on the same hot set (its slots are about to be overwritten).  Both
-streams keep the default priority.  This module only orders library calls
-(dsa_hot_cache_fetch, dsa_sparse_mla_decode) with streams and events; every
-step runs in the library's kernels.
+start as soon as the selection exists.  Each fetch is taken in its two
+halves (dsa_hot_cache_plan, dsa_hot_cache_copy): the plans (short kernels:
+hits, misses, victims) in layer order on one stream, the copies (host reads)
+in layer order on a second, attention in layer order on a third.  A copy
+waits for its plan, an attention for its copy, and a plan for the previous
+step's attention on the same hot set (whose slots it is about to reassign).
+So later layers' plans run beside a layer's copies, and a layer's attention
+beside the next layer's copies.  All streams keep the default priority.
 """
 from __future__ import annotations
 
-import ctypes
 from typing import List, Optional, Sequence
 
 import torch
@@ -39,15 +39,13 @@ class HotLayerGroup:
         self.L = len(batches)
         dev = hots[0].kv.device
         self.hot_batches = [h.batch(b) for h, b in zip(hots, batches)]
-        need_f = 0
-        for b, h in zip(batches, hots):
-            st = b.struct()
-            need_f = max(need_f, int(B.lib().dsa_hot_cache_workspace_size(ctypes.byref(st), k, h.capacity)))
-        self.ws_fetch = torch.empty(max(need_f, 256), dtype=torch.uint8, device=dev)
+        self.ws_fetch = [B.hot_cache_workspace(b, k, h, dev) for b, h in zip(batches, hots)]
         need_m = max(B.workspace_size(B.OP_MLA_DECODE, hb, k, n_heads) for hb in self.hot_batches)
         self.ws_mla = torch.empty(max(need_m, 256), dtype=torch.uint8, device=dev)
-        self.fetch_stream = torch.cuda.Stream(device=dev)
+        self.plan_stream = torch.cuda.Stream(device=dev)
+        self.copy_stream = torch.cuda.Stream(device=dev)
         self.mla_stream = torch.cuda.Stream(device=dev)
+        self.planned = [torch.cuda.Event() for _ in range(self.L)]
         self.fetched = [torch.cuda.Event() for _ in range(self.L)]
         self.attended = [torch.cuda.Event() for _ in range(self.L)]
         self.started = False
@@ -61,35 +59,41 @@ class HotLayerGroup:
              overlap: bool = True):
         """One decode step of the group for selection `indices` [T][k]:
         layer l's queries qs[l], outputs outs[l] (and lses[l], counts[l] when
-        given).  With overlap, layer l+1's fetch runs during layer l's
-        attention; without, fetch and attention alternate on the current
-        stream.  Ordered after the current stream's earlier work, and the
-        current stream's later work is ordered after it."""
+        given).  With overlap, the three-stream schedule above; without,
+        fetch and attention alternate on the current stream.  Ordered after
+        the current stream's earlier work, and the current stream's later
+        work is ordered after it."""
         main = torch.cuda.current_stream()
         lses = lses if lses is not None else [None] * self.L
         counts = counts if counts is not None else [None] * self.L
+        fetch = lambda l, phase, stream: B.hot_cache_fetch(
+            self.batches[l], self.host_kv[l], self.host_scales[l], self.d_latent, indices, self.hots[l],
+            counts=counts[l], workspace=self.ws_fetch[l], stream=stream, phase=phase)
+        attend = lambda l, stream: B.sparse_mla_decode(
+            self.hot_batches[l], self.hots[l].kv, self.hots[l].scales, self.d_latent, qs[l], indices, scale,
+            out=outs[l], lse=lses[l], workspace=self.ws_mla, stream=stream)
         if not overlap:
             for l in range(self.L):
-                B.hot_cache_fetch(self.batches[l], self.host_kv[l], self.host_scales[l], self.d_latent, indices,
-                                  self.hots[l], counts=counts[l], workspace=self.ws_fetch, stream=main)
-                B.sparse_mla_decode(self.hot_batches[l], self.hots[l].kv, self.hots[l].scales, self.d_latent, qs[l],
-                                    indices, scale, out=outs[l], lse=lses[l], workspace=self.ws_mla, stream=main)
+                fetch(l, "fetch", main)
+                attend(l, main)
             return
         start = torch.cuda.Event()
         start.record(main)
-        F, M = self.fetch_stream, self.mla_stream
-        F.wait_event(start)
-        M.wait_event(start)
+        P, F, M = self.plan_stream, self.copy_stream, self.mla_stream
+        for st in (P, F, M):
+            st.wait_event(start)
         for l in range(self.L):
             if self.started:
-                F.wait_event(self.attended[l])   # the previous step's attention on this hot set is done
-            B.hot_cache_fetch(self.batches[l], self.host_kv[l], self.host_scales[l], self.d_latent, indices,
-                              self.hots[l], counts=counts[l], workspace=self.ws_fetch, stream=F)
+                P.wait_event(self.attended[l])   # the previous step is done with this hot set and workspace
+            fetch(l, "plan", P)
+            self.planned[l].record(P)
+        for l in range(self.L):
+            F.wait_event(self.planned[l])
+            fetch(l, "copy", F)
             self.fetched[l].record(F)
+        for l in range(self.L):
             M.wait_event(self.fetched[l])
-            B.sparse_mla_decode(self.hot_batches[l], self.hots[l].kv, self.hots[l].scales, self.d_latent, qs[l],
-                                indices, scale, out=outs[l], lse=lses[l], workspace=self.ws_mla, stream=M)
+            attend(l, M)
             self.attended[l].record(M)
         self.started = True
         main.wait_event(self.attended[self.L - 1])
-        main.wait_event(self.fetched[self.L - 1])

@@ -181,3 +181,12 @@ def test_struct_layouts_match_the_header(tmp_path):
         assert int(got[name]) == C.sizeof(cls), name
         for f, _ in cls._fields_:
             assert int(got["%s.%s" % (name, f)]) == getattr(cls, f).offset, (name, f)
+
+
+def test_hot_cache_plan_and_copy_host_checks(L):
+    b = _batch()
+    bf = B.DsaLatentCache(0x10, None, B.BF16, 512, 64)
+    hot = B.DsaHotCache(0x100, None, 64, 0x200, 0x300, 0x400, 0x500)
+    assert L.dsa_hot_cache_plan(C.byref(b), C.byref(bf), None, 16, C.byref(hot), 0x1, 1 << 30, None) == -1
+    assert L.dsa_hot_cache_copy(C.byref(b), C.byref(bf), 0x1, 33, C.byref(hot), None, 0x1, 1 << 30, None) == -1
+    assert L.dsa_hot_cache_plan(C.byref(b), C.byref(bf), 0x1, 16, C.byref(hot), 0x1, 8, None) == -3
