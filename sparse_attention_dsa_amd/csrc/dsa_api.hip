@@ -99,7 +99,7 @@ StepLayout step_layout(const dsa_batch* b, int k, int n_heads, int mla_path_id) 
     l.tk = topk_layout(align_up(l.indices + sizeof(int32_t) * T * k), b);
     l.bound = l.tk.end;
     l.count = align_up(l.bound + sizeof(uint32_t) * T);
-    l.cand = align_up(l.count + sizeof(uint32_t) * T);
+    l.cand = align_up(l.count + sizeof(uint32_t) * T * ROW_COUNT_STRIDE);
     l.mla_base = align_up(l.cand + sizeof(uint64_t) * T * TOPK_LIST);
     l.ml = mla_layout(l.mla_base, b, k, n_heads, false, mla_path_id);
     l.end = l.ml.end;
@@ -128,7 +128,7 @@ FusedLayout fused_layout(const dsa_batch* b, int k, int n_heads) {
     l.indices = align_up(sizeof(float) * T * l.ld);
     l.cand = align_up(l.indices + sizeof(int32_t) * T * k);
     l.count = align_up(l.cand + sizeof(uint64_t) * T * TOPK_LIST);
-    l.excl = align_up(l.count + sizeof(uint32_t) * T);
+    l.excl = align_up(l.count + sizeof(uint32_t) * T * ROW_COUNT_STRIDE);
     l.req_done = align_up(l.excl + sizeof(uint64_t) * T);
     l.prefix = align_up(l.req_done + sizeof(uint32_t) * B);
     // chunks of 64 pages of 64 tokens: at most this many per request

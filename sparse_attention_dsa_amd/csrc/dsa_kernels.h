@@ -18,6 +18,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // TOPK_CHUNK-score chunks whose candidates fill slots of TOPK_CAND_CAP.
 constexpr int TOPK_MAX_K = 4096;
 constexpr int TOPK_LIST = 12288;
+// Candidate counters of the rows sit one 128-byte line apart: at the end of
+// their shares many waves append to the same few rows at once, and counters
+// sharing a line would serialise all of those atomics together.
+constexpr int ROW_COUNT_STRIDE = 32;
 constexpr int TOPK_CHUNK = 8192;
 constexpr int TOPK_CAND_CAP = 4096;
 
@@ -215,7 +219,7 @@ struct IndexerArgs {
     // per query row, the composites of the scores at or above the key bound
     // go to an unordered list of TOPK_LIST slots instead of the score rows
     uint32_t* bound;         // [T] key bound (written by the sample kernel)
-    uint32_t* row_count;     // [T] candidates appended (may exceed TOPK_LIST)
+    uint32_t* row_count;     // [T][ROW_COUNT_STRIDE]: candidates appended (may exceed TOPK_LIST)
     uint64_t* cand;          // [T][TOPK_LIST]
     int k;                   // top-K size the bound is drawn for
 };

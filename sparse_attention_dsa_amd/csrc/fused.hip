@@ -150,7 +150,7 @@ __global__ __launch_bounds__(1024) void fused_init(FusedArgs f, uint32_t grid) {
     __shared__ uint32_t s_pos[1024];
     for (int i = tid; i < FC_N; i += 1024) f.ctr[i] = 0u;
     for (int i = tid; i < G.T; i += 1024) {
-        f.ia.row_count[i] = 0u;
+        f.ia.row_count[(size_t)i * ROW_COUNT_STRIDE] = 0u;
         f.row_excl[i] = 0ull;
     }
     for (int i = tid; i < G.B; i += 1024) f.req_done[i] = 0u;
@@ -430,7 +430,7 @@ __device__ void fused_chunk(const FusedArgs& f, int r, int pg0, int npg, ChunkLd
         for (int i = 0; i < FU_WAVE_PAGES; ++i) total += __popcll(__ballot(kk[i] != 0u && kk[i] >= X));
         uint32_t base = 0u;
         if (lane == 0) {
-            base = atomicAdd(&a.row_count[t], (uint32_t)total);
+            base = atomicAdd(&a.row_count[(size_t)t * ROW_COUNT_STRIDE], (uint32_t)total);
             if (excl) atomicMax(&f.row_excl[t], excl);
         }
         base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
@@ -465,7 +465,7 @@ __device__ void fused_select(const FusedArgs& f, int r, SelShared<FU_THREADS>& S
         if (n <= (int)K) {   // every visible token, then -1 padding
             for (int i = tid; i < (int)K; i += FU_THREADS) st_agent(out + i, i < n ? i : -1);
         } else {
-            const uint32_t cnt = ld_relaxed(&ia.row_count[t]);
+            const uint32_t cnt = ld_relaxed(&ia.row_count[(size_t)t * ROW_COUNT_STRIDE]);
             bool done = false;
             if (cnt >= K && cnt <= (uint32_t)SEL_LIST) {
                 const int count = (int)cnt;

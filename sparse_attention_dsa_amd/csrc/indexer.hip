@@ -483,7 +483,7 @@ void indexer_fp8_persistent(IndexerArgs a, int qgroups) {
     auto flush = [&](int j) {      // reserve list space; the copy happens in complete()
         complete(j);
         if (nst[j] == 0) return;
-        if (lane == 0) pbase[j] = atomicAdd(&a.row_count[trow[j]], (uint32_t)nst[j]);
+        if (lane == 0) pbase[j] = atomicAdd(&a.row_count[(size_t)trow[j] * ROW_COUNT_STRIDE], (uint32_t)nst[j]);
         pn[j] = nst[j];
         ph[j] = half[j];
         prow[j] = trow[j];
@@ -597,11 +597,14 @@ void indexer_fp8_persistent(IndexerArgs a, int qgroups) {
         }
     }
     if constexpr (EMIT) {
+        // every row's last reservation in flight before waiting for any:
+        // at the end of the shares many waves append to the same few rows
 #pragma unroll
-        for (int j = 0; j < NQ; ++j) {
-            flush(j);
-            complete(j);
-        }
+        for (int j = 0; j < NQ; ++j) complete(j);
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) flush(j);
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) complete(j);
     }
 }
 
@@ -624,7 +627,7 @@ __global__ __launch_bounds__(SB_THREADS) void indexer_sample_bound(IndexerArgs a
     float wv[HT][4];
     load_query<HT>(a, t, lane, qf, wv);   // in flight while the row's length arrives
     const int n = row_visible(G, t);
-    if (tid == 0) a.row_count[t] = 0u;
+    if (tid == 0) a.row_count[(size_t)t * ROW_COUNT_STRIDE] = 0u;
     if (n <= TOPK_LIST) {
         if (tid == 0) a.bound[t] = 0u;
         return;

@@ -266,7 +266,7 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_select_cand(TopkArgs a, Inde
         return;
     }
     __shared__ SelShared<SEL_THREADS> S;
-    const uint32_t cnt = ia.row_count[t];
+    const uint32_t cnt = ia.row_count[(size_t)t * ROW_COUNT_STRIDE];
     if (cnt >= K && cnt <= (uint32_t)SEL_LIST) {
         const int count = (int)cnt;
         const uint64_t* src = ia.cand + (size_t)t * TOPK_LIST;
