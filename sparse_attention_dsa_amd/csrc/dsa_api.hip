@@ -130,7 +130,7 @@ FusedLayout fused_layout(const dsa_batch* b, int k, int n_heads) {
     l.count = align_up(l.cand + sizeof(uint64_t) * T * TOPK_LIST);
     l.excl = align_up(l.count + sizeof(uint32_t) * T * ROW_COUNT_STRIDE);
     l.req_done = align_up(l.excl + sizeof(uint64_t) * T);
-    l.prefix = align_up(l.req_done + sizeof(uint32_t) * B);
+    l.prefix = align_up(l.req_done + sizeof(uint32_t) * B * ROW_COUNT_STRIDE);
     // chunks of 64 pages of 64 tokens: at most this many per request
     const size_t max_chunks = B * (size_t)((b->max_context_len + 64 * 64 - 1) / (64 * 64));
     l.chunk_req = align_up(l.prefix + sizeof(uint32_t) * (B + 1));

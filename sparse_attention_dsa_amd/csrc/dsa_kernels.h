@@ -255,7 +255,10 @@ struct MlaArgs {
 // attention queue, the next chunk of the key stream, the attention slices not
 // yet finished, an error word, the number of chunks, and the number of
 // selection items (requests with query rows).
-enum { FC_SQ_HEAD = 0, FC_SQ_TAIL, FC_MQ_HEAD, FC_MQ_TAIL, FC_TICKET, FC_WORK, FC_ERROR, FC_NCHUNKS, FC_NSEL, FC_N = 16 };
+// Counters that every workgroup updates or polls sit on 128-byte lines of
+// their own (a queue's head and tail share one, as they are read together).
+enum { FC_SQ_HEAD = 0, FC_SQ_TAIL = 1, FC_MQ_HEAD = 32, FC_MQ_TAIL = 33, FC_TICKET = 64, FC_WORK = 96,
+       FC_ERROR = 128, FC_NCHUNKS = 160, FC_NSEL = 161, FC_N = 192 };
 enum { RQ_EMPTY = 0, RQ_SEL = 1, RQ_MLA = 2 };
 struct FusedArgs {
     IndexerArgs ia;                  // keys, queries, weights, k; cand/row_count: candidate lists;
@@ -265,7 +268,7 @@ struct FusedArgs {
     uint32_t* ctr;                   // [FC_N]
     uint32_t* chunk_prefix;          // [B] stream position of request r's first chunk
     uint32_t* chunk_req;             // [chunks][2] request and first page of each chunk of the stream
-    uint32_t* req_done;              // [B] waves done with the request's pages
+    uint32_t* req_done;              // [B][ROW_COUNT_STRIDE] waves done with the request's pages
     unsigned long long* row_excl;    // [T] largest composite a chunk left out (0: none)
     uint32_t* row_slot;              // [T] first partial slot of the row's slices
     uint32_t* row_splits;            // [T] slices of the row's attention

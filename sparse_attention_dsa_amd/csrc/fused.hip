@@ -153,7 +153,7 @@ __global__ __launch_bounds__(1024) void fused_init(FusedArgs f, uint32_t grid) {
         f.ia.row_count[(size_t)i * ROW_COUNT_STRIDE] = 0u;
         f.row_excl[i] = 0ull;
     }
-    for (int i = tid; i < G.B; i += 1024) f.req_done[i] = 0u;
+    for (int i = tid; i < G.B; i += 1024) f.req_done[(size_t)i * ROW_COUNT_STRIDE] = 0u;
     for (int i = tid; i < f.rq_cap; i += 1024) f.rq[4 * (size_t)i] = RQ_EMPTY;
     if (tid < 4) carry[tid] = 0u;
     __syncthreads();
@@ -652,8 +652,8 @@ void fused_decode(FusedArgs f) {
             if (tid == 0) {
                 const uint32_t nw = (uint32_t)min(4, (pages - cpg + FU_WAVE_PAGES - 1) / FU_WAVE_PAGES);
                 const uint32_t waves_r = (uint32_t)((pages + FU_WAVE_PAGES - 1) / FU_WAVE_PAGES);
-                const uint32_t prev = __hip_atomic_fetch_add(&f.req_done[r], nw, __ATOMIC_RELAXED,
-                                                             __HIP_MEMORY_SCOPE_AGENT);
+                const uint32_t prev = __hip_atomic_fetch_add(&f.req_done[(size_t)r * ROW_COUNT_STRIDE], nw,
+                                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if (prev + nw == waves_r) rq_push(f, 0, RQ_SEL, (uint32_t)r, 0u, 0u);
             }
         } else if (stop) {
