@@ -164,15 +164,28 @@ __device__ __forceinline__ void mla_slice(const MlaArgs& a, int t, int hbase, co
     const int tid = tid_x(), lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hh = lane >> 5, c32 = lane & 31;
-    const int head = hbase + wave * 32 + c32;
     const uint8_t* kvb = (const uint8_t*)a.kv;
     const float zscale = fabsf(a.scale) * LOG2E;
     const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
 
-    // the slice's rows first (every selection index load, then every
-    // page-table load, so each waits one round trip); the queries are loaded
-    // after the ring's first transfers are issued, so that waiting for them
-    // never delays the row chain
+    // The queries first: each wave's 32 heads (one contiguous 36 KB block)
+    // into ring buffer `wave` by 1 KB transfers, the 16-byte unit u of head h
+    // at 1152 h + 16 (u ^ (h & 7)); each transfer reads 1 KB of the block
+    // (units permuted within 128-byte groups), and the fragment reads below
+    // (8 lanes, 8 heads, one unit) hit distinct banks.  Their latency
+    // overlaps the row chain, whose waits cover them (in-order counter).
+    {
+        const uint8_t* qblk = (const uint8_t*)a.q + ((size_t)t * a.n_heads + hbase + 32 * wave) * M_ROW_BYTES;
+        const uint32_t qdst = lds_addr(&L.ks[wave][0]);
+#pragma unroll
+        for (int i = 0; i < M_TILE_BYTES / 1024; ++i) {
+            const int o = 1024 * i + 16 * lane;
+            const int h = o / M_ROW_BYTES, up = (o % M_ROW_BYTES) / 16;
+            dma16(qblk + (size_t)h * M_ROW_BYTES + 16 * (up ^ (h & 7)), qdst + 1024u * i);
+        }
+    }
+    // the slice's rows (every selection index load, then every page-table
+    // load, so each waits one round trip)
     {
         constexpr int PER = M3_MAX_SLICE / M_THREADS;
         const int bs = G.block_size;
@@ -201,7 +214,15 @@ __device__ __forceinline__ void mla_slice(const MlaArgs& a, int t, int hbase, co
             if (lane == 32 && j < ntiles * M_TILE) L.tvalid[j / M_TILE] = (uint32_t)(m >> 32);
         }
     }
-    __syncthreads();
+    u32x4 qf[M_DQK / 16];   // B operand of S^T = K Q^T, one 16-byte fragment per 16-wide k step
+    {
+        wait_vmcnt<0>();   // this wave's query transfers (the row chain has waited for them already)
+        const uint8_t* qb = &L.ks[wave][0] + c32 * M_ROW_BYTES;
+#pragma unroll
+        for (int ks = 0; ks < M_DQK / 16; ++ks)
+            qf[ks] = *(const u32x4*)(qb + 16 * ((2 * ks + hh) ^ (c32 & 7))) ^ qsign;
+    }
+    __syncthreads();   // rows and tile masks written; every wave's queries read (the ring is free)
 
     // per-wave transfers of one tile (bf16: 9 x 1 KB into ring buffer b;
     // e4m3: the wave's 5 or 4 staging transfers into staging slot b, and for
@@ -279,7 +300,6 @@ __device__ __forceinline__ void mla_slice(const MlaArgs& a, int t, int hbase, co
     f32x16* oacc = acc.o;
     float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
     bool overflow = false;
-    u32x4 qf[M_DQK / 16];   // B operand of S^T = K Q^T, one 16-byte fragment per 16-wide k step
 
     // Masks the slots of tile i that hold no token (their logits take no part).
     auto mask_tile = [&](f32x16& st, uint32_t vmask) {
@@ -445,11 +465,6 @@ __device__ __forceinline__ void mla_slice(const MlaArgs& a, int t, int hbase, co
 #pragma unroll
         for (int b = 0; b < 2; ++b)
             if (b < ntiles) issue(b, b);
-        if (pass == 0) {
-            const uint16_t* qp = (const uint16_t*)a.q + ((size_t)t * a.n_heads + head) * M_DQK + 8 * hh;
-#pragma unroll
-            for (int ks = 0; ks < M_DQK / 16; ++ks) qf[ks] = *(const u32x4*)(qp + 16 * ks) ^ qsign;
-        }
         bf16x8 pb_prev[2];
         for (int i = 0; i < ntiles; ++i) {
             // tile i landed (tile i+1's transfers may be outstanding), and
@@ -484,11 +499,6 @@ __device__ __forceinline__ void mla_slice(const MlaArgs& a, int t, int hbase, co
 #pragma unroll
         for (int b = 0; b < NRING - 1; ++b)
             if (b < ntiles) issue(b, b);
-        if (pass == 0) {
-            const uint16_t* qp = (const uint16_t*)a.q + ((size_t)t * a.n_heads + head) * M_DQK + 8 * hh;
-#pragma unroll
-            for (int ks = 0; ks < M_DQK / 16; ++ks) qf[ks] = *(const u32x4*)(qp + 16 * ks) ^ qsign;
-        }
         for (int i = 0; i < ntiles; ++i) {
             // this wave's transfers of tile i are done once at most the ones
             // of the (up to NRING - 2) later tiles already issued are outstanding
