@@ -168,6 +168,28 @@ int dsa_sparse_mla_decode(const dsa_batch *batch, const dsa_latent_cache *cache,
                           void *workspace, size_t workspace_bytes, dsa_stream_t stream);
 
 /*
+ * dsa_sparse_mla_decode over several layers that share one selection (the
+ * IndexShare pattern: "IndexShare", the full layer's top-K serves the
+ * layers after it), in one call: layer l attends with its own cache
+ * caches[l], queries q[l] and outputs out[l] (and lse[l]) over the same
+ * `indices`.  The 128-head path runs every layer in one launch (and merges
+ * every layer's splits in one more), so the layers' workgroups overlap;
+ * other shapes run the layers one after another.  Same results as
+ * n_layers calls of dsa_sparse_mla_decode, bit for bit.
+ *   caches, q, out: host arrays of n_layers entries (1 <= n_layers <= 4);
+ *           every cache has the same dtype, d_latent and d_rope.
+ *   lse:    host array of n_layers entries (each may be NULL), or NULL.
+ *   workspace: n_layers * dsa_workspace_size(DSA_OP_MLA_DECODE, batch, k,
+ *           n_heads) bytes.
+ * Errors as dsa_sparse_mla_decode; DSA_ERR_INVALID_ARG for n_layers out of
+ * range or NULL arrays, DSA_ERR_UNSUPPORTED for caches of different shapes.
+ */
+int dsa_sparse_mla_decode_layers(const dsa_batch *batch, const dsa_latent_cache *caches, int32_t n_layers,
+                                 const void *const *q, int32_t n_heads, const int32_t *indices, int32_t k,
+                                 float softmax_scale, void *const *out, float *const *lse,
+                                 void *workspace, size_t workspace_bytes, dsa_stream_t stream);
+
+/*
  * Sparse MQA-mode MLA for prefill-sized batches (many query rows per request,
  * e.g. a 4096-token chunk).  Same arguments and results as the decode entry;
  * each workgroup covers whole selections, so no partial results are merged.

@@ -23,7 +23,8 @@ EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_spars
            "dsa_decode_step", "dsa_workspace_size", "dsa_status_string", "dsa_check_device",
            "dsa_read_probe_sink_size", "dsa_read_probe", "dsa_hot_cache_reset", "dsa_hot_cache_workspace_size",
            "dsa_hot_cache_fetch", "dsa_decode_step_timed", "dsa_decode_step_noalloc",
-           "dsa_decode_step_fused", "dsa_check_batch", "dsa_hot_cache_plan", "dsa_hot_cache_copy")
+           "dsa_decode_step_fused", "dsa_check_batch", "dsa_hot_cache_plan", "dsa_hot_cache_copy",
+           "dsa_sparse_mla_decode_layers")
 CHECK_QUERY_START, CHECK_CONTEXT, CHECK_PAGE, CHECK_INDEX = 1, 2, 4, 8   # dsa_check_batch's bits
 ERR_BAD_DEVICE_ARG = -7
 STEP_EVENTS = 5   # events of dsa_decode_step_timed: start, after sampling, indexer, selection, attention
@@ -67,6 +68,8 @@ def lib():
         L.dsa_topk.argtypes = [P(DsaBatch), vp, i64, i32, vp, vp, sz, vp]
         mla = [P(DsaBatch), P(DsaLatentCache), vp, i32, vp, i32, f32, vp, vp, vp, sz, vp]
         L.dsa_sparse_mla_decode.argtypes = mla
+        L.dsa_sparse_mla_decode_layers.argtypes = [P(DsaBatch), P(DsaLatentCache), i32, P(vp), i32, vp, i32, f32,
+                                                   P(vp), P(vp), vp, sz, vp]
         L.dsa_sparse_mla_prefill.argtypes = mla
         L.dsa_decode_step.argtypes = [P(DsaBatch), P(DsaIndexCache), vp, vp, i32, P(DsaLatentCache), vp, i32,
                                       i32, f32, vp, vp, vp, vp, sz, vp]
@@ -91,7 +94,7 @@ def lib():
         L.dsa_decode_step_fused.argtypes = [P(DsaBatch), P(DsaIndexCache), vp, vp, i32, P(DsaLatentCache), vp, i32,
                                             i32, f32, vp, vp, vp, vp, sz, vp, P(vp), i32]
         L.dsa_check_batch.argtypes = [P(DsaBatch), i32, vp, i32, P(C.c_uint32), vp]
-        for name in ("dsa_check_batch", "dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
+        for name in ("dsa_sparse_mla_decode_layers", "dsa_check_batch", "dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
                      "dsa_decode_step", "dsa_check_device", "dsa_read_probe", "dsa_hot_cache_reset",
                      "dsa_hot_cache_fetch", "dsa_hot_cache_plan", "dsa_hot_cache_copy", "dsa_decode_step_timed", "dsa_decode_step_noalloc",
                      "dsa_decode_step_fused"):
@@ -243,6 +246,29 @@ def sparse_mla_decode(batch: Batch, kv, kv_scales, d_latent, q, indices, scale, 
                       workspace=None, stream=None):
     return _mla("dsa_sparse_mla_decode", OP_MLA_DECODE, batch, kv, kv_scales, d_latent, q, indices,
                 scale, out, lse, workspace, stream)
+
+
+def sparse_mla_decode_layers(batch: Batch, kvs, kv_scales, d_latent, qs, indices, scale, outs=None, lses=None,
+                             workspace=None, stream=None):
+    """dsa_sparse_mla_decode_layers: layer l attends over kvs[l] (scales
+    kv_scales[l]) with queries qs[l] and the shared `indices`; returns the
+    list of outputs."""
+    L = len(kvs)
+    k = indices.shape[1]
+    if outs is None:
+        outs = [_out_like(kv, q, d_latent) for kv, q in zip(kvs, qs)]
+    need = L * workspace_size(OP_MLA_DECODE, batch, k, qs[0].shape[1])
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=qs[0].device)
+    b = batch.struct()
+    caches = (DsaLatentCache * L)(*[latent_cache(kv, sc, d_latent) for kv, sc in zip(kvs, kv_scales)])
+    qp = (C.c_void_p * L)(*[_ptr(q) for q in qs])
+    op = (C.c_void_p * L)(*[_ptr(o) for o in outs])
+    lp = None if lses is None else (C.c_void_p * L)(*[_ptr(x) for x in lses])
+    _check("dsa_sparse_mla_decode_layers", lib().dsa_sparse_mla_decode_layers(
+        C.byref(b), caches, L, qp, qs[0].shape[1], _ptr(indices), k, float(scale), op, lp, _ptr(workspace),
+        workspace.numel(), _stream(stream)))
+    return outs
 
 
 def sparse_mla_prefill(batch: Batch, kv, kv_scales, d_latent, q, indices, scale, out=None, lse=None,

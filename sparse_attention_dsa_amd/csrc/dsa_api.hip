@@ -277,6 +277,8 @@ MlaArgs mla_args(const dsa_batch* b, const dsa_latent_cache* c, const void* q, i
     a.indices = indices; a.k = k; a.scale = scale;
     a.out = out; a.lse = lse;
     a.part_o = nullptr; a.part_lse = nullptr; a.arrive = nullptr; a.splits = 1;
+    a.n_layers = 1;
+    for (int l = 0; l < MLA_MAX_LAYERS; ++l) a.lay[l] = MlaLayer{c->kv, c->scales, q, out, lse};
     return a;
 }
 
@@ -402,6 +404,54 @@ int dsa_sparse_mla_decode(const dsa_batch* b, const dsa_latent_cache* c, const v
                           const int32_t* indices, int32_t k, float scale, void* out, float* lse, void* ws,
                           size_t ws_bytes, dsa_stream_t stream) {
     return mla_entry(b, c, q, n_heads, indices, k, scale, out, lse, ws, ws_bytes, stream, false);
+}
+
+int dsa_sparse_mla_decode_layers(const dsa_batch* b, const dsa_latent_cache* caches, int32_t n_layers,
+                                 const void* const* q, int32_t n_heads, const int32_t* indices, int32_t k,
+                                 float scale, void* const* out, float* const* lse, void* ws, size_t ws_bytes,
+                                 dsa_stream_t stream) {
+    if (!caches || !q || !out || !indices || n_layers < 1 || n_layers > MLA_MAX_LAYERS) return DSA_ERR_INVALID_ARG;
+    int st;
+    for (int l = 0; l < n_layers; ++l) {
+        if ((st = validate_mla(b, &caches[l], q[l], n_heads, k, out[l])) != DSA_OK) return st;
+        if (caches[l].dtype != caches[0].dtype || caches[l].d_latent != caches[0].d_latent ||
+            caches[l].d_rope != caches[0].d_rope)
+            return DSA_ERR_UNSUPPORTED;
+    }
+    const dsa_latent_cache* c0 = &caches[0];
+    const int path = scale == 0.f ? MLA_PATH_GENERIC : mla_path(c0->dtype, c0->d_latent, c0->d_rope, n_heads);
+    // each layer's share: the single-layer decode workspace for this batch
+    const size_t per = mla_layout(0, b, k, n_heads, false, mla_path(c0->dtype, c0->d_latent, c0->d_rope, n_heads)).end;
+    if (per > 0 && (!ws || ws_bytes < per * n_layers)) return DSA_ERR_WORKSPACE;
+    if ((st = check_device_cached()) != DSA_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    const bool dbg = debug_mode();
+    if (dbg) {
+        int nb = 0;
+        for (int l = 0; l < n_layers; ++l) nb = pool_blocks(nb, caches[l].num_blocks);
+        if ((st = run_batch_check(geometry(b), nb, true, indices, k, nullptr, s)) != DSA_OK) return st;
+    }
+    if (path == MLA_PATH_H128) {
+        // one launch over every layer (and one merge), the layers' partials
+        // side by side: all layers' fp16 partials, then all layers' lse pairs
+        MlaArgs a = mla_args(b, c0, q[0], n_heads, indices, k, scale, out[0], lse ? lse[0] : nullptr);
+        a.splits = mla_splits(path, b->total_q, n_heads, k, false);
+        if (a.splits > 1) {
+            const size_t th = (size_t)b->total_q * n_heads * a.splits;
+            a.part_o = (uint16_t*)ws;
+            a.part_lse = (float*)((char*)ws + align_up(sizeof(uint16_t) * th * 512 * n_layers));
+        }
+        a.n_layers = n_layers;
+        for (int l = 0; l < n_layers; ++l)
+            a.lay[l] = MlaLayer{caches[l].kv, caches[l].scales, q[l], out[l], lse ? lse[l] : nullptr};
+        st = launch_status(launch_mla(a, false, s));
+    } else {
+        st = DSA_OK;
+        for (int l = 0; l < n_layers && st == DSA_OK; ++l)
+            st = run_mla(b, &caches[l], q[l], n_heads, indices, k, scale, out[l], lse ? lse[l] : nullptr,
+                         (char*)ws, ws ? ws_bytes : 0, per * l, false, s);
+    }
+    return debug_finish(dbg, st, s);
 }
 
 int dsa_sparse_mla_prefill(const dsa_batch* b, const dsa_latent_cache* c, const void* q, int32_t n_heads,

@@ -237,6 +237,14 @@ struct TopkArgs {
     int nchunks;
 };
 
+// Per-layer buffers of a launch over several layers that share one selection
+// (layer l > 0 of the 128-head path; layer 0 is MlaArgs' own).
+constexpr int MLA_MAX_LAYERS = 4;
+struct MlaLayer {
+    const void* kv; const float* kv_scales;
+    const void* q;
+    void* out; float* lse;
+};
 struct MlaArgs {
     Geometry g;
     const void* kv; const float* kv_scales; int kv_dtype; int d_latent, d_rope;
@@ -244,11 +252,25 @@ struct MlaArgs {
     const int32_t* indices; int k;
     float scale;
     void* out; float* lse;
-    uint16_t* part_o;                 // split partials: fp16 [T][H][S][d], or nullptr
-    float* part_lse;                  // [T][H][S][2]: lse and the partial's scale 2^-k
+    uint16_t* part_o;                 // split partials: fp16 [layers][T][H][S][d], or nullptr
+    float* part_lse;                  // [layers][T][H][S][2]: lse and the partial's scale 2^-k
     uint32_t* arrive;                 // [T * H / 128]: slices finished (128-head path)
     int splits;
+    int n_layers;                     // >= 1; layers 1 .. n_layers - 1 in lay[]
+    MlaLayer lay[MLA_MAX_LAYERS];
 };
+// The arguments of layer `layer` of a multi-layer launch (the same for 0).
+__host__ __device__ inline MlaArgs mla_layer_args(const MlaArgs& a, int layer) {
+    MlaArgs b = a;
+    if (layer > 0) {
+        const MlaLayer& y = a.lay[layer];
+        b.kv = y.kv; b.kv_scales = y.kv_scales; b.q = y.q; b.out = y.out; b.lse = y.lse;
+        const size_t th = (size_t)a.g.T * a.n_heads * a.splits;
+        if (b.part_o) b.part_o += (size_t)layer * th * 512;
+        if (b.part_lse) b.part_lse += (size_t)layer * th * 2;
+    }
+    return b;
+}
 
 // The fused decode step's arguments (one persistent launch; see fused.hip).
 // Counters in ctr[]: head and tail of the selection queue and of the

@@ -341,16 +341,18 @@ __device__ __forceinline__ void copy_row(const uint8_t* __restrict__ src, uint8_
     if (o1 < bytes) *(u32x4*)(dst + o1) = v1;
 }
 
-__device__ __forceinline__ void hc_assign_one(const HotArgs& a, uint32_t i, int step, int lane) {
+// Returns (in lane 0) whether the victim held a token.
+__device__ __forceinline__ uint32_t hc_assign_one(const HotArgs& a, uint32_t i, int step, int lane) {
     const int64_t rs = a.miss[i];
     const int r = (int)(rs >> 32), s = (int)(rs & 0xFFFFFFFF);
     const int v = a.victims[i];
+    uint32_t evicted = 0u;
     if (lane == 0) {
         const int64_t old = a.owner[v];
         if (old >= 0) {
             const int orq = (int)(old >> 32), osl = (int)(old & 0xFFFFFFFF);
             if (orq < a.g.B && osl < a.maxctx) a.slot_of[(size_t)orq * a.maxctx + osl] = -1;
-            atomicAdd(&a.scal[HS_EVICT], 1u);
+            evicted = 1u;
         }
         a.owner[v] = rs;
         a.last_use[v] = step;
@@ -360,6 +362,7 @@ __device__ __forceinline__ void hc_assign_one(const HotArgs& a, uint32_t i, int 
     const int64_t row = (int64_t)a.host_pt[(size_t)r * a.g.max_blocks + s / bs] * bs + s % bs;
     copy_row(a.host_kv + row * a.row_bytes, a.hot_kv + (int64_t)v * a.row_bytes, a.row_bytes, lane);
     if (a.hot_scales && lane == 0) a.hot_scales[v] = a.host_scales[row];
+    return evicted;
 }
 
 // Per miss, one wave: evict the victim's token, claim the slot, copy the row
@@ -376,8 +379,10 @@ __global__ __launch_bounds__(HC_THREADS) void hc_assign(HotArgs a) {
         if (a.counts) a.counts[0] = (int32_t)M;
     }
     const uint32_t n = min(M, nv), nw = gridDim.x * HC_WAVES;
+    uint32_t evicted = 0u;   // counted per wave, added once: thousands of misses, one counter
     for (uint32_t i = blockIdx.x * HC_WAVES + (threadIdx.x >> 6); i < n; i += nw)
-        hc_assign_one(a, i, step, lane);
+        evicted += hc_assign_one(a, i, step, lane);
+    if (lane == 0 && evicted) atomicAdd(&a.scal[HS_EVICT], evicted);
 }
 
 __global__ void hc_finish(HotArgs a) {

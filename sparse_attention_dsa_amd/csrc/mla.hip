@@ -327,7 +327,8 @@ void mla_bf16_mfma(MlaArgs a, int slice) {
 }
 
 // Merge split partials: out = sum_s e^{lse_s - L} o_s with L = log-sum-exp.
-__global__ __launch_bounds__(256) void mla_combine(MlaArgs a) {
+__global__ __launch_bounds__(256) void mla_combine(MlaArgs a0) {
+    const MlaArgs a = mla_layer_args(a0, blockIdx.y);
     const int lane = threadIdx.x & 63;
     const size_t th = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (t, h), one wave each
     if (th >= (size_t)a.g.T * a.n_heads) return;
@@ -459,7 +460,8 @@ __global__ __launch_bounds__(256) void mla_generic(MlaArgs a) {
 // its log-sum-exp at its slice index, and mla_combine merges them.
 template <bool FP8>
 __global__ __attribute__((amdgpu_flat_work_group_size(M_THREADS, M_THREADS), amdgpu_waves_per_eu(1, 1)))
-void mla_h128(MlaArgs a, int slice) {
+void mla_h128(MlaArgs a0, int slice) {
+    const MlaArgs a = mla_layer_args(a0, blockIdx.z);
     const Geometry& G = a.g;
     const int hgroups = a.n_heads / M3_HEADS;
     const int unit = blockIdx.x;
@@ -514,16 +516,17 @@ hipError_t launch_mla(const MlaArgs& a, bool prefill, hipStream_t s) {
         int slice = (a.k + S - 1) / S;
         slice = (slice + M_TILE - 1) / M_TILE * M_TILE;
         if (slice > M3_MAX_SLICE) return hipErrorInvalidValue;
-        const dim3 grid(a.g.T * (a.n_heads / M3_HEADS), S);
+        const dim3 grid(a.g.T * (a.n_heads / M3_HEADS), S, a.n_layers);
         if (a.kv_dtype == 2) hipLaunchKernelGGL(mla_h128<true>, grid, dim3(M_THREADS), 0, s, a, slice);
         else hipLaunchKernelGGL(mla_h128<false>, grid, dim3(M_THREADS), 0, s, a, slice);
         hipError_t e = hipGetLastError();
         if (e == hipSuccess && S > 1) {
-            hipLaunchKernelGGL(mla_combine, dim3((a.g.T * a.n_heads + 3) / 4), dim3(256), 0, s, a);
+            hipLaunchKernelGGL(mla_combine, dim3((a.g.T * a.n_heads + 3) / 4, a.n_layers), dim3(256), 0, s, a);
             e = hipGetLastError();
         }
         return e;
     }
+    if (a.n_layers != 1) return hipErrorInvalidValue;   // several layers: the 128-head path only
     if (path == MLA_PATH_H64) {
         const int hgroups = a.n_heads / MLA_HEADS_PER_WG;
         const bool split = a.splits > 1;

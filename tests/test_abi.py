@@ -190,3 +190,19 @@ def test_hot_cache_plan_and_copy_host_checks(L):
     assert L.dsa_hot_cache_plan(C.byref(b), C.byref(bf), None, 16, C.byref(hot), 0x1, 1 << 30, None) == -1
     assert L.dsa_hot_cache_copy(C.byref(b), C.byref(bf), 0x1, 33, C.byref(hot), None, 0x1, 1 << 30, None) == -1
     assert L.dsa_hot_cache_plan(C.byref(b), C.byref(bf), 0x1, 16, C.byref(hot), 0x1, 8, None) == -3
+
+
+def test_mla_decode_layers_host_checks(L):
+    b = _batch()
+    caches = (B.DsaLatentCache * 2)(B.DsaLatentCache(0x10, None, B.BF16, 512, 64),
+                                   B.DsaLatentCache(0x20, None, B.BF16, 512, 64))
+    ptrs = (C.c_void_p * 2)(0x100, 0x200)
+    args = lambda n, c=caches, q=ptrs, o=ptrs: (C.byref(b), c, n, q, 128, 0x1, 2048, 0.1, o, None, 0x1, 1 << 30, None)
+    assert L.dsa_sparse_mla_decode_layers(*args(0)) == -1
+    assert L.dsa_sparse_mla_decode_layers(*args(5)) == -1
+    assert L.dsa_sparse_mla_decode_layers(*args(2, q=None)) == -1
+    mixed = (B.DsaLatentCache * 2)(B.DsaLatentCache(0x10, None, B.BF16, 512, 64),
+                                  B.DsaLatentCache(0x20, None, B.F32, 512, 64))
+    assert L.dsa_sparse_mla_decode_layers(*args(2, c=mixed)) == -2
+    small = (C.byref(b), caches, 2, ptrs, 128, 0x1, 2048, 0.1, ptrs, None, 0x1, 16, None)
+    assert L.dsa_sparse_mla_decode_layers(*small) == -3

@@ -301,6 +301,44 @@ def test_indexshare_decode_group(case):
         np.testing.assert_allclose(lse2[t], rl2, rtol=0, atol=1e-3)
 
 
+@pytest.mark.parametrize("case", ["bf16", "mtp_fp8", "h64"])
+def test_mla_decode_layers_matches_per_layer_calls(case):
+    """Three layers sharing one selection in one dsa_sparse_mla_decode_layers
+    call (one launch on the 128-head path, one call per layer on the 64-head
+    one): every layer's output and lse equal its own dsa_sparse_mla_decode
+    bit for bit, and the second layer's output matches the oracle."""
+    if case == "bf16":
+        wl = workloads.make_workload("single_b1_l32768", batch=3, context_lens=[3000, 9000, 2100], seed=51,
+                                     layers=2)
+    elif case == "mtp_fp8":
+        wl = workloads.make_workload("mtp_b8_l202752", batch=2, context_lens=[5000, 2100], seed=52, layers=2)
+    else:
+        wl = workloads.make_workload("single_b1_l32768", batch=2, context_lens=[4000, 2500], mla_heads=64, seed=53,
+                                     layers=2)
+    log("mla layers", case, wl.context_lens.tolist(), "heads", wl.mla_heads)
+    batch, d = upload(wl)
+    T, H = wl.total_q, wl.mla_heads
+    idx = torch.empty((T, wl.topk), dtype=torch.int32, device="cuda")
+    dsa.decode_step(batch, d["idx_keys"], d["idx_scales"], d["q_idx"], d["w"], d["kv"], d["kv_scales"], wl.d_latent,
+                    d["q_mla"], wl.topk, wl.softmax_scale, indices_out=idx)
+    roll = lambda x, dim: None if x is None else x.roll(1, dims=dim).contiguous()
+    kvs = [d["kv"], d["kv2"], roll(d["kv"], 0)]
+    scs = [d["kv_scales"], d["kv2_scales"], roll(d["kv_scales"], 0)]
+    qs = [d["q_mla"], d["q_mla2"], roll(d["q_mla"], 1)]
+    lses = [torch.empty((T, H), dtype=torch.float32, device="cuda") for _ in kvs]
+    outs = dsa.sparse_mla_decode_layers(batch, kvs, scs, wl.d_latent, qs, idx, wl.softmax_scale, lses=lses)
+    for l in range(len(kvs)):
+        lse1 = torch.empty((T, H), dtype=torch.float32, device="cuda")
+        one = dsa.sparse_mla_decode(batch, kvs[l], scs[l], wl.d_latent, qs[l], idx, wl.softmax_scale, lse=lse1)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[l], one), (case, l)
+        assert torch.equal(lses[l], lse1), (case, l)
+    out2, ix = outs[1].float().cpu().numpy(), idx.cpu().numpy()
+    for t in range(T):
+        ref, _ = oracle.query_mla(wl, t, ix[t][ix[t] >= 0], 2)
+        check_out(out2[t], ref, fp32=False)
+
+
 def _sample_positions(n, m=1024):
     """Token positions of the sample the decode step's top-K bound is drawn
     from (m per 128K tokens of the row): m / 16 runs of 16 consecutive tokens,
