@@ -59,16 +59,15 @@ TopkLayout topk_layout(size_t base, const dsa_batch* b) {
 }
 
 // Split partials: fp16 [T][H][S][512], then (lse, scale) [T][H][S][2].
-struct MlaLayout { size_t part_o, part_lse, arrive, end; int splits; };
+struct MlaLayout { size_t part_o, part_lse, end; int splits; };
 MlaLayout mla_layout(size_t base, const dsa_batch* b, int k, int n_heads, bool prefill, int path) {
     MlaLayout l;
     l.splits = mla_splits(path, b->total_q, n_heads, k, prefill);
-    l.part_o = l.part_lse = l.arrive = l.end = base;
+    l.part_o = l.part_lse = l.end = base;
     if (l.splits > 1) {
         const size_t th = (size_t)b->total_q * n_heads * l.splits;
         l.part_lse = align_up(base + sizeof(uint16_t) * th * 512);
-        l.arrive = align_up(l.part_lse + 2 * sizeof(float) * th);
-        l.end = l.arrive;
+        l.end = align_up(l.part_lse + 2 * sizeof(float) * th);
     }
     return l;
 }
@@ -276,7 +275,7 @@ MlaArgs mla_args(const dsa_batch* b, const dsa_latent_cache* c, const void* q, i
     a.q = q; a.n_heads = n_heads;
     a.indices = indices; a.k = k; a.scale = scale;
     a.out = out; a.lse = lse;
-    a.part_o = nullptr; a.part_lse = nullptr; a.arrive = nullptr; a.splits = 1;
+    a.part_o = nullptr; a.part_lse = nullptr; a.splits = 1;
     a.n_layers = 1;
     for (int l = 0; l < MLA_MAX_LAYERS; ++l) a.lay[l] = MlaLayer{c->kv, c->scales, q, out, lse};
     return a;

@@ -254,7 +254,6 @@ struct MlaArgs {
     void* out; float* lse;
     uint16_t* part_o;                 // split partials: fp16 [layers][T][H][S][d], or nullptr
     float* part_lse;                  // [layers][T][H][S][2]: lse and the partial's scale 2^-k
-    uint32_t* arrive;                 // [T * H / 128]: slices finished (128-head path)
     int splits;
     int n_layers;                     // >= 1; layers 1 .. n_layers - 1 in lay[]
     MlaLayer lay[MLA_MAX_LAYERS];

@@ -688,40 +688,14 @@ __global__ __launch_bounds__(256) void mla_combine_slots(FusedArgs f) {
     const int S = (int)f.row_splits[t];
     if (S <= 1) return;
     const size_t p0 = (size_t)f.row_slot[t] * a.n_heads + h;   // partial of slice s: p0 + s H
-    float mx = -INFINITY;
-    for (int s = 0; s < S; ++s) mx = fmaxf(mx, a.part_lse[2 * (p0 + (size_t)s * a.n_heads)]);
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float den = 0.f;
-    if (mx != -INFINITY) {
-        for (int s0 = 0; s0 < S; s0 += 4) {
-            u32x4 hv[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (s0 + u < S) hv[u] = *(const u32x4*)(a.part_o + (p0 + (size_t)(s0 + u) * a.n_heads) * M_DL + 8 * lane);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (s0 + u >= S) break;
-                const size_t p = p0 + (size_t)(s0 + u) * a.n_heads;
-                const float wgt = __expf(a.part_lse[2 * p] - mx);
-                den += wgt;
-                const float ws = wgt * a.part_lse[2 * p + 1];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const uint16_t b = (uint16_t)(hv[u][i >> 1] >> (16 * (i & 1)));
-                    acc[i] += ws * (float)__builtin_bit_cast(_Float16, b);
-                }
-            }
-        }
-        const float inv = 1.f / den;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] *= inv;
-    }
+    float acc[8];
+    const float lse = merge_partials_any(a.part_o, a.part_lse, p0, (size_t)a.n_heads, S, lane, acc);
     uint16_t* op = (uint16_t*)a.out + th * M_DL + 8 * lane;
     u32x4 w;
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
     *(u32x4*)op = w;
-    if (a.lse && lane == 0) a.lse[th] = mx == -INFINITY ? -INFINITY : mx + logf(den);
+    if (a.lse && lane == 0) a.lse[th] = lse;
 }
 
 bool fused_ok(const IndexerArgs& ia, const MlaArgs& ma) {

@@ -326,48 +326,22 @@ void mla_bf16_mfma(MlaArgs a, int slice) {
     }
 }
 
-// Merge split partials: out = sum_s e^{lse_s - L} o_s with L = log-sum-exp.
+// Merge split partials: out = sum_s e^{lse_s - L} o_s with L = log-sum-exp;
+// one wave per (query row, head), the row's slices adjacent.
 __global__ __launch_bounds__(256) void mla_combine(MlaArgs a0) {
     const MlaArgs a = mla_layer_args(a0, blockIdx.y);
     const int lane = threadIdx.x & 63;
     const size_t th = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (t, h), one wave each
     if (th >= (size_t)a.g.T * a.n_heads) return;
     const int S = a.splits;
-    const float* pl = a.part_lse + 2 * th * S;   // per slice: lse, 2^-k
-    const uint16_t* po = a.part_o + th * S * M_DL + 8 * lane;
-    float mx = -INFINITY;
-    for (int s = 0; s < S; ++s) mx = fmaxf(mx, pl[2 * s]);
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float den = 0.f;
-    if (mx != -INFINITY) {
-        for (int s0 = 0; s0 < S; s0 += 4) {
-            u32x4 h[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (s0 + u < S) h[u] = *(const u32x4*)(po + (size_t)(s0 + u) * M_DL);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (s0 + u >= S) break;
-                const float wgt = __expf(pl[2 * (s0 + u)] - mx);
-                den += wgt;
-                const float ws = wgt * pl[2 * (s0 + u) + 1];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const uint16_t b = (uint16_t)(h[u][i >> 1] >> (16 * (i & 1)));
-                    acc[i] += ws * (float)__builtin_bit_cast(_Float16, b);
-                }
-            }
-        }
-        const float inv = 1.f / den;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] *= inv;
-    }
+    float acc[8];
+    const float lse = merge_partials_any(a.part_o, a.part_lse, th * S, 1, S, lane, acc);
     uint16_t* op = (uint16_t*)a.out + th * M_DL + 8 * lane;
     u32x4 w;
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = f32_to_bf16(acc[2 * i]) | (f32_to_bf16(acc[2 * i + 1]) << 16);
     *(u32x4*)op = w;
-    if (a.lse && lane == 0) a.lse[th] = mx == -INFINITY ? -INFINITY : mx + logf(den);
+    if (a.lse && lane == 0) a.lse[th] = lse;
 }
 
 // Generic path: any dims and head counts, fp32 / bf16 / e4m3 latent.  One

@@ -58,6 +58,7 @@ constexpr int M3_VPF = 2;     // V^T fragments in flight
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_vptr;
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 
@@ -663,53 +664,64 @@ __device__ __forceinline__ void mla_store_partial(const MlaArgs& a, int t, int h
     mla_store_partial_at(a, ((size_t)t * a.n_heads + hbase) * S + sp, (size_t)S, acc, L);
 }
 
-// The last slice of a row to finish: merges the S slices' partials (indices
-// pbase + s, in slice order, so the result does not depend on which slice
-// finished last) by their log-sum-exp and writes the bf16 output and lse.
-__device__ __forceinline__ void mla_merge_final(const MlaArgs& a, int t, int head, size_t pbase, int S) {
-    const int hh = (tid_x() & 63) >> 5;
+// Merge of one (query row, head)'s split partials by their log-sum-exp, by
+// one wave: slice s is partial p0 + s ps (part_o row and part_lse pair), and
+// lane l accumulates output columns 8l .. 8l + 7 into acc (normalised).
+// Returns the natural-log lse (-inf when every slice is empty).  Up to NS
+// slices go through registers, with every load issued before any arithmetic
+// (one memory round trip); more slices are merged NS at a time.  The sums run
+// in slice order, so the result does not depend on NS.
+template <int NS>
+__device__ __forceinline__ float merge_partials(const uint16_t* part_o, const float* part_lse, size_t p0, size_t ps,
+                                                int S, int lane, float acc[8]) {
     float mx = -INFINITY;
-    for (int s = 0; s < S; ++s) mx = fmaxf(mx, a.part_lse[2 * (pbase + s)]);
-    f32x16 o[M_DL / 32];
-#pragma unroll
-    for (int cb = 0; cb < M_DL / 32; ++cb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[cb][e] = 0.f;
+    if (S > NS)
+        for (int s = 0; s < S; ++s) mx = fmaxf(mx, part_lse[2 * (p0 + (size_t)s * ps)]);
     float den = 0.f;
-    if (mx != -INFINITY) {
-        for (int s = 0; s < S; ++s) {
-            const size_t pidx = pbase + s;
-            const float ls = a.part_lse[2 * pidx];
-            if (ls == -INFINITY) continue;
-            const float wgt = __expf(ls - mx);
-            den += wgt;
-            const float ws = wgt * a.part_lse[2 * pidx + 1];
-            const uint16_t* po = a.part_o + pidx * M_DL;
 #pragma unroll
-            for (int cb = 0; cb < M_DL / 32; ++cb)
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int s0 = 0; s0 < S; s0 += NS) {
+        f32x2 pl[NS];
+        u32x4 h[NS];
 #pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) {
-                    const u32x2 w = *(const u32x2*)(po + 32 * cb + 8 * e4 + 4 * hh);
+        for (int u = 0; u < NS; ++u)
+            if (s0 + u < S) pl[u] = *(const f32x2*)(part_lse + 2 * (p0 + (size_t)(s0 + u) * ps));
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const uint16_t b = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
-                        o[cb][4 * e4 + q] += ws * (float)__builtin_bit_cast(_Float16, b);
-                    }
+        for (int u = 0; u < NS; ++u)
+            if (s0 + u < S) h[u] = *(const u32x4*)(part_o + (p0 + (size_t)(s0 + u) * ps) * M_DL + 8 * lane);
+        if (S <= NS)
+#pragma unroll
+            for (int u = 0; u < NS; ++u)
+                if (u < S) mx = fmaxf(mx, pl[u][0]);
+        if (mx == -INFINITY) break;
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+            if (s0 + u < S) {
+                const float wgt = __expf(pl[u][0] - mx);
+                den += wgt;
+                const float ws = wgt * pl[u][1];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint16_t b = (uint16_t)(h[u][i >> 1] >> (16 * (i & 1)));
+                    acc[i] += ws * (float)__builtin_bit_cast(_Float16, b);
                 }
+            }
         }
     }
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    uint16_t* op = (uint16_t*)a.out + ((size_t)t * a.n_heads + head) * M_DL;
+    if (mx == -INFINITY) return -INFINITY;
+    const float inv = 1.f / den;
 #pragma unroll
-    for (int cb = 0; cb < M_DL / 32; ++cb)
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-            u32x2 w;
-            w[0] = f32_to_bf16(o[cb][4 * e4] * inv) | (f32_to_bf16(o[cb][4 * e4 + 1] * inv) << 16);
-            w[1] = f32_to_bf16(o[cb][4 * e4 + 2] * inv) | (f32_to_bf16(o[cb][4 * e4 + 3] * inv) << 16);
-            *(u32x2*)(op + 32 * cb + 8 * e4 + 4 * hh) = w;
-        }
-    if (a.lse && hh == 0) a.lse[(size_t)t * a.n_heads + head] = mx == -INFINITY ? -INFINITY : mx + logf(den);
+    for (int i = 0; i < 8; ++i) acc[i] *= inv;
+    return mx + logf(den);
+}
+
+// merge_partials with the register depth picked from S (the splits of a
+// decode row are a power of two, at most 16 for K = 2048).
+__device__ __forceinline__ float merge_partials_any(const uint16_t* part_o, const float* part_lse, size_t p0,
+                                                    size_t ps, int S, int lane, float acc[8]) {
+    if (S <= 4) return merge_partials<4>(part_o, part_lse, p0, ps, S, lane, acc);
+    if (S <= 8) return merge_partials<8>(part_o, part_lse, p0, ps, S, lane, acc);
+    return merge_partials<16>(part_o, part_lse, p0, ps, S, lane, acc);
 }
 
 }  // namespace dsa
