@@ -688,14 +688,14 @@ __global__ __launch_bounds__(256) void mla_combine_slots(FusedArgs f) {
     const int S = (int)f.row_splits[t];
     if (S <= 1) return;
     const size_t p0 = (size_t)f.row_slot[t] * a.n_heads + h;   // partial of slice s: p0 + s H
-    float acc[8];
-    const float lse = merge_partials_any(a.part_o, a.part_lse, p0, (size_t)a.n_heads, S, lane, acc);
+    float acc[1][8], lse[1];
+    merge_partials_any<1>(a.part_o, a.part_lse, p0, 0, (size_t)a.n_heads, S, lane, acc, lse);
     uint16_t* op = (uint16_t*)a.out + th * M_DL + 8 * lane;
     u32x4 w;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(acc[0][2 * i], acc[0][2 * i + 1]);
     *(u32x4*)op = w;
-    if (a.lse && lane == 0) a.lse[th] = lse;
+    if (a.lse && lane == 0) a.lse[th] = lse[0];
 }
 
 bool fused_ok(const IndexerArgs& ia, const MlaArgs& ma) {

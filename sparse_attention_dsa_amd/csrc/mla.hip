@@ -326,22 +326,39 @@ void mla_bf16_mfma(MlaArgs a, int slice) {
     }
 }
 
-// Merge split partials: out = sum_s e^{lse_s - L} o_s with L = log-sum-exp;
-// one wave per (query row, head), the row's slices adjacent.
+// Merge split partials: out = sum_s e^{lse_s - L} o_s with L = log-sum-exp.
+// One wave per HP adjacent (query row, head) pairs (T H is even), each
+// pair's slices adjacent, so a wave's loads are HP S contiguous partial rows;
+// NS slices are held in registers.  The launch picks NS from S, and two pairs
+// a wave up to 8 slices, one beyond (the register count, and with it the
+// occupancy, follows the split count).
+template <int NS, int HP>
 __global__ __launch_bounds__(256) void mla_combine(MlaArgs a0) {
     const MlaArgs a = mla_layer_args(a0, blockIdx.y);
     const int lane = threadIdx.x & 63;
-    const size_t th = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (t, h), one wave each
-    if (th >= (size_t)a.g.T * a.n_heads) return;
+    const size_t th0 = ((size_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * HP;   // first (t, h) of the wave
+    if (th0 >= (size_t)a.g.T * a.n_heads) return;
     const int S = a.splits;
-    float acc[8];
-    const float lse = merge_partials_any(a.part_o, a.part_lse, th * S, 1, S, lane, acc);
-    uint16_t* op = (uint16_t*)a.out + th * M_DL + 8 * lane;
-    u32x4 w;
+    float acc[HP][8], lse[HP];
+    merge_partials<NS, HP>(a.part_o, a.part_lse, th0 * S, (size_t)S, 1, S, lane, acc, lse);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = f32_to_bf16(acc[2 * i]) | (f32_to_bf16(acc[2 * i + 1]) << 16);
-    *(u32x4*)op = w;
-    if (a.lse && lane == 0) a.lse[th] = lse;
+    for (int h = 0; h < HP; ++h) {
+        u32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = f32_to_bf16(acc[h][2 * i]) | (f32_to_bf16(acc[h][2 * i + 1]) << 16);
+        *(u32x4*)((uint16_t*)a.out + (th0 + h) * M_DL + 8 * lane) = w;
+        if (a.lse && lane == 0) a.lse[th0 + h] = lse[h];
+    }
+}
+
+static void launch_combine(const MlaArgs& a, hipStream_t s) {
+    const int pairs = a.g.T * a.n_heads;
+    if (a.splits <= 4)
+        hipLaunchKernelGGL((mla_combine<4, 2>), dim3((pairs / 2 + 3) / 4, a.n_layers), dim3(256), 0, s, a);
+    else if (a.splits <= 8)
+        hipLaunchKernelGGL((mla_combine<8, 2>), dim3((pairs / 2 + 3) / 4, a.n_layers), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((mla_combine<16, 1>), dim3((pairs + 3) / 4, a.n_layers), dim3(256), 0, s, a);
 }
 
 // Generic path: any dims and head counts, fp32 / bf16 / e4m3 latent.  One
@@ -495,7 +512,7 @@ hipError_t launch_mla(const MlaArgs& a, bool prefill, hipStream_t s) {
         else hipLaunchKernelGGL(mla_h128<false>, grid, dim3(M_THREADS), 0, s, a, slice);
         hipError_t e = hipGetLastError();
         if (e == hipSuccess && S > 1) {
-            hipLaunchKernelGGL(mla_combine, dim3((a.g.T * a.n_heads + 3) / 4, a.n_layers), dim3(256), 0, s, a);
+            launch_combine(a, s);
             e = hipGetLastError();
         }
         return e;
@@ -514,7 +531,7 @@ hipError_t launch_mla(const MlaArgs& a, bool prefill, hipStream_t s) {
             else hipLaunchKernelGGL((mla_bf16_mfma<false, true>), grid, dim3(M_THREADS), 0, s, a, slice);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
-            hipLaunchKernelGGL(mla_combine, dim3((a.g.T * a.n_heads + 3) / 4), dim3(256), 0, s, a);
+            launch_combine(a, s);
         } else {
             if (fp8) hipLaunchKernelGGL((mla_bf16_mfma<true, false>), grid, dim3(M_THREADS), 0, s, a, slice);
             else hipLaunchKernelGGL((mla_bf16_mfma<false, false>), grid, dim3(M_THREADS), 0, s, a, slice);

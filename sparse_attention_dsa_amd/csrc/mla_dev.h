@@ -664,64 +664,85 @@ __device__ __forceinline__ void mla_store_partial(const MlaArgs& a, int t, int h
     mla_store_partial_at(a, ((size_t)t * a.n_heads + hbase) * S + sp, (size_t)S, acc, L);
 }
 
-// Merge of one (query row, head)'s split partials by their log-sum-exp, by
-// one wave: slice s is partial p0 + s ps (part_o row and part_lse pair), and
-// lane l accumulates output columns 8l .. 8l + 7 into acc (normalised).
-// Returns the natural-log lse (-inf when every slice is empty).  Up to NS
-// slices go through registers, with every load issued before any arithmetic
-// (one memory round trip); more slices are merged NS at a time.  The sums run
-// in slice order, so the result does not depend on NS.
-template <int NS>
-__device__ __forceinline__ float merge_partials(const uint16_t* part_o, const float* part_lse, size_t p0, size_t ps,
-                                                int S, int lane, float acc[8]) {
-    float mx = -INFINITY;
-    if (S > NS)
-        for (int s = 0; s < S; ++s) mx = fmaxf(mx, part_lse[2 * (p0 + (size_t)s * ps)]);
-    float den = 0.f;
+// Merge of split partials by their log-sum-exp, by one wave, for HP heads:
+// slice s of head h is partial p0 + h hs + s ps (part_o row and part_lse
+// pair), and lane l accumulates the head's output columns 8l .. 8l + 7 into
+// acc[h] (normalised); lse[h] is the natural-log lse (-inf when every slice
+// is empty).  Up to NS slices of every head go through registers, with all
+// their loads issued before any arithmetic (one memory round trip); more
+// slices are merged NS at a time.  The sums run in slice order, so the
+// result depends on neither NS nor HP.
+template <int NS, int HP = 1>
+__device__ __forceinline__ void merge_partials(const uint16_t* part_o, const float* part_lse, size_t p0, size_t hs,
+                                               size_t ps, int S, int lane, float (&acc)[HP][8], float (&lse)[HP]) {
+    float mx[HP], den[HP];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int h = 0; h < HP; ++h) {
+        mx[h] = -INFINITY;
+        den[h] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
+        if (S > NS)
+            for (int s = 0; s < S; ++s) mx[h] = fmaxf(mx[h], part_lse[2 * (p0 + h * hs + (size_t)s * ps)]);
+    }
     for (int s0 = 0; s0 < S; s0 += NS) {
-        f32x2 pl[NS];
-        u32x4 h[NS];
+        f32x2 pl[HP][NS];
+        u32x4 v[HP][NS];
 #pragma unroll
-        for (int u = 0; u < NS; ++u)
-            if (s0 + u < S) pl[u] = *(const f32x2*)(part_lse + 2 * (p0 + (size_t)(s0 + u) * ps));
-#pragma unroll
-        for (int u = 0; u < NS; ++u)
-            if (s0 + u < S) h[u] = *(const u32x4*)(part_o + (p0 + (size_t)(s0 + u) * ps) * M_DL + 8 * lane);
-        if (S <= NS)
+        for (int h = 0; h < HP; ++h)
 #pragma unroll
             for (int u = 0; u < NS; ++u)
-                if (u < S) mx = fmaxf(mx, pl[u][0]);
-        if (mx == -INFINITY) break;
+                if (s0 + u < S) pl[h][u] = *(const f32x2*)(part_lse + 2 * (p0 + h * hs + (size_t)(s0 + u) * ps));
 #pragma unroll
-        for (int u = 0; u < NS; ++u) {
-            if (s0 + u < S) {
-                const float wgt = __expf(pl[u][0] - mx);
-                den += wgt;
-                const float ws = wgt * pl[u][1];
+        for (int h = 0; h < HP; ++h)
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const uint16_t b = (uint16_t)(h[u][i >> 1] >> (16 * (i & 1)));
-                    acc[i] += ws * (float)__builtin_bit_cast(_Float16, b);
+            for (int u = 0; u < NS; ++u)
+                if (s0 + u < S)
+                    v[h][u] = *(const u32x4*)(part_o + (p0 + h * hs + (size_t)(s0 + u) * ps) * M_DL + 8 * lane);
+#pragma unroll
+        for (int h = 0; h < HP; ++h) {
+            if (S <= NS)
+#pragma unroll
+                for (int u = 0; u < NS; ++u)
+                    if (u < S) mx[h] = fmaxf(mx[h], pl[h][u][0]);
+            if (mx[h] == -INFINITY) continue;
+#pragma unroll
+            for (int u = 0; u < NS; ++u) {
+                if (s0 + u < S) {
+                    const float wgt = __expf(pl[h][u][0] - mx[h]);
+                    den[h] += wgt;
+                    const float ws = wgt * pl[h][u][1];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const uint16_t b = (uint16_t)(v[h][u][i >> 1] >> (16 * (i & 1)));
+                        acc[h][i] += ws * (float)__builtin_bit_cast(_Float16, b);
+                    }
                 }
             }
         }
     }
-    if (mx == -INFINITY) return -INFINITY;
-    const float inv = 1.f / den;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] *= inv;
-    return mx + logf(den);
+    for (int h = 0; h < HP; ++h) {
+        if (mx[h] == -INFINITY) {
+            lse[h] = -INFINITY;
+            continue;
+        }
+        const float inv = 1.f / den[h];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[h][i] *= inv;
+        lse[h] = mx[h] + logf(den[h]);
+    }
 }
 
 // merge_partials with the register depth picked from S (the splits of a
 // decode row are a power of two, at most 16 for K = 2048).
-__device__ __forceinline__ float merge_partials_any(const uint16_t* part_o, const float* part_lse, size_t p0,
-                                                    size_t ps, int S, int lane, float acc[8]) {
-    if (S <= 4) return merge_partials<4>(part_o, part_lse, p0, ps, S, lane, acc);
-    if (S <= 8) return merge_partials<8>(part_o, part_lse, p0, ps, S, lane, acc);
-    return merge_partials<16>(part_o, part_lse, p0, ps, S, lane, acc);
+template <int HP = 1>
+__device__ __forceinline__ void merge_partials_any(const uint16_t* part_o, const float* part_lse, size_t p0,
+                                                   size_t hs, size_t ps, int S, int lane, float (&acc)[HP][8],
+                                                   float (&lse)[HP]) {
+    if (S <= 4) merge_partials<4, HP>(part_o, part_lse, p0, hs, ps, S, lane, acc, lse);
+    else if (S <= 8) merge_partials<8, HP>(part_o, part_lse, p0, hs, ps, S, lane, acc, lse);
+    else merge_partials<16, HP>(part_o, part_lse, p0, hs, ps, S, lane, acc, lse);
 }
 
 }  // namespace dsa
