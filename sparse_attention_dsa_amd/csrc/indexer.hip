@@ -353,6 +353,7 @@ static hipError_t launch_fp8_prefill(const IndexerArgs& a, hipStream_t s) {
 constexpr int PER_PF = 2;                  // pages in flight per wave
 constexpr int PER_MAX_ITEMS = 4096;        // (request, query group) pairs per launch
 constexpr int PER_WG_PER_CU = 2;
+constexpr int PER_MIN_PAGES = 2;       // pages per wave at least when emitting (small batches)
 
 // EMIT: instead of storing the scores, each wave stages the composites of its
 // scores at or above the row's key bound in LDS and appends them to the row's
@@ -739,7 +740,15 @@ template <int NQ, int HT>
 static hipError_t launch_fp8(const IndexerArgs& a, hipStream_t s, const hipEvent_t* se) {
     const int qgroups = (a.g.max_q_len + NQ - 1) / NQ;
     if (a.g.B * qgroups <= PER_MAX_ITEMS) {
-        const dim3 grid(device_cu_count() * PER_WG_PER_CU);
+        // Emitting into candidate lists, small batches take at most as many
+        // workgroups as give each wave PER_MIN_PAGES of the largest page
+        // count the batch can have (a host-known bound): every wave with
+        // pages makes one final reservation on its rows' counters, and on a
+        // single row 512 of them on one line cost more than the pages.
+        const long long pmax = (long long)a.g.B * qgroups * ((a.g.max_ctx + IDX_PAGE - 1) / IDX_PAGE);
+        const long long full = (long long)device_cu_count() * PER_WG_PER_CU;
+        const long long need = (pmax + 4 * PER_MIN_PAGES - 1) / (4 * PER_MIN_PAGES);
+        const dim3 grid((unsigned)(a.cand ? std::max(1LL, std::min(full, need)) : full));
         if (se) {   // start and stop events taken by the launch itself: the kernel's own duration
             if (a.cand)
                 hipExtLaunchKernelGGL((indexer_fp8_persistent<NQ, HT, true>), grid, dim3(IDX_THREADS), 0, s, se[0],
