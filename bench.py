@@ -770,6 +770,41 @@ def read_ceiling(log, nbytes=1 << 31, iters=20):
             "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
 
+def page_ceiling(rig, log, iters=20):
+    """dsa_page_probe over the workload's own index-key pages (every
+    request's visible pages in the indexer's order, 8 KB of keys and 256 B
+    of scales each, rotating the device copies as the timed loop does): the
+    rate the memory system gives the indexer's access pattern without its
+    arithmetic, in the indexer's launch shape."""
+    import numpy as np
+    import torch
+    from sparse_attention_dsa_amd import binding as B
+    wl = rig.wl
+    bs = wl.block_size
+    ids = np.concatenate([wl.page_table[r, : (int(wl.context_lens[r]) + bs - 1) // bs] for r in range(wl.batch)])
+    ids_t = torch.from_numpy(ids.astype(np.int32)).cuda()
+    copies = rig.copies
+    pb, sb_ = bs * wl.idx_dim, (4 * bs if copies[0]["idx_scales"] is not None else 0)
+    sink = B.page_probe(copies[0]["idx_keys"], pb, copies[0]["idx_scales"], sb_, ids_t)
+    for i in range(3):
+        B.page_probe(copies[i % len(copies)]["idx_keys"], pb, copies[i % len(copies)]["idx_scales"], sb_, ids_t, sink)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(iters):
+        c = copies[i % len(copies)]
+        B.page_probe(c["idx_keys"], pb, c["idx_scales"], sb_, ids_t, sink)
+    ev1.record()
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / iters
+    nbytes = int(len(ids)) * (pb + sb_)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    log("[bench] random-page read of the indexer's pages: %.1f us, %.1f MB -> %.0f GB/s" % (us, nbytes / 1e6, gbs))
+    return {"kernel": "dsa_page_probe (the indexer's pages, its grid and depth, no arithmetic)",
+            "us": round(us, 2), "pages": int(len(ids)), "bytes": nbytes, "achieved": round(gbs, 1),
+            "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 # ------------------------------------------------------------------ main
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -874,6 +909,7 @@ def main(argv=None):
 
     traffic = measured_traffic(wl.name)
     emit_traffic = measured_traffic(wl.name, "emit-")
+    pages = page_ceiling(rig, log) if wl.max_q_len == 1 and wl.idx_dtype == "e4m3" else None
     rig.free()
     del rig
 
@@ -976,6 +1012,7 @@ def main(argv=None):
         "other_configs": others,
         "hot_cache": hot,
         "hbm_ceiling": ceiling,
+        "page_read_ceiling": pages,
         "cpu_baseline": cpu,
         "parity": parity,
     }

@@ -426,6 +426,26 @@ int dsa_hot_cache_copy(const dsa_batch *batch, const dsa_latent_cache *host, con
 size_t dsa_read_probe_sink_size(void);
 int dsa_read_probe(const void *buf, int64_t nbytes, void *sink, size_t sink_bytes, dsa_stream_t stream);
 
+/* Measurement helper, not a step of the method: the read rate of the
+ * decode indexer's access pattern without its arithmetic.  dsa_page_probe
+ * reads, for each of the n_pages block ids in `block_ids` (device int32,
+ * caller-owned, ids into both pools; the caller keeps them in range),
+ * page_bytes at pages + id * page_bytes (device, 16-byte aligned; a
+ * multiple of 1024, at most 8192) and scale_bytes at scales + id *
+ * scale_bytes (device, 4-byte aligned; 0 to 256, a multiple of 4; scales
+ * may be NULL when scale_bytes is 0), with the indexer's grid (two 4-wave
+ * workgroups per CU), equal contiguous shares of the list per wave and two
+ * pages in flight per wave, and writes one 32-bit word per lane to `sink`
+ * (device, caller-owned, at least dsa_page_probe_sink_size() bytes): the
+ * XOR of the words that lane read, so the XOR of the whole sink is the XOR
+ * of every word read.  Asynchronous on `stream`; time it with events.
+ * DSA_ERR_INVALID_ARG for a null pointer, a bad size or a misaligned pool,
+ * DSA_ERR_WORKSPACE for a small sink, DSA_ERR_LAUNCH if the launch fails;
+ * n_pages = 0 launches nothing. */
+size_t dsa_page_probe_sink_size(void);
+int dsa_page_probe(const void *pages, int64_t page_bytes, const void *scales, int64_t scale_bytes,
+                   const int32_t *block_ids, int32_t n_pages, void *sink, size_t sink_bytes, dsa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

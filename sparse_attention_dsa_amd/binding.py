@@ -24,7 +24,7 @@ EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_spars
            "dsa_read_probe_sink_size", "dsa_read_probe", "dsa_hot_cache_reset", "dsa_hot_cache_workspace_size",
            "dsa_hot_cache_fetch", "dsa_decode_step_timed", "dsa_decode_step_noalloc",
            "dsa_decode_step_fused", "dsa_check_batch", "dsa_hot_cache_plan", "dsa_hot_cache_copy",
-           "dsa_sparse_mla_decode_layers")
+           "dsa_sparse_mla_decode_layers", "dsa_page_probe_sink_size", "dsa_page_probe")
 CHECK_QUERY_START, CHECK_CONTEXT, CHECK_PAGE, CHECK_INDEX = 1, 2, 4, 8   # dsa_check_batch's bits
 ERR_BAD_DEVICE_ARG = -7
 STEP_EVENTS = 5   # events of dsa_decode_step_timed: start, after sampling, indexer, selection, attention
@@ -81,6 +81,9 @@ def lib():
         L.dsa_read_probe_sink_size.argtypes = []
         L.dsa_read_probe_sink_size.restype = sz
         L.dsa_read_probe.argtypes = [vp, i64, vp, sz, vp]
+        L.dsa_page_probe_sink_size.argtypes = []
+        L.dsa_page_probe_sink_size.restype = sz
+        L.dsa_page_probe.argtypes = [vp, i64, vp, i64, vp, i32, vp, sz, vp]
         L.dsa_hot_cache_reset.argtypes = [P(DsaBatch), P(DsaHotCache), vp]
         L.dsa_hot_cache_workspace_size.argtypes = [P(DsaBatch), i32, i32]
         L.dsa_hot_cache_workspace_size.restype = sz
@@ -415,6 +418,20 @@ def read_probe(buf: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=No
     if sink is None:
         sink = torch.empty(max(int(lib().dsa_read_probe_sink_size()), 4), dtype=torch.uint8, device=buf.device)
     _check("dsa_read_probe", lib().dsa_read_probe(_ptr(buf), n, _ptr(sink), sink.numel(), _stream(stream)))
+    return sink
+
+
+def page_probe(pages: torch.Tensor, page_bytes: int, scales: Optional[torch.Tensor], scale_bytes: int,
+               block_ids: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Read the listed pages of a pool the way the decode indexer does, with
+    no arithmetic (measurement helper); returns the per-lane XOR sink."""
+    if block_ids.dtype != torch.int32 or not block_ids.is_cuda:
+        raise ValueError("block_ids must be an int32 device tensor")
+    if sink is None:
+        sink = torch.empty(int(lib().dsa_page_probe_sink_size()) // 4, dtype=torch.int32, device=pages.device)
+    _check("dsa_page_probe", lib().dsa_page_probe(_ptr(pages), page_bytes, _ptr(scales), scale_bytes,
+                                                  _ptr(block_ids), block_ids.numel(), _ptr(sink),
+                                                  sink.numel() * sink.element_size(), _stream(stream)))
     return sink
 
 

@@ -45,6 +45,52 @@ __global__ __launch_bounds__(PR_THREADS) void stream_read(const uint8_t* __restr
 
 int probe_grid() { return 8 * device_cu_count(); }
 
+// Random-page read probe: the pages a block-id list names, read the way the
+// persistent indexer reads its key pages (the same grid of 2 four-wave
+// workgroups per CU, equal contiguous shares of the list per wave, 2 pages
+// in flight per wave, 1 KB non-temporal loads) but with no arithmetic: the
+// memory system's rate for that access pattern.  Page b is page_bytes at
+// pages + b page_bytes (a multiple of 1 KB, at most 8 KB) plus scale_bytes
+// (0 or a multiple of 4, at most 256) at scales + b scale_bytes.  Each lane
+// folds what it read into one word; sink[w][lane] for wave w.
+constexpr int PP_WG_PER_CU = 2;
+constexpr int PP_INFLIGHT = 2;
+
+__global__ __launch_bounds__(256) void page_read(const uint8_t* __restrict__ pages, int page_kb,
+                                                 const uint8_t* __restrict__ scales, int scale_bytes,
+                                                 const int32_t* __restrict__ blocks, int n, uint32_t* __restrict__ sink) {
+    const int lane = threadIdx.x & 63;
+    const int gw = blockIdx.x * 4 + (threadIdx.x >> 6), nw = gridDim.x * 4;
+    const int p0 = (int)((long long)n * gw / nw), p1 = (int)((long long)n * (gw + 1) / nw);
+    const int64_t pstride = 1024 * (int64_t)page_kb;
+    const bool has_sc = 4 * lane < scale_bytes;
+    uint32_t acc = 0u;
+    for (int p = p0; p < p1; p += PP_INFLIGHT) {
+        u32x4 v[PP_INFLIGHT][8];
+        uint32_t sc[PP_INFLIGHT];
+#pragma unroll
+        for (int d = 0; d < PP_INFLIGHT; ++d) {
+            const bool live = p + d < p1;
+            const int64_t b = live ? blocks[p + d] : 0;
+            const uint8_t* src = pages + b * pstride + 16 * lane;
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                v[d][c] = live && c < page_kb ? __builtin_nontemporal_load((const u32x4*)(src + 1024 * c))
+                                              : (u32x4){0u, 0u, 0u, 0u};
+            sc[d] = live && has_sc ? *(const uint32_t*)(scales + b * scale_bytes + 4 * lane) : 0u;
+        }
+#pragma unroll
+        for (int d = 0; d < PP_INFLIGHT; ++d) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc ^= v[d][c][0] ^ v[d][c][1] ^ v[d][c][2] ^ v[d][c][3];
+            acc ^= sc[d];
+        }
+    }
+    sink[(size_t)gw * 64 + lane] = acc;
+}
+
+int page_probe_grid() { return PP_WG_PER_CU * device_cu_count(); }
+
 }  // namespace dsa
 
 extern "C" {
@@ -57,6 +103,24 @@ int dsa_read_probe(const void* buf, int64_t nbytes, void* sink, size_t sink_byte
     const int grid = dsa::probe_grid();
     if (sink_bytes < sizeof(uint32_t) * (size_t)grid) return DSA_ERR_WORKSPACE;
     hipLaunchKernelGGL(dsa::stream_read, dim3(grid), dim3(dsa::PR_THREADS), 0, (hipStream_t)stream, (const uint8_t*)buf, nbytes,
+                       (uint32_t*)sink);
+    return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
+}
+
+size_t dsa_page_probe_sink_size(void) { return sizeof(uint32_t) * 256 * (size_t)dsa::page_probe_grid(); }
+
+int dsa_page_probe(const void* pages, int64_t page_bytes, const void* scales, int64_t scale_bytes,
+                   const int32_t* block_ids, int32_t n_pages, void* sink, size_t sink_bytes, dsa_stream_t stream) {
+    if (!pages || !block_ids || !sink || n_pages < 0 || page_bytes < 1024 || page_bytes > 8192 ||
+        (page_bytes & 1023) || scale_bytes < 0 || scale_bytes > 256 || (scale_bytes & 3) ||
+        (scale_bytes > 0 && !scales) || ((uintptr_t)pages & 15) || ((uintptr_t)scales & 3))
+        return DSA_ERR_INVALID_ARG;
+    if (const int st = dsa_check_device(); st != DSA_OK) return st;
+    const int grid = dsa::page_probe_grid();
+    if (sink_bytes < sizeof(uint32_t) * 256 * (size_t)grid) return DSA_ERR_WORKSPACE;
+    if (n_pages == 0) return DSA_OK;
+    hipLaunchKernelGGL(dsa::page_read, dim3(grid), dim3(256), 0, (hipStream_t)stream, (const uint8_t*)pages,
+                       (int)(page_bytes / 1024), (const uint8_t*)scales, (int)scale_bytes, block_ids, n_pages,
                        (uint32_t*)sink);
     return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
 }

@@ -92,6 +92,21 @@ def test_invalid_arguments_rejected_before_device(L):
     assert L.dsa_read_probe(0x108, 1024, 0x100, 1 << 20, None) == -1
     assert L.dsa_read_probe(0x100, 1000, 0x100, 1 << 20, None) == -1
     assert L.dsa_read_probe(0x100, 1024, None, 1 << 20, None) == -1
+    # the random-page probe: null pointers, page size not a multiple of 1 KB or
+    # above 8 KB, scale size above 256 or not a multiple of 4, scales missing,
+    # misaligned pools, negative count
+    pp = L.dsa_page_probe
+    assert pp(None, 8192, 0x100, 256, 0x200, 10, 0x300, 1 << 20, None) == -1
+    assert pp(0x100, 8192, 0x100, 256, None, 10, 0x300, 1 << 20, None) == -1
+    assert pp(0x100, 8192, 0x100, 256, 0x200, 10, None, 1 << 20, None) == -1
+    assert pp(0x100, 8000, 0x100, 256, 0x200, 10, 0x300, 1 << 20, None) == -1
+    assert pp(0x100, 9216, 0x100, 256, 0x200, 10, 0x300, 1 << 20, None) == -1
+    assert pp(0x100, 8192, 0x100, 260, 0x200, 10, 0x300, 1 << 20, None) == -1
+    assert pp(0x100, 8192, 0x100, 6, 0x200, 10, 0x300, 1 << 20, None) == -1
+    assert pp(0x100, 8192, None, 256, 0x200, 10, 0x300, 1 << 20, None) == -1
+    assert pp(0x108, 8192, 0x100, 256, 0x200, 10, 0x300, 1 << 20, None) == -1
+    assert pp(0x100, 8192, 0x102, 256, 0x200, 10, 0x300, 1 << 20, None) == -1
+    assert pp(0x100, 8192, 0x100, 256, 0x200, -1, 0x300, 1 << 20, None) == -1
 
 
 def test_hot_cache_arguments_rejected_before_device(L):
@@ -131,6 +146,7 @@ def test_valid_call_without_gpu_reports_device(L):
     assert L.dsa_hot_cache_reset(C.byref(b), C.byref(hot), None) == -4
     assert L.dsa_hot_cache_fetch(C.byref(b), C.byref(bf), 0x1, 16, C.byref(hot), None, 0x1, 1 << 30, None) == -4
     assert L.dsa_read_probe(0x100, 1024, 0x100, 1 << 20, None) == -4
+    assert L.dsa_page_probe(0x100, 8192, None, 0, 0x200, 10, 0x300, 1 << 20, None) == -4
 
 
 def test_noalloc_rejects_batches_beyond_its_scratch(L):
