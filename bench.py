@@ -30,7 +30,10 @@ shape both are compute-bound; the top-K time is reported on its own.
 pinned host memory) on selections that drift from step to step: the fetch of
 the missing rows and sparse MLA over the hot set.
 `other_configs` gives the step on the other decode configurations, and
-`hbm_ceiling` a plain 2 GiB streaming read as the practical bandwidth ceiling.
+`hbm_ceiling` a plain 2 GiB streaming read as the practical bandwidth ceiling;
+`page_read_ceiling` and `attention_gather_ceiling` read the indexer's pages and
+the attention's selected rows in those kernels' launch shapes with no
+arithmetic.
 `indexshare` times groups of layers that share one selection (one full step,
 then sparse MLA only on the other layers' caches) and reports the amortised
 tokens/s per layer.  `all_128k` repeats the step measurement with every
@@ -805,6 +808,54 @@ def page_ceiling(rig, log, iters=20):
             "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
 
+def row_ceiling(rig, indices, log, iters=20):
+    """dsa_row_probe over the step's own selection (every query row's selected
+    latent rows, 1152 B each, in the attention's slice order and split count,
+    rotating the device copies as the timed loop does): the rate the memory
+    system gives the 128-head attention tile's gather without its
+    arithmetic, in that tile's launch shape."""
+    import numpy as np
+    import torch
+    from sparse_attention_dsa_amd import binding as B
+    wl = rig.wl
+    bs, T, K = wl.block_size, wl.total_q, wl.topk
+    if (indices < 0).any() or wl.kv_dtype != "bf16" or wl.mla_heads != 128:
+        return None
+    qsl = np.asarray(wl.query_start_loc)
+    req = np.searchsorted(qsl, np.arange(T), side="right") - 1
+    pt = np.asarray(wl.page_table)
+    rows = pt[req[:, None], indices // bs].astype(np.int64) * bs + indices % bs
+    # the attention's split count: enough workgroups for the chip, at least
+    # 128 tokens a slice
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    S = 1
+    while T * S < cus and K // (2 * S) >= 128:
+        S *= 2
+    per = K // S
+    if per % 32:
+        return None
+    ids_t = torch.from_numpy(rows.astype(np.int32).ravel()).cuda()
+    copies = rig.copies
+    sink = B.row_probe(copies[0]["kv"], 1152, ids_t, per)
+    for i in range(3):
+        B.row_probe(copies[i % len(copies)]["kv"], 1152, ids_t, per, sink)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(iters):
+        B.row_probe(copies[i % len(copies)]["kv"], 1152, ids_t, per, sink)
+    ev1.record()
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / iters
+    nbytes = int(rows.size) * 1152
+    gbs = nbytes / (us * 1e-6) / 1e9
+    log("[bench] gather of the attention's rows: %.1f us, %.1f MB -> %.0f GB/s (%d workgroups of %d rows)" %
+        (us, nbytes / 1e6, gbs, T * S, per))
+    return {"kernel": "dsa_row_probe (the attention's selected rows, its grid and LDS ring, no arithmetic)",
+            "us": round(us, 2), "rows": int(rows.size), "rows_per_workgroup": per, "bytes": nbytes,
+            "achieved": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 # ------------------------------------------------------------------ main
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -910,6 +961,7 @@ def main(argv=None):
     traffic = measured_traffic(wl.name)
     emit_traffic = measured_traffic(wl.name, "emit-")
     pages = page_ceiling(rig, log) if wl.max_q_len == 1 and wl.idx_dtype == "e4m3" else None
+    gather = row_ceiling(rig, indices, log)
     rig.free()
     del rig
 
@@ -1013,6 +1065,7 @@ def main(argv=None):
         "hot_cache": hot,
         "hbm_ceiling": ceiling,
         "page_read_ceiling": pages,
+        "attention_gather_ceiling": gather,
         "cpu_baseline": cpu,
         "parity": parity,
     }

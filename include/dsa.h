@@ -446,6 +446,26 @@ size_t dsa_page_probe_sink_size(void);
 int dsa_page_probe(const void *pages, int64_t page_bytes, const void *scales, int64_t scale_bytes,
                    const int32_t *block_ids, int32_t n_pages, void *sink, size_t sink_bytes, dsa_stream_t stream);
 
+/* Measurement helper, not a step of the method: the read rate of the
+ * 128-head sparse-MLA tile's gather without its arithmetic.  dsa_row_probe
+ * reads the n_rows rows listed in `row_ids` (device int32, caller-owned, row
+ * ids into the pool; the caller keeps them in range), row id r being
+ * row_bytes at base + r * row_bytes (device, 16-byte aligned; row_bytes a
+ * multiple of 128, at most 1152: a bf16 latent row of 512 + 64 values), in
+ * the tile's launch shape: one 4-wave workgroup per rows_per_wg consecutive
+ * entries of the list (a multiple of 32 that divides n_rows), 32-row tiles
+ * through a 4-deep LDS ring by direct global-to-LDS transfers, three tiles in
+ * flight.  It writes one 32-bit word per workgroup to `sink` (device,
+ * caller-owned, at least dsa_row_probe_sink_size(n_rows, rows_per_wg)
+ * bytes): the XOR of every 32-bit word of the workgroup's rows.
+ * Asynchronous on `stream`; time it with events.  DSA_ERR_INVALID_ARG for a
+ * null pointer, a misaligned pool or a bad size, DSA_ERR_WORKSPACE for a
+ * small sink, DSA_ERR_LAUNCH if the launch fails; n_rows = 0 launches
+ * nothing. */
+size_t dsa_row_probe_sink_size(int32_t n_rows, int32_t rows_per_wg);
+int dsa_row_probe(const void *base, int64_t row_bytes, const int32_t *row_ids, int32_t n_rows, int32_t rows_per_wg,
+                  void *sink, size_t sink_bytes, dsa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,8 @@ EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_spars
            "dsa_read_probe_sink_size", "dsa_read_probe", "dsa_hot_cache_reset", "dsa_hot_cache_workspace_size",
            "dsa_hot_cache_fetch", "dsa_decode_step_timed", "dsa_decode_step_noalloc",
            "dsa_decode_step_fused", "dsa_check_batch", "dsa_hot_cache_plan", "dsa_hot_cache_copy",
-           "dsa_sparse_mla_decode_layers", "dsa_page_probe_sink_size", "dsa_page_probe")
+           "dsa_sparse_mla_decode_layers", "dsa_page_probe_sink_size", "dsa_page_probe",
+           "dsa_row_probe_sink_size", "dsa_row_probe")
 CHECK_QUERY_START, CHECK_CONTEXT, CHECK_PAGE, CHECK_INDEX = 1, 2, 4, 8   # dsa_check_batch's bits
 ERR_BAD_DEVICE_ARG = -7
 STEP_EVENTS = 5   # events of dsa_decode_step_timed: start, after sampling, indexer, selection, attention
@@ -84,6 +85,10 @@ def lib():
         L.dsa_page_probe_sink_size.argtypes = []
         L.dsa_page_probe_sink_size.restype = sz
         L.dsa_page_probe.argtypes = [vp, i64, vp, i64, vp, i32, vp, sz, vp]
+        L.dsa_row_probe_sink_size.argtypes = [i32, i32]
+        L.dsa_row_probe_sink_size.restype = sz
+        L.dsa_row_probe.argtypes = [vp, i64, vp, i32, i32, vp, sz, vp]
+        L.dsa_row_probe.restype = C.c_int
         L.dsa_hot_cache_reset.argtypes = [P(DsaBatch), P(DsaHotCache), vp]
         L.dsa_hot_cache_workspace_size.argtypes = [P(DsaBatch), i32, i32]
         L.dsa_hot_cache_workspace_size.restype = sz
@@ -432,6 +437,22 @@ def page_probe(pages: torch.Tensor, page_bytes: int, scales: Optional[torch.Tens
     _check("dsa_page_probe", lib().dsa_page_probe(_ptr(pages), page_bytes, _ptr(scales), scale_bytes,
                                                   _ptr(block_ids), block_ids.numel(), _ptr(sink),
                                                   sink.numel() * sink.element_size(), _stream(stream)))
+    return sink
+
+
+def row_probe(pool: torch.Tensor, row_bytes: int, row_ids: torch.Tensor, rows_per_wg: int,
+              sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Gather the listed rows of a pool the way the 128-head sparse-MLA tile
+    does, with no arithmetic (measurement helper); returns the
+    per-workgroup XOR sink."""
+    if row_ids.dtype != torch.int32 or not row_ids.is_cuda:
+        raise ValueError("row_ids must be an int32 device tensor")
+    n = row_ids.numel()
+    if sink is None:
+        words = max(int(lib().dsa_row_probe_sink_size(n, rows_per_wg)) // 4, 1)
+        sink = torch.empty(words, dtype=torch.int32, device=pool.device)
+    _check("dsa_row_probe", lib().dsa_row_probe(_ptr(pool), row_bytes, _ptr(row_ids), n, rows_per_wg, _ptr(sink),
+                                                sink.numel() * sink.element_size(), _stream(stream)))
     return sink
 
 

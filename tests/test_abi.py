@@ -103,6 +103,19 @@ def test_invalid_arguments_rejected_before_device(L):
     assert pp(0x100, 9216, 0x100, 256, 0x200, 10, 0x300, 1 << 20, None) == -1
     assert pp(0x100, 8192, 0x100, 260, 0x200, 10, 0x300, 1 << 20, None) == -1
     assert pp(0x100, 8192, 0x100, 6, 0x200, 10, 0x300, 1 << 20, None) == -1
+    # the row-gather probe: null pointers, misaligned pool, row size not a
+    # multiple of 128 or above 1152, rows per workgroup not a multiple of 32
+    # or not dividing the count
+    rp = L.dsa_row_probe
+    assert rp(None, 1152, 0x200, 512, 256, 0x300, 1 << 20, None) == -1
+    assert rp(0x100, 1152, None, 512, 256, 0x300, 1 << 20, None) == -1
+    assert rp(0x100, 1152, 0x200, 512, 256, None, 1 << 20, None) == -1
+    assert rp(0x108, 1152, 0x200, 512, 256, 0x300, 1 << 20, None) == -1
+    assert rp(0x100, 1000, 0x200, 512, 256, 0x300, 1 << 20, None) == -1
+    assert rp(0x100, 1280, 0x200, 512, 256, 0x300, 1 << 20, None) == -1
+    assert rp(0x100, 1152, 0x200, 512, 48, 0x300, 1 << 20, None) == -1
+    assert rp(0x100, 1152, 0x200, 500, 256, 0x300, 1 << 20, None) == -1
+    assert L.dsa_row_probe_sink_size(512, 256) == 8
     assert pp(0x100, 8192, None, 256, 0x200, 10, 0x300, 1 << 20, None) == -1
     assert pp(0x108, 8192, 0x100, 256, 0x200, 10, 0x300, 1 << 20, None) == -1
     assert pp(0x100, 8192, 0x102, 256, 0x200, 10, 0x300, 1 << 20, None) == -1
@@ -147,6 +160,7 @@ def test_valid_call_without_gpu_reports_device(L):
     assert L.dsa_hot_cache_fetch(C.byref(b), C.byref(bf), 0x1, 16, C.byref(hot), None, 0x1, 1 << 30, None) == -4
     assert L.dsa_read_probe(0x100, 1024, 0x100, 1 << 20, None) == -4
     assert L.dsa_page_probe(0x100, 8192, None, 0, 0x200, 10, 0x300, 1 << 20, None) == -4
+    assert L.dsa_row_probe(0x100, 1152, 0x200, 512, 256, 0x300, 1 << 20, None) == -4
 
 
 def test_noalloc_rejects_batches_beyond_its_scratch(L):

@@ -126,6 +126,30 @@ def test_mla_decode_on_oracle_selection():
         np.testing.assert_allclose(lse[t], rlse, rtol=0, atol=1e-3)
 
 
+@pytest.mark.parametrize("k", [1024, 2048])
+def test_mla_single_slice(k):
+    """One slice per row (the prefill entry point), so the tile stores its
+    normalised rows itself instead of split partials; K = 1024 and 2048,
+    rows in descending score order, against the oracle."""
+    wl = _ragged()
+    batch, d = upload(wl)
+    T = wl.total_q
+    sel = np.full((T, k), -1, dtype=np.int32)
+    for t in range(T):
+        s = oracle.topk(oracle.query_scores(wl, t), k)
+        sel[t, :len(s)] = s[::-1]
+    lse = torch.empty((T, wl.mla_heads), dtype=torch.float32, device="cuda")
+    out = dsa.sparse_mla_prefill(batch, d["kv"], None, wl.d_latent, d["q_mla"], torch.from_numpy(sel).cuda(),
+                                 wl.softmax_scale, lse=lse)
+    out = out.float().cpu().numpy()
+    lse = lse.cpu().numpy()
+    for t in range(T):
+        s = sel[t][sel[t] >= 0]
+        ref, rlse = oracle.query_mla(wl, t, s)
+        check_out(out[t], ref, fp32=False)
+        np.testing.assert_allclose(lse[t], rlse, rtol=0, atol=1e-3)
+
+
 def test_mla_decode_unsorted_and_holey_indices():
     """Indices in any order with -1 holes anywhere give the same result."""
     wl = workloads.make_workload("single_b1_l32768", batch=1, context_lens=[3000], seed=4)

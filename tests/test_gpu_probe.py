@@ -1,6 +1,7 @@
 """The measurement probes read exactly what they are given: the XOR of the
 random-page probe's sink equals the XOR of every word of the listed pages and
-their scales (a list with repeats and a count that leaves waves empty)."""
+their scales (a list with repeats and a count that leaves waves empty), and
+each word of the row-gather probe's sink the XOR of its workgroup's rows."""
 import numpy as np
 import pytest
 import torch
@@ -30,6 +31,20 @@ def test_page_probe_reads_the_listed_pages(page_bytes, scale_bytes, n):
     if scale_bytes:
         want ^= _xor(scales[ids, :scale_bytes])
     assert _xor(sink.cpu().numpy()) == want
+
+
+@pytest.mark.parametrize("row_bytes,rows_per_wg,n", [(1152, 512, 4096), (1152, 32, 96), (128, 64, 640), (640, 96, 288)])
+def test_row_probe_reads_the_listed_rows(row_bytes, rows_per_wg, n):
+    rng = np.random.default_rng(row_bytes + n)
+    pool = 3000
+    rows = rng.integers(0, 256, size=(pool, row_bytes), dtype=np.uint8)
+    ids = rng.integers(0, pool, size=n).astype(np.int32)
+    print("row probe", row_bytes, rows_per_wg, n, flush=True)
+    sink = B.row_probe(torch.from_numpy(rows).cuda(), row_bytes, torch.from_numpy(ids).cuda(), rows_per_wg)
+    torch.cuda.synchronize()
+    got = sink.cpu().numpy().view(np.uint32)
+    for w in range(n // rows_per_wg):
+        assert int(got[w]) == _xor(rows[ids[w * rows_per_wg:(w + 1) * rows_per_wg]]), "workgroup %d" % w
 
 
 def test_read_probe_reads_the_buffer():
