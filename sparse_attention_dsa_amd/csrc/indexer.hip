@@ -692,6 +692,7 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
 // Generic path: any head count / dim, fp32, e4m3 or MXFP4 keys (fp32 or e4m3
 // queries), any block size.  One thread per (query row, token); the query and
 // weights sit in LDS.
+constexpr int GEN_MAX_D4 = 32;   // fp32 key rows held in registers: up to 128 elements
 __global__ __launch_bounds__(256) void indexer_generic(IndexerArgs a) {
     const Geometry& G = a.g;
     const int t = blockIdx.y;
@@ -719,16 +720,41 @@ __global__ __launch_bounds__(256) void indexer_generic(IndexerArgs a) {
     const uint8_t* f4e = (const uint8_t*)a.keys + blk * bs * (size_t)(D / 2 + D / 32) + (size_t)bs * (D / 2) +
                          (size_t)(s % bs) * (D / 32);
     float total = 0.f;
-    for (int h = 0; h < H; ++h) {
-        float dot = 0.f;
-        for (int d = 0; d < D; ++d) {
-            const size_t off = row * D + d;
-            float k;
-            if (f4) k = e2m1_to_f32((uint32_t)(f4c[d >> 1] >> (4 * (d & 1)))) * e8m0_to_f32(f4e[d >> 5]);
-            else k = f8 ? e4m3_to_f32(((const uint8_t*)a.keys)[off]) : ((const float*)a.keys)[off];
-            dot = fmaf(qv[h * D + d], k, dot);
+    if (a.key_dtype == 0 && (D & 3) == 0 && D <= 4 * GEN_MAX_D4) {
+        // fp32 keys of at most 128 elements: the token's row in registers by
+        // 16-byte loads all issued at once, then every head's dot product
+        // from them (same order of additions as below)
+        const f32x4* kr = (const f32x4*)((const float*)a.keys + row * D);
+        const int d4n = D >> 2;
+        f32x4 kv[GEN_MAX_D4];
+#pragma unroll
+        for (int i = 0; i < GEN_MAX_D4; ++i) kv[i] = i < d4n ? kr[i] : (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int h = 0; h < H; ++h) {
+            const float* qh = qv + h * D;
+            float dot = 0.f;
+#pragma unroll
+            for (int i = 0; i < GEN_MAX_D4; ++i) {
+                if (i < d4n) {
+                    dot = fmaf(qh[4 * i], kv[i][0], dot);
+                    dot = fmaf(qh[4 * i + 1], kv[i][1], dot);
+                    dot = fmaf(qh[4 * i + 2], kv[i][2], dot);
+                    dot = fmaf(qh[4 * i + 3], kv[i][3], dot);
+                }
+            }
+            total = fmaf(wv[h], fmaxf(dot, 0.f), total);
         }
-        total = fmaf(wv[h], fmaxf(dot, 0.f), total);
+    } else {
+        for (int h = 0; h < H; ++h) {
+            float dot = 0.f;
+            for (int d = 0; d < D; ++d) {
+                const size_t off = row * D + d;
+                float k;
+                if (f4) k = e2m1_to_f32((uint32_t)(f4c[d >> 1] >> (4 * (d & 1)))) * e8m0_to_f32(f4e[d >> 5]);
+                else k = f8 ? e4m3_to_f32(((const uint8_t*)a.keys)[off]) : ((const float*)a.keys)[off];
+                dot = fmaf(qv[h * D + d], k, dot);
+            }
+            total = fmaf(wv[h], fmaxf(dot, 0.f), total);
+        }
     }
     const float sc = a.key_scales ? a.key_scales[row] : 1.f;
     const float score = sc * total;

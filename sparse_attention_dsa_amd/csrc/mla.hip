@@ -363,6 +363,8 @@ static void launch_combine(const MlaArgs& a, hipStream_t s) {
 
 // Generic path: any dims and head counts, fp32 / bf16 / e4m3 latent.  One
 // workgroup per (query row, head); logits and probabilities in LDS.
+constexpr int GEN_MAX_W4 = 32;     // fp32 latent rows held in registers: up to 128 values
+constexpr int GEN_PV_BATCH = 16;   // value rows in flight per thread in the PV sum
 __global__ __launch_bounds__(256) void mla_generic(MlaArgs a) {
     const Geometry& G = a.g;
     const int t = blockIdx.x / a.n_heads, h = blockIdx.x % a.n_heads;
@@ -393,14 +395,34 @@ __global__ __launch_bounds__(256) void mla_generic(MlaArgs a) {
         if (a.kv_dtype == 1) return bf16_to_f32(((const uint16_t*)a.kv)[off]);
         return e4m3_to_f32(((const uint8_t*)a.kv)[off]) * a.kv_scales[row];
     };
+    // fp32 rows of at most 128 values whose sizes are multiples of 4: rows
+    // read by 16-byte loads all in flight at once (same order of additions)
+    const bool vec = f32 && (W & 3) == 0 && (D & 3) == 0 && W <= 4 * GEN_MAX_W4;
     float lmax = -INFINITY;
     for (int j = threadIdx.x; j < a.k; j += blockDim.x) {
         const int64_t row = rows[j];
         float zj = -INFINITY;
         if (row >= 0) {
             float dot = 0.f;
+            if (vec) {
+                const f32x4* kr = (const f32x4*)((const float*)a.kv + (size_t)row * W);
+                const int w4 = W >> 2;
+                f32x4 kv[GEN_MAX_W4];
+#pragma unroll
+                for (int i = 0; i < GEN_MAX_W4; ++i) kv[i] = i < w4 ? kr[i] : (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < GEN_MAX_W4; ++i) {
+                    if (i < w4) {
+                        dot = fmaf(qv[4 * i], kv[i][0], dot);
+                        dot = fmaf(qv[4 * i + 1], kv[i][1], dot);
+                        dot = fmaf(qv[4 * i + 2], kv[i][2], dot);
+                        dot = fmaf(qv[4 * i + 3], kv[i][3], dot);
+                    }
+                }
+            } else {
 #pragma unroll 8
-            for (int c = 0; c < W; ++c) dot = fmaf(qv[c], elem(row, c), dot);
+                for (int c = 0; c < W; ++c) dot = fmaf(qv[c], elem(row, c), dot);
+            }
             zj = dot * a.scale;
         }
         z[j] = zj;
@@ -428,6 +450,42 @@ __global__ __launch_bounds__(256) void mla_generic(MlaArgs a) {
     }
     const float den = red[0];
     const float inv = den > 0.f ? 1.f / den : 0.f;
+    if (vec) {
+        // 4 value columns a thread (D <= 128: at most 32 column groups), the
+        // selection split over 256 / (D / 4) groups of threads, GEN_PV_BATCH
+        // rows in flight per thread; the groups' sums are added in group order
+        __shared__ f32x4 part[256];
+        const int nc4 = D >> 2, groups = 256 / nc4;
+        const int c4 = threadIdx.x % nc4, g = threadIdx.x / nc4;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (g < groups) {
+            for (int j0 = g; j0 < a.k; j0 += groups * GEN_PV_BATCH) {
+                f32x4 v[GEN_PV_BATCH];
+                float p[GEN_PV_BATCH];
+#pragma unroll
+                for (int u = 0; u < GEN_PV_BATCH; ++u) {
+                    const int j = j0 + u * groups;
+                    const int64_t row = j < a.k ? rows[j] : -1;   // padding has p = 0: read row 0
+                    p[u] = j < a.k ? z[j] : 0.f;
+                    v[u] = ((const f32x4*)((const float*)a.kv + (size_t)(row < 0 ? 0 : row) * W))[c4];
+                }
+#pragma unroll
+                for (int u = 0; u < GEN_PV_BATCH; ++u) {
+                    acc[0] = fmaf(p[u], v[u][0], acc[0]);
+                    acc[1] = fmaf(p[u], v[u][1], acc[1]);
+                    acc[2] = fmaf(p[u], v[u][2], acc[2]);
+                    acc[3] = fmaf(p[u], v[u][3], acc[3]);
+                }
+            }
+        }
+        part[threadIdx.x] = acc;
+        __syncthreads();
+        for (int c = threadIdx.x; c < D; c += blockDim.x) {
+            float sum = 0.f;
+            for (int gg = 0; gg < groups; ++gg) sum += part[gg * nc4 + (c >> 2)][c & 3];
+            ((float*)a.out)[((size_t)t * a.n_heads + h) * D + c] = sum * inv;
+        }
+    } else
     for (int c = threadIdx.x; c < D; c += blockDim.x) {
         float acc = 0.f;
 #pragma unroll 8
