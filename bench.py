@@ -1045,7 +1045,9 @@ def main(argv=None):
                                + " (in dsa_decode_step)",
                      "achieved": round(emit_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(emit_gbs / PEAK_HBM_GBS, 4), "traffic": emit_traffic,
-                     "bytes_per_launch": emit_bytes, "us_per_launch": round(emit_us, 2)},
+                     "bytes_per_launch": emit_bytes, "us_per_launch": round(emit_us, 2),
+                     "scope": "the dominant kernel alone; the whole step's fraction is step_frac",
+                     "step_frac": round(step_gbs / PEAK_HBM_GBS, 4)},
         "step_phases_us": {k: round(v, 2) for k, v in phases.items()},
         "indexer_scores_kernel": {"kernel": "indexer_fp8_persistent<1, 4, false> (dsa_indexer_scores)",
                                   "achieved": round(idx_gbs, 1), "frac": round(idx_gbs / PEAK_HBM_GBS, 4),
