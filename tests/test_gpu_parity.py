@@ -409,6 +409,32 @@ def test_decode_step_shapes(case):
     check_step_rows(wl, list(range(wl.total_q)), out, lse, idx)
 
 
+@pytest.mark.parametrize("case", ["vec", "odd_widths", "wide_rows"])
+def test_generic_fp32_shapes(case):
+    """The generic fp32 kernels on both sides of their register-row path:
+    key and latent rows of at most 128 values that are multiples of 4 (rows
+    read by 16-byte loads), widths that are not (element loads), and latent
+    rows wider than 128 values; several rows, ragged contexts, pages
+    shuffled, every row against the oracle."""
+    kw = dict(batch=3, context_lens=[700, 4096, 2500], shuffle_pages=True, seed=31)
+    if case == "vec":
+        kw.update(idx_heads=3, idx_dim=36, mla_heads=8, d_latent=60, d_rope=8, topk=300)
+    elif case == "odd_widths":
+        kw.update(idx_heads=4, idx_dim=30, mla_heads=8, d_latent=62, d_rope=9, topk=256)
+    else:
+        kw.update(idx_heads=2, idx_dim=132, mla_heads=4, d_latent=192, d_rope=16, topk=512)
+    wl = workloads.make_workload("tiny_fp32_l4096", **kw)
+    log("generic fp32", case, "idx", wl.idx_heads, wl.idx_dim, "mla", wl.mla_heads, wl.d_latent, wl.d_rope)
+    batch, d = upload(wl)
+    out, lse, idx = gpu_step(wl, batch, d)
+    check_step_rows(wl, list(range(wl.total_q)), out, lse, idx)
+    sc = dsa.indexer_scores(batch, d["idx_keys"], d["idx_scales"], d["q_idx"], d["w"])
+    torch.cuda.synchronize()
+    sc = sc.cpu().numpy()
+    for t, (r, p, n) in enumerate(oracle.query_positions(wl)):
+        check_scores(wl, t, sc[t, :n])
+
+
 @pytest.mark.parametrize("q_len", [1, 2])
 def test_many_requests(q_len):
     """More than 4096 (request, query-group) items: 4200 short requests (16 to
