@@ -117,10 +117,14 @@ __device__ __forceinline__ T ld_agent(const T* p) {
     return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// max(x, 0).  (Inline asm would drop the canonicalizing v_max that fmaxf
-// puts before it, but inline asm is outside the compiler's hazard tracking:
-// a VALU read of an MFMA result then loses the wait states it needs.)
-__device__ __forceinline__ float relu(float x) { return fmaxf(x, 0.f); }
+// max(x, 0) for a float that is not a NaN, as a signed-integer max of its
+// bits: every negative float, -0 included, has the sign bit set and is below
+// 0 as an int32, and every other one keeps its bits.  One integer
+// instruction, where fmaxf first canonicalizes an input the compiler cannot
+// prove canonical (an MFMA result: a second instruction per element) and
+// inline asm would fall outside the compiler's hazard tracking (a VALU read
+// of an MFMA result then loses the wait states it needs).
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // ------------------------------------------------ asynchronous LDS fills
 // One 64-lane transfer global -> LDS at LDS address m0v (wave-uniform; lane
