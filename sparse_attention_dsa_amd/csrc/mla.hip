@@ -289,11 +289,13 @@ void mla_bf16_mfma(MlaArgs a, int slice) {
     const float lse_nat = empty ? -INFINITY : (m_run + log2f(l_run)) * LN2;
     if (SPLIT) {
         // the head's values sit in lanes col, col + 16, col + 32, col + 48
-        float amax = 0.f;
+        // (the magnitudes' maximum on their bits, as in max_abs_pair)
+        uint32_t amb = 0u;
 #pragma unroll
         for (int ct = 0; ct < M_DL / 16; ++ct)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(oacc[ct][i]));
+            for (int i = 0; i < 4; ++i) amb = max(amb, __float_as_uint(oacc[ct][i]) & 0x7FFFFFFFu);
+        float amax = __uint_as_float(amb);
         amax = fmaxf(amax, __shfl_xor(amax, 16));
         amax = fmaxf(amax, __shfl_xor(amax, 32));
         const int k = part_exponent(amax * inv);

@@ -74,6 +74,21 @@ struct MlaSliceLds {
 };
 static_assert(2 * M_TILE_BYTES + M3_FP8_NBUF * M3_FP8_TILE <= M3_NBUF * M_TILE_BYTES, "e4m3 staging fits");
 
+// Largest |value| of a lane's accumulators and those of lane (lane ^ 32).
+// Magnitudes of non-NaN floats order like their bit patterns read as
+// unsigned integers, so the maximum is taken on the bits with the sign
+// cleared: integer instructions, where fmaxf would first canonicalize every
+// accumulator (a second instruction per value).
+__device__ __forceinline__ float max_abs_pair(const f32x16 (&o)[M_DL / 32], int lane) {
+    uint32_t m = 0u;
+#pragma unroll
+    for (int cb = 0; cb < M_DL / 32; ++cb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) m = max(m, __float_as_uint(o[cb][e]) & 0x7FFFFFFFu);
+    const float a = __uint_as_float(m);
+    return fmaxf(a, lane_xor32(a, lane));
+}
+
 // Split partials are stored as fp16 with one power-of-two scale per (query
 // row, head, slice): the head's largest |value| times 2^k lies in
 // [2^14, 2^15), so every value keeps 11 significant bits relative to it and
@@ -640,12 +655,7 @@ __device__ __forceinline__ void mla_store_partial_at(const MlaArgs& a, size_t pf
     const float inv = empty ? 0.f : 1.f / acc.l_tot;
     const float lse_nat = empty ? -INFINITY : (acc.m_ref + log2f(acc.l_tot)) * LN2;
     // the head's values sit in lanes c32 and c32 + 32
-    float amax = 0.f;
-#pragma unroll
-    for (int cb = 0; cb < M_DL / 32; ++cb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(acc.o[cb][e]));
-    amax = fmaxf(amax, lane_xor32(amax, lane));
+    const float amax = max_abs_pair(acc.o, lane);
     const int k = part_exponent(amax * inv);
     mla_stage_rows<true>(acc, inv * pow2i(k), L);
     const size_t pidx = pfirst + pstride * hl;
